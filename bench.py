@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Benchmark of the per-rank ZeRO/FSDP optimizer step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one pass of the whole hot path over one batch of synthetic
+input, on one rank's real-size shard (inputs resident in HBM):
+  grad_accum over every micro-batch (bf16 -> fp32), grad_norm_sq (the norm
+  is formed every step: it feeds the clip when the workload clips and the
+  non-finite skip always), and the fused adamw_step with the bf16 re-cast.
+The shard range is host arithmetic done once at set-up.  Default workload:
+the Llama-7B-shaped buffer over 8 ranks, one 842,301,952-element shard,
+8 micro-batches.
+
+Prints ONE JSON line: whole-step throughput (shard elements per second),
+the roofline of the dominant kernel (adamw_step, timed live with HIP events
+on the launch stream) and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0   # MI355X published HBM3E bandwidth
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def step_bytes_per_elem(w) -> dict:
+    """Algorithmic HBM bytes per shard element of each kernel of one step."""
+    g = 2 if w.grad_dtype == "bf16" else 4
+    accum_first = g + 4
+    accum_next = g + 8
+    adamw = 28 + (2 if w.bf16_param else 0)
+    return {"grad_accum_first": accum_first, "grad_accum_next": accum_next,
+            "grad_norm_sq": 4, "adamw_step": adamw,
+            "step": accum_first + (w.micro_batches - 1) * accum_next + 4 + adamw}
+
+
+def shard_len(w) -> int:
+    import fsdp_sharded_optimizer_amd as zs
+    _, start, end, _ = zs.zero_shard_range(w.total, w.world, w.rank)
+    return end - start
+
+
+# ---------------------------------------------------------------------------
+# GPU leg
+# ---------------------------------------------------------------------------
+
+def run_gpu(w, steps: int, warmup: int):
+    import torch
+    import workloads
+    import fsdp_sharded_optimizer_amd as zs
+
+    n = shard_len(w)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    log(f"[bench] workload={w.name} shard_elems={n} micro_batches={w.micro_batches}")
+    master = workloads.master_init(w, n, dev)
+    param = master.to(torch.bfloat16) if w.bf16_param else None
+    exp_avg = torch.zeros(n, dtype=torch.float32, device=dev)
+    exp_avg_sq = torch.zeros(n, dtype=torch.float32, device=dev)
+    acc = torch.empty(n, dtype=torch.float32, device=dev)
+    grads = [workloads.grad_draw(w, n, 1, mb, dev) for mb in range(w.micro_batches)]
+    norm = torch.zeros(1, dtype=torch.float64, device=dev)
+    ws = torch.empty(max(zs.grad_norm_sq_workspace_bytes(n), 8), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs resident: {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    timing = []   # per step: (accum_start, norm_start, adamw_start, adamw_end)
+
+    def one_step(t: int, record: bool):
+        e = [ev() for _ in range(4)] if record else None
+        if record:
+            e[0].record()
+        for mb, g in enumerate(grads):
+            zs.grad_accum(acc, g, overwrite=(mb == 0))
+        if record:
+            e[1].record()
+        zs.grad_norm_sq(acc, w.grad_scale, norm, ws)
+        if record:
+            e[2].record()
+        hp = zs.AdamWConfig(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                            weight_decay=w.weight_decay, grad_scale=w.grad_scale,
+                            max_norm=w.max_norm, extra_norm_sq=workloads.other_ranks_norm_sq(w, 1, n),
+                            step=t)
+        zs.adamw_step(hp, master, exp_avg, exp_avg_sq, acc, param, norm_sq=norm)
+        if record:
+            e[3].record()
+            timing.append(e)
+
+    t = 0
+    for _ in range(warmup):
+        t += 1
+        one_step(t, record=False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        t += 1
+        one_step(t, record=True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    acc_ms = sum(e[0].elapsed_time(e[1]) for e in timing) / steps
+    norm_ms = sum(e[1].elapsed_time(e[2]) for e in timing) / steps
+    adamw_ms = sum(e[2].elapsed_time(e[3]) for e in timing) / steps
+    assert math.isfinite(norm.item()), "non-finite gradient norm in the bench"
+
+    # achievable-bandwidth reference: a plain device copy of 4 GiB (also the
+    # calibration kernel for the HBM byte counters)
+    src = torch.empty(1 << 30, dtype=torch.float32, device=dev)
+    src.fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0, c1 = ev(), ev()
+    c0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_ms = c0.elapsed_time(c1) / 5
+    copy_gbps = 2 * src.numel() * 4 / (copy_ms * 1e-3) / 1e9
+    del src, dst
+    return {"n": n, "wall_s": wall, "accum_ms": acc_ms, "norm_ms": norm_ms, "adamw_ms": adamw_ms,
+            "copy_gbps": copy_gbps}
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline leg: the oracle as it stands on a bounded sample
+# ---------------------------------------------------------------------------
+
+def run_cpu_baseline(w, target_s: float = 10.0, sample: int = 1 << 24):
+    import numpy as np
+    import torch
+    import oracle
+    import workloads
+
+    n = sample
+    master = workloads.master_init(w, n, "cpu").numpy().copy()
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    bf = np.zeros(n, np.uint16) if w.bf16_param else None
+    code = oracle.BF16 if w.grad_dtype == "bf16" else oracle.F32
+    grads = []
+    for mb in range(w.micro_batches):
+        g = workloads.grad_draw(w, n, 1, mb, "cpu")
+        grads.append(g.view(torch.int16).numpy().view(np.uint16).copy() if code == oracle.BF16
+                     else g.numpy().copy())
+    acc = np.empty(n, np.float32)
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        for mb, g in enumerate(grads):
+            oracle.grad_accum(acc, g, code, overwrite=(mb == 0))
+        s = oracle.grad_norm_sq(acc, w.grad_scale)
+        hp = oracle.make_hp(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, w.grad_scale, w.max_norm,
+                            workloads.other_ranks_norm_sq(w, 1, n), done + 1)
+        oracle.adamw_step(hp, master, m, v, acc, bf, norm_sq=s)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or done >= 20:
+            break
+    return {"value": n * done / el, "unit": "elements/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n} elements of the same workload (first {n} of a shard drawn by the same "
+                      f"recipe on the CPU), {done} whole steps ({w.micro_batches} micro-batch "
+                      f"accumulations + norm + AdamW/bf16) in {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama7b_shard")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU's shard only; --gpus {args.gpus} is not "
+              "supported (collectives are out of scope). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import workloads
+    if args.workload not in workloads.WORKLOADS:
+        sys.exit(f"unknown workload {args.workload}; one of {sorted(workloads.WORKLOADS)}")
+    w = workloads.WORKLOADS[args.workload]
+
+    import fsdp_sharded_optimizer_amd as zs
+    zs.lib()
+
+    r = run_gpu(w, args.steps, args.warmup)
+    n = r["n"]
+    bpe = step_bytes_per_elem(w)
+    ms_per_step = r["wall_s"] * 1e3 / args.steps
+    adamw_bytes = bpe["adamw_step"] * n
+    achieved = adamw_bytes / (r["adamw_ms"] * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host cores ...")
+        cpu = run_cpu_baseline(w, args.cpu_seconds)
+    step_gbps = bpe["step"] * n / (ms_per_step * 1e-3) / 1e9
+    out = {
+        "metric": "AdamW shard step: elements/s and achieved HBM GB/s (% of peak) per GPU",
+        "value": n / (ms_per_step * 1e-3),
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded U(-0.1,0.1) master, N(0,std) bf16 micro-batch grads)",
+        "config": {"workload": w.name, "shard_elems": n, "total_params": w.total, "world": w.world,
+                   "rank": w.rank, "micro_batches": w.micro_batches, "grad_dtype": w.grad_dtype,
+                   "state": "fp32 master/exp_avg/exp_avg_sq + bf16 param", "clip": w.max_norm > 0},
+        "step_hbm_gbps": step_gbps,
+        "step_hbm_frac": step_gbps / HBM_PEAK_GBPS,
+        "kernels_ms": {"grad_accum_all_micro_batches": r["accum_ms"], "grad_norm_sq": r["norm_ms"],
+                       "adamw_step": r["adamw_ms"]},
+        "bytes_per_elem": bpe,
+        "copy_ceiling_gbps": r["copy_gbps"],
+        "roofline": {"kernel": "adamw_step", "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

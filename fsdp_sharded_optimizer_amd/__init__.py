@@ -1,0 +1,29 @@
+"""MI355X-native per-rank ZeRO/FSDP optimizer step (libzshard).
+
+The Python names mirror the C ABI in include/zshard.h:
+
+    zero_shard_range(total, world, rank) -> (chunk, start, end, padded_total)
+    flat_pack(src_tensors, flat, padded_total=None)
+    flat_unpack(flat, dst_tensors)
+    grad_accum(acc, grad, overwrite)
+    grad_norm_sq(grad, grad_scale, out, workspace=None)
+    adamw_step(hp, master, exp_avg, exp_avg_sq, grad, param_bf16=None, norm_sq=None)
+
+All device work runs in the library's gfx950 HIP kernels on the current
+torch stream; torch supplies device memory and the stream only.
+"""
+from ._binding import (  # noqa: F401
+    EXPORTS,
+    LIB_PATH,
+    AdamWConfig,
+    ZShardError,
+    adamw_step,
+    flat_pack,
+    flat_unpack,
+    grad_accum,
+    grad_norm_sq,
+    grad_norm_sq_workspace_bytes,
+    lib,
+    zero_shard_range,
+)
+from .step import ShardOptimizer  # noqa: F401

@@ -1,0 +1,246 @@
+"""ctypes binding of libzshard.so (include/zshard.h).
+
+Argument marshalling only: torch tensors supply device pointers, sizes and
+the current HIP stream; every step of the path runs in the library's HIP
+kernels.  There is no fallback: if the library is not built, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libzshard.so")
+
+ZS_F32 = 0
+ZS_BF16 = 1
+ZS_OK = 0
+ZS_EINVAL = -1
+ZS_EOVERLAP = -2
+ZS_EWORKSPACE = -3
+ZS_EHIP = -4
+
+# every symbol include/zshard.h declares
+EXPORTS = (
+    "zero_shard_range", "flat_pack", "flat_unpack", "grad_accum",
+    "grad_norm_sq_workspace_bytes", "grad_norm_sq", "adamw_step",
+    "zs_strerror", "zs_last_hip_error",
+)
+
+
+class ZShardError(RuntimeError):
+    def __init__(self, fn: str, code: int, message: str):
+        super().__init__(f"{fn}: {message} (code {code})")
+        self.code = code
+
+
+class Shard(ctypes.Structure):
+    _fields_ = [("chunk", ctypes.c_int64), ("start", ctypes.c_int64),
+                ("end", ctypes.c_int64), ("padded_total", ctypes.c_int64)]
+
+    def as_tuple(self):
+        return (self.chunk, self.start, self.end, self.padded_total)
+
+
+class Tensor(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("numel", ctypes.c_int64)]
+
+
+class AdamW(ctypes.Structure):
+    _fields_ = [
+        ("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+        ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double),
+        ("grad_scale", ctypes.c_double), ("max_norm", ctypes.c_double),
+        ("extra_norm_sq", ctypes.c_double), ("step", ctypes.c_int64),
+    ]
+
+
+@dataclass
+class AdamWConfig:
+    """Hyperparameters of one step (``step`` is t >= 1)."""
+    lr: float
+    beta1: float = 0.9
+    beta2: float = 0.999
+    eps: float = 1e-8
+    weight_decay: float = 0.0
+    grad_scale: float = 1.0
+    max_norm: float = 0.0
+    extra_norm_sq: float = 0.0
+    step: int = 1
+
+    def c_struct(self) -> AdamW:
+        return AdamW(self.lr, self.beta1, self.beta2, self.eps, self.weight_decay,
+                     self.grad_scale, self.max_norm, self.extra_norm_sq, int(self.step))
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m fsdp_sharded_optimizer_amd.build` "
+                "(or __graft_entry__.build()); there is no fallback path")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64, D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        L.zero_shard_range.argtypes = [I64, I32, I32, ctypes.POINTER(Shard)]
+        L.zero_shard_range.restype = I32
+        L.flat_pack.argtypes = [ctypes.POINTER(Tensor), I32, I32, P, I32, I64, P]
+        L.flat_pack.restype = I32
+        L.flat_unpack.argtypes = [P, I32, ctypes.POINTER(Tensor), I32, I32, P]
+        L.flat_unpack.restype = I32
+        L.grad_accum.argtypes = [P, P, I32, I64, I32, P]
+        L.grad_accum.restype = I32
+        L.grad_norm_sq_workspace_bytes.argtypes = [I64]
+        L.grad_norm_sq_workspace_bytes.restype = I64
+        L.grad_norm_sq.argtypes = [P, I64, D, P, P, I64, P]
+        L.grad_norm_sq.restype = I32
+        L.adamw_step.argtypes = [ctypes.POINTER(AdamW), P, P, P, P, P, I64, P, P]
+        L.adamw_step.restype = I32
+        L.zs_strerror.argtypes = [I32]
+        L.zs_strerror.restype = ctypes.c_char_p
+        L.zs_last_hip_error.argtypes = []
+        L.zs_last_hip_error.restype = I32
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, code: int) -> None:
+    if code != ZS_OK:
+        msg = lib().zs_strerror(code).decode()
+        if code == ZS_EHIP:
+            msg += f" (hipError {lib().zs_last_hip_error()})"
+        raise ZShardError(fn, code, msg)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return ZS_F32
+    if t.dtype == torch.bfloat16:
+        return ZS_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: float32 or bfloat16")
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype=None) -> int:
+    """Device pointer of a contiguous GPU tensor (0 for None)."""
+    if t is None:
+        return 0
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a GPU tensor, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def zero_shard_range(total: int, world: int, rank: int):
+    """(chunk, start, end, padded_total) of `rank`'s range; host only."""
+    out = Shard()
+    _check("zero_shard_range", lib().zero_shard_range(int(total), int(world), int(rank), ctypes.byref(out)))
+    return out.as_tuple()
+
+
+def _tensor_list(ts: Sequence[torch.Tensor], name: str):
+    arr = (Tensor * max(len(ts), 1))()
+    dt = None
+    for i, t in enumerate(ts):
+        arr[i].ptr = _dev(t, f"{name}[{i}]")
+        arr[i].numel = t.numel()
+        code = _dtype_code(t)
+        if dt is not None and code != dt:
+            raise TypeError(f"{name}: all tensors must share one dtype")
+        dt = code
+    return arr, dt
+
+
+def flat_pack(src: Sequence[torch.Tensor], flat: torch.Tensor, padded_total: Optional[int] = None,
+              stream=None) -> None:
+    """flat[o_i + j] = src[i].view(-1)[j]; flat[sum numel:padded_total] = 0."""
+    arr, dt = _tensor_list(src, "src")
+    if dt is None:
+        dt = _dtype_code(flat)
+    pt = flat.numel() if padded_total is None else int(padded_total)
+    if pt > flat.numel():
+        raise ValueError("flat_pack: padded_total exceeds the flat buffer")
+    _check("flat_pack", lib().flat_pack(arr, len(src), dt, _dev(flat, "flat"), _dtype_code(flat), pt,
+                                        _stream(stream)))
+
+
+def flat_unpack(flat: torch.Tensor, dst: Sequence[torch.Tensor], stream=None) -> None:
+    """dst[i].view(-1)[j] = flat[o_i + j] (padding ignored)."""
+    arr, dt = _tensor_list(dst, "dst")
+    if dt is None:
+        dt = _dtype_code(flat)
+    total = sum(t.numel() for t in dst)
+    if total > flat.numel():
+        raise ValueError("flat_unpack: destinations exceed the flat buffer")
+    _check("flat_unpack", lib().flat_unpack(_dev(flat, "flat"), _dtype_code(flat), arr, len(dst), dt,
+                                            _stream(stream)))
+
+
+def grad_accum(acc: torch.Tensor, grad: torch.Tensor, overwrite: bool, stream=None) -> None:
+    """acc = widen(grad) (overwrite) or acc = acc + widen(grad), fp32."""
+    if grad.numel() != acc.numel():
+        raise ValueError("grad_accum: size mismatch")
+    _check("grad_accum", lib().grad_accum(_dev(acc, "acc", torch.float32), _dev(grad, "grad"),
+                                          _dtype_code(grad), acc.numel(), 1 if overwrite else 0,
+                                          _stream(stream)))
+
+
+def grad_norm_sq_workspace_bytes(n: int) -> int:
+    return int(lib().grad_norm_sq_workspace_bytes(int(n)))
+
+
+def grad_norm_sq(grad: torch.Tensor, grad_scale: float, out: torch.Tensor,
+                 workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """out[0] (fp64, device) = sum of (fl32(grad * scale))^2 in binary64."""
+    n = grad.numel()
+    need = grad_norm_sq_workspace_bytes(n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=grad.device)
+    if out.dtype != torch.float64 or out.numel() < 1:
+        raise TypeError("grad_norm_sq: out must hold one float64")
+    _check("grad_norm_sq", lib().grad_norm_sq(_dev(grad, "grad", torch.float32), n, float(grad_scale),
+                                              _dev(out, "out"), _dev(workspace, "workspace"),
+                                              workspace.numel() * workspace.element_size(),
+                                              _stream(stream)))
+    return out
+
+
+def adamw_step(hp: AdamWConfig, master: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor,
+               grad: torch.Tensor, param_bf16: Optional[torch.Tensor] = None,
+               norm_sq: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Fused AdamW update of the shard (in place), with the bf16 re-cast."""
+    n = master.numel()
+    for t, nm in ((exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq"), (grad, "grad")):
+        if t.numel() != n:
+            raise ValueError(f"adamw_step: {nm} size mismatch")
+    if param_bf16 is not None and param_bf16.numel() != n:
+        raise ValueError("adamw_step: param_bf16 size mismatch")
+    if norm_sq is not None and norm_sq.dtype != torch.float64:
+        raise TypeError("adamw_step: norm_sq must be float64")
+    c = hp.c_struct()
+    _check("adamw_step", lib().adamw_step(
+        ctypes.byref(c), _dev(master, "master", torch.float32), _dev(exp_avg, "exp_avg", torch.float32),
+        _dev(exp_avg_sq, "exp_avg_sq", torch.float32), _dev(grad, "grad", torch.float32),
+        _dev(param_bf16, "param_bf16", torch.bfloat16), n, _dev(norm_sq, "norm_sq"), _stream(stream)))

@@ -1,0 +1,258 @@
+// C-ABI entry points of libzshard (declared in include/zshard.h).
+//
+// Every call validates its arguments on the host first (null pointers,
+// ranges, dtypes, alignment, overlap) and returns an error code without
+// launching anything when they are wrong.  Valid calls only enqueue kernels
+// on the caller's stream.  Host scalars are formed in binary64 and rounded
+// to binary32 once.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/zshard.h"
+#include "zs_common.h"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+int32_t hip_status(hipError_t e) {
+    if (e == hipSuccess) return ZS_OK;
+    g_last_hip_error = (int32_t)e;
+    return ZS_EHIP;
+}
+
+inline uintptr_t addr(const void* p) { return reinterpret_cast<uintptr_t>(p); }
+inline bool aligned(const void* p, uintptr_t a) { return (addr(p) & (a - 1)) == 0; }
+
+// [p, p+bytes) and [q, q+qbytes) share a byte (empty ranges never overlap)
+inline bool overlap(const void* p, int64_t bytes, const void* q, int64_t qbytes) {
+    if (bytes <= 0 || qbytes <= 0) return false;
+    const uintptr_t a = addr(p), b = addr(q);
+    return a < b + (uintptr_t)qbytes && b < a + (uintptr_t)bytes;
+}
+
+inline int64_t elem_size(int32_t dtype) { return dtype == ZS_F32 ? 4 : 2; }
+inline bool dtype_ok(int32_t d) { return d == ZS_F32 || d == ZS_BF16; }
+inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+// elements whose byte size fits in int64 and in the address space
+inline bool size_ok(int64_t n, int64_t esize) { return n >= 0 && n <= INT64_MAX / 16 / esize; }
+
+}  // namespace
+
+extern "C" {
+
+const char* zs_strerror(int32_t code) {
+    switch (code) {
+        case ZS_OK: return "ok";
+        case ZS_EINVAL: return "invalid argument";
+        case ZS_EOVERLAP: return "buffers overlap";
+        case ZS_EWORKSPACE: return "workspace too small";
+        case ZS_EHIP: return "HIP launch failed";
+        default: return "unknown error code";
+    }
+}
+
+int32_t zs_last_hip_error(void) { return g_last_hip_error; }
+
+int32_t zero_shard_range(int64_t total, int32_t world, int32_t rank, zs_shard* out) {
+    if (out == nullptr || world < 1 || rank < 0 || rank >= world || total < 0) return ZS_EINVAL;
+    // ceil(total / world) without forming total + world - 1
+    const int64_t chunk = total / world + (total % world != 0 ? 1 : 0);
+    if (chunk > INT64_MAX / world) return ZS_EINVAL;
+    int64_t start = (int64_t)rank * chunk;
+    if (start > total) start = total;   // a rank past the end owns nothing
+    const int64_t end = total - start < chunk ? total : start + chunk;
+    out->chunk = chunk;
+    out->start = start;
+    out->end = end;
+    out->padded_total = (int64_t)world * chunk;
+    return ZS_OK;
+}
+
+int32_t grad_accum(float* acc, const void* grad, int32_t grad_dtype, int64_t n, int32_t overwrite,
+                   void* hip_stream) {
+    if (!dtype_ok(grad_dtype) || !size_ok(n, 4)) return ZS_EINVAL;
+    if (n == 0) return ZS_OK;
+    const int64_t gsz = elem_size(grad_dtype);
+    if (acc == nullptr || grad == nullptr) return ZS_EINVAL;
+    if (!aligned(acc, 4) || !aligned(grad, (uintptr_t)gsz)) return ZS_EINVAL;
+    if (overlap(acc, n * 4, grad, n * gsz)) return ZS_EOVERLAP;
+    const bool vec = aligned(acc, 16) && aligned(grad, 16);
+    return hip_status(zs::launch_grad_accum(acc, grad, grad_dtype == ZS_BF16, n, overwrite != 0, vec,
+                                            as_stream(hip_stream)));
+}
+
+int64_t grad_norm_sq_workspace_bytes(int64_t n) {
+    if (n < 0) return -1;
+    return zs::norm_partial_blocks(n) * (int64_t)sizeof(double);
+}
+
+int32_t grad_norm_sq(const float* grad, int64_t n, double grad_scale, double* out_sq_dev,
+                     void* workspace, int64_t workspace_bytes, void* hip_stream) {
+    if (!size_ok(n, 4) || out_sq_dev == nullptr || !aligned(out_sq_dev, 8)) return ZS_EINVAL;
+    if (!(grad_scale > 0.0) || !std::isfinite(grad_scale)) return ZS_EINVAL;
+    const int64_t need = grad_norm_sq_workspace_bytes(n);
+    if (n > 0 && (grad == nullptr || !aligned(grad, 4))) return ZS_EINVAL;
+    if (need > 0 && (workspace == nullptr || !aligned(workspace, 8))) return ZS_EINVAL;
+    if (workspace_bytes < need) return ZS_EWORKSPACE;
+    if (overlap(grad, n * 4, out_sq_dev, 8) || overlap(workspace, need, out_sq_dev, 8) ||
+        overlap(workspace, need, grad, n * 4))
+        return ZS_EOVERLAP;
+    const bool vec = aligned(grad, 16);
+    return hip_status(zs::launch_grad_norm_sq(grad, n, (float)grad_scale, out_sq_dev,
+                                              static_cast<double*>(workspace), vec,
+                                              as_stream(hip_stream)));
+}
+
+int32_t adamw_step(const zs_adamw* hp, float* master, float* exp_avg, float* exp_avg_sq,
+                   const float* grad, uint16_t* param_bf16, int64_t n, const double* norm_sq_dev,
+                   void* hip_stream) {
+    if (hp == nullptr || !size_ok(n, 4)) return ZS_EINVAL;
+    if (hp->step < 1) return ZS_EINVAL;
+    if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0) || !(hp->beta2 >= 0.0 && hp->beta2 < 1.0))
+        return ZS_EINVAL;
+    if (!(hp->eps > 0.0) || !std::isfinite(hp->eps)) return ZS_EINVAL;
+    if (!(hp->lr >= 0.0) || !std::isfinite(hp->lr)) return ZS_EINVAL;
+    if (!(hp->weight_decay >= 0.0) || !std::isfinite(hp->weight_decay)) return ZS_EINVAL;
+    if (!(hp->grad_scale > 0.0) || !std::isfinite(hp->grad_scale)) return ZS_EINVAL;
+    if (std::isnan(hp->max_norm) || hp->extra_norm_sq < 0.0) return ZS_EINVAL;
+    if (norm_sq_dev != nullptr && !aligned(norm_sq_dev, 8)) return ZS_EINVAL;
+    if (n == 0) return ZS_OK;
+    if (master == nullptr || exp_avg == nullptr || exp_avg_sq == nullptr || grad == nullptr)
+        return ZS_EINVAL;
+    if (!aligned(master, 4) || !aligned(exp_avg, 4) || !aligned(exp_avg_sq, 4) || !aligned(grad, 4) ||
+        (param_bf16 != nullptr && !aligned(param_bf16, 2)))
+        return ZS_EINVAL;
+    const void* bufs[5] = {master, exp_avg, exp_avg_sq, grad, param_bf16};
+    const int64_t bytes[5] = {n * 4, n * 4, n * 4, n * 4, param_bf16 ? n * 2 : 0};
+    for (int i = 0; i < 5; ++i) {
+        for (int j = i + 1; j < 5; ++j)
+            if (overlap(bufs[i], bytes[i], bufs[j], bytes[j])) return ZS_EOVERLAP;
+        if (norm_sq_dev != nullptr && i != 3 && overlap(bufs[i], bytes[i], norm_sq_dev, 8))
+            return ZS_EOVERLAP;
+    }
+
+    // host scalars: binary64, each rounded to binary32 once
+    const double t = (double)hp->step;
+    const double bias_correction1 = 1.0 - std::pow(hp->beta1, t);
+    const double bias_correction2 = 1.0 - std::pow(hp->beta2, t);
+    zs::AdamwArgs a;
+    a.beta1 = (float)hp->beta1;
+    a.beta2 = (float)hp->beta2;
+    a.one_minus_beta1 = (float)(1.0 - hp->beta1);
+    a.one_minus_beta2 = (float)(1.0 - hp->beta2);
+    a.step_size = (float)(hp->lr / bias_correction1);
+    a.bias_correction2_sqrt = (float)std::sqrt(bias_correction2);
+    a.eps = (float)hp->eps;
+    a.decay = (float)(1.0 - hp->lr * hp->weight_decay);
+    a.grad_scale = (float)hp->grad_scale;
+    a.clip = hp->max_norm > 0.0 ? 1 : 0;
+    a.max_norm = hp->max_norm;
+    a.extra_norm_sq = hp->extra_norm_sq;
+    a.norm_sq = norm_sq_dev;
+    a.master = master;
+    a.exp_avg = exp_avg;
+    a.exp_avg_sq = exp_avg_sq;
+    a.grad = grad;
+    a.param_bf16 = param_bf16;
+    a.n = n;
+    const bool vec = aligned(master, 16) && aligned(exp_avg, 16) && aligned(exp_avg_sq, 16) &&
+                     aligned(grad, 16) && (param_bf16 == nullptr || aligned(param_bf16, 16));
+    return hip_status(zs::launch_adamw(a, vec, as_stream(hip_stream)));
+}
+
+// ---------------------------------------------------------------------------
+// flatten / unflatten
+// ---------------------------------------------------------------------------
+
+static int32_t flat_common(const zs_tensor* tensors, int32_t count, void* flat, int32_t flat_dtype,
+                           int32_t tensor_dtype, int64_t padded_total, bool unpack,
+                           hipStream_t stream) {
+    if (count < 0 || (count > 0 && tensors == nullptr)) return ZS_EINVAL;
+    if (!dtype_ok(flat_dtype) || !dtype_ok(tensor_dtype)) return ZS_EINVAL;
+    int kind;
+    if (flat_dtype == tensor_dtype) kind = flat_dtype == ZS_F32 ? 0 : 1;
+    else if (!unpack && tensor_dtype == ZS_BF16 && flat_dtype == ZS_F32) kind = 2;
+    else if (unpack && flat_dtype == ZS_F32 && tensor_dtype == ZS_BF16) kind = 3;
+    else return ZS_EINVAL;
+    const int64_t fsz = elem_size(flat_dtype), tsz = elem_size(tensor_dtype);
+    int64_t total = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        const int64_t k = tensors[i].numel;
+        if (!size_ok(k, 4) || total > INT64_MAX / 16 / 4 - k) return ZS_EINVAL;
+        if (k > 0 && (tensors[i].ptr == nullptr || !aligned(tensors[i].ptr, (uintptr_t)tsz)))
+            return ZS_EINVAL;
+        total += k;
+    }
+    if (unpack) padded_total = total;
+    if (!size_ok(padded_total, 4) || total > padded_total) return ZS_EINVAL;
+    if (padded_total == 0) return ZS_OK;
+    if (flat == nullptr || !aligned(flat, (uintptr_t)fsz)) return ZS_EINVAL;
+    for (int32_t i = 0; i < count; ++i) {
+        const int64_t bi = tensors[i].numel * tsz;
+        if (overlap(tensors[i].ptr, bi, flat, padded_total * fsz)) return ZS_EOVERLAP;
+        if (unpack)   // written tensors must be pairwise disjoint
+            for (int32_t j = i + 1; j < count; ++j)
+                if (overlap(tensors[i].ptr, bi, tensors[j].ptr, tensors[j].numel * tsz))
+                    return ZS_EOVERLAP;
+    }
+
+    // batches of up to kFlatMaxTensors entries; the pack padding is one
+    // more entry with a NULL tensor
+    const int64_t tile = zs::flat_tile_elems();
+    const bool flat16 = aligned(flat, 16);
+    zs::FlatBatch b;
+    std::memset(&b, 0, sizeof(b));
+    b.flat = flat;
+    int64_t offset = 0;
+    auto flush = [&]() -> int32_t {
+        if (b.count == 0) return ZS_OK;
+        const int32_t rc = hip_status(zs::launch_flat(b, kind, unpack ? 1 : 0, stream));
+        std::memset(&b, 0, sizeof(b));
+        b.flat = flat;
+        return rc;
+    };
+    auto add = [&](void* ptr, int64_t flat_off, int64_t numel) -> int32_t {
+        if (b.count == zs::kFlatMaxTensors) {
+            const int32_t rc = flush();
+            if (rc != ZS_OK) return rc;
+        }
+        const int c = b.count;
+        b.tensor[c] = ptr;
+        b.flat_off[c] = flat_off;
+        b.numel[c] = numel;
+        b.vec_ok[c] = flat16 && (flat_off % 8 == 0) && (ptr == nullptr || aligned(ptr, 16));
+        b.tile_start[c + 1] = b.tile_start[c] + (numel + tile - 1) / tile;
+        b.count = c + 1;
+        return ZS_OK;
+    };
+    for (int32_t i = 0; i < count; ++i) {
+        const int64_t k = tensors[i].numel;
+        if (k > 0) {
+            const int32_t rc = add(tensors[i].ptr, offset, k);
+            if (rc != ZS_OK) return rc;
+        }
+        offset += k;
+    }
+    if (!unpack && padded_total > total) {
+        const int32_t rc = add(nullptr, total, padded_total - total);
+        if (rc != ZS_OK) return rc;
+    }
+    return flush();
+}
+
+int32_t flat_pack(const zs_tensor* src, int32_t count, int32_t src_dtype, void* flat,
+                  int32_t flat_dtype, int64_t padded_total, void* hip_stream) {
+    return flat_common(src, count, flat, flat_dtype, src_dtype, padded_total, false,
+                       as_stream(hip_stream));
+}
+
+int32_t flat_unpack(const void* flat, int32_t flat_dtype, const zs_tensor* dst, int32_t count,
+                    int32_t dst_dtype, void* hip_stream) {
+    return flat_common(dst, count, const_cast<void*>(flat), flat_dtype, dst_dtype, 0, true,
+                       as_stream(hip_stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+// Internal declarations shared by the libzshard sources (not installed).
+//
+// Device helpers for gfx950 (wave64, 128-bit global accesses) and the
+// launchers each kernel file provides to the C-ABI layer in api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace zs {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBlock = 256;   // threads per workgroup: 4 wave64s
+
+// --- bf16 <-> fp32 ---------------------------------------------------------
+// Widening is exact: the bf16 pattern is the upper half of the fp32 one.
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Round to nearest, ties to even, by adding 0x7FFF plus the lowest kept bit
+// and truncating; the carry walks into the exponent (and to +-inf) as IEEE
+// rounding does.  Every NaN becomes the quiet NaN 0x7FC0.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
+    uint32_t u = __float_as_uint(x);
+    uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? 0x7FC0u : r;
+}
+
+// Two bf16 patterns in one 32-bit word, element 0 in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// --- streaming loads / stores ---------------------------------------------
+// Every byte of the streamed buffers is touched exactly once per call, so
+// the accesses carry the non-temporal hint (no reuse to keep in L2/MALL).
+template <typename T>
+__device__ __forceinline__ T ld_stream(const T* p) { return __builtin_nontemporal_load(p); }
+template <typename T>
+__device__ __forceinline__ void st_stream(T* p, T v) { __builtin_nontemporal_store(v, p); }
+
+// --- scalars of one AdamW step, formed on the host ------------------------
+struct AdamwArgs {
+    float beta1, beta2;
+    float one_minus_beta1, one_minus_beta2;
+    float step_size;            // (float)(lr / bias_correction1)
+    float bias_correction2_sqrt;// (float)sqrt(bias_correction2)
+    float eps;
+    float decay;                // (float)(1 - lr*wd)
+    float grad_scale;           // (float)grad_scale
+    int32_t clip;               // max_norm > 0
+    double max_norm;
+    double extra_norm_sq;
+    const double* norm_sq;      // device, nullable
+    float* master;
+    float* exp_avg;
+    float* exp_avg_sq;
+    const float* grad;
+    uint16_t* param_bf16;       // nullable
+    int64_t n;
+};
+
+// Launchers: enqueue on `stream`, return the hipError_t of the launch.
+hipError_t launch_adamw(const AdamwArgs& a, bool vec_ok, hipStream_t stream);
+hipError_t launch_grad_accum(float* acc, const void* grad, int grad_bf16, int64_t n,
+                             int overwrite, bool vec_ok, hipStream_t stream);
+int64_t norm_partial_blocks(int64_t n);
+hipError_t launch_grad_norm_sq(const float* grad, int64_t n, float scale, double* out,
+                               double* partials, bool vec_ok, hipStream_t stream);
+
+// One launch of the flatten/unflatten copy covers up to kFlatMaxTensors
+// tensors (the table travels in the kernel arguments; no device allocation).
+constexpr int kFlatMaxTensors = 32;
+struct FlatBatch {
+    void* tensor[kFlatMaxTensors + 1];       // per tensor: src (pack) / dst (unpack); NULL = zero fill
+    int64_t flat_off[kFlatMaxTensors + 1];   // element offset of the tensor in the flat buffer
+    int64_t numel[kFlatMaxTensors + 1];
+    int64_t tile_start[kFlatMaxTensors + 2]; // first workgroup of each tensor; [count] = total
+    int32_t vec_ok[kFlatMaxTensors + 1];     // 128-bit path allowed for this tensor
+    int32_t count;                           // tensors in this batch (incl. a zero-fill entry)
+    void* flat;
+};
+// kind: 0 = f32->f32, 1 = bf16->bf16, 2 = bf16->f32 (pack widen), 3 = f32->bf16 (unpack RNE)
+hipError_t launch_flat(const FlatBatch& b, int kind, int unpack, hipStream_t stream);
+int64_t flat_tile_elems();
+
+}  // namespace zs

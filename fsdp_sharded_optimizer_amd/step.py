@@ -1,0 +1,61 @@
+"""One rank's sharded optimizer state and its step, on the library's entry points.
+
+The state is plain device buffers: the fp32 master shard, exp_avg and
+exp_avg_sq, the fp32 gradient accumulator, the bf16 parameter shard and the
+norm scratch.  A step is: ``accumulate`` once per micro-batch, then
+``step``: the squared-norm reduction (when requested) and the fused AdamW
+update with the bf16 re-cast.  Nothing here computes; it orders calls.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _binding as zs
+
+
+class ShardOptimizer:
+    def __init__(self, master: torch.Tensor, *, lr: float, betas=(0.9, 0.999), eps: float = 1e-8,
+                 weight_decay: float = 0.0, grad_scale: float = 1.0, max_norm: float = 0.0,
+                 param_bf16: Optional[torch.Tensor] = None, compute_norm: Optional[bool] = None):
+        if master.dtype != torch.float32 or master.device.type != "cuda":
+            raise TypeError("master must be an fp32 GPU tensor")
+        n = master.numel()
+        dev = master.device
+        self.master = master
+        self.exp_avg = torch.zeros(n, dtype=torch.float32, device=dev)
+        self.exp_avg_sq = torch.zeros(n, dtype=torch.float32, device=dev)
+        self.acc = torch.empty(n, dtype=torch.float32, device=dev)
+        self.param_bf16 = param_bf16
+        self.lr, self.betas, self.eps = lr, betas, eps
+        self.weight_decay, self.grad_scale, self.max_norm = weight_decay, grad_scale, max_norm
+        self.compute_norm = (max_norm > 0) if compute_norm is None else compute_norm
+        self.norm_sq = torch.zeros(1, dtype=torch.float64, device=dev)
+        self.workspace = torch.empty(max(zs.grad_norm_sq_workspace_bytes(n), 8), dtype=torch.uint8,
+                                     device=dev)
+        self.t = 0
+        self._pending = 0
+
+    def accumulate(self, grad: torch.Tensor) -> None:
+        """Add one micro-batch gradient (fp32 or bf16) into the fp32 buffer."""
+        zs.grad_accum(self.acc, grad, overwrite=(self._pending == 0))
+        self._pending += 1
+
+    def hp(self, extra_norm_sq: float = 0.0) -> zs.AdamWConfig:
+        return zs.AdamWConfig(lr=self.lr, beta1=self.betas[0], beta2=self.betas[1], eps=self.eps,
+                              weight_decay=self.weight_decay, grad_scale=self.grad_scale,
+                              max_norm=self.max_norm, extra_norm_sq=extra_norm_sq, step=self.t)
+
+    def step(self, extra_norm_sq: float = 0.0) -> None:
+        """Norm (if clipping or asked for), then the fused AdamW update."""
+        if self._pending == 0:
+            raise RuntimeError("step() without an accumulated gradient")
+        self.t += 1
+        norm = None
+        if self.compute_norm:
+            zs.grad_norm_sq(self.acc, self.grad_scale, self.norm_sq, self.workspace)
+            norm = self.norm_sq
+        zs.adamw_step(self.hp(extra_norm_sq), self.master, self.exp_avg, self.exp_avg_sq, self.acc,
+                      self.param_bf16, norm_sq=norm)
+        self._pending = 0

@@ -1,0 +1,213 @@
+/*
+ * zshard.h — C ABI of the MI355X (gfx950) per-rank ZeRO/FSDP optimizer-step
+ * library (libzshard.so).
+ *
+ * The library runs one data-parallel rank's share of a sharded optimizer
+ * step over a flattened 1-D parameter buffer: the shard range, flattening
+ * and unflattening, fp32 gradient accumulation, the scaled squared gradient
+ * norm with the global-norm clip, and the fused AdamW update of the fp32
+ * master / exp_avg / exp_avg_sq with the bf16 re-cast.  Collectives are the
+ * caller's business; the only cross-rank quantity the library consumes is
+ * the other ranks' share of the squared norm (zs_adamw.extra_norm_sq).
+ *
+ * Sources (pages; section or listing named):
+ *   [ZeRO page]   ai6s.net "cann-recipes-train" ZeRO 三阶段 page
+ *                 (https://ai6s.net/6a2abebd10ee7a33f27b4f16.html)
+ *   [Accum page]  ai6s.net LLaMA-13B 梯度累积 + Gradient Checkpoint page
+ *                 (https://ai6s.net/6a128b8710ee7a33f274bf75.html)
+ *   [Memory page] ybb.press "大模型分布式训练并行与显存工程实战"
+ *                 (https://www.ybb.press/ai-applications/14955.html)
+ *
+ * Conventions for every entry point:
+ *   - extern "C"; no exception crosses the ABI; every function is reentrant
+ *     and keeps no state except the thread-local last HIP error.
+ *   - Device buffers are owned by the caller (allocated and freed by it);
+ *     the library allocates nothing.  Host arrays passed in (zs_tensor
+ *     lists, zs_adamw) are read during the call only.
+ *   - hip_stream is a hipStream_t (NULL = the default stream).  Device calls
+ *     only enqueue work on it and return; nothing blocks, nothing syncs.
+ *   - Arguments are validated on the host before anything is enqueued; on
+ *     failure the call returns a negative code and launches nothing.
+ *     n == 0 (or count == 0 with nothing to pad) is a valid no-op.
+ *   - fp32 pointers must be 4-byte aligned, bf16 pointers 2-byte aligned,
+ *     fp64 pointers 8-byte aligned.  Any alignment beyond that only selects
+ *     a faster code path (16-byte aligned buffers use 128-bit accesses).
+ *   - bf16 values are passed as their 16-bit patterns (uint16_t).
+ */
+#ifndef ZSHARD_H
+#define ZSHARD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+enum { ZS_F32 = 0, ZS_BF16 = 1 };
+
+/* return codes */
+enum {
+    ZS_OK = 0,
+    ZS_EINVAL = -1,     /* bad argument: null pointer with work to do, range,
+                           dtype, misalignment, size mismatch */
+    ZS_EOVERLAP = -2,   /* two buffers that must be disjoint overlap */
+    ZS_EWORKSPACE = -3, /* workspace smaller than grad_norm_sq_workspace_bytes */
+    ZS_EHIP = -4        /* a HIP launch failed; see zs_last_hip_error() */
+};
+
+/* One rank's range of the flat buffer. */
+typedef struct {
+    int64_t chunk;        /* ceil(total / world) */
+    int64_t start;        /* min(rank * chunk, total) */
+    int64_t end;          /* min(start + chunk, total) */
+    int64_t padded_total; /* world * chunk */
+} zs_shard;
+
+/* A contiguous device tensor, seen as 1-D in row-major order. */
+typedef struct {
+    void* ptr;            /* device pointer; may be NULL only when numel == 0 */
+    int64_t numel;
+} zs_tensor;
+
+/* AdamW hyperparameters and step state, all host values.  Every scalar the
+ * kernel uses is formed from these in binary64 and rounded to binary32 once. */
+typedef struct {
+    double lr;            /* >= 0 */
+    double beta1, beta2;  /* in [0, 1) */
+    double eps;           /* > 0, added after the bias-corrected sqrt */
+    double weight_decay;  /* >= 0; decoupled (master *= 1 - lr*wd); 0 = Adam */
+    double grad_scale;    /* > 0; the stored gradient is multiplied by it:
+                             1/(accumulation_steps * world_size) */
+    double max_norm;      /* > 0: clip to this global L2 norm; <= 0: no clip */
+    double extra_norm_sq; /* >= 0 or non-finite: the other ranks' sum of
+                             squares of their scaled gradients (the result of
+                             the scalar all-reduce); 0 for a single rank */
+    int64_t step;         /* t >= 1, caller-owned, incremented before the call */
+} zs_adamw;
+
+/*
+ * zero_shard_range — the range of the flat buffer that `rank` owns.
+ * [ZeRO page] §"ZeRO-1: 切分 Optimizer States", ZeRO1Optimizer.__init__
+ * (chunk is the ceiling of total/world, start = rank*chunk, end clipped to
+ * total) and §"ZeRO-2" reduce_gradients (same chunk).  padded_total is the
+ * length the equal-size all-gather / reduce-scatter of those sections need.
+ * A rank that starts past the end gets the empty range [total, total).
+ * Host only (no GPU needed).  out: caller-owned host struct.
+ * Errors: ZS_EINVAL for out == NULL, world < 1, rank outside [0, world),
+ * total < 0, or world*chunk overflowing int64.
+ */
+int32_t zero_shard_range(int64_t total, int32_t world, int32_t rank, zs_shard* out);
+
+/*
+ * flat_pack — the FlatParameter flatten.
+ * [ZeRO page] §ZeRO-1 _flatten_gradients (each tensor viewed 1-D, in
+ * parameter order, concatenated; .float() widening) and [Memory page]
+ * §"FSDP 的关键抽象：FlatParameter" (one 1-D buffer per wrap unit).
+ * flat[o_i + j] = src[i][j], o_i = sum of the numels before i; the tail
+ * [sum(numel), padded_total) is set to zero (the padding to a multiple of
+ * the world size).
+ * src: host array of `count` device tensors of dtype src_dtype (read).
+ * flat: device buffer of padded_total elements of flat_dtype (written).
+ * dtype pairs: (F32,F32), (BF16,BF16) bit copies; (BF16,F32) exact widening.
+ * Errors: ZS_EINVAL (count < 0, negative numel, sum(numel) > padded_total,
+ * dtype pair, null/misaligned pointer), ZS_EOVERLAP (a source overlaps
+ * flat), ZS_EHIP.
+ */
+int32_t flat_pack(const zs_tensor* src, int32_t count, int32_t src_dtype,
+                  void* flat, int32_t flat_dtype, int64_t padded_total, void* hip_stream);
+
+/*
+ * flat_unpack — the inverse of flat_pack, padding dropped.
+ * [ZeRO page] §ZeRO-1 _apply_update (an offset walks the parameters, each
+ * taking its next numel elements of the flat buffer).
+ * dst[i][j] = flat[o_i + j].  flat: device, read; dst: host array of
+ * `count` device tensors, written; they must not overlap flat or each other.
+ * dtype pairs: (F32,F32), (BF16,BF16) bit copies; (F32,BF16) the bf16
+ * round-to-nearest-even re-cast (NaN -> 0x7FC0).
+ * Errors: as flat_pack.
+ */
+int32_t flat_unpack(const void* flat, int32_t flat_dtype,
+                    const zs_tensor* dst, int32_t count, int32_t dst_dtype, void* hip_stream);
+
+/*
+ * grad_accum — fp32 gradient accumulation over micro-batches.
+ * [ZeRO page] §"梯度累积——用计算换通信" GradientAccumulator.backward
+ * (an fp32 buffer adds each micro-batch's grad.float()) and [Memory page]
+ * §FlatParameter (reduce_dtype fp32: the reduction is a sum).
+ * overwrite != 0 (first micro-batch): acc[i] = widen(grad[i]) (a copy);
+ * overwrite == 0: acc[i] = fl32(acc[i] + widen(grad[i])).
+ * acc: device fp32[n], read-write; grad: device [n] of grad_dtype, read.
+ * Errors: ZS_EINVAL, ZS_EOVERLAP (acc overlaps grad), ZS_EHIP.
+ */
+int32_t grad_accum(float* acc, const void* grad, int32_t grad_dtype, int64_t n,
+                   int32_t overwrite, void* hip_stream);
+
+/*
+ * grad_norm_sq_workspace_bytes — bytes of device workspace grad_norm_sq
+ * needs for n elements (0 for n == 0; -1 for n < 0).  Host only.
+ */
+int64_t grad_norm_sq_workspace_bytes(int64_t n);
+
+/*
+ * grad_norm_sq — this shard's share of the squared global gradient norm.
+ * [ZeRO page] §ZeRO-1 step / §ZeRO-2 reduce_gradients (the summed gradient
+ * is divided by the world size), §"组合策略" recipe (the loss is divided by
+ * the accumulation steps; clip_grad_norm_(max_norm=1.0) over all
+ * parameters) and [Accum page] §"梯度累积：用时间换显存" (the same clip
+ * after the micro-batches).
+ * *out_sq_dev = sum_i (double)g1_i^2 with g1_i = fl32(grad[i] *
+ * (float)grad_scale); squares exact in binary64, summed in binary64 in a
+ * fixed order (the result depends only on n and the data, run to run).
+ * grad: device fp32[n], read.  out_sq_dev: device double, written (0 when
+ * n == 0).  workspace: device, >= grad_norm_sq_workspace_bytes(n) bytes,
+ * 8-byte aligned, scratch owned by the caller, may be reused after the
+ * stream reaches the end of this call.
+ * Errors: ZS_EINVAL, ZS_EWORKSPACE, ZS_EOVERLAP, ZS_EHIP.
+ */
+int32_t grad_norm_sq(const float* grad, int64_t n, double grad_scale, double* out_sq_dev,
+                     void* workspace, int64_t workspace_bytes, void* hip_stream);
+
+/*
+ * adamw_step — the fused AdamW update of one rank's shard.
+ * [ZeRO page] §ZeRO-1 step, §ZeRO-2 step, §ZeRO-3 step: step counter
+ * incremented before use; bias_correction1 = 1 - beta1^t,
+ * bias_correction2 = 1 - beta2^t; exp_avg = beta1*exp_avg + (1-beta1)*g;
+ * exp_avg_sq = beta2*exp_avg_sq + (1-beta2)*g*g; denom = sqrt(exp_avg_sq) /
+ * sqrt(bias_correction2) + eps; update = -(lr/bias_correction1) * exp_avg /
+ * denom.  [Memory page] §"一、显存账本": bf16 params with AdamW and an
+ * element-wise, independent update per parameter; decoupled decay is this
+ * library's reading (master *= 1 - lr*wd before the update).  The fp32
+ * master is updated and param_bf16 (if not NULL) receives its bf16
+ * round-to-nearest-even re-cast ([Memory page] FSDP MixedPrecision
+ * param_dtype=bf16; [ZeRO page] §"组合策略" FP32 master weights).
+ * Per element, one IEEE binary32 rounding per operation, no fusion:
+ *   g = fl(fl(grad*scale)*coef); m = fl(fl(b1*m) + fl((1-b1)*g));
+ *   v = fl(fl(b2*v) + fl((1-b2)*fl(g*g))); den = fl(fl(sqrt(v)/sqrt(bc2)) + eps);
+ *   master = fl(fl(master*(1-lr*wd)) - fl(fl(m/den)*(lr/bc1)))
+ * norm_sq_dev: NULL -> coef = 1, no check.  Otherwise a device double
+ * holding this shard's squared norm (grad_norm_sq); S = *norm_sq_dev +
+ * extra_norm_sq; a non-finite S leaves every buffer unchanged (the recipe
+ * skips the update on a non-finite grad norm); else, when max_norm > 0,
+ * coef = (float)min(1, max_norm / (sqrt(S) + 1e-6)), all in binary64 on the
+ * device ([ZeRO page] §"组合策略" clip_grad_norm_).
+ * master, exp_avg, exp_avg_sq: device fp32[n], read-write; grad: device
+ * fp32[n], read; param_bf16: device bf16[n] or NULL, written.  No two of
+ * them may overlap, nor overlap *norm_sq_dev.
+ * Errors: ZS_EINVAL (hp NULL or out of range, pointers), ZS_EOVERLAP, ZS_EHIP.
+ */
+int32_t adamw_step(const zs_adamw* hp, float* master, float* exp_avg, float* exp_avg_sq,
+                   const float* grad, uint16_t* param_bf16, int64_t n,
+                   const double* norm_sq_dev, void* hip_stream);
+
+/* Static description of a return code. */
+const char* zs_strerror(int32_t code);
+
+/* The hipError_t of the last ZS_EHIP on this thread (0 if none). */
+int32_t zs_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZSHARD_H */

@@ -1,0 +1,175 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol,
+and its argument checks return the documented codes before any launch.
+
+No test here reaches a kernel launch (there is no GPU in this container):
+every call either is host-only (zero_shard_range, the workspace size) or
+fails validation, or is an n == 0 no-op that returns before launching.
+Pointers passed to failing calls are never dereferenced.
+"""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import oracle
+import fsdp_sharded_optimizer_amd as zs
+from fsdp_sharded_optimizer_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zshard.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTS), names
+    L = zs.lib()
+    for name in names:
+        assert getattr(L, name) is not None
+
+
+def test_shard_range_matches_oracle_brute_force(orc):
+    for T in list(range(0, 130)) + [1_000_003, 6_738_415_616, 13_015_864_320, 855_654_400, 70_000_000_000]:
+        for N in (1, 2, 3, 7, 8, 13, 64, 129):
+            for r in sorted({0, 1, N // 2, N - 1} & set(range(N))):
+                assert zs.zero_shard_range(T, N, r) == oracle.shard_range(T, N, r), (T, N, r)
+
+
+def test_shard_range_golden():
+    with open(os.path.join(ROOT, "tests", "golden", "shard_ranges.json")) as f:
+        for c in json.load(f)["cases"]:
+            got = zs.zero_shard_range(c["total"], c["world"], c["rank"])
+            assert got == (c["chunk"], c["start"], c["end"], c["padded_total"]), c["name"]
+
+
+def test_shard_range_errors():
+    L = zs.lib()
+    out = B.Shard()
+    for args in [(10, 0, 0), (10, 4, 4), (10, 4, -1), (-1, 4, 0)]:
+        assert L.zero_shard_range(*args, ctypes.byref(out)) == B.ZS_EINVAL
+    assert L.zero_shard_range(10, 4, 0, None) == B.ZS_EINVAL
+    # world*chunk would overflow int64
+    assert L.zero_shard_range(2**63 - 1, 3, 0, ctypes.byref(out)) == B.ZS_EINVAL
+    with pytest.raises(zs.ZShardError):
+        zs.zero_shard_range(10, 0, 0)
+
+
+def test_workspace_bytes():
+    assert zs.grad_norm_sq_workspace_bytes(0) == 0
+    assert zs.grad_norm_sq_workspace_bytes(-1) == -1
+    assert zs.grad_norm_sq_workspace_bytes(1) == 8
+    # capped number of partials for large n
+    assert zs.grad_norm_sq_workspace_bytes(10**10) == zs.grad_norm_sq_workspace_bytes(10**9)
+
+
+FAKE = 0x7F0000000000   # never dereferenced: every call below fails validation
+
+
+def _hp(**kw):
+    base = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, grad_scale=1.0,
+                max_norm=0.0, extra_norm_sq=0.0, step=1)
+    base.update(kw)
+    return B.AdamW(**base)
+
+
+def _adamw(hp, master=FAKE, m=FAKE + 2**20, v=FAKE + 2**21, g=FAKE + 2**22, b=0, n=1024, norm=0):
+    return zs.lib().adamw_step(ctypes.byref(hp) if hp is not None else None, master, m, v, g, b, n,
+                               norm, None)
+
+
+def test_adamw_rejects_hyperparameters():
+    for bad in (dict(step=0), dict(beta1=1.0), dict(beta1=-0.5), dict(beta2=1.0), dict(eps=0.0),
+                dict(eps=float("nan")), dict(lr=-1e-3), dict(weight_decay=-0.1), dict(grad_scale=0.0),
+                dict(grad_scale=float("inf")), dict(max_norm=float("nan")), dict(extra_norm_sq=-1.0)):
+        assert _adamw(_hp(**bad)) == B.ZS_EINVAL, bad
+    assert _adamw(None) == B.ZS_EINVAL
+
+
+def test_adamw_rejects_pointers():
+    assert _adamw(_hp(), master=0) == B.ZS_EINVAL
+    assert _adamw(_hp(), g=0) == B.ZS_EINVAL
+    assert _adamw(_hp(), master=FAKE + 2) == B.ZS_EINVAL          # fp32 must be 4-byte aligned
+    assert _adamw(_hp(), b=FAKE + 2**23 + 1) == B.ZS_EINVAL       # bf16 must be 2-byte aligned
+    assert _adamw(_hp(), norm=FAKE + 2**24 + 4) == B.ZS_EINVAL    # fp64 must be 8-byte aligned
+    assert _adamw(_hp(), n=-1) == B.ZS_EINVAL
+    # overlaps: exp_avg inside master, bf16 over grad, norm inside exp_avg_sq
+    assert _adamw(_hp(), m=FAKE + 4) == B.ZS_EOVERLAP
+    assert _adamw(_hp(), b=FAKE + 2**22 + 64) == B.ZS_EOVERLAP
+    assert _adamw(_hp(), norm=FAKE + 2**21 + 8) == B.ZS_EOVERLAP
+    # adjacent, not overlapping buffers pass the overlap check (n = 0 no-op)
+    assert _adamw(_hp(), n=0) == B.ZS_OK
+    assert _adamw(_hp(), master=0, m=0, v=0, g=0, n=0) == B.ZS_OK
+
+
+def test_grad_accum_rejects():
+    L = zs.lib()
+    assert L.grad_accum(FAKE, FAKE + 2**20, 7, 16, 0, None) == B.ZS_EINVAL       # dtype
+    assert L.grad_accum(0, FAKE, B.ZS_BF16, 16, 0, None) == B.ZS_EINVAL
+    assert L.grad_accum(FAKE + 1, FAKE + 2**20, B.ZS_F32, 16, 0, None) == B.ZS_EINVAL
+    assert L.grad_accum(FAKE, FAKE + 2**20 + 1, B.ZS_BF16, 16, 0, None) == B.ZS_EINVAL
+    assert L.grad_accum(FAKE, FAKE + 32, B.ZS_BF16, 16, 0, None) == B.ZS_EOVERLAP
+    assert L.grad_accum(FAKE, FAKE, B.ZS_F32, -1, 0, None) == B.ZS_EINVAL
+    assert L.grad_accum(0, 0, B.ZS_F32, 0, 1, None) == B.ZS_OK                    # n = 0 no-op
+
+
+def test_grad_norm_sq_rejects():
+    L = zs.lib()
+    n = 1 << 20
+    need = zs.grad_norm_sq_workspace_bytes(n)
+    ws, out = FAKE + 2**30, FAKE + 2**31
+    assert L.grad_norm_sq(FAKE, n, 1.0, out, ws, need - 8, None) == B.ZS_EWORKSPACE
+    assert L.grad_norm_sq(FAKE, n, 1.0, 0, ws, need, None) == B.ZS_EINVAL
+    assert L.grad_norm_sq(FAKE, n, 1.0, out + 4, ws, need, None) == B.ZS_EINVAL
+    assert L.grad_norm_sq(FAKE, n, 0.0, out, ws, need, None) == B.ZS_EINVAL
+    assert L.grad_norm_sq(0, n, 1.0, out, ws, need, None) == B.ZS_EINVAL
+    assert L.grad_norm_sq(FAKE, n, 1.0, out, 0, need, None) == B.ZS_EINVAL
+    assert L.grad_norm_sq(FAKE, n, 1.0, FAKE + 8, ws, need, None) == B.ZS_EOVERLAP
+    assert L.grad_norm_sq(FAKE, n, 1.0, out, FAKE + 64, need, None) == B.ZS_EOVERLAP
+
+
+def _tensors(*pairs):
+    arr = (B.Tensor * len(pairs))()
+    for i, (p, k) in enumerate(pairs):
+        arr[i].ptr, arr[i].numel = p, k
+    return arr
+
+
+def test_flat_rejects():
+    L = zs.lib()
+    flat = FAKE + 2**30
+    two = _tensors((FAKE, 10), (FAKE + 2**20, 6))
+    assert L.flat_pack(two, 2, B.ZS_F32, flat, B.ZS_F32, 15, None) == B.ZS_EINVAL      # padded < total
+    assert L.flat_pack(two, 2, B.ZS_F32, flat, B.ZS_BF16, 16, None) == B.ZS_EINVAL     # narrowing pack
+    assert L.flat_unpack(flat, B.ZS_BF16, two, 2, B.ZS_F32, None) == B.ZS_EINVAL       # widening unpack
+    assert L.flat_pack(two, -1, B.ZS_F32, flat, B.ZS_F32, 16, None) == B.ZS_EINVAL
+    assert L.flat_pack(_tensors((0, 4)), 1, B.ZS_F32, flat, B.ZS_F32, 4, None) == B.ZS_EINVAL
+    assert L.flat_pack(_tensors((FAKE + 2, 4)), 1, B.ZS_F32, flat, B.ZS_F32, 4, None) == B.ZS_EINVAL
+    assert L.flat_pack(_tensors((FAKE, -4)), 1, B.ZS_F32, flat, B.ZS_F32, 4, None) == B.ZS_EINVAL
+    assert L.flat_pack(two, 2, B.ZS_F32, 0, B.ZS_F32, 16, None) == B.ZS_EINVAL
+    assert L.flat_pack(_tensors((flat + 8, 4)), 1, B.ZS_F32, flat, B.ZS_F32, 8, None) == B.ZS_EOVERLAP
+    # unpack destinations must not overlap each other
+    assert L.flat_unpack(flat, B.ZS_F32, _tensors((FAKE, 8), (FAKE + 16, 8)), 2, B.ZS_F32,
+                         None) == B.ZS_EOVERLAP
+    # nothing to do
+    assert L.flat_pack(None, 0, B.ZS_F32, 0, B.ZS_F32, 0, None) == B.ZS_OK
+    assert L.flat_unpack(flat, B.ZS_F32, _tensors((0, 0)), 1, B.ZS_F32, None) == B.ZS_OK
+
+
+def test_strerror():
+    L = zs.lib()
+    for code in (B.ZS_OK, B.ZS_EINVAL, B.ZS_EOVERLAP, B.ZS_EWORKSPACE, B.ZS_EHIP, 12345):
+        assert isinstance(L.zs_strerror(code), bytes)
+    assert L.zs_last_hip_error() == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        zs.grad_accum(torch.zeros(4), torch.zeros(4), overwrite=True)

@@ -1,0 +1,307 @@
+"""GPU parity of each library entry point against the oracle (small sizes).
+
+Sizes span several workgroup tiles and ragged tails; every case runs
+aligned (128-bit path) and as a misaligned view (scalar path).  Inputs are
+seeded and drawn on the CPU, then copied to the GPU, so both sides consume
+the same bits.  Every buffer carries a canary tail that must stay untouched.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import fsdp_sharded_optimizer_amd as zs
+from tests.parity import (NORM_TOL, StateCheck, bf16_ulps, bits_equal, from_np, identical_fraction,
+                          to_np)
+
+pytestmark = pytest.mark.gpu
+
+SIZES = [1, 7, 8, 9, 255, 2047, 2048, 2049, 8191, 100_003]
+CANARY = 64
+
+
+def dev_buf(a: np.ndarray, offset: int, bf16: bool = False):
+    """Device copy of `a` placed `offset` elements into a larger buffer with
+    a canary tail; returns (view, whole buffer)."""
+    n = a.size
+    fill = np.full(offset + n + CANARY, 0x7FBF if bf16 else 0, dtype=a.dtype)
+    if not bf16:
+        fill = fill.view(np.uint32)
+        fill[:] = 0x7FBADBAD
+        fill = fill.view(np.float32)
+    fill[offset:offset + n] = a
+    whole = from_np(fill, bf16=bf16)
+    return whole[offset:offset + n], whole
+
+
+def canary_ok(whole: torch.Tensor, offset: int, n: int) -> bool:
+    w = to_np(whole)
+    if w.dtype == np.uint16:
+        return bool(np.all(w[offset + n:] == 0x7FBF) and np.all(w[:offset] == 0x7FBF))
+    return bool(np.all(w.view(np.uint32)[offset + n:] == 0x7FBADBAD) and
+                np.all(w.view(np.uint32)[:offset] == 0x7FBADBAD))
+
+
+def rng_for(*key):
+    return np.random.default_rng(abs(hash(key)) % (2**32))
+
+
+# ---------------------------------------------------------------------------
+# grad_accum: bit-exact
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n", SIZES)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("offset", [0, 3])
+def test_grad_accum_bit_exact(n, dtype, offset):
+    print(f"grad_accum n={n} dtype={dtype} offset={offset}", flush=True)
+    rng = np.random.default_rng(n * 31 + offset)
+    M = 4
+    mbs32 = [(rng.standard_normal(n) * 1e-3).astype(np.float32) for _ in range(M)]
+    mbs = [oracle.bf16_rne(x) for x in mbs32] if dtype == "bf16" else mbs32
+    code = oracle.BF16 if dtype == "bf16" else oracle.F32
+    ref = np.empty(n, np.float32)
+    acc, acc_whole = dev_buf(np.zeros(n, np.float32), offset)
+    for k, g in enumerate(mbs):
+        oracle.grad_accum(ref, g, code, overwrite=(k == 0))
+        gd, g_whole = dev_buf(g, offset + 1 if offset else 0, bf16=(dtype == "bf16"))
+        zs.grad_accum(acc, gd, overwrite=(k == 0))
+        torch.cuda.synchronize()
+        assert canary_ok(g_whole, offset + 1 if offset else 0, n)
+        assert bits_equal(to_np(acc), ref), (k, identical_fraction(to_np(acc), ref))
+    assert canary_ok(acc_whole, offset, n)
+
+
+# ---------------------------------------------------------------------------
+# grad_norm_sq
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n", SIZES + [3_000_001])
+@pytest.mark.parametrize("offset", [0, 1])
+def test_grad_norm_sq(n, offset):
+    print(f"grad_norm_sq n={n} offset={offset}", flush=True)
+    rng = np.random.default_rng(n + 17 * offset)
+    acc = (rng.standard_normal(n) * 1e-2).astype(np.float32)
+    scale = 1.0 / 32
+    want = oracle.grad_norm_sq(acc, scale)
+    g, whole = dev_buf(acc, offset)
+    out = torch.full((1,), float("nan"), dtype=torch.float64, device="cuda")
+    zs.grad_norm_sq(g, scale, out)
+    got = float(out.item())
+    assert abs(math.sqrt(got) - math.sqrt(want)) <= NORM_TOL * math.sqrt(want)
+    # a fixed association: the same bits run to run, and from the other alignment path
+    out2 = torch.full((1,), float("nan"), dtype=torch.float64, device="cuda")
+    zs.grad_norm_sq(g, scale, out2)
+    g2, _ = dev_buf(acc, 0 if offset else 1)
+    out3 = torch.full((1,), float("nan"), dtype=torch.float64, device="cuda")
+    zs.grad_norm_sq(g2, scale, out3)
+    assert out2.item() == got and out3.item() == got
+    assert canary_ok(whole, offset, n)
+
+
+def test_grad_norm_sq_empty_and_closed_form():
+    out = torch.full((1,), float("nan"), dtype=torch.float64, device="cuda")
+    zs.grad_norm_sq(torch.empty(0, dtype=torch.float32, device="cuda"), 1.0, out)
+    assert out.item() == 0.0
+    # 2^20 + 3 elements of 2^-7 at scale 1/8: exactly 1 + 3 * 2^-20
+    g = torch.full(((1 << 20) + 3,), 2.0**-7, dtype=torch.float32, device="cuda")
+    zs.grad_norm_sq(g, 1.0 / 8, out)
+    assert out.item() == 1.0 + 3 * 2.0**-20
+
+
+# ---------------------------------------------------------------------------
+# adamw_step
+# ---------------------------------------------------------------------------
+
+def _hp(step, lr=3e-4, b1=0.9, b2=0.95, eps=1e-8, wd=0.1, scale=1 / 64, max_norm=0.0, extra=0.0):
+    return (zs.AdamWConfig(lr=lr, beta1=b1, beta2=b2, eps=eps, weight_decay=wd, grad_scale=scale,
+                           max_norm=max_norm, extra_norm_sq=extra, step=step),
+            oracle.make_hp(lr, b1, b2, eps, wd, scale, max_norm, extra, step))
+
+
+@pytest.mark.parametrize("n", SIZES)
+@pytest.mark.parametrize("offset", [0, 3])
+@pytest.mark.parametrize("mode", ["adam_f32", "adamw_bf16", "adamw_bf16_clip"])
+def test_adamw_step_parity(n, offset, mode):
+    """Three consecutive steps; each compared with the oracle to the bar,
+    the GPU using its own norm and the oracle its own."""
+    print(f"adamw n={n} offset={offset} mode={mode}", flush=True)
+    rng = np.random.default_rng(n * 7 + offset + len(mode))
+    p0 = rng.uniform(-0.1, 0.1, n).astype(np.float32)
+    wd = 0.0 if mode == "adam_f32" else 0.1
+    bf16 = mode != "adam_f32"
+    clip = mode.endswith("clip")
+    p_ref, m_ref, v_ref = p0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    b_ref = np.zeros(n, np.uint16)
+    p, pw = dev_buf(p0, offset)
+    m, mw = dev_buf(np.zeros(n, np.float32), 0)
+    v, vw = dev_buf(np.zeros(n, np.float32), 0)
+    b, bw = dev_buf(np.zeros(n, np.uint16), offset, bf16=True) if bf16 else (None, None)
+    norm = torch.zeros(1, dtype=torch.float64, device="cuda")
+    for t in range(1, 4):
+        acc = (rng.standard_normal(n) * 3e-3).astype(np.float32)
+        g, gw = dev_buf(acc, offset)
+        S_ref = oracle.grad_norm_sq(acc, 1 / 64)
+        max_norm = 0.5 * math.sqrt(S_ref * 8) if clip else 0.0
+        extra = 7 * S_ref if clip else 0.0          # the other ranks' share
+        hp_gpu, hp_orc = _hp(t, wd=wd, max_norm=max_norm, extra=extra)
+        prev = {"p": p_ref.copy(), "m": m_ref.copy()}
+        oracle.adamw_step(hp_orc, p_ref, m_ref, v_ref, acc, b_ref if bf16 else None,
+                          norm_sq=S_ref if clip else None)
+        if clip:
+            zs.grad_norm_sq(g, 1 / 64, norm)
+        zs.adamw_step(hp_gpu, p, m, v, g, b, norm_sq=norm if clip else None)
+        torch.cuda.synchronize()
+        s = oracle.adamw_scalars(hp_orc)
+        coef = oracle.clip_coef(S_ref, extra, max_norm) if clip else 1.0
+        g2 = (acc * np.float32(1 / 64)) * np.float32(coef)
+        gpu = {"p": to_np(p), "m": to_np(m), "v": to_np(v), "b": to_np(b) if bf16 else None}
+        res = StateCheck(0.9, 3e-4, wd, s.step_size).check(
+            gpu, {"p": p_ref, "m": m_ref, "v": v_ref, "b": b_ref}, prev, g2, f"t={t}")
+        print(f"  t={t} {res}", flush=True)
+        assert canary_ok(gw, offset, n)
+    for whole, off in ((pw, offset), (mw, 0), (vw, 0)) + (((bw, offset),) if bf16 else ()):
+        assert canary_ok(whole, off, n)
+
+
+@pytest.mark.parametrize("n", [2049, 100_003])
+@pytest.mark.parametrize("offset", [0, 1])
+def test_adamw_bit_exact_given_the_oracle_norm(n, offset):
+    """With the oracle's squared norm handed to the kernel, every output is
+    bit-identical to the oracle: the element update is the same sequence of
+    IEEE binary32 operations and the clip coefficient the same binary64 ones."""
+    rng = np.random.default_rng(n + offset)
+    p_ref = rng.uniform(-0.1, 0.1, n).astype(np.float32)
+    m_ref, v_ref, b_ref = np.zeros(n, np.float32), np.zeros(n, np.float32), np.zeros(n, np.uint16)
+    p, _ = dev_buf(p_ref, offset)
+    m, _ = dev_buf(m_ref, offset)
+    v, _ = dev_buf(v_ref, offset)
+    b, _ = dev_buf(b_ref, offset, bf16=True)
+    for t in range(1, 6):
+        acc = (rng.standard_normal(n) * 1e-2).astype(np.float32)
+        S = oracle.grad_norm_sq(acc, 1 / 32)
+        hp_gpu, hp_orc = _hp(t, scale=1 / 32, max_norm=math.sqrt(S) * 0.8 if t % 2 else 0.0,
+                             extra=0.25 * S)
+        oracle.adamw_step(hp_orc, p_ref, m_ref, v_ref, acc, b_ref, norm_sq=S)
+        g, _ = dev_buf(acc, offset)
+        norm = torch.tensor([S], dtype=torch.float64, device="cuda")
+        zs.adamw_step(hp_gpu, p, m, v, g, b, norm_sq=norm)
+        for name, gpu, ref in (("p", p, p_ref), ("m", m, m_ref), ("v", v, v_ref), ("b", b, b_ref)):
+            assert bits_equal(to_np(gpu), ref), (t, name, identical_fraction(to_np(gpu), ref))
+
+
+def test_adamw_skips_on_nonfinite_norm():
+    n = 4099
+    rng = np.random.default_rng(5)
+    p0 = rng.uniform(-0.1, 0.1, n).astype(np.float32)
+    acc = rng.standard_normal(n).astype(np.float32)
+    acc[1234] = np.inf
+    p, m, v = from_np(p0), torch.ones(n, device="cuda"), torch.ones(n, device="cuda")
+    b = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+    g = from_np(acc)
+    norm = torch.zeros(1, dtype=torch.float64, device="cuda")
+    zs.grad_norm_sq(g, 1.0, norm)
+    assert math.isinf(norm.item())
+    hp_gpu, hp_orc = _hp(1, max_norm=1.0)
+    zs.adamw_step(hp_gpu, p, m, v, g, b, norm_sq=norm)
+    assert bits_equal(to_np(p), p0) and torch.all(m == 1) and torch.all(v == 1)
+    assert not torch.any(b.view(torch.int16) != 0)
+    # a finite local norm with a non-finite share from the other ranks
+    good = from_np(np.ones(n, np.float32))
+    zs.grad_norm_sq(good, 1.0, norm)
+    hp_gpu, _ = _hp(1, max_norm=1.0, extra=float("inf"))
+    zs.adamw_step(hp_gpu, p, m, v, good, b, norm_sq=norm)
+    assert bits_equal(to_np(p), p0)
+    # the oracle agrees
+    pr, mr, vr = p0.copy(), np.ones(n, np.float32), np.ones(n, np.float32)
+    assert oracle.adamw_step(hp_orc, pr, mr, vr, acc, norm_sq=float("inf")) == 1
+
+
+def test_adamw_resume_is_bit_identical():
+    """k steps straight vs j steps, a copy of the state through the host, and
+    k - j more: the state is plain buffers plus the caller's step count."""
+    n, k, j = 50_001, 6, 2
+    rng = np.random.default_rng(9)
+    p0 = rng.uniform(-0.1, 0.1, n).astype(np.float32)
+    grads = [from_np((rng.standard_normal(n) * 1e-3).astype(np.float32)) for _ in range(k)]
+
+    def run(state, steps):
+        p, m, v, b = state
+        for t in steps:
+            zs.adamw_step(_hp(t)[0], p, m, v, grads[t - 1], b)
+        return state
+
+    fresh = lambda: [from_np(p0), torch.zeros(n, device="cuda"), torch.zeros(n, device="cuda"),
+                     torch.zeros(n, dtype=torch.bfloat16, device="cuda")]
+    a = run(fresh(), range(1, k + 1))
+    half = run(fresh(), range(1, j + 1))
+    host = [to_np(x) for x in half]
+    reloaded = [from_np(host[0]), from_np(host[1]), from_np(host[2]), from_np(host[3], bf16=True)]
+    b = run(reloaded, range(j + 1, k + 1))
+    for x, y in zip(a, b):
+        assert bits_equal(to_np(x), to_np(y))
+
+
+# ---------------------------------------------------------------------------
+# flat_pack / flat_unpack: bit-exact
+# ---------------------------------------------------------------------------
+
+def _shapes(rng, count, big=False):
+    out = []
+    for _ in range(count):
+        nd = int(rng.integers(1, 3))
+        hi = 300 if big else 40
+        out.append(tuple(int(d) for d in rng.integers(1, hi, size=nd)))
+    return out
+
+
+@pytest.mark.parametrize("kind", ["f32", "bf16", "bf16_to_f32"])
+@pytest.mark.parametrize("count,world,aligned_sizes", [(1, 8, True), (9, 64, True), (5, 3, False),
+                                                       (40, 7, False), (70, 8, True)])
+def test_flat_pack_unpack(kind, count, world, aligned_sizes):
+    print(f"flat kind={kind} count={count} world={world}", flush=True)
+    rng = np.random.default_rng(count * 101 + world)
+    shapes = _shapes(rng, count, big=aligned_sizes)
+    if aligned_sizes:   # numels multiple of 8: the 128-bit path
+        shapes = [tuple(list(s[:-1]) + [s[-1] * 8]) for s in shapes]
+    src_bf16 = kind != "f32"
+    flat_bf16 = kind == "bf16"
+    srcs_np = []
+    for s in shapes:
+        x = rng.uniform(-1, 1, s).astype(np.float32)
+        srcs_np.append(oracle.bf16_rne(x).reshape(s) if src_bf16 else x)
+    T = sum(x.size for x in srcs_np)
+    _, _, _, padded = oracle.shard_range(T, world, 0)
+    scode = oracle.BF16 if src_bf16 else oracle.F32
+    fcode = oracle.BF16 if flat_bf16 else oracle.F32
+    want = oracle.flat_pack(srcs_np, scode, fcode, padded)
+    srcs = [from_np(x, bf16=src_bf16) for x in srcs_np]
+    flat, flat_whole = dev_buf(np.zeros(padded, np.uint16 if flat_bf16 else np.float32), 0, bf16=flat_bf16)
+    # poison the flat buffer so the zero padding must be written
+    flat.fill_(float("nan"))
+    zs.flat_pack(srcs, flat, padded)
+    assert bits_equal(to_np(flat), want)
+    assert canary_ok(flat_whole, 0, padded)
+    # unflatten into fresh tensors of the flat dtype (or re-cast to bf16)
+    dst_bf16 = flat_bf16 or kind == "bf16_to_f32"
+    dsts = [torch.empty(s, dtype=torch.bfloat16 if dst_bf16 else torch.float32, device="cuda")
+            for s in shapes]
+    zs.flat_unpack(flat, dsts)
+    back = oracle.flat_unpack(want, fcode, [x.size for x in srcs_np],
+                              oracle.BF16 if dst_bf16 else oracle.F32)
+    for d, r in zip(dsts, back):
+        assert bits_equal(to_np(d).reshape(-1), r)
+
+
+def test_flat_pack_misaligned_views():
+    """Sources that are views at odd element offsets take the scalar path."""
+    rng = np.random.default_rng(77)
+    base = from_np(oracle.bf16_rne(rng.uniform(-1, 1, 10_000).astype(np.float32)), bf16=True)
+    views = [base[1:2050], base[3000:3001], base[4001:9000]]
+    T = sum(v.numel() for v in views)
+    flat = torch.empty(T + 5, dtype=torch.float32, device="cuda")
+    zs.flat_pack(views, flat, T + 5)
+    want = oracle.flat_pack([to_np(v) for v in views], oracle.BF16, oracle.F32, T + 5)
+    assert bits_equal(to_np(flat), want)
