@@ -140,7 +140,7 @@ def run_gpu(w, steps: int, warmup: int):
 # CPU baseline leg: the oracle as it stands on a bounded sample
 # ---------------------------------------------------------------------------
 
-def run_cpu_baseline(w, target_s: float = 10.0, sample: int = 1 << 24):
+def run_cpu_baseline(w, target_s: float = 10.0, sample: int = 1 << 25):
     import numpy as np
     import torch
     import oracle
@@ -169,7 +169,7 @@ def run_cpu_baseline(w, target_s: float = 10.0, sample: int = 1 << 24):
         oracle.adamw_step(hp, master, m, v, acc, bf, norm_sq=s)
         done += 1
         el = time.perf_counter() - t0
-        if el >= target_s or done >= 20:
+        if el >= target_s or done >= 1000:
             break
     return {"value": n * done / el, "unit": "elements/s", "cores": oracle.num_threads(),
             "kind": "oracle",

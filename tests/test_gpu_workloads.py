@@ -1,0 +1,269 @@
+"""GPU parity of whole per-rank steps on the five workloads.
+
+Each workload runs end to end through the library (accumulate every
+micro-batch, form the norm, clip, AdamW with the bf16 re-cast; pack and
+unpack for the FSDP unit) next to the oracle, step by step.  Inputs are
+drawn on the GPU with seeded generators and copied to the host for the
+oracle, so both sides consume the same bits; no oracle input comes from
+the library's outputs.
+
+Small cases compare every element.  Full-size cases (the real shard
+lengths) compare the squared norm over the whole shard (the oracle
+accumulates the full micro-batches itself) and the optimizer state on a
+sample of elements (the update is element-wise, so the oracle steps the
+sampled elements alone), plus every element of the FSDP unit.
+"""
+import math
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import fsdp_sharded_optimizer_amd as zs
+from tests.parity import NORM_TOL, StateCheck, bits_equal, identical_fraction, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def sample_indices(n: int, k: int = 1 << 20, seed: int = 0) -> torch.Tensor:
+    """First and last 4096 elements, the neighbourhoods of a few workgroup
+    tile edges, and k uniform random indices; sorted, unique."""
+    rng = np.random.default_rng(seed)
+    parts = [np.arange(min(n, 4096)), np.arange(max(0, n - 4096), n),
+             rng.integers(0, n, size=min(k, n))]
+    for edge in (2048, 4096, 8192 * 7, 1 << 20, (n // 2048) * 2048):
+        parts.append(np.arange(max(0, edge - 9), min(n, edge + 9)))
+    idx = np.unique(np.concatenate(parts))
+    return torch.from_numpy(idx.astype(np.int64)).to(DEV)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return to_np(t)
+
+
+def run_shard(w: workloads.Workload, n: int, sampled: bool, full_norm: bool):
+    """Drive the library and the oracle through w.steps steps of one shard."""
+    master = workloads.master_init(w, n, DEV)
+    param = master.to(torch.bfloat16) if w.bf16_param else None
+    exp_avg = torch.zeros(n, dtype=torch.float32, device=DEV)
+    exp_avg_sq = torch.zeros(n, dtype=torch.float32, device=DEV)
+    acc = torch.empty(n, dtype=torch.float32, device=DEV)
+    norm = torch.zeros(1, dtype=torch.float64, device=DEV)
+    ws = torch.empty(max(zs.grad_norm_sq_workspace_bytes(n), 8), dtype=torch.uint8, device=DEV)
+
+    idx = sample_indices(n, seed=w.cfg) if sampled else None
+    pick = (lambda t: t[idx]) if sampled else (lambda t: t)
+    p_ref = host(pick(master))
+    m_ref = np.zeros(p_ref.size, np.float32)
+    v_ref = np.zeros(p_ref.size, np.float32)
+    b_ref = host(pick(param)) if param is not None else None
+    acc_ref = np.empty(p_ref.size, np.float32)
+    acc_full = np.empty(n, np.float32) if full_norm else None
+    code = oracle.BF16 if w.grad_dtype == "bf16" else oracle.F32
+    report = []
+    for t in range(1, w.steps + 1):
+        t0 = time.perf_counter()
+        for mb in range(w.micro_batches):
+            g = workloads.grad_draw(w, n, t, mb, DEV)
+            zs.grad_accum(acc, g, overwrite=(mb == 0))
+            oracle.grad_accum(acc_ref, host(pick(g)), code, overwrite=(mb == 0))
+            if full_norm:
+                oracle.grad_accum(acc_full, host(g), code, overwrite=(mb == 0))
+            del g
+        zs.grad_norm_sq(acc, w.grad_scale, norm, ws)
+        s_gpu = float(norm.item())
+        s_ref = oracle.grad_norm_sq(acc_full if full_norm else acc_ref, w.grad_scale) \
+            if (full_norm or not sampled) else None
+        if s_ref is not None:
+            assert abs(math.sqrt(s_gpu) - math.sqrt(s_ref)) <= NORM_TOL * math.sqrt(s_ref), (t, s_gpu, s_ref)
+        # the accumulated gradient itself is bit-exact
+        assert bits_equal(host(pick(acc)), acc_ref), (t, "acc")
+        extra = workloads.other_ranks_norm_sq(w, t, n)
+        hp = zs.AdamWConfig(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                            weight_decay=w.weight_decay, grad_scale=w.grad_scale, max_norm=w.max_norm,
+                            extra_norm_sq=extra, step=t)
+        zs.adamw_step(hp, master, exp_avg, exp_avg_sq, acc, param, norm_sq=norm)
+        ohp = oracle.make_hp(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, w.grad_scale, w.max_norm,
+                             extra, t)
+        prev = {"p": p_ref.copy(), "m": m_ref.copy()}
+        clip_norm = s_ref if s_ref is not None else None
+        if w.max_norm > 0:
+            assert clip_norm is not None, "a clipped workload needs the oracle's own norm"
+        assert oracle.adamw_step(ohp, p_ref, m_ref, v_ref, acc_ref, b_ref, norm_sq=clip_norm) == 0
+        coef = oracle.clip_coef(clip_norm, extra, w.max_norm) if clip_norm is not None else 1.0
+        g2 = (acc_ref * np.float32(w.grad_scale)) * np.float32(coef)
+        gpu = {"p": host(pick(master)), "m": host(pick(exp_avg)), "v": host(pick(exp_avg_sq)),
+               "b": host(pick(param)) if param is not None else None}
+        s = oracle.adamw_scalars(ohp)
+        res = StateCheck(w.beta1, w.lr, w.weight_decay, s.step_size).check(
+            gpu, {"p": p_ref, "m": m_ref, "v": v_ref, "b": b_ref}, prev, g2, f"{w.name} t={t}")
+        res.update(step=t, coef=coef, norm=math.sqrt(s_gpu + extra), secs=round(time.perf_counter() - t0, 1))
+        log(f"  {w.name} n={n} {res}")
+        report.append(res)
+    return report
+
+
+# ---------------------------------------------------------------------------
+# small sizes: every element
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,n", [("llama7b_shard", 1_000_037), ("llama13b_shard_clip", 600_011),
+                                    ("zero3_70b_shard", 2_000_003)])
+def test_workload_small(name, n):
+    w = workloads.WORKLOADS[name]
+    log(f"workload {name} small n={n}")
+    rep = run_shard(w, n, sampled=False, full_norm=False)
+    if name == "llama13b_shard_clip":
+        clipped = [r["step"] for r in rep if r["coef"] < 1.0]
+        assert clipped == [2, 5, 8], clipped
+    if name == "zero3_70b_shard":
+        assert all(r["coef"] < 1.0 for r in rep)
+
+
+def test_tiny_zero1_rank3_view():
+    """The ZeRO-1 workload: rank 3's shard is a view into the flat fp32
+    parameter and gradient buffers (element offset 375,003: not 16-byte
+    aligned), moments are this rank's own buffers; 5 steps of Adam.
+    Everything outside the shard must stay bit-identical."""
+    w = workloads.WORKLOADS["tiny_zero1"]
+    chunk, start, end, padded = zs.zero_shard_range(w.total, w.world, w.rank)
+    assert (chunk, start, end, padded) == oracle.shard_range(w.total, w.world, w.rank)
+    n = end - start
+    flat_p = torch.zeros(padded, dtype=torch.float32, device=DEV)
+    flat_p[:w.total] = workloads.master_init(w, w.total, DEV)
+    flat_g = torch.zeros(padded, dtype=torch.float32, device=DEV)
+    p_all0 = host(flat_p)
+    p_ref = p_all0[start:end].copy()
+    m = torch.zeros(n, dtype=torch.float32, device=DEV)
+    v = torch.zeros(n, dtype=torch.float32, device=DEV)
+    m_ref, v_ref = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    for t in range(1, w.steps + 1):
+        flat_g[:w.total] = workloads.grad_draw(w, w.total, t, 0, DEV)
+        g_ref = host(flat_g)[start:end]
+        hp = zs.AdamWConfig(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=0.0,
+                            grad_scale=w.grad_scale, step=t)
+        zs.adamw_step(hp, flat_p[start:end], m, v, flat_g[start:end])
+        ohp = oracle.make_hp(w.lr, w.beta1, w.beta2, w.eps, 0.0, w.grad_scale, 0.0, 0.0, t)
+        prev = {"p": p_ref.copy(), "m": m_ref.copy()}
+        oracle.adamw_step(ohp, p_ref, m_ref, v_ref, g_ref)
+        p_all = host(flat_p)
+        res = StateCheck(w.beta1, w.lr, 0.0, 0.0).check(
+            {"p": p_all[start:end], "m": host(m), "v": host(v)}, {"p": p_ref, "m": m_ref, "v": v_ref},
+            prev, g_ref * np.float32(w.grad_scale), f"tiny t={t}")
+        log(f"  tiny_zero1 {res}")
+        assert bits_equal(p_all[:start], p_all0[:start]) and bits_equal(p_all[end:], p_all0[end:])
+    assert not host(flat_p)[w.total:].any()
+
+
+def _unit(w, shapes):
+    """The FSDP unit flow for one rank: pack the unit, widen the rank's
+    range into the fp32 master, accumulate its bf16 gradient, AdamW with the
+    bf16 re-cast written back into the flat buffer, unpack.  Returns the
+    GPU results and the oracle's."""
+    total = sum(workloads.numel_of(s) for s in shapes)
+    chunk, start, end, padded = zs.zero_shard_range(total, w.world, w.rank)
+    assert (chunk, start, end, padded) == oracle.shard_range(total, w.world, w.rank)
+    n = end - start
+    wu = workloads.replace_unit(w, shapes)
+    params = workloads.unit_tensors(wu, DEV)
+    params_ref = [host(p) for p in params]
+    flat = torch.empty(padded, dtype=torch.bfloat16, device=DEV)
+    zs.flat_pack(params, flat, padded)
+    flat_ref = oracle.flat_pack(params_ref, oracle.BF16, oracle.BF16, padded)
+    assert bits_equal(host(flat), flat_ref), "flat_pack"
+    master = torch.empty(n, dtype=torch.float32, device=DEV)
+    zs.flat_pack([flat[start:end]], master, n)
+    master_ref = oracle.flat_pack([flat_ref[start:end]], oracle.BF16, oracle.F32, n)
+    assert bits_equal(host(master), master_ref), "widen"
+    g = workloads.grad_draw(w, n, 1, 0, DEV)
+    acc = torch.empty(n, dtype=torch.float32, device=DEV)
+    zs.grad_accum(acc, g, overwrite=True)
+    acc_ref = np.empty(n, np.float32)
+    oracle.grad_accum(acc_ref, host(g), oracle.BF16, overwrite=True)
+    m = torch.zeros(n, dtype=torch.float32, device=DEV)
+    v = torch.zeros(n, dtype=torch.float32, device=DEV)
+    m_ref, v_ref = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    hp = zs.AdamWConfig(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
+                        grad_scale=w.grad_scale, step=1)
+    zs.adamw_step(hp, master, m, v, acc, flat[start:end])
+    ohp = oracle.make_hp(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, w.grad_scale, 0.0, 0.0, 1)
+    prev = {"p": master_ref.copy(), "m": m_ref.copy()}
+    b_ref = flat_ref[start:end]            # a view: the oracle writes its bf16 into its flat buffer
+    oracle.adamw_step(ohp, master_ref, m_ref, v_ref, acc_ref, b_ref)
+    res = StateCheck(w.beta1, w.lr, w.weight_decay, 0.0).check(
+        {"p": host(master), "m": host(m), "v": host(v), "b": host(flat[start:end])},
+        {"p": master_ref, "m": m_ref, "v": v_ref, "b": b_ref}, prev, acc_ref * np.float32(w.grad_scale),
+        "unit")
+    outs = [torch.empty_like(p) for p in params]
+    zs.flat_unpack(flat, outs)
+    outs_ref = oracle.flat_unpack(flat_ref, oracle.BF16, [p.size for p in params_ref], oracle.BF16)
+    return params_ref, outs, outs_ref, (start, end), res
+
+
+def _check_unit(shapes, params_ref, outs, outs_ref, rng):
+    """Outside the rank's range every element is bit-identical to the input;
+    inside it is the oracle's re-cast (<= 1 bf16 ulp; bit-identical
+    fraction reported)."""
+    start, end = rng
+    off = 0
+    same = 0
+    for s, p0, o, r in zip(shapes, params_ref, outs, outs_ref):
+        o = host(o).reshape(-1)
+        k = o.size
+        lo, hi = max(start - off, 0), min(end - off, k)
+        inside = np.zeros(k, bool)
+        if lo < hi:
+            inside[lo:hi] = True
+        assert np.array_equal(o[~inside], p0.reshape(-1)[~inside]), f"outside the shard changed in {s}"
+        if inside.any():
+            d = np.abs(o[inside].astype(np.int32) - r[inside].astype(np.int32))
+            assert d.max() <= 1
+            same += int((d == 0).sum())
+        off += k
+    return same / max(end - start, 1)
+
+
+def test_fsdp_unit_scaled_block():
+    """The 70B-style block with every dimension divided by 16 (same tensor
+    order, world 64, rank 17), every element compared."""
+    w = workloads.WORKLOADS["fsdp_unit_70b_block"]
+    shapes = workloads.block70b_tensor_shapes(hidden=512, ffn=1792, q_heads=64, kv_heads=8, head_dim=8)
+    params_ref, outs, outs_ref, rng, res = _unit(w, shapes)
+    frac = _check_unit(shapes, params_ref, outs, outs_ref, rng)
+    log(f"  unit (scaled) {res} bf16 identical {frac:.6f}")
+
+
+# ---------------------------------------------------------------------------
+# full sizes (the real shard lengths)
+# ---------------------------------------------------------------------------
+
+def test_full_fsdp_unit_70b_block():
+    w = workloads.WORKLOADS["fsdp_unit_70b_block"]
+    log("full fsdp unit 70b block: 855,654,400 elements, world 64, rank 17")
+    params_ref, outs, outs_ref, rng, res = _unit(w, list(w.unit_shapes))
+    assert rng == (227_283_200, 240_652_800)
+    frac = _check_unit(list(w.unit_shapes), params_ref, outs, outs_ref, rng)
+    log(f"  unit {res} bf16 identical {frac:.6f}")
+
+
+@pytest.mark.parametrize("name,full_norm", [("llama7b_shard", False), ("zero3_70b_shard", True),
+                                            ("llama13b_shard_clip", True)])
+def test_full_shard(name, full_norm):
+    w = workloads.WORKLOADS[name]
+    _, start, end, _ = zs.zero_shard_range(w.total, w.world, w.rank)
+    n = end - start
+    log(f"full {name}: shard of {n} elements, {w.steps} steps x {w.micro_batches} micro-batches")
+    rep = run_shard(w, n, sampled=True, full_norm=full_norm)
+    if name == "llama13b_shard_clip":
+        assert [r["step"] for r in rep if r["coef"] < 1.0] == [2, 5, 8]
+    if name == "zero3_70b_shard":
+        assert all(0.70 < r["coef"] < 0.76 for r in rep), rep
+    torch.cuda.empty_cache()

@@ -222,3 +222,9 @@ def small_variant(w: Workload, total: int) -> Workload:
     """The same workload at a reduced buffer size (for parity at small sizes)."""
     from dataclasses import replace
     return replace(w, total=total)
+
+
+def replace_unit(w: Workload, shapes) -> Workload:
+    """The same workload over a different list of unit tensor shapes."""
+    from dataclasses import replace
+    return replace(w, unit_shapes=tuple(shapes), total=sum(numel_of(s) for _, s in shapes))
