@@ -31,6 +31,34 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0   # MI355X published HBM3E bandwidth
 
+# HBM bytes per adamw_step launch on the Llama-7B shard, from two rocprofv3
+# --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch),
+# each scaled by what the same counter reads for the 4 GiB device copy this
+# script also runs (FETCH_SIZE reads 2,097,193 KiB for it: x2.0; WRITE_SIZE
+# reads 4,194,304 KiB: x1.0).  Valid only for the kernel source it was taken
+# on: the hash covers the kernel file and its header.
+PMC_TRAFFIC = {
+    "adamw_step": {"sources": ("csrc/adamw.hip", "csrc/zs_common.h"),
+                   "sha256_16": "eca8fbe8b4017e7c", "shard_elems": 842301952,
+                   "fetch_kib": 6580537.9, "fetch_scale": 2.0,
+                   "write_kib": 11516056.2, "write_scale": 1.0},
+}
+
+
+def pmc_traffic(kernel: str, n: int):
+    """Measured HBM bytes per launch, or None if the kernel changed since."""
+    import hashlib
+    rec = PMC_TRAFFIC.get(kernel)
+    if rec is None or rec["shard_elems"] != n:
+        return None
+    h = hashlib.sha256()
+    for rel in rec["sources"]:
+        with open(os.path.join(ROOT, "fsdp_sharded_optimizer_amd", rel), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest()[:16] != rec["sha256_16"]:
+        return None
+    return rec["fetch_kib"] * 1024 * rec["fetch_scale"] + rec["write_kib"] * 1024 * rec["write_scale"]
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -233,10 +261,11 @@ def main():
         "kernels_ms": {"grad_accum_all_micro_batches": r["accum_ms"], "grad_norm_sq": r["norm_ms"],
                        "adamw_step": r["adamw_ms"]},
         "bytes_per_elem": bpe,
-        "copy_ceiling_gbps": r["copy_gbps"],
+        "device_copy_gbps": r["copy_gbps"],
         "roofline": {"kernel": "adamw_step", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": None},
+                     "traffic": pmc_traffic("adamw_step", n), "traffic_unit": "bytes/launch",
+                     "algorithmic_bytes": adamw_bytes, "launch_ms": r["adamw_ms"]},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

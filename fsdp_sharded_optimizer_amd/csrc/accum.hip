@@ -3,31 +3,26 @@
 //
 // HBM-bound streaming: bf16 gradients move 6 B/element on the first
 // micro-batch (read 2, write 4) and 10 B/element after it (read 2 + 4,
-// write 4); fp32 gradients move 8 and 12.  Thread k owns elements
-// [8k, 8k+8): one 128-bit bf16 load (or two fp32 loads) and two 128-bit fp32
-// accesses per stream.
+// write 4); fp32 gradients move 8 and 12.
+//
+// Layout: lane-contiguous groups of 4 elements (a 64-bit bf16 or 128-bit
+// fp32 load and a 128-bit fp32 access per lane).  A workgroup covers Q
+// groups per lane, the q-th at offset q*1024 in its tile, with every load
+// of the tile issued before the first store: Q = 2 for the accumulating
+// form and Q = 1 for the overwriting form (the faster shapes on gfx950).
 #include "zs_common.h"
 
 namespace zs {
 namespace {
 
 template <bool BF16>
-__device__ __forceinline__ void load8(const void* grad, int64_t first, float (&g)[8]) {
+__device__ __forceinline__ f32x4 load4(const void* grad, int64_t i) {
     if (BF16) {
-        const u32x4 w = ld_stream(reinterpret_cast<const u32x4*>(
-            static_cast<const uint16_t*>(grad) + first));
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            g[2 * j] = bf16_to_f32(ws[j] & 0xFFFFu);
-            g[2 * j + 1] = bf16_to_f32(ws[j] >> 16);
-        }
-    } else {
-        const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(grad) + first);
-        const f32x4 a = ld_stream(p), b = ld_stream(p + 1);
-        g[0] = a.x; g[1] = a.y; g[2] = a.z; g[3] = a.w;
-        g[4] = b.x; g[5] = b.y; g[6] = b.z; g[7] = b.w;
+        const u32x2 w = ld_stream(reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(grad) + i));
+        return f32x4{bf16_to_f32(w.x & 0xFFFFu), bf16_to_f32(w.x >> 16),
+                     bf16_to_f32(w.y & 0xFFFFu), bf16_to_f32(w.y >> 16)};
     }
+    return ld_stream(reinterpret_cast<const f32x4*>(static_cast<const float*>(grad) + i));
 }
 
 template <bool BF16>
@@ -36,58 +31,64 @@ __device__ __forceinline__ float load1(const void* grad, int64_t i) {
     return static_cast<const float*>(grad)[i];
 }
 
-template <int VEC, bool BF16, bool OVERWRITE>
+template <int Q, bool VEC, bool BF16, bool OVERWRITE>
 __global__ __launch_bounds__(kBlock) void accum_kernel(float* __restrict__ acc,
                                                        const void* __restrict__ grad, int64_t n) {
-    const int64_t first = ((int64_t)blockIdx.x * kBlock + threadIdx.x) * VEC;
-    if (first >= n) return;
-    if (VEC == 8 && first + 8 <= n) {
-        float g[8];
-        f32x4* a4 = reinterpret_cast<f32x4*>(acc + first);
-        f32x4 a0, a1;
-        if (!OVERWRITE) { a0 = ld_stream(a4); a1 = ld_stream(a4 + 1); }
-        load8<BF16>(grad, first, g);
-        if (OVERWRITE) {
-            a0 = f32x4{g[0], g[1], g[2], g[3]};
-            a1 = f32x4{g[4], g[5], g[6], g[7]};
-        } else {
-            a0 = f32x4{a0.x + g[0], a0.y + g[1], a0.z + g[2], a0.w + g[3]};
-            a1 = f32x4{a1.x + g[4], a1.y + g[5], a1.z + g[6], a1.w + g[7]};
+    constexpr int64_t kGroup = kBlock * 4;
+    const int64_t tile = (int64_t)blockIdx.x * kGroup * Q;
+    const int64_t lane0 = tile + threadIdx.x * 4;
+    if (VEC && tile + kGroup * Q <= n) {   // whole tile in range
+        f32x4 g[Q], a[Q];
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            g[q] = load4<BF16>(grad, lane0 + q * kGroup);
+            if (!OVERWRITE) a[q] = ld_stream(reinterpret_cast<const f32x4*>(acc + lane0 + q * kGroup));
         }
-        st_stream(a4, a0);
-        st_stream(a4 + 1, a1);
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const f32x4 r = OVERWRITE ? g[q]
+                                      : f32x4{a[q].x + g[q].x, a[q].y + g[q].y, a[q].z + g[q].z,
+                                              a[q].w + g[q].w};
+            st_stream(reinterpret_cast<f32x4*>(acc + lane0 + q * kGroup), r);
+        }
         return;
     }
-    const int64_t last = first + VEC < n ? first + VEC : n;
-    for (int64_t i = first; i < last; ++i) {
-        const float g = load1<BF16>(grad, i);
-        acc[i] = OVERWRITE ? g : acc[i] + g;
+    // ragged tile (or a misaligned buffer): element by element
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const int64_t first = lane0 + q * kGroup;
+        const int64_t last = first + 4 < n ? first + 4 : n;
+        for (int64_t i = first; i < last; ++i) {
+            const float g = load1<BF16>(grad, i);
+            acc[i] = OVERWRITE ? g : acc[i] + g;
+        }
     }
 }
 
-template <int VEC, bool BF16, bool OVERWRITE>
+template <int Q, bool VEC, bool BF16, bool OVERWRITE>
 hipError_t launch(float* acc, const void* grad, int64_t n, hipStream_t stream) {
-    const int64_t threads = (n + VEC - 1) / VEC;
-    const int64_t blocks = (threads + kBlock - 1) / kBlock;
-    hipLaunchKernelGGL((accum_kernel<VEC, BF16, OVERWRITE>), dim3((unsigned)blocks), dim3(kBlock), 0,
+    const int64_t per_block = (int64_t)kBlock * 4 * Q;
+    const int64_t blocks = (n + per_block - 1) / per_block;
+    hipLaunchKernelGGL((accum_kernel<Q, VEC, BF16, OVERWRITE>), dim3((unsigned)blocks), dim3(kBlock), 0,
                        stream, acc, grad, n);
     return hipGetLastError();
+}
+
+template <bool VEC>
+hipError_t dispatch(float* acc, const void* grad, int grad_bf16, int64_t n, int overwrite,
+                    hipStream_t stream) {
+    if (grad_bf16) return overwrite ? launch<1, VEC, true, true>(acc, grad, n, stream)
+                                    : launch<2, VEC, true, false>(acc, grad, n, stream);
+    return overwrite ? launch<1, VEC, false, true>(acc, grad, n, stream)
+                     : launch<2, VEC, false, false>(acc, grad, n, stream);
 }
 
 }  // namespace
 
 hipError_t launch_grad_accum(float* acc, const void* grad, int grad_bf16, int64_t n, int overwrite,
                              bool vec_ok, hipStream_t stream) {
-    if (vec_ok) {
-        if (grad_bf16) return overwrite ? launch<8, true, true>(acc, grad, n, stream)
-                                        : launch<8, true, false>(acc, grad, n, stream);
-        return overwrite ? launch<8, false, true>(acc, grad, n, stream)
-                         : launch<8, false, false>(acc, grad, n, stream);
-    }
-    if (grad_bf16) return overwrite ? launch<1, true, true>(acc, grad, n, stream)
-                                    : launch<1, true, false>(acc, grad, n, stream);
-    return overwrite ? launch<1, false, true>(acc, grad, n, stream)
-                     : launch<1, false, false>(acc, grad, n, stream);
+    return vec_ok ? dispatch<true>(acc, grad, grad_bf16, n, overwrite, stream)
+                  : dispatch<false>(acc, grad, grad_bf16, n, overwrite, stream);
 }
 
 }  // namespace zs

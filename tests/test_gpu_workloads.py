@@ -118,7 +118,13 @@ def run_shard(w: workloads.Workload, n: int, sampled: bool, full_norm: bool):
 @pytest.mark.parametrize("name,n", [("llama7b_shard", 1_000_037), ("llama13b_shard_clip", 600_011),
                                     ("zero3_70b_shard", 2_000_003)])
 def test_workload_small(name, n):
+    """Every element, at a reduced shard length.  The gradient std is scaled
+    by sqrt(full/n) so the global norm, and with it the clipping pattern of
+    the 13B workload, is the one of the full shard."""
+    from dataclasses import replace
     w = workloads.WORKLOADS[name]
+    _, start, end, _ = zs.zero_shard_range(w.total, w.world, w.rank)
+    w = replace(w, grad_std=w.grad_std * math.sqrt((end - start) / n))
     log(f"workload {name} small n={n}")
     rep = run_shard(w, n, sampled=False, full_norm=False)
     if name == "llama13b_shard_clip":
@@ -168,7 +174,7 @@ def _unit(w, shapes):
     range into the fp32 master, accumulate its bf16 gradient, AdamW with the
     bf16 re-cast written back into the flat buffer, unpack.  Returns the
     GPU results and the oracle's."""
-    total = sum(workloads.numel_of(s) for s in shapes)
+    total = sum(workloads.numel_of(s) for _, s in shapes)
     chunk, start, end, padded = zs.zero_shard_range(total, w.world, w.rank)
     assert (chunk, start, end, padded) == oracle.shard_range(total, w.world, w.rank)
     n = end - start
