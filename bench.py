@@ -5,9 +5,11 @@
 
 One step is one pass of the whole hot path over one batch of synthetic
 input, on one rank's real-size shard (inputs resident in HBM):
-  grad_accum over every micro-batch (bf16 -> fp32), grad_norm_sq (the norm
-  is formed every step: it feeds the clip when the workload clips and the
-  non-finite skip always), and the fused adamw_step with the bf16 re-cast.
+  grad_accum over every micro-batch but the last (bf16 -> fp32),
+  grad_accum_norm_sq for the last one (the accumulation and this shard's
+  squared norm in one pass; the norm is formed every step: it feeds the clip
+  when the workload clips and the non-finite skip always), and the fused
+  adamw_step with the bf16 re-cast.
 The shard range is host arithmetic done once at set-up.  Default workload:
 the Llama-7B-shaped buffer over 8 ranks, one 842,301,952-element shard,
 8 micro-batches.
@@ -39,9 +41,9 @@ HBM_PEAK_GBPS = 8000.0   # MI355X published HBM3E bandwidth
 # on: the hash covers the kernel file and its header.
 PMC_TRAFFIC = {
     "adamw_step": {"sources": ("csrc/adamw.hip", "csrc/zs_common.h"),
-                   "sha256_16": "eca8fbe8b4017e7c", "shard_elems": 842301952,
+                   "sha256_16": "2381c1755ddcaf2a", "shard_elems": 842301952,
                    "fetch_kib": 6580537.9, "fetch_scale": 2.0,
-                   "write_kib": 11516056.2, "write_scale": 1.0},
+                   "write_kib": 11515934.5, "write_scale": 1.0},
 }
 
 
@@ -70,9 +72,11 @@ def step_bytes_per_elem(w) -> dict:
     accum_first = g + 4
     accum_next = g + 8
     adamw = 28 + (2 if w.bf16_param else 0)
+    # the last micro-batch also forms the norm, without another read
+    accum = accum_first + (w.micro_batches - 1) * accum_next
+    last = accum_first if w.micro_batches == 1 else accum_next
     return {"grad_accum_first": accum_first, "grad_accum_next": accum_next,
-            "grad_norm_sq": 4, "adamw_step": adamw,
-            "step": accum_first + (w.micro_batches - 1) * accum_next + 4 + adamw}
+            "grad_accum_norm_sq_last": last, "adamw_step": adamw, "step": accum + adamw}
 
 
 def shard_len(w) -> int:
@@ -101,22 +105,23 @@ def run_gpu(w, steps: int, warmup: int):
     acc = torch.empty(n, dtype=torch.float32, device=dev)
     grads = [workloads.grad_draw(w, n, 1, mb, dev) for mb in range(w.micro_batches)]
     norm = torch.zeros(1, dtype=torch.float64, device=dev)
-    ws = torch.empty(max(zs.grad_norm_sq_workspace_bytes(n), 8), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(zs.grad_accum_norm_sq_workspace_bytes(n), 8), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     log(f"[bench] inputs resident: {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
-    timing = []   # per step: (accum_start, norm_start, adamw_start, adamw_end)
+    timing = []   # per step: (start, last micro-batch start, adamw start, adamw end)
+    last = len(grads) - 1
 
     def one_step(t: int, record: bool):
         e = [ev() for _ in range(4)] if record else None
         if record:
             e[0].record()
-        for mb, g in enumerate(grads):
+        for mb, g in enumerate(grads[:last]):
             zs.grad_accum(acc, g, overwrite=(mb == 0))
         if record:
             e[1].record()
-        zs.grad_norm_sq(acc, w.grad_scale, norm, ws)
+        zs.grad_accum_norm_sq(acc, grads[last], last == 0, w.grad_scale, norm, ws)
         if record:
             e[2].record()
         hp = zs.AdamWConfig(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
@@ -141,7 +146,7 @@ def run_gpu(w, steps: int, warmup: int):
     wall = time.perf_counter() - t0
 
     acc_ms = sum(e[0].elapsed_time(e[1]) for e in timing) / steps
-    norm_ms = sum(e[1].elapsed_time(e[2]) for e in timing) / steps
+    last_ms = sum(e[1].elapsed_time(e[2]) for e in timing) / steps
     adamw_ms = sum(e[2].elapsed_time(e[3]) for e in timing) / steps
     assert math.isfinite(norm.item()), "non-finite gradient norm in the bench"
 
@@ -160,7 +165,7 @@ def run_gpu(w, steps: int, warmup: int):
     copy_ms = c0.elapsed_time(c1) / 5
     copy_gbps = 2 * src.numel() * 4 / (copy_ms * 1e-3) / 1e9
     del src, dst
-    return {"n": n, "wall_s": wall, "accum_ms": acc_ms, "norm_ms": norm_ms, "adamw_ms": adamw_ms,
+    return {"n": n, "wall_s": wall, "accum_ms": acc_ms, "last_ms": last_ms, "adamw_ms": adamw_ms,
             "copy_gbps": copy_gbps}
 
 
@@ -191,7 +196,7 @@ def run_cpu_baseline(w, target_s: float = 10.0, sample: int = 1 << 25):
     while True:
         for mb, g in enumerate(grads):
             oracle.grad_accum(acc, g, code, overwrite=(mb == 0))
-        s = oracle.grad_norm_sq(acc, w.grad_scale)
+        s = oracle.grad_norm_sq(acc, w.grad_scale)   # the oracle has no fused form
         hp = oracle.make_hp(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, w.grad_scale, w.max_norm,
                             workloads.other_ranks_norm_sq(w, 1, n), done + 1)
         oracle.adamw_step(hp, master, m, v, acc, bf, norm_sq=s)
@@ -258,7 +263,7 @@ def main():
                    "state": "fp32 master/exp_avg/exp_avg_sq + bf16 param", "clip": w.max_norm > 0},
         "step_hbm_gbps": step_gbps,
         "step_hbm_frac": step_gbps / HBM_PEAK_GBPS,
-        "kernels_ms": {"grad_accum_all_micro_batches": r["accum_ms"], "grad_norm_sq": r["norm_ms"],
+        "kernels_ms": {"grad_accum_all_but_last": r["accum_ms"], "grad_accum_norm_sq_last": r["last_ms"],
                        "adamw_step": r["adamw_ms"]},
         "bytes_per_elem": bpe,
         "device_copy_gbps": r["copy_gbps"],

@@ -28,7 +28,8 @@ ZS_EHIP = -4
 # every symbol include/zshard.h declares
 EXPORTS = (
     "zero_shard_range", "flat_pack", "flat_unpack", "grad_accum",
-    "grad_norm_sq_workspace_bytes", "grad_norm_sq", "adamw_step",
+    "grad_norm_sq_workspace_bytes", "grad_norm_sq", "grad_accum_norm_sq_workspace_bytes",
+    "grad_accum_norm_sq", "adamw_step",
     "zs_strerror", "zs_last_hip_error",
 )
 
@@ -103,6 +104,10 @@ def lib() -> ctypes.CDLL:
         L.grad_norm_sq_workspace_bytes.restype = I64
         L.grad_norm_sq.argtypes = [P, I64, D, P, P, I64, P]
         L.grad_norm_sq.restype = I32
+        L.grad_accum_norm_sq_workspace_bytes.argtypes = [I64]
+        L.grad_accum_norm_sq_workspace_bytes.restype = I64
+        L.grad_accum_norm_sq.argtypes = [P, P, I32, I64, I32, D, P, P, I64, P]
+        L.grad_accum_norm_sq.restype = I32
         L.adamw_step.argtypes = [ctypes.POINTER(AdamW), P, P, P, P, P, I64, P, P]
         L.adamw_step.restype = I32
         L.zs_strerror.argtypes = [I32]
@@ -224,6 +229,28 @@ def grad_norm_sq(grad: torch.Tensor, grad_scale: float, out: torch.Tensor,
                                               _dev(out, "out"), _dev(workspace, "workspace"),
                                               workspace.numel() * workspace.element_size(),
                                               _stream(stream)))
+    return out
+
+
+def grad_accum_norm_sq_workspace_bytes(n: int) -> int:
+    return int(lib().grad_accum_norm_sq_workspace_bytes(int(n)))
+
+
+def grad_accum_norm_sq(acc: torch.Tensor, grad: torch.Tensor, overwrite: bool, grad_scale: float,
+                       out: torch.Tensor, workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """grad_accum, then out[0] (fp64, device) = squared norm of fl32(acc * scale), in one pass."""
+    n = acc.numel()
+    if grad.numel() != n:
+        raise ValueError("grad_accum_norm_sq: size mismatch")
+    need = grad_accum_norm_sq_workspace_bytes(n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=acc.device)
+    if out.dtype != torch.float64 or out.numel() < 1:
+        raise TypeError("grad_accum_norm_sq: out must hold one float64")
+    _check("grad_accum_norm_sq", lib().grad_accum_norm_sq(
+        _dev(acc, "acc", torch.float32), _dev(grad, "grad"), _dtype_code(grad), n, 1 if overwrite else 0,
+        float(grad_scale), _dev(out, "out"), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
 
 

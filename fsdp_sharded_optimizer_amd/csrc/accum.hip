@@ -1,16 +1,25 @@
 // fp32 gradient accumulation over micro-batches: acc = widen(g) for the
-// first micro-batch, acc = fl(acc + widen(g)) after it.
+// first micro-batch, acc = fl(acc + widen(g)) after it; optionally fused
+// with this shard's squared norm of the scaled result (the last micro-batch).
 //
 // HBM-bound streaming: bf16 gradients move 6 B/element on the first
 // micro-batch (read 2, write 4) and 10 B/element after it (read 2 + 4,
-// write 4); fp32 gradients move 8 and 12.
+// write 4); fp32 gradients move 8 and 12.  The fused norm adds no traffic
+// beyond one binary64 partial per workgroup.
 //
 // Layout: lane-contiguous groups of 4 elements (a 64-bit bf16 or 128-bit
 // fp32 load and a 128-bit fp32 access per lane).  A workgroup covers Q
-// groups per lane, the q-th at offset q*1024 in its tile, with every load
-// of the tile issued before the first store: Q = 2 for the accumulating
-// form and Q = 1 for the overwriting form (the faster shapes on gfx950).
-#include "zs_common.h"
+// groups per lane, the q-th at offset q*1024 in its tile, every load of the
+// tile issued before the first store.  Q = 1 for the plain forms (the
+// fastest shape on gfx950: 82 % of peak for the accumulating form against
+// 74-76 % for Q = 2 or 4), Q = 4 for the fused form (its workgroup
+// reduction is amortised over 4096 elements).
+//
+// Fused norm association (fixed by n): each lane adds the squares of its
+// groups q = 0..Q-1, elements 0, 2 into one running sum and 1, 3 into the
+// other; lanes and waves combine in a fixed tree; workgroup partials are
+// reduced in fixed contiguous chunks, then by one workgroup.
+#include "reduce.h"
 
 namespace zs {
 namespace {
@@ -31,12 +40,13 @@ __device__ __forceinline__ float load1(const void* grad, int64_t i) {
     return static_cast<const float*>(grad)[i];
 }
 
-template <int Q, bool VEC, bool BF16, bool OVERWRITE>
-__global__ __launch_bounds__(kBlock) void accum_kernel(float* __restrict__ acc,
-                                                       const void* __restrict__ grad, int64_t n) {
+template <int Q, bool VEC, bool BF16, bool OVERWRITE, bool NORM>
+__global__ __launch_bounds__(kBlock) void accum_kernel(float* __restrict__ acc, const void* __restrict__ grad,
+                                                       int64_t n, float scale, double* __restrict__ partials) {
     constexpr int64_t kGroup = kBlock * 4;
     const int64_t tile = (int64_t)blockIdx.x * kGroup * Q;
     const int64_t lane0 = tile + threadIdx.x * 4;
+    double s0 = 0.0, s1 = 0.0;
     if (VEC && tile + kGroup * Q <= n) {   // whole tile in range
         f32x4 g[Q], a[Q];
 #pragma unroll
@@ -50,45 +60,86 @@ __global__ __launch_bounds__(kBlock) void accum_kernel(float* __restrict__ acc,
                                       : f32x4{a[q].x + g[q].x, a[q].y + g[q].y, a[q].z + g[q].z,
                                               a[q].w + g[q].w};
             st_stream(reinterpret_cast<f32x4*>(acc + lane0 + q * kGroup), r);
+            if (NORM) {
+                const float rv[4] = {r.x, r.y, r.z, r.w};
+                add_squares4(rv, scale, s0, s1);
+            }
         }
-        return;
-    }
-    // ragged tile (or a misaligned buffer): element by element
+    } else {
+        // ragged tile (or a misaligned buffer): element by element, the same
+        // association for the norm (out-of-range elements add +0)
 #pragma unroll
-    for (int q = 0; q < Q; ++q) {
-        const int64_t first = lane0 + q * kGroup;
-        const int64_t last = first + 4 < n ? first + 4 : n;
-        for (int64_t i = first; i < last; ++i) {
-            const float g = load1<BF16>(grad, i);
-            acc[i] = OVERWRITE ? g : acc[i] + g;
+        for (int q = 0; q < Q; ++q) {
+            const int64_t first = lane0 + q * kGroup;
+            float rv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t i = first + j;
+                if (i < n) {
+                    const float g = load1<BF16>(grad, i);
+                    const float r = OVERWRITE ? g : acc[i] + g;
+                    acc[i] = r;
+                    rv[j] = r;
+                }
+            }
+            if (NORM) add_squares4(rv, scale, s0, s1);
         }
+    }
+    if (NORM) {
+        const double total = block_sum(s0 + s1);
+        if (threadIdx.x == 0) partials[blockIdx.x] = total;
     }
 }
 
-template <int Q, bool VEC, bool BF16, bool OVERWRITE>
-hipError_t launch(float* acc, const void* grad, int64_t n, hipStream_t stream) {
-    const int64_t per_block = (int64_t)kBlock * 4 * Q;
-    const int64_t blocks = (n + per_block - 1) / per_block;
-    hipLaunchKernelGGL((accum_kernel<Q, VEC, BF16, OVERWRITE>), dim3((unsigned)blocks), dim3(kBlock), 0,
-                       stream, acc, grad, n);
+template <int Q>
+constexpr int64_t per_block() { return (int64_t)kBlock * 4 * Q; }
+
+template <int Q, bool VEC, bool BF16, bool OVERWRITE, bool NORM>
+hipError_t launch(float* acc, const void* grad, int64_t n, float scale, double* partials, hipStream_t stream) {
+    const int64_t blocks = (n + per_block<Q>() - 1) / per_block<Q>();
+    hipLaunchKernelGGL((accum_kernel<Q, VEC, BF16, OVERWRITE, NORM>), dim3((unsigned)blocks), dim3(kBlock), 0,
+                       stream, acc, grad, n, scale, partials);
     return hipGetLastError();
 }
 
-template <bool VEC>
-hipError_t dispatch(float* acc, const void* grad, int grad_bf16, int64_t n, int overwrite,
-                    hipStream_t stream) {
-    if (grad_bf16) return overwrite ? launch<1, VEC, true, true>(acc, grad, n, stream)
-                                    : launch<2, VEC, true, false>(acc, grad, n, stream);
-    return overwrite ? launch<1, VEC, false, true>(acc, grad, n, stream)
-                     : launch<2, VEC, false, false>(acc, grad, n, stream);
+template <int Q, bool NORM>
+hipError_t dispatch(float* acc, const void* grad, int grad_bf16, int64_t n, int overwrite, bool vec, float scale,
+                    double* partials, hipStream_t stream) {
+    if (vec) {
+        if (grad_bf16) return overwrite ? launch<Q, true, true, true, NORM>(acc, grad, n, scale, partials, stream)
+                                        : launch<Q, true, true, false, NORM>(acc, grad, n, scale, partials, stream);
+        return overwrite ? launch<Q, true, false, true, NORM>(acc, grad, n, scale, partials, stream)
+                         : launch<Q, true, false, false, NORM>(acc, grad, n, scale, partials, stream);
+    }
+    if (grad_bf16) return overwrite ? launch<Q, false, true, true, NORM>(acc, grad, n, scale, partials, stream)
+                                    : launch<Q, false, true, false, NORM>(acc, grad, n, scale, partials, stream);
+    return overwrite ? launch<Q, false, false, true, NORM>(acc, grad, n, scale, partials, stream)
+                     : launch<Q, false, false, false, NORM>(acc, grad, n, scale, partials, stream);
 }
+
+constexpr int kFusedQ = 4;
 
 }  // namespace
 
 hipError_t launch_grad_accum(float* acc, const void* grad, int grad_bf16, int64_t n, int overwrite,
                              bool vec_ok, hipStream_t stream) {
-    return vec_ok ? dispatch<true>(acc, grad, grad_bf16, n, overwrite, stream)
-                  : dispatch<false>(acc, grad, grad_bf16, n, overwrite, stream);
+    return dispatch<1, false>(acc, grad, grad_bf16, n, overwrite, vec_ok, 0.0f, nullptr, stream);
+}
+
+int64_t accum_norm_partials(int64_t n) {
+    return n <= 0 ? 0 : (n + per_block<kFusedQ>() - 1) / per_block<kFusedQ>();
+}
+
+hipError_t launch_grad_accum_norm_sq(float* acc, const void* grad, int grad_bf16, int64_t n, int overwrite,
+                                     float scale, double* out, double* workspace, bool vec_ok,
+                                     hipStream_t stream) {
+    const int64_t parts = accum_norm_partials(n);
+    if (parts > 0) {
+        const hipError_t e = dispatch<kFusedQ, true>(acc, grad, grad_bf16, n, overwrite, vec_ok, scale,
+                                                     workspace, stream);
+        if (e != hipSuccess) return e;
+    }
+    return launch_sum_partials(workspace, parts, workspace + parts, out, stream);
 }
 
 }  // namespace zs

@@ -10,7 +10,7 @@
 #include <cstring>
 
 #include "../../include/zshard.h"
-#include "zs_common.h"
+#include "reduce.h"
 
 namespace {
 
@@ -104,6 +104,35 @@ int32_t grad_norm_sq(const float* grad, int64_t n, double grad_scale, double* ou
     return hip_status(zs::launch_grad_norm_sq(grad, n, (float)grad_scale, out_sq_dev,
                                               static_cast<double*>(workspace), vec,
                                               as_stream(hip_stream)));
+}
+
+int64_t grad_accum_norm_sq_workspace_bytes(int64_t n) {
+    if (n < 0) return -1;
+    const int64_t parts = zs::accum_norm_partials(n);
+    return parts == 0 ? 0 : (parts + zs::kReduceChunks) * (int64_t)sizeof(double);
+}
+
+int32_t grad_accum_norm_sq(float* acc, const void* grad, int32_t grad_dtype, int64_t n, int32_t overwrite,
+                           double grad_scale, double* out_sq_dev, void* workspace, int64_t workspace_bytes,
+                           void* hip_stream) {
+    if (!dtype_ok(grad_dtype) || !size_ok(n, 4)) return ZS_EINVAL;
+    if (out_sq_dev == nullptr || !aligned(out_sq_dev, 8)) return ZS_EINVAL;
+    if (!(grad_scale > 0.0) || !std::isfinite(grad_scale)) return ZS_EINVAL;
+    const int64_t gsz = elem_size(grad_dtype);
+    if (n > 0 && (acc == nullptr || grad == nullptr || !aligned(acc, 4) || !aligned(grad, (uintptr_t)gsz)))
+        return ZS_EINVAL;
+    const int64_t need = grad_accum_norm_sq_workspace_bytes(n);
+    if (need > 0 && (workspace == nullptr || !aligned(workspace, 8))) return ZS_EINVAL;
+    if (workspace_bytes < need) return ZS_EWORKSPACE;
+    if (overlap(acc, n * 4, grad, n * gsz) || overlap(acc, n * 4, out_sq_dev, 8) ||
+        overlap(grad, n * gsz, out_sq_dev, 8) || overlap(workspace, need, out_sq_dev, 8) ||
+        overlap(workspace, need, acc, n * 4) || overlap(workspace, need, grad, n * gsz))
+        return ZS_EOVERLAP;
+    const bool vec = aligned(acc, 16) && aligned(grad, 16);
+    return hip_status(zs::launch_grad_accum_norm_sq(acc, grad, grad_dtype == ZS_BF16, n, overwrite != 0,
+                                                    (float)grad_scale, out_sq_dev,
+                                                    static_cast<double*>(workspace), vec,
+                                                    as_stream(hip_stream)));
 }
 
 int32_t adamw_step(const zs_adamw* hp, float* master, float* exp_avg, float* exp_avg_sq,

@@ -11,35 +11,12 @@
 // Stage 2: one workgroup adds the P partials in a fixed tree.
 // The association is fixed by n alone, so the result is bit-identical run
 // to run, whichever alignment path loaded the data.
-#include "zs_common.h"
+#include "reduce.h"
 
 namespace zs {
 namespace {
 
 constexpr int64_t kMaxPartials = 2048;   // 8 workgroups per CU on 256 CUs
-
-__device__ __forceinline__ double wave_sum(double x) {
-    // butterfly over the 64 lanes of a wave
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-    return x;
-}
-
-// Sum over the workgroup, result valid in thread 0.
-__device__ __forceinline__ double block_sum(double x) {
-    __shared__ double wave_part[kBlock / 64];
-    x = wave_sum(x);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (lane == 0) wave_part[wave] = x;
-    __syncthreads();
-    double s = 0.0;
-    if (threadIdx.x == 0) {
-        s = wave_part[0];
-#pragma unroll
-        for (int w = 1; w < kBlock / 64; ++w) s += wave_part[w];
-    }
-    return s;
-}
 
 template <bool ALIGNED>
 __global__ __launch_bounds__(kBlock) void norm_partial_kernel(const float* __restrict__ grad,
@@ -58,14 +35,7 @@ __global__ __launch_bounds__(kBlock) void norm_partial_kernel(const float* __res
 #pragma unroll
             for (int j = 0; j < 4; ++j) g[j] = first + j < n ? grad[first + j] : 0.0f;
         }
-        // the binary64 product of two binary32 values is exact, so the
-        // fused form equals fl64(s + g1*g1)
-        const double a0 = (double)(g[0] * scale), a1 = (double)(g[1] * scale);
-        const double a2 = (double)(g[2] * scale), a3 = (double)(g[3] * scale);
-        s0 = __builtin_fma(a0, a0, s0);
-        s1 = __builtin_fma(a1, a1, s1);
-        s0 = __builtin_fma(a2, a2, s0);
-        s1 = __builtin_fma(a3, a3, s1);
+        add_squares4(g, scale, s0, s1);
     }
     const double total = block_sum(s0 + s1);
     if (threadIdx.x == 0) partials[blockIdx.x] = total;
@@ -79,7 +49,35 @@ __global__ __launch_bounds__(kBlock) void norm_final_kernel(const double* __rest
     if (threadIdx.x == 0) *out = total;
 }
 
+// workgroup c adds partials [c*per, min((c+1)*per, count))
+__global__ __launch_bounds__(kBlock) void chunk_sum_kernel(const double* __restrict__ partials,
+                                                           int64_t count, int64_t per,
+                                                           double* __restrict__ stage) {
+    const int64_t lo = (int64_t)blockIdx.x * per;
+    const int64_t hi = lo + per < count ? lo + per : count;
+    double s = 0.0;
+    for (int64_t i = lo + threadIdx.x; i < hi; i += kBlock) s += partials[i];
+    const double total = block_sum(s);
+    if (threadIdx.x == 0) stage[blockIdx.x] = total;
+}
+
 }  // namespace
+
+hipError_t launch_sum_partials(const double* partials, int64_t count, double* stage, double* out,
+                               hipStream_t stream) {
+    if (count <= kBlock * 8) {   // small: one workgroup
+        hipLaunchKernelGGL(norm_final_kernel, dim3(1), dim3(kBlock), 0, stream, partials, count, out);
+        return hipGetLastError();
+    }
+    const int64_t per = (count + kReduceChunks - 1) / kReduceChunks;
+    const int64_t chunks = (count + per - 1) / per;
+    hipLaunchKernelGGL(chunk_sum_kernel, dim3((unsigned)chunks), dim3(kBlock), 0, stream, partials, count, per,
+                       stage);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(norm_final_kernel, dim3(1), dim3(kBlock), 0, stream, stage, chunks, out);
+    return hipGetLastError();
+}
 
 int64_t norm_partial_blocks(int64_t n) {
     if (n <= 0) return 0;

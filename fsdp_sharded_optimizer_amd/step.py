@@ -2,9 +2,10 @@
 
 The state is plain device buffers: the fp32 master shard, exp_avg and
 exp_avg_sq, the fp32 gradient accumulator, the bf16 parameter shard and the
-norm scratch.  A step is: ``accumulate`` once per micro-batch, then
-``step``: the squared-norm reduction (when requested) and the fused AdamW
-update with the bf16 re-cast.  Nothing here computes; it orders calls.
+norm scratch.  A step is: ``accumulate`` once per micro-batch (the last one
+may form the squared norm in the same pass), then ``step``: the norm (if
+not formed yet and requested) and the fused AdamW update with the bf16
+re-cast.  Nothing here computes; it orders calls.
 """
 from __future__ import annotations
 
@@ -32,14 +33,24 @@ class ShardOptimizer:
         self.weight_decay, self.grad_scale, self.max_norm = weight_decay, grad_scale, max_norm
         self.compute_norm = (max_norm > 0) if compute_norm is None else compute_norm
         self.norm_sq = torch.zeros(1, dtype=torch.float64, device=dev)
-        self.workspace = torch.empty(max(zs.grad_norm_sq_workspace_bytes(n), 8), dtype=torch.uint8,
-                                     device=dev)
+        ws = max(zs.grad_norm_sq_workspace_bytes(n), zs.grad_accum_norm_sq_workspace_bytes(n), 8)
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+        self._norm_ready = False
         self.t = 0
         self._pending = 0
+        self._norm_ready = False
 
-    def accumulate(self, grad: torch.Tensor) -> None:
-        """Add one micro-batch gradient (fp32 or bf16) into the fp32 buffer."""
-        zs.grad_accum(self.acc, grad, overwrite=(self._pending == 0))
+    def accumulate(self, grad: torch.Tensor, last: bool = False) -> None:
+        """Add one micro-batch gradient (fp32 or bf16) into the fp32 buffer.
+        With last=True (and a norm wanted) the same pass also forms the
+        squared norm, so step() needs no separate read of the buffer."""
+        first = self._pending == 0
+        if last and self.compute_norm:
+            zs.grad_accum_norm_sq(self.acc, grad, first, self.grad_scale, self.norm_sq, self.workspace)
+            self._norm_ready = True
+        else:
+            zs.grad_accum(self.acc, grad, overwrite=first)
+            self._norm_ready = False
         self._pending += 1
 
     def hp(self, extra_norm_sq: float = 0.0) -> zs.AdamWConfig:
@@ -54,8 +65,10 @@ class ShardOptimizer:
         self.t += 1
         norm = None
         if self.compute_norm:
-            zs.grad_norm_sq(self.acc, self.grad_scale, self.norm_sq, self.workspace)
+            if not self._norm_ready:
+                zs.grad_norm_sq(self.acc, self.grad_scale, self.norm_sq, self.workspace)
             norm = self.norm_sq
         zs.adamw_step(self.hp(extra_norm_sq), self.master, self.exp_avg, self.exp_avg_sq, self.acc,
                       self.param_bf16, norm_sq=norm)
         self._pending = 0
+        self._norm_ready = False

@@ -169,6 +169,33 @@ int32_t grad_norm_sq(const float* grad, int64_t n, double grad_scale, double* ou
                      void* workspace, int64_t workspace_bytes, void* hip_stream);
 
 /*
+ * grad_accum_norm_sq_workspace_bytes — bytes of device workspace
+ * grad_accum_norm_sq needs for n elements (0 for n == 0; -1 for n < 0).
+ */
+int64_t grad_accum_norm_sq_workspace_bytes(int64_t n);
+
+/*
+ * grad_accum_norm_sq — grad_accum fused with grad_norm_sq for the last
+ * micro-batch: one pass accumulates and forms this shard's squared norm of
+ * the scaled result, saving the norm's separate read of the accumulator.
+ * Same sources as grad_accum and grad_norm_sq ([ZeRO page] "梯度累积" and
+ * §"组合策略"; [Accum page] §"梯度累积：用时间换显存": the clip follows the
+ * last micro-batch).
+ * acc[i] as grad_accum; then *out_sq_dev = sum_i (double)g1_i^2 with
+ * g1_i = fl32(acc[i] * (float)grad_scale), binary64, in a fixed order that
+ * depends only on n (not the one grad_norm_sq uses: the two agree to
+ * rounding, each is bit-reproducible run to run).
+ * acc: device fp32[n], read-write; grad: device [n] of grad_dtype, read;
+ * out_sq_dev: device double, written (0 when n == 0); workspace: device,
+ * >= grad_accum_norm_sq_workspace_bytes(n) bytes, 8-byte aligned.
+ * Errors: ZS_EINVAL, ZS_EWORKSPACE, ZS_EOVERLAP (any two of acc, grad,
+ * *out_sq_dev, workspace), ZS_EHIP.
+ */
+int32_t grad_accum_norm_sq(float* acc, const void* grad, int32_t grad_dtype, int64_t n, int32_t overwrite,
+                           double grad_scale, double* out_sq_dev, void* workspace, int64_t workspace_bytes,
+                           void* hip_stream);
+
+/*
  * adamw_step — the fused AdamW update of one rank's shard.
  * [ZeRO page] §ZeRO-1 step, §ZeRO-2 step, §ZeRO-3 step: step counter
  * incremented before use; bias_correction1 = 1 - beta1^t,

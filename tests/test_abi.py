@@ -134,6 +134,29 @@ def test_grad_norm_sq_rejects():
     assert L.grad_norm_sq(FAKE, n, 1.0, out, FAKE + 64, need, None) == B.ZS_EOVERLAP
 
 
+def test_grad_accum_norm_sq_rejects():
+    L = zs.lib()
+    n = 1 << 20
+    need = zs.grad_accum_norm_sq_workspace_bytes(n)
+    assert need == (n // 4096 + 256) * 8
+    assert zs.grad_accum_norm_sq_workspace_bytes(0) == 0 and zs.grad_accum_norm_sq_workspace_bytes(-3) == -1
+    acc, g, ws, out = FAKE, FAKE + 2**30, FAKE + 2**31, FAKE + 2**32
+    call = lambda **k: L.grad_accum_norm_sq(k.get("acc", acc), k.get("g", g), k.get("dt", B.ZS_BF16), k.get("n", n),
+                                            0, k.get("s", 1.0), k.get("out", out), k.get("ws", ws),
+                                            k.get("wsb", need), None)
+    assert call(wsb=need - 8) == B.ZS_EWORKSPACE
+    assert call(dt=5) == B.ZS_EINVAL
+    assert call(out=0) == B.ZS_EINVAL
+    assert call(out=out + 4) == B.ZS_EINVAL
+    assert call(s=-1.0) == B.ZS_EINVAL
+    assert call(acc=0) == B.ZS_EINVAL
+    assert call(ws=0) == B.ZS_EINVAL
+    assert call(g=FAKE + 64) == B.ZS_EOVERLAP                      # grad inside acc
+    assert call(out=FAKE + 16) == B.ZS_EOVERLAP                    # norm inside acc
+    assert call(ws=g + 1024) == B.ZS_EOVERLAP                      # workspace inside grad
+    assert call(n=-1) == B.ZS_EINVAL
+
+
 def _tensors(*pairs):
     arr = (B.Tensor * len(pairs))()
     for i, (p, k) in enumerate(pairs):

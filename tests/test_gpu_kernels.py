@@ -101,6 +101,50 @@ def test_grad_norm_sq(n, offset):
     assert canary_ok(whole, offset, n)
 
 
+@pytest.mark.parametrize("n", [1, 7, 4095, 4096, 4097, 100_003, 9_000_011])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("offset", [0, 3])
+@pytest.mark.parametrize("overwrite", [False, True])
+def test_grad_accum_norm_sq(n, dtype, offset, overwrite):
+    """The fused last micro-batch: the accumulator bit-exact, the squared
+    norm of the scaled result within the bar and reproducible to the bit."""
+    print(f"grad_accum_norm_sq n={n} dtype={dtype} offset={offset} overwrite={overwrite}", flush=True)
+    rng = np.random.default_rng(n * 13 + offset + overwrite)
+    code = oracle.BF16 if dtype == "bf16" else oracle.F32
+    acc0 = (rng.standard_normal(n) * 1e-2).astype(np.float32)
+    g32 = (rng.standard_normal(n) * 1e-2).astype(np.float32)
+    g = oracle.bf16_rne(g32) if dtype == "bf16" else g32
+    scale = 1.0 / 16
+    ref = acc0.copy()
+    oracle.grad_accum(ref, g, code, overwrite=overwrite)
+    want = oracle.grad_norm_sq(ref, scale)
+    outs = []
+    for _ in range(2):
+        acc, acc_whole = dev_buf(acc0, offset)
+        gd, g_whole = dev_buf(g, offset, bf16=(dtype == "bf16"))
+        out = torch.full((1,), float("nan"), dtype=torch.float64, device="cuda")
+        zs.grad_accum_norm_sq(acc, gd, overwrite, scale, out)
+        assert bits_equal(to_np(acc), ref)
+        assert canary_ok(acc_whole, offset, n) and canary_ok(g_whole, offset, n)
+        outs.append(out.item())
+    assert outs[0] == outs[1]
+    assert abs(math.sqrt(outs[0]) - math.sqrt(want)) <= NORM_TOL * math.sqrt(want)
+
+
+def test_grad_accum_norm_sq_empty_and_closed_form():
+    out = torch.full((1,), float("nan"), dtype=torch.float64, device="cuda")
+    e = torch.empty(0, dtype=torch.float32, device="cuda")
+    zs.grad_accum_norm_sq(e, e.to(torch.bfloat16), True, 1.0, out)
+    assert out.item() == 0.0
+    # first micro-batch of 2^23 + 3 elements of 2^-7 at scale 1/8: exactly (2^23 + 3) * 2^-20
+    n = (1 << 23) + 3
+    acc = torch.empty(n, dtype=torch.float32, device="cuda")
+    g = torch.full((n,), 2.0**-7, dtype=torch.bfloat16, device="cuda")
+    zs.grad_accum_norm_sq(acc, g, True, 1.0 / 8, out)
+    assert out.item() == n * 2.0**-20
+    assert torch.all(acc == 2.0**-7)
+
+
 def test_grad_norm_sq_empty_and_closed_form():
     out = torch.full((1,), float("nan"), dtype=torch.float64, device="cuda")
     zs.grad_norm_sq(torch.empty(0, dtype=torch.float32, device="cuda"), 1.0, out)

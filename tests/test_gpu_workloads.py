@@ -49,15 +49,19 @@ def host(t: torch.Tensor) -> np.ndarray:
     return to_np(t)
 
 
-def run_shard(w: workloads.Workload, n: int, sampled: bool, full_norm: bool):
-    """Drive the library and the oracle through w.steps steps of one shard."""
+def run_shard(w: workloads.Workload, n: int, sampled: bool, full_norm: bool, fused: bool = True):
+    """Drive the library and the oracle through w.steps steps of one shard.
+    fused: the last micro-batch forms the norm in the same pass
+    (grad_accum_norm_sq, as bench.py runs it); otherwise grad_accum for
+    every micro-batch, then grad_norm_sq."""
     master = workloads.master_init(w, n, DEV)
     param = master.to(torch.bfloat16) if w.bf16_param else None
     exp_avg = torch.zeros(n, dtype=torch.float32, device=DEV)
     exp_avg_sq = torch.zeros(n, dtype=torch.float32, device=DEV)
     acc = torch.empty(n, dtype=torch.float32, device=DEV)
     norm = torch.zeros(1, dtype=torch.float64, device=DEV)
-    ws = torch.empty(max(zs.grad_norm_sq_workspace_bytes(n), 8), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(max(zs.grad_norm_sq_workspace_bytes(n), zs.grad_accum_norm_sq_workspace_bytes(n), 8),
+                     dtype=torch.uint8, device=DEV)
 
     idx = sample_indices(n, seed=w.cfg) if sampled else None
     pick = (lambda t: t[idx]) if sampled else (lambda t: t)
@@ -73,12 +77,16 @@ def run_shard(w: workloads.Workload, n: int, sampled: bool, full_norm: bool):
         t0 = time.perf_counter()
         for mb in range(w.micro_batches):
             g = workloads.grad_draw(w, n, t, mb, DEV)
-            zs.grad_accum(acc, g, overwrite=(mb == 0))
+            if fused and mb == w.micro_batches - 1:
+                zs.grad_accum_norm_sq(acc, g, mb == 0, w.grad_scale, norm, ws)
+            else:
+                zs.grad_accum(acc, g, overwrite=(mb == 0))
             oracle.grad_accum(acc_ref, host(pick(g)), code, overwrite=(mb == 0))
             if full_norm:
                 oracle.grad_accum(acc_full, host(g), code, overwrite=(mb == 0))
             del g
-        zs.grad_norm_sq(acc, w.grad_scale, norm, ws)
+        if not fused:
+            zs.grad_norm_sq(acc, w.grad_scale, norm, ws)
         s_gpu = float(norm.item())
         s_ref = oracle.grad_norm_sq(acc_full if full_norm else acc_ref, w.grad_scale) \
             if (full_norm or not sampled) else None
@@ -115,9 +123,11 @@ def run_shard(w: workloads.Workload, n: int, sampled: bool, full_norm: bool):
 # small sizes: every element
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name,n", [("llama7b_shard", 1_000_037), ("llama13b_shard_clip", 600_011),
-                                    ("zero3_70b_shard", 2_000_003)])
-def test_workload_small(name, n):
+@pytest.mark.parametrize("name,n,fused", [("llama7b_shard", 1_000_037, True), ("llama7b_shard", 1_000_037, False),
+                                          ("llama13b_shard_clip", 600_011, True),
+                                          ("llama13b_shard_clip", 600_011, False),
+                                          ("zero3_70b_shard", 2_000_003, True), ("zero3_70b_shard", 2_000_003, False)])
+def test_workload_small(name, n, fused):
     """Every element, at a reduced shard length.  The gradient std is scaled
     by sqrt(full/n) so the global norm, and with it the clipping pattern of
     the 13B workload, is the one of the full shard."""
@@ -126,7 +136,7 @@ def test_workload_small(name, n):
     _, start, end, _ = zs.zero_shard_range(w.total, w.world, w.rank)
     w = replace(w, grad_std=w.grad_std * math.sqrt((end - start) / n))
     log(f"workload {name} small n={n}")
-    rep = run_shard(w, n, sampled=False, full_norm=False)
+    rep = run_shard(w, n, sampled=False, full_norm=False, fused=fused)
     if name == "llama13b_shard_clip":
         clipped = [r["step"] for r in rep if r["coef"] < 1.0]
         assert clipped == [2, 5, 8], clipped
@@ -260,14 +270,14 @@ def test_full_fsdp_unit_70b_block():
     log(f"  unit {res} bf16 identical {frac:.6f}")
 
 
-@pytest.mark.parametrize("name,full_norm", [("llama7b_shard", False), ("zero3_70b_shard", True),
-                                            ("llama13b_shard_clip", True)])
-def test_full_shard(name, full_norm):
+@pytest.mark.parametrize("name,full_norm,fused", [("llama7b_shard", False, True), ("zero3_70b_shard", True, False),
+                                                  ("llama13b_shard_clip", True, True)])
+def test_full_shard(name, full_norm, fused):
     w = workloads.WORKLOADS[name]
     _, start, end, _ = zs.zero_shard_range(w.total, w.world, w.rank)
     n = end - start
     log(f"full {name}: shard of {n} elements, {w.steps} steps x {w.micro_batches} micro-batches")
-    rep = run_shard(w, n, sampled=True, full_norm=full_norm)
+    rep = run_shard(w, n, sampled=True, full_norm=full_norm, fused=fused)
     if name == "llama13b_shard_clip":
         assert [r["step"] for r in rep if r["coef"] < 1.0] == [2, 5, 8]
     if name == "zero3_70b_shard":
