@@ -41,9 +41,9 @@ HBM_PEAK_GBPS = 8000.0   # MI355X published HBM3E bandwidth
 # on: the hash covers the kernel file and its header.
 PMC_TRAFFIC = {
     "adamw_step": {"sources": ("csrc/adamw.hip", "csrc/zs_common.h"),
-                   "sha256_16": "2381c1755ddcaf2a", "shard_elems": 842301952,
-                   "fetch_kib": 6580537.9, "fetch_scale": 2.0,
-                   "write_kib": 11515934.5, "write_scale": 1.0},
+                   "sha256_16": "4551c1e0b6095426", "shard_elems": 842301952,
+                   "fetch_kib": 6580544.9, "fetch_scale": 2.0,
+                   "write_kib": 11515848.3, "write_scale": 1.0},
 }
 
 
@@ -169,6 +169,39 @@ def run_gpu(w, steps: int, warmup: int):
             "copy_gbps": copy_gbps}
 
 
+def run_flat(w, reps: int = 10):
+    """FSDP unit: time flat_pack of the unit's tensors into the padded flat
+    bf16 buffer and flat_unpack back (4 B per element each)."""
+    import torch
+    import workloads
+    import fsdp_sharded_optimizer_amd as zs
+
+    dev = torch.device("cuda", 0)
+    params = workloads.unit_tensors(w, dev)
+    _, _, _, padded = zs.zero_shard_range(w.total, w.world, w.rank)
+    flat = torch.empty(padded, dtype=torch.bfloat16, device=dev)
+    outs = [torch.empty_like(p) for p in params]
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    zs.flat_pack(params, flat, padded)
+    zs.flat_unpack(flat, outs)
+    e = [ev() for _ in range(3)]
+    e[0].record()
+    for _ in range(reps):
+        zs.flat_pack(params, flat, padded)
+    e[1].record()
+    for _ in range(reps):
+        zs.flat_unpack(flat, outs)
+    e[2].record()
+    torch.cuda.synchronize()
+    pack_ms = e[0].elapsed_time(e[1]) / reps
+    unpack_ms = e[1].elapsed_time(e[2]) / reps
+    assert all(torch.equal(a.view(torch.int16), b.view(torch.int16)) for a, b in zip(params, outs))
+    bytes_ = 4 * w.total
+    return {"tensors": len(params), "elements": w.total, "padded": padded,
+            "pack_ms": pack_ms, "unpack_ms": unpack_ms,
+            "pack_gbps": bytes_ / (pack_ms * 1e-3) / 1e9, "unpack_gbps": bytes_ / (unpack_ms * 1e-3) / 1e9}
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline leg: the oracle as it stands on a bounded sample
 # ---------------------------------------------------------------------------
@@ -236,6 +269,11 @@ def main():
 
     r = run_gpu(w, args.steps, args.warmup)
     n = r["n"]
+    flat = None
+    if w.unit_shapes:
+        import torch
+        torch.cuda.empty_cache()
+        flat = run_flat(w)
     bpe = step_bytes_per_elem(w)
     ms_per_step = r["wall_s"] * 1e3 / args.steps
     adamw_bytes = bpe["adamw_step"] * n
@@ -272,6 +310,7 @@ def main():
                      "traffic": pmc_traffic("adamw_step", n), "traffic_unit": "bytes/launch",
                      "algorithmic_bytes": adamw_bytes, "launch_ms": r["adamw_ms"]},
         "cpu_baseline": cpu,
+        "flat_unit": flat,
     }
     print(json.dumps(out), flush=True)
 

@@ -97,6 +97,7 @@ constexpr int64_t per_block() { return (int64_t)kBlock * 4 * Q; }
 template <int Q, bool VEC, bool BF16, bool OVERWRITE, bool NORM>
 hipError_t launch(float* acc, const void* grad, int64_t n, float scale, double* partials, hipStream_t stream) {
     const int64_t blocks = (n + per_block<Q>() - 1) / per_block<Q>();
+    if (blocks > (int64_t)UINT32_MAX) return hipErrorInvalidValue;
     hipLaunchKernelGGL((accum_kernel<Q, VEC, BF16, OVERWRITE, NORM>), dim3((unsigned)blocks), dim3(kBlock), 0,
                        stream, acc, grad, n, scale, partials);
     return hipGetLastError();

@@ -134,6 +134,7 @@ template <int KIND, bool UNPACK>
 hipError_t launch(const FlatBatch& b, hipStream_t stream) {
     const int64_t blocks = b.tile_start[b.count];
     if (blocks <= 0) return hipSuccess;
+    if (blocks > (int64_t)UINT32_MAX) return hipErrorInvalidValue;
     hipLaunchKernelGGL((flat_kernel<KIND, UNPACK>), dim3((unsigned)blocks), dim3(kBlock), 0, stream, b);
     return hipGetLastError();
 }
