@@ -55,39 +55,62 @@ class AdamWScalars(ctypes.Structure):
         "bias_correction2_sqrt", "eps", "decay", "grad_scale")]
 
 
+def _configure(L):
+    """Declare the C signatures on a loaded oracle library."""
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    I32 = ctypes.c_int32
+    L.orc_bf16_rne.argtypes = [ctypes.c_float]
+    L.orc_bf16_rne.restype = ctypes.c_uint16
+    L.orc_bf16_rne_array.argtypes = [P, P, I64]
+    L.orc_bf16_rne_array.restype = None
+    L.orc_shard_range.argtypes = [I64, I32, I32, P]
+    L.orc_shard_range.restype = ctypes.c_int
+    L.orc_flat_pack.argtypes = [P, P, I32, I32, P, I32, I64]
+    L.orc_flat_pack.restype = ctypes.c_int
+    L.orc_flat_unpack.argtypes = [P, I32, P, P, I32, I32]
+    L.orc_flat_unpack.restype = ctypes.c_int
+    L.orc_grad_accum.argtypes = [P, P, I32, I64, I32]
+    L.orc_grad_accum.restype = ctypes.c_int
+    L.orc_grad_norm_sq.argtypes = [P, I64, ctypes.c_double]
+    L.orc_grad_norm_sq.restype = ctypes.c_double
+    L.orc_adamw_scalars_make.argtypes = [ctypes.POINTER(AdamWHp), ctypes.POINTER(AdamWScalars)]
+    L.orc_adamw_scalars_make.restype = ctypes.c_int
+    L.orc_clip_coef.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_double]
+    L.orc_clip_coef.restype = ctypes.c_float
+    L.orc_adamw_step.argtypes = [ctypes.POINTER(AdamWHp), P, P, P, P, P, I64, P]
+    L.orc_adamw_step.restype = ctypes.c_int
+    L.orc_num_threads.argtypes = []
+    L.orc_num_threads.restype = ctypes.c_int
+    return L
+
+
 def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
             build()
-        L = ctypes.CDLL(_LIB_PATH)
-        P = ctypes.c_void_p
-        I64 = ctypes.c_int64
-        I32 = ctypes.c_int32
-        L.orc_bf16_rne.argtypes = [ctypes.c_float]
-        L.orc_bf16_rne.restype = ctypes.c_uint16
-        L.orc_bf16_rne_array.argtypes = [P, P, I64]
-        L.orc_bf16_rne_array.restype = None
-        L.orc_shard_range.argtypes = [I64, I32, I32, P]
-        L.orc_shard_range.restype = ctypes.c_int
-        L.orc_flat_pack.argtypes = [P, P, I32, I32, P, I32, I64]
-        L.orc_flat_pack.restype = ctypes.c_int
-        L.orc_flat_unpack.argtypes = [P, I32, P, P, I32, I32]
-        L.orc_flat_unpack.restype = ctypes.c_int
-        L.orc_grad_accum.argtypes = [P, P, I32, I64, I32]
-        L.orc_grad_accum.restype = ctypes.c_int
-        L.orc_grad_norm_sq.argtypes = [P, I64, ctypes.c_double]
-        L.orc_grad_norm_sq.restype = ctypes.c_double
-        L.orc_adamw_scalars_make.argtypes = [ctypes.POINTER(AdamWHp), ctypes.POINTER(AdamWScalars)]
-        L.orc_adamw_scalars_make.restype = ctypes.c_int
-        L.orc_clip_coef.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_double]
-        L.orc_clip_coef.restype = ctypes.c_float
-        L.orc_adamw_step.argtypes = [ctypes.POINTER(AdamWHp), P, P, P, P, P, I64, P]
-        L.orc_adamw_step.restype = ctypes.c_int
-        L.orc_num_threads.argtypes = []
-        L.orc_num_threads.restype = ctypes.c_int
-        _lib = L
+        _lib = _configure(ctypes.CDLL(_LIB_PATH))
     return _lib
+
+
+class use_library:
+    """Context manager: route every oracle call to another build of oracle.c
+    (the mutation tests load deliberately broken copies this way)."""
+
+    def __init__(self, path: str):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        self.saved = lib()
+        _lib = _configure(ctypes.CDLL(self.path))
+        return self
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
 
 
 def _ptr(a: np.ndarray):

@@ -64,6 +64,9 @@ def test_bf16_rne_ties_and_overflow(orc):
     assert oracle.bf16_rne(np.array([0x7F7FFFFF], dtype=np.uint32).view(np.float32))[0] == 0x7F80
     assert oracle.bf16_rne(np.array([0xFF7FFFFF], dtype=np.uint32).view(np.float32))[0] == 0xFF80
     assert oracle.bf16_rne(np.float32(-0.0))[()] == 0x8000
+    # every NaN (quiet, signalling, negative, any payload) becomes 0x7FC0
+    nans = np.array([0x7FC00000, 0x7F800001, 0xFFC00000, 0x7FFFFFFF, 0xFF812345], dtype=np.uint32)
+    assert np.all(oracle.bf16_rne(nans.view(np.float32)) == 0x7FC0)
 
 
 def test_bf16_widen_all_patterns_vs_torch(orc):
@@ -85,12 +88,9 @@ def test_shard_range_golden(orc):
         assert got == (case["chunk"], case["start"], case["end"], case["padded_total"]), case["name"]
 
 
-def test_shard_range_brute_force(orc):
-    """For every T <= 300, N <= 40 and rank: the ranges are exactly the
-    index classes {i in [0,T): i // c == r} for the smallest c with N*c >= T,
-    found by search, so they tile [0, T) with no overlap."""
-    for T in range(0, 301):
-        for N in range(1, 41):
+def _shard_brute(max_total: int, max_world: int):
+    for T in range(0, max_total + 1):
+        for N in range(1, max_world + 1):
             c = 0
             while N * c < T:
                 c += 1
@@ -107,6 +107,17 @@ def test_shard_range_brute_force(orc):
                 covered += list(range(start, end))
             assert covered == list(range(T))
             assert padded % N == 0 and padded - T < max(N, 1)
+
+
+def test_shard_range_brute_force(orc):
+    """For every T <= 300, N <= 40 and rank: the ranges are exactly the
+    index classes {i in [0,T): i // c == r} for the smallest c with N*c >= T,
+    found by search, so they tile [0, T) with no overlap."""
+    _shard_brute(300, 40)
+
+
+def test_shard_range_brute_force_small(orc):
+    _shard_brute(60, 12)
 
 
 def test_shard_range_rejects(orc):
