@@ -130,10 +130,14 @@ def num_threads() -> int:
     return int(lib().orc_num_threads())
 
 
-def bf16_rne(x) -> np.ndarray:
+def bf16_rne(x, out: np.ndarray = None) -> np.ndarray:
     """bf16 bit patterns of fp32 values, round to nearest even."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    out = np.empty(x.shape, dtype=np.uint16)
+    if out is None:
+        out = np.empty(x.shape, dtype=np.uint16)
+    _need(out, np.uint16, "out")
+    if out.size != x.size:
+        raise ValueError("bf16_rne: out has the wrong size")
     lib().orc_bf16_rne_array(_ptr(x), _ptr(out), x.size)
     return out
 
