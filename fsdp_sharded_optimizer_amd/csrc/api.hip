@@ -230,7 +230,8 @@ static int32_t flat_common(const zs_tensor* tensors, int32_t count, void* flat, 
 
     // batches of up to kFlatMaxTensors entries; the pack padding is one
     // more entry with a NULL tensor
-    const int64_t tile = zs::flat_tile_elems();
+    const int64_t tile = zs::flat_tile_elems(kind);
+    const int64_t ve = zs::flat_vec_elems(kind);
     const bool flat16 = aligned(flat, 16);
     zs::FlatBatch b;
     std::memset(&b, 0, sizeof(b));
@@ -244,16 +245,18 @@ static int32_t flat_common(const zs_tensor* tensors, int32_t count, void* flat, 
         return rc;
     };
     auto add = [&](void* ptr, int64_t flat_off, int64_t numel) -> int32_t {
-        if (b.count == zs::kFlatMaxTensors) {
+        const int64_t tiles = (numel + tile - 1) / tile;
+        if (b.count == zs::kFlatMaxTensors || (int64_t)b.tile_start[b.count] + tiles > (int64_t)UINT32_MAX) {
             const int32_t rc = flush();
             if (rc != ZS_OK) return rc;
         }
+        if (tiles > (int64_t)UINT32_MAX) return ZS_EINVAL;   // one tensor beyond a launch's grid
         const int c = b.count;
-        b.tensor[c] = ptr;
-        b.flat_off[c] = flat_off;
-        b.numel[c] = numel;
-        b.vec_ok[c] = flat16 && (flat_off % 8 == 0) && (ptr == nullptr || aligned(ptr, 16));
-        b.tile_start[c + 1] = b.tile_start[c] + (numel + tile - 1) / tile;
+        b.e[c].tensor = ptr;
+        b.e[c].flat_off = flat_off;
+        b.e[c].numel = numel;
+        b.e[c].vec_ok = flat16 && (flat_off % ve == 0) && (ptr == nullptr || aligned(ptr, 16));
+        b.tile_start[c + 1] = b.tile_start[c] + (uint32_t)tiles;
         b.count = c + 1;
         return ZS_OK;
     };

@@ -76,18 +76,25 @@ hipError_t launch_grad_norm_sq(const float* grad, int64_t n, float scale, double
 
 // One launch of the flatten/unflatten copy covers up to kFlatMaxTensors
 // tensors (the table travels in the kernel arguments; no device allocation).
+// The workgroup table is 32-bit so a workgroup finds its tensor from two
+// scalar loads; each tensor's record is then one more 32-byte load.
 constexpr int kFlatMaxTensors = 32;
+struct FlatEntry {
+    void* tensor;        // src (pack) / dst (unpack); NULL = zero fill
+    int64_t flat_off;    // element offset of the tensor in the flat buffer
+    int64_t numel;
+    int32_t vec_ok;      // vector path allowed for this tensor
+    int32_t pad_;
+};
 struct FlatBatch {
-    void* tensor[kFlatMaxTensors + 1];       // per tensor: src (pack) / dst (unpack); NULL = zero fill
-    int64_t flat_off[kFlatMaxTensors + 1];   // element offset of the tensor in the flat buffer
-    int64_t numel[kFlatMaxTensors + 1];
-    int64_t tile_start[kFlatMaxTensors + 2]; // first workgroup of each tensor; [count] = total
-    int32_t vec_ok[kFlatMaxTensors + 1];     // 128-bit path allowed for this tensor
-    int32_t count;                           // tensors in this batch (incl. a zero-fill entry)
+    uint32_t tile_start[kFlatMaxTensors + 1];   // first workgroup of each tensor; [count] = total
+    int32_t count;                             // tensors in this batch (incl. a zero-fill entry)
     void* flat;
+    FlatEntry e[kFlatMaxTensors];
 };
 // kind: 0 = f32->f32, 1 = bf16->bf16, 2 = bf16->f32 (pack widen), 3 = f32->bf16 (unpack RNE)
 hipError_t launch_flat(const FlatBatch& b, int kind, int unpack, hipStream_t stream);
-int64_t flat_tile_elems();
+int64_t flat_tile_elems(int kind);   // elements per workgroup
+int64_t flat_vec_elems(int kind);    // elements per lane on the vector path
 
 }  // namespace zs
