@@ -41,9 +41,9 @@ HBM_PEAK_GBPS = 8000.0   # MI355X published HBM3E bandwidth
 # on: the hash covers the kernel file and its header.
 PMC_TRAFFIC = {
     "adamw_step": {"sources": ("csrc/adamw.hip", "csrc/zs_common.h"),
-                   "sha256_16": "4551c1e0b6095426", "shard_elems": 842301952,
-                   "fetch_kib": 6580544.9, "fetch_scale": 2.0,
-                   "write_kib": 11515848.3, "write_scale": 1.0},
+                   "sha256_16": "448609d23130f47e", "shard_elems": 842301952,
+                   "fetch_kib": 6580549.0, "fetch_scale": 2.0,
+                   "write_kib": 11515849.5, "write_scale": 1.0},
 }
 
 
@@ -150,6 +150,19 @@ def run_gpu(w, steps: int, warmup: int):
     adamw_ms = sum(e[2].elapsed_time(e[3]) for e in timing) / steps
     assert math.isfinite(norm.item()), "non-finite gradient norm in the bench"
 
+    # outside the step: the reduce-scatter's arithmetic on this rank's shard,
+    # the same buffers read as N rank chunks, in one pass
+    reduce_ms = None
+    if len(grads) > 1:
+        r0, r1 = ev(), ev()
+        zs.grad_reduce_chunks(acc, grads, True)
+        r0.record()
+        for _ in range(3):
+            zs.grad_reduce_chunks(acc, grads, True)
+        r1.record()
+        torch.cuda.synchronize()
+        reduce_ms = r0.elapsed_time(r1) / 3
+
     # achievable-bandwidth reference: a plain device copy of 4 GiB (also the
     # calibration kernel for the HBM byte counters)
     src = torch.empty(1 << 30, dtype=torch.float32, device=dev)
@@ -166,6 +179,7 @@ def run_gpu(w, steps: int, warmup: int):
     copy_gbps = 2 * src.numel() * 4 / (copy_ms * 1e-3) / 1e9
     del src, dst
     return {"n": n, "wall_s": wall, "accum_ms": acc_ms, "last_ms": last_ms, "adamw_ms": adamw_ms,
+            "reduce_ms": reduce_ms, "chunks": len(grads),
             "copy_gbps": copy_gbps}
 
 
@@ -311,6 +325,9 @@ def main():
                      "algorithmic_bytes": adamw_bytes, "launch_ms": r["adamw_ms"]},
         "cpu_baseline": cpu,
         "flat_unit": flat,
+        "reduce_chunks": None if r["reduce_ms"] is None else {
+            "chunks": r["chunks"], "ms": r["reduce_ms"],
+            "gbps": (r["chunks"] * (2 if w.grad_dtype == "bf16" else 4) + 4) * n / (r["reduce_ms"] * 1e-3) / 1e9},
     }
     print(json.dumps(out), flush=True)
 

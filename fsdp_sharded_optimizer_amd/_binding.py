@@ -27,7 +27,7 @@ ZS_EHIP = -4
 
 # every symbol include/zshard.h declares
 EXPORTS = (
-    "zero_shard_range", "flat_pack", "flat_unpack", "grad_accum",
+    "zero_shard_range", "flat_pack", "flat_unpack", "grad_accum", "grad_reduce_chunks",
     "grad_norm_sq_workspace_bytes", "grad_norm_sq", "grad_accum_norm_sq_workspace_bytes",
     "grad_accum_norm_sq", "adamw_step",
     "zs_strerror", "zs_last_hip_error",
@@ -100,6 +100,8 @@ def lib() -> ctypes.CDLL:
         L.flat_unpack.restype = I32
         L.grad_accum.argtypes = [P, P, I32, I64, I32, P]
         L.grad_accum.restype = I32
+        L.grad_reduce_chunks.argtypes = [P, P, I32, I32, I64, I32, P]
+        L.grad_reduce_chunks.restype = I32
         L.grad_norm_sq_workspace_bytes.argtypes = [I64]
         L.grad_norm_sq_workspace_bytes.restype = I64
         L.grad_norm_sq.argtypes = [P, I64, D, P, P, I64, P]
@@ -210,6 +212,24 @@ def grad_accum(acc: torch.Tensor, grad: torch.Tensor, overwrite: bool, stream=No
     _check("grad_accum", lib().grad_accum(_dev(acc, "acc", torch.float32), _dev(grad, "grad"),
                                           _dtype_code(grad), acc.numel(), 1 if overwrite else 0,
                                           _stream(stream)))
+
+
+def grad_reduce_chunks(acc: torch.Tensor, chunks: Sequence[torch.Tensor], overwrite: bool, stream=None) -> None:
+    """acc = (acc or 0) + chunks[0] + chunks[1] + ... in order, fp32 (reduce-scatter arithmetic)."""
+    n = acc.numel()
+    ptrs = (ctypes.c_void_p * max(len(chunks), 1))()
+    dt = None
+    for k, c in enumerate(chunks):
+        if c.numel() != n:
+            raise ValueError("grad_reduce_chunks: size mismatch")
+        code = _dtype_code(c)
+        if dt is not None and code != dt:
+            raise TypeError("grad_reduce_chunks: all chunks must share one dtype")
+        dt = code
+        ptrs[k] = _dev(c, f"chunks[{k}]")
+    _check("grad_reduce_chunks", lib().grad_reduce_chunks(
+        _dev(acc, "acc", torch.float32), ctypes.cast(ptrs, ctypes.c_void_p), len(chunks),
+        ZS_BF16 if dt is None else dt, n, 1 if overwrite else 0, _stream(stream)))
 
 
 def grad_norm_sq_workspace_bytes(n: int) -> int:

@@ -148,3 +148,122 @@ hipError_t launch_grad_accum_norm_sq(float* acc, const void* grad, int grad_bf16
 }
 
 }  // namespace zs
+
+// ---------------------------------------------------------------------------
+// Sum of N rank chunks into this rank's fp32 shard, in rank order: the
+// arithmetic of a reduce-scatter's receiving side.  One pass per launch of up
+// to kReduceMaxChunks chunks: acc = ((acc + widen(c0)) + widen(c1)) + ...,
+// the same left fold, rounding for rounding, as one grad_accum call per
+// chunk, at 2 B (bf16) or 4 B (fp32) per chunk element plus 8 B of acc
+// traffic per element instead of ~10 B per chunk element.
+// ---------------------------------------------------------------------------
+namespace zs {
+namespace {
+
+// Layout: one-wave workgroups, two groups of 4 elements per lane, 256
+// elements apart (every chunk's loads for both groups issued before the
+// fold): 76 % of the HBM peak on gfx950 for 8 bf16 chunks, against 68 % for
+// one group per lane in 256-thread workgroups.  Capping residency, which
+// helps adamw, hurts this read-heavy kernel.
+constexpr int kReduceBlock = 64;
+constexpr int kReduceGroups = 2;
+
+// The loaded words stay in their storage width (2 VGPRs per bf16 group, not
+// 4) until the fold widens them: with 16 chunks x 2 groups in flight this
+// keeps the kernel at 6+ waves per SIMD instead of 3.
+template <bool BF16> struct Raw4;
+template <> struct Raw4<true> {
+    using T = u32x2;
+    static __device__ __forceinline__ T load(const void* p, int64_t i) {
+        return ld_stream(reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p) + i));
+    }
+    static __device__ __forceinline__ f32x4 widen(T w) {
+        return f32x4{bf16_to_f32(w.x & 0xFFFFu), bf16_to_f32(w.x >> 16), bf16_to_f32(w.y & 0xFFFFu),
+                     bf16_to_f32(w.y >> 16)};
+    }
+};
+template <> struct Raw4<false> {
+    using T = f32x4;
+    static __device__ __forceinline__ T load(const void* p, int64_t i) {
+        return ld_stream(reinterpret_cast<const f32x4*>(static_cast<const float*>(p) + i));
+    }
+    static __device__ __forceinline__ f32x4 widen(T w) { return w; }
+};
+
+template <bool VEC, bool BF16, bool OVERWRITE>
+__global__ __launch_bounds__(kReduceBlock) void reduce_chunks_kernel(float* __restrict__ acc, const ChunkBatch b,
+                                                                     int64_t n) {
+    constexpr int64_t kGroup = kReduceBlock * 4;
+    const int64_t tile = (int64_t)blockIdx.x * kGroup * kReduceGroups;
+    const int64_t lane0 = tile + threadIdx.x * 4;
+    const int count = b.count;
+    if (VEC && tile + kGroup * kReduceGroups <= n) {   // whole tile in range
+        using R = Raw4<BF16>;
+        f32x4 r[kReduceGroups];
+        typename R::T g[kReduceGroups][kReduceMaxChunks];
+#pragma unroll
+        for (int q = 0; q < kReduceGroups; ++q) {
+            r[q] = OVERWRITE ? f32x4{0.0f, 0.0f, 0.0f, 0.0f}
+                             : ld_stream(reinterpret_cast<const f32x4*>(acc + lane0 + q * kGroup));
+#pragma unroll
+            for (int k = 0; k < kReduceMaxChunks; ++k)
+                if (k < count) g[q][k] = R::load(b.chunk[k], lane0 + q * kGroup);
+        }
+#pragma unroll
+        for (int q = 0; q < kReduceGroups; ++q) {
+#pragma unroll
+            for (int k = 0; k < kReduceMaxChunks; ++k) {
+                if (k < count) {
+                    const f32x4 x = R::widen(g[q][k]);
+                    // the first chunk of an overwriting batch is a copy (keeps -0.0)
+                    r[q] = (OVERWRITE && k == 0) ? x
+                                                 : f32x4{r[q].x + x.x, r[q].y + x.y, r[q].z + x.z, r[q].w + x.w};
+                }
+            }
+            st_stream(reinterpret_cast<f32x4*>(acc + lane0 + q * kGroup), r[q]);
+        }
+        return;
+    }
+    // ragged tile (or a misaligned buffer): element by element
+#pragma unroll
+    for (int q = 0; q < kReduceGroups; ++q) {
+        const int64_t first = lane0 + q * kGroup;
+        const int64_t last = first + 4 < n ? first + 4 : n;
+        for (int64_t i = first; i < last; ++i) {
+            float r = OVERWRITE ? 0.0f : acc[i];
+            for (int k = 0; k < count; ++k) {
+                const float g = load1<BF16>(b.chunk[k], i);
+                r = (OVERWRITE && k == 0) ? g : r + g;
+            }
+            acc[i] = r;
+        }
+    }
+}
+
+template <bool VEC, bool BF16, bool OVERWRITE>
+hipError_t launch_reduce(float* acc, const ChunkBatch& b, int64_t n, hipStream_t stream) {
+    const int64_t per = (int64_t)kReduceBlock * 4 * kReduceGroups;
+    const int64_t blocks = (n + per - 1) / per;
+    if (blocks > (int64_t)UINT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((reduce_chunks_kernel<VEC, BF16, OVERWRITE>), dim3((unsigned)blocks), dim3(kReduceBlock), 0,
+                       stream, acc, b, n);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_reduce_chunks(float* acc, const ChunkBatch& b, int grad_bf16, int64_t n, int overwrite,
+                                bool vec_ok, hipStream_t stream) {
+    if (vec_ok) {
+        if (grad_bf16) return overwrite ? launch_reduce<true, true, true>(acc, b, n, stream)
+                                        : launch_reduce<true, true, false>(acc, b, n, stream);
+        return overwrite ? launch_reduce<true, false, true>(acc, b, n, stream)
+                         : launch_reduce<true, false, false>(acc, b, n, stream);
+    }
+    if (grad_bf16) return overwrite ? launch_reduce<false, true, true>(acc, b, n, stream)
+                                    : launch_reduce<false, true, false>(acc, b, n, stream);
+    return overwrite ? launch_reduce<false, false, true>(acc, b, n, stream)
+                     : launch_reduce<false, false, false>(acc, b, n, stream);
+}
+
+}  // namespace zs

@@ -84,6 +84,32 @@ int32_t grad_accum(float* acc, const void* grad, int32_t grad_dtype, int64_t n, 
                                             as_stream(hip_stream)));
 }
 
+int32_t grad_reduce_chunks(float* acc, const void* const* chunks, int32_t count, int32_t grad_dtype, int64_t n,
+                           int32_t overwrite, void* hip_stream) {
+    if (!dtype_ok(grad_dtype) || !size_ok(n, 4) || count < 0) return ZS_EINVAL;
+    if (n == 0) return ZS_OK;
+    if (count == 0) return overwrite ? ZS_EINVAL : ZS_OK;
+    if (acc == nullptr || chunks == nullptr || !aligned(acc, 4)) return ZS_EINVAL;
+    const int64_t gsz = elem_size(grad_dtype);
+    bool vec = aligned(acc, 16);
+    for (int32_t k = 0; k < count; ++k) {
+        if (chunks[k] == nullptr || !aligned(chunks[k], (uintptr_t)gsz)) return ZS_EINVAL;
+        if (overlap(acc, n * 4, chunks[k], n * gsz)) return ZS_EOVERLAP;
+        vec = vec && aligned(chunks[k], 16);
+    }
+    for (int32_t k0 = 0; k0 < count; k0 += zs::kReduceMaxChunks) {
+        zs::ChunkBatch b;
+        std::memset(&b, 0, sizeof(b));
+        b.count = count - k0 < zs::kReduceMaxChunks ? count - k0 : zs::kReduceMaxChunks;
+        for (int32_t k = 0; k < b.count; ++k) b.chunk[k] = chunks[k0 + k];
+        const int32_t rc = hip_status(zs::launch_reduce_chunks(acc, b, grad_dtype == ZS_BF16, n,
+                                                               (k0 == 0 && overwrite) ? 1 : 0, vec,
+                                                               as_stream(hip_stream)));
+        if (rc != ZS_OK) return rc;
+    }
+    return ZS_OK;
+}
+
 int64_t grad_norm_sq_workspace_bytes(int64_t n) {
     if (n < 0) return -1;
     return zs::norm_partial_blocks(n) * (int64_t)sizeof(double);

@@ -74,6 +74,16 @@ hipError_t launch_grad_accum_norm_sq(float* acc, const void* grad, int grad_bf16
 hipError_t launch_grad_norm_sq(const float* grad, int64_t n, float scale, double* out,
                                double* partials, bool vec_ok, hipStream_t stream);
 
+// Up to kReduceMaxChunks rank chunks summed per launch (pointers travel in
+// the kernel arguments).
+constexpr int kReduceMaxChunks = 16;
+struct ChunkBatch {
+    const void* chunk[kReduceMaxChunks];
+    int32_t count;
+};
+hipError_t launch_reduce_chunks(float* acc, const ChunkBatch& b, int grad_bf16, int64_t n, int overwrite,
+                                bool vec_ok, hipStream_t stream);
+
 // One launch of the flatten/unflatten copy covers up to kFlatMaxTensors
 // tensors (the table travels in the kernel arguments; no device allocation).
 // The workgroup table is 32-bit so a workgroup finds its tensor from two

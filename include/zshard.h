@@ -144,6 +144,25 @@ int32_t grad_accum(float* acc, const void* grad, int32_t grad_dtype, int64_t n,
                    int32_t overwrite, void* hip_stream);
 
 /*
+ * grad_reduce_chunks — the receiving side of a reduce-scatter on one GPU:
+ * this rank's fp32 shard is the sum, in rank order, of the N ranks' chunks
+ * for it.  [ZeRO page] §"ZeRO-2" reduce_gradients (reduce_scatter_tensor with
+ * SUM, then the division by the world size, which this library applies
+ * later as part of zs_adamw.grad_scale) and [Memory page] §FlatParameter
+ * (the reduce-scatter runs with reduce_dtype fp32).
+ * acc = (overwrite ? widen(chunks[0]) : fl32(acc + widen(chunks[0]))), then
+ * acc = fl32(acc + widen(chunks[k])) for k = 1 .. count-1: the same left fold,
+ * bit for bit, as one grad_accum call per chunk, in one pass per 16 chunks.
+ * acc: device fp32[n], read-write; chunks: host array of `count` device
+ * pointers, each [n] of grad_dtype, read (they may alias each other, not
+ * acc).  count == 0 with overwrite == 0 is a no-op.
+ * Errors: ZS_EINVAL (count < 0, count == 0 with overwrite, null/misaligned
+ * pointer, dtype), ZS_EOVERLAP (a chunk overlaps acc), ZS_EHIP.
+ */
+int32_t grad_reduce_chunks(float* acc, const void* const* chunks, int32_t count, int32_t grad_dtype, int64_t n,
+                           int32_t overwrite, void* hip_stream);
+
+/*
  * grad_norm_sq_workspace_bytes — bytes of device workspace grad_norm_sq
  * needs for n elements (0 for n == 0; -1 for n < 0).  Host only.
  */

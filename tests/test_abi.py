@@ -134,6 +134,30 @@ def test_grad_norm_sq_rejects():
     assert L.grad_norm_sq(FAKE, n, 1.0, out, FAKE + 64, need, None) == B.ZS_EOVERLAP
 
 
+def test_grad_reduce_chunks_rejects():
+    L = zs.lib()
+    n = 1 << 16
+    acc = FAKE
+    chunks = (ctypes.c_void_p * 3)(FAKE + 2**30, FAKE + 2**31, FAKE + 2**32)
+    call = lambda **k: L.grad_reduce_chunks(k.get("acc", acc), k.get("chunks", chunks), k.get("count", 3),
+                                            k.get("dt", B.ZS_BF16), k.get("n", n), k.get("ow", 1), None)
+    assert call(count=-1) == B.ZS_EINVAL
+    assert call(count=0, ow=1) == B.ZS_EINVAL
+    assert call(count=0, ow=0) == B.ZS_OK                  # nothing to add
+    assert call(n=0) == B.ZS_OK
+    assert call(dt=9) == B.ZS_EINVAL
+    assert call(acc=0) == B.ZS_EINVAL
+    assert call(chunks=None) == B.ZS_EINVAL
+    bad = (ctypes.c_void_p * 3)(FAKE + 2**30, 0, FAKE + 2**32)
+    assert call(chunks=bad) == B.ZS_EINVAL
+    odd = (ctypes.c_void_p * 3)(FAKE + 2**30, FAKE + 2**31 + 1, FAKE + 2**32)
+    assert call(chunks=odd) == B.ZS_EINVAL                  # bf16 must be 2-byte aligned
+    over = (ctypes.c_void_p * 3)(FAKE + 2**30, FAKE + 1024, FAKE + 2**32)
+    assert call(chunks=over) == B.ZS_EOVERLAP               # a chunk inside acc
+    same = (ctypes.c_void_p * 3)(FAKE + 2**30, FAKE + 2**30, FAKE + 2**30)
+    assert call(chunks=same, n=-1) == B.ZS_EINVAL
+
+
 def test_grad_accum_norm_sq_rejects():
     L = zs.lib()
     n = 1 << 20

@@ -349,3 +349,60 @@ def test_flat_pack_misaligned_views():
     zs.flat_pack(views, flat, T + 5)
     want = oracle.flat_pack([to_np(v) for v in views], oracle.BF16, oracle.F32, T + 5)
     assert bits_equal(to_np(flat), want)
+
+
+# ---------------------------------------------------------------------------
+# grad_reduce_chunks (reduce-scatter arithmetic) and the all-gather placement
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N", [1, 2, 7, 16, 17, 64])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("overwrite", [True, False])
+@pytest.mark.parametrize("offset", [0, 1])
+def test_grad_reduce_chunks_bit_exact(N, dtype, overwrite, offset):
+    """N rank chunks summed in rank order equal N sequential accumulations
+    (the oracle's), bit for bit, with one chunk aliased twice."""
+    n = 4097 if N > 16 else 100_003
+    print(f"grad_reduce_chunks N={N} dtype={dtype} overwrite={overwrite} offset={offset} n={n}", flush=True)
+    rng = np.random.default_rng(N * 7 + offset + 3 * overwrite)
+    code = oracle.BF16 if dtype == "bf16" else oracle.F32
+    chunks = []
+    for _ in range(N):
+        x = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+        chunks.append(oracle.bf16_rne(x) if dtype == "bf16" else x)
+    if N > 2:
+        chunks[2] = chunks[0]                       # aliasing is allowed
+    acc0 = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    ref = acc0.copy()
+    for k, c in enumerate(chunks):
+        oracle.grad_accum(ref, c, code, overwrite=(overwrite and k == 0))
+    acc, acc_whole = dev_buf(acc0, offset)
+    dev_chunks = [dev_buf(c, offset, bf16=(dtype == "bf16"))[0] for c in chunks]
+    if N > 2:
+        dev_chunks[2] = dev_chunks[0]
+    zs.grad_reduce_chunks(acc, dev_chunks, overwrite)
+    assert bits_equal(to_np(acc), ref)
+    assert canary_ok(acc_whole, offset, n)
+
+
+def test_allgather_placement_roundtrip():
+    """The all-gather's placement: the N ranks' bf16 chunks packed in rank
+    order rebuild the FlatParameter bit for bit, and unflatten to the unit's
+    tensors (a 70B-style block scaled down, world 64)."""
+    import workloads
+    shapes = workloads.block70b_tensor_shapes(hidden=512, ffn=1792, q_heads=64, kv_heads=8, head_dim=8)
+    rng = np.random.default_rng(21)
+    params = [oracle.bf16_rne(rng.uniform(-0.1, 0.1, s).astype(np.float32)).reshape(s) for _, s in shapes]
+    total = sum(p.size for p in params)
+    world = 64
+    chunk, _, _, padded = zs.zero_shard_range(total, world, 0)
+    flat_ref = oracle.flat_pack(params, oracle.BF16, oracle.BF16, padded)
+    # each rank's chunk, as it would arrive from that rank
+    chunks = [from_np(flat_ref[r * chunk:(r + 1) * chunk].copy(), bf16=True) for r in range(world)]
+    flat = torch.empty(padded, dtype=torch.bfloat16, device="cuda")
+    zs.flat_pack(chunks, flat, padded)
+    assert bits_equal(to_np(flat), flat_ref)
+    outs = [torch.empty(s, dtype=torch.bfloat16, device="cuda") for _, s in shapes]
+    zs.flat_unpack(flat, outs)
+    for o, p in zip(outs, params):
+        assert bits_equal(to_np(o).reshape(-1), p.reshape(-1))
