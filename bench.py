@@ -163,6 +163,22 @@ def run_gpu(w, steps: int, warmup: int):
         torch.cuda.synchronize()
         reduce_ms = r0.elapsed_time(r1) / 3
 
+    # outside the step: the variant with no fp32 master (24 B/element), on the
+    # same buffers (state after the timed steps)
+    no_master_ms = None
+    if param is not None:
+        n0, n1 = ev(), ev()
+        hp = zs.AdamWConfig(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
+                            grad_scale=w.grad_scale, step=t + 1)
+        zs.adamw_step_no_master(hp, param, exp_avg, exp_avg_sq, acc)
+        n0.record()
+        for k in range(3):
+            hp.step = t + 2 + k
+            zs.adamw_step_no_master(hp, param, exp_avg, exp_avg_sq, acc)
+        n1.record()
+        torch.cuda.synchronize()
+        no_master_ms = n0.elapsed_time(n1) / 3
+
     # achievable-bandwidth reference: a plain device copy of 4 GiB (also the
     # calibration kernel for the HBM byte counters)
     src = torch.empty(1 << 30, dtype=torch.float32, device=dev)
@@ -179,7 +195,7 @@ def run_gpu(w, steps: int, warmup: int):
     copy_gbps = 2 * src.numel() * 4 / (copy_ms * 1e-3) / 1e9
     del src, dst
     return {"n": n, "wall_s": wall, "accum_ms": acc_ms, "last_ms": last_ms, "adamw_ms": adamw_ms,
-            "reduce_ms": reduce_ms, "chunks": len(grads),
+            "reduce_ms": reduce_ms, "chunks": len(grads), "no_master_ms": no_master_ms,
             "copy_gbps": copy_gbps}
 
 
@@ -325,6 +341,9 @@ def main():
                      "algorithmic_bytes": adamw_bytes, "launch_ms": r["adamw_ms"]},
         "cpu_baseline": cpu,
         "flat_unit": flat,
+        "adamw_step_no_master": None if r["no_master_ms"] is None else {
+            "ms": r["no_master_ms"], "bytes_per_elem": 24,
+            "gbps": 24 * n / (r["no_master_ms"] * 1e-3) / 1e9},
         "reduce_chunks": None if r["reduce_ms"] is None else {
             "chunks": r["chunks"], "ms": r["reduce_ms"],
             "gbps": (r["chunks"] * (2 if w.grad_dtype == "bf16" else 4) + 4) * n / (r["reduce_ms"] * 1e-3) / 1e9},

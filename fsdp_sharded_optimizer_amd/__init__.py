@@ -10,6 +10,7 @@ The Python names mirror the C ABI in include/zshard.h:
     grad_accum_norm_sq(acc, grad, overwrite, grad_scale, out, workspace=None)
     grad_norm_sq(grad, grad_scale, out, workspace=None)
     adamw_step(hp, master, exp_avg, exp_avg_sq, grad, param_bf16=None, norm_sq=None)
+    adamw_step_no_master(hp, param_bf16, exp_avg, exp_avg_sq, grad, norm_sq=None)
 
 All device work runs in the library's gfx950 HIP kernels on the current
 torch stream; torch supplies device memory and the stream only.
@@ -20,6 +21,7 @@ from ._binding import (  # noqa: F401
     AdamWConfig,
     ZShardError,
     adamw_step,
+    adamw_step_no_master,
     flat_pack,
     flat_unpack,
     grad_accum,

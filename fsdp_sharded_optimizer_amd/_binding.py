@@ -29,7 +29,7 @@ ZS_EHIP = -4
 EXPORTS = (
     "zero_shard_range", "flat_pack", "flat_unpack", "grad_accum", "grad_reduce_chunks",
     "grad_norm_sq_workspace_bytes", "grad_norm_sq", "grad_accum_norm_sq_workspace_bytes",
-    "grad_accum_norm_sq", "adamw_step",
+    "grad_accum_norm_sq", "adamw_step", "adamw_step_no_master",
     "zs_strerror", "zs_last_hip_error",
 )
 
@@ -112,6 +112,8 @@ def lib() -> ctypes.CDLL:
         L.grad_accum_norm_sq.restype = I32
         L.adamw_step.argtypes = [ctypes.POINTER(AdamW), P, P, P, P, P, I64, P, P]
         L.adamw_step.restype = I32
+        L.adamw_step_no_master.argtypes = [ctypes.POINTER(AdamW), P, P, P, P, I64, P, P]
+        L.adamw_step_no_master.restype = I32
         L.zs_strerror.argtypes = [I32]
         L.zs_strerror.restype = ctypes.c_char_p
         L.zs_last_hip_error.argtypes = []
@@ -291,3 +293,20 @@ def adamw_step(hp: AdamWConfig, master: torch.Tensor, exp_avg: torch.Tensor, exp
         ctypes.byref(c), _dev(master, "master", torch.float32), _dev(exp_avg, "exp_avg", torch.float32),
         _dev(exp_avg_sq, "exp_avg_sq", torch.float32), _dev(grad, "grad", torch.float32),
         _dev(param_bf16, "param_bf16", torch.bfloat16), n, _dev(norm_sq, "norm_sq"), _stream(stream)))
+
+
+def adamw_step_no_master(hp: AdamWConfig, param_bf16: torch.Tensor, exp_avg: torch.Tensor,
+                         exp_avg_sq: torch.Tensor, grad: torch.Tensor, norm_sq: Optional[torch.Tensor] = None,
+                         stream=None) -> None:
+    """AdamW on a bf16 parameter shard with no fp32 master (in place)."""
+    n = param_bf16.numel()
+    for t, nm in ((exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq"), (grad, "grad")):
+        if t.numel() != n:
+            raise ValueError(f"adamw_step_no_master: {nm} size mismatch")
+    if norm_sq is not None and norm_sq.dtype != torch.float64:
+        raise TypeError("adamw_step_no_master: norm_sq must be float64")
+    c = hp.c_struct()
+    _check("adamw_step_no_master", lib().adamw_step_no_master(
+        ctypes.byref(c), _dev(param_bf16, "param_bf16", torch.bfloat16), _dev(exp_avg, "exp_avg", torch.float32),
+        _dev(exp_avg_sq, "exp_avg_sq", torch.float32), _dev(grad, "grad", torch.float32), n,
+        _dev(norm_sq, "norm_sq"), _stream(stream)))

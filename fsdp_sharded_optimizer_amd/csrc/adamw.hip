@@ -71,7 +71,9 @@ __device__ __forceinline__ bool clip_coef(const AdamwArgs& a, float& coef) {
 constexpr int kVecBlock = 64;
 constexpr unsigned kVecLdsReserve = 16384;
 
-template <int VEC, bool BF16, int BS>
+// NO_MASTER: the bf16 parameter is read, updated and rounded back in place
+// (no fp32 master): 24 B/element (R g, m, v 12 + p 2; W m, v 8 + p 2).
+template <int VEC, bool BF16, int BS, bool NO_MASTER = false>
 __global__ __launch_bounds__(BS) void adamw_kernel(const AdamwArgs a) {
     const int64_t n = a.n;
     const int64_t first = ((int64_t)blockIdx.x * BS + threadIdx.x) * VEC;
@@ -82,7 +84,14 @@ __global__ __launch_bounds__(BS) void adamw_kernel(const AdamwArgs a) {
         // The loads are issued before the clip coefficient is resolved, so
         // the latency of the norm's read overlaps with them.
         const f32x4 g4 = ld_stream(reinterpret_cast<const f32x4*>(a.grad + first));
-        const f32x4 p4 = ld_stream(reinterpret_cast<const f32x4*>(a.master + first));
+        f32x4 p4;
+        if (NO_MASTER) {
+            const u32x2 w = ld_stream(reinterpret_cast<const u32x2*>(a.param_bf16 + first));
+            p4 = f32x4{bf16_to_f32(w.x & 0xFFFFu), bf16_to_f32(w.x >> 16), bf16_to_f32(w.y & 0xFFFFu),
+                       bf16_to_f32(w.y >> 16)};
+        } else {
+            p4 = ld_stream(reinterpret_cast<const f32x4*>(a.master + first));
+        }
         const f32x4 m4 = ld_stream(reinterpret_cast<const f32x4*>(a.exp_avg + first));
         const f32x4 v4 = ld_stream(reinterpret_cast<const f32x4*>(a.exp_avg_sq + first));
         float coef;
@@ -93,10 +102,11 @@ __global__ __launch_bounds__(BS) void adamw_kernel(const AdamwArgs a) {
         float vs[4] = {v4.x, v4.y, v4.z, v4.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) adamw_elem(a, coef, gs[j], ps[j], ms[j], vs[j]);
-        st_stream(reinterpret_cast<f32x4*>(a.master + first), f32x4{ps[0], ps[1], ps[2], ps[3]});
+        if (!NO_MASTER)
+            st_stream(reinterpret_cast<f32x4*>(a.master + first), f32x4{ps[0], ps[1], ps[2], ps[3]});
         st_stream(reinterpret_cast<f32x4*>(a.exp_avg + first), f32x4{ms[0], ms[1], ms[2], ms[3]});
         st_stream(reinterpret_cast<f32x4*>(a.exp_avg_sq + first), f32x4{vs[0], vs[1], vs[2], vs[3]});
-        if (BF16)
+        if (BF16 || NO_MASTER)
             st_stream(reinterpret_cast<u32x2*>(a.param_bf16 + first),
                       u32x2{pack_bf16x2(ps[0], ps[1]), pack_bf16x2(ps[2], ps[3])});
         return;
@@ -106,25 +116,31 @@ __global__ __launch_bounds__(BS) void adamw_kernel(const AdamwArgs a) {
     if (!clip_coef(a, coef)) return;
     const int64_t last = first + VEC < n ? first + VEC : n;
     for (int64_t i = first; i < last; ++i) {
-        float p = a.master[i], m = a.exp_avg[i], v = a.exp_avg_sq[i];
+        float p = NO_MASTER ? bf16_to_f32(a.param_bf16[i]) : a.master[i];
+        float m = a.exp_avg[i], v = a.exp_avg_sq[i];
         adamw_elem(a, coef, a.grad[i], p, m, v);
-        a.master[i] = p;
+        if (!NO_MASTER) a.master[i] = p;
         a.exp_avg[i] = m;
         a.exp_avg_sq[i] = v;
-        if (BF16) a.param_bf16[i] = (uint16_t)f32_to_bf16_rne(p);
+        if (BF16 || NO_MASTER) a.param_bf16[i] = (uint16_t)f32_to_bf16_rne(p);
     }
 }
 
-template <int VEC, bool BF16, int BS>
+template <int VEC, bool BF16, int BS, bool NO_MASTER = false>
 hipError_t launch(const AdamwArgs& a, unsigned lds, hipStream_t stream) {
     const int64_t threads = (a.n + VEC - 1) / VEC;
     const int64_t blocks = (threads + BS - 1) / BS;
     if (blocks > (int64_t)UINT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((adamw_kernel<VEC, BF16, BS>), dim3((unsigned)blocks), dim3(BS), lds, stream, a);
+    hipLaunchKernelGGL((adamw_kernel<VEC, BF16, BS, NO_MASTER>), dim3((unsigned)blocks), dim3(BS), lds, stream, a);
     return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_adamw_no_master(const AdamwArgs& a, bool vec_ok, hipStream_t stream) {
+    if (vec_ok) return launch<4, true, kVecBlock, true>(a, kVecLdsReserve, stream);
+    return launch<1, true, kBlock, true>(a, 0, stream);
+}
 
 hipError_t launch_adamw(const AdamwArgs& a, bool vec_ok, hipStream_t stream) {
     const bool bf16 = a.param_bf16 != nullptr;

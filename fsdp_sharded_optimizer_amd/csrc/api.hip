@@ -161,9 +161,7 @@ int32_t grad_accum_norm_sq(float* acc, const void* grad, int32_t grad_dtype, int
                                                     as_stream(hip_stream)));
 }
 
-int32_t adamw_step(const zs_adamw* hp, float* master, float* exp_avg, float* exp_avg_sq,
-                   const float* grad, uint16_t* param_bf16, int64_t n, const double* norm_sq_dev,
-                   void* hip_stream) {
+static int32_t adamw_check_hp(const zs_adamw* hp, int64_t n, const double* norm_sq_dev) {
     if (hp == nullptr || !size_ok(n, 4)) return ZS_EINVAL;
     if (hp->step < 1) return ZS_EINVAL;
     if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0) || !(hp->beta2 >= 0.0 && hp->beta2 < 1.0))
@@ -174,26 +172,16 @@ int32_t adamw_step(const zs_adamw* hp, float* master, float* exp_avg, float* exp
     if (!(hp->grad_scale > 0.0) || !std::isfinite(hp->grad_scale)) return ZS_EINVAL;
     if (std::isnan(hp->max_norm) || hp->extra_norm_sq < 0.0) return ZS_EINVAL;
     if (norm_sq_dev != nullptr && !aligned(norm_sq_dev, 8)) return ZS_EINVAL;
-    if (n == 0) return ZS_OK;
-    if (master == nullptr || exp_avg == nullptr || exp_avg_sq == nullptr || grad == nullptr)
-        return ZS_EINVAL;
-    if (!aligned(master, 4) || !aligned(exp_avg, 4) || !aligned(exp_avg_sq, 4) || !aligned(grad, 4) ||
-        (param_bf16 != nullptr && !aligned(param_bf16, 2)))
-        return ZS_EINVAL;
-    const void* bufs[5] = {master, exp_avg, exp_avg_sq, grad, param_bf16};
-    const int64_t bytes[5] = {n * 4, n * 4, n * 4, n * 4, param_bf16 ? n * 2 : 0};
-    for (int i = 0; i < 5; ++i) {
-        for (int j = i + 1; j < 5; ++j)
-            if (overlap(bufs[i], bytes[i], bufs[j], bytes[j])) return ZS_EOVERLAP;
-        if (norm_sq_dev != nullptr && i != 3 && overlap(bufs[i], bytes[i], norm_sq_dev, 8))
-            return ZS_EOVERLAP;
-    }
+    return ZS_OK;
+}
 
-    // host scalars: binary64, each rounded to binary32 once
+// host scalars: binary64, each rounded to binary32 once
+static zs::AdamwArgs adamw_scalars(const zs_adamw* hp, const double* norm_sq_dev) {
     const double t = (double)hp->step;
     const double bias_correction1 = 1.0 - std::pow(hp->beta1, t);
     const double bias_correction2 = 1.0 - std::pow(hp->beta2, t);
     zs::AdamwArgs a;
+    std::memset(&a, 0, sizeof(a));
     a.beta1 = (float)hp->beta1;
     a.beta2 = (float)hp->beta2;
     a.one_minus_beta1 = (float)(1.0 - hp->beta1);
@@ -207,6 +195,39 @@ int32_t adamw_step(const zs_adamw* hp, float* master, float* exp_avg, float* exp
     a.max_norm = hp->max_norm;
     a.extra_norm_sq = hp->extra_norm_sq;
     a.norm_sq = norm_sq_dev;
+    return a;
+}
+
+// the five buffers (any may be absent: bytes 0) pairwise disjoint, and none
+// that is written overlapping the norm
+static int32_t adamw_check_overlap(const void* const* bufs, const int64_t* bytes, const bool* written,
+                                   const double* norm_sq_dev) {
+    for (int i = 0; i < 5; ++i) {
+        for (int j = i + 1; j < 5; ++j)
+            if (overlap(bufs[i], bytes[i], bufs[j], bytes[j])) return ZS_EOVERLAP;
+        if (norm_sq_dev != nullptr && written[i] && overlap(bufs[i], bytes[i], norm_sq_dev, 8))
+            return ZS_EOVERLAP;
+    }
+    return ZS_OK;
+}
+
+int32_t adamw_step(const zs_adamw* hp, float* master, float* exp_avg, float* exp_avg_sq,
+                   const float* grad, uint16_t* param_bf16, int64_t n, const double* norm_sq_dev,
+                   void* hip_stream) {
+    int32_t rc = adamw_check_hp(hp, n, norm_sq_dev);
+    if (rc != ZS_OK) return rc;
+    if (n == 0) return ZS_OK;
+    if (master == nullptr || exp_avg == nullptr || exp_avg_sq == nullptr || grad == nullptr)
+        return ZS_EINVAL;
+    if (!aligned(master, 4) || !aligned(exp_avg, 4) || !aligned(exp_avg_sq, 4) || !aligned(grad, 4) ||
+        (param_bf16 != nullptr && !aligned(param_bf16, 2)))
+        return ZS_EINVAL;
+    const void* bufs[5] = {master, exp_avg, exp_avg_sq, grad, param_bf16};
+    const int64_t bytes[5] = {n * 4, n * 4, n * 4, n * 4, param_bf16 ? n * 2 : 0};
+    const bool written[5] = {true, true, true, false, true};
+    rc = adamw_check_overlap(bufs, bytes, written, norm_sq_dev);
+    if (rc != ZS_OK) return rc;
+    zs::AdamwArgs a = adamw_scalars(hp, norm_sq_dev);
     a.master = master;
     a.exp_avg = exp_avg;
     a.exp_avg_sq = exp_avg_sq;
@@ -216,6 +237,31 @@ int32_t adamw_step(const zs_adamw* hp, float* master, float* exp_avg, float* exp
     const bool vec = aligned(master, 16) && aligned(exp_avg, 16) && aligned(exp_avg_sq, 16) &&
                      aligned(grad, 16) && (param_bf16 == nullptr || aligned(param_bf16, 16));
     return hip_status(zs::launch_adamw(a, vec, as_stream(hip_stream)));
+}
+
+int32_t adamw_step_no_master(const zs_adamw* hp, uint16_t* param_bf16, float* exp_avg, float* exp_avg_sq,
+                             const float* grad, int64_t n, const double* norm_sq_dev, void* hip_stream) {
+    int32_t rc = adamw_check_hp(hp, n, norm_sq_dev);
+    if (rc != ZS_OK) return rc;
+    if (n == 0) return ZS_OK;
+    if (param_bf16 == nullptr || exp_avg == nullptr || exp_avg_sq == nullptr || grad == nullptr)
+        return ZS_EINVAL;
+    if (!aligned(param_bf16, 2) || !aligned(exp_avg, 4) || !aligned(exp_avg_sq, 4) || !aligned(grad, 4))
+        return ZS_EINVAL;
+    const void* bufs[5] = {param_bf16, exp_avg, exp_avg_sq, grad, nullptr};
+    const int64_t bytes[5] = {n * 2, n * 4, n * 4, n * 4, 0};
+    const bool written[5] = {true, true, true, false, false};
+    rc = adamw_check_overlap(bufs, bytes, written, norm_sq_dev);
+    if (rc != ZS_OK) return rc;
+    zs::AdamwArgs a = adamw_scalars(hp, norm_sq_dev);
+    a.exp_avg = exp_avg;
+    a.exp_avg_sq = exp_avg_sq;
+    a.grad = grad;
+    a.param_bf16 = param_bf16;
+    a.n = n;
+    const bool vec = aligned(param_bf16, 16) && aligned(exp_avg, 16) && aligned(exp_avg_sq, 16) &&
+                     aligned(grad, 16);
+    return hip_status(zs::launch_adamw_no_master(a, vec, as_stream(hip_stream)));
 }
 
 // ---------------------------------------------------------------------------

@@ -64,6 +64,7 @@ struct AdamwArgs {
 
 // Launchers: enqueue on `stream`, return the hipError_t of the launch.
 hipError_t launch_adamw(const AdamwArgs& a, bool vec_ok, hipStream_t stream);
+hipError_t launch_adamw_no_master(const AdamwArgs& a, bool vec_ok, hipStream_t stream);
 hipError_t launch_grad_accum(float* acc, const void* grad, int grad_bf16, int64_t n,
                              int overwrite, bool vec_ok, hipStream_t stream);
 int64_t norm_partial_blocks(int64_t n);

@@ -246,6 +246,22 @@ int32_t adamw_step(const zs_adamw* hp, float* master, float* exp_avg, float* exp
                    const float* grad, uint16_t* param_bf16, int64_t n,
                    const double* norm_sq_dev, void* hip_stream);
 
+/*
+ * adamw_step_no_master — the same update with no fp32 master: the bf16
+ * parameter shard is read, updated and rounded back in place.
+ * [ZeRO page] §"ZeRO-3: 切分参数", ZeRO3Optimizer.step (the update is added
+ * straight into the low-precision parameter chunk).  Per element:
+ * p = widen(param_bf16); m, v, den and the update as in adamw_step;
+ * param_bf16 = bf16_rne(fl(fl(p*(1-lr*wd)) - update)).  Saves 4 B of state
+ * and 6 B of traffic per element, but an update smaller than half a bf16
+ * ulp of the parameter is lost every step (the stall an fp32 master avoids).
+ * param_bf16: device bf16[n], read-write; exp_avg, exp_avg_sq: device
+ * fp32[n], read-write; grad: device fp32[n], read; norm_sq_dev as in
+ * adamw_step.  Errors: as adamw_step.
+ */
+int32_t adamw_step_no_master(const zs_adamw* hp, uint16_t* param_bf16, float* exp_avg, float* exp_avg_sq,
+                             const float* grad, int64_t n, const double* norm_sq_dev, void* hip_stream);
+
 /* Static description of a return code. */
 const char* zs_strerror(int32_t code);
 

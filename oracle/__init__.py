@@ -80,6 +80,8 @@ def _configure(L):
     L.orc_clip_coef.restype = ctypes.c_float
     L.orc_adamw_step.argtypes = [ctypes.POINTER(AdamWHp), P, P, P, P, P, I64, P]
     L.orc_adamw_step.restype = ctypes.c_int
+    L.orc_adamw_step_no_master.argtypes = [ctypes.POINTER(AdamWHp), P, P, P, P, I64, P]
+    L.orc_adamw_step_no_master.restype = ctypes.c_int
     L.orc_num_threads.argtypes = []
     L.orc_num_threads.restype = ctypes.c_int
     return L
@@ -232,4 +234,20 @@ def adamw_step(hp: AdamWHp, master, exp_avg, exp_avg_sq, grad, param_bf16=None, 
                               ctypes.byref(nsq) if nsq is not None else None)
     if rc < 0:
         raise ValueError("adamw_step: invalid arguments")
+    return int(rc)
+
+
+def adamw_step_no_master(hp: AdamWHp, param_bf16, exp_avg, exp_avg_sq, grad, norm_sq=None) -> int:
+    """In-place step on a bf16 parameter with no fp32 master; 0 or 1 (skipped)."""
+    _need(param_bf16, np.uint16, "param_bf16")
+    for a, nm in ((exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq"), (grad, "grad")):
+        _need(a, np.float32, nm)
+        if a.size != param_bf16.size:
+            raise ValueError("adamw_step_no_master: size mismatch")
+    nsq = ctypes.c_double(float(norm_sq)) if norm_sq is not None else None
+    rc = lib().orc_adamw_step_no_master(ctypes.byref(hp), _ptr(param_bf16), _ptr(exp_avg), _ptr(exp_avg_sq),
+                                        _ptr(grad), param_bf16.size,
+                                        ctypes.byref(nsq) if nsq is not None else None)
+    if rc < 0:
+        raise ValueError("adamw_step_no_master: invalid arguments")
     return int(rc)

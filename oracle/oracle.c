@@ -373,6 +373,46 @@ int orc_adamw_step(const orc_adamw_hp* hp, float* master, float* exp_avg, float*
     return 0;
 }
 
+/*
+ * The same step with no fp32 master: the bf16 parameter itself is read,
+ * updated and rounded back ([ZeRO page] §"ZeRO-3: 切分参数", ZeRO3Optimizer.step
+ * adds the update straight into the low-precision parameter chunk).  Per
+ * element: p = widen(param_bf16[i]); m, v, den, u as in orc_adamw_step;
+ * param_bf16[i] = bf16_rne(fl(fl(p*decay) - u)).  An update smaller than
+ * half a bf16 ulp of p leaves the parameter unchanged: the stall an fp32
+ * master avoids.  Returns 0 (updated), 1 (skipped) or -1.
+ */
+int orc_adamw_step_no_master(const orc_adamw_hp* hp, uint16_t* param_bf16, float* exp_avg, float* exp_avg_sq,
+                             const float* grad, int64_t n, const double* norm_sq)
+{
+    orc_adamw_scalars s;
+    if (n < 0 || !param_bf16 || orc_adamw_scalars_make(hp, &s) != 0) return -1;
+    float coef = 1.0f;
+    if (norm_sq) {
+        double S = *norm_sq + hp->extra_norm_sq;
+        if (!isfinite(S)) return 1;
+        coef = orc_clip_coef(*norm_sq, hp->extra_norm_sq, hp->max_norm);
+    }
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        float g = grad[i] * s.grad_scale;
+        g = g * coef;
+        float m = exp_avg[i];
+        float v = exp_avg_sq[i];
+        float p = orc_bf16_widen(param_bf16[i]);
+        m = s.beta1 * m + s.one_minus_beta1 * g;
+        float gg = g * g;
+        v = s.beta2 * v + s.one_minus_beta2 * gg;
+        float den = sqrtf(v) / s.bias_correction2_sqrt + s.eps;
+        float u = (m / den) * s.step_size;
+        float pd = p * s.decay;
+        exp_avg[i] = m;
+        exp_avg_sq[i] = v;
+        param_bf16[i] = orc_bf16_rne(pd - u);
+    }
+    return 0;
+}
+
 /* Thread count OpenMP will use for the loops above (reported by the
  * CPU-baseline timing). */
 #ifdef _OPENMP

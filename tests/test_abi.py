@@ -108,6 +108,18 @@ def test_adamw_rejects_pointers():
     assert _adamw(_hp(), master=0, m=0, v=0, g=0, n=0) == B.ZS_OK
 
 
+def test_adamw_no_master_rejects():
+    L = zs.lib()
+    call = lambda hp=None, b=FAKE, m=FAKE + 2**20, v=FAKE + 2**21, g=FAKE + 2**22, n=1024, norm=0: \
+        L.adamw_step_no_master(ctypes.byref(hp or _hp()), b, m, v, g, n, norm, None)
+    assert call(hp=_hp(step=0)) == B.ZS_EINVAL
+    assert call(b=0) == B.ZS_EINVAL
+    assert call(b=FAKE + 1) == B.ZS_EINVAL
+    assert call(m=FAKE + 1024) == B.ZS_EOVERLAP                   # exp_avg inside the bf16 parameter
+    assert call(norm=FAKE + 2**21 + 64) == B.ZS_EOVERLAP          # norm inside exp_avg_sq
+    assert call(n=0) == B.ZS_OK
+
+
 def test_grad_accum_rejects():
     L = zs.lib()
     assert L.grad_accum(FAKE, FAKE + 2**20, 7, 16, 0, None) == B.ZS_EINVAL       # dtype

@@ -20,7 +20,8 @@ import tests.test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "oracle.c")
 
-# (name, text in oracle.c, replacement); each text occurs exactly once
+# (name, text in oracle.c, replacement); every occurrence is replaced (a slip
+# in arithmetic the two AdamW forms share is made in both)
 MUTANTS = [
     ("bf16: ties always round down",
      "if (lo > 0x8000u || (lo == 0x8000u && (hi & 1u))) hi += 1u;", "if (lo > 0x8000u) hi += 1u;"),
@@ -74,6 +75,8 @@ MUTANTS = [
     ("adamw: bf16 cast of the old master", "param_bf16[i] = orc_bf16_rne(p);",
      "param_bf16[i] = orc_bf16_rne(pd);"),
     ("adamw: non-finite norm not skipped", "if (!isfinite(S)) return 1;", ""),
+    ("no master: decay skipped", "param_bf16[i] = orc_bf16_rne(pd - u);", "param_bf16[i] = orc_bf16_rne(p - u);"),
+    ("no master: update dropped", "param_bf16[i] = orc_bf16_rne(pd - u);", "param_bf16[i] = orc_bf16_rne(pd);"),
 ]
 
 
@@ -105,6 +108,8 @@ def pin_suite():
         lambda: pins.test_adamw_float64_brute_force(orc),
         lambda: pins.test_nonfinite_norm_skips_update(orc),
         lambda: pins.test_adamw_rejects(orc),
+        lambda: pins.test_no_master_one_step_equals_master_recast(orc),
+        lambda: pins.test_no_master_stalls_below_half_an_ulp(orc),
     ]
     for seed in range(3):
         suite.append(lambda seed=seed: pins.test_flat_pack_matches_concatenate(orc, seed))
@@ -148,6 +153,6 @@ def test_unmutated_oracle_passes_every_fast_pin(workdir):
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_mutant_is_caught(workdir, name, old, new):
     source = open(SRC).read()
-    assert source.count(old) == 1, f"mutation site not unique or missing: {name}"
+    assert source.count(old) >= 1, f"mutation site missing: {name}"
     so = compile_variant(source.replace(old, new), workdir, str(abs(hash(name))))
     assert failures(so) > 0, f"no pin catches: {name}"

@@ -552,3 +552,53 @@ def test_adamw_rejects(orc):
                 dict(wd=-0.1), dict(scale=0.0)):
         with pytest.raises(ValueError):
             oracle.adamw_step(hp(**bad), p, m, v, np.zeros(4, np.float32))
+
+
+# ---------------------------------------------------------------------------
+# the step with no fp32 master (the ZeRO page's ZeRO-3 listing)
+# ---------------------------------------------------------------------------
+
+def test_no_master_one_step_equals_master_recast(orc):
+    """From master = widen(param) the two forms compute the same fp32 value;
+    the no-master form's parameter is that value's bf16 re-cast.  The second
+    case decays hard (lr*wd = 0.05) so a dropped or misplaced decay shows
+    through the bf16 rounding; widen(param) is checked against a manual
+    (1 - lr wd) p - u to a few bf16 ulps."""
+    rng = np.random.default_rng(31)
+    n = 4099
+    b0 = oracle.bf16_rne(rng.uniform(-0.1, 0.1, n).astype(np.float32))
+    g = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    for lr, wd in ((3e-4, 0.1), (1e-2, 5.0)):
+        H = hp(lr=lr, beta1=0.9, beta2=0.95, wd=wd, scale=1 / 8)
+        master = oracle.bf16_widen(b0).copy()
+        m1, v1, b1 = np.zeros(n, np.float32), np.zeros(n, np.float32), b0.copy()
+        oracle.adamw_step(H, master, m1, v1, g, b1)
+        b2, m2, v2 = b0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+        oracle.adamw_step_no_master(H, b2, m2, v2, g)
+        assert np.array_equal(b1, b2) and np.array_equal(m1, m2) and np.array_equal(v1, v2)
+        p0 = oracle.bf16_widen(b0).astype(np.float64)
+        gd = g.astype(np.float64) / 8
+        want = p0 * (1 - lr * wd) - lr * gd / (np.abs(gd) + 1e-8)
+        ulp = np.abs(want) * 2.0**-7 + 1e-30
+        assert np.all(np.abs(oracle.bf16_widen(b2) - want) <= ulp)
+
+
+def test_no_master_stalls_below_half_an_ulp(orc):
+    """Worked by hand: 0.1 rounds to bf16 0x3DCD; its ulp is 2^-11 =
+    4.8828125e-4.  With constant g (wd = 0) every step moves by lr in real
+    arithmetic.  lr = 1e-4 is under half an ulp: the bf16 parameter never
+    moves (the fp32 master moves 10 lr in 10 steps).  lr = 3e-4 is over
+    half an ulp: the parameter moves a whole ulp each step."""
+    n = 64
+    g = np.full(n, 2e-3, np.float32)
+    for lr, want in ((1e-4, 0x3DCD), (3e-4, 0x3DCD - 10)):
+        b = np.full(n, 0x3DCD, np.uint16)
+        m, v = np.zeros(n, np.float32), np.zeros(n, np.float32)
+        master = oracle.bf16_widen(b).copy()
+        mm, vv = np.zeros(n, np.float32), np.zeros(n, np.float32)
+        for t in range(1, 11):
+            H = hp(lr=lr, beta1=0.9, beta2=0.999, step=t)
+            oracle.adamw_step_no_master(H, b, m, v, g)
+            oracle.adamw_step(H, master, mm, vv, g)
+        assert np.all(b == want), (lr, hex(int(b[0])))
+        assert np.allclose(master, oracle.bf16_widen(np.full(n, 0x3DCD, np.uint16)) - 10 * lr, rtol=0, atol=1e-6)
