@@ -232,6 +232,67 @@ def run_flat(w, reps: int = 10):
             "pack_gbps": bytes_ / (pack_ms * 1e-3) / 1e9, "unpack_gbps": bytes_ / (unpack_ms * 1e-3) / 1e9}
 
 
+def run_zero1_flow(w, shapes, reps: int = 3):
+    """The ZeRO page's ZeRO-1 flow at the same model size: the full fp32
+    gradient resident as one flat buffer, this rank's adam_update on its
+    slice writing its chunk of the gathered update (24 B per shard element),
+    and flat_apply_update of the whole gathered update into every parameter
+    tensor of the model: bf16 parameters (8 B per model element) and fp32
+    parameters (12 B).  Values are synthetic; the timing has no data
+    dependence."""
+    import torch
+    import fsdp_sharded_optimizer_amd as zs
+
+    dev = torch.device("cuda", 0)
+    chunk, start, end, padded = zs.zero_shard_range(w.total, w.world, w.rank)
+    n = end - start
+    flat_grad = torch.empty(padded, dtype=torch.float32, device=dev).normal_(0.0, 1e-3)
+    gathered = torch.empty(padded, dtype=torch.float32, device=dev).normal_(0.0, 1e-5)
+    m = torch.zeros(n, dtype=torch.float32, device=dev)
+    v = torch.zeros(n, dtype=torch.float32, device=dev)
+    mine = gathered[w.rank * chunk:w.rank * chunk + n]
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        fn(0)
+        e0, e1 = ev(), ev()
+        e0.record()
+        for k in range(reps):
+            fn(k + 1)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def update(k):
+        hp = zs.AdamWConfig(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=0.0,
+                            grad_scale=1.0 / w.world, step=k + 1)
+        zs.adam_update(hp, m, v, flat_grad[start:end], mine)
+
+    upd_ms = timed(update)
+    del m, v, flat_grad
+    out = {"workload": f"{w.name} as ZeRO-1: full flat fp32 grad and gathered update of {w.total} elements, "
+                       f"rank {w.rank} of {w.world}",
+           "tensors": len(shapes),
+           "adam_update": {"ms": upd_ms, "elements": n, "bytes_per_elem": 24,
+                           "gbps": 24 * n / (upd_ms * 1e-3) / 1e9}}
+    from workloads import numel_of
+    for dtype, bpe, key in ((torch.bfloat16, 8, "apply_bf16"), (torch.float32, 12, "apply_f32")):
+        buf = torch.empty(w.total, dtype=dtype, device=dev).uniform_(-0.1, 0.1)
+        params, off = [], 0
+        for _, shp in shapes:
+            k = numel_of(shp)
+            params.append(buf[off:off + k].view(shp))
+            off += k
+        assert off == w.total
+        ms = timed(lambda k: zs.flat_apply_update(gathered, params))
+        assert bool(torch.isfinite(buf[:: 1 << 20]).all())
+        out[key] = {"ms": ms, "elements": w.total, "bytes_per_elem": bpe,
+                    "gbps": bpe * w.total / (ms * 1e-3) / 1e9}
+        del params, buf
+    del gathered, mine
+    return out
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline leg: the oracle as it stands on a bounded sample
 # ---------------------------------------------------------------------------
@@ -281,6 +342,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama7b_shard")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--no-zero1", action="store_true", help="skip the ZeRO-1 flow timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
 
@@ -304,6 +366,11 @@ def main():
         import torch
         torch.cuda.empty_cache()
         flat = run_flat(w)
+    zero1 = None
+    if w.name == "llama7b_shard" and not args.no_zero1:
+        import torch
+        torch.cuda.empty_cache()
+        zero1 = run_zero1_flow(w, workloads.LLAMA7B)
     bpe = step_bytes_per_elem(w)
     ms_per_step = r["wall_s"] * 1e3 / args.steps
     adamw_bytes = bpe["adamw_step"] * n
@@ -341,6 +408,7 @@ def main():
                      "algorithmic_bytes": adamw_bytes, "launch_ms": r["adamw_ms"]},
         "cpu_baseline": cpu,
         "flat_unit": flat,
+        "zero1_flow": zero1,
         "adamw_step_no_master": None if r["no_master_ms"] is None else {
             "ms": r["no_master_ms"], "bytes_per_elem": 24,
             "gbps": 24 * n / (r["no_master_ms"] * 1e-3) / 1e9},

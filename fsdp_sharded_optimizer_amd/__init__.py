@@ -11,6 +11,8 @@ The Python names mirror the C ABI in include/zshard.h:
     grad_norm_sq(grad, grad_scale, out, workspace=None)
     adamw_step(hp, master, exp_avg, exp_avg_sq, grad, param_bf16=None, norm_sq=None)
     adamw_step_no_master(hp, param_bf16, exp_avg, exp_avg_sq, grad, norm_sq=None)
+    adam_update(hp, exp_avg, exp_avg_sq, grad, update, norm_sq=None)
+    flat_apply_update(update, dst_tensors)
 
 All device work runs in the library's gfx950 HIP kernels on the current
 torch stream; torch supplies device memory and the stream only.
@@ -20,8 +22,10 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     AdamWConfig,
     ZShardError,
+    adam_update,
     adamw_step,
     adamw_step_no_master,
+    flat_apply_update,
     flat_pack,
     flat_unpack,
     grad_accum,

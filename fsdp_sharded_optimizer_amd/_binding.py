@@ -29,7 +29,7 @@ ZS_EHIP = -4
 EXPORTS = (
     "zero_shard_range", "flat_pack", "flat_unpack", "grad_accum", "grad_reduce_chunks",
     "grad_norm_sq_workspace_bytes", "grad_norm_sq", "grad_accum_norm_sq_workspace_bytes",
-    "grad_accum_norm_sq", "adamw_step", "adamw_step_no_master",
+    "grad_accum_norm_sq", "adamw_step", "adamw_step_no_master", "adam_update", "flat_apply_update",
     "zs_strerror", "zs_last_hip_error",
 )
 
@@ -114,6 +114,10 @@ def lib() -> ctypes.CDLL:
         L.adamw_step.restype = I32
         L.adamw_step_no_master.argtypes = [ctypes.POINTER(AdamW), P, P, P, P, I64, P, P]
         L.adamw_step_no_master.restype = I32
+        L.adam_update.argtypes = [ctypes.POINTER(AdamW), P, P, P, P, I64, P, P]
+        L.adam_update.restype = I32
+        L.flat_apply_update.argtypes = [P, ctypes.POINTER(Tensor), I32, I32, P]
+        L.flat_apply_update.restype = I32
         L.zs_strerror.argtypes = [I32]
         L.zs_strerror.restype = ctypes.c_char_p
         L.zs_last_hip_error.argtypes = []
@@ -205,6 +209,19 @@ def flat_unpack(flat: torch.Tensor, dst: Sequence[torch.Tensor], stream=None) ->
         raise ValueError("flat_unpack: destinations exceed the flat buffer")
     _check("flat_unpack", lib().flat_unpack(_dev(flat, "flat"), _dtype_code(flat), arr, len(dst), dt,
                                             _stream(stream)))
+
+
+def flat_apply_update(update: torch.Tensor, dst: Sequence[torch.Tensor], stream=None) -> None:
+    """dst[i].view(-1)[j] += update[o_i + j] in place (fp32 or bf16 tensors;
+    the update is fp32, its padding ignored)."""
+    arr, dt = _tensor_list(dst, "dst")
+    if dt is None:
+        dt = ZS_F32
+    total = sum(t.numel() for t in dst)
+    if total > update.numel():
+        raise ValueError("flat_apply_update: destinations exceed the update buffer")
+    _check("flat_apply_update", lib().flat_apply_update(_dev(update, "update", torch.float32), arr, len(dst), dt,
+                                                        _stream(stream)))
 
 
 def grad_accum(acc: torch.Tensor, grad: torch.Tensor, overwrite: bool, stream=None) -> None:
@@ -309,4 +326,21 @@ def adamw_step_no_master(hp: AdamWConfig, param_bf16: torch.Tensor, exp_avg: tor
     _check("adamw_step_no_master", lib().adamw_step_no_master(
         ctypes.byref(c), _dev(param_bf16, "param_bf16", torch.bfloat16), _dev(exp_avg, "exp_avg", torch.float32),
         _dev(exp_avg_sq, "exp_avg_sq", torch.float32), _dev(grad, "grad", torch.float32), n,
+        _dev(norm_sq, "norm_sq"), _stream(stream)))
+
+
+def adam_update(hp: AdamWConfig, exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor, grad: torch.Tensor,
+                update: torch.Tensor, norm_sq: Optional[torch.Tensor] = None, stream=None) -> None:
+    """ZeRO-1 form: Adam (weight_decay 0) moments in place, the update vector
+    -(lr/bc1) * m / den into ``update``."""
+    n = update.numel()
+    for t, nm in ((exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq"), (grad, "grad")):
+        if t.numel() != n:
+            raise ValueError(f"adam_update: {nm} size mismatch")
+    if norm_sq is not None and norm_sq.dtype != torch.float64:
+        raise TypeError("adam_update: norm_sq must be float64")
+    c = hp.c_struct()
+    _check("adam_update", lib().adam_update(
+        ctypes.byref(c), _dev(exp_avg, "exp_avg", torch.float32), _dev(exp_avg_sq, "exp_avg_sq", torch.float32),
+        _dev(grad, "grad", torch.float32), _dev(update, "update", torch.float32), n,
         _dev(norm_sq, "norm_sq"), _stream(stream)))

@@ -9,6 +9,11 @@
 // gfx950 vector rate at 8 TB/s, so the kernel is HBM-bound: the design goal
 // is deep memory-level parallelism and fully coalesced 128-bit accesses.
 //
+// Two more forms share the code: the bf16 parameter updated in place with no
+// master (the ZeRO page's ZeRO-3 step; 24 B/element), and the ZeRO-1 form
+// that writes the update vector -u instead of a parameter (Adam without
+// decay; R grad, m, v and W m, v, update: 24 B/element).
+//
 // Layout: every array is a flat 1-D fp32 (bf16) buffer; thread k of the grid
 // owns the 4 consecutive elements [4k, 4k+4): one 128-bit access per fp32
 // stream and one 64-bit access for the bf16 stream, so each wave64 access
@@ -26,12 +31,12 @@
 namespace zs {
 namespace {
 
-// One element of the update, in the order and with the roundings the
-// header documents.  Built with -ffp-contract=off: no multiply-add fusion;
-// the quotient and square root are IEEE round-to-nearest (correctly rounded
-// fp32 division and sqrt are requested at compile time).
-__device__ __forceinline__ void adamw_elem(const AdamwArgs& a, float coef, float gr, float& p,
-                                           float& m, float& v) {
+// One element: the moments in place and the returned step u, in the order
+// and with the roundings the header documents.  Built with
+// -ffp-contract=off: no multiply-add fusion; the quotient and square root
+// are IEEE round-to-nearest (correctly rounded fp32 division and sqrt are
+// requested at compile time).
+__device__ __forceinline__ float adam_elem(const AdamwArgs& a, float coef, float gr, float& m, float& v) {
     float g = gr * a.grad_scale;
     g = g * coef;
     const float m_keep = a.beta1 * m;
@@ -45,9 +50,13 @@ __device__ __forceinline__ void adamw_elem(const AdamwArgs& a, float coef, float
     float den = root / a.bias_correction2_sqrt;
     den = den + a.eps;
     const float ratio = m / den;
-    const float u = ratio * a.step_size;
+    return ratio * a.step_size;
+}
+
+// the parameter after the step: decoupled decay, then the step
+__device__ __forceinline__ float apply_step(const AdamwArgs& a, float p, float u) {
     const float pd = p * a.decay;
-    p = pd - u;
+    return pd - u;
 }
 
 // Clip coefficient from the squared norm, in binary64 (uniform per wave).
@@ -71,10 +80,16 @@ __device__ __forceinline__ bool clip_coef(const AdamwArgs& a, float& coef) {
 constexpr int kVecBlock = 64;
 constexpr unsigned kVecLdsReserve = 16384;
 
-// NO_MASTER: the bf16 parameter is read, updated and rounded back in place
-// (no fp32 master): 24 B/element (R g, m, v 12 + p 2; W m, v 8 + p 2).
-template <int VEC, bool BF16, int BS, bool NO_MASTER = false>
+// What a step reads and writes besides grad, exp_avg and exp_avg_sq:
+//   kMaster      R/W fp32 master                          28 B/element
+//   kMasterBf16  R/W fp32 master, W bf16 re-cast          30 B/element
+//   kNoMaster    R/W bf16 parameter (no fp32 master)      24 B/element
+//   kUpdate      W fp32 update = -u (no parameter, no decay) 24 B/element
+enum Form : int { kMaster = 0, kMasterBf16 = 1, kNoMaster = 2, kUpdate = 3 };
+
+template <int VEC, int FORM, int BS>
 __global__ __launch_bounds__(BS) void adamw_kernel(const AdamwArgs a) {
+    constexpr bool kReadP = FORM != kUpdate;
     const int64_t n = a.n;
     const int64_t first = ((int64_t)blockIdx.x * BS + threadIdx.x) * VEC;
     if (first >= n) return;
@@ -84,12 +99,12 @@ __global__ __launch_bounds__(BS) void adamw_kernel(const AdamwArgs a) {
         // The loads are issued before the clip coefficient is resolved, so
         // the latency of the norm's read overlaps with them.
         const f32x4 g4 = ld_stream(reinterpret_cast<const f32x4*>(a.grad + first));
-        f32x4 p4;
-        if (NO_MASTER) {
+        f32x4 p4 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (FORM == kNoMaster) {
             const u32x2 w = ld_stream(reinterpret_cast<const u32x2*>(a.param_bf16 + first));
             p4 = f32x4{bf16_to_f32(w.x & 0xFFFFu), bf16_to_f32(w.x >> 16), bf16_to_f32(w.y & 0xFFFFu),
                        bf16_to_f32(w.y >> 16)};
-        } else {
+        } else if constexpr (kReadP) {
             p4 = ld_stream(reinterpret_cast<const f32x4*>(a.master + first));
         }
         const f32x4 m4 = ld_stream(reinterpret_cast<const f32x4*>(a.exp_avg + first));
@@ -101,12 +116,17 @@ __global__ __launch_bounds__(BS) void adamw_kernel(const AdamwArgs a) {
         float ms[4] = {m4.x, m4.y, m4.z, m4.w};
         float vs[4] = {v4.x, v4.y, v4.z, v4.w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) adamw_elem(a, coef, gs[j], ps[j], ms[j], vs[j]);
-        if (!NO_MASTER)
+        for (int j = 0; j < 4; ++j) {
+            const float u = adam_elem(a, coef, gs[j], ms[j], vs[j]);
+            ps[j] = FORM == kUpdate ? -u : apply_step(a, ps[j], u);
+        }
+        if constexpr (FORM == kMaster || FORM == kMasterBf16)
             st_stream(reinterpret_cast<f32x4*>(a.master + first), f32x4{ps[0], ps[1], ps[2], ps[3]});
+        if constexpr (FORM == kUpdate)
+            st_stream(reinterpret_cast<f32x4*>(a.update + first), f32x4{ps[0], ps[1], ps[2], ps[3]});
         st_stream(reinterpret_cast<f32x4*>(a.exp_avg + first), f32x4{ms[0], ms[1], ms[2], ms[3]});
         st_stream(reinterpret_cast<f32x4*>(a.exp_avg_sq + first), f32x4{vs[0], vs[1], vs[2], vs[3]});
-        if (BF16 || NO_MASTER)
+        if constexpr (FORM == kMasterBf16 || FORM == kNoMaster)
             st_stream(reinterpret_cast<u32x2*>(a.param_bf16 + first),
                       u32x2{pack_bf16x2(ps[0], ps[1]), pack_bf16x2(ps[2], ps[3])});
         return;
@@ -116,38 +136,50 @@ __global__ __launch_bounds__(BS) void adamw_kernel(const AdamwArgs a) {
     if (!clip_coef(a, coef)) return;
     const int64_t last = first + VEC < n ? first + VEC : n;
     for (int64_t i = first; i < last; ++i) {
-        float p = NO_MASTER ? bf16_to_f32(a.param_bf16[i]) : a.master[i];
         float m = a.exp_avg[i], v = a.exp_avg_sq[i];
-        adamw_elem(a, coef, a.grad[i], p, m, v);
-        if (!NO_MASTER) a.master[i] = p;
+        const float u = adam_elem(a, coef, a.grad[i], m, v);
         a.exp_avg[i] = m;
         a.exp_avg_sq[i] = v;
-        if (BF16 || NO_MASTER) a.param_bf16[i] = (uint16_t)f32_to_bf16_rne(p);
+        if constexpr (FORM == kUpdate) {
+            a.update[i] = -u;
+        } else if constexpr (FORM == kNoMaster) {
+            a.param_bf16[i] = (uint16_t)f32_to_bf16_rne(apply_step(a, bf16_to_f32(a.param_bf16[i]), u));
+        } else {
+            const float p = apply_step(a, a.master[i], u);
+            a.master[i] = p;
+            if constexpr (FORM == kMasterBf16) a.param_bf16[i] = (uint16_t)f32_to_bf16_rne(p);
+        }
     }
 }
 
-template <int VEC, bool BF16, int BS, bool NO_MASTER = false>
+template <int VEC, int FORM, int BS>
 hipError_t launch(const AdamwArgs& a, unsigned lds, hipStream_t stream) {
     const int64_t threads = (a.n + VEC - 1) / VEC;
     const int64_t blocks = (threads + BS - 1) / BS;
     if (blocks > (int64_t)UINT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((adamw_kernel<VEC, BF16, BS, NO_MASTER>), dim3((unsigned)blocks), dim3(BS), lds, stream, a);
+    hipLaunchKernelGGL((adamw_kernel<VEC, FORM, BS>), dim3((unsigned)blocks), dim3(BS), lds, stream, a);
     return hipGetLastError();
+}
+
+template <int FORM>
+hipError_t launch_form(const AdamwArgs& a, bool vec_ok, hipStream_t stream) {
+    if (vec_ok) return launch<4, FORM, kVecBlock>(a, kVecLdsReserve, stream);
+    return launch<1, FORM, kBlock>(a, 0, stream);
 }
 
 }  // namespace
 
-hipError_t launch_adamw_no_master(const AdamwArgs& a, bool vec_ok, hipStream_t stream) {
-    if (vec_ok) return launch<4, true, kVecBlock, true>(a, kVecLdsReserve, stream);
-    return launch<1, true, kBlock, true>(a, 0, stream);
+hipError_t launch_adamw(const AdamwArgs& a, bool vec_ok, hipStream_t stream) {
+    return a.param_bf16 != nullptr ? launch_form<kMasterBf16>(a, vec_ok, stream)
+                                   : launch_form<kMaster>(a, vec_ok, stream);
 }
 
-hipError_t launch_adamw(const AdamwArgs& a, bool vec_ok, hipStream_t stream) {
-    const bool bf16 = a.param_bf16 != nullptr;
-    if (vec_ok)
-        return bf16 ? launch<4, true, kVecBlock>(a, kVecLdsReserve, stream)
-                    : launch<4, false, kVecBlock>(a, kVecLdsReserve, stream);
-    return bf16 ? launch<1, true, kBlock>(a, 0, stream) : launch<1, false, kBlock>(a, 0, stream);
+hipError_t launch_adamw_no_master(const AdamwArgs& a, bool vec_ok, hipStream_t stream) {
+    return launch_form<kNoMaster>(a, vec_ok, stream);
+}
+
+hipError_t launch_adam_update(const AdamwArgs& a, bool vec_ok, hipStream_t stream) {
+    return launch_form<kUpdate>(a, vec_ok, stream);
 }
 
 }  // namespace zs

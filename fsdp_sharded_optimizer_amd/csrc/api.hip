@@ -264,17 +264,45 @@ int32_t adamw_step_no_master(const zs_adamw* hp, uint16_t* param_bf16, float* ex
     return hip_status(zs::launch_adamw_no_master(a, vec, as_stream(hip_stream)));
 }
 
+int32_t adam_update(const zs_adamw* hp, float* exp_avg, float* exp_avg_sq, const float* grad, float* update,
+                    int64_t n, const double* norm_sq_dev, void* hip_stream) {
+    int32_t rc = adamw_check_hp(hp, n, norm_sq_dev);
+    if (rc != ZS_OK) return rc;
+    if (hp->weight_decay != 0.0) return ZS_EINVAL;
+    if (n == 0) return ZS_OK;
+    if (exp_avg == nullptr || exp_avg_sq == nullptr || grad == nullptr || update == nullptr) return ZS_EINVAL;
+    if (!aligned(exp_avg, 4) || !aligned(exp_avg_sq, 4) || !aligned(grad, 4) || !aligned(update, 4))
+        return ZS_EINVAL;
+    const void* bufs[5] = {update, exp_avg, exp_avg_sq, grad, nullptr};
+    const int64_t bytes[5] = {n * 4, n * 4, n * 4, n * 4, 0};
+    const bool written[5] = {true, true, true, false, false};
+    rc = adamw_check_overlap(bufs, bytes, written, norm_sq_dev);
+    if (rc != ZS_OK) return rc;
+    zs::AdamwArgs a = adamw_scalars(hp, norm_sq_dev);
+    a.exp_avg = exp_avg;
+    a.exp_avg_sq = exp_avg_sq;
+    a.grad = grad;
+    a.update = update;
+    a.n = n;
+    const bool vec = aligned(update, 16) && aligned(exp_avg, 16) && aligned(exp_avg_sq, 16) && aligned(grad, 16);
+    return hip_status(zs::launch_adam_update(a, vec, as_stream(hip_stream)));
+}
+
 // ---------------------------------------------------------------------------
-// flatten / unflatten
+// flatten / unflatten / apply
 // ---------------------------------------------------------------------------
 
+// apply: the tensors take += of the (fp32) flat buffer instead of a copy
 static int32_t flat_common(const zs_tensor* tensors, int32_t count, void* flat, int32_t flat_dtype,
                            int32_t tensor_dtype, int64_t padded_total, bool unpack,
-                           hipStream_t stream) {
+                           hipStream_t stream, bool apply = false) {
     if (count < 0 || (count > 0 && tensors == nullptr)) return ZS_EINVAL;
     if (!dtype_ok(flat_dtype) || !dtype_ok(tensor_dtype)) return ZS_EINVAL;
     int kind;
-    if (flat_dtype == tensor_dtype) kind = flat_dtype == ZS_F32 ? 0 : 1;
+    if (apply) {
+        if (!unpack || flat_dtype != ZS_F32) return ZS_EINVAL;
+        kind = tensor_dtype == ZS_F32 ? 4 : 5;
+    } else if (flat_dtype == tensor_dtype) kind = flat_dtype == ZS_F32 ? 0 : 1;
     else if (!unpack && tensor_dtype == ZS_BF16 && flat_dtype == ZS_F32) kind = 2;
     else if (unpack && flat_dtype == ZS_F32 && tensor_dtype == ZS_BF16) kind = 3;
     else return ZS_EINVAL;
@@ -357,6 +385,12 @@ int32_t flat_unpack(const void* flat, int32_t flat_dtype, const zs_tensor* dst, 
                     int32_t dst_dtype, void* hip_stream) {
     return flat_common(dst, count, const_cast<void*>(flat), flat_dtype, dst_dtype, 0, true,
                        as_stream(hip_stream));
+}
+
+int32_t flat_apply_update(const float* update, const zs_tensor* dst, int32_t count, int32_t dst_dtype,
+                          void* hip_stream) {
+    return flat_common(dst, count, const_cast<float*>(update), ZS_F32, dst_dtype, 0, true,
+                       as_stream(hip_stream), true);
 }
 
 }  // extern "C"

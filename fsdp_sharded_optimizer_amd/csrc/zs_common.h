@@ -59,12 +59,14 @@ struct AdamwArgs {
     float* exp_avg_sq;
     const float* grad;
     uint16_t* param_bf16;       // nullable
+    float* update;              // the ZeRO-1 form's output
     int64_t n;
 };
 
 // Launchers: enqueue on `stream`, return the hipError_t of the launch.
 hipError_t launch_adamw(const AdamwArgs& a, bool vec_ok, hipStream_t stream);
 hipError_t launch_adamw_no_master(const AdamwArgs& a, bool vec_ok, hipStream_t stream);
+hipError_t launch_adam_update(const AdamwArgs& a, bool vec_ok, hipStream_t stream);
 hipError_t launch_grad_accum(float* acc, const void* grad, int grad_bf16, int64_t n,
                              int overwrite, bool vec_ok, hipStream_t stream);
 int64_t norm_partial_blocks(int64_t n);
@@ -103,7 +105,8 @@ struct FlatBatch {
     void* flat;
     FlatEntry e[kFlatMaxTensors];
 };
-// kind: 0 = f32->f32, 1 = bf16->bf16, 2 = bf16->f32 (pack widen), 3 = f32->bf16 (unpack RNE)
+// kind: 0 = f32->f32, 1 = bf16->bf16, 2 = bf16->f32 (pack widen), 3 = f32->bf16 (unpack RNE),
+// 4 = f32 tensor += f32 flat, 5 = bf16 tensor = RNE(widen(tensor) + f32 flat) (apply, unpack side)
 hipError_t launch_flat(const FlatBatch& b, int kind, int unpack, hipStream_t stream);
 int64_t flat_tile_elems(int kind);   // elements per workgroup
 int64_t flat_vec_elems(int kind);    // elements per lane on the vector path

@@ -131,6 +131,23 @@ int32_t flat_unpack(const void* flat, int32_t flat_dtype,
                     const zs_tensor* dst, int32_t count, int32_t dst_dtype, void* hip_stream);
 
 /*
+ * flat_apply_update — add a gathered fp32 update into the parameters.
+ * [ZeRO page] §ZeRO-1 _apply_update: an offset walks the parameters and each
+ * adds its next numel elements of the full (all-gathered) update in place.
+ * dst[i][j] += update[o_i + j], o_i = sum of the numels before i; elements
+ * of update past sum(numel) (the all-gather's padding) are not read.
+ * F32 tensors: fl(p + u).  BF16 tensors: bf16_rne(fl(widen(p) + u)), the
+ * in-place add on a low-precision tensor done as one fp32 add rounded once.
+ * update: device fp32[sum(numel)] or longer, read; dst: host array of
+ * `count` device tensors of dst_dtype, read-write; they must not overlap
+ * update or each other.
+ * Errors: ZS_EINVAL (count < 0, negative numel, dtype, null/misaligned
+ * pointer), ZS_EOVERLAP, ZS_EHIP.
+ */
+int32_t flat_apply_update(const float* update, const zs_tensor* dst, int32_t count, int32_t dst_dtype,
+                          void* hip_stream);
+
+/*
  * grad_accum — fp32 gradient accumulation over micro-batches.
  * [ZeRO page] §"梯度累积——用计算换通信" GradientAccumulator.backward
  * (an fp32 buffer adds each micro-batch's grad.float()) and [Memory page]
@@ -261,6 +278,26 @@ int32_t adamw_step(const zs_adamw* hp, float* master, float* exp_avg, float* exp
  */
 int32_t adamw_step_no_master(const zs_adamw* hp, uint16_t* param_bf16, float* exp_avg, float* exp_avg_sq,
                              const float* grad, int64_t n, const double* norm_sq_dev, void* hip_stream);
+
+/*
+ * adam_update — the ZeRO-1 form of the step: the update as a vector.
+ * [ZeRO page] §"ZeRO-1: 切分优化器状态", ZeRO1Optimizer.step: plain Adam on
+ * this rank's slice of the full averaged gradient (often a view at any
+ * element offset of one resident flat buffer), producing
+ * update = exp_avg / denom * (-lr/bias_correction1), which the caller
+ * all-gathers and adds into the parameters (flat_apply_update).  m, v, den
+ * and the clip as in adamw_step; update = fl(fl(m/den) * -(lr/bc1)).  The
+ * page's ZeRO-1 has no weight decay, and decoupled decay has no
+ * update-vector form with the same bits, so hp->weight_decay must be 0.
+ * Adding the update to an fp32 parameter gives the bits adamw_step gives.
+ * exp_avg, exp_avg_sq: device fp32[n], read-write; grad: device fp32[n],
+ * read; update: device fp32[n], written.  No two may overlap, nor overlap
+ * *norm_sq_dev.  A non-finite S writes nothing.
+ * Errors: ZS_EINVAL (as adamw_step, or weight_decay != 0), ZS_EOVERLAP,
+ * ZS_EHIP.
+ */
+int32_t adam_update(const zs_adamw* hp, float* exp_avg, float* exp_avg_sq, const float* grad, float* update,
+                    int64_t n, const double* norm_sq_dev, void* hip_stream);
 
 /* Static description of a return code. */
 const char* zs_strerror(int32_t code);

@@ -82,6 +82,10 @@ def _configure(L):
     L.orc_adamw_step.restype = ctypes.c_int
     L.orc_adamw_step_no_master.argtypes = [ctypes.POINTER(AdamWHp), P, P, P, P, I64, P]
     L.orc_adamw_step_no_master.restype = ctypes.c_int
+    L.orc_adam_update.argtypes = [ctypes.POINTER(AdamWHp), P, P, P, P, I64, P]
+    L.orc_adam_update.restype = ctypes.c_int
+    L.orc_flat_apply_update.argtypes = [P, P, P, I32, I32]
+    L.orc_flat_apply_update.restype = ctypes.c_int
     L.orc_num_threads.argtypes = []
     L.orc_num_threads.restype = ctypes.c_int
     return L
@@ -251,3 +255,34 @@ def adamw_step_no_master(hp: AdamWHp, param_bf16, exp_avg, exp_avg_sq, grad, nor
     if rc < 0:
         raise ValueError("adamw_step_no_master: invalid arguments")
     return int(rc)
+
+
+def adam_update(hp: AdamWHp, exp_avg, exp_avg_sq, grad, update, norm_sq=None) -> int:
+    """ZeRO-1 form: exp_avg / exp_avg_sq in place, the update vector into
+    ``update``; 0 or 1 (skipped).  weight_decay must be 0."""
+    for a, nm in ((exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq"), (grad, "grad"), (update, "update")):
+        _need(a, np.float32, nm)
+        if a.size != exp_avg.size:
+            raise ValueError("adam_update: size mismatch")
+    nsq = ctypes.c_double(float(norm_sq)) if norm_sq is not None else None
+    rc = lib().orc_adam_update(ctypes.byref(hp), _ptr(exp_avg), _ptr(exp_avg_sq), _ptr(grad), _ptr(update),
+                               exp_avg.size, ctypes.byref(nsq) if nsq is not None else None)
+    if rc < 0:
+        raise ValueError("adam_update: invalid arguments")
+    return int(rc)
+
+
+def flat_apply_update(update: np.ndarray, dsts, dst_dtype: int) -> None:
+    """In place: dsts[i] += update[o_i : o_i + numel_i] (fp32 or bf16 tensors)."""
+    _need(update, np.float32, "update")
+    for d in dsts:
+        _need(d, _np_dtype(dst_dtype), "dst")
+    if sum(d.size for d in dsts) > update.size:
+        raise ValueError("flat_apply_update: update shorter than the tensors")
+    n = len(dsts)
+    ptrs = (ctypes.c_void_p * max(n, 1))(*[d.ctypes.data for d in dsts])
+    numel = (ctypes.c_int64 * max(n, 1))(*[d.size for d in dsts])
+    rc = lib().orc_flat_apply_update(_ptr(update), ctypes.cast(ptrs, ctypes.c_void_p),
+                                     ctypes.cast(numel, ctypes.c_void_p), n, dst_dtype)
+    if rc != 0:
+        raise ValueError("flat_apply_update: invalid arguments")

@@ -413,6 +413,82 @@ int orc_adamw_step_no_master(const orc_adamw_hp* hp, uint16_t* param_bf16, float
     return 0;
 }
 
+/*
+ * The ZeRO-1 form of the step ([ZeRO page] §"ZeRO-1: 切分优化器状态",
+ * ZeRO1Optimizer.step): plain Adam over this rank's slice of the full,
+ * averaged gradient, whose result is an update vector rather than a new
+ * parameter.  Every rank's update is then gathered into one full-length
+ * buffer and added into the parameters (orc_flat_apply_update below).
+ * Per element: g, m, v, den as in orc_adamw_step, then
+ *   update[i] = fl(fl(m/den) * (-step_size))
+ * the page's exp_avg / denom * (-step_size).  The page's ZeRO-1 has no
+ * weight decay, and a decoupled decay has no update-vector form that adds
+ * to the same bits, so weight_decay must be 0 (else -1).  Adding the update
+ * to p gives fl(p - u): the master path of orc_adamw_step with decay 1.
+ * Returns 0 (written), 1 (skipped: non-finite norm) or -1.
+ */
+int orc_adam_update(const orc_adamw_hp* hp, float* exp_avg, float* exp_avg_sq, const float* grad,
+                    float* update, int64_t n, const double* norm_sq)
+{
+    orc_adamw_scalars s;
+    if (n < 0 || hp->weight_decay != 0.0 || orc_adamw_scalars_make(hp, &s) != 0) return -1;
+    float coef = 1.0f;
+    if (norm_sq) {
+        double S = *norm_sq + hp->extra_norm_sq;
+        if (!isfinite(S)) return 1;
+        coef = orc_clip_coef(*norm_sq, hp->extra_norm_sq, hp->max_norm);
+    }
+    const float neg_step_size = -s.step_size;
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        float g = grad[i] * s.grad_scale;
+        g = g * coef;
+        float m = s.beta1 * exp_avg[i] + s.one_minus_beta1 * g;
+        float v = s.beta2 * exp_avg_sq[i] + s.one_minus_beta2 * (g * g);
+        float denom = sqrtf(v) / s.bias_correction2_sqrt + s.eps;
+        exp_avg[i] = m;
+        exp_avg_sq[i] = v;
+        update[i] = m / denom * neg_step_size;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Apply a gathered update  ([ZeRO page] §ZeRO-1 _apply_update: walk an */
+/* offset over the parameters; each adds the next numel elements of the */
+/* full update in place)                                                */
+/* ------------------------------------------------------------------ */
+/*
+ * dst_i[j] += update[o_i + j], o_i the running sum of the earlier numels.
+ * fp32 parameters: fl(p + u).  bf16 parameters: bf16_rne(fl(widen(p) + u)),
+ * the page's in-place add on a low-precision tensor read as one fp32 add
+ * rounded once into the parameter's dtype.  Elements past sum(numel) (the
+ * all-gather's padding) are never read.  Returns 0, or -1 for a negative
+ * numel or an unknown dtype.
+ */
+int orc_flat_apply_update(const float* update, void* const* dst, const int64_t* numel, int32_t count,
+                          int32_t dst_dtype)
+{
+    if (count < 0 || !dtype_ok(dst_dtype)) return -1;
+    for (int32_t t = 0; t < count; ++t)
+        if (numel[t] < 0) return -1;
+    int64_t offset = 0;
+    for (int32_t t = 0; t < count; ++t) {
+        for (int64_t j = 0; j < numel[t]; ++j) {
+            float u = update[offset + j];
+            if (dst_dtype == ORC_F32) {
+                float* p = (float*)dst[t];
+                p[j] = p[j] + u;
+            } else {
+                uint16_t* p = (uint16_t*)dst[t];
+                p[j] = orc_bf16_rne(orc_bf16_widen(p[j]) + u);
+            }
+        }
+        offset += numel[t];
+    }
+    return 0;
+}
+
 /* Thread count OpenMP will use for the loops above (reported by the
  * CPU-baseline timing). */
 #ifdef _OPENMP

@@ -27,6 +27,14 @@ def declared_functions():
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)))
 
 
+@pytest.fixture(autouse=True)
+def no_launch_reached():
+    """Every call here must stop before a launch: on a host without a GPU a
+    launch attempt leaves a HIP error behind, and that fails the test."""
+    yield
+    assert zs.lib().zs_last_hip_error() == 0, "a call got past validation to a kernel launch"
+
+
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) == set(B.EXPORTS), names
@@ -118,6 +126,34 @@ def test_adamw_no_master_rejects():
     assert call(m=FAKE + 1024) == B.ZS_EOVERLAP                   # exp_avg inside the bf16 parameter
     assert call(norm=FAKE + 2**21 + 64) == B.ZS_EOVERLAP          # norm inside exp_avg_sq
     assert call(n=0) == B.ZS_OK
+
+
+def test_adam_update_rejects():
+    L = zs.lib()
+    call = lambda hp=None, m=FAKE, v=FAKE + 2**20, g=FAKE + 2**21, u=FAKE + 2**22, n=1024, norm=0: \
+        L.adam_update(ctypes.byref(hp or _hp()), m, v, g, u, n, norm, None)
+    assert call(hp=_hp(weight_decay=0.1)) == B.ZS_EINVAL            # the ZeRO-1 form has no decay
+    assert call(hp=_hp(weight_decay=0.1), n=0) == B.ZS_EINVAL
+    assert call(hp=_hp(step=0)) == B.ZS_EINVAL
+    assert call(u=0) == B.ZS_EINVAL
+    assert call(g=FAKE + 2**21 + 2) == B.ZS_EINVAL                  # fp32 must be 4-byte aligned
+    assert call(u=FAKE + 2**21 + 4) == B.ZS_EOVERLAP                # update over grad
+    assert call(norm=FAKE + 2**22 + 8) == B.ZS_EOVERLAP             # norm inside the update
+    assert call(n=0) == B.ZS_OK
+
+
+def test_flat_apply_update_rejects():
+    L = zs.lib()
+    upd = FAKE + 2**30
+    two = _tensors((FAKE, 10), (FAKE + 2**20, 6))
+    assert L.flat_apply_update(upd, two, 2, 7, None) == B.ZS_EINVAL                   # dtype
+    assert L.flat_apply_update(upd, two, -1, B.ZS_F32, None) == B.ZS_EINVAL
+    assert L.flat_apply_update(0, two, 2, B.ZS_F32, None) == B.ZS_EINVAL
+    assert L.flat_apply_update(upd + 2, two, 2, B.ZS_F32, None) == B.ZS_EINVAL        # misaligned update
+    assert L.flat_apply_update(upd, _tensors((FAKE + 1, 4)), 1, B.ZS_BF16, None) == B.ZS_EINVAL
+    assert L.flat_apply_update(upd, _tensors((upd + 8, 4)), 1, B.ZS_F32, None) == B.ZS_EOVERLAP   # [upd+8, upd+24) over [upd, upd+16)
+    assert L.flat_apply_update(upd, _tensors((FAKE, 8), (FAKE + 16, 8)), 2, B.ZS_F32, None) == B.ZS_EOVERLAP
+    assert L.flat_apply_update(upd, _tensors((0, 0)), 1, B.ZS_BF16, None) == B.ZS_OK
 
 
 def test_grad_accum_rejects():

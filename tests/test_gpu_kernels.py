@@ -463,3 +463,82 @@ def test_no_master_stalls_on_the_gpu():
           f"differ after 20 steps: {differ:.3f}", flush=True)
     assert differ > 0.3
     assert moved_master > moved_direct
+
+
+# ---------------------------------------------------------------------------
+# adam_update and flat_apply_update (the ZeRO page's ZeRO-1 flow)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n", [1, 7, 4097, 100_003])
+@pytest.mark.parametrize("offset", [0, 1, 3])
+@pytest.mark.parametrize("clip", [False, True])
+def test_adam_update_bit_exact(n, offset, clip):
+    """The gradient (and the update) as views at any element offset, as a
+    rank's slice of one resident flat buffer is; the moments are the rank's
+    own allocations.  Given the oracle's squared norm every output is
+    bit-identical, and nothing past the views is written."""
+    print(f"adam_update n={n} offset={offset} clip={clip}", flush=True)
+    rng = np.random.default_rng(3 * n + offset + 7 * clip)
+    m_ref, v_ref, u_ref = np.zeros(n, np.float32), np.zeros(n, np.float32), np.empty(n, np.float32)
+    m, mw = dev_buf(m_ref, 0)
+    v, vw = dev_buf(v_ref, 0)
+    u, uw = dev_buf(np.zeros(n, np.float32), offset)
+    for t in range(1, 5):
+        acc = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+        S = oracle.grad_norm_sq(acc, 1 / 8)
+        hp_gpu, hp_orc = _hp(t, lr=1e-4, b2=0.999, wd=0.0, scale=1 / 8,
+                             max_norm=0.7 * math.sqrt(S * 8) if clip else 0.0, extra=7 * S)
+        assert oracle.adam_update(hp_orc, m_ref, v_ref, acc, u_ref, norm_sq=S if clip else None) == 0
+        g, gw = dev_buf(acc, offset)
+        norm = torch.tensor([S], dtype=torch.float64, device="cuda") if clip else None
+        zs.adam_update(hp_gpu, m, v, g, u, norm_sq=norm)
+        torch.cuda.synchronize()
+        for name, gpu, ref in (("update", u, u_ref), ("m", m, m_ref), ("v", v, v_ref)):
+            assert bits_equal(to_np(gpu), ref), (t, name, identical_fraction(to_np(gpu), ref))
+        assert canary_ok(gw, offset, n)
+    for whole, off in ((uw, offset), (mw, 0), (vw, 0)):
+        assert canary_ok(whole, off, n)
+
+
+def test_adam_update_skips_on_nonfinite_norm():
+    n = 4099
+    g = from_np(np.ones(n, np.float32))
+    m, v = torch.ones(n, device="cuda"), torch.ones(n, device="cuda")
+    u = torch.full((n,), 7.0, device="cuda")
+    norm = torch.tensor([float("nan")], dtype=torch.float64, device="cuda")
+    zs.adam_update(_hp(1, wd=0.0, max_norm=1.0)[0], m, v, g, u, norm_sq=norm)
+    torch.cuda.synchronize()
+    assert torch.all(u == 7.0) and torch.all(m == 1) and torch.all(v == 1)
+    with pytest.raises(zs.ZShardError):
+        zs.adam_update(_hp(1, wd=0.1)[0], m, v, g, u)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("count,aligned_sizes,upd_offset", [(1, True, 0), (12, False, 0), (40, False, 0),
+                                                            (70, True, 0), (9, True, 1)])
+def test_flat_apply_update_bit_exact(dtype, count, aligned_sizes, upd_offset):
+    """Every tensor adds its part of the gathered update; the update's
+    padding is NaN and must never be read; batches of more than 32 tensors
+    and tensors at unaligned offsets of the update are covered."""
+    print(f"flat_apply_update dtype={dtype} count={count} upd_offset={upd_offset}", flush=True)
+    rng = np.random.default_rng(count * 13 + len(dtype) + upd_offset)
+    shapes = _shapes(rng, count, big=aligned_sizes)
+    if aligned_sizes:
+        shapes = [tuple(list(s[:-1]) + [s[-1] * 8]) for s in shapes]
+    numels = [int(np.prod(s)) for s in shapes]
+    T = sum(numels)
+    upd_ref = np.full(T + 13, np.nan, np.float32)
+    upd_ref[:T] = (rng.standard_normal(T) * 1e-2).astype(np.float32)
+    bf16 = dtype == "bf16"
+    if bf16:
+        p_ref = [oracle.bf16_rne(rng.uniform(-1, 1, k).astype(np.float32)) for k in numels]
+    else:
+        p_ref = [rng.uniform(-1, 1, k).astype(np.float32) for k in numels]
+    params = [from_np(x, bf16=bf16).reshape(s) for x, s in zip(p_ref, shapes)]
+    upd, upd_whole = dev_buf(upd_ref, upd_offset)
+    oracle.flat_apply_update(upd_ref, p_ref, oracle.BF16 if bf16 else oracle.F32)
+    zs.flat_apply_update(upd, params)
+    torch.cuda.synchronize()
+    for d, r in zip(params, p_ref):
+        assert bits_equal(to_np(d).reshape(-1), r)
+    assert canary_ok(upd_whole, upd_offset, T + 13)

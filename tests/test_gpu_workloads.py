@@ -283,3 +283,56 @@ def test_full_shard(name, full_norm, fused):
     if name == "zero3_70b_shard":
         assert all(0.70 < r["coef"] < 0.76 for r in rep), rep
     torch.cuda.empty_cache()
+
+
+def test_tiny_zero1_full_flow():
+    """The ZeRO page's ZeRO-1 flow for the 1,000,003-parameter model over 8
+    ranks, every rank's share run on this GPU: flatten the model's fp32
+    grads (padded to 8 x 125,001), each rank's Adam update on its slice of
+    the resident flat gradient (odd ranks' slices and chunks start at
+    misaligned offsets) written into its chunk of the gathered buffer, then
+    the apply into the 12 parameter tensors.  Five steps, bit-identical to
+    the oracle running the same flow; the gathered buffer's padding is NaN
+    and never reaches a parameter."""
+    w = workloads.WORKLOADS["tiny_zero1"]
+    T, N = w.total, w.world
+    chunk, _, _, padded = zs.zero_shard_range(T, N, 0)
+    ranges = [zs.zero_shard_range(T, N, r)[1:3] for r in range(N)]
+    params = [p.cuda() for p in workloads.param_tensors(w)]
+    p_ref = [p.numpy().reshape(-1).copy() for p in workloads.param_tensors(w)]
+    m = [torch.zeros(chunk, device="cuda") for _ in range(N)]
+    v = [torch.zeros(chunk, device="cuda") for _ in range(N)]
+    m_ref = [np.zeros(chunk, np.float32) for _ in range(N)]
+    v_ref = [np.zeros(chunk, np.float32) for _ in range(N)]
+    flat = torch.empty(padded, device="cuda")
+    gathered = torch.empty(padded, device="cuda")
+    for t in range(1, w.steps + 1):
+        log(f"  tiny_zero1 flow step {t}")
+        grads = workloads.grad_tensors(w, t)
+        hp = zs.AdamWConfig(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=0.0,
+                            grad_scale=w.grad_scale, step=t)
+        hp_orc = oracle.make_hp(w.lr, w.beta1, w.beta2, w.eps, 0.0, w.grad_scale, 0.0, 0.0, t)
+        zs.flat_pack([g.cuda() for g in grads], flat, padded)
+        gathered.fill_(float("nan"))
+        for r, (s, e) in enumerate(ranges):
+            k = e - s
+            zs.adam_update(hp, m[r][:k], v[r][:k], flat[s:e], gathered[r * chunk:r * chunk + k])
+        zs.flat_apply_update(gathered, params)
+        # the oracle runs the same flow
+        flat_ref = oracle.flat_pack([g.numpy().reshape(-1) for g in grads], oracle.F32, oracle.F32, padded)
+        g_ref = np.full(padded, np.nan, np.float32)
+        for r, (s, e) in enumerate(ranges):
+            k = e - s
+            mm, vv, uu = m_ref[r][:k].copy(), v_ref[r][:k].copy(), np.empty(k, np.float32)
+            oracle.adam_update(hp_orc, mm, vv, np.ascontiguousarray(flat_ref[s:e]), uu)
+            m_ref[r][:k], v_ref[r][:k] = mm, vv
+            g_ref[r * chunk:r * chunk + k] = uu
+        oracle.flat_apply_update(g_ref, p_ref, oracle.F32)
+        torch.cuda.synchronize()
+        assert bits_equal(to_np(flat)[:T], flat_ref[:T])
+        assert bits_equal(to_np(gathered), g_ref)
+        for i, (a, b) in enumerate(zip(params, p_ref)):
+            assert bits_equal(to_np(a).reshape(-1), b), (t, i)
+        for r in range(N):
+            assert bits_equal(to_np(m[r]), m_ref[r]) and bits_equal(to_np(v[r]), v_ref[r]), (t, r)
+    assert all(bool(torch.isfinite(p).all()) for p in params)

@@ -77,6 +77,17 @@ MUTANTS = [
     ("adamw: non-finite norm not skipped", "if (!isfinite(S)) return 1;", ""),
     ("no master: decay skipped", "param_bf16[i] = orc_bf16_rne(pd - u);", "param_bf16[i] = orc_bf16_rne(p - u);"),
     ("no master: update dropped", "param_bf16[i] = orc_bf16_rne(pd - u);", "param_bf16[i] = orc_bf16_rne(pd);"),
+    ("zero-1 update: sign not flipped", "const float neg_step_size = -s.step_size;",
+     "const float neg_step_size = s.step_size;"),
+    ("zero-1 update: first moment not stored",
+     "        exp_avg[i] = m;\n        exp_avg_sq[i] = v;\n        update[i]",
+     "        exp_avg_sq[i] = v;\n        update[i]"),
+    ("zero-1 update: bias correction of v dropped", "float denom = sqrtf(v) / s.bias_correction2_sqrt + s.eps;",
+     "float denom = sqrtf(v) + s.eps;"),
+    ("apply: offset ignored", "float u = update[offset + j];", "float u = update[j];"),
+    ("apply: bf16 truncated instead of rounded", "p[j] = orc_bf16_rne(orc_bf16_widen(p[j]) + u);",
+     "p[j] = (uint16_t)(f32_bits(orc_bf16_widen(p[j]) + u) >> 16);"),
+    ("apply: fp32 update subtracted", "p[j] = p[j] + u;", "p[j] = p[j] - u;"),
 ]
 
 
@@ -110,11 +121,18 @@ def pin_suite():
         lambda: pins.test_adamw_rejects(orc),
         lambda: pins.test_no_master_one_step_equals_master_recast(orc),
         lambda: pins.test_no_master_stalls_below_half_an_ulp(orc),
+        lambda: pins.test_adam_update_added_to_param_equals_master_step(orc),
+        lambda: pins.test_adam_update_vs_pages_zero1_float64(orc),
+        lambda: pins.test_adam_update_step1_closed_form(orc),
+        lambda: pins.test_adam_update_rejects_decay_and_skips_nonfinite(orc),
+        lambda: pins.test_flat_apply_update_zero_update_is_identity(orc),
+        lambda: pins.test_zero1_flow_equals_one_buffer_step(orc),
     ]
     for seed in range(3):
         suite.append(lambda seed=seed: pins.test_flat_pack_matches_concatenate(orc, seed))
     for seed in range(2):
         suite.append(lambda seed=seed: pins.test_adamw_vs_torch_adamw(orc, seed))
+        suite.append(lambda seed=seed: pins.test_flat_apply_update_matches_slices(orc, seed))
     return suite
 
 

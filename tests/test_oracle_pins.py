@@ -602,3 +602,165 @@ def test_no_master_stalls_below_half_an_ulp(orc):
             oracle.adamw_step(H, master, mm, vv, g)
         assert np.all(b == want), (lr, hex(int(b[0])))
         assert np.allclose(master, oracle.bf16_widen(np.full(n, 0x3DCD, np.uint16)) - 10 * lr, rtol=0, atol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# ZeRO-1 form: the update vector, its gather and its apply
+# ---------------------------------------------------------------------------
+
+def _abits(a):
+    return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+
+
+def test_adam_update_added_to_param_equals_master_step(orc):
+    """With no decay, p + update is the master path's new p, bit for bit
+    (fl(p + fl(r * -s)) = fl(p - fl(r * s)) as IEEE rounding is symmetric),
+    over steps with and without a clip; the moments agree too."""
+    rng = np.random.default_rng(41)
+    n = 5003
+    p0 = rng.uniform(-0.1, 0.1, n).astype(np.float32)
+    p0[:3] = (0.0, -0.0, 1e-40)
+    master, m1, v1 = p0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    p, m2, v2 = p0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    upd = np.empty(n, np.float32)
+    for t in range(1, 7):
+        acc = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+        acc[:2] = 0.0
+        S = oracle.grad_norm_sq(acc, 1 / 8)
+        H = hp(lr=1e-4, beta1=0.9, beta2=0.999, scale=1 / 8, max_norm=0.6 * math.sqrt(S) if t % 2 else 0.0,
+               extra=0.1 * S, step=t)
+        assert oracle.adamw_step(H, master, m1, v1, acc, norm_sq=S) == 0
+        assert oracle.adam_update(H, m2, v2, acc, upd, norm_sq=S) == 0
+        p = p + upd   # numpy float32 addition, IEEE round to nearest
+        assert np.array_equal(_abits(p), _abits(master)), t
+        assert np.array_equal(m1, m2) and np.array_equal(v1, v2)
+
+
+def test_adam_update_vs_pages_zero1_float64(orc):
+    """The ZeRO page's ZeRO-1 step (mul_/add_/addcmul_, sqrt / sqrt(bc2) + eps,
+    exp_avg / denom * -step_size) run with torch float64 ops on the CPU; the
+    fp32 update and moments agree to a few fp32 ulps per step."""
+    rng = np.random.default_rng(43)
+    n = 4096
+    lr, b1, b2, eps = 1e-4, 0.9, 0.999, 1e-8
+    m, v, upd = np.zeros(n, np.float32), np.zeros(n, np.float32), np.empty(n, np.float32)
+    em, ev = torch.zeros(n, dtype=torch.float64), torch.zeros(n, dtype=torch.float64)
+    for t in range(1, 9):
+        acc = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+        assert oracle.adam_update(hp(lr=lr, beta1=b1, beta2=b2, eps=eps, scale=1 / 8, step=t), m, v, acc, upd) == 0
+        g = torch.from_numpy(acc).double() / 8
+        kappa_m = (b1 * em.abs() + (1 - b1) * g.abs()).numpy()   # guards a cancellation in m
+        em.mul_(b1).add_(g, alpha=1 - b1)
+        ev.mul_(b2).addcmul_(g, g, value=1 - b2)
+        denom = (ev.sqrt() / math.sqrt(1 - b2 ** t)).add_(eps)
+        ref = (em / denom * (-lr / (1 - b1 ** t))).numpy()
+        assert np.max(np.abs(upd - ref)) <= 4e-7 * t * lr, t
+        assert np.max(np.abs(m - em.numpy()) / kappa_m) <= 1e-6 * t
+        assert np.max(np.abs(v - ev.numpy()) / ev.numpy()) <= 1e-6 * t
+
+
+def test_adam_update_step1_closed_form(orc):
+    """At t = 1 the bias corrections cancel the (1 - beta) factors:
+    update = -lr g / (|g| + eps) up to a few roundings."""
+    rng = np.random.default_rng(47)
+    n = 3001
+    g = (rng.standard_normal(n) * 1e-2).astype(np.float32)
+    m, v, upd = np.zeros(n, np.float32), np.zeros(n, np.float32), np.empty(n, np.float32)
+    assert oracle.adam_update(hp(lr=0.01, beta1=0.8, beta2=0.99, eps=1e-8), m, v, g, upd) == 0
+    gd = g.astype(np.float64)
+    want = -0.01 * gd / (np.abs(gd) + 1e-8)
+    assert np.max(np.abs(upd - want)) <= 1e-8
+    assert np.all(np.sign(upd) == -np.sign(g))
+
+
+def test_adam_update_rejects_decay_and_skips_nonfinite(orc):
+    n = 16
+    m, v, g, u = (np.zeros(n, np.float32) for _ in range(4))
+    with pytest.raises(ValueError):
+        oracle.adam_update(hp(wd=0.1), m, v, g, u)
+    u[:] = 7.0
+    assert oracle.adam_update(hp(max_norm=1.0), m, v, g + 1, u, norm_sq=float("nan")) == 1
+    assert np.all(u == 7.0) and np.all(m == 0)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_flat_apply_update_matches_slices(orc, seed):
+    """fp32 tensors: numpy slicing of the update at the running offsets plus
+    numpy float32 addition.  bf16 tensors: torch's in-place add of an fp32
+    tensor into a bf16 one on the CPU.  Padding past the tensors is NaN and
+    must never be read."""
+    rng = np.random.default_rng(200 + seed)
+    shapes = _rand_shapes(rng, int(rng.integers(1, 40)))
+    numels = [int(np.prod(s)) for s in shapes]
+    T = sum(numels)
+    upd = np.full(T + 11, np.nan, np.float32)
+    upd[:T] = (rng.standard_normal(T) * 1e-3).astype(np.float32)
+    p32 = [rng.uniform(-1, 1, k).astype(np.float32) for k in numels]
+    want32 = []
+    off = 0
+    for x, k in zip(p32, numels):
+        want32.append(x + upd[off:off + k])
+        off += k
+    oracle.flat_apply_update(upd, p32, F32)
+    for a, b in zip(p32, want32):
+        assert np.array_equal(_abits(a), _abits(b))
+    pb = [oracle.bf16_rne(rng.uniform(-1, 1, k).astype(np.float32)) for k in numels]
+    wantb = []
+    off = 0
+    for x, k in zip(pb, numels):
+        t = torch.from_numpy(x.view(np.int16).copy()).view(torch.bfloat16)
+        t.add_(torch.from_numpy(upd[off:off + k].copy()))
+        wantb.append(t.view(torch.int16).numpy().view(np.uint16))
+        off += k
+    oracle.flat_apply_update(upd, pb, BF16)
+    for a, b in zip(pb, wantb):
+        assert np.array_equal(a, b)
+
+
+def test_flat_apply_update_zero_update_is_identity(orc):
+    rng = np.random.default_rng(5)
+    p = [rng.uniform(-1, 1, k).astype(np.float32) for k in (3, 1, 17)]
+    before = [x.copy() for x in p]
+    oracle.flat_apply_update(np.zeros(21, np.float32), p, F32)
+    for a, b in zip(p, before):
+        assert np.array_equal(a, b)
+
+
+def test_zero1_flow_equals_one_buffer_step(orc):
+    """The ZeRO page's ZeRO-1 flow on N ranks: flatten the model's grads
+    (padded to N*chunk), each rank runs the update on its slice (a view at
+    any element offset) with its own moments and writes its chunk of the
+    gathered buffer, then every parameter adds its part.  The parameters
+    equal one master step over the whole buffer followed by an unflatten:
+    ranks are independent because the update is element-wise."""
+    rng = np.random.default_rng(53)
+    shapes = [(37, 11), (5,), (64, 3), (1,), (29, 7)]
+    numels = [int(np.prod(s)) for s in shapes]
+    T, N = sum(numels), 6
+    chunk, _, _, padded = oracle.shard_range(T, N, 0)
+    params = [rng.uniform(-0.1, 0.1, k).astype(np.float32) for k in numels]
+    flat_master = oracle.flat_pack(params, F32, F32, padded)
+    M, V = np.zeros(padded, np.float32), np.zeros(padded, np.float32)
+    ms = [np.zeros(chunk, np.float32) for _ in range(N)]
+    vs = [np.zeros(chunk, np.float32) for _ in range(N)]
+    for t in range(1, 4):
+        grads = [(rng.standard_normal(k) * 1e-3).astype(np.float32) for k in numels]
+        flat_grad = oracle.flat_pack(grads, F32, F32, padded)
+        H = hp(lr=1e-3, beta1=0.9, beta2=0.99, scale=1 / N, step=t)
+        gathered = np.full(padded, np.nan, np.float32)
+        for r in range(N):
+            _, start, end, _ = oracle.shard_range(T, N, r)
+            k = end - start
+            u = np.empty(k, np.float32)
+            m, v = ms[r][:k].copy(), vs[r][:k].copy()
+            assert oracle.adam_update(H, m, v, np.ascontiguousarray(flat_grad[start:end]), u) == 0
+            ms[r][:k], vs[r][:k] = m, v
+            gathered[r * chunk:r * chunk + k] = u
+        oracle.flat_apply_update(gathered, params, F32)
+        oracle.adamw_step(H, flat_master, M, V, flat_grad)
+        back = oracle.flat_unpack(flat_master, F32, numels, F32)
+        for a, b in zip(params, back):
+            assert np.array_equal(_abits(a), _abits(b)), t
+        for r in range(N):
+            _, start, end, _ = oracle.shard_range(T, N, r)
+            assert np.array_equal(ms[r][:end - start], M[start:end])

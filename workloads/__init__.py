@@ -13,7 +13,9 @@ sharded over 64 ranks (ZeRO-3).  No dataset or trained weight is involved:
 parameters are U(-0.1, 0.1) and gradients are scaled standard normals.
 
 Seed of every draw: 0x5EED0000 + 0x1000*cfg + 0x100*purpose + 0x10*step + mb
-(purpose 0 = master init, 1 = gradient z, 2 = outlier mask, 3 = unit tensors).
+(purpose 0 = master init, 1 = gradient z, 2 = outlier mask, 3 = unit or model
+tensors, 4 = per-tensor gradients; for purposes 3 and 4 ``mb`` is the tensor
+index).
 """
 from __future__ import annotations
 
@@ -26,6 +28,7 @@ PURPOSE_MASTER = 0
 PURPOSE_GRAD = 1
 PURPOSE_OUTLIER = 2
 PURPOSE_UNIT = 3
+PURPOSE_TENSOR_GRAD = 4
 
 
 def seed_of(cfg: int, purpose: int, step: int = 0, mb: int = 0) -> int:
@@ -80,6 +83,20 @@ def block70b_tensor_shapes(hidden: int = 8192, ffn: int = 28672, q_heads: int = 
     ]
 
 
+def tiny_model_shapes():
+    """A one-layer decoder (hidden 256, ffn 600, vocab 1000) plus an odd
+    103x197 output projection: 1,000,003 parameters in 12 tensors, so the
+    flat buffer's length is odd and its last tensor ends mid-vector."""
+    h, f = 256, 600
+    return [
+        ("embed_tokens", (1000, h)),
+        ("q_proj", (h, h)), ("k_proj", (h, h)), ("v_proj", (h, h)), ("o_proj", (h, h)),
+        ("gate_proj", (f, h)), ("up_proj", (f, h)), ("down_proj", (h, f)),
+        ("input_layernorm", (h,)), ("post_attention_layernorm", (h,)), ("norm", (h,)),
+        ("out_proj", (103, 197)),
+    ]
+
+
 def numel_of(shape) -> int:
     n = 1
     for d in shape:
@@ -115,6 +132,7 @@ class Workload:
     outlier_mult: float = 1.0
     other_ranks_norm_sq: Optional[float] = None   # fixed stand-in, if any
     unit_shapes: tuple = field(default=())        # FSDP unit tensors (C4)
+    param_shapes: tuple = field(default=())       # model tensors of the flat buffer (ZeRO-1 flow)
     description: str = ""
 
     def std_at(self, step: int) -> float:
@@ -126,6 +144,7 @@ class Workload:
 
 C3_MULTIPLIERS = (0.6, 1.5, 0.8, 0.7, 2.0, 0.9, 0.5, 1.25, 0.75, 0.85)
 
+TINY = tiny_model_shapes()
 LLAMA7B = llama_tensor_shapes(32, 4096, 11008, 32000)
 LLAMA13B = llama_tensor_shapes(40, 5120, 13824, 32000)
 BLOCK70B = block70b_tensor_shapes()
@@ -135,7 +154,9 @@ WORKLOADS = {
         cfg=1, name="tiny_zero1", total=1_000_003, world=8, rank=3, steps=5, micro_batches=1,
         grad_dtype="f32", grad_std=1e-3, lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8,
         weight_decay=0.0, grad_scale=1.0 / 8, max_norm=0.0, bf16_param=False,
-        description="flat fp32 buffer of 1,000,003 params, world 8, rank 3; Adam; 5 steps"),
+        param_shapes=tuple(TINY),
+        description="flat fp32 buffer of 1,000,003 params (12 tensors), world 8, rank 3; Adam; "
+                    "5 steps"),
     "llama7b_shard": Workload(
         cfg=2, name="llama7b_shard", total=sum(numel_of(s) for _, s in LLAMA7B), world=8, rank=0,
         steps=3, micro_batches=8, grad_dtype="bf16", grad_std=1e-3, lr=3e-4, beta1=0.9,
@@ -215,6 +236,25 @@ def unit_tensors(w: Workload, device="cpu"):
         g = _gen(seed_of(w.cfg, PURPOSE_UNIT, 0, i), device)
         t = torch.rand(shape, generator=g, device=device, dtype=torch.float32).mul_(0.2).sub_(0.1)
         out.append(t.to(torch.bfloat16))
+    return out
+
+
+def param_tensors(w: Workload, device="cpu"):
+    """The model's fp32 parameters, U(-0.1, 0.1), one tensor per shape."""
+    out = []
+    for i, (_, shape) in enumerate(w.param_shapes):
+        g = _gen(seed_of(w.cfg, PURPOSE_UNIT, 0, i), device)
+        out.append(torch.rand(shape, generator=g, device=device, dtype=torch.float32).mul_(0.2).sub_(0.1))
+    return out
+
+
+def grad_tensors(w: Workload, step: int, device="cpu"):
+    """The model's gradients at 1-based step ``step``: fp32 std * z per tensor
+    (already the sum over ranks; the workload's grad_scale averages it)."""
+    out = []
+    for i, (_, shape) in enumerate(w.param_shapes):
+        g = _gen(seed_of(w.cfg, PURPOSE_TENSOR_GRAD, step, i), device)
+        out.append(torch.randn(shape, generator=g, device=device, dtype=torch.float32).mul_(w.std_at(step)))
     return out
 
 
