@@ -20,7 +20,7 @@
 // covers 1 KiB of a stream with no gaps.  One-shot grid of one-wave
 // workgroups (256 elements each), with residency capped at 10 workgroups
 // per CU: each workgroup reserves 16 KiB of LDS it never touches, out of
-// gfx950's 160 KiB per CU.  Eight concurrent streams per element (4 read,
+// gfx950's 160 KiB per CU (12 KiB, 13 per CU, for the six-stream forms).  Eight concurrent streams per element (4 read,
 // 4 written) otherwise keep too many DRAM rows open at once; on gfx950 the
 // cap lifts the kernel from 74 % to 83 % of the 8 TB/s peak (fewer waves:
 // 64-71 %; more: 73-81 %).  A misaligned shard (a view whose element offset
@@ -76,9 +76,13 @@ __device__ __forceinline__ bool clip_coef(const AdamwArgs& a, float& coef) {
     return true;
 }
 
-// vector path: one wave per workgroup, 16 KiB of LDS reserved per workgroup
+// vector path: one wave per workgroup, with LDS reserved per workgroup to
+// cap residency: 16 KiB (10 workgroups per CU) for the eight-stream master
+// forms; 12 KiB (13 per CU) for the six-stream no-master and update forms,
+// which measured 84-85 % there against 80-82 % at 16 KiB.
 constexpr int kVecBlock = 64;
 constexpr unsigned kVecLdsReserve = 16384;
+constexpr unsigned kVecLdsReserve6 = 12288;
 
 // What a step reads and writes besides grad, exp_avg and exp_avg_sq:
 //   kMaster      R/W fp32 master                          28 B/element
@@ -163,7 +167,8 @@ hipError_t launch(const AdamwArgs& a, unsigned lds, hipStream_t stream) {
 
 template <int FORM>
 hipError_t launch_form(const AdamwArgs& a, bool vec_ok, hipStream_t stream) {
-    if (vec_ok) return launch<4, FORM, kVecBlock>(a, kVecLdsReserve, stream);
+    constexpr unsigned lds = (FORM == kNoMaster || FORM == kUpdate) ? kVecLdsReserve6 : kVecLdsReserve;
+    if (vec_ok) return launch<4, FORM, kVecBlock>(a, lds, stream);
     return launch<1, FORM, kBlock>(a, 0, stream);
 }
 
