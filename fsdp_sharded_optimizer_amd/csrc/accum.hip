@@ -163,10 +163,19 @@ namespace {
 // Layout: one-wave workgroups, two groups of 4 elements per lane, 256
 // elements apart (every chunk's loads for both groups issued before the
 // fold): 76 % of the HBM peak on gfx950 for 8 bf16 chunks, against 68 % for
-// one group per lane in 256-thread workgroups.  Capping residency, which
-// helps adamw, hurts this read-heavy kernel.
+// one group per lane in 256-thread workgroups.
 constexpr int kReduceBlock = 64;
 constexpr int kReduceGroups = 2;
+
+// LDS reserved (never touched) per workgroup to cap residency, by chunk
+// dtype and count, as measured on gfx950: a few bf16 chunks want a mild cap
+// (2 chunks: 81 -> 85 %, 4: 82 -> 85 %), 5-8 bf16 chunks over an 842M shard
+// 20 KiB (8 workgroups per CU: 76 -> 79 %); more chunks, or fp32 chunks
+// beyond two, run best uncapped.
+unsigned reduce_lds_reserve(bool bf16, int count) {
+    if (bf16) return count <= 2 ? 8192u : count <= 4 ? 12288u : count <= 8 ? 20480u : 0u;
+    return count <= 2 ? 12288u : 0u;
+}
 
 // The loaded words stay in their storage width (2 VGPRs per bf16 group, not
 // 4) until the fold widens them: with 16 chunks x 2 groups in flight this
@@ -245,7 +254,8 @@ hipError_t launch_reduce(float* acc, const ChunkBatch& b, int64_t n, hipStream_t
     const int64_t per = (int64_t)kReduceBlock * 4 * kReduceGroups;
     const int64_t blocks = (n + per - 1) / per;
     if (blocks > (int64_t)UINT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((reduce_chunks_kernel<VEC, BF16, OVERWRITE>), dim3((unsigned)blocks), dim3(kReduceBlock), 0,
+    const unsigned lds = VEC ? reduce_lds_reserve(BF16, b.count) : 0u;
+    hipLaunchKernelGGL((reduce_chunks_kernel<VEC, BF16, OVERWRITE>), dim3((unsigned)blocks), dim3(kReduceBlock), lds,
                        stream, acc, b, n);
     return hipGetLastError();
 }
