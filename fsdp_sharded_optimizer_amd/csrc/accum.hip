@@ -10,19 +10,17 @@
 // Layout: lane-contiguous groups of 4 elements (a 64-bit bf16 or 128-bit
 // fp32 load and a 128-bit fp32 access per lane).  A workgroup of BS threads
 // covers Q groups per lane, the q-th at offset q*BS*4 in its tile, every
-// load of the tile issued before the first store.  The plain forms run
-// Q = 1 in one-wave workgroups (the fastest shape on gfx950: 84 % of peak
-// for the accumulating form and 85 % for the overwriting one, against 82 %
-// and 83 % in 256-thread workgroups and 74-79 % for Q = 2 or 8 elements per
-// lane).  The fused form uses 256 threads, Q = 2, with residency capped at 5
-// workgroups per CU (each reserves 32 KiB of gfx950's 160 KiB LDS without
-// touching it): 79 % of peak, against 75 % for its best uncapped shape; the
-// workgroup reduction it adds is amortised over 2048 elements.
+// load of the tile issued before the first store.  Every form, the fused
+// one included, runs Q = 1 in one-wave workgroups, uncapped: the fastest
+// shape on gfx950 (84 % of peak for the accumulating form, 85 % for the
+// overwriting one, 84.5 % with the norm partials, against 82 %, 83 % and
+// 79.8 % in 256-thread workgroups with the best Q and residency cap).
 //
-// Fused norm association (fixed by n): each lane adds the squares of its
-// groups q = 0..Q-1, elements 0, 2 into one running sum and 1, 3 into the
-// other; lanes and waves combine in a fixed tree; workgroup partials are
-// reduced in fixed contiguous chunks, then by one workgroup.
+// Fused norm association (fixed by n): each lane adds the squares of its 4
+// elements, 0 and 2 into one running sum, 1 and 3 into the other; the 64
+// lanes combine in a fixed butterfly into one binary64 partial per 256
+// elements; the partials are reduced in fixed contiguous chunks (at most
+// kReduceChunks), then by one workgroup.
 #include "reduce.h"
 
 namespace zs {
@@ -47,7 +45,7 @@ __device__ __forceinline__ float load1(const void* grad, int64_t i) {
 template <int Q, int BS, bool VEC, bool BF16, bool OVERWRITE, bool NORM>
 __global__ __launch_bounds__(BS) void accum_kernel(float* __restrict__ acc, const void* __restrict__ grad,
                                                    int64_t n, float scale, double* __restrict__ partials) {
-    static_assert(!NORM || BS == kBlock, "the fused norm's workgroup tree assumes kBlock threads");
+    static_assert(!NORM || BS == 64, "the fused norm's partial is one wave's butterfly");
     constexpr int64_t kGroup = BS * 4;
     const int64_t tile = (int64_t)blockIdx.x * kGroup * Q;
     const int64_t lane0 = tile + threadIdx.x * 4;
@@ -91,29 +89,24 @@ __global__ __launch_bounds__(BS) void accum_kernel(float* __restrict__ acc, cons
         }
     }
     if (NORM) {
-        const double total = block_sum(s0 + s1);
+        const double total = wave_sum(s0 + s1);
         if (threadIdx.x == 0) partials[blockIdx.x] = total;
     }
 }
 
-// threads per workgroup: one wave for the plain forms, kBlock when fused
-template <bool NORM>
-constexpr int block_of() { return NORM ? kBlock : 64; }
+constexpr int kAccumBlock = 64;   // one wave per workgroup
 
-template <int Q, bool NORM>
-constexpr int64_t per_block() { return (int64_t)block_of<NORM>() * 4 * Q; }
+template <int Q>
+constexpr int64_t per_block() { return (int64_t)kAccumBlock * 4 * Q; }
 
-constexpr int kFusedQ = 2;
-constexpr unsigned kFusedLdsReserve = 32768;   // 5 workgroups per CU
+constexpr int kFusedQ = 1;
 
 template <int Q, bool VEC, bool BF16, bool OVERWRITE, bool NORM>
 hipError_t launch(float* acc, const void* grad, int64_t n, float scale, double* partials, hipStream_t stream) {
-    constexpr int BS = block_of<NORM>();
-    const int64_t blocks = (n + per_block<Q, NORM>() - 1) / per_block<Q, NORM>();
+    const int64_t blocks = (n + per_block<Q>() - 1) / per_block<Q>();
     if (blocks > (int64_t)UINT32_MAX) return hipErrorInvalidValue;
-    const unsigned lds = (NORM && VEC) ? kFusedLdsReserve : 0;
-    hipLaunchKernelGGL((accum_kernel<Q, BS, VEC, BF16, OVERWRITE, NORM>), dim3((unsigned)blocks), dim3(BS), lds,
-                       stream, acc, grad, n, scale, partials);
+    hipLaunchKernelGGL((accum_kernel<Q, kAccumBlock, VEC, BF16, OVERWRITE, NORM>), dim3((unsigned)blocks),
+                       dim3(kAccumBlock), 0, stream, acc, grad, n, scale, partials);
     return hipGetLastError();
 }
 
@@ -140,7 +133,7 @@ hipError_t launch_grad_accum(float* acc, const void* grad, int grad_bf16, int64_
 }
 
 int64_t accum_norm_partials(int64_t n) {
-    return n <= 0 ? 0 : (n + per_block<kFusedQ, true>() - 1) / per_block<kFusedQ, true>();
+    return n <= 0 ? 0 : (n + per_block<kFusedQ>() - 1) / per_block<kFusedQ>();
 }
 
 hipError_t launch_grad_accum_norm_sq(float* acc, const void* grad, int grad_bf16, int64_t n, int overwrite,

@@ -210,7 +210,7 @@ def test_grad_accum_norm_sq_rejects():
     L = zs.lib()
     n = 1 << 20
     need = zs.grad_accum_norm_sq_workspace_bytes(n)
-    assert need == (n // 2048 + 256) * 8
+    assert need == (n // 256 + 2048) * 8         # one partial per 256 elements + the chunk stage
     assert zs.grad_accum_norm_sq_workspace_bytes(0) == 0 and zs.grad_accum_norm_sq_workspace_bytes(-3) == -1
     acc, g, ws, out = FAKE, FAKE + 2**30, FAKE + 2**31, FAKE + 2**32
     call = lambda **k: L.grad_accum_norm_sq(k.get("acc", acc), k.get("g", g), k.get("dt", B.ZS_BF16), k.get("n", n),
