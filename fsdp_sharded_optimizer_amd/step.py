@@ -38,7 +38,6 @@ class ShardOptimizer:
         self._norm_ready = False
         self.t = 0
         self._pending = 0
-        self._norm_ready = False
 
     def accumulate(self, grad: torch.Tensor, last: bool = False) -> None:
         """Add one micro-batch gradient (fp32 or bf16) into the fp32 buffer.

@@ -1,0 +1,63 @@
+"""ShardOptimizer (the call-ordering layer) on the GPU against the oracle.
+
+Four bf16 micro-batches per step, a global-norm clip with the other ranks'
+share as a stand-in, three steps, on a ragged shard; once with the norm
+formed in the last accumulation pass and once with a separate norm pass.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import fsdp_sharded_optimizer_amd as zs
+from tests.parity import NORM_TOL, StateCheck, bits_equal, from_np, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_shard_optimizer_matches_the_oracle(fused):
+    print(f"ShardOptimizer fused={fused}", flush=True)
+    n, M, scale, lr, wd = 100_003, 4, 1 / 32, 3e-4, 0.1
+    rng = np.random.default_rng(17)
+    p0 = rng.uniform(-0.1, 0.1, n).astype(np.float32)
+    master = from_np(p0.copy())
+    param = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    opt = zs.ShardOptimizer(master, lr=lr, betas=(0.9, 0.95), weight_decay=wd, grad_scale=scale, max_norm=1.0,
+                            param_bf16=param)
+    p_ref, m_ref, v_ref = p0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    b_ref = np.zeros(n, np.uint16)
+    for t in range(1, 4):
+        mbs = [oracle.bf16_rne((rng.standard_normal(n) * 0.05 * t).astype(np.float32)) for _ in range(M)]
+        acc_ref = np.empty(n, np.float32)
+        for k, g in enumerate(mbs):
+            oracle.grad_accum(acc_ref, g, oracle.BF16, overwrite=(k == 0))
+            opt.accumulate(from_np(g, bf16=True), last=fused and k == M - 1)
+        S = oracle.grad_norm_sq(acc_ref, scale)
+        extra = 3.0 * S                                   # the other ranks' share
+        prev = {"p": p_ref.copy(), "m": m_ref.copy()}
+        H = oracle.make_hp(lr, 0.9, 0.95, 1e-8, wd, scale, 1.0, extra, t)
+        assert oracle.adamw_step(H, p_ref, m_ref, v_ref, acc_ref, b_ref, norm_sq=S) == 0
+        opt.step(extra_norm_sq=extra)
+        torch.cuda.synchronize()
+        assert opt.t == t
+        assert bits_equal(to_np(opt.acc), acc_ref)
+        assert abs(opt.norm_sq.item() - S) <= NORM_TOL * S
+        coef = oracle.clip_coef(S, extra, 1.0)
+        assert coef < 1.0                                 # every step clips
+        g2 = (acc_ref * np.float32(scale)) * np.float32(coef)
+        s = oracle.adamw_scalars(H)
+        gpu = {"p": to_np(master), "m": to_np(opt.exp_avg), "v": to_np(opt.exp_avg_sq), "b": to_np(param)}
+        res = StateCheck(0.9, lr, wd, s.step_size).check(gpu, {"p": p_ref, "m": m_ref, "v": v_ref, "b": b_ref},
+                                                          prev, g2, f"t={t}")
+        print(f"  t={t} norm {math.sqrt(S + extra):.4f} coef {coef:.4f} {res}", flush=True)
+
+
+def test_shard_optimizer_refuses_a_step_without_gradients():
+    opt = zs.ShardOptimizer(torch.zeros(16, device="cuda"), lr=1e-3)
+    with pytest.raises(RuntimeError):
+        opt.step()
+    with pytest.raises(TypeError):
+        zs.ShardOptimizer(torch.zeros(16, device="cuda", dtype=torch.float64), lr=1e-3)
