@@ -96,8 +96,11 @@ __global__ __launch_bounds__(BS) void adamw_kernel(const AdamwArgs a) {
     constexpr bool kReadP = FORM != kUpdate;
     const int64_t n = a.n;
     const int64_t first = ((int64_t)blockIdx.x * BS + threadIdx.x) * VEC;
-    if (first >= n) return;
-
+    // No early exit for lanes past the end: they fall through the scalar
+    // path's empty loop.  Every path then uses the buffer pointers, so the
+    // kernel-argument loads issue together with n's instead of one round
+    // trip after it (a second scalar round trip before the first vector load
+    // costs every workgroup of this residency-capped launch).
     if (VEC == 4 && first + 4 <= n) {
         // One 128-bit access per fp32 stream, lane-contiguous across the wave.
         // The loads are issued before the clip coefficient is resolved, so
