@@ -7,6 +7,7 @@ Flags that matter for the numerics and for gfx950:
   -fhip-fp32-correctly-rounded-divide-sqrt   IEEE fp32 division and square root
   -Xclang -target-feature -Xclang -packed-fp32-ops
                                              no packed-fp32 (v_pk_*_f32) instructions
+  -fvisibility=hidden                        export only the C ABI (ZS_API in zshard.h)
 """
 from __future__ import annotations
 
@@ -21,7 +22,7 @@ LIB = os.path.join(HERE, "libzshard.so")
 ARCH = "gfx950"
 
 FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-command-line-argument",

@@ -39,6 +39,14 @@
 
 #include <stdint.h>
 
+/* Only the functions below are exported from libzshard.so; the library is
+ * built with hidden visibility for everything else. */
+#if defined(__GNUC__) || defined(__clang__)
+#define ZS_API __attribute__((visibility("default")))
+#else
+#define ZS_API
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -97,7 +105,7 @@ typedef struct {
  * Errors: ZS_EINVAL for out == NULL, world < 1, rank outside [0, world),
  * total < 0, or world*chunk overflowing int64.
  */
-int32_t zero_shard_range(int64_t total, int32_t world, int32_t rank, zs_shard* out);
+ZS_API int32_t zero_shard_range(int64_t total, int32_t world, int32_t rank, zs_shard* out);
 
 /*
  * flat_pack — the FlatParameter flatten.
@@ -114,7 +122,7 @@ int32_t zero_shard_range(int64_t total, int32_t world, int32_t rank, zs_shard* o
  * dtype pair, null/misaligned pointer), ZS_EOVERLAP (a source overlaps
  * flat), ZS_EHIP.
  */
-int32_t flat_pack(const zs_tensor* src, int32_t count, int32_t src_dtype,
+ZS_API int32_t flat_pack(const zs_tensor* src, int32_t count, int32_t src_dtype,
                   void* flat, int32_t flat_dtype, int64_t padded_total, void* hip_stream);
 
 /*
@@ -127,7 +135,7 @@ int32_t flat_pack(const zs_tensor* src, int32_t count, int32_t src_dtype,
  * round-to-nearest-even re-cast (NaN -> 0x7FC0).
  * Errors: as flat_pack.
  */
-int32_t flat_unpack(const void* flat, int32_t flat_dtype,
+ZS_API int32_t flat_unpack(const void* flat, int32_t flat_dtype,
                     const zs_tensor* dst, int32_t count, int32_t dst_dtype, void* hip_stream);
 
 /*
@@ -144,7 +152,7 @@ int32_t flat_unpack(const void* flat, int32_t flat_dtype,
  * Errors: ZS_EINVAL (count < 0, negative numel, dtype, null/misaligned
  * pointer), ZS_EOVERLAP, ZS_EHIP.
  */
-int32_t flat_apply_update(const float* update, const zs_tensor* dst, int32_t count, int32_t dst_dtype,
+ZS_API int32_t flat_apply_update(const float* update, const zs_tensor* dst, int32_t count, int32_t dst_dtype,
                           void* hip_stream);
 
 /*
@@ -157,7 +165,7 @@ int32_t flat_apply_update(const float* update, const zs_tensor* dst, int32_t cou
  * acc: device fp32[n], read-write; grad: device [n] of grad_dtype, read.
  * Errors: ZS_EINVAL, ZS_EOVERLAP (acc overlaps grad), ZS_EHIP.
  */
-int32_t grad_accum(float* acc, const void* grad, int32_t grad_dtype, int64_t n,
+ZS_API int32_t grad_accum(float* acc, const void* grad, int32_t grad_dtype, int64_t n,
                    int32_t overwrite, void* hip_stream);
 
 /*
@@ -176,14 +184,14 @@ int32_t grad_accum(float* acc, const void* grad, int32_t grad_dtype, int64_t n,
  * Errors: ZS_EINVAL (count < 0, count == 0 with overwrite, null/misaligned
  * pointer, dtype), ZS_EOVERLAP (a chunk overlaps acc), ZS_EHIP.
  */
-int32_t grad_reduce_chunks(float* acc, const void* const* chunks, int32_t count, int32_t grad_dtype, int64_t n,
+ZS_API int32_t grad_reduce_chunks(float* acc, const void* const* chunks, int32_t count, int32_t grad_dtype, int64_t n,
                            int32_t overwrite, void* hip_stream);
 
 /*
  * grad_norm_sq_workspace_bytes — bytes of device workspace grad_norm_sq
  * needs for n elements (0 for n == 0; -1 for n < 0).  Host only.
  */
-int64_t grad_norm_sq_workspace_bytes(int64_t n);
+ZS_API int64_t grad_norm_sq_workspace_bytes(int64_t n);
 
 /*
  * grad_norm_sq — this shard's share of the squared global gradient norm.
@@ -201,14 +209,14 @@ int64_t grad_norm_sq_workspace_bytes(int64_t n);
  * stream reaches the end of this call.
  * Errors: ZS_EINVAL, ZS_EWORKSPACE, ZS_EOVERLAP, ZS_EHIP.
  */
-int32_t grad_norm_sq(const float* grad, int64_t n, double grad_scale, double* out_sq_dev,
+ZS_API int32_t grad_norm_sq(const float* grad, int64_t n, double grad_scale, double* out_sq_dev,
                      void* workspace, int64_t workspace_bytes, void* hip_stream);
 
 /*
  * grad_accum_norm_sq_workspace_bytes — bytes of device workspace
  * grad_accum_norm_sq needs for n elements (0 for n == 0; -1 for n < 0).
  */
-int64_t grad_accum_norm_sq_workspace_bytes(int64_t n);
+ZS_API int64_t grad_accum_norm_sq_workspace_bytes(int64_t n);
 
 /*
  * grad_accum_norm_sq — grad_accum fused with grad_norm_sq for the last
@@ -227,7 +235,7 @@ int64_t grad_accum_norm_sq_workspace_bytes(int64_t n);
  * Errors: ZS_EINVAL, ZS_EWORKSPACE, ZS_EOVERLAP (any two of acc, grad,
  * *out_sq_dev, workspace), ZS_EHIP.
  */
-int32_t grad_accum_norm_sq(float* acc, const void* grad, int32_t grad_dtype, int64_t n, int32_t overwrite,
+ZS_API int32_t grad_accum_norm_sq(float* acc, const void* grad, int32_t grad_dtype, int64_t n, int32_t overwrite,
                            double grad_scale, double* out_sq_dev, void* workspace, int64_t workspace_bytes,
                            void* hip_stream);
 
@@ -259,7 +267,7 @@ int32_t grad_accum_norm_sq(float* acc, const void* grad, int32_t grad_dtype, int
  * them may overlap, nor overlap *norm_sq_dev.
  * Errors: ZS_EINVAL (hp NULL or out of range, pointers), ZS_EOVERLAP, ZS_EHIP.
  */
-int32_t adamw_step(const zs_adamw* hp, float* master, float* exp_avg, float* exp_avg_sq,
+ZS_API int32_t adamw_step(const zs_adamw* hp, float* master, float* exp_avg, float* exp_avg_sq,
                    const float* grad, uint16_t* param_bf16, int64_t n,
                    const double* norm_sq_dev, void* hip_stream);
 
@@ -276,7 +284,7 @@ int32_t adamw_step(const zs_adamw* hp, float* master, float* exp_avg, float* exp
  * fp32[n], read-write; grad: device fp32[n], read; norm_sq_dev as in
  * adamw_step.  Errors: as adamw_step.
  */
-int32_t adamw_step_no_master(const zs_adamw* hp, uint16_t* param_bf16, float* exp_avg, float* exp_avg_sq,
+ZS_API int32_t adamw_step_no_master(const zs_adamw* hp, uint16_t* param_bf16, float* exp_avg, float* exp_avg_sq,
                              const float* grad, int64_t n, const double* norm_sq_dev, void* hip_stream);
 
 /*
@@ -296,14 +304,14 @@ int32_t adamw_step_no_master(const zs_adamw* hp, uint16_t* param_bf16, float* ex
  * Errors: ZS_EINVAL (as adamw_step, or weight_decay != 0), ZS_EOVERLAP,
  * ZS_EHIP.
  */
-int32_t adam_update(const zs_adamw* hp, float* exp_avg, float* exp_avg_sq, const float* grad, float* update,
+ZS_API int32_t adam_update(const zs_adamw* hp, float* exp_avg, float* exp_avg_sq, const float* grad, float* update,
                     int64_t n, const double* norm_sq_dev, void* hip_stream);
 
 /* Static description of a return code. */
-const char* zs_strerror(int32_t code);
+ZS_API const char* zs_strerror(int32_t code);
 
 /* The hipError_t of the last ZS_EHIP on this thread (0 if none). */
-int32_t zs_last_hip_error(void);
+ZS_API int32_t zs_last_hip_error(void);
 
 #ifdef __cplusplus
 }

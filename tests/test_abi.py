@@ -24,7 +24,7 @@ HEADER = os.path.join(ROOT, "include", "zshard.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*ZS_API\s+(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)))
 
 
 @pytest.fixture(autouse=True)
@@ -37,10 +37,24 @@ def no_launch_reached():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert set(names) == set(B.EXPORTS), names
+    assert len(names) == 15 and set(names) == set(B.EXPORTS), names
     L = zs.lib()
     for name in names:
         assert getattr(L, name) is not None
+
+
+def test_library_exports_nothing_else():
+    """The dynamic symbol table holds the declared functions and no internal
+    (launcher, kernel stub) symbol of the library's own code."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    defined = {line.split()[-1] for line in out.splitlines() if line.split() and line.split()[-2] in ("T", "W")}
+    ours = {s for s in defined if s.startswith("_ZN2zs") or s in B.EXPORTS}
+    assert ours == set(B.EXPORTS), sorted(ours - set(B.EXPORTS))
 
 
 def test_shard_range_matches_oracle_brute_force(orc):
