@@ -143,13 +143,17 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 def _dev(t: Optional[torch.Tensor], name: str, dtype=None) -> int:
-    """Device pointer of a contiguous GPU tensor (0 for None)."""
+    """Device pointer of a contiguous tensor on the current GPU (0 for None).
+    Every call runs on the current device's stream, so every buffer must live
+    on that device."""
     if t is None:
         return 0
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name}: expected a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name}: must be a GPU tensor, got {t.device}")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name}: on {t.device}, but the current device is cuda:{torch.cuda.current_device()}")
     if not t.is_contiguous():
         raise ValueError(f"{name}: must be contiguous")
     if dtype is not None and t.dtype != dtype:
@@ -159,7 +163,17 @@ def _dev(t: Optional[torch.Tensor], name: str, dtype=None) -> int:
 
 def _stream(stream=None) -> int:
     s = stream if stream is not None else torch.cuda.current_stream()
+    if s.device.index != torch.cuda.current_device():
+        raise ValueError(f"stream on {s.device}, but the current device is cuda:{torch.cuda.current_device()}")
     return int(s.cuda_stream)
+
+
+def _norm(norm_sq: Optional[torch.Tensor], fn: str) -> int:
+    if norm_sq is None:
+        return 0
+    if norm_sq.dtype != torch.float64 or norm_sq.numel() < 1:
+        raise TypeError(f"{fn}: norm_sq must hold one float64")
+    return _dev(norm_sq, "norm_sq")
 
 
 # ---------------------------------------------------------------------------
@@ -303,13 +317,11 @@ def adamw_step(hp: AdamWConfig, master: torch.Tensor, exp_avg: torch.Tensor, exp
             raise ValueError(f"adamw_step: {nm} size mismatch")
     if param_bf16 is not None and param_bf16.numel() != n:
         raise ValueError("adamw_step: param_bf16 size mismatch")
-    if norm_sq is not None and norm_sq.dtype != torch.float64:
-        raise TypeError("adamw_step: norm_sq must be float64")
     c = hp.c_struct()
     _check("adamw_step", lib().adamw_step(
         ctypes.byref(c), _dev(master, "master", torch.float32), _dev(exp_avg, "exp_avg", torch.float32),
         _dev(exp_avg_sq, "exp_avg_sq", torch.float32), _dev(grad, "grad", torch.float32),
-        _dev(param_bf16, "param_bf16", torch.bfloat16), n, _dev(norm_sq, "norm_sq"), _stream(stream)))
+        _dev(param_bf16, "param_bf16", torch.bfloat16), n, _norm(norm_sq, "adamw_step"), _stream(stream)))
 
 
 def adamw_step_no_master(hp: AdamWConfig, param_bf16: torch.Tensor, exp_avg: torch.Tensor,
@@ -320,13 +332,11 @@ def adamw_step_no_master(hp: AdamWConfig, param_bf16: torch.Tensor, exp_avg: tor
     for t, nm in ((exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq"), (grad, "grad")):
         if t.numel() != n:
             raise ValueError(f"adamw_step_no_master: {nm} size mismatch")
-    if norm_sq is not None and norm_sq.dtype != torch.float64:
-        raise TypeError("adamw_step_no_master: norm_sq must be float64")
     c = hp.c_struct()
     _check("adamw_step_no_master", lib().adamw_step_no_master(
         ctypes.byref(c), _dev(param_bf16, "param_bf16", torch.bfloat16), _dev(exp_avg, "exp_avg", torch.float32),
         _dev(exp_avg_sq, "exp_avg_sq", torch.float32), _dev(grad, "grad", torch.float32), n,
-        _dev(norm_sq, "norm_sq"), _stream(stream)))
+        _norm(norm_sq, "adamw_step_no_master"), _stream(stream)))
 
 
 def adam_update(hp: AdamWConfig, exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor, grad: torch.Tensor,
@@ -337,10 +347,8 @@ def adam_update(hp: AdamWConfig, exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor
     for t, nm in ((exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq"), (grad, "grad")):
         if t.numel() != n:
             raise ValueError(f"adam_update: {nm} size mismatch")
-    if norm_sq is not None and norm_sq.dtype != torch.float64:
-        raise TypeError("adam_update: norm_sq must be float64")
     c = hp.c_struct()
     _check("adam_update", lib().adam_update(
         ctypes.byref(c), _dev(exp_avg, "exp_avg", torch.float32), _dev(exp_avg_sq, "exp_avg_sq", torch.float32),
         _dev(grad, "grad", torch.float32), _dev(update, "update", torch.float32), n,
-        _dev(norm_sq, "norm_sq"), _stream(stream)))
+        _norm(norm_sq, "adam_update"), _stream(stream)))

@@ -542,3 +542,15 @@ def test_flat_apply_update_bit_exact(dtype, count, aligned_sizes, upd_offset):
     for d, r in zip(params, p_ref):
         assert bits_equal(to_np(d).reshape(-1), r)
     assert canary_ok(upd_whole, upd_offset, T + 13)
+
+
+def test_binding_rejects_bad_norm_buffers():
+    """The binding refuses a norm buffer that is not one float64, before any launch."""
+    n = 1024
+    p, m, v, g = (torch.zeros(n, device="cuda") for _ in range(4))
+    hp = _hp(1)[0]
+    for bad in (torch.zeros(1, device="cuda"), torch.zeros(0, dtype=torch.float64, device="cuda")):
+        with pytest.raises(TypeError):
+            zs.adamw_step(hp, p, m, v, g, norm_sq=bad)
+    with pytest.raises(ValueError):
+        zs.adamw_step(hp, p, m, v, g[:-1])
