@@ -36,8 +36,11 @@ inline int64_t elem_size(int32_t dtype) { return dtype == ZS_F32 ? 4 : 2; }
 inline bool dtype_ok(int32_t d) { return d == ZS_F32 || d == ZS_BF16; }
 inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
-// elements whose byte size fits in int64 and in the address space
-inline bool size_ok(int64_t n, int64_t esize) { return n >= 0 && n <= INT64_MAX / 16 / esize; }
+// At most 2^39 elements per call (2 TiB of fp32, beyond any one GPU's
+// memory): byte sizes stay far inside int64, and every launch grid (tiles of
+// 256 elements or more) fits the 32-bit grid dimension.
+constexpr int64_t kMaxElems = int64_t(1) << 39;
+inline bool size_ok(int64_t n) { return n >= 0 && n <= kMaxElems; }
 
 }  // namespace
 
@@ -73,7 +76,7 @@ int32_t zero_shard_range(int64_t total, int32_t world, int32_t rank, zs_shard* o
 
 int32_t grad_accum(float* acc, const void* grad, int32_t grad_dtype, int64_t n, int32_t overwrite,
                    void* hip_stream) {
-    if (!dtype_ok(grad_dtype) || !size_ok(n, 4)) return ZS_EINVAL;
+    if (!dtype_ok(grad_dtype) || !size_ok(n)) return ZS_EINVAL;
     if (n == 0) return ZS_OK;
     const int64_t gsz = elem_size(grad_dtype);
     if (acc == nullptr || grad == nullptr) return ZS_EINVAL;
@@ -86,7 +89,7 @@ int32_t grad_accum(float* acc, const void* grad, int32_t grad_dtype, int64_t n, 
 
 int32_t grad_reduce_chunks(float* acc, const void* const* chunks, int32_t count, int32_t grad_dtype, int64_t n,
                            int32_t overwrite, void* hip_stream) {
-    if (!dtype_ok(grad_dtype) || !size_ok(n, 4) || count < 0) return ZS_EINVAL;
+    if (!dtype_ok(grad_dtype) || !size_ok(n) || count < 0) return ZS_EINVAL;
     if (n == 0) return ZS_OK;
     if (count == 0) return overwrite ? ZS_EINVAL : ZS_OK;
     if (acc == nullptr || chunks == nullptr || !aligned(acc, 4)) return ZS_EINVAL;
@@ -117,7 +120,7 @@ int64_t grad_norm_sq_workspace_bytes(int64_t n) {
 
 int32_t grad_norm_sq(const float* grad, int64_t n, double grad_scale, double* out_sq_dev,
                      void* workspace, int64_t workspace_bytes, void* hip_stream) {
-    if (!size_ok(n, 4) || out_sq_dev == nullptr || !aligned(out_sq_dev, 8)) return ZS_EINVAL;
+    if (!size_ok(n) || out_sq_dev == nullptr || !aligned(out_sq_dev, 8)) return ZS_EINVAL;
     if (!(grad_scale > 0.0) || !std::isfinite(grad_scale)) return ZS_EINVAL;
     const int64_t need = grad_norm_sq_workspace_bytes(n);
     if (n > 0 && (grad == nullptr || !aligned(grad, 4))) return ZS_EINVAL;
@@ -141,7 +144,7 @@ int64_t grad_accum_norm_sq_workspace_bytes(int64_t n) {
 int32_t grad_accum_norm_sq(float* acc, const void* grad, int32_t grad_dtype, int64_t n, int32_t overwrite,
                            double grad_scale, double* out_sq_dev, void* workspace, int64_t workspace_bytes,
                            void* hip_stream) {
-    if (!dtype_ok(grad_dtype) || !size_ok(n, 4)) return ZS_EINVAL;
+    if (!dtype_ok(grad_dtype) || !size_ok(n)) return ZS_EINVAL;
     if (out_sq_dev == nullptr || !aligned(out_sq_dev, 8)) return ZS_EINVAL;
     if (!(grad_scale > 0.0) || !std::isfinite(grad_scale)) return ZS_EINVAL;
     const int64_t gsz = elem_size(grad_dtype);
@@ -162,7 +165,7 @@ int32_t grad_accum_norm_sq(float* acc, const void* grad, int32_t grad_dtype, int
 }
 
 static int32_t adamw_check_hp(const zs_adamw* hp, int64_t n, const double* norm_sq_dev) {
-    if (hp == nullptr || !size_ok(n, 4)) return ZS_EINVAL;
+    if (hp == nullptr || !size_ok(n)) return ZS_EINVAL;
     if (hp->step < 1) return ZS_EINVAL;
     if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0) || !(hp->beta2 >= 0.0 && hp->beta2 < 1.0))
         return ZS_EINVAL;
@@ -310,13 +313,13 @@ static int32_t flat_common(const zs_tensor* tensors, int32_t count, void* flat, 
     int64_t total = 0;
     for (int32_t i = 0; i < count; ++i) {
         const int64_t k = tensors[i].numel;
-        if (!size_ok(k, 4) || total > INT64_MAX / 16 / 4 - k) return ZS_EINVAL;
+        if (!size_ok(k) || total > kMaxElems - k) return ZS_EINVAL;
         if (k > 0 && (tensors[i].ptr == nullptr || !aligned(tensors[i].ptr, (uintptr_t)tsz)))
             return ZS_EINVAL;
         total += k;
     }
     if (unpack) padded_total = total;
-    if (!size_ok(padded_total, 4) || total > padded_total) return ZS_EINVAL;
+    if (!size_ok(padded_total) || total > padded_total) return ZS_EINVAL;
     if (padded_total == 0) return ZS_OK;
     if (flat == nullptr || !aligned(flat, (uintptr_t)fsz)) return ZS_EINVAL;
     for (int32_t i = 0; i < count; ++i) {

@@ -29,6 +29,8 @@
  *   - Arguments are validated on the host before anything is enqueued; on
  *     failure the call returns a negative code and launches nothing.
  *     n == 0 (or count == 0 with nothing to pad) is a valid no-op.
+ *   - Element counts (n, numel, padded_total, their sums) are at most 2^39
+ *     per call; larger counts are ZS_EINVAL.
  *   - fp32 pointers must be 4-byte aligned, bf16 pointers 2-byte aligned,
  *     fp64 pointers 8-byte aligned.  Any alignment beyond that only selects
  *     a faster code path (16-byte aligned buffers use 128-bit accesses).

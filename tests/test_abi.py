@@ -282,3 +282,20 @@ def test_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(ValueError):
         zs.grad_accum(torch.zeros(4), torch.zeros(4), overwrite=True)
+
+
+def test_element_count_limit():
+    """More than 2^39 elements in one call is refused before any launch
+    (every launch grid then fits 32 bits); far-apart fake buffers so that only
+    the count is wrong."""
+    L = zs.lib()
+    big = (1 << 39) + 1
+    step = 1 << 42
+    a, g = FAKE, FAKE + step
+    assert L.grad_accum(a, g, B.ZS_BF16, big, 1, None) == B.ZS_EINVAL
+    assert L.grad_reduce_chunks(a, (ctypes.c_void_p * 1)(g), 1, B.ZS_BF16, big, 1, None) == B.ZS_EINVAL
+    assert L.grad_norm_sq(a, big, 1.0, g, FAKE + 2 * step, 1 << 40, None) == B.ZS_EINVAL
+    assert _adamw(_hp(), master=FAKE, m=FAKE + step, v=FAKE + 2 * step, g=FAKE + 3 * step, n=big) == B.ZS_EINVAL
+    assert L.flat_unpack(a, B.ZS_F32, _tensors((g, big)), 1, B.ZS_F32, None) == B.ZS_EINVAL
+    half = (1 << 38) + 1   # each tensor allowed, their sum not
+    assert L.flat_unpack(a, B.ZS_F32, _tensors((g, half), (g + step, half)), 2, B.ZS_F32, None) == B.ZS_EINVAL
