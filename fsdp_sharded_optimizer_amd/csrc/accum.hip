@@ -28,12 +28,12 @@ namespace {
 
 template <bool BF16>
 __device__ __forceinline__ f32x4 load4(const void* grad, int64_t i) {
-    if (BF16) {
-        const u32x2 w = ld_stream(reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(grad) + i));
+    if (BF16) {   // read-only: dword alignment suffices
+        const u32x2 w = ld_stream_u32x2_a4(static_cast<const uint16_t*>(grad) + i);
         return f32x4{bf16_to_f32(w.x & 0xFFFFu), bf16_to_f32(w.x >> 16),
                      bf16_to_f32(w.y & 0xFFFFu), bf16_to_f32(w.y >> 16)};
     }
-    return ld_stream(reinterpret_cast<const f32x4*>(static_cast<const float*>(grad) + i));
+    return ld_stream_f32x4_a4(static_cast<const float*>(grad) + i);
 }
 
 template <bool BF16>
@@ -185,7 +185,7 @@ template <bool BF16> struct Raw4;
 template <> struct Raw4<true> {
     using T = u32x2;
     static __device__ __forceinline__ T load(const void* p, int64_t i) {
-        return ld_stream(reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p) + i));
+        return ld_stream_u32x2_a4(static_cast<const uint16_t*>(p) + i);   // read-only: dword alignment
     }
     static __device__ __forceinline__ f32x4 widen(T w) {
         return f32x4{bf16_to_f32(w.x & 0xFFFFu), bf16_to_f32(w.x >> 16), bf16_to_f32(w.y & 0xFFFFu),
@@ -195,7 +195,7 @@ template <> struct Raw4<true> {
 template <> struct Raw4<false> {
     using T = f32x4;
     static __device__ __forceinline__ T load(const void* p, int64_t i) {
-        return ld_stream(reinterpret_cast<const f32x4*>(static_cast<const float*>(p) + i));
+        return ld_stream_f32x4_a4(static_cast<const float*>(p) + i);
     }
     static __device__ __forceinline__ f32x4 widen(T w) { return w; }
 };

@@ -25,7 +25,8 @@
 // cap lifts the kernel from 74 % to 83 % of the 8 TB/s peak (fewer waves:
 // 64-71 %; more: 73-81 %).  A misaligned shard (a view whose element offset
 // is not a multiple of 4) takes the VEC = 1 instantiation of the same code,
-// in 256-thread workgroups without the cap.
+// in 256-thread workgroups without the cap; the read-only gradient alone may
+// sit at any 4-byte boundary on the vector path.
 #include "zs_common.h"
 
 namespace zs {
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(BS) void adamw_kernel(const AdamwArgs a) {
         // One 128-bit access per fp32 stream, lane-contiguous across the wave.
         // The loads are issued before the clip coefficient is resolved, so
         // the latency of the norm's read overlaps with them.
-        const f32x4 g4 = ld_stream(reinterpret_cast<const f32x4*>(a.grad + first));
+        const f32x4 g4 = ld_stream_f32x4_a4(a.grad + first);   // read-only: dword alignment suffices
         f32x4 p4 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         if constexpr (FORM == kNoMaster) {
             const u32x2 w = ld_stream(reinterpret_cast<const u32x2*>(a.param_bf16 + first));

@@ -82,7 +82,8 @@ int32_t grad_accum(float* acc, const void* grad, int32_t grad_dtype, int64_t n, 
     if (acc == nullptr || grad == nullptr) return ZS_EINVAL;
     if (!aligned(acc, 4) || !aligned(grad, (uintptr_t)gsz)) return ZS_EINVAL;
     if (overlap(acc, n * 4, grad, n * gsz)) return ZS_EOVERLAP;
-    const bool vec = aligned(acc, 16) && aligned(grad, 16);
+    // written streams 16-byte aligned; the read-only gradient dword aligned
+    const bool vec = aligned(acc, 16) && aligned(grad, 4);
     return hip_status(zs::launch_grad_accum(acc, grad, grad_dtype == ZS_BF16, n, overwrite != 0, vec,
                                             as_stream(hip_stream)));
 }
@@ -98,7 +99,7 @@ int32_t grad_reduce_chunks(float* acc, const void* const* chunks, int32_t count,
     for (int32_t k = 0; k < count; ++k) {
         if (chunks[k] == nullptr || !aligned(chunks[k], (uintptr_t)gsz)) return ZS_EINVAL;
         if (overlap(acc, n * 4, chunks[k], n * gsz)) return ZS_EOVERLAP;
-        vec = vec && aligned(chunks[k], 16);
+        vec = vec && aligned(chunks[k], 4);   // read-only: dword alignment suffices
     }
     for (int32_t k0 = 0; k0 < count; k0 += zs::kReduceMaxChunks) {
         zs::ChunkBatch b;
@@ -129,10 +130,8 @@ int32_t grad_norm_sq(const float* grad, int64_t n, double grad_scale, double* ou
     if (overlap(grad, n * 4, out_sq_dev, 8) || overlap(workspace, need, out_sq_dev, 8) ||
         overlap(workspace, need, grad, n * 4))
         return ZS_EOVERLAP;
-    const bool vec = aligned(grad, 16);
     return hip_status(zs::launch_grad_norm_sq(grad, n, (float)grad_scale, out_sq_dev,
-                                              static_cast<double*>(workspace), vec,
-                                              as_stream(hip_stream)));
+                                              static_cast<double*>(workspace), as_stream(hip_stream)));
 }
 
 int64_t grad_accum_norm_sq_workspace_bytes(int64_t n) {
@@ -157,7 +156,7 @@ int32_t grad_accum_norm_sq(float* acc, const void* grad, int32_t grad_dtype, int
         overlap(grad, n * gsz, out_sq_dev, 8) || overlap(workspace, need, out_sq_dev, 8) ||
         overlap(workspace, need, acc, n * 4) || overlap(workspace, need, grad, n * gsz))
         return ZS_EOVERLAP;
-    const bool vec = aligned(acc, 16) && aligned(grad, 16);
+    const bool vec = aligned(acc, 16) && aligned(grad, 4);
     return hip_status(zs::launch_grad_accum_norm_sq(acc, grad, grad_dtype == ZS_BF16, n, overwrite != 0,
                                                     (float)grad_scale, out_sq_dev,
                                                     static_cast<double*>(workspace), vec,
@@ -237,8 +236,9 @@ int32_t adamw_step(const zs_adamw* hp, float* master, float* exp_avg, float* exp
     a.grad = grad;
     a.param_bf16 = param_bf16;
     a.n = n;
+    // written streams 16-byte aligned; the read-only gradient is 4-byte aligned already
     const bool vec = aligned(master, 16) && aligned(exp_avg, 16) && aligned(exp_avg_sq, 16) &&
-                     aligned(grad, 16) && (param_bf16 == nullptr || aligned(param_bf16, 16));
+                     (param_bf16 == nullptr || aligned(param_bf16, 16));
     return hip_status(zs::launch_adamw(a, vec, as_stream(hip_stream)));
 }
 
@@ -262,8 +262,7 @@ int32_t adamw_step_no_master(const zs_adamw* hp, uint16_t* param_bf16, float* ex
     a.grad = grad;
     a.param_bf16 = param_bf16;
     a.n = n;
-    const bool vec = aligned(param_bf16, 16) && aligned(exp_avg, 16) && aligned(exp_avg_sq, 16) &&
-                     aligned(grad, 16);
+    const bool vec = aligned(param_bf16, 16) && aligned(exp_avg, 16) && aligned(exp_avg_sq, 16);
     return hip_status(zs::launch_adamw_no_master(a, vec, as_stream(hip_stream)));
 }
 
@@ -287,7 +286,7 @@ int32_t adam_update(const zs_adamw* hp, float* exp_avg, float* exp_avg_sq, const
     a.grad = grad;
     a.update = update;
     a.n = n;
-    const bool vec = aligned(update, 16) && aligned(exp_avg, 16) && aligned(exp_avg_sq, 16) && aligned(grad, 16);
+    const bool vec = aligned(update, 16) && aligned(exp_avg, 16) && aligned(exp_avg_sq, 16);
     return hip_status(zs::launch_adam_update(a, vec, as_stream(hip_stream)));
 }
 
@@ -334,8 +333,6 @@ static int32_t flat_common(const zs_tensor* tensors, int32_t count, void* flat, 
     // batches of up to kFlatMaxTensors entries; the pack padding is one
     // more entry with a NULL tensor
     const int64_t tile = zs::flat_tile_elems(kind);
-    const int64_t ve = zs::flat_vec_elems(kind);
-    const bool flat16 = aligned(flat, 16);
     zs::FlatBatch b;
     std::memset(&b, 0, sizeof(b));
     b.flat = flat;
@@ -358,7 +355,11 @@ static int32_t flat_common(const zs_tensor* tensors, int32_t count, void* flat, 
         b.e[c].tensor = ptr;
         b.e[c].flat_off = flat_off;
         b.e[c].numel = numel;
-        b.e[c].vec_ok = flat16 && (flat_off % ve == 0) && (ptr == nullptr || aligned(ptr, 16));
+        // the vector path writes 16-byte aligned vectors and reads dword-aligned ones
+        const void* flat_at = static_cast<const char*>(flat) + flat_off * fsz;
+        const void* written = unpack ? ptr : flat_at;
+        const void* read = unpack ? flat_at : ptr;   // NULL: the zero fill reads nothing
+        b.e[c].vec_ok = aligned(written, 16) && (read == nullptr || aligned(read, 4));
         b.tile_start[c + 1] = b.tile_start[c] + (uint32_t)tiles;
         b.count = c + 1;
         return ZS_OK;

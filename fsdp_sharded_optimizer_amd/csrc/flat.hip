@@ -62,12 +62,12 @@ __device__ __forceinline__ typename Kind<KIND>::D apply1(typename Kind<KIND>::D 
 template <int KIND>
 __device__ __forceinline__ void apply_vec(const float* upd, typename Kind<KIND>::D* dst) {
     if constexpr (KIND == 4) {
-        const f32x4 u = ld_stream(reinterpret_cast<const f32x4*>(upd));
+        const f32x4 u = ld_stream_f32x4_a4(upd);   // read-only: dword alignment suffices
         const f32x4 p = ld_stream(reinterpret_cast<const f32x4*>(dst));
         st_stream(reinterpret_cast<f32x4*>(dst), f32x4{p.x + u.x, p.y + u.y, p.z + u.z, p.w + u.w});
     } else {
-        const f32x4 u = ld_stream(reinterpret_cast<const f32x4*>(upd));
-        const f32x4 v = ld_stream(reinterpret_cast<const f32x4*>(upd + 4));
+        const f32x4 u = ld_stream_f32x4_a4(upd);
+        const f32x4 v = ld_stream_f32x4_a4(upd + 4);
         const u32x4 w = ld_stream(reinterpret_cast<const u32x4*>(dst));
         st_stream(reinterpret_cast<u32x4*>(dst),
                   u32x4{pack_bf16x2(bf16_to_f32(w.x & 0xFFFFu) + u.x, bf16_to_f32(w.x >> 16) + u.y),
@@ -82,14 +82,14 @@ __device__ __forceinline__ void apply_vec(const float* upd, typename Kind<KIND>:
 template <int KIND>
 __device__ __forceinline__ void copy_vec(const void* src, void* dst, bool zero) {
     if constexpr (KIND == 0 || KIND == 1) {   // 16-byte bit copy
-        const u32x4 x = zero ? u32x4{0, 0, 0, 0} : ld_stream(static_cast<const u32x4*>(src));
+        const u32x4 x = zero ? u32x4{0, 0, 0, 0} : ld_stream_u32x4_a4(src);   // the read side: dword alignment
         st_stream(static_cast<u32x4*>(dst), x);
     } else if constexpr (KIND == 2) {          // 4 bf16 -> 4 fp32
-        const u32x2 w = zero ? u32x2{0, 0} : ld_stream(static_cast<const u32x2*>(src));
+        const u32x2 w = zero ? u32x2{0, 0} : ld_stream_u32x2_a4(src);
         st_stream(static_cast<u32x4*>(dst),
                   u32x4{w.x << 16, w.x & 0xFFFF0000u, w.y << 16, w.y & 0xFFFF0000u});
     } else {                                   // 4 fp32 -> 4 bf16, round to nearest even
-        const f32x4 f = zero ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : ld_stream(static_cast<const f32x4*>(src));
+        const f32x4 f = zero ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : ld_stream_f32x4_a4(src);
         st_stream(static_cast<u32x2*>(dst), u32x2{pack_bf16x2(f.x, f.y), pack_bf16x2(f.z, f.w)});
     }
 }
@@ -163,16 +163,6 @@ hipError_t launch(const FlatBatch& b, hipStream_t stream) {
 
 }  // namespace
 
-int64_t flat_vec_elems(int kind) {
-    switch (kind) {
-        case 0: return Kind<0>::VE;
-        case 1: return Kind<1>::VE;
-        case 2: return Kind<2>::VE;
-        case 3: return Kind<3>::VE;
-        case 4: return Kind<4>::VE;
-        default: return Kind<5>::VE;
-    }
-}
 int64_t flat_tile_elems(int kind) {
     switch (kind) {
         case 0: return (int64_t)Kind<0>::BS * Kind<0>::VE;

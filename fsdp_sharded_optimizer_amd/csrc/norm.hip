@@ -10,7 +10,8 @@
 // and each workgroup writes one binary64 partial to the workspace.
 // Stage 2: one workgroup adds the P partials in a fixed tree.
 // The association is fixed by n alone, so the result is bit-identical run
-// to run, whichever alignment path loaded the data.
+// to run.  The gradient is only read, so any 4-byte-aligned start takes the
+// 128-bit path.
 #include "reduce.h"
 
 namespace zs {
@@ -18,7 +19,6 @@ namespace {
 
 constexpr int64_t kMaxPartials = 2048;   // 8 workgroups per CU on 256 CUs
 
-template <bool ALIGNED>
 __global__ __launch_bounds__(kBlock) void norm_partial_kernel(const float* __restrict__ grad,
                                                               int64_t n, float scale,
                                                               double* __restrict__ partials) {
@@ -28,8 +28,8 @@ __global__ __launch_bounds__(kBlock) void norm_partial_kernel(const float* __res
     for (int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x; k < nvec; k += stride) {
         const int64_t first = k * 4;
         float g[4];
-        if (ALIGNED && first + 4 <= n) {
-            const f32x4 a = ld_stream(reinterpret_cast<const f32x4*>(grad + first));
+        if (first + 4 <= n) {   // read-only: a dword-aligned 128-bit load at any offset
+            const f32x4 a = ld_stream_f32x4_a4(grad + first);
             g[0] = a.x; g[1] = a.y; g[2] = a.z; g[3] = a.w;
         } else {
 #pragma unroll
@@ -87,15 +87,11 @@ int64_t norm_partial_blocks(int64_t n) {
 }
 
 hipError_t launch_grad_norm_sq(const float* grad, int64_t n, float scale, double* out,
-                               double* partials, bool vec_ok, hipStream_t stream) {
+                               double* partials, hipStream_t stream) {
     const int64_t blocks = norm_partial_blocks(n);
     if (blocks > 0) {
-        if (vec_ok)
-            hipLaunchKernelGGL((norm_partial_kernel<true>), dim3((unsigned)blocks), dim3(kBlock), 0,
-                               stream, grad, n, scale, partials);
-        else
-            hipLaunchKernelGGL((norm_partial_kernel<false>), dim3((unsigned)blocks), dim3(kBlock), 0,
-                               stream, grad, n, scale, partials);
+        hipLaunchKernelGGL(norm_partial_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, stream, grad, n, scale,
+                           partials);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

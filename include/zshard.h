@@ -33,7 +33,10 @@
  *     per call; larger counts are ZS_EINVAL.
  *   - fp32 pointers must be 4-byte aligned, bf16 pointers 2-byte aligned,
  *     fp64 pointers 8-byte aligned.  Any alignment beyond that only selects
- *     a faster code path (16-byte aligned buffers use 128-bit accesses).
+ *     a faster code path: 128-bit accesses when every buffer a call writes
+ *     is 16-byte aligned and every buffer it only reads is 4-byte aligned
+ *     (a view at any element offset of an fp32 buffer, or at an even one of
+ *     a bf16 buffer); element-wise accesses otherwise.
  *   - bf16 values are passed as their 16-bit patterns (uint16_t).
  */
 #ifndef ZSHARD_H

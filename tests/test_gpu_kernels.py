@@ -52,26 +52,33 @@ def rng_for(*key):
 # grad_accum: bit-exact
 # ---------------------------------------------------------------------------
 
+# (acc offset, grad offset) in elements: both aligned; both misaligned (the
+# scalar path); the read-only gradient alone off a 16-byte boundary (the
+# vector path with dword-aligned gradient loads, except a bf16 gradient at an
+# odd element, which is only 2-byte aligned)
+OFFSETS = [(0, 0), (3, 4), (0, 1), (0, 2)]
+
+
 @pytest.mark.parametrize("n", SIZES)
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("offset", [0, 3])
-def test_grad_accum_bit_exact(n, dtype, offset):
-    print(f"grad_accum n={n} dtype={dtype} offset={offset}", flush=True)
-    rng = np.random.default_rng(n * 31 + offset)
+@pytest.mark.parametrize("acc_off,grad_off", OFFSETS)
+def test_grad_accum_bit_exact(n, dtype, acc_off, grad_off):
+    print(f"grad_accum n={n} dtype={dtype} offsets={acc_off},{grad_off}", flush=True)
+    rng = np.random.default_rng(n * 31 + acc_off * 7 + grad_off)
     M = 4
     mbs32 = [(rng.standard_normal(n) * 1e-3).astype(np.float32) for _ in range(M)]
     mbs = [oracle.bf16_rne(x) for x in mbs32] if dtype == "bf16" else mbs32
     code = oracle.BF16 if dtype == "bf16" else oracle.F32
     ref = np.empty(n, np.float32)
-    acc, acc_whole = dev_buf(np.zeros(n, np.float32), offset)
+    acc, acc_whole = dev_buf(np.zeros(n, np.float32), acc_off)
     for k, g in enumerate(mbs):
         oracle.grad_accum(ref, g, code, overwrite=(k == 0))
-        gd, g_whole = dev_buf(g, offset + 1 if offset else 0, bf16=(dtype == "bf16"))
+        gd, g_whole = dev_buf(g, grad_off, bf16=(dtype == "bf16"))
         zs.grad_accum(acc, gd, overwrite=(k == 0))
         torch.cuda.synchronize()
-        assert canary_ok(g_whole, offset + 1 if offset else 0, n)
+        assert canary_ok(g_whole, grad_off, n)
         assert bits_equal(to_np(acc), ref), (k, identical_fraction(to_np(acc), ref))
-    assert canary_ok(acc_whole, offset, n)
+    assert canary_ok(acc_whole, acc_off, n)
 
 
 # ---------------------------------------------------------------------------
@@ -103,13 +110,13 @@ def test_grad_norm_sq(n, offset):
 
 @pytest.mark.parametrize("n", [1, 7, 4095, 4096, 4097, 100_003, 9_000_011])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("offset", [0, 3])
+@pytest.mark.parametrize("acc_off,grad_off", OFFSETS)
 @pytest.mark.parametrize("overwrite", [False, True])
-def test_grad_accum_norm_sq(n, dtype, offset, overwrite):
+def test_grad_accum_norm_sq(n, dtype, acc_off, grad_off, overwrite):
     """The fused last micro-batch: the accumulator bit-exact, the squared
     norm of the scaled result within the bar and reproducible to the bit."""
-    print(f"grad_accum_norm_sq n={n} dtype={dtype} offset={offset} overwrite={overwrite}", flush=True)
-    rng = np.random.default_rng(n * 13 + offset + overwrite)
+    print(f"grad_accum_norm_sq n={n} dtype={dtype} offsets={acc_off},{grad_off} overwrite={overwrite}", flush=True)
+    rng = np.random.default_rng(n * 13 + acc_off * 5 + grad_off + overwrite)
     code = oracle.BF16 if dtype == "bf16" else oracle.F32
     acc0 = (rng.standard_normal(n) * 1e-2).astype(np.float32)
     g32 = (rng.standard_normal(n) * 1e-2).astype(np.float32)
@@ -120,12 +127,12 @@ def test_grad_accum_norm_sq(n, dtype, offset, overwrite):
     want = oracle.grad_norm_sq(ref, scale)
     outs = []
     for _ in range(2):
-        acc, acc_whole = dev_buf(acc0, offset)
-        gd, g_whole = dev_buf(g, offset, bf16=(dtype == "bf16"))
+        acc, acc_whole = dev_buf(acc0, acc_off)
+        gd, g_whole = dev_buf(g, grad_off, bf16=(dtype == "bf16"))
         out = torch.full((1,), float("nan"), dtype=torch.float64, device="cuda")
         zs.grad_accum_norm_sq(acc, gd, overwrite, scale, out)
         assert bits_equal(to_np(acc), ref)
-        assert canary_ok(acc_whole, offset, n) and canary_ok(g_whole, offset, n)
+        assert canary_ok(acc_whole, acc_off, n) and canary_ok(g_whole, grad_off, n)
         outs.append(out.item())
     assert outs[0] == outs[1]
     assert abs(math.sqrt(outs[0]) - math.sqrt(want)) <= NORM_TOL * math.sqrt(want)
@@ -211,12 +218,13 @@ def test_adamw_step_parity(n, offset, mode):
 
 
 @pytest.mark.parametrize("n", [2049, 100_003])
-@pytest.mark.parametrize("offset", [0, 1])
-def test_adamw_bit_exact_given_the_oracle_norm(n, offset):
+@pytest.mark.parametrize("offset,grad_off", [(0, 0), (1, 1), (0, 1), (0, 3)])
+def test_adamw_bit_exact_given_the_oracle_norm(n, offset, grad_off):
     """With the oracle's squared norm handed to the kernel, every output is
     bit-identical to the oracle: the element update is the same sequence of
     IEEE binary32 operations and the clip coefficient the same binary64 ones."""
-    rng = np.random.default_rng(n + offset)
+    print(f"adamw bit-exact n={n} offset={offset} grad_off={grad_off}", flush=True)
+    rng = np.random.default_rng(n + offset + 10 * grad_off)
     p_ref = rng.uniform(-0.1, 0.1, n).astype(np.float32)
     m_ref, v_ref, b_ref = np.zeros(n, np.float32), np.zeros(n, np.float32), np.zeros(n, np.uint16)
     p, _ = dev_buf(p_ref, offset)
@@ -229,11 +237,12 @@ def test_adamw_bit_exact_given_the_oracle_norm(n, offset):
         hp_gpu, hp_orc = _hp(t, scale=1 / 32, max_norm=math.sqrt(S) * 0.8 if t % 2 else 0.0,
                              extra=0.25 * S)
         oracle.adamw_step(hp_orc, p_ref, m_ref, v_ref, acc, b_ref, norm_sq=S)
-        g, _ = dev_buf(acc, offset)
+        g, gw = dev_buf(acc, grad_off)
         norm = torch.tensor([S], dtype=torch.float64, device="cuda")
         zs.adamw_step(hp_gpu, p, m, v, g, b, norm_sq=norm)
         for name, gpu, ref in (("p", p, p_ref), ("m", m, m_ref), ("v", v, v_ref), ("b", b, b_ref)):
             assert bits_equal(to_np(gpu), ref), (t, name, identical_fraction(to_np(gpu), ref))
+        assert canary_ok(gw, grad_off, n)
 
 
 def test_adamw_skips_on_nonfinite_norm():
@@ -340,7 +349,8 @@ def test_flat_pack_unpack(kind, count, world, aligned_sizes):
 
 
 def test_flat_pack_misaligned_views():
-    """Sources that are views at odd element offsets take the scalar path."""
+    """Sources that are views at odd element offsets (2-byte aligned bf16)
+    take the scalar path."""
     rng = np.random.default_rng(77)
     base = from_np(oracle.bf16_rne(rng.uniform(-1, 1, 10_000).astype(np.float32)), bf16=True)
     views = [base[1:2050], base[3000:3001], base[4001:9000]]
@@ -358,13 +368,14 @@ def test_flat_pack_misaligned_views():
 @pytest.mark.parametrize("N", [1, 2, 7, 16, 17, 64])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("overwrite", [True, False])
-@pytest.mark.parametrize("offset", [0, 1])
-def test_grad_reduce_chunks_bit_exact(N, dtype, overwrite, offset):
+@pytest.mark.parametrize("acc_off,grad_off", [(0, 0), (1, 1), (0, 1), (0, 2)])
+def test_grad_reduce_chunks_bit_exact(N, dtype, overwrite, acc_off, grad_off):
     """N rank chunks summed in rank order equal N sequential accumulations
     (the oracle's), bit for bit, with one chunk aliased twice."""
     n = 4097 if N > 16 else 100_003
-    print(f"grad_reduce_chunks N={N} dtype={dtype} overwrite={overwrite} offset={offset} n={n}", flush=True)
-    rng = np.random.default_rng(N * 7 + offset + 3 * overwrite)
+    print(f"grad_reduce_chunks N={N} dtype={dtype} overwrite={overwrite} offsets={acc_off},{grad_off} n={n}",
+          flush=True)
+    rng = np.random.default_rng(N * 7 + acc_off * 11 + grad_off + 3 * overwrite)
     code = oracle.BF16 if dtype == "bf16" else oracle.F32
     chunks = []
     for _ in range(N):
@@ -376,13 +387,13 @@ def test_grad_reduce_chunks_bit_exact(N, dtype, overwrite, offset):
     ref = acc0.copy()
     for k, c in enumerate(chunks):
         oracle.grad_accum(ref, c, code, overwrite=(overwrite and k == 0))
-    acc, acc_whole = dev_buf(acc0, offset)
-    dev_chunks = [dev_buf(c, offset, bf16=(dtype == "bf16"))[0] for c in chunks]
+    acc, acc_whole = dev_buf(acc0, acc_off)
+    dev_chunks = [dev_buf(c, grad_off + (k % 2) * 2, bf16=(dtype == "bf16"))[0] for k, c in enumerate(chunks)]
     if N > 2:
         dev_chunks[2] = dev_chunks[0]
     zs.grad_reduce_chunks(acc, dev_chunks, overwrite)
     assert bits_equal(to_np(acc), ref)
-    assert canary_ok(acc_whole, offset, n)
+    assert canary_ok(acc_whole, acc_off, n)
 
 
 def test_allgather_placement_roundtrip():
@@ -414,10 +425,11 @@ def test_allgather_placement_roundtrip():
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("n", [1, 7, 4097, 100_003])
-@pytest.mark.parametrize("offset", [0, 1])
+@pytest.mark.parametrize("offset,grad_off", [(0, 0), (1, 1), (0, 1)])
 @pytest.mark.parametrize("clip", [False, True])
-def test_adamw_no_master_bit_exact(n, offset, clip):
-    rng = np.random.default_rng(n + offset + clip)
+def test_adamw_no_master_bit_exact(n, offset, grad_off, clip):
+    print(f"no-master n={n} offset={offset} grad_off={grad_off} clip={clip}", flush=True)
+    rng = np.random.default_rng(n + offset + 3 * grad_off + clip)
     b_ref = oracle.bf16_rne(rng.uniform(-0.1, 0.1, n).astype(np.float32))
     m_ref, v_ref = np.zeros(n, np.float32), np.zeros(n, np.float32)
     b, _ = dev_buf(b_ref, offset, bf16=True)
@@ -428,7 +440,7 @@ def test_adamw_no_master_bit_exact(n, offset, clip):
         S = oracle.grad_norm_sq(acc, 1 / 32)
         hp_gpu, hp_orc = _hp(t, scale=1 / 32, max_norm=math.sqrt(S) * 0.7 if clip else 0.0, extra=0.1 * S)
         oracle.adamw_step_no_master(hp_orc, b_ref, m_ref, v_ref, acc, norm_sq=S if clip else None)
-        g, _ = dev_buf(acc, offset)
+        g, _ = dev_buf(acc, grad_off)
         norm = torch.tensor([S], dtype=torch.float64, device="cuda") if clip else None
         zs.adamw_step_no_master(hp_gpu, b, m, v, g, norm_sq=norm)
         for name, gpu, ref in (("b", b, b_ref), ("m", m, m_ref), ("v", v, v_ref)):
@@ -470,19 +482,19 @@ def test_no_master_stalls_on_the_gpu():
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("n", [1, 7, 4097, 100_003])
-@pytest.mark.parametrize("offset", [0, 1, 3])
+@pytest.mark.parametrize("offset,upd_off", [(0, 0), (1, 1), (3, 3), (1, 0), (3, 0)])
 @pytest.mark.parametrize("clip", [False, True])
-def test_adam_update_bit_exact(n, offset, clip):
+def test_adam_update_bit_exact(n, offset, upd_off, clip):
     """The gradient (and the update) as views at any element offset, as a
     rank's slice of one resident flat buffer is; the moments are the rank's
     own allocations.  Given the oracle's squared norm every output is
     bit-identical, and nothing past the views is written."""
-    print(f"adam_update n={n} offset={offset} clip={clip}", flush=True)
-    rng = np.random.default_rng(3 * n + offset + 7 * clip)
+    print(f"adam_update n={n} grad offset={offset} update offset={upd_off} clip={clip}", flush=True)
+    rng = np.random.default_rng(3 * n + offset + 5 * upd_off + 7 * clip)
     m_ref, v_ref, u_ref = np.zeros(n, np.float32), np.zeros(n, np.float32), np.empty(n, np.float32)
     m, mw = dev_buf(m_ref, 0)
     v, vw = dev_buf(v_ref, 0)
-    u, uw = dev_buf(np.zeros(n, np.float32), offset)
+    u, uw = dev_buf(np.zeros(n, np.float32), upd_off)
     for t in range(1, 5):
         acc = (rng.standard_normal(n) * 1e-3).astype(np.float32)
         S = oracle.grad_norm_sq(acc, 1 / 8)
@@ -496,7 +508,7 @@ def test_adam_update_bit_exact(n, offset, clip):
         for name, gpu, ref in (("update", u, u_ref), ("m", m, m_ref), ("v", v, v_ref)):
             assert bits_equal(to_np(gpu), ref), (t, name, identical_fraction(to_np(gpu), ref))
         assert canary_ok(gw, offset, n)
-    for whole, off in ((uw, offset), (mw, 0), (vw, 0)):
+    for whole, off in ((uw, upd_off), (mw, 0), (vw, 0)):
         assert canary_ok(whole, off, n)
 
 
@@ -554,3 +566,42 @@ def test_binding_rejects_bad_norm_buffers():
             zs.adamw_step(hp, p, m, v, g, norm_sq=bad)
     with pytest.raises(ValueError):
         zs.adamw_step(hp, p, m, v, g[:-1])
+
+
+
+@pytest.mark.parametrize("src_off", [2, 4, 6])
+def test_flat_dword_aligned_read_side(src_off):
+    """Views 4 bytes past a 16-byte boundary on the read side (bf16 sources
+    at even offsets for the pack, a flat view for the unpack) keep the vector
+    path with dword-aligned loads; bit-exact, nothing written outside."""
+    rng = np.random.default_rng(300 + src_off)
+    base_np = oracle.bf16_rne(rng.uniform(-1, 1, 20_000).astype(np.float32))
+    base = from_np(base_np, bf16=True)
+    spans = [(src_off, src_off + 4096), (src_off + 5000, src_off + 5000 + 2051), (src_off + 8000, src_off + 16000)]
+    views = [base[a:b] for a, b in spans]
+    T = sum(b - a for a, b in spans)
+    for flat_bf16 in (False, True):
+        flat, flat_whole = dev_buf(np.zeros(T + 3, np.uint16 if flat_bf16 else np.float32), 0, bf16=flat_bf16)
+        zs.flat_pack(views, flat, T + 3)
+        code = oracle.BF16 if flat_bf16 else oracle.F32
+        want = oracle.flat_pack([base_np[a:b] for a, b in spans], oracle.BF16, code, T + 3)
+        assert bits_equal(to_np(flat), want)
+        assert canary_ok(flat_whole, 0, T + 3)
+    # unpack from a flat view that starts src_off elements into a bf16 buffer
+    flat_np = oracle.bf16_rne(rng.uniform(-1, 1, T + 16).astype(np.float32))
+    fv, _ = dev_buf(flat_np[src_off:src_off + T], src_off, bf16=True)
+    outs = [torch.empty(b - a, dtype=torch.bfloat16, device="cuda") for a, b in spans]
+    zs.flat_unpack(fv, outs)
+    back = oracle.flat_unpack(np.ascontiguousarray(flat_np[src_off:src_off + T]), oracle.BF16,
+                              [b - a for a, b in spans], oracle.BF16)
+    for o, r in zip(outs, back):
+        assert bits_equal(to_np(o), r)
+    # apply: an fp32 update view 4 bytes past a boundary into aligned fp32 tensors
+    upd_np = (rng.standard_normal(T + 8) * 1e-2).astype(np.float32)
+    uv, _ = dev_buf(upd_np[1:1 + T], 1)
+    ps_np = [rng.uniform(-1, 1, b - a).astype(np.float32) for a, b in spans]
+    ps = [from_np(x) for x in ps_np]
+    zs.flat_apply_update(uv, ps)
+    oracle.flat_apply_update(np.ascontiguousarray(upd_np[1:1 + T]), ps_np, oracle.F32)
+    for a_, r in zip(ps, ps_np):
+        assert bits_equal(to_np(a_), r)
