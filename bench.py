@@ -150,6 +150,29 @@ def run_gpu(w, steps: int, warmup: int):
     adamw_ms = sum(e[2].elapsed_time(e[3]) for e in timing) / steps
     assert math.isfinite(norm.item()), "non-finite gradient norm in the bench"
 
+    # outside the step: the same step captured once in a HIP graph and
+    # replayed (the library allocates, clears and synchronises nothing, so
+    # the step captures as is; launch overhead matters for small shards)
+    graph_ms = None
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        one_step(t + 1, record=False)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        one_step(t + 1, record=False)
+    graph.replay()
+    g0, g1 = ev(), ev()
+    g0.record()
+    for _ in range(steps):
+        graph.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    graph_ms = g0.elapsed_time(g1) / steps
+    del graph
+
     # outside the step: the reduce-scatter's arithmetic on this rank's shard,
     # the same buffers read as N rank chunks, in one pass
     reduce_ms = None
@@ -194,7 +217,7 @@ def run_gpu(w, steps: int, warmup: int):
     copy_ms = c0.elapsed_time(c1) / 5
     copy_gbps = 2 * src.numel() * 4 / (copy_ms * 1e-3) / 1e9
     del src, dst
-    return {"n": n, "wall_s": wall, "accum_ms": acc_ms, "last_ms": last_ms, "adamw_ms": adamw_ms,
+    return {"n": n, "wall_s": wall, "accum_ms": acc_ms, "last_ms": last_ms, "adamw_ms": adamw_ms, "graph_ms": graph_ms,
             "reduce_ms": reduce_ms, "chunks": len(grads), "no_master_ms": no_master_ms,
             "copy_gbps": copy_gbps}
 
@@ -396,6 +419,7 @@ def main():
         "config": {"workload": w.name, "shard_elems": n, "total_params": w.total, "world": w.world,
                    "rank": w.rank, "micro_batches": w.micro_batches, "grad_dtype": w.grad_dtype,
                    "state": "fp32 master/exp_avg/exp_avg_sq + bf16 param", "clip": w.max_norm > 0},
+        "graph_ms_per_step": r["graph_ms"],
         "step_hbm_gbps": step_gbps,
         "step_hbm_frac": step_gbps / HBM_PEAK_GBPS,
         "kernels_ms": {"grad_accum_all_but_last": r["accum_ms"], "grad_accum_norm_sq_last": r["last_ms"],
