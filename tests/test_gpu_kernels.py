@@ -605,3 +605,78 @@ def test_flat_dword_aligned_read_side(src_off):
     oracle.flat_apply_update(np.ascontiguousarray(upd_np[1:1 + T]), ps_np, oracle.F32)
     for a_, r in zip(ps, ps_np):
         assert bits_equal(to_np(a_), r)
+
+
+# ---------------------------------------------------------------------------
+# degenerate hyperparameters and special gradient values
+# ---------------------------------------------------------------------------
+
+def _special_grads(n, rng):
+    """Normal gradients with zeros of both signs, subnormals, values whose
+    square overflows or underflows, the extremes of fp32, inf and NaN."""
+    g = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    specials = np.array([0.0, -0.0, 1e-45, -1e-45, 1e-40, 3e-39, 1e-20, 1e20, 3e38, -3.4e38,
+                         np.inf, -np.inf, np.nan], dtype=np.float32)
+    idx = rng.choice(n, size=len(specials) * 20, replace=False)
+    g[idx] = np.tile(specials, 20)
+    return g
+
+
+def _same(gpu, ref):
+    """Bit-identical, except that any NaN matches any NaN (payloads and signs
+    of NaNs made by arithmetic differ between the CPU and the GPU)."""
+    if gpu.dtype == np.uint16:
+        nan_g = ((gpu & 0x7F80) == 0x7F80) & ((gpu & 0x7F) != 0)
+        nan_r = ((ref & 0x7F80) == 0x7F80) & ((ref & 0x7F) != 0)
+    else:
+        nan_g, nan_r = np.isnan(gpu), np.isnan(ref)
+    if not np.array_equal(nan_g, nan_r):
+        return False
+    return bits_equal(gpu[~nan_g], ref[~nan_r])
+
+
+@pytest.mark.parametrize("case", ["betas_zero", "lr_zero", "eps_large", "wd_large", "beta_near_one"])
+def test_adamw_degenerate_hyperparameters_and_special_values(case):
+    """No norm pointer (nothing is skipped): inf and NaN gradients propagate
+    element-wise, as in the oracle.  Three steps; every element identical to
+    the oracle's, NaNs matched by position."""
+    print(f"adamw degenerate case={case}", flush=True)
+    hpk = dict(lr=3e-4, b1=0.9, b2=0.95, eps=1e-8, wd=0.1, scale=1 / 8)
+    hpk.update({"betas_zero": dict(b1=0.0, b2=0.0), "lr_zero": dict(lr=0.0), "eps_large": dict(eps=1.0),
+                "wd_large": dict(wd=1000.0, lr=1e-3), "beta_near_one": dict(b1=0.999999, b2=0.9999999)}[case])
+    n = 8199
+    rng = np.random.default_rng(len(case))
+    p_ref = rng.uniform(-0.1, 0.1, n).astype(np.float32)
+    p_ref[:4] = (0.0, -0.0, 1e-40, 3e38)
+    m_ref, v_ref, b_ref = np.zeros(n, np.float32), np.zeros(n, np.float32), np.zeros(n, np.uint16)
+    p, m, v = from_np(p_ref.copy()), from_np(m_ref.copy()), from_np(v_ref.copy())
+    b = from_np(b_ref.copy(), bf16=True)
+    for t in range(1, 4):
+        acc = _special_grads(n, rng)
+        hp_gpu, hp_orc = _hp(t, **hpk)
+        assert oracle.adamw_step(hp_orc, p_ref, m_ref, v_ref, acc, b_ref) == 0
+        zs.adamw_step(hp_gpu, p, m, v, from_np(acc), b)
+        for name, gpu, ref in (("p", p, p_ref), ("m", m, m_ref), ("v", v, v_ref), ("b", b, b_ref)):
+            assert _same(to_np(gpu), ref), (case, t, name)
+
+
+def test_adam_update_and_no_master_special_values():
+    n = 8199
+    rng = np.random.default_rng(99)
+    b0 = oracle.bf16_rne(rng.uniform(-0.1, 0.1, n).astype(np.float32))
+    m_ref, v_ref = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    m2_ref, v2_ref, u_ref, b_ref = m_ref.copy(), v_ref.copy(), np.empty(n, np.float32), b0.copy()
+    m, v, m2, v2 = (from_np(x.copy()) for x in (m_ref, v_ref, m2_ref, v2_ref))
+    u = torch.empty(n, device="cuda")
+    b = from_np(b0.copy(), bf16=True)
+    for t in range(1, 4):
+        acc = _special_grads(n, rng)
+        hp_gpu, hp_orc = _hp(t, wd=0.0, scale=1 / 8)
+        oracle.adam_update(hp_orc, m_ref, v_ref, acc, u_ref)
+        oracle.adamw_step_no_master(hp_orc, b_ref, m2_ref, v2_ref, acc)
+        g = from_np(acc)
+        zs.adam_update(hp_gpu, m, v, g, u)
+        zs.adamw_step_no_master(hp_gpu, b, m2, v2, g)
+        for name, gpu, ref in (("update", u, u_ref), ("m", m, m_ref), ("v", v, v_ref), ("b", b, b_ref),
+                               ("m2", m2, m2_ref), ("v2", v2, v2_ref)):
+            assert _same(to_np(gpu), ref), (t, name)
