@@ -115,7 +115,7 @@ int32_t grad_reduce_chunks(float* acc, const void* const* chunks, int32_t count,
 }
 
 int64_t grad_norm_sq_workspace_bytes(int64_t n) {
-    if (n < 0) return -1;
+    if (!size_ok(n)) return -1;
     return zs::norm_partial_blocks(n) * (int64_t)sizeof(double);
 }
 
@@ -135,7 +135,7 @@ int32_t grad_norm_sq(const float* grad, int64_t n, double grad_scale, double* ou
 }
 
 int64_t grad_accum_norm_sq_workspace_bytes(int64_t n) {
-    if (n < 0) return -1;
+    if (!size_ok(n)) return -1;
     const int64_t parts = zs::accum_norm_partials(n);
     return parts == 0 ? 0 : (parts + zs::kReduceChunks) * (int64_t)sizeof(double);
 }

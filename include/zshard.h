@@ -194,7 +194,7 @@ ZS_API int32_t grad_reduce_chunks(float* acc, const void* const* chunks, int32_t
 
 /*
  * grad_norm_sq_workspace_bytes — bytes of device workspace grad_norm_sq
- * needs for n elements (0 for n == 0; -1 for n < 0).  Host only.
+ * needs for n elements (0 for n == 0; -1 for n < 0 or n > 2^39).  Host only.
  */
 ZS_API int64_t grad_norm_sq_workspace_bytes(int64_t n);
 
@@ -219,7 +219,8 @@ ZS_API int32_t grad_norm_sq(const float* grad, int64_t n, double grad_scale, dou
 
 /*
  * grad_accum_norm_sq_workspace_bytes — bytes of device workspace
- * grad_accum_norm_sq needs for n elements (0 for n == 0; -1 for n < 0).
+ * grad_accum_norm_sq needs for n elements (0 for n == 0; -1 for n < 0 or
+ * n > 2^39).
  */
 ZS_API int64_t grad_accum_norm_sq_workspace_bytes(int64_t n);
 

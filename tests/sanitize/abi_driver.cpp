@@ -1,0 +1,88 @@
+// Drives the C ABI's host-side validation under AddressSanitizer and
+// UndefinedBehaviorSanitizer (built with hipcc, the sanitizers on the host
+// pass only; run by tests/test_sanitizers.py on a machine without a GPU).
+// Every call below fails validation or is a no-op, so nothing reaches a
+// launch and no pointer is dereferenced; tensor lists and chunk tables are
+// allocated at their exact sizes, so reading one entry too many is reported.
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <vector>
+
+#include "../../include/zshard.h"
+
+#define CHECK(cond, code)                                          \
+    do {                                                           \
+        if (!(cond)) {                                             \
+            std::fprintf(stderr, "check failed: %s\n", #cond);     \
+            return code;                                           \
+        }                                                          \
+    } while (0)
+
+static const uintptr_t FAKE = 0x7F0000000000ull;
+static void* fake(uint64_t off) { return reinterpret_cast<void*>(FAKE + off); }
+
+int main() {
+    for (int64_t T = 0; T <= 64; ++T)
+        for (int32_t N = 1; N <= 9; ++N)
+            for (int32_t r = 0; r < N; ++r) {
+                zs_shard s;
+                CHECK(zero_shard_range(T, N, r, &s) == ZS_OK, 1);
+                CHECK(s.start <= s.end && s.end <= T && s.padded_total == (int64_t)N * s.chunk, 2);
+            }
+    zs_shard s;
+    CHECK(zero_shard_range(INT64_MAX, 1, 0, &s) == ZS_OK, 3);
+    CHECK(zero_shard_range(INT64_MAX, 3, 2, &s) == ZS_EINVAL, 3);   // 3 * ceil(T/3) overflows
+    CHECK(zero_shard_range(INT64_MAX - 1, 3, 2, &s) == ZS_OK && s.end == INT64_MAX - 1, 3);
+    CHECK(zero_shard_range(10, 0, 0, &s) == ZS_EINVAL && zero_shard_range(10, 2, 2, nullptr) == ZS_EINVAL, 3);
+
+    CHECK(grad_norm_sq_workspace_bytes(-1) == -1 && grad_accum_norm_sq_workspace_bytes(-5) == -1, 4);
+    CHECK(grad_norm_sq_workspace_bytes(INT64_MAX) == -1 && grad_accum_norm_sq_workspace_bytes(INT64_MAX) == -1, 4);
+    CHECK(grad_norm_sq_workspace_bytes(int64_t(1) << 39) > 0 && grad_accum_norm_sq_workspace_bytes(int64_t(1) << 39) > 0,
+          4);
+
+    zs_adamw hp{3e-4, 0.9, 0.95, 1e-8, 0.1, 1.0, 0.0, 0.0, 1};
+    zs_adamw bad = hp;
+    bad.beta1 = NAN;
+    float* f = static_cast<float*>(fake(0));
+    CHECK(adamw_step(&bad, f, f + 1024, f + 2048, f + 4096, nullptr, 16, nullptr, nullptr) == ZS_EINVAL, 5);
+    CHECK(adamw_step(&hp, f, f + 2, f + 2048, f + 4096, nullptr, 16, nullptr, nullptr) == ZS_EOVERLAP, 5);
+    CHECK(adamw_step(&hp, f, f, f, f, nullptr, 0, nullptr, nullptr) == ZS_OK, 5);
+    CHECK(adamw_step(&hp, f, f + 1024, f + 2048, f + 4096, nullptr, int64_t(1) << 40, nullptr, nullptr) ==
+              ZS_EINVAL, 5);
+    CHECK(adamw_step_no_master(&hp, static_cast<uint16_t*>(fake(1)), f + 1024, f + 2048, f + 4096, 8, nullptr,
+                               nullptr) == ZS_EINVAL, 6);
+    CHECK(adam_update(&hp, f, f + 1024, f + 2048, f + 4096, 8, nullptr, nullptr) == ZS_EINVAL, 6);   // decay
+
+    CHECK(grad_accum(f, f + 1, 3, 8, 0, nullptr) == ZS_EINVAL, 7);
+    CHECK(grad_accum(f, f + 1, ZS_F32, 8, 0, nullptr) == ZS_EOVERLAP, 7);
+    CHECK(grad_accum(f, f + 1, ZS_F32, 0, 0, nullptr) == ZS_OK, 7);
+    double* d = static_cast<double*>(fake(1 << 20));
+    CHECK(grad_norm_sq(f, 1 << 20, 1.0, d, d + 1, 8, nullptr) == ZS_EWORKSPACE, 8);   // needs 8 KiB
+    CHECK(grad_accum_norm_sq(f, f + 4096, ZS_BF16, 1 << 16, 1, 1.0, d, d + 8, 16, nullptr) == ZS_EWORKSPACE, 8);
+
+    // chunk tables and tensor lists of every length up to 40, exactly sized;
+    // the last entry is the one that fails, so every entry is read
+    for (int count = 1; count <= 40; ++count) {
+        std::vector<const void*> chunks(count);
+        for (int k = 0; k < count; ++k) chunks[k] = fake(uint64_t(1 + k) << 24);
+        chunks[count - 1] = fake((uint64_t(count) << 24) + 1);   // misaligned bf16
+        CHECK(grad_reduce_chunks(f, chunks.data(), count, ZS_BF16, 64, 1, nullptr) == ZS_EINVAL, 9);
+        std::vector<zs_tensor> ts(count);
+        for (int k = 0; k < count; ++k) ts[k] = zs_tensor{fake(uint64_t(1 + k) << 24), 16};
+        ts[count - 1].numel = -1;
+        CHECK(flat_pack(ts.data(), count, ZS_F32, fake(1ull << 40), ZS_F32, 16 * count, nullptr) == ZS_EINVAL, 10);
+        CHECK(flat_unpack(fake(1ull << 40), ZS_F32, ts.data(), count, ZS_F32, nullptr) == ZS_EINVAL, 10);
+        CHECK(flat_apply_update(f, ts.data(), count, ZS_BF16, nullptr) == ZS_EINVAL, 10);
+        ts[count - 1].numel = 16;
+        if (count > 1) {   // two tensors overlap: the last one starts inside the first
+            ts[count - 1].ptr = fake((1ull << 24) + 8);
+            CHECK(flat_unpack(fake(1ull << 40), ZS_F32, ts.data(), count, ZS_F32, nullptr) == ZS_EOVERLAP, 11);
+        }
+    }
+    CHECK(zs_last_hip_error() == 0, 12);   // nothing reached a launch
+    for (int32_t c = -6; c <= 1; ++c) CHECK(zs_strerror(c) != nullptr, 13);
+    std::printf("abi sanitizer drive: ok\n");
+    return 0;
+}

@@ -87,8 +87,9 @@ def test_workspace_bytes():
     assert zs.grad_norm_sq_workspace_bytes(0) == 0
     assert zs.grad_norm_sq_workspace_bytes(-1) == -1
     assert zs.grad_norm_sq_workspace_bytes(1) == 8
-    # capped number of partials for large n
+    # capped number of partials for large n; beyond the per-call element limit: -1
     assert zs.grad_norm_sq_workspace_bytes(10**10) == zs.grad_norm_sq_workspace_bytes(10**9)
+    assert zs.grad_norm_sq_workspace_bytes(2**63 - 1) == -1 and zs.grad_accum_norm_sq_workspace_bytes(2**39 + 1) == -1
 
 
 FAKE = 0x7F0000000000   # never dereferenced: every call below fails validation
