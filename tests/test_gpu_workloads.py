@@ -336,3 +336,64 @@ def test_tiny_zero1_full_flow():
         for r in range(N):
             assert bits_equal(to_np(m[r]), m_ref[r]) and bits_equal(to_np(v[r]), v_ref[r]), (t, r)
     assert all(bool(torch.isfinite(p).all()) for p in params)
+
+
+def test_zero1_flow_llama7b_sampled():
+    """The ZeRO-1 flow at the Llama-7B size in bench.py's launch configuration:
+    adam_update on rank 0's 842,301,952-element slice (two steps, the second
+    clipped) and flat_apply_update of a 6,738,415,616-element update into the
+    291 bf16 parameter tensors.  Both are element-wise, so the oracle runs the
+    sampled elements alone (first and last 4096, tile edges, 2^20 random)."""
+    w = workloads.WORKLOADS["llama7b_shard"]
+    chunk, start, end, padded = zs.zero_shard_range(w.total, w.world, w.rank)
+    n = end - start
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(workloads.seed_of(w.cfg, workloads.PURPOSE_GRAD, 9, 0))
+    idx = sample_indices(n, seed=1)
+    grad = torch.randn(n, generator=gen, device=DEV).mul_(1e-3 / 8)
+    m = torch.zeros(n, device=DEV)
+    v = torch.zeros(n, device=DEV)
+    upd = torch.empty(n, device=DEV)
+    m_ref, v_ref = np.zeros(idx.numel(), np.float32), np.zeros(idx.numel(), np.float32)
+    for t in (1, 2):
+        clip = t == 2
+        norm = None
+        hp = zs.AdamWConfig(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=0.0,
+                            grad_scale=1.0 / w.world, max_norm=1.0 if clip else 0.0, extra_norm_sq=3.0, step=t)
+        S = 0.0
+        if clip:   # the oracle's norm over the whole slice feeds both sides; the GPU's is checked against it
+            S = oracle.grad_norm_sq(host(grad), 1.0 / w.world)
+            gpu_norm = torch.zeros(1, dtype=torch.float64, device=DEV)
+            zs.grad_norm_sq(grad, 1.0 / w.world, gpu_norm)
+            assert abs(math.sqrt(gpu_norm.item()) - math.sqrt(S)) <= NORM_TOL * math.sqrt(S)
+            norm = torch.tensor([S], dtype=torch.float64, device=DEV)
+        log(f"  zero1 7B adam_update step {t} clip={clip}")
+        zs.adam_update(hp, m, v, grad, upd, norm_sq=norm)
+        g_s = host(grad[idx])
+        u_ref = np.empty(idx.numel(), np.float32)
+        H = oracle.make_hp(w.lr, w.beta1, w.beta2, w.eps, 0.0, 1.0 / w.world, hp.max_norm, 3.0, t)
+        if clip:
+            assert oracle.clip_coef(S, 3.0, 1.0) < 0.9   # the second step clips
+        assert oracle.adam_update(H, m_ref, v_ref, g_s, u_ref, norm_sq=S if clip else None) == 0
+        for name, gpu, ref in (("update", upd, u_ref), ("m", m, m_ref), ("v", v, v_ref)):
+            got = host(gpu[idx])
+            assert bits_equal(got, ref), (t, name, identical_fraction(got, ref))
+    del grad, m, v, upd
+    torch.cuda.empty_cache()
+
+    log("  zero1 7B flat_apply_update over 291 tensors")
+    gathered = torch.randn(padded, generator=gen, device=DEV).mul_(1e-4)
+    buf = torch.rand(w.total, generator=gen, device=DEV).mul_(0.2).sub_(0.1).to(torch.bfloat16)
+    params, off = [], 0
+    for _, shp in workloads.LLAMA7B:
+        k = workloads.numel_of(shp)
+        params.append(buf[off:off + k].view(shp))
+        off += k
+    pidx = sample_indices(w.total, seed=2)
+    before = host(buf[pidx]).copy()
+    u_s = host(gathered[pidx])
+    zs.flat_apply_update(gathered, params)
+    torch.cuda.synchronize()
+    oracle.flat_apply_update(u_s, [before], oracle.BF16)   # element-wise: the samples as one tensor
+    got = host(buf[pidx])
+    assert bits_equal(got, before), identical_fraction(got, before)
