@@ -397,3 +397,42 @@ def test_zero1_flow_llama7b_sampled():
     oracle.flat_apply_update(u_s, [before], oracle.BF16)   # element-wise: the samples as one tensor
     got = host(buf[pidx])
     assert bits_equal(got, before), identical_fraction(got, before)
+
+
+def test_reduce_chunks_and_no_master_full_size_sampled():
+    """The two entry points bench.py times after the step, at the Llama-7B
+    shard size in the same launch configuration: grad_reduce_chunks over the
+    8 bf16 micro-batch draws (overwrite), then adamw_step_no_master on the
+    bf16 shard with that sum as its gradient, two steps.  Element-wise, so
+    the oracle runs the sampled elements alone."""
+    w = workloads.WORKLOADS["llama7b_shard"]
+    _, start, end, _ = zs.zero_shard_range(w.total, w.world, w.rank)
+    n = end - start
+    idx = sample_indices(n, seed=3)
+    grads = [workloads.grad_draw(w, n, 1, mb, DEV) for mb in range(w.micro_batches)]
+    acc = torch.empty(n, device=DEV)
+    log("  7B grad_reduce_chunks, 8 bf16 chunks")
+    zs.grad_reduce_chunks(acc, grads, True)
+    acc_ref = np.empty(idx.numel(), np.float32)
+    for k, g in enumerate(grads):
+        oracle.grad_accum(acc_ref, host(g[idx]), oracle.BF16, overwrite=(k == 0))
+    got = host(acc[idx])
+    assert bits_equal(got, acc_ref), identical_fraction(got, acc_ref)
+    del grads
+    torch.cuda.empty_cache()
+
+    param = workloads.master_init(w, n, DEV).to(torch.bfloat16)
+    m = torch.zeros(n, device=DEV)
+    v = torch.zeros(n, device=DEV)
+    b_ref = host(param[idx])
+    m_ref, v_ref = np.zeros(idx.numel(), np.float32), np.zeros(idx.numel(), np.float32)
+    for t in (1, 2):
+        log(f"  7B adamw_step_no_master step {t}")
+        hp = zs.AdamWConfig(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
+                            grad_scale=w.grad_scale, step=t)
+        zs.adamw_step_no_master(hp, param, m, v, acc)
+        H = oracle.make_hp(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, w.grad_scale, 0.0, 0.0, t)
+        assert oracle.adamw_step_no_master(H, b_ref, m_ref, v_ref, acc_ref) == 0
+        for name, gpu, ref in (("b", param, b_ref), ("m", m, m_ref), ("v", v, v_ref)):
+            got = host(gpu[idx])
+            assert bits_equal(got, ref), (t, name, identical_fraction(got, ref))
