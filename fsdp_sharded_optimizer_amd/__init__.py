@@ -10,6 +10,8 @@ The Python names mirror the C ABI in include/zshard.h:
     grad_accum_norm_sq(acc, grad, overwrite, grad_scale, out, workspace=None)
     grad_norm_sq(grad, grad_scale, out, workspace=None)
     adamw_step(hp, master, exp_avg, exp_avg_sq, grad, param_bf16=None, norm_sq=None)
+    adamw_scalars(hp) / scalars_bytes(hp)       the step's binary32 scalars, on the host
+    adamw_step_dev(scalars_dev, master, exp_avg, exp_avg_sq, grad, param_bf16=None, norm_sq=None)
     adamw_step_no_master(hp, param_bf16, exp_avg, exp_avg_sq, grad, norm_sq=None)
     adam_update(hp, exp_avg, exp_avg_sq, grad, update, norm_sq=None)
     flat_apply_update(update, dst_tensors)
@@ -22,8 +24,11 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     AdamWConfig,
     ZShardError,
+    AdamWScalars,
     adam_update,
+    adamw_scalars,
     adamw_step,
+    adamw_step_dev,
     adamw_step_no_master,
     flat_apply_update,
     flat_pack,
@@ -35,6 +40,7 @@ from ._binding import (  # noqa: F401
     grad_norm_sq,
     grad_norm_sq_workspace_bytes,
     lib,
+    scalars_bytes,
     zero_shard_range,
 )
 from .step import ShardOptimizer  # noqa: F401

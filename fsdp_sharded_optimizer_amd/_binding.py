@@ -29,7 +29,8 @@ ZS_EHIP = -4
 EXPORTS = (
     "zero_shard_range", "flat_pack", "flat_unpack", "grad_accum", "grad_reduce_chunks",
     "grad_norm_sq_workspace_bytes", "grad_norm_sq", "grad_accum_norm_sq_workspace_bytes",
-    "grad_accum_norm_sq", "adamw_step", "adamw_step_no_master", "adam_update", "flat_apply_update",
+    "grad_accum_norm_sq", "adamw_step", "adamw_scalars", "adamw_step_dev", "adamw_step_no_master", "adam_update",
+    "flat_apply_update",
     "zs_strerror", "zs_last_hip_error",
 )
 
@@ -59,6 +60,14 @@ class AdamW(ctypes.Structure):
         ("grad_scale", ctypes.c_double), ("max_norm", ctypes.c_double),
         ("extra_norm_sq", ctypes.c_double), ("step", ctypes.c_int64),
     ]
+
+
+class AdamWScalars(ctypes.Structure):
+    """zs_adamw_scalars: one step's binary32 scalars (56 bytes)."""
+    _fields_ = [(name, ctypes.c_float) for name in (
+        "beta1", "beta2", "one_minus_beta1", "one_minus_beta2", "step_size", "bias_correction2_sqrt", "eps",
+        "decay", "grad_scale")] + [("clip", ctypes.c_int32), ("max_norm", ctypes.c_double),
+                                   ("extra_norm_sq", ctypes.c_double)]
 
 
 @dataclass
@@ -112,6 +121,10 @@ def lib() -> ctypes.CDLL:
         L.grad_accum_norm_sq.restype = I32
         L.adamw_step.argtypes = [ctypes.POINTER(AdamW), P, P, P, P, P, I64, P, P]
         L.adamw_step.restype = I32
+        L.adamw_scalars.argtypes = [ctypes.POINTER(AdamW), ctypes.POINTER(AdamWScalars)]
+        L.adamw_scalars.restype = I32
+        L.adamw_step_dev.argtypes = [P, P, P, P, P, P, I64, P, P]
+        L.adamw_step_dev.restype = I32
         L.adamw_step_no_master.argtypes = [ctypes.POINTER(AdamW), P, P, P, P, I64, P, P]
         L.adamw_step_no_master.restype = I32
         L.adam_update.argtypes = [ctypes.POINTER(AdamW), P, P, P, P, I64, P, P]
@@ -322,6 +335,40 @@ def adamw_step(hp: AdamWConfig, master: torch.Tensor, exp_avg: torch.Tensor, exp
         ctypes.byref(c), _dev(master, "master", torch.float32), _dev(exp_avg, "exp_avg", torch.float32),
         _dev(exp_avg_sq, "exp_avg_sq", torch.float32), _dev(grad, "grad", torch.float32),
         _dev(param_bf16, "param_bf16", torch.bfloat16), n, _norm(norm_sq, "adamw_step"), _stream(stream)))
+
+
+def adamw_scalars(hp: AdamWConfig) -> AdamWScalars:
+    """The binary32 scalars adamw_step forms from hp (host only)."""
+    out = AdamWScalars()
+    c = hp.c_struct()
+    _check("adamw_scalars", lib().adamw_scalars(ctypes.byref(c), ctypes.byref(out)))
+    return out
+
+
+def scalars_bytes(hp: AdamWConfig) -> bytes:
+    """adamw_scalars(hp) as the bytes adamw_step_dev reads from device memory."""
+    return bytes(adamw_scalars(hp))
+
+
+def adamw_step_dev(scalars_dev: torch.Tensor, master: torch.Tensor, exp_avg: torch.Tensor,
+                   exp_avg_sq: torch.Tensor, grad: torch.Tensor, param_bf16: Optional[torch.Tensor] = None,
+                   norm_sq: Optional[torch.Tensor] = None, stream=None) -> None:
+    """adamw_step with its scalars read from device memory when the kernels
+    run: scalars_dev is a uint8 GPU tensor holding scalars_bytes(hp)."""
+    if scalars_dev.dtype != torch.uint8 or scalars_dev.numel() < ctypes.sizeof(AdamWScalars):
+        raise TypeError("adamw_step_dev: scalars_dev must be a uint8 tensor of at least "
+                        f"{ctypes.sizeof(AdamWScalars)} bytes")
+    n = master.numel()
+    for t, nm in ((exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq"), (grad, "grad")):
+        if t.numel() != n:
+            raise ValueError(f"adamw_step_dev: {nm} size mismatch")
+    if param_bf16 is not None and param_bf16.numel() != n:
+        raise ValueError("adamw_step_dev: param_bf16 size mismatch")
+    _check("adamw_step_dev", lib().adamw_step_dev(
+        _dev(scalars_dev, "scalars_dev"), _dev(master, "master", torch.float32),
+        _dev(exp_avg, "exp_avg", torch.float32), _dev(exp_avg_sq, "exp_avg_sq", torch.float32),
+        _dev(grad, "grad", torch.float32), _dev(param_bf16, "param_bf16", torch.bfloat16), n,
+        _norm(norm_sq, "adamw_step_dev"), _stream(stream)))
 
 
 def adamw_step_no_master(hp: AdamWConfig, param_bf16: torch.Tensor, exp_avg: torch.Tensor,

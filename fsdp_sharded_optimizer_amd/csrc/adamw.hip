@@ -37,7 +37,7 @@ namespace {
 // -ffp-contract=off: no multiply-add fusion; the quotient and square root
 // are IEEE round-to-nearest (correctly rounded fp32 division and sqrt are
 // requested at compile time).
-__device__ __forceinline__ float adam_elem(const AdamwArgs& a, float coef, float gr, float& m, float& v) {
+__device__ __forceinline__ float adam_elem(const AdamwScalars& a, float coef, float gr, float& m, float& v) {
     float g = gr * a.grad_scale;
     g = g * coef;
     const float m_keep = a.beta1 * m;
@@ -55,7 +55,7 @@ __device__ __forceinline__ float adam_elem(const AdamwArgs& a, float coef, float
 }
 
 // the parameter after the step: decoupled decay, then the step
-__device__ __forceinline__ float apply_step(const AdamwArgs& a, float p, float u) {
+__device__ __forceinline__ float apply_step(const AdamwScalars& a, float p, float u) {
     const float pd = p * a.decay;
     return pd - u;
 }
@@ -63,10 +63,10 @@ __device__ __forceinline__ float apply_step(const AdamwArgs& a, float p, float u
 // Clip coefficient from the squared norm, in binary64 (uniform per wave).
 // Returns false when the global squared norm is not finite: the step is
 // skipped and nothing is written.
-__device__ __forceinline__ bool clip_coef(const AdamwArgs& a, float& coef) {
+__device__ __forceinline__ bool clip_coef(const AdamwScalars& a, const double* norm_sq, float& coef) {
     coef = 1.0f;
-    if (a.norm_sq == nullptr) return true;
-    const double s = *a.norm_sq + a.extra_norm_sq;
+    if (norm_sq == nullptr) return true;
+    const double s = *norm_sq + a.extra_norm_sq;
     if (!__builtin_isfinite(s)) return false;
     if (a.clip) {
         const double total = sqrt(s);
@@ -92,9 +92,13 @@ constexpr unsigned kVecLdsReserve6 = 12288;
 //   kUpdate      W fp32 update = -u (no parameter, no decay) 24 B/element
 enum Form : int { kMaster = 0, kMasterBf16 = 1, kNoMaster = 2, kUpdate = 3 };
 
-template <int VEC, int FORM, int BS>
+// DEV: the scalars come from device memory (one uniform load per wave) instead
+// of the kernel arguments, so a captured graph replays any step whose scalars
+// the caller copied in beforehand.
+template <int VEC, int FORM, int BS, bool DEV>
 __global__ __launch_bounds__(BS) void adamw_kernel(const AdamwArgs a) {
     constexpr bool kReadP = FORM != kUpdate;
+    const AdamwScalars sc = DEV ? *a.sc_dev : a.sc;
     const int64_t n = a.n;
     const int64_t first = ((int64_t)blockIdx.x * BS + threadIdx.x) * VEC;
     // No early exit for lanes past the end: they fall through the scalar
@@ -118,15 +122,15 @@ __global__ __launch_bounds__(BS) void adamw_kernel(const AdamwArgs a) {
         const f32x4 m4 = ld_stream(reinterpret_cast<const f32x4*>(a.exp_avg + first));
         const f32x4 v4 = ld_stream(reinterpret_cast<const f32x4*>(a.exp_avg_sq + first));
         float coef;
-        if (!clip_coef(a, coef)) return;
+        if (!clip_coef(sc, a.norm_sq, coef)) return;
         float gs[4] = {g4.x, g4.y, g4.z, g4.w};
         float ps[4] = {p4.x, p4.y, p4.z, p4.w};
         float ms[4] = {m4.x, m4.y, m4.z, m4.w};
         float vs[4] = {v4.x, v4.y, v4.z, v4.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float u = adam_elem(a, coef, gs[j], ms[j], vs[j]);
-            ps[j] = FORM == kUpdate ? -u : apply_step(a, ps[j], u);
+            const float u = adam_elem(sc, coef, gs[j], ms[j], vs[j]);
+            ps[j] = FORM == kUpdate ? -u : apply_step(sc, ps[j], u);
         }
         if constexpr (FORM == kMaster || FORM == kMasterBf16)
             st_stream(reinterpret_cast<f32x4*>(a.master + first), f32x4{ps[0], ps[1], ps[2], ps[3]});
@@ -141,44 +145,47 @@ __global__ __launch_bounds__(BS) void adamw_kernel(const AdamwArgs a) {
     }
     // scalar path: VEC == 1, or the ragged tail of the VEC == 4 grid
     float coef;
-    if (!clip_coef(a, coef)) return;
+    if (!clip_coef(sc, a.norm_sq, coef)) return;
     const int64_t last = first + VEC < n ? first + VEC : n;
     for (int64_t i = first; i < last; ++i) {
         float m = a.exp_avg[i], v = a.exp_avg_sq[i];
-        const float u = adam_elem(a, coef, a.grad[i], m, v);
+        const float u = adam_elem(sc, coef, a.grad[i], m, v);
         a.exp_avg[i] = m;
         a.exp_avg_sq[i] = v;
         if constexpr (FORM == kUpdate) {
             a.update[i] = -u;
         } else if constexpr (FORM == kNoMaster) {
-            a.param_bf16[i] = (uint16_t)f32_to_bf16_rne(apply_step(a, bf16_to_f32(a.param_bf16[i]), u));
+            a.param_bf16[i] = (uint16_t)f32_to_bf16_rne(apply_step(sc, bf16_to_f32(a.param_bf16[i]), u));
         } else {
-            const float p = apply_step(a, a.master[i], u);
+            const float p = apply_step(sc, a.master[i], u);
             a.master[i] = p;
             if constexpr (FORM == kMasterBf16) a.param_bf16[i] = (uint16_t)f32_to_bf16_rne(p);
         }
     }
 }
 
-template <int VEC, int FORM, int BS>
+template <int VEC, int FORM, int BS, bool DEV>
 hipError_t launch(const AdamwArgs& a, unsigned lds, hipStream_t stream) {
     const int64_t threads = (a.n + VEC - 1) / VEC;
     const int64_t blocks = (threads + BS - 1) / BS;
     if (blocks > (int64_t)UINT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((adamw_kernel<VEC, FORM, BS>), dim3((unsigned)blocks), dim3(BS), lds, stream, a);
+    hipLaunchKernelGGL((adamw_kernel<VEC, FORM, BS, DEV>), dim3((unsigned)blocks), dim3(BS), lds, stream, a);
     return hipGetLastError();
 }
 
-template <int FORM>
+template <int FORM, bool DEV = false>
 hipError_t launch_form(const AdamwArgs& a, bool vec_ok, hipStream_t stream) {
     constexpr unsigned lds = (FORM == kNoMaster || FORM == kUpdate) ? kVecLdsReserve6 : kVecLdsReserve;
-    if (vec_ok) return launch<4, FORM, kVecBlock>(a, lds, stream);
-    return launch<1, FORM, kBlock>(a, 0, stream);
+    if (vec_ok) return launch<4, FORM, kVecBlock, DEV>(a, lds, stream);
+    return launch<1, FORM, kBlock, DEV>(a, 0, stream);
 }
 
 }  // namespace
 
 hipError_t launch_adamw(const AdamwArgs& a, bool vec_ok, hipStream_t stream) {
+    if (a.sc_dev != nullptr)
+        return a.param_bf16 != nullptr ? launch_form<kMasterBf16, true>(a, vec_ok, stream)
+                                       : launch_form<kMaster, true>(a, vec_ok, stream);
     return a.param_bf16 != nullptr ? launch_form<kMasterBf16>(a, vec_ok, stream)
                                    : launch_form<kMaster>(a, vec_ok, stream);
 }

@@ -7,6 +7,7 @@
 // to binary32 once.
 #include <cmath>
 #include <cstdint>
+#include <cstddef>
 #include <cstring>
 
 #include "../../include/zshard.h"
@@ -178,27 +179,42 @@ static int32_t adamw_check_hp(const zs_adamw* hp, int64_t n, const double* norm_
 }
 
 // host scalars: binary64, each rounded to binary32 once
-static zs::AdamwArgs adamw_scalars(const zs_adamw* hp, const double* norm_sq_dev) {
+static zs::AdamwScalars make_scalars(const zs_adamw* hp) {
     const double t = (double)hp->step;
     const double bias_correction1 = 1.0 - std::pow(hp->beta1, t);
     const double bias_correction2 = 1.0 - std::pow(hp->beta2, t);
+    zs::AdamwScalars c;
+    std::memset(&c, 0, sizeof(c));
+    c.beta1 = (float)hp->beta1;
+    c.beta2 = (float)hp->beta2;
+    c.one_minus_beta1 = (float)(1.0 - hp->beta1);
+    c.one_minus_beta2 = (float)(1.0 - hp->beta2);
+    c.step_size = (float)(hp->lr / bias_correction1);
+    c.bias_correction2_sqrt = (float)std::sqrt(bias_correction2);
+    c.eps = (float)hp->eps;
+    c.decay = (float)(1.0 - hp->lr * hp->weight_decay);
+    c.grad_scale = (float)hp->grad_scale;
+    c.clip = hp->max_norm > 0.0 ? 1 : 0;
+    c.max_norm = hp->max_norm;
+    c.extra_norm_sq = hp->extra_norm_sq;
+    return c;
+}
+
+static zs::AdamwArgs make_args(const zs_adamw* hp, const double* norm_sq_dev) {
     zs::AdamwArgs a;
     std::memset(&a, 0, sizeof(a));
-    a.beta1 = (float)hp->beta1;
-    a.beta2 = (float)hp->beta2;
-    a.one_minus_beta1 = (float)(1.0 - hp->beta1);
-    a.one_minus_beta2 = (float)(1.0 - hp->beta2);
-    a.step_size = (float)(hp->lr / bias_correction1);
-    a.bias_correction2_sqrt = (float)std::sqrt(bias_correction2);
-    a.eps = (float)hp->eps;
-    a.decay = (float)(1.0 - hp->lr * hp->weight_decay);
-    a.grad_scale = (float)hp->grad_scale;
-    a.clip = hp->max_norm > 0.0 ? 1 : 0;
-    a.max_norm = hp->max_norm;
-    a.extra_norm_sq = hp->extra_norm_sq;
+    a.sc = make_scalars(hp);
     a.norm_sq = norm_sq_dev;
     return a;
 }
+
+// the public struct and the kernels' one are the same bytes
+static_assert(sizeof(zs_adamw_scalars) == sizeof(zs::AdamwScalars), "scalar layout");
+static_assert(offsetof(zs_adamw_scalars, grad_scale) == offsetof(zs::AdamwScalars, grad_scale), "scalar layout");
+static_assert(offsetof(zs_adamw_scalars, clip) == offsetof(zs::AdamwScalars, clip), "scalar layout");
+static_assert(offsetof(zs_adamw_scalars, max_norm) == offsetof(zs::AdamwScalars, max_norm), "scalar layout");
+static_assert(offsetof(zs_adamw_scalars, extra_norm_sq) == offsetof(zs::AdamwScalars, extra_norm_sq),
+              "scalar layout");
 
 // the five buffers (any may be absent: bytes 0) pairwise disjoint, and none
 // that is written overlapping the norm
@@ -213,11 +229,18 @@ static int32_t adamw_check_overlap(const void* const* bufs, const int64_t* bytes
     return ZS_OK;
 }
 
-int32_t adamw_step(const zs_adamw* hp, float* master, float* exp_avg, float* exp_avg_sq,
-                   const float* grad, uint16_t* param_bf16, int64_t n, const double* norm_sq_dev,
-                   void* hip_stream) {
-    int32_t rc = adamw_check_hp(hp, n, norm_sq_dev);
-    if (rc != ZS_OK) return rc;
+// the master-form step: host scalars (hp) or a device copy of them (sc_dev)
+static int32_t adamw_master(const zs_adamw* hp, const zs_adamw_scalars* sc_dev, float* master, float* exp_avg,
+                            float* exp_avg_sq, const float* grad, uint16_t* param_bf16, int64_t n,
+                            const double* norm_sq_dev, void* hip_stream) {
+    int32_t rc;
+    if (sc_dev == nullptr) {
+        rc = adamw_check_hp(hp, n, norm_sq_dev);
+        if (rc != ZS_OK) return rc;
+    } else {
+        if (!size_ok(n) || !aligned(sc_dev, 8)) return ZS_EINVAL;
+        if (norm_sq_dev != nullptr && !aligned(norm_sq_dev, 8)) return ZS_EINVAL;
+    }
     if (n == 0) return ZS_OK;
     if (master == nullptr || exp_avg == nullptr || exp_avg_sq == nullptr || grad == nullptr)
         return ZS_EINVAL;
@@ -229,7 +252,18 @@ int32_t adamw_step(const zs_adamw* hp, float* master, float* exp_avg, float* exp
     const bool written[5] = {true, true, true, false, true};
     rc = adamw_check_overlap(bufs, bytes, written, norm_sq_dev);
     if (rc != ZS_OK) return rc;
-    zs::AdamwArgs a = adamw_scalars(hp, norm_sq_dev);
+    if (sc_dev != nullptr)   // the scalars are read while the buffers are written
+        for (int i = 0; i < 5; ++i)
+            if (written[i] && overlap(bufs[i], bytes[i], sc_dev, (int64_t)sizeof(zs_adamw_scalars)))
+                return ZS_EOVERLAP;
+    zs::AdamwArgs a;
+    if (sc_dev == nullptr) {
+        a = make_args(hp, norm_sq_dev);
+    } else {
+        std::memset(&a, 0, sizeof(a));
+        a.sc_dev = reinterpret_cast<const zs::AdamwScalars*>(sc_dev);
+        a.norm_sq = norm_sq_dev;
+    }
     a.master = master;
     a.exp_avg = exp_avg;
     a.exp_avg_sq = exp_avg_sq;
@@ -240,6 +274,30 @@ int32_t adamw_step(const zs_adamw* hp, float* master, float* exp_avg, float* exp
     const bool vec = aligned(master, 16) && aligned(exp_avg, 16) && aligned(exp_avg_sq, 16) &&
                      (param_bf16 == nullptr || aligned(param_bf16, 16));
     return hip_status(zs::launch_adamw(a, vec, as_stream(hip_stream)));
+}
+
+int32_t adamw_step(const zs_adamw* hp, float* master, float* exp_avg, float* exp_avg_sq,
+                   const float* grad, uint16_t* param_bf16, int64_t n, const double* norm_sq_dev,
+                   void* hip_stream) {
+    if (hp == nullptr) return ZS_EINVAL;
+    return adamw_master(hp, nullptr, master, exp_avg, exp_avg_sq, grad, param_bf16, n, norm_sq_dev, hip_stream);
+}
+
+int32_t adamw_scalars(const zs_adamw* hp, zs_adamw_scalars* out) {
+    if (out == nullptr) return ZS_EINVAL;
+    const int32_t rc = adamw_check_hp(hp, 0, nullptr);
+    if (rc != ZS_OK) return rc;
+    const zs::AdamwScalars c = make_scalars(hp);
+    std::memcpy(out, &c, sizeof(c));
+    return ZS_OK;
+}
+
+int32_t adamw_step_dev(const zs_adamw_scalars* scalars_dev, float* master, float* exp_avg, float* exp_avg_sq,
+                       const float* grad, uint16_t* param_bf16, int64_t n, const double* norm_sq_dev,
+                       void* hip_stream) {
+    if (scalars_dev == nullptr) return ZS_EINVAL;
+    return adamw_master(nullptr, scalars_dev, master, exp_avg, exp_avg_sq, grad, param_bf16, n, norm_sq_dev,
+                        hip_stream);
 }
 
 int32_t adamw_step_no_master(const zs_adamw* hp, uint16_t* param_bf16, float* exp_avg, float* exp_avg_sq,
@@ -256,7 +314,7 @@ int32_t adamw_step_no_master(const zs_adamw* hp, uint16_t* param_bf16, float* ex
     const bool written[5] = {true, true, true, false, false};
     rc = adamw_check_overlap(bufs, bytes, written, norm_sq_dev);
     if (rc != ZS_OK) return rc;
-    zs::AdamwArgs a = adamw_scalars(hp, norm_sq_dev);
+    zs::AdamwArgs a = make_args(hp, norm_sq_dev);
     a.exp_avg = exp_avg;
     a.exp_avg_sq = exp_avg_sq;
     a.grad = grad;
@@ -280,7 +338,7 @@ int32_t adam_update(const zs_adamw* hp, float* exp_avg, float* exp_avg_sq, const
     const bool written[5] = {true, true, true, false, false};
     rc = adamw_check_overlap(bufs, bytes, written, norm_sq_dev);
     if (rc != ZS_OK) return rc;
-    zs::AdamwArgs a = adamw_scalars(hp, norm_sq_dev);
+    zs::AdamwArgs a = make_args(hp, norm_sq_dev);
     a.exp_avg = exp_avg;
     a.exp_avg_sq = exp_avg_sq;
     a.grad = grad;

@@ -61,7 +61,9 @@ __device__ __forceinline__ u32x2 ld_stream_u32x2_a4(const void* p) {
 }
 
 // --- scalars of one AdamW step, formed on the host ------------------------
-struct AdamwArgs {
+// Binary64 on the host, each rounded to binary32 once; the same layout as
+// zs_adamw_scalars in zshard.h (checked in api.hip).
+struct AdamwScalars {
     float beta1, beta2;
     float one_minus_beta1, one_minus_beta2;
     float step_size;            // (float)(lr / bias_correction1)
@@ -72,6 +74,11 @@ struct AdamwArgs {
     int32_t clip;               // max_norm > 0
     double max_norm;
     double extra_norm_sq;
+};
+
+struct AdamwArgs {
+    AdamwScalars sc;            // in the kernel arguments, unless sc_dev is set
+    const AdamwScalars* sc_dev; // device copy of the scalars (a step replayable from a graph), nullable
     const double* norm_sq;      // device, nullable
     float* master;
     float* exp_avg;

@@ -278,6 +278,47 @@ ZS_API int32_t adamw_step(const zs_adamw* hp, float* master, float* exp_avg, flo
                    const double* norm_sq_dev, void* hip_stream);
 
 /*
+ * The per-step scalars of adamw_step, formed on the host from zs_adamw in
+ * binary64 and each rounded to binary32 once (beta1, beta2, 1 - beta1,
+ * 1 - beta2, lr / (1 - beta1^t), sqrt(1 - beta2^t), eps, 1 - lr*wd,
+ * grad_scale), plus the clip switch and the two binary64 clip inputs.
+ */
+typedef struct {
+    float beta1, beta2;
+    float one_minus_beta1, one_minus_beta2;
+    float step_size;              /* (float)(lr / (1 - beta1^t)) */
+    float bias_correction2_sqrt;  /* (float)sqrt(1 - beta2^t) */
+    float eps;
+    float decay;                  /* (float)(1 - lr * weight_decay) */
+    float grad_scale;
+    int32_t clip;                 /* max_norm > 0 */
+    double max_norm;
+    double extra_norm_sq;
+} zs_adamw_scalars;
+
+/*
+ * adamw_scalars — the scalars adamw_step forms from hp, on the host.
+ * Validates hp as adamw_step does (ZS_EINVAL; also for out == NULL).
+ */
+ZS_API int32_t adamw_scalars(const zs_adamw* hp, zs_adamw_scalars* out);
+
+/*
+ * adamw_step_dev — adamw_step with its scalars read from device memory.
+ * The kernels read *scalars_dev (adamw_scalars' output, copied to the
+ * device by the caller) when they run, not when the call is made: a step
+ * captured once in a HIP graph, behind a copy of the next step's scalars
+ * into scalars_dev, replays every later step (step counter, learning-rate
+ * schedule, clip inputs) without re-capture.  Results are those of
+ * adamw_step with the same hyperparameters, bit for bit.  scalars_dev:
+ * device, 8-byte aligned, read; it must not overlap any written buffer.
+ * The values are not validated (they are not on the host).  Other
+ * arguments, layout and errors as adamw_step.
+ */
+ZS_API int32_t adamw_step_dev(const zs_adamw_scalars* scalars_dev, float* master, float* exp_avg,
+                              float* exp_avg_sq, const float* grad, uint16_t* param_bf16, int64_t n,
+                              const double* norm_sq_dev, void* hip_stream);
+
+/*
  * adamw_step_no_master — the same update with no fp32 master: the bf16
  * parameter shard is read, updated and rounded back in place.
  * [ZeRO page] §"ZeRO-3: 切分参数", ZeRO3Optimizer.step (the update is added

@@ -37,7 +37,7 @@ def no_launch_reached():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 15 and set(names) == set(B.EXPORTS), names
+    assert len(names) == 17 and set(names) == set(B.EXPORTS), names
     L = zs.lib()
     for name in names:
         assert getattr(L, name) is not None
@@ -140,6 +140,49 @@ def test_adamw_no_master_rejects():
     assert call(b=FAKE + 1) == B.ZS_EINVAL
     assert call(m=FAKE + 1024) == B.ZS_EOVERLAP                   # exp_avg inside the bf16 parameter
     assert call(norm=FAKE + 2**21 + 64) == B.ZS_EOVERLAP          # norm inside exp_avg_sq
+    assert call(n=0) == B.ZS_OK
+
+
+def test_adamw_scalars_match_the_oracle_bit_for_bit(orc):
+    """The library's host scalars and the oracle's are formed independently
+    (both binary64, one rounding each): identical bits over random
+    hyperparameters and steps, and the hand-worked golden patterns."""
+    import random
+    import struct
+    rnd = random.Random(5)
+    names = ("beta1", "beta2", "one_minus_beta1", "one_minus_beta2", "step_size", "bias_correction2_sqrt", "eps",
+             "decay", "grad_scale")
+    bits = lambda x: struct.unpack("<I", struct.pack("<f", x))[0]
+    for _ in range(300):
+        kw = dict(lr=10 ** rnd.uniform(-6, -1), beta1=rnd.choice([0.0, 0.5, 0.9, rnd.uniform(0, 0.999999)]),
+                  beta2=rnd.choice([0.0, 0.95, 0.999, rnd.uniform(0, 0.9999999)]), eps=10 ** rnd.uniform(-12, 0),
+                  weight_decay=rnd.choice([0.0, 0.1, rnd.uniform(0, 10)]), grad_scale=2.0 ** -rnd.randint(0, 12),
+                  max_norm=rnd.choice([0.0, 1.0]), extra_norm_sq=rnd.uniform(0, 3), step=rnd.randint(1, 100000))
+        got = zs.adamw_scalars(zs.AdamWConfig(**kw))
+        want = oracle.adamw_scalars(oracle.make_hp(kw["lr"], kw["beta1"], kw["beta2"], kw["eps"],
+                                                   kw["weight_decay"], kw["grad_scale"], kw["max_norm"],
+                                                   kw["extra_norm_sq"], kw["step"]))
+        for nm in names:
+            assert bits(getattr(got, nm)) == bits(getattr(want, nm)), (nm, kw)
+        assert got.clip == (1 if kw["max_norm"] > 0 else 0)
+        assert got.max_norm == kw["max_norm"] and got.extra_norm_sq == kw["extra_norm_sq"]
+    assert len(zs.scalars_bytes(zs.AdamWConfig(lr=1e-3))) == 56
+
+
+def test_adamw_scalars_and_step_dev_reject():
+    L = zs.lib()
+    out = B.AdamWScalars()
+    assert L.adamw_scalars(ctypes.byref(_hp(step=0)), ctypes.byref(out)) == B.ZS_EINVAL
+    assert L.adamw_scalars(ctypes.byref(_hp()), None) == B.ZS_EINVAL
+    assert L.adamw_scalars(None, ctypes.byref(out)) == B.ZS_EINVAL
+    sc = FAKE + 2**30
+    call = lambda s=sc, master=FAKE, n=1024, norm=0: L.adamw_step_dev(
+        s, master, FAKE + 2**20, FAKE + 2**21, FAKE + 2**22, 0, n, norm, None)
+    assert call(s=0) == B.ZS_EINVAL
+    assert call(s=sc + 4) == B.ZS_EINVAL                     # scalars must be 8-byte aligned
+    assert call(s=FAKE + 64) == B.ZS_EOVERLAP                # scalars inside the master being written
+    assert call(norm=FAKE + 2**21 + 8) == B.ZS_EOVERLAP      # norm inside exp_avg_sq
+    assert call(n=(1 << 39) + 1) == B.ZS_EINVAL
     assert call(n=0) == B.ZS_OK
 
 
