@@ -370,7 +370,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU's shard only; --gpus {args.gpus} is not "
+        print(f"bench.py measures one GPU's shard only; --gpus {args.gpus} is not "
               "supported (collectives are out of scope). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 

@@ -10,7 +10,7 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
-    config.addinivalue_line("markers", "slow: full-size parity case (GPU box only)")
+    config.addinivalue_line("markers", "slow: full-size parity case (needs a GPU)")
 
 
 @pytest.fixture(scope="session")
