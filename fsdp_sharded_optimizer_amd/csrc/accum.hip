@@ -10,17 +10,18 @@
 // Layout: lane-contiguous groups of 4 elements (a 64-bit bf16 or 128-bit
 // fp32 load and a 128-bit fp32 access per lane).  A workgroup of BS threads
 // covers Q groups per lane, the q-th at offset q*BS*4 in its tile, every
-// load of the tile issued before the first store.  Every form, the fused
-// one included, runs Q = 1 in one-wave workgroups, uncapped: the fastest
-// shape on gfx950 (84 % of peak for the accumulating form, 85 % for the
-// overwriting one, 84.5 % with the norm partials, against 82 %, 83 % and
-// 79.8 % in 256-thread workgroups with the best Q and residency cap).
+// load of the tile issued before the first store.  The plain forms and the
+// accumulating fused form run Q = 1 in one-wave workgroups, uncapped: the
+// fastest shape on gfx950 (84 % of peak for the accumulating form, 85 % for
+// the overwriting one, 84.5 % with the norm partials, against 82 %, 83 % and
+// 79.8 % in 256-thread workgroups with the best Q and residency cap); the
+// overwriting fused form runs Q = 4 (see launch_grad_accum_norm_sq).
 //
-// Fused norm association (fixed by n): each lane adds the squares of its 4
-// elements, 0 and 2 into one running sum, 1 and 3 into the other; the 64
-// lanes combine in a fixed butterfly into one binary64 partial per 256
-// elements; the partials are reduced in fixed contiguous chunks (at most
-// kReduceChunks), then by one workgroup.
+// Fused norm association (fixed by n and the overwrite flag): each lane adds
+// the squares of its Q groups of 4 elements, 0 and 2 into one running sum, 1
+// and 3 into the other; the 64 lanes combine in a fixed butterfly into one
+// binary64 partial per 256*Q elements; the partials are reduced in fixed
+// contiguous chunks (at most kReduceChunks), then by one workgroup.
 #include "reduce.h"
 
 namespace zs {
@@ -99,53 +100,66 @@ constexpr int kAccumBlock = 64;   // one wave per workgroup
 template <int Q>
 constexpr int64_t per_block() { return (int64_t)kAccumBlock * 4 * Q; }
 
-constexpr int kFusedQ = 1;
+// The fused forms: the accumulating one runs Q = 1 uncapped (84.5 % of the
+// HBM peak); the overwriting one moves only 6 B per element, so its waves
+// are short and the norm's tail weighs more: Q = 4 (1024 elements and one
+// partial per workgroup) with residency capped at 13 workgroups per CU
+// measured 82.7 % on gfx950 against 76-78 % for Q = 1.
+constexpr int kFusedQAdd = 1;
+constexpr int kFusedQOverwrite = 4;
+constexpr unsigned kFusedOverwriteLds = 12288;
 
 template <int Q, bool VEC, bool BF16, bool OVERWRITE, bool NORM>
-hipError_t launch(float* acc, const void* grad, int64_t n, float scale, double* partials, hipStream_t stream) {
+hipError_t launch(float* acc, const void* grad, int64_t n, float scale, double* partials, unsigned lds,
+                  hipStream_t stream) {
     const int64_t blocks = (n + per_block<Q>() - 1) / per_block<Q>();
     if (blocks > (int64_t)UINT32_MAX) return hipErrorInvalidValue;
     hipLaunchKernelGGL((accum_kernel<Q, kAccumBlock, VEC, BF16, OVERWRITE, NORM>), dim3((unsigned)blocks),
-                       dim3(kAccumBlock), 0, stream, acc, grad, n, scale, partials);
+                       dim3(kAccumBlock), lds, stream, acc, grad, n, scale, partials);
     return hipGetLastError();
 }
 
-template <int Q, bool NORM>
-hipError_t dispatch(float* acc, const void* grad, int grad_bf16, int64_t n, int overwrite, bool vec, float scale,
-                    double* partials, hipStream_t stream) {
-    if (vec) {
-        if (grad_bf16) return overwrite ? launch<Q, true, true, true, NORM>(acc, grad, n, scale, partials, stream)
-                                        : launch<Q, true, true, false, NORM>(acc, grad, n, scale, partials, stream);
-        return overwrite ? launch<Q, true, false, true, NORM>(acc, grad, n, scale, partials, stream)
-                         : launch<Q, true, false, false, NORM>(acc, grad, n, scale, partials, stream);
-    }
-    if (grad_bf16) return overwrite ? launch<Q, false, true, true, NORM>(acc, grad, n, scale, partials, stream)
-                                    : launch<Q, false, true, false, NORM>(acc, grad, n, scale, partials, stream);
-    return overwrite ? launch<Q, false, false, true, NORM>(acc, grad, n, scale, partials, stream)
-                     : launch<Q, false, false, false, NORM>(acc, grad, n, scale, partials, stream);
+template <int Q, bool NORM, bool OVERWRITE>
+hipError_t dispatch(float* acc, const void* grad, int grad_bf16, int64_t n, bool vec, float scale,
+                    double* partials, unsigned lds, hipStream_t stream) {
+    if (vec)
+        return grad_bf16 ? launch<Q, true, true, OVERWRITE, NORM>(acc, grad, n, scale, partials, lds, stream)
+                         : launch<Q, true, false, OVERWRITE, NORM>(acc, grad, n, scale, partials, lds, stream);
+    return grad_bf16 ? launch<Q, false, true, OVERWRITE, NORM>(acc, grad, n, scale, partials, 0, stream)
+                     : launch<Q, false, false, OVERWRITE, NORM>(acc, grad, n, scale, partials, 0, stream);
 }
 
 }  // namespace
 
 hipError_t launch_grad_accum(float* acc, const void* grad, int grad_bf16, int64_t n, int overwrite,
                              bool vec_ok, hipStream_t stream) {
-    return dispatch<1, false>(acc, grad, grad_bf16, n, overwrite, vec_ok, 0.0f, nullptr, stream);
+    return overwrite ? dispatch<1, false, true>(acc, grad, grad_bf16, n, vec_ok, 0.0f, nullptr, 0, stream)
+                     : dispatch<1, false, false>(acc, grad, grad_bf16, n, vec_ok, 0.0f, nullptr, 0, stream);
 }
 
+// workspace partials: the larger count of the two fused shapes
 int64_t accum_norm_partials(int64_t n) {
-    return n <= 0 ? 0 : (n + per_block<kFusedQ>() - 1) / per_block<kFusedQ>();
+    return n <= 0 ? 0 : (n + per_block<kFusedQAdd>() - 1) / per_block<kFusedQAdd>();
 }
 
 hipError_t launch_grad_accum_norm_sq(float* acc, const void* grad, int grad_bf16, int64_t n, int overwrite,
                                      float scale, double* out, double* workspace, bool vec_ok,
                                      hipStream_t stream) {
-    const int64_t parts = accum_norm_partials(n);
-    if (parts > 0) {
-        const hipError_t e = dispatch<kFusedQ, true>(acc, grad, grad_bf16, n, overwrite, vec_ok, scale,
-                                                     workspace, stream);
+    int64_t parts = 0;
+    if (n > 0) {
+        hipError_t e;
+        if (overwrite) {
+            parts = (n + per_block<kFusedQOverwrite>() - 1) / per_block<kFusedQOverwrite>();
+            e = dispatch<kFusedQOverwrite, true, true>(acc, grad, grad_bf16, n, vec_ok, scale, workspace,
+                                                       kFusedOverwriteLds, stream);
+        } else {
+            parts = (n + per_block<kFusedQAdd>() - 1) / per_block<kFusedQAdd>();
+            e = dispatch<kFusedQAdd, true, false>(acc, grad, grad_bf16, n, vec_ok, scale, workspace, 0, stream);
+        }
         if (e != hipSuccess) return e;
     }
-    return launch_sum_partials(workspace, parts, workspace + parts, out, stream);
+    // the stage buffer follows the largest partial count the workspace is sized for
+    return launch_sum_partials(workspace, parts, workspace + accum_norm_partials(n), out, stream);
 }
 
 }  // namespace zs
