@@ -24,8 +24,11 @@
  *   - Device buffers are owned by the caller (allocated and freed by it);
  *     the library allocates nothing.  Host arrays passed in (zs_tensor
  *     lists, zs_adamw) are read during the call only.
- *   - hip_stream is a hipStream_t (NULL = the default stream).  Device calls
- *     only enqueue work on it and return; nothing blocks, nothing syncs.
+ *   - hip_stream is a hipStream_t (NULL = the default stream) of the current
+ *     device, and every device buffer lives on that device.  Device calls
+ *     only enqueue work on it and return; nothing blocks, nothing syncs,
+ *     nothing is allocated or cleared, so a sequence of calls can be
+ *     captured into a HIP graph as is.
  *   - Arguments are validated on the host before anything is enqueued; on
  *     failure the call returns a negative code and launches nothing.
  *     n == 0 (or count == 0 with nothing to pad) is a valid no-op.
