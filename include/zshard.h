@@ -131,7 +131,7 @@ ZS_API int32_t zero_shard_range(int64_t total, int32_t world, int32_t rank, zs_s
  * flat), ZS_EHIP.
  */
 ZS_API int32_t flat_pack(const zs_tensor* src, int32_t count, int32_t src_dtype,
-                  void* flat, int32_t flat_dtype, int64_t padded_total, void* hip_stream);
+                         void* flat, int32_t flat_dtype, int64_t padded_total, void* hip_stream);
 
 /*
  * flat_unpack — the inverse of flat_pack, padding dropped.
@@ -144,7 +144,7 @@ ZS_API int32_t flat_pack(const zs_tensor* src, int32_t count, int32_t src_dtype,
  * Errors: as flat_pack.
  */
 ZS_API int32_t flat_unpack(const void* flat, int32_t flat_dtype,
-                    const zs_tensor* dst, int32_t count, int32_t dst_dtype, void* hip_stream);
+                           const zs_tensor* dst, int32_t count, int32_t dst_dtype, void* hip_stream);
 
 /*
  * flat_apply_update — add a gathered fp32 update into the parameters.
@@ -161,7 +161,7 @@ ZS_API int32_t flat_unpack(const void* flat, int32_t flat_dtype,
  * pointer), ZS_EOVERLAP, ZS_EHIP.
  */
 ZS_API int32_t flat_apply_update(const float* update, const zs_tensor* dst, int32_t count, int32_t dst_dtype,
-                          void* hip_stream);
+                                 void* hip_stream);
 
 /*
  * grad_accum — fp32 gradient accumulation over micro-batches.
@@ -174,7 +174,7 @@ ZS_API int32_t flat_apply_update(const float* update, const zs_tensor* dst, int3
  * Errors: ZS_EINVAL, ZS_EOVERLAP (acc overlaps grad), ZS_EHIP.
  */
 ZS_API int32_t grad_accum(float* acc, const void* grad, int32_t grad_dtype, int64_t n,
-                   int32_t overwrite, void* hip_stream);
+                          int32_t overwrite, void* hip_stream);
 
 /*
  * grad_reduce_chunks — the receiving side of a reduce-scatter on one GPU:
@@ -193,7 +193,7 @@ ZS_API int32_t grad_accum(float* acc, const void* grad, int32_t grad_dtype, int6
  * pointer, dtype), ZS_EOVERLAP (a chunk overlaps acc), ZS_EHIP.
  */
 ZS_API int32_t grad_reduce_chunks(float* acc, const void* const* chunks, int32_t count, int32_t grad_dtype, int64_t n,
-                           int32_t overwrite, void* hip_stream);
+                                  int32_t overwrite, void* hip_stream);
 
 /*
  * grad_norm_sq_workspace_bytes — bytes of device workspace grad_norm_sq
@@ -218,7 +218,7 @@ ZS_API int64_t grad_norm_sq_workspace_bytes(int64_t n);
  * Errors: ZS_EINVAL, ZS_EWORKSPACE, ZS_EOVERLAP, ZS_EHIP.
  */
 ZS_API int32_t grad_norm_sq(const float* grad, int64_t n, double grad_scale, double* out_sq_dev,
-                     void* workspace, int64_t workspace_bytes, void* hip_stream);
+                            void* workspace, int64_t workspace_bytes, void* hip_stream);
 
 /*
  * grad_accum_norm_sq_workspace_bytes — bytes of device workspace
@@ -245,8 +245,8 @@ ZS_API int64_t grad_accum_norm_sq_workspace_bytes(int64_t n);
  * *out_sq_dev, workspace), ZS_EHIP.
  */
 ZS_API int32_t grad_accum_norm_sq(float* acc, const void* grad, int32_t grad_dtype, int64_t n, int32_t overwrite,
-                           double grad_scale, double* out_sq_dev, void* workspace, int64_t workspace_bytes,
-                           void* hip_stream);
+                                  double grad_scale, double* out_sq_dev, void* workspace, int64_t workspace_bytes,
+                                  void* hip_stream);
 
 /*
  * adamw_step — the fused AdamW update of one rank's shard.
@@ -277,8 +277,8 @@ ZS_API int32_t grad_accum_norm_sq(float* acc, const void* grad, int32_t grad_dty
  * Errors: ZS_EINVAL (hp NULL or out of range, pointers), ZS_EOVERLAP, ZS_EHIP.
  */
 ZS_API int32_t adamw_step(const zs_adamw* hp, float* master, float* exp_avg, float* exp_avg_sq,
-                   const float* grad, uint16_t* param_bf16, int64_t n,
-                   const double* norm_sq_dev, void* hip_stream);
+                          const float* grad, uint16_t* param_bf16, int64_t n,
+                          const double* norm_sq_dev, void* hip_stream);
 
 /*
  * The per-step scalars of adamw_step, formed on the host from zs_adamw in
@@ -335,7 +335,7 @@ ZS_API int32_t adamw_step_dev(const zs_adamw_scalars* scalars_dev, float* master
  * adamw_step.  Errors: as adamw_step.
  */
 ZS_API int32_t adamw_step_no_master(const zs_adamw* hp, uint16_t* param_bf16, float* exp_avg, float* exp_avg_sq,
-                             const float* grad, int64_t n, const double* norm_sq_dev, void* hip_stream);
+                                    const float* grad, int64_t n, const double* norm_sq_dev, void* hip_stream);
 
 /*
  * adam_update — the ZeRO-1 form of the step: the update as a vector.
@@ -355,7 +355,7 @@ ZS_API int32_t adamw_step_no_master(const zs_adamw* hp, uint16_t* param_bf16, fl
  * ZS_EHIP.
  */
 ZS_API int32_t adam_update(const zs_adamw* hp, float* exp_avg, float* exp_avg_sq, const float* grad, float* update,
-                    int64_t n, const double* norm_sq_dev, void* hip_stream);
+                           int64_t n, const double* norm_sq_dev, void* hip_stream);
 
 /* Static description of a return code. */
 ZS_API const char* zs_strerror(int32_t code);
