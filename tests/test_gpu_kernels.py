@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import fsdp_sharded_optimizer_amd as zs
-from tests.parity import (NORM_TOL, StateCheck, bf16_ulps, bits_equal, from_np, identical_fraction,
+from tests.parity import (NORM_TOL, StateCheck, bits_equal, from_np, identical_fraction,
                           to_np)
 
 pytestmark = pytest.mark.gpu
