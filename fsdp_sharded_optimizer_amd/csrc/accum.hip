@@ -17,11 +17,12 @@
 // 79.8 % in 256-thread workgroups with the best Q and residency cap); the
 // overwriting fused form runs Q = 4 (see launch_grad_accum_norm_sq).
 //
-// Fused norm association (fixed by n and the overwrite flag): each lane adds
-// the squares of its Q groups of 4 elements, 0 and 2 into one running sum, 1
-// and 3 into the other; the 64 lanes combine in a fixed butterfly into one
-// binary64 partial per 256*Q elements; the partials are reduced in fixed
-// contiguous chunks (at most kReduceChunks), then by one workgroup.
+// Fused norm association (fixed by n, the overwrite flag and the gradient
+// dtype): each lane adds the squares of its Q groups of 4 elements, 0 and 2
+// into one running sum, 1 and 3 into the other; the 64 lanes combine in a
+// fixed butterfly into one binary64 partial per 256*Q elements; the partials
+// are reduced in fixed contiguous chunks (at most kReduceChunks), then by one
+// workgroup.
 #include "reduce.h"
 
 namespace zs {
@@ -100,11 +101,13 @@ constexpr int kAccumBlock = 64;   // one wave per workgroup
 template <int Q>
 constexpr int64_t per_block() { return (int64_t)kAccumBlock * 4 * Q; }
 
-// The fused forms: the accumulating one runs Q = 1 uncapped (84.5 % of the
-// HBM peak); the overwriting one moves only 6 B per element, so its waves
-// are short and the norm's tail weighs more: Q = 4 (1024 elements and one
+// The fused forms run Q = 1 uncapped (84.5 % of the HBM peak accumulating a
+// bf16 gradient, 83.5 % overwriting with an fp32 one), except the overwriting
+// form with a bf16 gradient: it moves only 6 B per element, so its waves are
+// short and the norm's tail weighs more, and Q = 4 (1024 elements and one
 // partial per workgroup) with residency capped at 13 workgroups per CU
-// measured 82.7 % on gfx950 against 76-78 % for Q = 1.
+// measured 82.7 % on gfx950 against 76-78 % for Q = 1 (for an fp32 gradient
+// that shape gives 80 %).
 constexpr int kFusedQAdd = 1;
 constexpr int kFusedQOverwrite = 4;
 constexpr unsigned kFusedOverwriteLds = 12288;
@@ -148,13 +151,16 @@ hipError_t launch_grad_accum_norm_sq(float* acc, const void* grad, int grad_bf16
     int64_t parts = 0;
     if (n > 0) {
         hipError_t e;
-        if (overwrite) {
+        if (overwrite && grad_bf16) {
             parts = (n + per_block<kFusedQOverwrite>() - 1) / per_block<kFusedQOverwrite>();
             e = dispatch<kFusedQOverwrite, true, true>(acc, grad, grad_bf16, n, vec_ok, scale, workspace,
                                                        kFusedOverwriteLds, stream);
         } else {
             parts = (n + per_block<kFusedQAdd>() - 1) / per_block<kFusedQAdd>();
-            e = dispatch<kFusedQAdd, true, false>(acc, grad, grad_bf16, n, vec_ok, scale, workspace, 0, stream);
+            e = overwrite ? dispatch<kFusedQAdd, true, true>(acc, grad, grad_bf16, n, vec_ok, scale, workspace, 0,
+                                                             stream)
+                          : dispatch<kFusedQAdd, true, false>(acc, grad, grad_bf16, n, vec_ok, scale, workspace, 0,
+                                                              stream);
         }
         if (e != hipSuccess) return e;
     }
