@@ -339,23 +339,41 @@ def run_cpu_baseline(w, target_s: float = 10.0, sample: int = 1 << 25):
                      else g.numpy().copy())
     acc = np.empty(n, np.float32)
     done = 0
+    phase = {"accumulate": 0.0, "norm": 0.0, "adamw": 0.0}
     t0 = time.perf_counter()
     while True:
+        ta = time.perf_counter()
         for mb, g in enumerate(grads):
             oracle.grad_accum(acc, g, code, overwrite=(mb == 0))
+        tb = time.perf_counter()
         s = oracle.grad_norm_sq(acc, w.grad_scale)   # the oracle has no fused form
+        tc = time.perf_counter()
         hp = oracle.make_hp(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, w.grad_scale, w.max_norm,
                             workloads.other_ranks_norm_sq(w, 1, n), done + 1)
         oracle.adamw_step(hp, master, m, v, acc, bf, norm_sq=s)
+        td = time.perf_counter()
+        phase["accumulate"] += tb - ta
+        phase["norm"] += tc - tb
+        phase["adamw"] += td - tc
         done += 1
         el = time.perf_counter() - t0
         if el >= target_s or done >= 1000:
             break
+    bpe = step_bytes_per_elem(w)
+    accum_bytes = bpe["step"] - bpe["adamw_step"]   # every micro-batch's accumulation
+    phases = {
+        "accumulate": {"ms_per_step": phase["accumulate"] * 1e3 / done,
+                       "gbps": accum_bytes * n * done / phase["accumulate"] / 1e9},
+        "norm": {"ms_per_step": phase["norm"] * 1e3 / done, "gbps": 4 * n * done / phase["norm"] / 1e9},
+        "adamw": {"ms_per_step": phase["adamw"] * 1e3 / done,
+                  "gbps": bpe["adamw_step"] * n * done / phase["adamw"] / 1e9},
+    }
     return {"value": n * done / el, "unit": "elements/s", "cores": oracle.num_threads(),
             "kind": "oracle",
             "sample": f"{n} elements of the same workload (first {n} of a shard drawn by the same "
                       f"recipe on the CPU), {done} whole steps ({w.micro_batches} micro-batch "
-                      f"accumulations + norm + AdamW/bf16) in {el:.1f} s"}
+                      f"accumulations + norm + AdamW/bf16) in {el:.1f} s",
+            "phases": phases}
 
 
 def main():
