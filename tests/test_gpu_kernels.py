@@ -680,3 +680,89 @@ def test_adam_update_and_no_master_special_values():
         for name, gpu, ref in (("update", u, u_ref), ("m", m, m_ref), ("v", v, v_ref), ("b", b, b_ref),
                                ("m2", m2, m2_ref), ("v2", v2, v2_ref)):
             assert _same(to_np(gpu), ref), (t, name)
+
+
+# ---------------------------------------------------------------------------
+# every size from 0 to 257, aligned and as misaligned views
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("offset", [0, 1])
+def test_every_small_size(offset):
+    """Each entry point at every n in [0, 257] (all tails of the 4- and
+    8-element vectors and of the first workgroup tiles), against the oracle:
+    accumulations, reductions and the three step forms bit-exact, the norm
+    within the bar, flatten and unflatten of a random 3-way split bit-exact."""
+    rng = np.random.default_rng(1234 + offset)
+    norm = torch.zeros(1, dtype=torch.float64, device="cuda")
+    for n in range(0, 258):
+        g32 = (rng.standard_normal(n) * 1e-2).astype(np.float32)
+        g16 = oracle.bf16_rne((rng.standard_normal(n) * 1e-2).astype(np.float32))
+        acc0 = (rng.standard_normal(n) * 1e-2).astype(np.float32)
+        # grad_accum (bf16, add) and grad_accum_norm_sq (fp32, overwrite)
+        ref = acc0.copy()
+        oracle.grad_accum(ref, g16, oracle.BF16, overwrite=False)
+        acc, aw = dev_buf(acc0, offset)
+        zs.grad_accum(acc, dev_buf(g16, offset, bf16=True)[0], overwrite=False)
+        assert bits_equal(to_np(acc), ref), ("grad_accum", n)
+        ref2 = acc0.copy()
+        oracle.grad_accum(ref2, g32, oracle.F32, overwrite=True)
+        acc2, _ = dev_buf(acc0, offset)
+        zs.grad_accum_norm_sq(acc2, dev_buf(g32, offset)[0], True, 0.5, norm)
+        assert bits_equal(to_np(acc2), ref2), ("grad_accum_norm_sq", n)
+        want = oracle.grad_norm_sq(ref2, 0.5)
+        got = norm.item()
+        assert (got == 0.0 and want == 0.0) or abs(math.sqrt(got) - math.sqrt(want)) <= NORM_TOL * math.sqrt(want), n
+        zs.grad_norm_sq(dev_buf(ref2, offset)[0], 0.5, norm)
+        got = norm.item()
+        assert (got == 0.0 and want == 0.0) or abs(math.sqrt(got) - math.sqrt(want)) <= NORM_TOL * math.sqrt(want), n
+        # grad_reduce_chunks: three bf16 chunks into acc
+        chunks = [oracle.bf16_rne((rng.standard_normal(n) * 1e-2).astype(np.float32)) for _ in range(3)]
+        ref3 = acc0.copy()
+        for c in chunks:
+            oracle.grad_accum(ref3, c, oracle.BF16, overwrite=False)
+        acc3, _ = dev_buf(acc0, offset)
+        zs.grad_reduce_chunks(acc3, [dev_buf(c, offset, bf16=True)[0] for c in chunks], False)
+        assert bits_equal(to_np(acc3), ref3), ("grad_reduce_chunks", n)
+        # the three step forms, clipped with the oracle's norm
+        S = oracle.grad_norm_sq(g32, 1 / 8) + 1e-3
+        nrm = torch.tensor([S], dtype=torch.float64, device="cuda")
+        hp_gpu, hp_orc = _hp(3, scale=1 / 8, max_norm=0.5 * math.sqrt(S), extra=0.0)
+        hp0_gpu, hp0_orc = _hp(3, wd=0.0, scale=1 / 8, max_norm=0.5 * math.sqrt(S), extra=0.0)
+        p0 = rng.uniform(-0.1, 0.1, n).astype(np.float32)
+        m0 = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+        v0 = (rng.uniform(0, 1e-7, n)).astype(np.float32)
+        pr, mr, vr, br = p0.copy(), m0.copy(), v0.copy(), np.zeros(n, np.uint16)
+        oracle.adamw_step(hp_orc, pr, mr, vr, g32, br, norm_sq=S)
+        p, m, v, b = dev_buf(p0, offset)[0], dev_buf(m0, offset)[0], dev_buf(v0, offset)[0], \
+            dev_buf(np.zeros(n, np.uint16), offset, bf16=True)[0]
+        zs.adamw_step(hp_gpu, p, m, v, dev_buf(g32, offset)[0], b, norm_sq=nrm)
+        for name, x, r in (("p", p, pr), ("m", m, mr), ("v", v, vr), ("b", b, br)):
+            assert bits_equal(to_np(x), r), ("adamw_step", n, name)
+        mu, vu, uu = m0.copy(), v0.copy(), np.empty(n, np.float32)
+        oracle.adam_update(hp0_orc, mu, vu, g32, uu, norm_sq=S)
+        m, v, u = dev_buf(m0, offset)[0], dev_buf(v0, offset)[0], dev_buf(np.zeros(n, np.float32), offset)[0]
+        zs.adam_update(hp0_gpu, m, v, dev_buf(g32, offset)[0], u, norm_sq=nrm)
+        for name, x, r in (("update", u, uu), ("m", m, mu), ("v", v, vu)):
+            assert bits_equal(to_np(x), r), ("adam_update", n, name)
+        b0 = oracle.bf16_rne(p0)
+        bn, mn, vn = b0.copy(), m0.copy(), v0.copy()
+        oracle.adamw_step_no_master(hp_orc, bn, mn, vn, g32, norm_sq=S)
+        b, m, v = dev_buf(b0, offset, bf16=True)[0], dev_buf(m0, offset)[0], dev_buf(v0, offset)[0]
+        zs.adamw_step_no_master(hp_gpu, b, m, v, dev_buf(g32, offset)[0], norm_sq=nrm)
+        for name, x, r in (("b", b, bn), ("m", m, mn), ("v", v, vn)):
+            assert bits_equal(to_np(x), r), ("adamw_step_no_master", n, name)
+        # flatten a random 3-way split of n bf16 elements (padded by 0..3) and unflatten it
+        cuts = np.sort(rng.integers(0, n + 1, size=2))
+        parts = [g16[:cuts[0]], g16[cuts[0]:cuts[1]], g16[cuts[1]:]]
+        pad = n + int(rng.integers(0, 4))
+        want_flat = oracle.flat_pack([np.ascontiguousarray(x) for x in parts], oracle.BF16, oracle.F32, pad)
+        flat, _ = dev_buf(np.zeros(pad, np.float32), offset)
+        if pad > 0:
+            flat.fill_(float("nan"))
+        zs.flat_pack([dev_buf(np.ascontiguousarray(x), offset, bf16=True)[0] for x in parts], flat, pad)
+        assert bits_equal(to_np(flat), want_flat), ("flat_pack", n)
+        outs = [dev_buf(np.zeros(x.size, np.uint16), offset, bf16=True)[0] for x in parts]
+        zs.flat_unpack(flat, outs)
+        for o, x in zip(outs, parts):
+            assert bits_equal(to_np(o), oracle.bf16_rne(oracle.bf16_widen(x))), ("flat_unpack", n)
+    torch.cuda.synchronize()
