@@ -224,7 +224,10 @@ def run_gpu(w, steps: int, warmup: int):
 
 def run_flat(w, reps: int = 10):
     """FSDP unit: time flat_pack of the unit's tensors into the padded flat
-    bf16 buffer and flat_unpack back (4 B per element each)."""
+    bf16 buffer and flat_unpack back (4 B per element each), then the two
+    conversions: the widening pack into an fp32 flat buffer (the master's
+    initialisation) and the re-casting unpack from it (6 B per element
+    each)."""
     import torch
     import workloads
     import fsdp_sharded_optimizer_amd as zs
@@ -249,10 +252,28 @@ def run_flat(w, reps: int = 10):
     pack_ms = e[0].elapsed_time(e[1]) / reps
     unpack_ms = e[1].elapsed_time(e[2]) / reps
     assert all(torch.equal(a.view(torch.int16), b.view(torch.int16)) for a, b in zip(params, outs))
+    del flat
+    flat32 = torch.empty(padded, dtype=torch.float32, device=dev)
+    zs.flat_pack(params, flat32, padded)
+    zs.flat_unpack(flat32, outs)
+    e[0].record()
+    for _ in range(reps):
+        zs.flat_pack(params, flat32, padded)
+    e[1].record()
+    for _ in range(reps):
+        zs.flat_unpack(flat32, outs)
+    e[2].record()
+    torch.cuda.synchronize()
+    widen_ms = e[0].elapsed_time(e[1]) / reps
+    recast_ms = e[1].elapsed_time(e[2]) / reps
+    assert all(torch.equal(a.view(torch.int16), b.view(torch.int16)) for a, b in zip(params, outs))
     bytes_ = 4 * w.total
+    gbps = lambda b, ms: b / (ms * 1e-3) / 1e9
     return {"tensors": len(params), "elements": w.total, "padded": padded,
             "pack_ms": pack_ms, "unpack_ms": unpack_ms,
-            "pack_gbps": bytes_ / (pack_ms * 1e-3) / 1e9, "unpack_gbps": bytes_ / (unpack_ms * 1e-3) / 1e9}
+            "pack_gbps": gbps(bytes_, pack_ms), "unpack_gbps": gbps(bytes_, unpack_ms),
+            "widen_pack_ms": widen_ms, "recast_unpack_ms": recast_ms,
+            "widen_pack_gbps": gbps(6 * w.total, widen_ms), "recast_unpack_gbps": gbps(6 * w.total, recast_ms)}
 
 
 def run_zero1_flow(w, shapes, reps: int = 3):

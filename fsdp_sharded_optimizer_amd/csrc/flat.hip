@@ -4,10 +4,10 @@
 // travels in the kernel arguments, up to kFlatMaxTensors tensors per launch,
 // so nothing is allocated on the device.  Workgroups are laid out tensor
 // after tensor: workgroup w finds its tensor t with a uniform (scalar) scan
-// of the first-workgroup table, then copies one tile of that tensor, one
-// 128-bit (or 64-bit, for the bf16 side of a conversion) vector per lane in
-// one-wave workgroups: 512 elements for bf16 copies, 256 for fp32 copies and
-// conversions.  Every
+// of the first-workgroup table, then copies one tile of that tensor in
+// one-wave workgroups: one 128-bit vector per lane for bit copies (512 bf16
+// or 256 fp32 elements), two groups of 4 elements per lane for conversions
+// (512 elements; a 64-bit access on the bf16 side).  Every
 // workgroup works on a single tensor with uniform base addresses; only a
 // tensor's last tile is ragged.  A pack entry with a NULL tensor zero-fills
 // the padding [total, padded_total).  (One vector per lane measured 81 % of
@@ -25,7 +25,7 @@
 namespace zs {
 namespace {
 
-// element types, vector width and workgroup size per kind:
+// element types, vector width, groups per lane and workgroup size per kind:
 // 0 f32->f32, 1 bf16->bf16, 2 bf16->f32 (widen), 3 f32->bf16 (re-cast),
 // 4 f32 += f32, 5 bf16 = RNE(widen(bf16) + f32) (apply; S is the update).
 // Every kind runs one-wave workgroups; the bf16 apply takes 8 elements per
@@ -33,14 +33,21 @@ namespace {
 // 256-thread workgroups: the bf16 apply over the 291 Llama-7B tensors in
 // batches of 32 from 64 % to 82 % of the HBM peak, the fp32 apply 81 -> 83 %;
 // over the 70B block's 9 tensors the fp32 copy 81 -> 83.5 %, the bf16 copy
-// 81 -> 83 %, the widening pack 72 -> 78 %, the re-casting unpack 77 -> 79 %.
+// 81 -> 83 %.  The conversions (one 64-bit access on their bf16 side) take
+// Q = 2 groups of 4 elements per lane, a wave's width (256 elements) apart,
+// both loads issued before either store: the widening pack 74 -> 81 %, the
+// re-casting unpack 76 -> 81 % (Q = 4: 73 / 77 %; one group as 8 contiguous
+// elements, so two 128-bit fp32 stores 32 bytes apart per lane: 40 %;
+// residency capped by reserved LDS: 35-67 %).
 template <int KIND> struct Kind;
-template <> struct Kind<0> { using S = float; using D = float; static constexpr int VE = 4, BS = 64; };
-template <> struct Kind<1> { using S = uint16_t; using D = uint16_t; static constexpr int VE = 8, BS = 64; };
-template <> struct Kind<2> { using S = uint16_t; using D = float; static constexpr int VE = 4, BS = 64; };
-template <> struct Kind<3> { using S = float; using D = uint16_t; static constexpr int VE = 4, BS = 64; };
-template <> struct Kind<4> { using S = float; using D = float; static constexpr int VE = 4, BS = 64; };
-template <> struct Kind<5> { using S = float; using D = uint16_t; static constexpr int VE = 8, BS = 64; };
+template <> struct Kind<0> { using S = float; using D = float; static constexpr int VE = 4, Q = 1, BS = 64; };
+template <> struct Kind<1> { using S = uint16_t; using D = uint16_t; static constexpr int VE = 8, Q = 1, BS = 64; };
+template <> struct Kind<2> { using S = uint16_t; using D = float; static constexpr int VE = 4, Q = 2, BS = 64; };
+template <> struct Kind<3> { using S = float; using D = uint16_t; static constexpr int VE = 4, Q = 2, BS = 64; };
+template <> struct Kind<4> { using S = float; using D = float; static constexpr int VE = 4, Q = 1, BS = 64; };
+template <> struct Kind<5> { using S = float; using D = uint16_t; static constexpr int VE = 8, Q = 1, BS = 64; };
+template <int KIND> constexpr int64_t kGroupElems = (int64_t)Kind<KIND>::BS * Kind<KIND>::VE;
+template <int KIND> constexpr int64_t kTileElems = kGroupElems<KIND> * Kind<KIND>::Q;
 constexpr bool is_apply(int kind) { return kind >= 4; }
 
 template <int KIND>
@@ -94,12 +101,40 @@ __device__ __forceinline__ void copy_vec(const void* src, void* dst, bool zero) 
     }
 }
 
+// A conversion lane's Q vectors, `stride` elements apart: every load first,
+// then every store, so Q loads per lane are in flight together.
+template <int KIND>
+__device__ __forceinline__ void convert_vecs(const typename Kind<KIND>::S* src, typename Kind<KIND>::D* dst,
+                                             bool zero, int64_t stride) {
+    constexpr int Q = Kind<KIND>::Q;
+    if constexpr (KIND == 2) {
+        u32x2 w[Q];
+#pragma unroll
+        for (int g = 0; g < Q; ++g) w[g] = zero ? u32x2{0, 0} : ld_stream_u32x2_a4(src + g * stride);
+#pragma unroll
+        for (int g = 0; g < Q; ++g)
+            st_stream(reinterpret_cast<u32x4*>(dst + g * stride),
+                      u32x4{w[g].x << 16, w[g].x & 0xFFFF0000u, w[g].y << 16, w[g].y & 0xFFFF0000u});
+    } else {
+        static_assert(KIND == 3, "conversions only");
+        f32x4 f[Q];
+#pragma unroll
+        for (int g = 0; g < Q; ++g)
+            f[g] = zero ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : ld_stream_f32x4_a4(src + g * stride);
+#pragma unroll
+        for (int g = 0; g < Q; ++g)
+            st_stream(reinterpret_cast<u32x2*>(dst + g * stride),
+                      u32x2{pack_bf16x2(f[g].x, f[g].y), pack_bf16x2(f[g].z, f[g].w)});
+    }
+}
+
 template <int KIND, bool UNPACK>
 __global__ __launch_bounds__(Kind<KIND>::BS) void flat_kernel(const FlatBatch b) {
     using S = typename Kind<KIND>::S;
     using D = typename Kind<KIND>::D;
     constexpr int VE = Kind<KIND>::VE;
-    constexpr int64_t kTile = (int64_t)Kind<KIND>::BS * VE;
+    constexpr int Q = Kind<KIND>::Q;
+    constexpr int64_t kGroup = kGroupElems<KIND>;
     // the tensor this workgroup copies: the number of later tensors whose
     // first workgroup is <= w (the table is nondecreasing).  A fixed-length,
     // branch-free count (its second half only for batches of more than 16
@@ -124,7 +159,7 @@ __global__ __launch_bounds__(Kind<KIND>::BS) void flat_kernel(const FlatBatch b)
     }
     const FlatEntry e = b.e[t];
     const int64_t numel = e.numel;
-    const int64_t j = (int64_t)(w - first) * kTile + threadIdx.x * VE;
+    const int64_t j = (int64_t)(w - first) * kTileElems<KIND> + threadIdx.x * VE;   // the lane's first group
     if (j >= numel) return;
     const S* src;
     D* dst;
@@ -145,12 +180,24 @@ __global__ __launch_bounds__(Kind<KIND>::BS) void flat_kernel(const FlatBatch b)
         return;
     }
     const bool zero = src == nullptr;
-    if (e.vec_ok && j + VE <= numel) {
-        copy_vec<KIND>(zero ? nullptr : src + j, dst + j, zero);
-        return;
+    if constexpr (Q > 1) {
+        if (e.vec_ok && j + (Q - 1) * kGroup + VE <= numel) {   // all of the lane's groups whole
+            convert_vecs<KIND>(zero ? nullptr : src + j, dst + j, zero, kGroup);
+            return;
+        }
     }
-    const int64_t last = j + VE < numel ? j + VE : numel;
-    for (int64_t i = j; i < last; ++i) dst[i] = zero ? D(0) : convert1<KIND>(src[i]);
+    // one group at a time: the tensor's last tile (and unaligned tensors)
+#pragma unroll
+    for (int g = 0; g < Q; ++g) {
+        const int64_t jg = j + g * kGroup;
+        if (jg >= numel) return;
+        if (e.vec_ok && jg + VE <= numel) {
+            copy_vec<KIND>(zero ? nullptr : src + jg, dst + jg, zero);
+            continue;
+        }
+        const int64_t last = jg + VE < numel ? jg + VE : numel;
+        for (int64_t i = jg; i < last; ++i) dst[i] = zero ? D(0) : convert1<KIND>(src[i]);
+    }
 }
 
 template <int KIND, bool UNPACK>
@@ -165,12 +212,12 @@ hipError_t launch(const FlatBatch& b, hipStream_t stream) {
 
 int64_t flat_tile_elems(int kind) {
     switch (kind) {
-        case 0: return (int64_t)Kind<0>::BS * Kind<0>::VE;
-        case 1: return (int64_t)Kind<1>::BS * Kind<1>::VE;
-        case 2: return (int64_t)Kind<2>::BS * Kind<2>::VE;
-        case 3: return (int64_t)Kind<3>::BS * Kind<3>::VE;
-        case 4: return (int64_t)Kind<4>::BS * Kind<4>::VE;
-        default: return (int64_t)Kind<5>::BS * Kind<5>::VE;
+        case 0: return kTileElems<0>;
+        case 1: return kTileElems<1>;
+        case 2: return kTileElems<2>;
+        case 3: return kTileElems<3>;
+        case 4: return kTileElems<4>;
+        default: return kTileElems<5>;
     }
 }
 

@@ -44,10 +44,6 @@ def canary_ok(whole: torch.Tensor, offset: int, n: int) -> bool:
                 np.all(w.view(np.uint32)[:offset] == 0x7FBADBAD))
 
 
-def rng_for(*key):
-    return np.random.default_rng(abs(hash(key)) % (2**32))
-
-
 # ---------------------------------------------------------------------------
 # grad_accum: bit-exact
 # ---------------------------------------------------------------------------
@@ -605,6 +601,59 @@ def test_flat_dword_aligned_read_side(src_off):
     oracle.flat_apply_update(np.ascontiguousarray(upd_np[1:1 + T]), ps_np, oracle.F32)
     for a_, r in zip(ps, ps_np):
         assert bits_equal(to_np(a_), r)
+
+
+# sizes at and around the conversions' group (256 elements) and tile (512)
+# boundaries: a lane's second group ragged, absent, or whole
+CONVERSION_SIZES = [1, 3, 4, 5, 252, 255, 256, 257, 259, 260, 261, 508, 511, 512, 513, 516, 517, 767, 768,
+                    769, 1023, 1024, 1025, 1029, 100_003]
+
+
+def _fp32_with_specials(rng, n):
+    """Random fp32 values whose low 16 bits are arbitrary, with exact halfway
+    cases (both parities), values that round up to infinity, subnormals,
+    signed zeros, infinities and NaNs mixed in."""
+    x = rng.uniform(-2, 2, n).astype(np.float32)
+    u = x.view(np.uint32)
+    specials = np.array([0x3F808000, 0x3F818000, 0xBF808000, 0x7F7FFFFF, 0x7F7F8000, 0xFF7FFFFF,
+                         0x00000001, 0x80008000, 0x00000000, 0x80000000, 0x7F800000, 0xFF800000,
+                         0x7FC00001, 0xFFBFFFFF, 0x7F800001], dtype=np.uint32)
+    k = min(n, len(specials))
+    idx = rng.choice(n, size=k, replace=False)
+    u[idx] = specials[:k]
+    return u.view(np.float32)
+
+
+@pytest.mark.parametrize("n", CONVERSION_SIZES)
+@pytest.mark.parametrize("offset", [0, 1, 2])
+def test_flat_conversions_at_tile_edges(n, offset):
+    """The widening pack (bf16 -> fp32) and the re-casting unpack (fp32 ->
+    bf16, round to nearest even) over tensors whose sizes sit at the edges of
+    the conversion kernels' groups and tiles, at element offsets 0 (aligned),
+    1 (scalar path) and 2 (bf16 side 4-byte aligned): bit-exact against the
+    oracle, nothing written outside."""
+    print(f"flat conversions n={n} offset={offset}", flush=True)
+    rng = np.random.default_rng(n * 3 + offset)
+    sizes = [n, n + 1, 7]
+    T = sum(sizes)
+    padded = T + 5
+    # pack: bf16 tensors at `offset` into an fp32 flat buffer (poisoned, so
+    # the zero padding must be written)
+    srcs_np = [oracle.bf16_rne(rng.uniform(-1, 1, k).astype(np.float32)) for k in sizes]
+    srcs = [dev_buf(x, offset, bf16=True)[0] for x in srcs_np]
+    flat, flat_whole = dev_buf(np.full(padded, np.nan, np.float32), offset)
+    zs.flat_pack(srcs, flat, padded)
+    assert bits_equal(to_np(flat), oracle.flat_pack(srcs_np, oracle.BF16, oracle.F32, padded))
+    assert canary_ok(flat_whole, offset, padded)
+    # unpack: an fp32 flat buffer of arbitrary values into bf16 tensors at `offset`
+    flat_np = _fp32_with_specials(rng, T)
+    fv, _ = dev_buf(flat_np, offset)
+    outs, wholes = zip(*[dev_buf(np.zeros(k, np.uint16), offset, bf16=True) for k in sizes])
+    zs.flat_unpack(fv, list(outs))
+    back = oracle.flat_unpack(flat_np, oracle.F32, sizes, oracle.BF16)
+    for o, w_, r, k in zip(outs, wholes, back, sizes):
+        assert bits_equal(to_np(o), r)
+        assert canary_ok(w_, offset, k)
 
 
 # ---------------------------------------------------------------------------
