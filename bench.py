@@ -79,6 +79,17 @@ def step_bytes_per_elem(w) -> dict:
             "grad_accum_norm_sq_last": last, "adamw_step": adamw, "step": accum + adamw}
 
 
+def ceiling_report(ms_by_lds: dict, nbytes: int, adamw_ms: float) -> dict:
+    """The AdamW-traffic kernel's time at each residency cap, its best, and
+    the AdamW step's bandwidth as a fraction of that best."""
+    best = min(ms_by_lds, key=ms_by_lds.get)
+    gbps = nbytes / (ms_by_lds[best] * 1e-3) / 1e9
+    return {"kernel": "zsc_adamw_traffic", "algorithmic_bytes": nbytes,
+            "ms_by_lds_bytes": {str(k): v for k, v in ms_by_lds.items()},
+            "best_lds_bytes": best, "gbps": gbps, "frac": gbps / HBM_PEAK_GBPS,
+            "adamw_step_of_ceiling": ms_by_lds[best] / adamw_ms}
+
+
 def shard_len(w) -> int:
     import fsdp_sharded_optimizer_amd as zs
     _, start, end, _ = zs.zero_shard_range(w.total, w.world, w.rank)
@@ -202,6 +213,13 @@ def run_gpu(w, steps: int, warmup: int):
         torch.cuda.synchronize()
         no_master_ms = n0.elapsed_time(n1) / 3
 
+    # achievable-bandwidth reference for the AdamW step's own traffic: the
+    # same bytes per element and accesses, one addition per stream in place
+    # of the update, at several residency caps (run last on these buffers:
+    # it changes them)
+    ceiling = {lds: _time_adamw_traffic(master, exp_avg, exp_avg_sq, acc, param, n, lds)
+               for lds in CEILING_LDS}
+
     # achievable-bandwidth reference: a plain device copy of 4 GiB (also the
     # calibration kernel for the HBM byte counters)
     src = torch.empty(1 << 30, dtype=torch.float32, device=dev)
@@ -219,7 +237,41 @@ def run_gpu(w, steps: int, warmup: int):
     del src, dst
     return {"n": n, "wall_s": wall, "accum_ms": acc_ms, "last_ms": last_ms, "adamw_ms": adamw_ms, "graph_ms": graph_ms,
             "reduce_ms": reduce_ms, "chunks": len(grads), "no_master_ms": no_master_ms,
-            "copy_gbps": copy_gbps}
+            "copy_gbps": copy_gbps, "ceiling_ms": ceiling}
+
+
+CEILING_LDS = (0, 8192, 12288, 16384, 20480)   # LDS reserved per one-wave workgroup
+
+
+def _time_adamw_traffic(master, exp_avg, exp_avg_sq, grad, bf16, n: int, lds: int, reps: int = 5) -> float:
+    """Average launch time of the AdamW-traffic ceiling kernel
+    (libzsceiling.so, built next to libzshard.so), each launch bracketed by
+    HIP events on the stream it runs on."""
+    import ctypes
+    import torch
+    from fsdp_sharded_optimizer_amd import build as zbuild
+
+    if not os.path.exists(zbuild.CEILING_LIB):
+        raise RuntimeError(f"{zbuild.CEILING_LIB} is not built: run python -m fsdp_sharded_optimizer_amd.build")
+    lib = ctypes.CDLL(zbuild.CEILING_LIB)
+    f = lib.zsc_adamw_traffic
+    f.restype = ctypes.c_int32
+    f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]
+    stream = torch.cuda.current_stream()
+    args = [master.data_ptr(), exp_avg.data_ptr(), exp_avg_sq.data_ptr(), grad.data_ptr(),
+            bf16.data_ptr() if bf16 is not None else None, n, lds, stream.cuda_stream]
+    events = []
+    for k in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        rc = f(*args)
+        e1.record(stream)
+        if rc != 0:
+            raise RuntimeError(f"zsc_adamw_traffic returned {rc}")
+        if k:
+            events.append((e0, e1))
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in events) / reps
 
 
 def run_flat(w, reps: int = 10):
@@ -465,6 +517,7 @@ def main():
                        "adamw_step": r["adamw_ms"]},
         "bytes_per_elem": bpe,
         "device_copy_gbps": r["copy_gbps"],
+        "adamw_traffic_ceiling": ceiling_report(r["ceiling_ms"], adamw_bytes, r["adamw_ms"]),
         "roofline": {"kernel": "adamw_step", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": pmc_traffic("adamw_step", n), "traffic_unit": "bytes/launch",

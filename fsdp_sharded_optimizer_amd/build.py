@@ -1,4 +1,6 @@
-"""Build libzshard.so in-tree with hipcc for gfx950.
+"""Build libzshard.so (the library) and libzsceiling.so (the benchmark's
+bandwidth-ceiling kernel, not part of the library's interface) in-tree with
+hipcc for gfx950.
 
     python -m fsdp_sharded_optimizer_amd.build
 
@@ -19,6 +21,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libzshard.so")
+CEILING_LIB = os.path.join(HERE, "libzsceiling.so")
 ARCH = "gfx950"
 
 FLAGS = [
@@ -29,14 +32,19 @@ FLAGS = [
 ]
 
 
-def sources():
-    return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
+def sources(sub: str = "csrc"):
+    return sorted(glob.glob(os.path.join(HERE, sub, "*.hip")))
 
 
 def build(verbose: bool = False) -> str:
+    _compile(CEILING_LIB, sources("ceiling"), verbose)
+    return _compile(LIB, sources(), verbose)
+
+
+def _compile(lib: str, srcs, verbose: bool) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, *sources()]
+    tmp = lib + ".tmp"
+    cmd = [hipcc, *FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)
@@ -47,8 +55,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -343,3 +343,26 @@ def test_element_count_limit():
     assert L.flat_unpack(a, B.ZS_F32, _tensors((g, big)), 1, B.ZS_F32, None) == B.ZS_EINVAL
     half = (1 << 38) + 1   # each tensor allowed, their sum not
     assert L.flat_unpack(a, B.ZS_F32, _tensors((g, half), (g + step, half)), 2, B.ZS_F32, None) == B.ZS_EINVAL
+
+
+def test_ceiling_library_rejects_before_launch():
+    """The benchmark's bandwidth-ceiling kernel (libzsceiling.so) exports one
+    symbol and rejects bad arguments, or returns for n == 0, without a
+    launch (a launch attempt here would return a HIP error, not -1 or 0)."""
+    from fsdp_sharded_optimizer_amd import build as zbuild
+    if not os.path.exists(zbuild.CEILING_LIB):
+        pytest.skip("libzsceiling.so not built")
+    L = ctypes.CDLL(zbuild.CEILING_LIB)
+    f = L.zsc_adamw_traffic
+    f.restype = ctypes.c_int32
+    f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]
+    a = 1 << 20   # 16-byte aligned, never dereferenced: every call below fails validation or is a no-op
+    assert f(a, a + 64, a + 128, a + 192, None, 0, 0, None) == 0           # empty: nothing to do
+    assert f(a, a + 64, a + 128, a + 192, None, -1, 0, None) == -1         # negative n
+    assert f(a, a + 64, a + 128, a + 192, None, (1 << 39) + 1, 0, None) == -1
+    assert f(None, a + 64, a + 128, a + 192, None, 16, 0, None) == -1      # null buffer
+    assert f(a + 4, a + 64, a + 128, a + 192, None, 16, 0, None) == -1     # written buffer off 16 bytes
+    assert f(a, a + 64, a + 128, a + 194, None, 16, 0, None) == -1         # grad off 4 bytes
+    assert f(a, a + 64, a + 128, a + 192, a + 258, 16, 0, None) == -1      # bf16 output off 16 bytes
+    assert f(a, a + 64, a + 128, a + 192, None, 16, -1, None) == -1        # LDS reservation out of range
+    assert f(a, a + 64, a + 128, a + 192, None, 16, 65537, None) == -1
