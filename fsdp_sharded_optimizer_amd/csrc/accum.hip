@@ -112,14 +112,25 @@ constexpr int kFusedQAdd = 1;
 constexpr int kFusedQOverwrite = 4;
 constexpr unsigned kFusedOverwriteLds = 12288;
 
+static_assert(kLaunchElems % per_block<kFusedQOverwrite>() == 0, "pieces keep the partials' positions");
+
+// one launch per kLaunchElems elements; piece k's partials follow piece
+// k-1's, so the partials (and the norm) are those of a single launch
 template <int Q, bool VEC, bool BF16, bool OVERWRITE, bool NORM>
 hipError_t launch(float* acc, const void* grad, int64_t n, float scale, double* partials, unsigned lds,
                   hipStream_t stream) {
-    const int64_t blocks = (n + per_block<Q>() - 1) / per_block<Q>();
-    if (blocks > (int64_t)UINT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((accum_kernel<Q, kAccumBlock, VEC, BF16, OVERWRITE, NORM>), dim3((unsigned)blocks),
-                       dim3(kAccumBlock), lds, stream, acc, grad, n, scale, partials);
-    return hipGetLastError();
+    const int64_t gsz = BF16 ? 2 : 4;
+    for (int64_t off = 0; off < n; off += kLaunchElems) {
+        const int64_t m = launch_piece(n, off);
+        const int64_t blocks = (m + per_block<Q>() - 1) / per_block<Q>();
+        hipLaunchKernelGGL((accum_kernel<Q, kAccumBlock, VEC, BF16, OVERWRITE, NORM>), dim3((unsigned)blocks),
+                           dim3(kAccumBlock), lds, stream, acc + off,
+                           static_cast<const char*>(grad) + off * gsz, m, scale,
+                           NORM ? partials + off / per_block<Q>() : nullptr);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <int Q, bool NORM, bool OVERWRITE>
@@ -270,15 +281,23 @@ __global__ __launch_bounds__(kReduceBlock) void reduce_chunks_kernel(float* __re
     }
 }
 
+// one launch per kLaunchElems elements, the chunk pointers advanced with acc
 template <bool VEC, bool BF16, bool OVERWRITE>
 hipError_t launch_reduce(float* acc, const ChunkBatch& b, int64_t n, hipStream_t stream) {
     const int64_t per = (int64_t)kReduceBlock * 4 * kReduceGroups;
-    const int64_t blocks = (n + per - 1) / per;
-    if (blocks > (int64_t)UINT32_MAX) return hipErrorInvalidValue;
+    const int64_t gsz = BF16 ? 2 : 4;
     const unsigned lds = VEC ? reduce_lds_reserve(BF16, b.count) : 0u;
-    hipLaunchKernelGGL((reduce_chunks_kernel<VEC, BF16, OVERWRITE>), dim3((unsigned)blocks), dim3(kReduceBlock), lds,
-                       stream, acc, b, n);
-    return hipGetLastError();
+    for (int64_t off = 0; off < n; off += kLaunchElems) {
+        const int64_t m = launch_piece(n, off);
+        ChunkBatch p = b;
+        for (int k = 0; k < b.count; ++k) p.chunk[k] = static_cast<const char*>(b.chunk[k]) + off * gsz;
+        const int64_t blocks = (m + per - 1) / per;
+        hipLaunchKernelGGL((reduce_chunks_kernel<VEC, BF16, OVERWRITE>), dim3((unsigned)blocks), dim3(kReduceBlock),
+                           lds, stream, acc + off, p, m);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace

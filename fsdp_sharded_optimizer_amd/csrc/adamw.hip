@@ -164,13 +164,27 @@ __global__ __launch_bounds__(BS) void adamw_kernel(const AdamwArgs a) {
     }
 }
 
+template <typename T>
+T* advance(T* p, int64_t off) { return p == nullptr ? nullptr : p + off; }
+
+// one launch per kLaunchElems elements, each on its own slice of the buffers
 template <int VEC, int FORM, int BS, bool DEV>
 hipError_t launch(const AdamwArgs& a, unsigned lds, hipStream_t stream) {
-    const int64_t threads = (a.n + VEC - 1) / VEC;
-    const int64_t blocks = (threads + BS - 1) / BS;
-    if (blocks > (int64_t)UINT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((adamw_kernel<VEC, FORM, BS, DEV>), dim3((unsigned)blocks), dim3(BS), lds, stream, a);
-    return hipGetLastError();
+    for (int64_t off = 0; off < a.n; off += kLaunchElems) {
+        AdamwArgs p = a;
+        p.n = launch_piece(a.n, off);
+        p.master = advance(a.master, off);
+        p.exp_avg = advance(a.exp_avg, off);
+        p.exp_avg_sq = advance(a.exp_avg_sq, off);
+        p.grad = advance(a.grad, off);
+        p.param_bf16 = advance(a.param_bf16, off);
+        p.update = advance(a.update, off);
+        const int64_t blocks = ((p.n + VEC - 1) / VEC + BS - 1) / BS;
+        hipLaunchKernelGGL((adamw_kernel<VEC, FORM, BS, DEV>), dim3((unsigned)blocks), dim3(BS), lds, stream, p);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <int FORM, bool DEV = false>

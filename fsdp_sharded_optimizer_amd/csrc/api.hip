@@ -38,8 +38,9 @@ inline bool dtype_ok(int32_t d) { return d == ZS_F32 || d == ZS_BF16; }
 inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 // At most 2^39 elements per call (2 TiB of fp32, beyond any one GPU's
-// memory): byte sizes stay far inside int64, and every launch grid (tiles of
-// 256 elements or more) fits the 32-bit grid dimension.
+// memory): byte sizes stay far inside int64.  The launchers split a call
+// into launches of at most 2^30 elements, so every grid stays below 2^32
+// work-items.
 constexpr int64_t kMaxElems = int64_t(1) << 39;
 inline bool size_ok(int64_t n) { return n >= 0 && n <= kMaxElems; }
 
@@ -388,9 +389,14 @@ static int32_t flat_common(const zs_tensor* tensors, int32_t count, void* flat, 
                     return ZS_EOVERLAP;
     }
 
-    // batches of up to kFlatMaxTensors entries; the pack padding is one
-    // more entry with a NULL tensor
+    // batches of up to kFlatMaxTensors entries and fewer than 2^32
+    // work-items; a tensor longer than kLaunchElems takes one entry per
+    // kLaunchElems elements (a multiple of every tile: each piece keeps the
+    // tensor's alignment); the pack padding is one more entry with a NULL
+    // tensor
     const int64_t tile = zs::flat_tile_elems(kind);
+    const int64_t max_tiles = zs::flat_max_batch_tiles(kind);
+    const int64_t tsz_bytes = tsz;
     zs::FlatBatch b;
     std::memset(&b, 0, sizeof(b));
     b.flat = flat;
@@ -402,13 +408,12 @@ static int32_t flat_common(const zs_tensor* tensors, int32_t count, void* flat, 
         b.flat = flat;
         return rc;
     };
-    auto add = [&](void* ptr, int64_t flat_off, int64_t numel) -> int32_t {
-        const int64_t tiles = (numel + tile - 1) / tile;
-        if (b.count == zs::kFlatMaxTensors || (int64_t)b.tile_start[b.count] + tiles > (int64_t)UINT32_MAX) {
+    auto add_piece = [&](void* ptr, int64_t flat_off, int64_t numel) -> int32_t {
+        const int64_t tiles = (numel + tile - 1) / tile;   // numel <= kLaunchElems: tiles << max_tiles
+        if (b.count == zs::kFlatMaxTensors || (int64_t)b.tile_start[b.count] + tiles > max_tiles) {
             const int32_t rc = flush();
             if (rc != ZS_OK) return rc;
         }
-        if (tiles > (int64_t)UINT32_MAX) return ZS_EINVAL;   // one tensor beyond a launch's grid
         const int c = b.count;
         b.e[c].tensor = ptr;
         b.e[c].flat_off = flat_off;
@@ -420,6 +425,14 @@ static int32_t flat_common(const zs_tensor* tensors, int32_t count, void* flat, 
         b.e[c].vec_ok = aligned(written, 16) && (read == nullptr || aligned(read, 4));
         b.tile_start[c + 1] = b.tile_start[c] + (uint32_t)tiles;
         b.count = c + 1;
+        return ZS_OK;
+    };
+    auto add = [&](void* ptr, int64_t flat_off, int64_t numel) -> int32_t {
+        for (int64_t off = 0; off < numel; off += zs::kLaunchElems) {
+            void* piece = ptr == nullptr ? nullptr : static_cast<char*>(ptr) + off * tsz_bytes;
+            const int32_t rc = add_piece(piece, flat_off + off, zs::launch_piece(numel, off));
+            if (rc != ZS_OK) return rc;
+        }
         return ZS_OK;
     };
     for (int32_t i = 0; i < count; ++i) {

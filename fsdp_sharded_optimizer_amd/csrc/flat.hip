@@ -221,6 +221,13 @@ int64_t flat_tile_elems(int kind) {
     }
 }
 
+int64_t flat_max_batch_tiles(int kind) {
+    static_assert(Kind<0>::BS == 64 && Kind<1>::BS == 64 && Kind<2>::BS == 64 && Kind<3>::BS == 64 &&
+                  Kind<4>::BS == 64 && Kind<5>::BS == 64, "one workgroup size for every kind");
+    (void)kind;
+    return (int64_t)UINT32_MAX / 64;
+}
+
 hipError_t launch_flat(const FlatBatch& b, int kind, int unpack, hipStream_t stream) {
     if (unpack) {
         switch (kind) {

@@ -89,7 +89,16 @@ struct AdamwArgs {
     int64_t n;
 };
 
-// Launchers: enqueue on `stream`, return the hipError_t of the launch.
+// One launch covers at most kLaunchElems elements.  A HIP launch must keep
+// gridDim.x * blockDim.x below 2^32 work-items, and the scalar AdamW path
+// runs one element per work-item, so a longer call is split into launches
+// at multiples of kLaunchElems: a multiple of every tile, workgroup partial
+// and vector width, so the pieces keep the tiles, partial indices (results
+// bit-identical to one launch) and 16-byte alignment of a single launch.
+constexpr int64_t kLaunchElems = int64_t(1) << 30;
+inline int64_t launch_piece(int64_t n, int64_t off) { return n - off < kLaunchElems ? n - off : kLaunchElems; }
+
+// Launchers: enqueue on `stream`, return the hipError_t of the (first failed) launch.
 hipError_t launch_adamw(const AdamwArgs& a, bool vec_ok, hipStream_t stream);
 hipError_t launch_adamw_no_master(const AdamwArgs& a, bool vec_ok, hipStream_t stream);
 hipError_t launch_adam_update(const AdamwArgs& a, bool vec_ok, hipStream_t stream);
@@ -134,6 +143,7 @@ struct FlatBatch {
 // kind: 0 = f32->f32, 1 = bf16->bf16, 2 = bf16->f32 (pack widen), 3 = f32->bf16 (unpack RNE),
 // 4 = f32 tensor += f32 flat, 5 = bf16 tensor = RNE(widen(tensor) + f32 flat) (apply, unpack side)
 hipError_t launch_flat(const FlatBatch& b, int kind, int unpack, hipStream_t stream);
-int64_t flat_tile_elems(int kind);   // elements per workgroup
+int64_t flat_tile_elems(int kind);        // elements per workgroup
+int64_t flat_max_batch_tiles(int kind);   // workgroups one launch may hold (< 2^32 work-items)
 
 }  // namespace zs

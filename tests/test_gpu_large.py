@@ -1,0 +1,280 @@
+"""GPU parity for calls longer than one launch.
+
+A HIP launch must stay below 2^32 work-items, so the library runs a call of
+more than 2^30 elements as several launches over consecutive pieces of the
+buffers (and several table entries per tensor for the flat copies).  Every
+case here crosses at least one piece boundary, aligned (vector path) and as
+a view one element off (scalar path), and the last one runs the scalar
+AdamW path past 2^32 elements.  Inputs are drawn on the GPU with seeded
+generators and copied to the host for the oracle.  The steps are
+element-wise, so the oracle runs the sampled elements alone (both sides of
+every piece boundary, the head, the tail and random elements) and carries
+its own state from step to step; the norm it forms over the whole buffer.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import fsdp_sharded_optimizer_amd as zs
+from tests.parity import NORM_TOL, bits_equal, identical_fraction, to_np
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+DEV = "cuda"
+PIECE = 1 << 30            # elements per launch
+N = PIECE + 4099           # one piece boundary, a ragged last piece
+FILL = 1 << 27             # elements per generator call when filling
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return to_np(t)
+
+
+def sample_indices(n: int, seed: int, k: int = 1 << 16) -> torch.Tensor:
+    rng = np.random.default_rng(seed)
+    parts = [np.arange(min(n, 2048)), np.arange(max(0, n - 2048), n), rng.integers(0, n, size=k)]
+    for b in range(PIECE, n, PIECE):
+        parts.append(np.arange(b - 2048, min(n, b + 2048)))
+    return torch.from_numpy(np.unique(np.concatenate(parts)).astype(np.int64)).to(DEV)
+
+
+def gen(seed: int) -> torch.Generator:
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    return g
+
+
+def buffer(n: int, offset: int, dtype=torch.float32):
+    """A length-n view `offset` elements into a fresh allocation."""
+    whole = torch.empty(n + offset + 8, dtype=dtype, device=DEV)
+    return whole[offset:offset + n]
+
+
+def fill_normal(t: torch.Tensor, std: float, seed: int) -> torch.Tensor:
+    g = gen(seed)
+    for a in range(0, t.numel(), FILL):
+        t[a:a + FILL].normal_(0.0, std, generator=g)
+    return t
+
+
+def fill_uniform(t: torch.Tensor, lo: float, hi: float, seed: int) -> torch.Tensor:
+    g = gen(seed)
+    for a in range(0, t.numel(), FILL):
+        t[a:a + FILL].uniform_(lo, hi, generator=g)
+    return t
+
+
+def bf16_normal(n: int, offset: int, std: float, seed: int) -> torch.Tensor:
+    out = buffer(n, offset, torch.bfloat16)
+    tmp = torch.empty(min(n, FILL), dtype=torch.float32, device=DEV)
+    g = gen(seed)
+    for a in range(0, n, FILL):
+        b = min(n, a + FILL)
+        tmp[:b - a].normal_(0.0, std, generator=g)
+        out[a:b].copy_(tmp[:b - a])   # round to nearest even
+    return out
+
+
+def release():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def check(name, gpu: torch.Tensor, idx: torch.Tensor, ref: np.ndarray):
+    got = host(gpu[idx])
+    assert bits_equal(got, ref), (name, identical_fraction(got, ref))
+
+
+@pytest.mark.parametrize("offset", [0, 1])
+def test_adamw_forms_across_pieces(offset):
+    """adamw_step (clipped, bf16 re-cast), then adamw_step_no_master and
+    adam_update on the same state, over N elements: bit-exact on the
+    sample."""
+    log(f"adamw forms across pieces n={N} offset={offset}")
+    idx = sample_indices(N, seed=11 + offset)
+    master = fill_uniform(buffer(N, offset), -0.1, 0.1, 101)
+    m = fill_normal(buffer(N, offset), 1e-4, 102)
+    v = fill_uniform(buffer(N, offset), 0.0, 1e-8, 103)
+    grad = fill_normal(buffer(N, offset), 1e-3, 104)
+    bf16 = buffer(N, offset, torch.bfloat16)
+    scale, extra, max_norm = 1.0 / 64, 2.0, 1.0
+    S = oracle.grad_norm_sq(host(grad), scale)   # the oracle's norm over the whole buffer feeds both sides
+    gpu_norm = torch.zeros(1, dtype=torch.float64, device=DEV)
+    zs.grad_norm_sq(grad, scale, gpu_norm)
+    assert abs(math.sqrt(gpu_norm.item()) - math.sqrt(S)) <= NORM_TOL * math.sqrt(S)
+    assert oracle.clip_coef(S, extra, max_norm) < 1.0
+    norm = torch.tensor([S], dtype=torch.float64, device=DEV)
+    p_ref, m_ref, v_ref, g_s = host(master[idx]), host(m[idx]), host(v[idx]), host(grad[idx])
+    b_ref = np.empty(idx.numel(), np.uint16)
+
+    log("  adamw_step")
+    hp = zs.AdamWConfig(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, grad_scale=scale,
+                        max_norm=max_norm, extra_norm_sq=extra, step=3)
+    zs.adamw_step(hp, master, m, v, grad, bf16, norm_sq=norm)
+    H = oracle.make_hp(3e-4, 0.9, 0.95, 1e-8, 0.1, scale, max_norm, extra, 3)
+    assert oracle.adamw_step(H, p_ref, m_ref, v_ref, g_s, b_ref, norm_sq=S) == 0
+    for name, gpu, ref in (("master", master, p_ref), ("m", m, m_ref), ("v", v, v_ref), ("bf16", bf16, b_ref)):
+        check(name, gpu, idx, ref)
+
+    log("  adamw_step_no_master")
+    hp.step = 4
+    zs.adamw_step_no_master(hp, bf16, m, v, grad, norm_sq=norm)
+    H = oracle.make_hp(3e-4, 0.9, 0.95, 1e-8, 0.1, scale, max_norm, extra, 4)
+    assert oracle.adamw_step_no_master(H, b_ref, m_ref, v_ref, g_s, norm_sq=S) == 0
+    for name, gpu, ref in (("bf16", bf16, b_ref), ("m", m, m_ref), ("v", v, v_ref)):
+        check(name, gpu, idx, ref)
+
+    log("  adam_update")
+    hu = zs.AdamWConfig(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.0, grad_scale=scale,
+                        max_norm=max_norm, extra_norm_sq=extra, step=5)
+    zs.adam_update(hu, m, v, grad, master, norm_sq=norm)   # the update into the master's buffer
+    H = oracle.make_hp(3e-4, 0.9, 0.95, 1e-8, 0.0, scale, max_norm, extra, 5)
+    u_ref = np.empty(idx.numel(), np.float32)
+    assert oracle.adam_update(H, m_ref, v_ref, g_s, u_ref, norm_sq=S) == 0
+    for name, gpu, ref in (("update", master, u_ref), ("m", m, m_ref), ("v", v, v_ref)):
+        check(name, gpu, idx, ref)
+    del master, m, v, grad, bf16
+    release()
+
+
+@pytest.mark.parametrize("offset", [0, 1])
+def test_accumulations_across_pieces(offset):
+    """grad_accum (overwrite, add) and grad_accum_norm_sq (the accumulating
+    Q = 1 form; the overwriting bf16 Q = 4 form; the overwriting fp32 form)
+    over N elements: acc bit-exact on the sample, the norm within the bar of
+    the oracle's over the whole buffer."""
+    log(f"accumulations across pieces n={N} offset={offset}")
+    idx = sample_indices(N, seed=21 + offset)
+    scale = 1.0 / 32
+    acc = buffer(N, offset)
+    gs = [bf16_normal(N, offset, 1e-3, 201 + k) for k in range(3)]
+    ws = torch.empty(zs.grad_accum_norm_sq_workspace_bytes(N), dtype=torch.uint8, device=DEV)
+    norm = torch.zeros(1, dtype=torch.float64, device=DEV)
+
+    log("  overwrite, add, add + norm")
+    zs.grad_accum(acc, gs[0], overwrite=True)
+    zs.grad_accum(acc, gs[1], overwrite=False)
+    zs.grad_accum_norm_sq(acc, gs[2], False, scale, norm, ws)
+    full = np.empty(N, np.float32)
+    for k, g in enumerate(gs):
+        oracle.grad_accum(full, host(g), oracle.BF16, overwrite=(k == 0))
+    S = oracle.grad_norm_sq(full, scale)
+    assert abs(math.sqrt(norm.item()) - math.sqrt(S)) <= NORM_TOL * math.sqrt(S)
+    check("acc", acc, idx, full[host(idx)])
+
+    log("  overwrite + norm (bf16)")
+    zs.grad_accum_norm_sq(acc, gs[1], True, scale, norm, ws)
+    ref = oracle.bf16_widen(host(gs[1]))
+    S = oracle.grad_norm_sq(ref, scale)
+    assert abs(math.sqrt(norm.item()) - math.sqrt(S)) <= NORM_TOL * math.sqrt(S)
+    check("acc", acc, idx, ref[host(idx)])
+    del gs, ref, full
+
+    log("  overwrite + norm (fp32)")
+    g32 = fill_normal(buffer(N, offset), 1e-3, 210)
+    zs.grad_accum_norm_sq(acc, g32, True, scale, norm, ws)
+    ref = host(g32)
+    S = oracle.grad_norm_sq(ref, scale)
+    assert abs(math.sqrt(norm.item()) - math.sqrt(S)) <= NORM_TOL * math.sqrt(S)
+    check("acc", acc, idx, ref[host(idx)])
+    del acc, g32, ws
+    release()
+
+
+@pytest.mark.parametrize("offset", [0, 1])
+def test_reduce_chunks_across_pieces(offset):
+    """Three bf16 rank chunks (the third the first again) summed into acc
+    over N elements, overwriting: bit-exact on the sample."""
+    log(f"grad_reduce_chunks across pieces n={N} offset={offset}")
+    idx = sample_indices(N, seed=31 + offset)
+    acc = buffer(N, offset)
+    c0 = bf16_normal(N, offset, 1e-3, 301)
+    c1 = bf16_normal(N, 1 - offset, 1e-3, 302)
+    zs.grad_reduce_chunks(acc, [c0, c1, c0], True)
+    ref = np.empty(idx.numel(), np.float32)
+    s0, s1 = host(c0[idx]), host(c1[idx])
+    for k, c in enumerate((s0, s1, s0)):
+        oracle.grad_accum(ref, c, oracle.BF16, overwrite=(k == 0))
+    check("acc", acc, idx, ref)
+    del acc, c0, c1
+    release()
+
+
+@pytest.mark.parametrize("offset", [0, 1])
+def test_flat_across_pieces(offset):
+    """flat_pack (bf16 copy with padding; bf16 -> fp32 widening),
+    flat_unpack (fp32 -> bf16 re-cast) and flat_apply_update (bf16
+    tensors) with a tensor of N elements between two small ones: bit-exact
+    on the sample, the padding zero."""
+    log(f"flat across pieces n={N} offset={offset}")
+    sizes = [5, N, 7]
+    T = sum(sizes)
+    padded = T + 3
+    idx = sample_indices(N, seed=41 + offset)
+    ts = [bf16_normal(k, offset, 0.1, 401 + i) for i, k in enumerate(sizes)]
+    fidx = idx + sizes[0]   # the big tensor's elements in the flat buffer
+
+    log("  pack, bf16 copy")
+    flat = buffer(padded, offset, torch.bfloat16)
+    flat[-3:].fill_(1.0)
+    zs.flat_pack(ts, flat, padded)
+    check("pack", flat, fidx, host(ts[1][idx]))
+    assert bits_equal(host(flat[:5]), host(ts[0])) and bits_equal(host(flat[T - 7:T]), host(ts[2]))
+    assert not host(flat[T:]).any()
+    del flat
+
+    log("  pack, widening")
+    flat32 = buffer(padded, offset)
+    flat32[-3:].fill_(float("nan"))
+    zs.flat_pack(ts, flat32, padded)
+    check("widen", flat32, fidx, oracle.bf16_widen(host(ts[1][idx])))
+    assert not host(flat32[T:]).view(np.uint32).any()
+
+    log("  unpack, re-cast")
+    fill_normal(flat32, 1.0, 402)
+    outs = [buffer(k, 1 - offset, torch.bfloat16) for k in sizes]
+    zs.flat_unpack(flat32[:T], outs)
+    check("recast", outs[1], idx, oracle.bf16_rne(host(flat32[fidx])))
+    assert bits_equal(host(outs[2]), oracle.bf16_rne(host(flat32[T - 7:T])))
+
+    log("  apply, bf16 tensors")
+    fill_normal(flat32, 1e-2, 403)
+    before = host(ts[1][idx])
+    upd = host(flat32[fidx])
+    zs.flat_apply_update(flat32[:T], ts)
+    ref = [before]
+    oracle.flat_apply_update(upd, ref, oracle.BF16)
+    check("apply", ts[1], idx, ref[0])
+    del ts, flat32, outs
+    release()
+
+
+def test_adamw_scalar_path_past_2_to_32():
+    """The scalar AdamW path (a view one element off: 256-thread workgroups,
+    one element per work-item) over 2^32 + 5 elements, four piece boundaries
+    and a ragged tail: bit-exact on the sample (about 77 GB of buffers)."""
+    n = (1 << 32) + 5
+    log(f"adamw scalar path n={n} offset=1")
+    idx = sample_indices(n, seed=51)
+    master = fill_uniform(buffer(n, 1), -0.1, 0.1, 501)
+    m = torch.zeros(n + 9, device=DEV)[1:n + 1]
+    v = torch.zeros(n + 9, device=DEV)[1:n + 1]
+    grad = fill_normal(buffer(n, 1), 1e-3, 502)
+    bf16 = buffer(n, 1, torch.bfloat16)
+    p_ref, g_s = host(master[idx]), host(grad[idx])
+    m_ref, v_ref = np.zeros(idx.numel(), np.float32), np.zeros(idx.numel(), np.float32)
+    b_ref = np.empty(idx.numel(), np.uint16)
+    hp = zs.AdamWConfig(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, grad_scale=1.0 / 64, step=1)
+    zs.adamw_step(hp, master, m, v, grad, bf16)
+    H = oracle.make_hp(3e-4, 0.9, 0.95, 1e-8, 0.1, 1.0 / 64, 0.0, 0.0, 1)
+    assert oracle.adamw_step(H, p_ref, m_ref, v_ref, g_s, b_ref) == 0
+    for name, gpu, ref in (("master", master, p_ref), ("m", m, m_ref), ("v", v, v_ref), ("bf16", bf16, b_ref)):
+        check(name, gpu, idx, ref)
+    del master, m, v, grad, bf16
+    release()
