@@ -39,7 +39,7 @@ inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 // At most 2^39 elements per call (2 TiB of fp32, beyond any one GPU's
 // memory): byte sizes stay far inside int64.  The launchers split a call
-// into launches of at most 2^30 elements, so every grid stays below 2^32
+// into launches of at most 2^31 elements, so every grid stays below 2^32
 // work-items.
 constexpr int64_t kMaxElems = int64_t(1) << 39;
 inline bool size_ok(int64_t n) { return n >= 0 && n <= kMaxElems; }

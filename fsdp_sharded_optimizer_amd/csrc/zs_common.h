@@ -91,11 +91,12 @@ struct AdamwArgs {
 
 // One launch covers at most kLaunchElems elements.  A HIP launch must keep
 // gridDim.x * blockDim.x below 2^32 work-items, and the scalar AdamW path
-// runs one element per work-item, so a longer call is split into launches
+// runs one element per work-item (2^31 of them at most, then), so a longer
+// call is split into launches
 // at multiples of kLaunchElems: a multiple of every tile, workgroup partial
 // and vector width, so the pieces keep the tiles, partial indices (results
 // bit-identical to one launch) and 16-byte alignment of a single launch.
-constexpr int64_t kLaunchElems = int64_t(1) << 30;
+constexpr int64_t kLaunchElems = int64_t(1) << 31;
 inline int64_t launch_piece(int64_t n, int64_t off) { return n - off < kLaunchElems ? n - off : kLaunchElems; }
 
 // Launchers: enqueue on `stream`, return the hipError_t of the (first failed) launch.

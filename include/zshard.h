@@ -33,8 +33,8 @@
  *     failure the call returns a negative code and launches nothing.
  *     n == 0 (or count == 0 with nothing to pad) is a valid no-op.
  *   - Element counts (n, numel, padded_total, their sums) are at most 2^39
- *     per call; larger counts are ZS_EINVAL.  A call over more than 2^30
- *     elements is enqueued as several launches of at most 2^30 elements
+ *     per call; larger counts are ZS_EINVAL.  A call over more than 2^31
+ *     elements is enqueued as several launches of at most 2^31 elements
  *     each (HIP grids stay below 2^32 work-items), with the same results as
  *     one; a ZS_EHIP from a later launch leaves the earlier ones enqueued.
  *   - fp32 pointers must be 4-byte aligned, bf16 pointers 2-byte aligned,

@@ -1,7 +1,7 @@
 """GPU parity for calls longer than one launch.
 
 A HIP launch must stay below 2^32 work-items, so the library runs a call of
-more than 2^30 elements as several launches over consecutive pieces of the
+more than 2^31 elements as several launches over consecutive pieces of the
 buffers (and several table entries per tensor for the flat copies).  Every
 case here crosses at least one piece boundary, aligned (vector path) and as
 a view one element off (scalar path), and the last one runs the scalar
@@ -23,7 +23,7 @@ from tests.parity import NORM_TOL, bits_equal, identical_fraction, to_np
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 DEV = "cuda"
-PIECE = 1 << 30            # elements per launch
+PIECE = 1 << 31            # elements per launch
 N = PIECE + 4099           # one piece boundary, a ragged last piece
 FILL = 1 << 27             # elements per generator call when filling
 
