@@ -6,6 +6,10 @@ norm scratch.  A step is: ``accumulate`` once per micro-batch (the last one
 may form the squared norm in the same pass), then ``step``: the norm (if
 not formed yet and requested) and the fused AdamW update with the bf16
 re-cast.  Nothing here computes; it orders calls.
+
+``state_dict`` / ``load_state_dict`` carry the step counter and the fp32
+master, exp_avg and exp_avg_sq between runs: a resumed run continues bit
+for bit (the bf16 parameter is the master's re-cast, rewritten every step).
 """
 from __future__ import annotations
 
@@ -58,16 +62,41 @@ class ShardOptimizer:
                               max_norm=self.max_norm, extra_norm_sq=extra_norm_sq, step=self.t)
 
     def step(self, extra_norm_sq: float = 0.0) -> None:
-        """Norm (if clipping or asked for), then the fused AdamW update."""
+        """Norm (if clipping or asked for), then the fused AdamW update.  The
+        step counter advances only once the update is enqueued."""
         if self._pending == 0:
             raise RuntimeError("step() without an accumulated gradient")
-        self.t += 1
         norm = None
         if self.compute_norm:
             if not self._norm_ready:
                 zs.grad_norm_sq(self.acc, self.grad_scale, self.norm_sq, self.workspace)
             norm = self.norm_sq
-        zs.adamw_step(self.hp(extra_norm_sq), self.master, self.exp_avg, self.exp_avg_sq, self.acc,
-                      self.param_bf16, norm_sq=norm)
+        hp = self.hp(extra_norm_sq)
+        hp.step = self.t + 1
+        zs.adamw_step(hp, self.master, self.exp_avg, self.exp_avg_sq, self.acc, self.param_bf16, norm_sq=norm)
+        self.t += 1
+        self._pending = 0
+        self._norm_ready = False
+
+    def state_dict(self) -> dict:
+        """The optimizer state: the step counter and the fp32 master,
+        exp_avg and exp_avg_sq (the live device tensors, not copies)."""
+        return {"step": self.t, "master": self.master, "exp_avg": self.exp_avg, "exp_avg_sq": self.exp_avg_sq}
+
+    def load_state_dict(self, state: dict) -> None:
+        """Copy a state_dict's tensors (any device) into this shard's buffers
+        and take its step counter; sizes must match.  Drops any pending
+        accumulation."""
+        names = ("master", "exp_avg", "exp_avg_sq")
+        for name in names:   # every check before the first copy: a refused state changes nothing
+            src, dst = state[name], getattr(self, name)
+            if src.numel() != dst.numel() or src.dtype != torch.float32:
+                raise ValueError(f"load_state_dict: {name} must be {dst.numel()} float32 elements")
+        t = int(state["step"])
+        if t < 0:
+            raise ValueError("load_state_dict: step must be >= 0")
+        for name in names:
+            getattr(self, name).copy_(state[name].reshape(-1))
+        self.t = t
         self._pending = 0
         self._norm_ready = False

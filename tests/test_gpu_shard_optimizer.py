@@ -61,3 +61,43 @@ def test_shard_optimizer_refuses_a_step_without_gradients():
         opt.step()
     with pytest.raises(TypeError):
         zs.ShardOptimizer(torch.zeros(16, device="cuda", dtype=torch.float64), lr=1e-3)
+
+
+def test_shard_optimizer_resume_is_bit_identical():
+    """Five steps in one run against two steps, a state_dict copied to the
+    host, a fresh optimizer loading it and three more steps: master, moments,
+    bf16 parameter and step counter bit-identical."""
+    print("ShardOptimizer resume", flush=True)
+    n, M, scale = 70_001, 2, 1 / 16
+    rng = np.random.default_rng(23)
+    p0 = rng.uniform(-0.1, 0.1, n).astype(np.float32)
+    grads = [[oracle.bf16_rne((rng.standard_normal(n) * 0.05).astype(np.float32)) for _ in range(M)]
+             for _ in range(5)]
+    kw = dict(lr=3e-4, betas=(0.9, 0.95), weight_decay=0.1, grad_scale=scale, max_norm=1.0)
+
+    def run(opt, steps):
+        for mbs in steps:
+            for k, g in enumerate(mbs):
+                opt.accumulate(from_np(g, bf16=True), last=k == M - 1)
+            opt.step(extra_norm_sq=0.25)
+
+    whole = zs.ShardOptimizer(from_np(p0.copy()), param_bf16=torch.empty(n, dtype=torch.bfloat16, device="cuda"),
+                              **kw)
+    run(whole, grads)
+    first = zs.ShardOptimizer(from_np(p0.copy()), **kw)
+    run(first, grads[:2])
+    saved = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in first.state_dict().items()}
+    del first
+    resumed = zs.ShardOptimizer(torch.empty(n, device="cuda"),
+                                param_bf16=torch.empty(n, dtype=torch.bfloat16, device="cuda"), **kw)
+    resumed.load_state_dict(saved)
+    assert resumed.t == 2
+    run(resumed, grads[2:])
+    torch.cuda.synchronize()
+    assert resumed.t == whole.t == 5
+    for name in ("master", "exp_avg", "exp_avg_sq", "param_bf16"):
+        assert bits_equal(to_np(getattr(resumed, name)), to_np(getattr(whole, name))), name
+    before = to_np(resumed.master)
+    with pytest.raises(ValueError):
+        resumed.load_state_dict({**saved, "exp_avg": saved["exp_avg"][:-1]})
+    assert resumed.t == 5 and bits_equal(to_np(resumed.master), before)   # a refused state changes nothing
