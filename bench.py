@@ -36,14 +36,14 @@ HBM_PEAK_GBPS = 8000.0   # MI355X published HBM3E bandwidth
 # HBM bytes per adamw_step launch on the Llama-7B shard, from two rocprofv3
 # --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch),
 # each scaled by what the same counter reads for the 4 GiB device copy this
-# script also runs (FETCH_SIZE reads 2,097,193 KiB for it: x2.0; WRITE_SIZE
+# script also runs (FETCH_SIZE reads 2,097,194 KiB for it: x2.0; WRITE_SIZE
 # reads 4,194,304 KiB: x1.0).  Valid only for the kernel source it was taken
 # on: the hash covers the kernel file and its header.
 PMC_TRAFFIC = {
     "adamw_step": {"sources": ("csrc/adamw.hip", "csrc/zs_common.h"),
-                   "sha256_16": "e85d06743139e146", "shard_elems": 842301952,
-                   "fetch_kib": 6580556.2, "fetch_scale": 2.0,
-                   "write_kib": 11515848.0, "write_scale": 1.0},
+                   "sha256_16": "de86c32008879139", "shard_elems": 842301952,
+                   "fetch_kib": 6580559.3, "fetch_scale": 2.0,
+                   "write_kib": 11515848.8, "write_scale": 1.0},
 }
 
 
