@@ -66,6 +66,81 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+class DeviceEvent:
+    """A timing HIP event recorded with a device-scope release
+    (hipEventReleaseToDevice).  A default event's system-scope release makes
+    its timestamp wait for a write-back of the GPU caches, which lands inside
+    the timed interval; with a device-scope release the interval between two
+    events is the work between them.  Same interface as torch.cuda.Event;
+    created through the HIP runtime torch has loaded (one runtime per
+    process).  FLAGS falls back to 0 (a default event) if the runtime
+    refuses the flag, and the JSON line says which was used."""
+    RELEASE_TO_DEVICE = 0x40000000
+    FLAGS = None
+    _hip = None
+
+    @classmethod
+    def hip(cls):
+        if cls._hip is None:
+            import ctypes
+            import torch
+            torch.cuda.init()
+            path = None
+            with open("/proc/self/maps") as f:
+                for line in f:
+                    if "libamdhip64.so" in line:
+                        path = line.split()[-1]
+                        break
+            if path is None:
+                raise RuntimeError("the HIP runtime is not loaded")
+            L = ctypes.CDLL(path)
+            L.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            for fn in ("hipEventCreateWithFlags", "hipEventRecord", "hipEventElapsedTime", "hipEventDestroy"):
+                getattr(L, fn).restype = ctypes.c_int
+            probe = ctypes.c_void_p()
+            if L.hipEventCreateWithFlags(ctypes.byref(probe), cls.RELEASE_TO_DEVICE) == 0:
+                cls.FLAGS = cls.RELEASE_TO_DEVICE
+                L.hipEventDestroy(probe)
+            else:
+                cls.FLAGS = 0
+            cls._hip = L
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self._ct = ctypes
+        self.h = ctypes.c_void_p()
+        rc = self.hip().hipEventCreateWithFlags(ctypes.byref(self.h), self.FLAGS)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags returned {rc}")
+
+    def record(self, stream=None):
+        import torch
+        s = stream if stream is not None else torch.cuda.current_stream()
+        rc = self.hip().hipEventRecord(self.h, self._ct.c_void_p(s.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord returned {rc}")
+
+    def elapsed_time(self, end: "DeviceEvent") -> float:
+        ms = self._ct.c_float()
+        rc = self.hip().hipEventElapsedTime(self._ct.byref(ms), self.h, end.h)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime returned {rc}")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self.h:
+            self._hip.hipEventDestroy(self.h)
+
+
+def timing_events() -> str:
+    DeviceEvent.hip()
+    return "hipEventReleaseToDevice" if DeviceEvent.FLAGS else "default (system-scope release)"
+
+
 def step_bytes_per_elem(w) -> dict:
     """Algorithmic HBM bytes per shard element of each kernel of one step."""
     g = 2 if w.grad_dtype == "bf16" else 4
@@ -120,7 +195,7 @@ def run_gpu(w, steps: int, warmup: int):
     torch.cuda.synchronize()
     log(f"[bench] inputs resident: {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
 
-    ev = lambda: torch.cuda.Event(enable_timing=True)
+    ev = DeviceEvent
     timing = []   # per step: (start, last micro-batch start, adamw start, adamw end)
     last = len(grads) - 1
 
@@ -262,7 +337,7 @@ def _time_adamw_traffic(master, exp_avg, exp_avg_sq, grad, bf16, n: int, lds: in
             bf16.data_ptr() if bf16 is not None else None, n, lds, stream.cuda_stream]
     events = []
     for k in range(reps + 1):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = DeviceEvent(), DeviceEvent()
         e0.record(stream)
         rc = f(*args)
         e1.record(stream)
@@ -289,7 +364,7 @@ def run_flat(w, reps: int = 10):
     _, _, _, padded = zs.zero_shard_range(w.total, w.world, w.rank)
     flat = torch.empty(padded, dtype=torch.bfloat16, device=dev)
     outs = [torch.empty_like(p) for p in params]
-    ev = lambda: torch.cuda.Event(enable_timing=True)
+    ev = DeviceEvent
     zs.flat_pack(params, flat, padded)
     zs.flat_unpack(flat, outs)
     e = [ev() for _ in range(3)]
@@ -347,7 +422,7 @@ def run_zero1_flow(w, shapes, reps: int = 3):
     m = torch.zeros(n, dtype=torch.float32, device=dev)
     v = torch.zeros(n, dtype=torch.float32, device=dev)
     mine = gathered[w.rank * chunk:w.rank * chunk + n]
-    ev = lambda: torch.cuda.Event(enable_timing=True)
+    ev = DeviceEvent
 
     def timed(fn):
         fn(0)
@@ -517,6 +592,7 @@ def main():
                        "adamw_step": r["adamw_ms"]},
         "bytes_per_elem": bpe,
         "device_copy_gbps": r["copy_gbps"],
+        "timing_events": timing_events(),
         "adamw_traffic_ceiling": ceiling_report(r["ceiling_ms"], adamw_bytes, r["adamw_ms"]),
         "roofline": {"kernel": "adamw_step", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
