@@ -191,7 +191,8 @@ def run_gpu(w, steps: int, warmup: int):
     acc = torch.empty(n, dtype=torch.float32, device=dev)
     grads = [workloads.grad_draw(w, n, 1, mb, dev) for mb in range(w.micro_batches)]
     norm = torch.zeros(1, dtype=torch.float64, device=dev)
-    ws = torch.empty(max(zs.grad_accum_norm_sq_workspace_bytes(n), 8), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(zs.grad_accum_norm_sq_workspace_bytes(n), zs.grad_norm_sq_workspace_bytes(n), 8),
+                     dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     log(f"[bench] inputs resident: {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
 
@@ -272,6 +273,18 @@ def run_gpu(w, steps: int, warmup: int):
         torch.cuda.synchronize()
         reduce_ms = r0.elapsed_time(r1) / 3
 
+    # outside the step: the standalone squared norm over the accumulated
+    # gradient (4 B/element), as when the gradient arrives from a
+    # reduce-scatter instead of this rank's own accumulation
+    n0, n1 = ev(), ev()
+    zs.grad_norm_sq(acc, w.grad_scale, norm, ws)
+    n0.record()
+    for _ in range(5):
+        zs.grad_norm_sq(acc, w.grad_scale, norm, ws)
+    n1.record()
+    torch.cuda.synchronize()
+    norm_ms = n0.elapsed_time(n1) / 5
+
     # outside the step: the variant with no fp32 master (24 B/element), on the
     # same buffers (state after the timed steps)
     no_master_ms = None
@@ -312,7 +325,7 @@ def run_gpu(w, steps: int, warmup: int):
     del src, dst
     return {"n": n, "wall_s": wall, "accum_ms": acc_ms, "last_ms": last_ms, "adamw_ms": adamw_ms, "graph_ms": graph_ms,
             "reduce_ms": reduce_ms, "chunks": len(grads), "no_master_ms": no_master_ms,
-            "copy_gbps": copy_gbps, "ceiling_ms": ceiling}
+            "copy_gbps": copy_gbps, "ceiling_ms": ceiling, "norm_ms": norm_ms}
 
 
 CEILING_LDS = (0, 8192, 12288, 16384, 20480)   # LDS reserved per one-wave workgroup
@@ -601,6 +614,9 @@ def main():
         "cpu_baseline": cpu,
         "flat_unit": flat,
         "zero1_flow": zero1,
+        "grad_norm_sq": {"ms": r["norm_ms"], "bytes_per_elem": 4,
+                         "gbps": 4 * n / (r["norm_ms"] * 1e-3) / 1e9,
+                         "frac": 4 * n / (r["norm_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS},
         "adamw_step_no_master": None if r["no_master_ms"] is None else {
             "ms": r["no_master_ms"], "bytes_per_elem": 24,
             "gbps": 24 * n / (r["no_master_ms"] * 1e-3) / 1e9},

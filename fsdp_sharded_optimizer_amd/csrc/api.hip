@@ -118,7 +118,10 @@ int32_t grad_reduce_chunks(float* acc, const void* const* chunks, int32_t count,
 
 int64_t grad_norm_sq_workspace_bytes(int64_t n) {
     if (!size_ok(n)) return -1;
-    return zs::norm_partial_blocks(n) * (int64_t)sizeof(double);
+    // one partial per 4096-element tile, then (beyond one workgroup's share)
+    // the chunk stage of the partials' reduction
+    const int64_t parts = zs::norm_partials(n);
+    return (parts <= zs::kSumOneGroup ? parts : parts + zs::kReduceChunks) * (int64_t)sizeof(double);
 }
 
 int32_t grad_norm_sq(const float* grad, int64_t n, double grad_scale, double* out_sq_dev,

@@ -1,41 +1,57 @@
 // This shard's share of the squared global gradient norm, in two stages.
 //
-// Stage 1 (HBM-bound, 4 B/element): a fixed grid of P workgroups, P a
-// function of n only, grid-strides over 4-element vectors (one 128-bit
-// lane-contiguous load per lane and iteration; P <= 2048 measured best on
-// gfx950 against larger grids, deeper unrolls and one-shot tiles).  Each thread
-// forms g1 = fl32(g * scale), squares it exactly in binary64 and adds it to
-// a binary64 running sum; the 64 lanes of a wave are combined by a fixed
-// butterfly of cross-lane shuffles, the 4 waves of a workgroup through LDS,
-// and each workgroup writes one binary64 partial to the workspace.
-// Stage 2: one workgroup adds the P partials in a fixed tree.
-// The association is fixed by n alone, so the result is bit-identical run
-// to run.  The gradient is only read, so any 4-byte-aligned start takes the
-// 128-bit path.
+// Stage 1 (HBM-bound, 4 B/element): a one-shot grid of 256-thread
+// workgroups, each reading one tile of kNormTile = 4096 elements: four
+// lane-contiguous 128-bit loads per lane, the q-th 1024 elements after the
+// first, all issued before the first square.  Each thread forms
+// g1 = fl32(g * scale), squares it exactly in binary64 and adds it to two
+// binary64 running sums (its groups in order, elements 0 and 2 of each into
+// one sum, 1 and 3 into the other); the 64 lanes of a wave are combined by a
+// fixed butterfly of cross-lane shuffles, the 4 waves through LDS, and each
+// workgroup writes one binary64 partial to the workspace.  Residency is
+// capped at 6 workgroups per CU by 24 KiB of reserved LDS.  Measured on
+// gfx950 (842M elements, random data): 87.3-87.7 % of the HBM peak, against
+// 83.7-84.0 % for a grid-striding grid of 2048 workgroups (the earlier
+// shape), 85-87 % with two loads per lane, 72-75 % with one; a plain fp32
+// read-sum of the same shape reaches 88.8 %.
+// Stage 2: the partials are added in a fixed tree (contiguous chunks, then
+// one workgroup).  The association is fixed by n alone, so the result is
+// bit-identical run to run.  The gradient is only read, so any
+// 4-byte-aligned start takes the 128-bit path.
 #include "reduce.h"
 
 namespace zs {
 namespace {
 
-constexpr int64_t kMaxPartials = 2048;   // 8 workgroups per CU on 256 CUs
+constexpr int kNormQ = 4;
+constexpr int64_t kNormTile = (int64_t)kBlock * 4 * kNormQ;
+constexpr unsigned kNormLds = 24576;
+static_assert(kLaunchElems % kNormTile == 0, "launch pieces keep the partials' positions");
 
 __global__ __launch_bounds__(kBlock) void norm_partial_kernel(const float* __restrict__ grad,
                                                               int64_t n, float scale,
                                                               double* __restrict__ partials) {
-    const int64_t nvec = (n + 3) / 4;
-    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    const int64_t tile = (int64_t)blockIdx.x * kNormTile;
+    const int64_t lane0 = tile + threadIdx.x * 4;
     double s0 = 0.0, s1 = 0.0;
-    for (int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x; k < nvec; k += stride) {
-        const int64_t first = k * 4;
-        float g[4];
-        if (first + 4 <= n) {   // read-only: a dword-aligned 128-bit load at any offset
-            const f32x4 a = ld_stream_f32x4_a4(grad + first);
-            g[0] = a.x; g[1] = a.y; g[2] = a.z; g[3] = a.w;
-        } else {
+    if (tile + kNormTile <= n) {   // whole tile; read-only: dword-aligned 128-bit loads at any offset
+        f32x4 v[kNormQ];
+#pragma unroll
+        for (int q = 0; q < kNormQ; ++q) v[q] = ld_stream_f32x4_a4(grad + lane0 + q * kBlock * 4);
+#pragma unroll
+        for (int q = 0; q < kNormQ; ++q) {
+            const float g[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+            add_squares4(g, scale, s0, s1);
+        }
+    } else {   // the ragged last tile: out-of-range elements add +0
+#pragma unroll
+        for (int q = 0; q < kNormQ; ++q) {
+            const int64_t first = lane0 + q * kBlock * 4;
+            float g[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) g[j] = first + j < n ? grad[first + j] : 0.0f;
+            add_squares4(g, scale, s0, s1);
         }
-        add_squares4(g, scale, s0, s1);
     }
     const double total = block_sum(s0 + s1);
     if (threadIdx.x == 0) partials[blockIdx.x] = total;
@@ -65,7 +81,7 @@ __global__ __launch_bounds__(kBlock) void chunk_sum_kernel(const double* __restr
 
 hipError_t launch_sum_partials(const double* partials, int64_t count, double* stage, double* out,
                                hipStream_t stream) {
-    if (count <= kBlock * 8) {   // small: one workgroup
+    if (count <= kSumOneGroup) {   // small: one workgroup
         hipLaunchKernelGGL(norm_final_kernel, dim3(1), dim3(kBlock), 0, stream, partials, count, out);
         return hipGetLastError();
     }
@@ -79,24 +95,21 @@ hipError_t launch_sum_partials(const double* partials, int64_t count, double* st
     return hipGetLastError();
 }
 
-int64_t norm_partial_blocks(int64_t n) {
-    if (n <= 0) return 0;
-    const int64_t nvec = (n + 3) / 4;
-    const int64_t b = (nvec + kBlock - 1) / kBlock;
-    return b < kMaxPartials ? b : kMaxPartials;
-}
+int64_t norm_partials(int64_t n) { return n <= 0 ? 0 : (n + kNormTile - 1) / kNormTile; }
 
+// stage 1 in launches of at most kLaunchElems elements (piece k's partials
+// follow piece k-1's), then the fixed tree over all partials
 hipError_t launch_grad_norm_sq(const float* grad, int64_t n, float scale, double* out,
-                               double* partials, hipStream_t stream) {
-    const int64_t blocks = norm_partial_blocks(n);
-    if (blocks > 0) {
-        hipLaunchKernelGGL(norm_partial_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, stream, grad, n, scale,
-                           partials);
+                               double* workspace, hipStream_t stream) {
+    const int64_t parts = norm_partials(n);
+    for (int64_t off = 0; off < n; off += kLaunchElems) {
+        const int64_t m = launch_piece(n, off);
+        hipLaunchKernelGGL(norm_partial_kernel, dim3((unsigned)((m + kNormTile - 1) / kNormTile)), dim3(kBlock),
+                           kNormLds, stream, grad + off, m, scale, workspace + off / kNormTile);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(norm_final_kernel, dim3(1), dim3(kBlock), 0, stream, partials, blocks, out);
-    return hipGetLastError();
+    return launch_sum_partials(workspace, parts, workspace + parts, out, stream);
 }
 
 }  // namespace zs

@@ -48,6 +48,7 @@ __device__ __forceinline__ void add_squares4(const float (&g)[4], float scale, d
 // writes 0.  (The fused accumulation leaves one partial per 256 elements:
 // 3.3M for an 842M shard, about 1,600 per chunk.)
 constexpr int64_t kReduceChunks = 2048;
+constexpr int64_t kSumOneGroup = kBlock * 8;   // up to this many partials: one workgroup, no stage
 hipError_t launch_sum_partials(const double* partials, int64_t count, double* stage, double* out,
                                hipStream_t stream);
 

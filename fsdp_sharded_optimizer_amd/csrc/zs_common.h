@@ -105,13 +105,13 @@ hipError_t launch_adamw_no_master(const AdamwArgs& a, bool vec_ok, hipStream_t s
 hipError_t launch_adam_update(const AdamwArgs& a, bool vec_ok, hipStream_t stream);
 hipError_t launch_grad_accum(float* acc, const void* grad, int grad_bf16, int64_t n,
                              int overwrite, bool vec_ok, hipStream_t stream);
-int64_t norm_partial_blocks(int64_t n);
+int64_t norm_partials(int64_t n);   // grad_norm_sq's stage-1 partials for n elements
 int64_t accum_norm_partials(int64_t n);
 hipError_t launch_grad_accum_norm_sq(float* acc, const void* grad, int grad_bf16, int64_t n, int overwrite,
                                      float scale, double* out, double* workspace, bool vec_ok,
                                      hipStream_t stream);
 hipError_t launch_grad_norm_sq(const float* grad, int64_t n, float scale, double* out,
-                               double* partials, hipStream_t stream);
+                               double* workspace, hipStream_t stream);
 
 // Up to kReduceMaxChunks rank chunks summed per launch (pointers travel in
 // the kernel arguments).

@@ -87,8 +87,11 @@ def test_workspace_bytes():
     assert zs.grad_norm_sq_workspace_bytes(0) == 0
     assert zs.grad_norm_sq_workspace_bytes(-1) == -1
     assert zs.grad_norm_sq_workspace_bytes(1) == 8
-    # capped number of partials for large n; beyond the per-call element limit: -1
-    assert zs.grad_norm_sq_workspace_bytes(10**10) == zs.grad_norm_sq_workspace_bytes(10**9)
+    # one partial per 4096-element tile; beyond 2048 partials, a 2048-entry chunk stage too
+    assert zs.grad_norm_sq_workspace_bytes(4096 * 2048) == 2048 * 8
+    assert zs.grad_norm_sq_workspace_bytes(4096 * 2048 + 1) == (2049 + 2048) * 8
+    assert zs.grad_norm_sq_workspace_bytes(10**10) == (-(-10**10 // 4096) + 2048) * 8
+    # beyond the per-call element limit: -1
     assert zs.grad_norm_sq_workspace_bytes(2**63 - 1) == -1 and zs.grad_accum_norm_sq_workspace_bytes(2**39 + 1) == -1
 
 
