@@ -41,9 +41,9 @@ HBM_PEAK_GBPS = 8000.0   # MI355X published HBM3E bandwidth
 # on: the hash covers the kernel file and its header.
 PMC_TRAFFIC = {
     "adamw_step": {"sources": ("csrc/adamw.hip", "csrc/zs_common.h"),
-                   "sha256_16": "de86c32008879139", "shard_elems": 842301952,
-                   "fetch_kib": 6580559.3, "fetch_scale": 2.0,
-                   "write_kib": 11515848.8, "write_scale": 1.0},
+                   "sha256_16": "1fec0d6ae7b7f2ea", "shard_elems": 842301952,
+                   "fetch_kib": 6580558.7, "fetch_scale": 2.0,
+                   "write_kib": 11515848.1, "write_scale": 1.0},
 }
 
 
