@@ -1,0 +1,174 @@
+"""Property tests of the C ABI's host-side validation (CPU only).
+
+Random argument sets for adamw_step, flat_pack and flat_unpack: sizes,
+alignments, null pointers, overlapping buffers and hyperparameters.  A
+Python model of the rules include/zshard.h documents (and of the order in
+which they are checked) predicts each return code.  Only argument sets the
+model says must fail, or are no-ops, are passed to the library, so no call
+reaches a kernel launch; the autouse fixture also checks that no HIP error
+was left behind.  Pointers are never dereferenced.
+"""
+import ctypes
+import math
+
+import pytest
+from hypothesis import HealthCheck, given, settings
+from hypothesis import strategies as st
+
+import fsdp_sharded_optimizer_amd as zs
+from fsdp_sharded_optimizer_amd import _binding as B
+
+BASE = 0x7F0000000000      # fake device addresses, never dereferenced
+MAX_ELEMS = 1 << 39
+EINVAL, EOVERLAP, OK = B.ZS_EINVAL, B.ZS_EOVERLAP, B.ZS_OK
+
+SETTINGS = settings(max_examples=1500, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+
+
+@pytest.fixture(autouse=True)
+def no_launch_reached():
+    yield
+    assert zs.lib().zs_last_hip_error() == 0, "a call got past validation to a kernel launch"
+
+
+def overlap(p, nbytes, q, qbytes):
+    if nbytes <= 0 or qbytes <= 0:
+        return False
+    return p < q + qbytes and q < p + nbytes
+
+
+# A pointer: rarely null, else one of a few slots 4 KiB apart (so that
+# buffers of a few thousand bytes often overlap) plus a byte offset (mostly
+# aligned, sometimes 1 or 2 bytes off).
+pointers = st.sampled_from([0] + [None] * 9).flatmap(
+    lambda z: st.just(0) if z == 0 else st.builds(lambda slot, off: BASE + slot * 4096 + off, st.integers(0, 7),
+                                                    st.sampled_from([0, 0, 0, 4, 8, 16, 64, 1, 2, 6])))
+odd_values = st.sampled_from([0.0, -0.0, -1e-3, 1.0, 1.5, math.inf, -math.inf, math.nan, 1e-300])
+VALID_HP = (3e-4, 0.9, 0.95, 1e-8, 0.1, 1.0 / 64, 1.0, 0.5, 3)
+
+
+@st.composite
+def hyperparameters(draw):
+    """A valid set, or (half the time) one field replaced by an odd value."""
+    hp = list(VALID_HP)
+    if draw(st.booleans()):
+        i = draw(st.integers(0, 8))
+        hp[i] = draw(st.integers(-2, 1)) if i == 8 else draw(odd_values)
+    return tuple(hp)
+
+
+# ---------------------------------------------------------------------------
+# adamw_step
+# ---------------------------------------------------------------------------
+
+def adamw_model(hp, ptrs, n, norm):
+    lr, b1, b2, eps, wd, scale, max_norm, extra, step = hp
+    if not (0 <= n <= MAX_ELEMS) or step < 1:
+        return EINVAL
+    if not (0.0 <= b1 < 1.0) or not (0.0 <= b2 < 1.0):
+        return EINVAL
+    if not (eps > 0.0 and math.isfinite(eps)) or not (lr >= 0.0 and math.isfinite(lr)):
+        return EINVAL
+    if not (wd >= 0.0 and math.isfinite(wd)) or not (scale > 0.0 and math.isfinite(scale)):
+        return EINVAL
+    if math.isnan(max_norm) or extra < 0.0:
+        return EINVAL
+    if norm and norm % 8:
+        return EINVAL
+    if n == 0:
+        return OK
+    master, m, v, g, b = ptrs
+    if not (master and m and v and g):
+        return EINVAL
+    if master % 4 or m % 4 or v % 4 or g % 4 or (b and b % 2):
+        return EINVAL
+    bufs = [(master, 4 * n, True), (m, 4 * n, True), (v, 4 * n, True), (g, 4 * n, False), (b, 2 * n if b else 0, True)]
+    for i in range(5):
+        for j in range(i + 1, 5):
+            if overlap(bufs[i][0], bufs[i][1], bufs[j][0], bufs[j][1]):
+                return EOVERLAP
+        if norm and bufs[i][2] and overlap(bufs[i][0], bufs[i][1], norm, 8):
+            return EOVERLAP
+    return None   # valid: would launch
+
+
+@SETTINGS
+@given(hp=hyperparameters(),
+       ptrs=st.tuples(pointers, pointers, pointers, pointers, pointers),
+       n=st.sampled_from([-1, 0, 1, 3, 64, 1000, 1000, 1500, 5000, MAX_ELEMS + 1]),
+       norm=st.one_of(st.just(0), st.builds(lambda slot, off: BASE + slot * 4096 + off,
+                                            st.integers(0, 7), st.sampled_from([0, 8, 4000, 4]))))
+def test_adamw_step_validation_matches_the_documented_rules(hp, ptrs, n, norm):
+    want = adamw_model(hp, ptrs, n, norm)
+    if want is None:
+        return   # a valid call would launch a kernel: not made here
+    c = B.AdamW(*hp[:8], hp[8])
+    got = zs.lib().adamw_step(ctypes.byref(c), *[p or None for p in ptrs], n, norm or None, None)
+    assert got == want, (hp, [hex(p) for p in ptrs], n, hex(norm))
+
+
+# ---------------------------------------------------------------------------
+# flat_pack / flat_unpack
+# ---------------------------------------------------------------------------
+
+def flat_model(tensors, count, flat, flat_dt, t_dt, padded, unpack):
+    if count < 0:
+        return EINVAL
+    if flat_dt not in (0, 1) or t_dt not in (0, 1):
+        return EINVAL
+    if flat_dt != t_dt and not ((not unpack and t_dt == 1 and flat_dt == 0) or (unpack and flat_dt == 0 and t_dt == 1)):
+        return EINVAL
+    fsz, tsz = (4 if flat_dt == 0 else 2), (4 if t_dt == 0 else 2)
+    total = 0
+    for p, k in tensors[:count]:
+        if not (0 <= k <= MAX_ELEMS) or total > MAX_ELEMS - k:
+            return EINVAL
+        if k > 0 and (not p or p % tsz):
+            return EINVAL
+        total += k
+    if unpack:
+        padded = total
+    if not (0 <= padded <= MAX_ELEMS) or total > padded:
+        return EINVAL
+    if padded == 0:
+        return OK
+    if not flat or flat % fsz:
+        return EINVAL
+    for i, (p, k) in enumerate(tensors[:count]):
+        if overlap(p, k * tsz, flat, padded * fsz):
+            return EOVERLAP
+        if unpack:
+            for q, kk in tensors[i + 1:count]:
+                if overlap(p, k * tsz, q, kk * tsz):
+                    return EOVERLAP
+    return None
+
+
+numels = st.sampled_from([0, 1, 5, 300, 1000, 2000, 1000, 300, -1, MAX_ELEMS])
+tensor_lists = st.lists(st.tuples(pointers, numels), min_size=0, max_size=4)
+dtype_pairs = st.sampled_from([(0, 0), (1, 1), (0, 1), (1, 0), (0, 0), (1, 1), (0, 1), (2, 0), (0, -1)])
+
+
+@SETTINGS
+@given(tensors=tensor_lists, flat=pointers, dts=dtype_pairs,
+       pad=st.sampled_from([0, 0, 3, 700, -1, MAX_ELEMS + 1]), unpack=st.booleans(),
+       count_delta=st.sampled_from([0, 0, 0, 0, 0, -1]))
+def test_flat_validation_matches_the_documented_rules(tensors, flat, dts, pad, unpack, count_delta):
+    """dts = (flat dtype, tensor dtype); the pack's padded_total is the
+    tensors' total plus pad (or pad itself when it is out of range)."""
+    flat_dt, t_dt = dts
+    count = len(tensors) if count_delta == 0 else -1
+    total = sum(max(k, 0) for _, k in tensors)
+    padded = pad if pad < 0 or pad > MAX_ELEMS else total + pad
+    want = flat_model(tensors, count, flat, flat_dt, t_dt, padded, unpack)
+    if want is None:
+        return
+    arr = (B.Tensor * max(len(tensors), 1))()
+    for i, (p, k) in enumerate(tensors):
+        arr[i].ptr, arr[i].numel = p or None, k
+    L = zs.lib()
+    if unpack:
+        got = L.flat_unpack(flat or None, flat_dt, arr, count, t_dt, None)
+    else:
+        got = L.flat_pack(arr, count, t_dt, flat or None, flat_dt, padded, None)
+    assert got == want, (tensors, count, hex(flat), flat_dt, t_dt, padded, unpack)
