@@ -81,7 +81,12 @@ def test_grad_accum_bit_exact(n, dtype, acc_off, grad_off):
 # grad_norm_sq
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("n", SIZES + [3_000_001])
+# the norm's 4096-element tiles and its partials' reduction: one workgroup up
+# to 2048 partials (8,388,608 elements), chunks then one workgroup beyond
+NORM_SIZES = SIZES + [4095, 4096, 4097, 3_000_001, 8_388_608, 8_388_609, 8_392_705]
+
+
+@pytest.mark.parametrize("n", NORM_SIZES)
 @pytest.mark.parametrize("offset", [0, 1])
 def test_grad_norm_sq(n, offset):
     print(f"grad_norm_sq n={n} offset={offset}", flush=True)
