@@ -369,3 +369,25 @@ def test_ceiling_library_rejects_before_launch():
     assert f(a, a + 64, a + 128, a + 192, a + 258, 16, 0, None) == -1      # bf16 output off 16 bytes
     assert f(a, a + 64, a + 128, a + 192, None, 16, -1, None) == -1        # LDS reservation out of range
     assert f(a, a + 64, a + 128, a + 192, None, 16, 65537, None) == -1
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    """No fallback path: with the library absent every call raises."""
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "libzshard.so"))
+    with pytest.raises(RuntimeError, match="no fallback"):
+        B.lib()
+    with pytest.raises(RuntimeError):
+        zs.zero_shard_range(10, 2, 0)
+
+
+def test_product_code_does_not_use_the_oracle():
+    """The package (binding, call ordering, ledger, HIP sources) neither
+    imports nor loads anything under oracle/."""
+    pkg = os.path.join(ROOT, "fsdp_sharded_optimizer_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".c", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, flags=re.M), f
+                assert "orc_" not in text and "liboracle" not in text and "oracle/" not in text, f
