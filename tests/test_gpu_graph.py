@@ -152,3 +152,102 @@ def test_one_graph_replays_every_step_with_device_scalars():
         for k in state:
             assert bits_equal(got[k], to_np(twin[k])), (t, k)
         _ = (acc * 3).sum().item()   # unrelated eager work between replays
+
+
+def test_every_other_entry_point_replays_bit_exact():
+    """flat_pack (bit copy with padding; widening), grad_reduce_chunks,
+    grad_norm_sq, adamw_step_no_master, adam_update, flat_unpack (re-cast)
+    and flat_apply_update (bf16 and fp32 tensors) captured in one graph and
+    replayed four times with fresh inputs, each replay bit-identical to the
+    same calls made eagerly on a twin state."""
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    sizes, world = [20_001, 7, 30_000], 8
+    T = sum(sizes)
+    _, _, _, padded = zs.zero_shard_range(T, world, 0)
+    params = [torch.empty(k, dtype=torch.bfloat16, device=dev) for k in sizes]   # shared inputs
+    chunks = [torch.empty(T, dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    scale = 1 / 24
+    hp = zs.AdamWConfig(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, grad_scale=scale,
+                        max_norm=0.5, extra_norm_sq=0.01, step=4)
+    hu = zs.AdamWConfig(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.0, grad_scale=scale,
+                        max_norm=0.5, extra_norm_sq=0.01, step=4)
+
+    def side():
+        return {"flat": torch.empty(padded, dtype=torch.bfloat16, device=dev),
+                "flat32": torch.empty(padded, device=dev),
+                "acc": torch.empty(T, device=dev),
+                "norm": torch.zeros(1, dtype=torch.float64, device=dev),
+                "ws": torch.empty(max(zs.grad_norm_sq_workspace_bytes(T), 8), dtype=torch.uint8, device=dev),
+                "p16": (torch.rand(T, generator=gen, device=dev) * 0.2 - 0.1).to(torch.bfloat16),
+                "m1": torch.zeros(T, device=dev), "v1": torch.zeros(T, device=dev),
+                "m2": torch.zeros(T, device=dev), "v2": torch.zeros(T, device=dev),
+                "upd": torch.empty(T, device=dev),
+                "outs": [torch.empty(k, dtype=torch.bfloat16, device=dev) for k in sizes],
+                "tb": [(torch.rand(k, generator=gen, device=dev) - 0.5).to(torch.bfloat16) for k in sizes],
+                "tf": [torch.rand(k, generator=gen, device=dev) - 0.5 for k in sizes]}
+
+    a = side()
+    b = {k: ([t.clone() for t in v] if isinstance(v, list) else v.clone()) for k, v in a.items()}
+
+    def calls(s):
+        zs.flat_pack(params, s["flat"], padded)
+        zs.flat_pack(params, s["flat32"], padded)
+        zs.grad_reduce_chunks(s["acc"], chunks, True)
+        zs.grad_norm_sq(s["acc"], scale, s["norm"], s["ws"])
+        zs.adamw_step_no_master(hp, s["p16"], s["m1"], s["v1"], s["acc"], norm_sq=s["norm"])
+        zs.adam_update(hu, s["m2"], s["v2"], s["acc"], s["upd"], norm_sq=s["norm"])
+        zs.flat_unpack(s["flat32"], s["outs"])
+        zs.flat_apply_update(s["upd"], s["tb"])
+        zs.flat_apply_update(s["upd"], s["tf"])
+
+    def fresh(r):
+        for p in params:
+            p.copy_((torch.rand(p.numel(), generator=gen, device=dev) - 0.5) * (r + 1))
+        for c in chunks:
+            c.copy_(torch.randn(T, generator=gen, device=dev) * 1e-2 * (r + 1))
+
+    def flat_bits(s):
+        out = {}
+        for k, v in s.items():
+            if k == "ws":
+                continue
+            out[k] = [to_np(t) for t in v] if isinstance(v, list) else to_np(v)
+        return out
+
+    fresh(0)
+    torch.cuda.synchronize()
+    warm = torch.cuda.Stream()
+    warm.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(warm):       # warm-up outside the capture, on the twin
+        calls(b)
+    torch.cuda.current_stream().wait_stream(warm)
+    torch.cuda.synchronize()
+    for k, v in a.items():              # both sides equal again before the replays
+        if isinstance(v, list):
+            for x, y in zip(v, b[k]):
+                x.copy_(y)
+        else:
+            v.copy_(b[k])
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls(a)
+    torch.cuda.synchronize()
+    for r in range(4):
+        print(f"  replay {r}", flush=True)
+        fresh(r + 1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = flat_bits(a)
+        calls(b)                        # the same calls, eagerly, on the twin
+        torch.cuda.synchronize()
+        want = flat_bits(b)
+        for k in want:
+            if isinstance(want[k], list):
+                assert all(bits_equal(x, y) for x, y in zip(got[k], want[k])), (r, k)
+            else:
+                assert bits_equal(got[k], want[k]), (r, k)
+        assert not got["flat"][T:].any() and not got["flat32"][T:].view(np.uint32).any()   # padding zero
+        _ = (a["acc"] * 2).sum().item()  # unrelated eager work between replays
