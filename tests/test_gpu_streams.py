@@ -58,3 +58,64 @@ def test_calls_run_on_the_stream_they_are_given():
     H = oracle.make_hp(1e-3, 0.9, 0.999, 1e-8, 0.0, 1.0, 0.0, 0.0, 1)
     assert oracle.adamw_step(H, p_ref, m_ref, v_ref, oracle.bf16_widen(g_np)) == 0
     assert bits_equal(to_np(master), p_ref) and bits_equal(to_np(m), m_ref) and bits_equal(to_np(v), v_ref)
+
+
+def test_two_host_threads_on_two_streams_match_serial_runs():
+    """The library keeps no global state (only a thread-local error code):
+    two host threads, each driving its own shard on its own stream through
+    ten accumulate / fused-norm / clipped-AdamW steps, end bit-identical to
+    the same sequences run one after the other on the default stream."""
+    import threading
+    print("two threads, two streams", flush=True)
+    n, M, steps, scale = 300_007, 3, 10, 1 / 24
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(99)
+    grads = [[(torch.randn(n, generator=gen, device="cuda") * 1e-2 * (k + 1)).to(torch.bfloat16) for k in range(M)]
+             for _ in range(2)]
+    init = [(torch.rand(n, generator=gen, device="cuda") * 0.2 - 0.1) for _ in range(2)]
+
+    def make(i):
+        return {"master": init[i].clone(), "m": torch.zeros(n, device="cuda"), "v": torch.zeros(n, device="cuda"),
+                "b": torch.empty(n, dtype=torch.bfloat16, device="cuda"), "acc": torch.empty(n, device="cuda"),
+                "norm": torch.zeros(1, dtype=torch.float64, device="cuda"),
+                "ws": torch.empty(zs.grad_accum_norm_sq_workspace_bytes(n), dtype=torch.uint8, device="cuda")}
+
+    def run(i, s, stream):
+        for t in range(1, steps + 1):
+            for k in range(M - 1):
+                zs.grad_accum(s["acc"], grads[i][k], overwrite=(k == 0), stream=stream)
+            zs.grad_accum_norm_sq(s["acc"], grads[i][M - 1], False, scale, s["norm"], s["ws"], stream=stream)
+            hp = zs.AdamWConfig(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, grad_scale=scale,
+                                max_norm=0.5, extra_norm_sq=0.01 * i, step=t)
+            zs.adamw_step(hp, s["master"], s["m"], s["v"], s["acc"], s["b"], norm_sq=s["norm"], stream=stream)
+
+    serial = [make(0), make(1)]
+    run(0, serial[0], None)
+    run(1, serial[1], None)
+    torch.cuda.synchronize()
+
+    par = [make(0), make(1)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for st_ in streams:
+        st_.wait_stream(torch.cuda.current_stream())   # inputs are ready before either thread starts
+    errors = []
+
+    def worker(i):
+        try:
+            torch.cuda.set_device(0)
+            run(i, par[i], streams[i])
+            streams[i].synchronize()
+        except Exception as e:   # re-raised below on the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=120)
+    assert not any(th.is_alive() for th in threads), "a worker thread did not finish"
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for i in range(2):
+        for k in ("master", "m", "v", "b", "acc", "norm"):
+            assert bits_equal(to_np(par[i][k]), to_np(serial[i][k])), (i, k)
