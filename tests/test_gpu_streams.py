@@ -29,29 +29,53 @@ def _held_side_stream():
     return s
 
 
+def _spin_ms() -> float:
+    """How long the spin holds a stream on this GPU."""
+    s = torch.cuda.Stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(s):
+        e0.record()
+        torch.cuda._sleep(SPIN)
+        e1.record()
+    s.synchronize()
+    return e0.elapsed_time(e1)
+
+
 def test_calls_run_on_the_stream_they_are_given():
     print("explicit streams", flush=True)
+    import time
+    if not hasattr(torch.cuda, "_sleep"):
+        pytest.skip("torch.cuda._sleep is not available")
     n = 1 << 20
     rng = np.random.default_rng(5)
     g_np = oracle.bf16_rne((rng.standard_normal(n) * 1e-2).astype(np.float32))
     g = from_np(g_np, bf16=True)
-    acc = torch.zeros(n, device="cuda")
     srcs = [from_np(oracle.bf16_rne(rng.uniform(-1, 1, k).astype(np.float32)), bf16=True) for k in (1000, 5)]
+    acc = torch.zeros(n, device="cuda")
     flat = torch.zeros(1008, dtype=torch.bfloat16, device="cuda")
-    master = torch.zeros(n, device="cuda")
-    m = torch.zeros(n, device="cuda")
-    v = torch.zeros(n, device="cuda")
-    torch.cuda.synchronize()
-
-    s = _held_side_stream()
-    zs.grad_accum(acc, g, overwrite=True, stream=s)
-    zs.flat_pack(srcs, flat, 1008, stream=s)
+    master, m, v = (torch.zeros(n, device="cuda") for _ in range(3))
     hp = zs.AdamWConfig(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, grad_scale=1.0, step=1)
-    zs.adamw_step(hp, master, m, v, acc, stream=s)
-    early = [to_np(t) for t in (acc, flat, master)]       # the default stream does not wait for s
-    assert not early[0].any() and not early[1].any() and not early[2].any(), "a call did not wait on its stream"
-
-    s.synchronize()
+    spin = _spin_ms()
+    observed = False
+    for attempt in range(3):   # the check needs the host to read within the spin: retry if it did not
+        for t in (acc, flat, master, m, v):
+            t.zero_()
+        torch.cuda.synchronize()
+        s = _held_side_stream()
+        t0 = time.perf_counter()
+        zs.grad_accum(acc, g, overwrite=True, stream=s)
+        zs.flat_pack(srcs, flat, 1008, stream=s)
+        zs.adamw_step(hp, master, m, v, acc, stream=s)
+        early = [to_np(t) for t in (acc, flat, master)]   # the default stream does not wait for s
+        host_ms = (time.perf_counter() - t0) * 1e3
+        s.synchronize()
+        if host_ms < 0.5 * spin:
+            assert not any(e.any() for e in early), "a call did not wait on its stream"
+            observed = True
+            break
+        print(f"  attempt {attempt}: host took {host_ms:.1f} ms of a {spin:.1f} ms spin, inconclusive", flush=True)
+    if not observed:
+        pytest.skip("the host could not read within the spin; ordering not observed")
     assert bits_equal(to_np(acc), oracle.bf16_widen(g_np))
     assert bits_equal(to_np(flat), oracle.flat_pack([to_np(x) for x in srcs], oracle.BF16, oracle.BF16, 1008))
     p_ref, m_ref, v_ref = np.zeros(n, np.float32), np.zeros(n, np.float32), np.zeros(n, np.float32)
