@@ -101,7 +101,9 @@ typedef struct {
     double max_norm;      /* > 0: clip to this global L2 norm; <= 0: no clip */
     double extra_norm_sq; /* >= 0 or non-finite: the other ranks' sum of
                              squares of their scaled gradients (the result of
-                             the scalar all-reduce); 0 for a single rank */
+                             the scalar all-reduce); 0 for a single rank, or
+                             when *norm_sq_dev was itself all-reduced across
+                             ranks on the device (no host synchronisation) */
     int64_t step;         /* t >= 1, caller-owned, incremented before the call */
 } zs_adamw;
 
