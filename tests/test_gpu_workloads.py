@@ -436,3 +436,33 @@ def test_reduce_chunks_and_no_master_full_size_sampled():
         for name, gpu, ref in (("b", param, b_ref), ("m", m, m_ref), ("v", v, v_ref)):
             got = host(gpu[idx])
             assert bits_equal(got, ref), (t, name, identical_fraction(got, ref))
+
+
+def test_full_unit_conversions_every_element():
+    """The two conversions bench.py times on the 70B block unit, at full
+    size and in the same launch configuration: the widening pack of the 9
+    bf16 tensors (855,654,400 elements) into an fp32 flat buffer, and the
+    re-casting unpack of an fp32 flat buffer of arbitrary values back into
+    bf16 tensors; every element against the oracle."""
+    w = workloads.WORKLOADS["fsdp_unit_70b_block"]
+    params = workloads.unit_tensors(w, DEV)
+    sizes = [p.numel() for p in params]
+    total = sum(sizes)
+    log(f"  unit widening pack: {total} elements")
+    flat32 = torch.full((total,), float("nan"), device=DEV)
+    zs.flat_pack(params, flat32, total)
+    params_ref = [host(p).reshape(-1) for p in params]
+    want = oracle.flat_pack(params_ref, oracle.BF16, oracle.F32, total)
+    assert bits_equal(host(flat32), want)
+    del want
+    log("  unit re-casting unpack")
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(workloads.seed_of(w.cfg, workloads.PURPOSE_GRAD, 7, 0))
+    flat32.normal_(0.0, 0.05, generator=gen)      # arbitrary fp32 values: the re-cast must round
+    outs = [torch.empty_like(p) for p in params]
+    zs.flat_unpack(flat32, outs)
+    back = oracle.flat_unpack(host(flat32), oracle.F32, sizes, oracle.BF16)
+    for i, (o, r) in enumerate(zip(outs, back)):
+        assert bits_equal(host(o).reshape(-1), r), i
+    del params, outs, flat32, back
+    torch.cuda.empty_cache()
