@@ -466,3 +466,36 @@ def test_full_unit_conversions_every_element():
         assert bits_equal(host(o).reshape(-1), r), i
     del params, outs, flat32, back
     torch.cuda.empty_cache()
+
+
+def test_full_size_fp32_gradient_paths():
+    """fp32 gradients (a reduce-scatter's fp32 output) at the Llama-7B shard
+    size: the overwriting fused accumulation with the norm (one group per
+    lane, uncapped) and the two-chunk fp32 reduction (its own residency
+    cap); the accumulator on a sample, the norm over the whole shard."""
+    w = workloads.WORKLOADS["llama7b_shard"]
+    _, start, end, _ = zs.zero_shard_range(w.total, w.world, w.rank)
+    n = end - start
+    idx = sample_indices(n, seed=5)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(workloads.seed_of(w.cfg, workloads.PURPOSE_GRAD, 8, 0))
+    c0 = torch.randn(n, generator=gen, device=DEV).mul_(1e-3)
+    c1 = torch.randn(n, generator=gen, device=DEV).mul_(1e-3)
+    acc = torch.empty(n, device=DEV)
+    norm = torch.zeros(1, dtype=torch.float64, device=DEV)
+    log("  7B fp32 overwrite + norm")
+    zs.grad_accum_norm_sq(acc, c0, True, w.grad_scale, norm)
+    c0_host = host(c0)
+    S = oracle.grad_norm_sq(c0_host, w.grad_scale)
+    assert abs(math.sqrt(norm.item()) - math.sqrt(S)) <= NORM_TOL * math.sqrt(S)
+    assert bits_equal(host(acc[idx]), c0_host[host(idx)])
+    del c0_host
+    log("  7B fp32 reduce, two chunks")
+    zs.grad_reduce_chunks(acc, [c0, c1], True)
+    ref = np.empty(idx.numel(), np.float32)
+    oracle.grad_accum(ref, host(c0[idx]), oracle.F32, overwrite=True)
+    oracle.grad_accum(ref, host(c1[idx]), oracle.F32, overwrite=False)
+    got = host(acc[idx])
+    assert bits_equal(got, ref), identical_fraction(got, ref)
+    del c0, c1, acc
+    torch.cuda.empty_cache()
