@@ -33,28 +33,34 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0   # MI355X published HBM3E bandwidth
 
-# HBM bytes per adamw_step launch on the Llama-7B shard, from two rocprofv3
-# --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch),
-# each scaled by what the same counter reads for the 4 GiB device copy this
-# script also runs (FETCH_SIZE reads 2,097,194 KiB for it: x2.0; WRITE_SIZE
-# reads 4,194,304 KiB: x1.0).  Valid only for the kernel source it was taken
-# on: the hash covers the kernel file and its header.
+# HBM bytes per adamw_step launch, per shard size (the Llama-7B shard and the
+# 70B ZeRO-3 shard), from two rocprofv3 --pmc runs of this script for that
+# workload (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what
+# the same counter reads for the 4 GiB device copy this script also runs
+# (FETCH_SIZE reads about 2,097,194 KiB for it: x2.0; WRITE_SIZE reads
+# 4,194,304 KiB: x1.0).  Valid only for the kernel source it was taken on: the
+# hash covers the kernel file and its header.
+PMC_SOURCES = ("csrc/adamw.hip", "csrc/zs_common.h")
 PMC_TRAFFIC = {
-    "adamw_step": {"sources": ("csrc/adamw.hip", "csrc/zs_common.h"),
-                   "sha256_16": "1fec0d6ae7b7f2ea", "shard_elems": 842301952,
-                   "fetch_kib": 6580558.7, "fetch_scale": 2.0,
-                   "write_kib": 11515848.1, "write_scale": 1.0},
+    "adamw_step": [
+        {"sha256_16": "1fec0d6ae7b7f2ea", "shard_elems": 842301952,
+         "fetch_kib": 6580558.7, "fetch_scale": 2.0, "write_kib": 11515848.1, "write_scale": 1.0},
+        {"sha256_16": "1fec0d6ae7b7f2ea", "shard_elems": 1093750000,
+         "fetch_kib": 8545004.1, "fetch_scale": 2.0, "write_kib": 14953617.1, "write_scale": 1.0},
+    ],
 }
 
 
 def pmc_traffic(kernel: str, n: int):
-    """Measured HBM bytes per launch, or None if the kernel changed since."""
+    """Measured HBM bytes per launch, or None if there is no record for this
+    shard size or the kernel changed since it was taken."""
     import hashlib
-    rec = PMC_TRAFFIC.get(kernel)
-    if rec is None or rec["shard_elems"] != n:
+    recs = [r for r in PMC_TRAFFIC.get(kernel, []) if r["shard_elems"] == n]
+    if not recs:
         return None
+    rec = recs[0]
     h = hashlib.sha256()
-    for rel in rec["sources"]:
+    for rel in PMC_SOURCES:
         with open(os.path.join(ROOT, "fsdp_sharded_optimizer_amd", rel), "rb") as f:
             h.update(f.read())
     if h.hexdigest()[:16] != rec["sha256_16"]:
