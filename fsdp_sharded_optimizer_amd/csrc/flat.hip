@@ -15,7 +15,8 @@
 //
 // The same walk applies a gathered update (the ZeRO page's _apply_update):
 // each tensor adds the next numel elements of an fp32 flat buffer in place,
-// in one-wave workgroups of 256 (fp32 tensors) or 512 (bf16) elements.
+// in 256-thread workgroups of 1024 (fp32 tensors) or 2048 (bf16) elements,
+// residency capped at 6 per CU.
 //
 // HBM-bound: 4 B/element for bf16 copies, 8 for fp32, 6 for the bf16->fp32
 // widening and the fp32->bf16 re-cast; the apply reads the update and the
@@ -28,12 +29,14 @@ namespace {
 // element types, vector width, groups per lane and workgroup size per kind:
 // 0 f32->f32, 1 bf16->bf16, 2 bf16->f32 (widen), 3 f32->bf16 (re-cast),
 // 4 f32 += f32, 5 bf16 = RNE(widen(bf16) + f32) (apply; S is the update).
-// Every kind runs one-wave workgroups; the bf16 apply takes 8 elements per
-// lane (one 128-bit access to the parameter).  Measured on gfx950 against
-// 256-thread workgroups: the bf16 apply over the 291 Llama-7B tensors in
-// batches of 32 from 64 % to 82 % of the HBM peak, the fp32 apply 81 -> 83 %;
-// over the 70B block's 9 tensors the fp32 copy 81 -> 83.5 %, the bf16 copy
-// 81 -> 83 %.  The conversions (one 64-bit access on their bf16 side) take
+// The copies and conversions run one-wave workgroups (over the 70B block's 9
+// tensors, against 256-thread workgroups: the fp32 copy 81 -> 83.5 % of the
+// HBM peak, the bf16 copy 81 -> 83 %).  The applies run 256-thread
+// workgroups with 24 KiB of LDS reserved (6 per CU): over the 291 Llama-7B
+// tensors in batches of 32, the bf16 apply (8 elements per lane, one 128-bit
+// access to the parameter) 81.6 -> 82.2 % and the fp32 apply 81.3 -> 83.0 %
+// against one-wave workgroups; the cap is sharp (256 threads at 20 / 28 / 32
+// KiB: 80 / 79-81 / 69-75 %; 128 or 512 threads: 71-81 %).  The conversions (one 64-bit access on their bf16 side) take
 // Q = 2 groups of 4 elements per lane, a wave's width (256 elements) apart,
 // both loads issued before either store: the widening pack 74 -> 81 %, the
 // re-casting unpack 76 -> 81 % (Q = 4: 73 / 77 %; one group as 8 contiguous
@@ -48,11 +51,14 @@ template <> struct Kind<0> { using S = float; using D = float; static constexpr 
 template <> struct Kind<1> { using S = uint16_t; using D = uint16_t; static constexpr int VE = 8, Q = 1, BS = 64; };
 template <> struct Kind<2> { using S = uint16_t; using D = float; static constexpr int VE = 4, Q = 2, BS = 64; };
 template <> struct Kind<3> { using S = float; using D = uint16_t; static constexpr int VE = 4, Q = 2, BS = 64; };
-template <> struct Kind<4> { using S = float; using D = float; static constexpr int VE = 4, Q = 1, BS = 64; };
-template <> struct Kind<5> { using S = float; using D = uint16_t; static constexpr int VE = 8, Q = 1, BS = 64; };
+template <> struct Kind<4> { using S = float; using D = float; static constexpr int VE = 4, Q = 1, BS = 256; };
+template <> struct Kind<5> { using S = float; using D = uint16_t; static constexpr int VE = 8, Q = 1, BS = 256; };
 template <int KIND> constexpr int64_t kGroupElems = (int64_t)Kind<KIND>::BS * Kind<KIND>::VE;
 template <int KIND> constexpr int64_t kTileElems = kGroupElems<KIND> * Kind<KIND>::Q;
 constexpr bool is_apply(int kind) { return kind >= 4; }
+// LDS reserved (never touched) per workgroup to cap residency: the applies
+// run 256-thread workgroups, 6 per CU.
+template <int KIND> constexpr unsigned kLdsReserve = is_apply(KIND) ? 24576u : 0u;
 
 template <int KIND>
 __device__ __forceinline__ typename Kind<KIND>::D convert1(typename Kind<KIND>::S x) {
@@ -208,7 +214,8 @@ template <int KIND, bool UNPACK>
 hipError_t launch(const FlatBatch& b, hipStream_t stream) {
     const int64_t blocks = b.tile_start[b.count];
     if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL((flat_kernel<KIND, UNPACK>), dim3((unsigned)blocks), dim3(Kind<KIND>::BS), 0, stream, b);
+    hipLaunchKernelGGL((flat_kernel<KIND, UNPACK>), dim3((unsigned)blocks), dim3(Kind<KIND>::BS), kLdsReserve<KIND>,
+                       stream, b);
     return hipGetLastError();
 }
 
@@ -226,10 +233,10 @@ int64_t flat_tile_elems(int kind) {
 }
 
 int64_t flat_max_batch_tiles(int kind) {
-    static_assert(Kind<0>::BS == 64 && Kind<1>::BS == 64 && Kind<2>::BS == 64 && Kind<3>::BS == 64 &&
-                  Kind<4>::BS == 64 && Kind<5>::BS == 64, "one workgroup size for every kind");
-    (void)kind;
-    return (int64_t)UINT32_MAX / 64;
+    static_assert(Kind<4>::BS == Kind<5>::BS && Kind<0>::BS == Kind<1>::BS && Kind<0>::BS == Kind<2>::BS &&
+                  Kind<0>::BS == Kind<3>::BS, "one workgroup size for the copies, one for the applies");
+    const int64_t bs = is_apply(kind) ? Kind<4>::BS : Kind<0>::BS;
+    return (int64_t)UINT32_MAX / bs;   // workgroups x workgroup size < 2^32 work-items
 }
 
 hipError_t launch_flat(const FlatBatch& b, int kind, int unpack, hipStream_t stream) {
