@@ -31,7 +31,8 @@ namespace {
 // 4 f32 += f32, 5 bf16 = RNE(widen(bf16) + f32) (apply; S is the update).
 // The copies and conversions run one-wave workgroups (over the 70B block's 9
 // tensors, against 256-thread workgroups: the fp32 copy 81 -> 83.5 % of the
-// HBM peak, the bf16 copy 81 -> 83 %).  The applies run 256-thread
+// HBM peak, the bf16 copy 81 -> 83 %; 256-thread workgroups with the applies'
+// residency caps, 20-28 KiB: copies 69-83 %, conversions 51-82 %).  The applies run 256-thread
 // workgroups with 24 KiB of LDS reserved (6 per CU): over the 291 Llama-7B
 // tensors in batches of 32, the bf16 apply (8 elements per lane, one 128-bit
 // access to the parameter) 81.6 -> 82.2 % and the fp32 apply 81.3 -> 83.0 %
