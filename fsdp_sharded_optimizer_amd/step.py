@@ -10,11 +10,15 @@ re-cast.  Nothing here computes; it orders calls.
 ``state_dict`` / ``load_state_dict`` carry the step counter and the fp32
 master, exp_avg and exp_avg_sq between runs: a resumed run continues bit
 for bit (the bf16 parameter is the master's re-cast, rewritten every step).
+``capture`` records one whole step in a HIP graph that replays every later
+step (the AdamW scalars are read from device memory), for shards small
+enough that launch overhead counts.
 """
 from __future__ import annotations
 
 from typing import Optional
 
+import numpy as np
 import torch
 
 from . import _binding as zs
@@ -78,6 +82,16 @@ class ShardOptimizer:
         self._pending = 0
         self._norm_ready = False
 
+    def capture(self, grads: list, extra_norm_sq: float = 0.0) -> "CapturedStep":
+        """Record one whole step (accumulate every tensor of ``grads`` in
+        order, the norm if wanted, AdamW with the bf16 re-cast) into a HIP
+        graph whose AdamW scalars are read from device memory, so the same
+        graph replays every later step.  ``grads`` are fixed device tensors
+        the caller refills with each step's micro-batch gradients before
+        ``replay()``.  Nothing is allocated at replay; the step counter
+        advances on the host and its scalars are copied in by the graph."""
+        return CapturedStep(self, list(grads), extra_norm_sq)
+
     def state_dict(self) -> dict:
         """The optimizer state: the step counter and the fp32 master,
         exp_avg and exp_avg_sq (the live device tensors, not copies)."""
@@ -100,3 +114,68 @@ class ShardOptimizer:
         self.t = t
         self._pending = 0
         self._norm_ready = False
+
+
+class CapturedStep:
+    """One ShardOptimizer step captured in a HIP graph (see
+    ShardOptimizer.capture).  replay() runs the next step: t + 1, with the
+    optimizer's hyperparameters and this capture's extra_norm_sq."""
+
+    def __init__(self, opt: ShardOptimizer, grads: list, extra_norm_sq: float):
+        if not grads:
+            raise ValueError("capture: at least one gradient buffer")
+        self.opt = opt
+        self.grads = grads
+        self.extra_norm_sq = extra_norm_sq
+        dev = opt.master.device
+        nbytes = len(zs.scalars_bytes(zs.AdamWConfig(lr=opt.lr)))
+        self._host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+        self._dev = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self._done = torch.cuda.Event()
+        self._write_scalars(opt.t + 1)
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        # one warm-up run on a side stream, as capture requires; the state it
+        # steps is saved first and restored after, so capturing changes nothing
+        saved = {k: getattr(opt, k).clone() for k in ("master", "exp_avg", "exp_avg_sq")}
+        saved_bf16 = opt.param_bf16.clone() if opt.param_bf16 is not None else None
+        with torch.cuda.stream(side):
+            self._body()
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize(dev)
+        for k, v in saved.items():
+            getattr(opt, k).copy_(v)
+        if saved_bf16 is not None:
+            opt.param_bf16.copy_(saved_bf16)
+        torch.cuda.synchronize(dev)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self._body()
+        opt._pending = 0
+        opt._norm_ready = False
+
+    def _write_scalars(self, t: int) -> None:
+        hp = self.opt.hp(self.extra_norm_sq)
+        hp.step = t
+        self._host.numpy()[:] = np.frombuffer(zs.scalars_bytes(hp), dtype=np.uint8)
+
+    def _body(self) -> None:
+        opt = self.opt
+        last = len(self.grads) - 1
+        for k, g in enumerate(self.grads):
+            if k == last and opt.compute_norm:
+                zs.grad_accum_norm_sq(opt.acc, g, k == 0, opt.grad_scale, opt.norm_sq, opt.workspace)
+            else:
+                zs.grad_accum(opt.acc, g, overwrite=(k == 0))
+        self._dev.copy_(self._host, non_blocking=True)
+        zs.adamw_step_dev(self._dev, opt.master, opt.exp_avg, opt.exp_avg_sq, opt.acc, opt.param_bf16,
+                          norm_sq=opt.norm_sq if opt.compute_norm else None)
+
+    def replay(self) -> None:
+        """Run the next step.  Waits for the previous replay to have read the
+        pinned scalars before rewriting them."""
+        self._done.synchronize()
+        self._write_scalars(self.opt.t + 1)
+        self.graph.replay()
+        self._done.record()
+        self.opt.t += 1

@@ -101,3 +101,36 @@ def test_shard_optimizer_resume_is_bit_identical():
     with pytest.raises(ValueError):
         resumed.load_state_dict({**saved, "exp_avg": saved["exp_avg"][:-1]})
     assert resumed.t == 5 and bits_equal(to_np(resumed.master), before)   # a refused state changes nothing
+
+
+@pytest.mark.parametrize("max_norm", [0.5, 0.0])
+def test_captured_step_replays_like_eager_steps(max_norm):
+    """ShardOptimizer.capture: one graph, replayed for four steps with new
+    gradients each time, bit-identical to the same steps taken eagerly by a
+    twin optimizer (step counter, master, moments, bf16 parameter, norm)."""
+    print(f"ShardOptimizer capture max_norm={max_norm}", flush=True)
+    n, M, scale = 50_003, 3, 1 / 24
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(31)
+    p0 = torch.rand(n, generator=gen, device="cuda") * 0.2 - 0.1
+    kw = dict(lr=3e-4, betas=(0.9, 0.95), weight_decay=0.1, grad_scale=scale, max_norm=max_norm)
+    a = zs.ShardOptimizer(p0.clone(), param_bf16=torch.empty(n, dtype=torch.bfloat16, device="cuda"), **kw)
+    b = zs.ShardOptimizer(p0.clone(), param_bf16=torch.empty(n, dtype=torch.bfloat16, device="cuda"), **kw)
+    grads = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for _ in range(M)]
+    cap = a.capture(grads, extra_norm_sq=0.02)
+    torch.cuda.synchronize()
+    assert a.t == 0 and bits_equal(to_np(a.master), to_np(p0))   # capturing changed nothing
+    for t in range(1, 5):
+        for k, g in enumerate(grads):
+            g.copy_((torch.randn(n, generator=gen, device="cuda") * 1e-2 * (k + t)).to(torch.bfloat16))
+        cap.replay()
+        for k, g in enumerate(grads):
+            b.accumulate(g, last=k == M - 1)
+        b.step(extra_norm_sq=0.02)
+        torch.cuda.synchronize()
+        assert a.t == b.t == t
+        for name in ("master", "exp_avg", "exp_avg_sq", "param_bf16", "acc"):
+            assert bits_equal(to_np(getattr(a, name)), to_np(getattr(b, name))), (t, name)
+        if max_norm > 0:
+            assert a.norm_sq.item() == b.norm_sq.item()
+        _ = (a.acc * 2).sum().item()   # unrelated eager work between replays
