@@ -89,7 +89,10 @@ class ShardOptimizer:
         graph replays every later step.  ``grads`` are fixed device tensors
         the caller refills with each step's micro-batch gradients before
         ``replay()``.  Nothing is allocated at replay; the step counter
-        advances on the host and its scalars are copied in by the graph."""
+        advances on the host and its scalars are copied in by the graph.
+        Capturing runs the step once, as graph capture requires, on the
+        optimizer's state and restores it after, so it briefly holds a copy
+        of the fp32 master and moments (12 B per element)."""
         return CapturedStep(self, list(grads), extra_norm_sq)
 
     def state_dict(self) -> dict:

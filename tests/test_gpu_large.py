@@ -81,6 +81,14 @@ def bf16_normal(n: int, offset: int, std: float, seed: int) -> torch.Tensor:
     return out
 
 
+def need_gib(gib: float):
+    """Skip (on a smaller GPU) when the device has less free memory than a
+    case needs."""
+    free = torch.cuda.mem_get_info()[0] / 2**30
+    if free < gib:
+        pytest.skip(f"needs {gib:.0f} GiB of free device memory, {free:.0f} GiB free")
+
+
 def release():
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -96,6 +104,7 @@ def test_adamw_forms_across_pieces(offset):
     """adamw_step (clipped, bf16 re-cast), then adamw_step_no_master and
     adam_update on the same state, over N elements: bit-exact on the
     sample."""
+    need_gib(45)
     log(f"adamw forms across pieces n={N} offset={offset}")
     idx = sample_indices(N, seed=11 + offset)
     master = fill_uniform(buffer(N, offset), -0.1, 0.1, 101)
@@ -149,6 +158,7 @@ def test_accumulations_across_pieces(offset):
     Q = 1 form; the overwriting bf16 Q = 4 form; the overwriting fp32 form)
     over N elements: acc bit-exact on the sample, the norm within the bar of
     the oracle's over the whole buffer."""
+    need_gib(40)
     log(f"accumulations across pieces n={N} offset={offset}")
     idx = sample_indices(N, seed=21 + offset)
     scale = 1.0 / 32
@@ -191,6 +201,7 @@ def test_accumulations_across_pieces(offset):
 def test_reduce_chunks_across_pieces(offset):
     """Three bf16 rank chunks (the third the first again) summed into acc
     over N elements, overwriting: bit-exact on the sample."""
+    need_gib(25)
     log(f"grad_reduce_chunks across pieces n={N} offset={offset}")
     idx = sample_indices(N, seed=31 + offset)
     acc = buffer(N, offset)
@@ -212,6 +223,7 @@ def test_flat_across_pieces(offset):
     flat_unpack (fp32 -> bf16 re-cast) and flat_apply_update (bf16
     tensors) with a tensor of N elements between two small ones: bit-exact
     on the sample, the padding zero."""
+    need_gib(35)
     log(f"flat across pieces n={N} offset={offset}")
     sizes = [5, N, 7]
     T = sum(sizes)
@@ -259,6 +271,7 @@ def test_adamw_scalar_path_past_2_to_32():
     """The scalar AdamW path (a view one element off: 256-thread workgroups,
     one element per work-item) over 2^32 + 5 elements, four piece boundaries
     and a ragged tail: bit-exact on the sample (about 77 GB of buffers)."""
+    need_gib(85)
     n = (1 << 32) + 5
     log(f"adamw scalar path n={n} offset=1")
     idx = sample_indices(n, seed=51)
