@@ -86,6 +86,12 @@ def _configure(L):
     L.orc_adam_update.restype = ctypes.c_int
     L.orc_flat_apply_update.argtypes = [P, P, P, I32, I32]
     L.orc_flat_apply_update.restype = ctypes.c_int
+    L.orc_state_tiled_numel.argtypes = [I64, I64]
+    L.orc_state_tiled_numel.restype = I64
+    L.orc_state_tile.argtypes = [P, P, P, P, I64, I64]
+    L.orc_state_tile.restype = ctypes.c_int
+    L.orc_state_untile.argtypes = [P, P, P, P, I64, I64]
+    L.orc_state_untile.restype = ctypes.c_int
     L.orc_num_threads.argtypes = []
     L.orc_num_threads.restype = ctypes.c_int
     return L
@@ -286,3 +292,40 @@ def flat_apply_update(update: np.ndarray, dsts, dst_dtype: int) -> None:
                                      ctypes.cast(numel, ctypes.c_void_p), n, dst_dtype)
     if rc != 0:
         raise ValueError("flat_apply_update: invalid arguments")
+
+
+def state_tiled_numel(n: int, tile: int) -> int:
+    """Floats of the tiled optimizer state for n elements (-1 if invalid)."""
+    return int(lib().orc_state_tiled_numel(int(n), int(tile)))
+
+
+def state_tile(master, exp_avg, exp_avg_sq, n: int, tile: int) -> np.ndarray:
+    """The tiled state buffer of three fp32 arrays of n elements (None = zeros)."""
+    srcs = []
+    for a, nm in ((master, "master"), (exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq")):
+        if a is not None:
+            _need(a, np.float32, nm)
+            if a.size != n:
+                raise ValueError(f"state_tile: {nm} size mismatch")
+        srcs.append(a)
+    total = state_tiled_numel(n, tile)
+    if total < 0:
+        raise ValueError("state_tile: invalid arguments")
+    state = np.full(total, np.nan, dtype=np.float32)   # poison: every float must be written
+    rc = lib().orc_state_tile(_ptr(srcs[0]), _ptr(srcs[1]), _ptr(srcs[2]), _ptr(state), int(n), int(tile))
+    if rc != 0:
+        raise ValueError("state_tile: invalid arguments")
+    return state
+
+
+def state_untile(state: np.ndarray, n: int, tile: int):
+    """(master, exp_avg, exp_avg_sq) fp32 arrays of n elements from a tiled state."""
+    _need(state, np.float32, "state")
+    total = state_tiled_numel(n, tile)
+    if total < 0 or state.size < total:
+        raise ValueError("state_untile: state too small or invalid arguments")
+    outs = [np.empty(int(n), dtype=np.float32) for _ in range(3)]
+    rc = lib().orc_state_untile(_ptr(state), _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]), int(n), int(tile))
+    if rc != 0:
+        raise ValueError("state_untile: invalid arguments")
+    return tuple(outs)

@@ -489,6 +489,64 @@ int orc_flat_apply_update(const float* update, void* const* dst, const int64_t* 
     return 0;
 }
 
+/* ------------------------------------------------------------------ */
+/* Tiled optimizer state: a storage layout, not arithmetic.  The pages  */
+/* keep an fp32 master, exp_avg and exp_avg_sq per parameter ([Memory   */
+/* page] "一、显存账本": 4 + 4 + 4 of the 16 B per parameter) and update */
+/* every element on its own ([Memory page] same section; [ZeRO page]    */
+/* §ZeRO-1/2/3 step), so where the three values are stored cannot       */
+/* change any result.  The layout groups the shard in tiles of `tile`   */
+/* elements; tile t holds, one after the other, the master, exp_avg and */
+/* exp_avg_sq of its elements [t*tile, (t+1)*tile).                     */
+/* ------------------------------------------------------------------ */
+/* floats a tiled buffer of n elements occupies: three runs of `tile` per
+ * started tile.  -1 for n < 0 or tile < 1. */
+int64_t orc_state_tiled_numel(int64_t n, int64_t tile)
+{
+    if (n < 0 || tile < 1) return -1;
+    int64_t tiles = n / tile;
+    if (n % tile != 0) tiles += 1;
+    return 3 * tile * tiles;
+}
+
+/* state[(3t + k)*tile + j] = src_k[t*tile + j] for t*tile + j < n, and 0 past
+ * n (the unused end of the last tile).  A NULL src_k stands for zeros.
+ * Returns 0, or -1 for n < 0 or tile < 1. */
+int orc_state_tile(const float* master, const float* exp_avg, const float* exp_avg_sq, float* state,
+                   int64_t n, int64_t tile)
+{
+    int64_t total = orc_state_tiled_numel(n, tile);
+    if (total < 0) return -1;
+    const float* src[3] = {master, exp_avg, exp_avg_sq};
+    int64_t tiles = total / (3 * tile);
+    for (int64_t t = 0; t < tiles; ++t)
+        for (int k = 0; k < 3; ++k)
+            for (int64_t j = 0; j < tile; ++j) {
+                int64_t e = t * tile + j;
+                float x = 0.0f;
+                if (e < n && src[k] != NULL) x = src[k][e];
+                state[(3 * t + k) * tile + j] = x;
+            }
+    return 0;
+}
+
+/* The inverse: dst_k[e] = state[(3*(e / tile) + k)*tile + e % tile] for
+ * e < n; a NULL dst_k is skipped.  Returns 0, or -1 for n < 0 or tile < 1. */
+int orc_state_untile(const float* state, float* master, float* exp_avg, float* exp_avg_sq,
+                     int64_t n, int64_t tile)
+{
+    if (orc_state_tiled_numel(n, tile) < 0) return -1;
+    float* dst[3] = {master, exp_avg, exp_avg_sq};
+    for (int k = 0; k < 3; ++k) {
+        if (dst[k] == NULL) continue;
+        for (int64_t e = 0; e < n; ++e) {
+            int64_t t = e / tile, j = e % tile;
+            dst[k][e] = state[(3 * t + k) * tile + j];
+        }
+    }
+    return 0;
+}
+
 /* Thread count OpenMP will use for the loops above (reported by the
  * CPU-baseline timing). */
 #ifdef _OPENMP

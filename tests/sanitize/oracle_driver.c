@@ -132,6 +132,17 @@ int main(void)
         bad.step = 1;
         CHECK(orc_adamw_step(&bad, p, m, v, acc, b, n, &inf) == 1, 13);   /* non-finite: skipped */
         (void)orc_clip_coef(S, 0.25, 1.0);
+        /* tiled state: exact-size buffer, a tile that divides n and one that does not */
+        for (int64_t tile = 1; tile <= 8; tile += 7) {
+            const int64_t ts = orc_state_tiled_numel(n, tile);
+            CHECK(ts >= 3 * n && ts < 3 * (n + tile), 14);
+            float* st = xmalloc(sizeof(float) * ts);
+            CHECK(orc_state_tile(p, NULL, v, st, n, tile) == 0, 14);
+            CHECK(orc_state_untile(st, p, m, NULL, n, tile) == 0, 14);
+            CHECK(orc_state_tile(p, m, v, st, -1, tile) == -1, 14);
+            CHECK(orc_state_untile(st, p, m, v, n, 0) == -1, 14);
+            free(st);
+        }
         free(acc); free(g32); free(g16); free(p); free(m); free(v); free(u); free(b);
     }
     for (int t = 0; t < count; ++t) {

@@ -764,3 +764,75 @@ def test_zero1_flow_equals_one_buffer_step(orc):
         for r in range(N):
             _, start, end, _ = oracle.shard_range(T, N, r)
             assert np.array_equal(ms[r][:end - start], M[start:end])
+
+
+# ---------------------------------------------------------------------------
+# Tiled optimizer state (a storage layout: the three fp32 values of each
+# element grouped per tile of `tile` elements)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,tile", [(0, 4), (1, 4), (3, 4), (4, 4), (5, 4), (17, 8), (64, 16), (8193, 8192),
+                                    (3 * 8192 - 1, 8192)])
+def test_state_tile_matches_numpy_reshape(orc, n, tile):
+    """Against the layout's definition written with numpy: the buffer viewed
+    as [tiles, 3, tile] holds master, exp_avg, exp_avg_sq of the tile's
+    elements in rows 0, 1, 2; the end of the last tile is zero."""
+    rng = np.random.default_rng(n + tile)
+    p, m, v = (rng.standard_normal(n).astype(np.float32) for _ in range(3))
+    state = oracle.state_tile(p, m, v, n, tile)
+    tiles = -(-n // tile)
+    assert state.size == oracle.state_tiled_numel(n, tile) == 3 * tile * tiles
+    view = state.reshape(tiles, 3, tile)
+    for k, src in enumerate((p, m, v)):
+        stream = view[:, k, :].reshape(-1)
+        assert np.array_equal(stream[:n].view(np.uint32), src.view(np.uint32))
+        assert np.all(stream[n:].view(np.uint32) == 0)
+    back = oracle.state_untile(state, n, tile)
+    for a, b in zip(back, (p, m, v)):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_state_tile_element_positions_brute_force(orc):
+    """Each element's three values sit where the index arithmetic puts them,
+    checked one element at a time on a small buffer with distinct values."""
+    n, tile = 23, 4
+    p = np.arange(n, dtype=np.float32)
+    m = p + 1000
+    v = p + 2000
+    state = oracle.state_tile(p, m, v, n, tile)
+    for e in range(n):
+        t, j = divmod(e, tile)
+        for k, base in enumerate((0, 1000, 2000)):
+            assert state[(3 * t + k) * tile + j] == e + base
+
+
+def test_state_tile_bits_and_missing_sources(orc):
+    """Bit patterns (NaN payloads, -0.0, subnormals, inf) survive the
+    round trip; a missing source tiles as zeros and a missing destination
+    is left alone."""
+    special = np.array([0x80000000, 0x7FC01234, 0xFF800000, 0x00000001, 0x7F7FFFFF, 0x3F800000, 0xFFFFFFFF],
+                       dtype=np.uint32).view(np.float32)
+    n, tile = special.size, 4
+    state = oracle.state_tile(special, None, special[::-1].copy(), n, tile)
+    p, m, v = oracle.state_untile(state, n, tile)
+    assert np.array_equal(p.view(np.uint32), special.view(np.uint32))
+    assert np.all(m.view(np.uint32) == 0)
+    assert np.array_equal(v.view(np.uint32), special[::-1].view(np.uint32))
+    assert oracle.state_tiled_numel(-1, 4) == -1 and oracle.state_tiled_numel(4, 0) == -1
+
+
+def test_state_tile_then_step_equals_step(orc):
+    """The layout changes no result: stepping the untiled arrays equals
+    stepping the arrays read back out of a tiled buffer (the update is
+    element-wise, so a permutation of storage commutes with it)."""
+    rng = np.random.default_rng(9)
+    n, tile = 1000, 64
+    p = rng.uniform(-0.1, 0.1, n).astype(np.float32)
+    m, v = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    g = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    H = hp(lr=3e-4, beta1=0.9, beta2=0.95, wd=0.1, step=1)
+    p2, m2, v2 = oracle.state_untile(oracle.state_tile(p, m, v, n, tile), n, tile)
+    oracle.adamw_step(H, p, m, v, g)
+    oracle.adamw_step(H, p2, m2, v2, g)
+    for a, b in ((p, p2), (m, m2), (v, v2)):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
