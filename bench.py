@@ -9,14 +9,17 @@ input, on one rank's real-size shard (inputs resident in HBM):
   grad_accum_norm_sq for the last one (the accumulation and this shard's
   squared norm in one pass; the norm is formed every step: it feeds the clip
   when the workload clips and the non-finite skip always), and the fused
-  adamw_step with the bf16 re-cast.
+  AdamW step with the bf16 re-cast, on the optimizer state held in the
+  library's tiled layout (adamw_step_tiled, as ShardOptimizer holds it by
+  default).  The same AdamW step on three separate state buffers
+  (adamw_step) is timed after the step on the same evolved state.
 The shard range is host arithmetic done once at set-up.  Default workload:
 the Llama-7B-shaped buffer over 8 ranks, one 842,301,952-element shard,
 8 micro-batches.
 
 Prints ONE JSON line: whole-step throughput (shard elements per second),
-the roofline of the dominant kernel (adamw_step, timed live with HIP events
-on the launch stream) and the CPU oracle timed on a bounded sample.
+the roofline of the dominant kernel (adamw_step_tiled, timed live with HIP
+events on the launch stream) and the CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -42,6 +45,7 @@ HBM_PEAK_GBPS = 8000.0   # MI355X published HBM3E bandwidth
 # hash covers the kernel file and its header.
 PMC_SOURCES = ("csrc/adamw.hip", "csrc/zs_common.h")
 PMC_TRAFFIC = {
+    "adamw_step_tiled": [],
     "adamw_step": [
         {"sha256_16": "1fec0d6ae7b7f2ea", "shard_elems": 842301952,
          "fetch_kib": 6580558.7, "fetch_scale": 2.0, "write_kib": 11515848.1, "write_scale": 1.0},
@@ -192,6 +196,10 @@ def run_gpu(w, steps: int, warmup: int):
     log(f"[bench] workload={w.name} shard_elems={n} micro_batches={w.micro_batches}")
     master = workloads.master_init(w, n, dev)
     param = master.to(torch.bfloat16) if w.bf16_param else None
+    # the step's optimizer state, tiled: master values in, moments zero
+    state = torch.empty(zs.state_tiled_numel(n), dtype=torch.float32, device=dev)
+    zs.state_tile(master, None, None, state)
+    # split buffers: the adamw_step comparison and the no-master variant
     exp_avg = torch.zeros(n, dtype=torch.float32, device=dev)
     exp_avg_sq = torch.zeros(n, dtype=torch.float32, device=dev)
     acc = torch.empty(n, dtype=torch.float32, device=dev)
@@ -206,6 +214,12 @@ def run_gpu(w, steps: int, warmup: int):
     timing = []   # per step: (start, last micro-batch start, adamw start, adamw end)
     last = len(grads) - 1
 
+    def step_hp(t: int):
+        return zs.AdamWConfig(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                              weight_decay=w.weight_decay, grad_scale=w.grad_scale,
+                              max_norm=w.max_norm, extra_norm_sq=workloads.other_ranks_norm_sq(w, 1, n),
+                              step=t)
+
     def one_step(t: int, record: bool):
         e = [ev() for _ in range(4)] if record else None
         if record:
@@ -217,11 +231,7 @@ def run_gpu(w, steps: int, warmup: int):
         zs.grad_accum_norm_sq(acc, grads[last], last == 0, w.grad_scale, norm, ws)
         if record:
             e[2].record()
-        hp = zs.AdamWConfig(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
-                            weight_decay=w.weight_decay, grad_scale=w.grad_scale,
-                            max_norm=w.max_norm, extra_norm_sq=workloads.other_ranks_norm_sq(w, 1, n),
-                            step=t)
-        zs.adamw_step(hp, master, exp_avg, exp_avg_sq, acc, param, norm_sq=norm)
+        zs.adamw_step_tiled(step_hp(t), state, acc, param, norm_sq=norm)
         if record:
             e[3].record()
             timing.append(e)
@@ -265,6 +275,20 @@ def run_gpu(w, steps: int, warmup: int):
     torch.cuda.synchronize()
     graph_ms = g0.elapsed_time(g1) / steps
     del graph
+
+    # outside the step: the same AdamW step on three separate state buffers
+    # (adamw_step), loaded with the tiled state as the timed steps left it so
+    # both layouts stream the same values
+    zs.state_untile(state, master, exp_avg, exp_avg_sq)
+    split_ms = []
+    for k in range(steps):
+        e0, e1 = ev(), ev()
+        e0.record()
+        zs.adamw_step(step_hp(t + 1 + k), master, exp_avg, exp_avg_sq, acc, param, norm_sq=norm)
+        e1.record()
+        split_ms.append((e0, e1))
+    torch.cuda.synchronize()
+    split_ms = sum(a.elapsed_time(b) for a, b in split_ms) / steps
 
     # outside the step: the reduce-scatter's arithmetic on this rank's shard,
     # the same buffers read as N rank chunks, in one pass
@@ -311,8 +335,10 @@ def run_gpu(w, steps: int, warmup: int):
     # same bytes per element and accesses, one addition per stream in place
     # of the update, at several residency caps (run last on these buffers:
     # it changes them)
-    ceiling = {lds: _time_adamw_traffic(master, exp_avg, exp_avg_sq, acc, param, n, lds)
+    ceiling = {lds: _time_adamw_traffic(state, None, None, acc, param, n, lds, tiled=True)
                for lds in CEILING_LDS}
+    ceiling_split = {lds: _time_adamw_traffic(master, exp_avg, exp_avg_sq, acc, param, n, lds)
+                     for lds in CEILING_LDS}
 
     # achievable-bandwidth reference: a plain device copy of 4 GiB (also the
     # calibration kernel for the HBM byte counters)
@@ -330,17 +356,19 @@ def run_gpu(w, steps: int, warmup: int):
     copy_gbps = 2 * src.numel() * 4 / (copy_ms * 1e-3) / 1e9
     del src, dst
     return {"n": n, "wall_s": wall, "accum_ms": acc_ms, "last_ms": last_ms, "adamw_ms": adamw_ms, "graph_ms": graph_ms,
-            "reduce_ms": reduce_ms, "chunks": len(grads), "no_master_ms": no_master_ms,
-            "copy_gbps": copy_gbps, "ceiling_ms": ceiling, "norm_ms": norm_ms}
+            "split_ms": split_ms, "reduce_ms": reduce_ms, "chunks": len(grads), "no_master_ms": no_master_ms,
+            "copy_gbps": copy_gbps, "ceiling_ms": ceiling, "ceiling_split_ms": ceiling_split, "norm_ms": norm_ms}
 
 
-CEILING_LDS = (0, 8192, 12288, 16384, 20480)   # LDS reserved per one-wave workgroup
+CEILING_LDS = (0, 8192, 12288, 14336, 16384, 20480)   # LDS reserved per one-wave workgroup
 
 
-def _time_adamw_traffic(master, exp_avg, exp_avg_sq, grad, bf16, n: int, lds: int, reps: int = 5) -> float:
+def _time_adamw_traffic(master, exp_avg, exp_avg_sq, grad, bf16, n: int, lds: int, reps: int = 5,
+                        tiled: bool = False) -> float:
     """Average launch time of the AdamW-traffic ceiling kernel
     (libzsceiling.so, built next to libzshard.so), each launch bracketed by
-    HIP events on the stream it runs on."""
+    HIP events on the stream it runs on.  tiled: `master` is the tiled state
+    buffer and the kernel walks that layout."""
     import ctypes
     import torch
     from fsdp_sharded_optimizer_amd import build as zbuild
@@ -348,12 +376,19 @@ def _time_adamw_traffic(master, exp_avg, exp_avg_sq, grad, bf16, n: int, lds: in
     if not os.path.exists(zbuild.CEILING_LIB):
         raise RuntimeError(f"{zbuild.CEILING_LIB} is not built: run python -m fsdp_sharded_optimizer_amd.build")
     lib = ctypes.CDLL(zbuild.CEILING_LIB)
-    f = lib.zsc_adamw_traffic
-    f.restype = ctypes.c_int32
-    f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]
     stream = torch.cuda.current_stream()
-    args = [master.data_ptr(), exp_avg.data_ptr(), exp_avg_sq.data_ptr(), grad.data_ptr(),
-            bf16.data_ptr() if bf16 is not None else None, n, lds, stream.cuda_stream]
+    bptr = bf16.data_ptr() if bf16 is not None else None
+    if tiled:
+        f = lib.zsc_adamw_traffic_tiled
+        f.restype = ctypes.c_int32
+        f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]
+        args = [master.data_ptr(), grad.data_ptr(), bptr, n, lds, stream.cuda_stream]
+    else:
+        f = lib.zsc_adamw_traffic
+        f.restype = ctypes.c_int32
+        f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]
+        args = [master.data_ptr(), exp_avg.data_ptr(), exp_avg_sq.data_ptr(), grad.data_ptr(), bptr, n, lds,
+                stream.cuda_stream]
     events = []
     for k in range(reps + 1):
         e0, e1 = DeviceEvent(), DeviceEvent()
@@ -603,20 +638,25 @@ def main():
         "data": "synthetic (seeded U(-0.1,0.1) master, N(0,std) bf16 micro-batch grads)",
         "config": {"workload": w.name, "shard_elems": n, "total_params": w.total, "world": w.world,
                    "rank": w.rank, "micro_batches": w.micro_batches, "grad_dtype": w.grad_dtype,
-                   "state": "fp32 master/exp_avg/exp_avg_sq + bf16 param", "clip": w.max_norm > 0},
+                   "state": "fp32 master/exp_avg/exp_avg_sq (tiled layout) + bf16 param", "clip": w.max_norm > 0},
         "graph_ms_per_step": r["graph_ms"],
         "step_hbm_gbps": step_gbps,
         "step_hbm_frac": step_gbps / HBM_PEAK_GBPS,
         "kernels_ms": {"grad_accum_all_but_last": r["accum_ms"], "grad_accum_norm_sq_last": r["last_ms"],
-                       "adamw_step": r["adamw_ms"]},
+                       "adamw_step_tiled": r["adamw_ms"]},
         "bytes_per_elem": bpe,
         "device_copy_gbps": r["copy_gbps"],
         "timing_events": timing_events(),
         "adamw_traffic_ceiling": ceiling_report(r["ceiling_ms"], adamw_bytes, r["adamw_ms"]),
-        "roofline": {"kernel": "adamw_step", "bound": "hbm", "achieved": achieved,
+        "roofline": {"kernel": "adamw_step_tiled", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": pmc_traffic("adamw_step", n), "traffic_unit": "bytes/launch",
+                     "traffic": pmc_traffic("adamw_step_tiled", n), "traffic_unit": "bytes/launch",
                      "algorithmic_bytes": adamw_bytes, "launch_ms": r["adamw_ms"]},
+        "adamw_step_split": {
+            "ms": r["split_ms"], "bytes_per_elem": bpe["adamw_step"],
+            "gbps": adamw_bytes / (r["split_ms"] * 1e-3) / 1e9,
+            "frac": adamw_bytes / (r["split_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "traffic_ceiling": ceiling_report(r["ceiling_split_ms"], adamw_bytes, r["split_ms"])},
         "cpu_baseline": cpu,
         "flat_unit": flat,
         "zero1_flow": zero1,

@@ -15,6 +15,11 @@ The Python names mirror the C ABI in include/zshard.h:
     adamw_step_no_master(hp, param_bf16, exp_avg, exp_avg_sq, grad, norm_sq=None)
     adam_update(hp, exp_avg, exp_avg_sq, grad, update, norm_sq=None)
     flat_apply_update(update, dst_tensors)
+    state_tiled_numel(n)                        floats of the tiled optimizer state
+    state_tile(master, exp_avg, exp_avg_sq, state, n=None)     split -> tiled (None sources: zeros)
+    state_untile(state, master, exp_avg, exp_avg_sq, n=None)   tiled -> split (None: skipped)
+    adamw_step_tiled(hp, state, grad, param_bf16=None, norm_sq=None)
+    adamw_step_tiled_dev(scalars_dev, state, grad, param_bf16=None, norm_sq=None)
 
 All device work runs in the library's gfx950 HIP kernels on the current
 torch stream; torch supplies device memory and the stream only.
@@ -22,6 +27,7 @@ torch stream; torch supplies device memory and the stream only.
 from ._binding import (  # noqa: F401
     EXPORTS,
     LIB_PATH,
+    STATE_TILE,
     AdamWConfig,
     ZShardError,
     AdamWScalars,
@@ -30,6 +36,8 @@ from ._binding import (  # noqa: F401
     adamw_step,
     adamw_step_dev,
     adamw_step_no_master,
+    adamw_step_tiled,
+    adamw_step_tiled_dev,
     flat_apply_update,
     flat_pack,
     flat_unpack,
@@ -41,6 +49,9 @@ from ._binding import (  # noqa: F401
     grad_norm_sq_workspace_bytes,
     lib,
     scalars_bytes,
+    state_tile,
+    state_tiled_numel,
+    state_untile,
     zero_shard_range,
 )
 from .step import ShardOptimizer  # noqa: F401

@@ -30,9 +30,12 @@ EXPORTS = (
     "zero_shard_range", "flat_pack", "flat_unpack", "grad_accum", "grad_reduce_chunks",
     "grad_norm_sq_workspace_bytes", "grad_norm_sq", "grad_accum_norm_sq_workspace_bytes",
     "grad_accum_norm_sq", "adamw_step", "adamw_scalars", "adamw_step_dev", "adamw_step_no_master", "adam_update",
-    "flat_apply_update",
+    "flat_apply_update", "state_tiled_numel", "state_tile", "state_untile", "adamw_step_tiled",
+    "adamw_step_tiled_dev",
     "zs_strerror", "zs_last_hip_error",
 )
+
+STATE_TILE = 8192   # ZS_STATE_TILE: elements per tile of the tiled optimizer state
 
 
 class ZShardError(RuntimeError):
@@ -131,6 +134,16 @@ def lib() -> ctypes.CDLL:
         L.adam_update.restype = I32
         L.flat_apply_update.argtypes = [P, ctypes.POINTER(Tensor), I32, I32, P]
         L.flat_apply_update.restype = I32
+        L.state_tiled_numel.argtypes = [I64]
+        L.state_tiled_numel.restype = I64
+        L.state_tile.argtypes = [P, P, P, P, I64, P]
+        L.state_tile.restype = I32
+        L.state_untile.argtypes = [P, P, P, P, I64, P]
+        L.state_untile.restype = I32
+        L.adamw_step_tiled.argtypes = [ctypes.POINTER(AdamW), P, P, P, I64, P, P]
+        L.adamw_step_tiled.restype = I32
+        L.adamw_step_tiled_dev.argtypes = [P, P, P, P, I64, P, P]
+        L.adamw_step_tiled_dev.restype = I32
         L.zs_strerror.argtypes = [I32]
         L.zs_strerror.restype = ctypes.c_char_p
         L.zs_last_hip_error.argtypes = []
@@ -399,3 +412,83 @@ def adam_update(hp: AdamWConfig, exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor
         ctypes.byref(c), _dev(exp_avg, "exp_avg", torch.float32), _dev(exp_avg_sq, "exp_avg_sq", torch.float32),
         _dev(grad, "grad", torch.float32), _dev(update, "update", torch.float32), n,
         _norm(norm_sq, "adam_update"), _stream(stream)))
+
+
+def state_tiled_numel(n: int) -> int:
+    """Floats of the tiled optimizer state of n elements (host only)."""
+    out = int(lib().state_tiled_numel(int(n)))
+    if out < 0:
+        raise ValueError(f"state_tiled_numel: invalid element count {n}")
+    return out
+
+
+def _state_buffer(state: torch.Tensor, n: int, fn: str) -> int:
+    if state.numel() < state_tiled_numel(n):
+        raise ValueError(f"{fn}: state holds {state.numel()} floats, the tiled layout of {n} elements needs "
+                         f"{state_tiled_numel(n)}")
+    return _dev(state, "state", torch.float32)
+
+
+def state_tile(master: Optional[torch.Tensor], exp_avg: Optional[torch.Tensor], exp_avg_sq: Optional[torch.Tensor],
+               state: torch.Tensor, n: Optional[int] = None, stream=None) -> None:
+    """Split fp32 arrays (None = zeros) into the tiled state buffer."""
+    srcs = (master, exp_avg, exp_avg_sq)
+    if n is None:
+        n = next((t.numel() for t in srcs if t is not None), None)
+        if n is None:
+            raise ValueError("state_tile: give n when every source is None")
+    for t, nm in zip(srcs, ("master", "exp_avg", "exp_avg_sq")):
+        if t is not None and t.numel() != n:
+            raise ValueError(f"state_tile: {nm} size mismatch")
+    _check("state_tile", lib().state_tile(
+        _dev(master, "master", torch.float32), _dev(exp_avg, "exp_avg", torch.float32),
+        _dev(exp_avg_sq, "exp_avg_sq", torch.float32), _state_buffer(state, n, "state_tile"), int(n),
+        _stream(stream)))
+
+
+def state_untile(state: torch.Tensor, master: Optional[torch.Tensor], exp_avg: Optional[torch.Tensor],
+                 exp_avg_sq: Optional[torch.Tensor], n: Optional[int] = None, stream=None) -> None:
+    """The tiled state back into split fp32 arrays (None = that stream skipped)."""
+    dsts = (master, exp_avg, exp_avg_sq)
+    if n is None:
+        n = next((t.numel() for t in dsts if t is not None), None)
+        if n is None:
+            raise ValueError("state_untile: give n when every destination is None")
+    for t, nm in zip(dsts, ("master", "exp_avg", "exp_avg_sq")):
+        if t is not None and t.numel() != n:
+            raise ValueError(f"state_untile: {nm} size mismatch")
+    _check("state_untile", lib().state_untile(
+        _state_buffer(state, n, "state_untile"), _dev(master, "master", torch.float32),
+        _dev(exp_avg, "exp_avg", torch.float32), _dev(exp_avg_sq, "exp_avg_sq", torch.float32), int(n),
+        _stream(stream)))
+
+
+def adamw_step_tiled(hp: AdamWConfig, state: torch.Tensor, grad: torch.Tensor,
+                     param_bf16: Optional[torch.Tensor] = None, norm_sq: Optional[torch.Tensor] = None,
+                     stream=None) -> None:
+    """Fused AdamW update of the shard held in the tiled state layout (in
+    place), with the bf16 re-cast; n is the gradient's length."""
+    n = grad.numel()
+    if param_bf16 is not None and param_bf16.numel() != n:
+        raise ValueError("adamw_step_tiled: param_bf16 size mismatch")
+    c = hp.c_struct()
+    _check("adamw_step_tiled", lib().adamw_step_tiled(
+        ctypes.byref(c), _state_buffer(state, n, "adamw_step_tiled"), _dev(grad, "grad", torch.float32),
+        _dev(param_bf16, "param_bf16", torch.bfloat16), n, _norm(norm_sq, "adamw_step_tiled"), _stream(stream)))
+
+
+def adamw_step_tiled_dev(scalars_dev: torch.Tensor, state: torch.Tensor, grad: torch.Tensor,
+                         param_bf16: Optional[torch.Tensor] = None, norm_sq: Optional[torch.Tensor] = None,
+                         stream=None) -> None:
+    """adamw_step_tiled with its scalars read from device memory when the
+    kernels run (scalars_dev: uint8 GPU tensor holding scalars_bytes(hp))."""
+    if scalars_dev.dtype != torch.uint8 or scalars_dev.numel() < ctypes.sizeof(AdamWScalars):
+        raise TypeError("adamw_step_tiled_dev: scalars_dev must be a uint8 tensor of at least "
+                        f"{ctypes.sizeof(AdamWScalars)} bytes")
+    n = grad.numel()
+    if param_bf16 is not None and param_bf16.numel() != n:
+        raise ValueError("adamw_step_tiled_dev: param_bf16 size mismatch")
+    _check("adamw_step_tiled_dev", lib().adamw_step_tiled_dev(
+        _dev(scalars_dev, "scalars_dev"), _state_buffer(state, n, "adamw_step_tiled_dev"),
+        _dev(grad, "grad", torch.float32), _dev(param_bf16, "param_bf16", torch.bfloat16), n,
+        _norm(norm_sq, "adamw_step_tiled_dev"), _stream(stream)))

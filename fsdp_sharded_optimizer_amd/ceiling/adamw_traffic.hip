@@ -22,6 +22,14 @@
 // 16-byte aligned and grad 4-byte aligned; lds_bytes in [0, 65536].
 // Returns 0, -1 for a bad argument (nothing launched), or the hipError_t of
 // the launch.
+//
+//   int32_t zsc_adamw_traffic_tiled(float* state, const float* grad,
+//                                   uint16_t* bf16_or_null, int64_t n,
+//                                   int32_t lds_bytes, void* hip_stream)
+// The same traffic on libzshard's tiled state layout (per tile of 8192
+// elements: the masters, then the exp_avgs, then the exp_avg_sqs, 8192 floats
+// each), the reference for adamw_step_tiled.  state: 16-byte aligned, at
+// least 3 * 8192 * ceil(n / 8192) floats.
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
@@ -32,23 +40,34 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
 constexpr int kBlock = 64;
+constexpr int64_t kTile = 8192;   // libzshard's ZS_STATE_TILE
 
-template <bool BF16>
+// TILED: p is the tiled state (m and v unused); element i's three values sit
+// at tile_base + (i mod kTile) + {0, 1, 2} * kTile.
+template <bool BF16, bool TILED>
 __global__ __launch_bounds__(kBlock) void adamw_traffic_kernel(float* __restrict__ p, float* __restrict__ m,
                                                                float* __restrict__ v, const float* __restrict__ g,
                                                                uint16_t* __restrict__ b, int64_t n) {
     const int64_t first = ((int64_t)blockIdx.x * kBlock + threadIdx.x) * 4;
     if (first + 4 <= n) {
+        float* pp = p + first;
+        float* mp = TILED ? nullptr : m + first;
+        float* vp = TILED ? nullptr : v + first;
+        if (TILED) {
+            pp = p + (first / kTile) * (3 * kTile) + first % kTile;
+            mp = pp + kTile;
+            vp = pp + 2 * kTile;
+        }
         const f32x4 g4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4_a4*>(g + first));
-        f32x4 p4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + first));
-        f32x4 m4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(m + first));
-        f32x4 v4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(v + first));
+        f32x4 p4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(pp));
+        f32x4 m4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(mp));
+        f32x4 v4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(vp));
         p4 += g4;
         m4 += g4;
         v4 += g4;
-        __builtin_nontemporal_store(p4, reinterpret_cast<f32x4*>(p + first));
-        __builtin_nontemporal_store(m4, reinterpret_cast<f32x4*>(m + first));
-        __builtin_nontemporal_store(v4, reinterpret_cast<f32x4*>(v + first));
+        __builtin_nontemporal_store(p4, reinterpret_cast<f32x4*>(pp));
+        __builtin_nontemporal_store(m4, reinterpret_cast<f32x4*>(mp));
+        __builtin_nontemporal_store(v4, reinterpret_cast<f32x4*>(vp));
         if (BF16) {
             const uint32_t w0 = (__float_as_uint(p4.x) >> 16) | (__float_as_uint(p4.y) & 0xFFFF0000u);
             const uint32_t w1 = (__float_as_uint(p4.z) >> 16) | (__float_as_uint(p4.w) & 0xFFFF0000u);
@@ -57,10 +76,18 @@ __global__ __launch_bounds__(kBlock) void adamw_traffic_kernel(float* __restrict
         return;
     }
     for (int64_t i = first; i < n; ++i) {
-        p[i] += g[i];
-        m[i] += g[i];
-        v[i] += g[i];
-        if (BF16) b[i] = (uint16_t)(__float_as_uint(p[i]) >> 16);
+        float* pi = p + i;
+        float* mi = TILED ? nullptr : m + i;
+        float* vi = TILED ? nullptr : v + i;
+        if (TILED) {
+            pi = p + (i / kTile) * (3 * kTile) + i % kTile;
+            mi = pi + kTile;
+            vi = pi + 2 * kTile;
+        }
+        *pi += g[i];
+        *mi += g[i];
+        *vi += g[i];
+        if (BF16) b[i] = (uint16_t)(__float_as_uint(*pi) >> 16);
     }
 }
 
@@ -81,10 +108,27 @@ extern "C" __attribute__((visibility("default"))) int32_t zsc_adamw_traffic(
     if (blocks > (int64_t)UINT32_MAX) return -1;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     if (bf16)
-        hipLaunchKernelGGL(adamw_traffic_kernel<true>, dim3((unsigned)blocks), dim3(kBlock), (unsigned)lds_bytes, s, master,
-                           exp_avg, exp_avg_sq, grad, bf16, n);
+        hipLaunchKernelGGL((adamw_traffic_kernel<true, false>), dim3((unsigned)blocks), dim3(kBlock), (unsigned)lds_bytes,
+                           s, master, exp_avg, exp_avg_sq, grad, bf16, n);
     else
-        hipLaunchKernelGGL(adamw_traffic_kernel<false>, dim3((unsigned)blocks), dim3(kBlock), (unsigned)lds_bytes, s, master,
-                           exp_avg, exp_avg_sq, grad, bf16, n);
+        hipLaunchKernelGGL((adamw_traffic_kernel<false, false>), dim3((unsigned)blocks), dim3(kBlock), (unsigned)lds_bytes,
+                           s, master, exp_avg, exp_avg_sq, grad, bf16, n);
+    return (int32_t)hipGetLastError();
+}
+
+extern "C" __attribute__((visibility("default"))) int32_t zsc_adamw_traffic_tiled(
+        float* state, const float* grad, uint16_t* bf16, int64_t n, int32_t lds_bytes, void* hip_stream) {
+    if (n < 0 || (int64_t)1 << 31 < n || lds_bytes < 0 || lds_bytes > 65536) return -1;
+    if (n == 0) return 0;
+    if (!state || !grad) return -1;
+    if (!aligned(state, 16) || !aligned(grad, 4) || (bf16 && !aligned(bf16, 16))) return -1;
+    const int64_t blocks = (n + 4 * kBlock - 1) / (4 * kBlock);
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    if (bf16)
+        hipLaunchKernelGGL((adamw_traffic_kernel<true, true>), dim3((unsigned)blocks), dim3(kBlock), (unsigned)lds_bytes,
+                           s, state, nullptr, nullptr, grad, bf16, n);
+    else
+        hipLaunchKernelGGL((adamw_traffic_kernel<false, true>), dim3((unsigned)blocks), dim3(kBlock), (unsigned)lds_bytes,
+                           s, state, nullptr, nullptr, grad, bf16, n);
     return (int32_t)hipGetLastError();
 }

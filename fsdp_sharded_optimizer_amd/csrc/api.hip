@@ -304,6 +304,103 @@ int32_t adamw_step_dev(const zs_adamw_scalars* scalars_dev, float* master, float
                         hip_stream);
 }
 
+// ---------------------------------------------------------------------------
+// tiled optimizer state
+// ---------------------------------------------------------------------------
+
+static_assert(ZS_STATE_TILE == zs::kStateTile, "tile length of the header and the kernels");
+
+int64_t state_tiled_numel(int64_t n) {
+    if (!size_ok(n)) return -1;
+    return 3 * ((n + zs::kStateTile - 1) / zs::kStateTile) * zs::kStateTile;
+}
+
+int32_t state_tile(const float* master, const float* exp_avg, const float* exp_avg_sq, float* state, int64_t n,
+                   void* hip_stream) {
+    if (!size_ok(n)) return ZS_EINVAL;
+    if (n == 0) return ZS_OK;
+    if (state == nullptr || !aligned(state, 16)) return ZS_EINVAL;
+    const float* src[3] = {master, exp_avg, exp_avg_sq};
+    const int64_t state_bytes = state_tiled_numel(n) * 4;
+    for (int k = 0; k < 3; ++k) {
+        if (src[k] != nullptr && !aligned(src[k], 4)) return ZS_EINVAL;
+        if (overlap(src[k], src[k] ? n * 4 : 0, state, state_bytes)) return ZS_EOVERLAP;
+    }
+    return hip_status(zs::launch_state_tile(src, state, n, as_stream(hip_stream)));
+}
+
+int32_t state_untile(const float* state, float* master, float* exp_avg, float* exp_avg_sq, int64_t n,
+                     void* hip_stream) {
+    if (!size_ok(n)) return ZS_EINVAL;
+    if (n == 0) return ZS_OK;
+    if (state == nullptr || !aligned(state, 16)) return ZS_EINVAL;
+    float* dst[3] = {master, exp_avg, exp_avg_sq};
+    const int64_t state_bytes = state_tiled_numel(n) * 4;
+    bool vec = true;
+    for (int k = 0; k < 3; ++k) {
+        if (dst[k] == nullptr) continue;
+        if (!aligned(dst[k], 4)) return ZS_EINVAL;
+        if (overlap(dst[k], n * 4, state, state_bytes)) return ZS_EOVERLAP;
+        for (int j = k + 1; j < 3; ++j)
+            if (dst[j] != nullptr && overlap(dst[k], n * 4, dst[j], n * 4)) return ZS_EOVERLAP;
+        vec = vec && aligned(dst[k], 16);
+    }
+    return hip_status(zs::launch_state_untile(state, dst, n, vec, as_stream(hip_stream)));
+}
+
+// the tiled master-form step: host scalars (hp) or a device copy of them (sc_dev)
+static int32_t adamw_tiled(const zs_adamw* hp, const zs_adamw_scalars* sc_dev, float* state, const float* grad,
+                           uint16_t* param_bf16, int64_t n, const double* norm_sq_dev, void* hip_stream) {
+    int32_t rc;
+    if (sc_dev == nullptr) {
+        rc = adamw_check_hp(hp, n, norm_sq_dev);
+        if (rc != ZS_OK) return rc;
+    } else {
+        if (!size_ok(n) || !aligned(sc_dev, 8)) return ZS_EINVAL;
+        if (norm_sq_dev != nullptr && !aligned(norm_sq_dev, 8)) return ZS_EINVAL;
+    }
+    if (n == 0) return ZS_OK;
+    if (state == nullptr || grad == nullptr) return ZS_EINVAL;
+    if (!aligned(state, 16) || !aligned(grad, 4) || (param_bf16 != nullptr && !aligned(param_bf16, 2)))
+        return ZS_EINVAL;
+    const void* bufs[5] = {state, grad, param_bf16, nullptr, nullptr};
+    const int64_t bytes[5] = {state_tiled_numel(n) * 4, n * 4, param_bf16 ? n * 2 : 0, 0, 0};
+    const bool written[5] = {true, false, true, false, false};
+    rc = adamw_check_overlap(bufs, bytes, written, norm_sq_dev);
+    if (rc != ZS_OK) return rc;
+    if (sc_dev != nullptr)   // the scalars are read while the buffers are written
+        for (int i = 0; i < 5; ++i)
+            if (written[i] && overlap(bufs[i], bytes[i], sc_dev, (int64_t)sizeof(zs_adamw_scalars)))
+                return ZS_EOVERLAP;
+    zs::AdamwArgs a;
+    if (sc_dev == nullptr) {
+        a = make_args(hp, norm_sq_dev);
+    } else {
+        std::memset(&a, 0, sizeof(a));
+        a.sc_dev = reinterpret_cast<const zs::AdamwScalars*>(sc_dev);
+        a.norm_sq = norm_sq_dev;
+    }
+    a.state = state;
+    a.grad = grad;
+    a.param_bf16 = param_bf16;
+    a.n = n;
+    // the state is 16-byte aligned by contract; the bf16 output decides the path
+    const bool vec = param_bf16 == nullptr || aligned(param_bf16, 16);
+    return hip_status(zs::launch_adamw_tiled(a, vec, as_stream(hip_stream)));
+}
+
+int32_t adamw_step_tiled(const zs_adamw* hp, float* state, const float* grad, uint16_t* param_bf16, int64_t n,
+                         const double* norm_sq_dev, void* hip_stream) {
+    if (hp == nullptr) return ZS_EINVAL;
+    return adamw_tiled(hp, nullptr, state, grad, param_bf16, n, norm_sq_dev, hip_stream);
+}
+
+int32_t adamw_step_tiled_dev(const zs_adamw_scalars* scalars_dev, float* state, const float* grad,
+                             uint16_t* param_bf16, int64_t n, const double* norm_sq_dev, void* hip_stream) {
+    if (scalars_dev == nullptr) return ZS_EINVAL;
+    return adamw_tiled(nullptr, scalars_dev, state, grad, param_bf16, n, norm_sq_dev, hip_stream);
+}
+
 int32_t adamw_step_no_master(const zs_adamw* hp, uint16_t* param_bf16, float* exp_avg, float* exp_avg_sq,
                              const float* grad, int64_t n, const double* norm_sq_dev, void* hip_stream) {
     int32_t rc = adamw_check_hp(hp, n, norm_sq_dev);

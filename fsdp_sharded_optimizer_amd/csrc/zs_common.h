@@ -76,10 +76,24 @@ struct AdamwScalars {
     double extra_norm_sq;
 };
 
+// --- tiled optimizer state ------------------------------------------------
+// The fp32 master, exp_avg and exp_avg_sq of a shard in one buffer: for each
+// tile of kStateTile elements, the tile's masters, then its exp_avgs, then its
+// exp_avg_sqs, each a run of kStateTile floats (the last tile keeps full-length
+// runs; its unused ends are padding).  Element i's master sits at
+// tiled_offset(i), its exp_avg kStateTile floats later, its exp_avg_sq
+// 2*kStateTile later.  Equal to ZS_STATE_TILE in zshard.h (checked in api.hip).
+constexpr int64_t kStateTile = 8192;
+__host__ __device__ __forceinline__ int64_t tiled_offset(int64_t i) {
+    const uint64_t u = (uint64_t)i;
+    return (int64_t)((u / kStateTile) * (3 * kStateTile) + (u % kStateTile));
+}
+
 struct AdamwArgs {
     AdamwScalars sc;            // in the kernel arguments, unless sc_dev is set
     const AdamwScalars* sc_dev; // device copy of the scalars (a step replayable from a graph), nullable
     const double* norm_sq;      // device, nullable
+    float* state;               // tiled form: master, exp_avg, exp_avg_sq in the tiled layout
     float* master;
     float* exp_avg;
     float* exp_avg_sq;
@@ -103,6 +117,12 @@ inline int64_t launch_piece(int64_t n, int64_t off) { return n - off < kLaunchEl
 hipError_t launch_adamw(const AdamwArgs& a, bool vec_ok, hipStream_t stream);
 hipError_t launch_adamw_no_master(const AdamwArgs& a, bool vec_ok, hipStream_t stream);
 hipError_t launch_adam_update(const AdamwArgs& a, bool vec_ok, hipStream_t stream);
+hipError_t launch_adamw_tiled(const AdamwArgs& a, bool vec_ok, hipStream_t stream);
+// split fp32 arrays (each nullable: zeros) -> tiled state, padding zeroed; and back
+// (each destination nullable: skipped)
+hipError_t launch_state_tile(const float* const src[3], float* state, int64_t n, hipStream_t stream);
+hipError_t launch_state_untile(const float* state, float* const dst[3], int64_t n, bool vec_ok,
+                               hipStream_t stream);
 hipError_t launch_grad_accum(float* acc, const void* grad, int grad_bf16, int64_t n,
                              int overwrite, bool vec_ok, hipStream_t stream);
 int64_t norm_partials(int64_t n);   // grad_norm_sq's stage-1 partials for n elements

@@ -7,6 +7,14 @@ may form the squared norm in the same pass), then ``step``: the norm (if
 not formed yet and requested) and the fused AdamW update with the bf16
 re-cast.  Nothing here computes; it orders calls.
 
+``layout="tiled"`` (the default) keeps master, exp_avg and exp_avg_sq in
+one buffer in the library's tiled state layout, which the AdamW step
+streams faster than three buffers; the ``master``, ``exp_avg`` and
+``exp_avg_sq`` attributes then read fresh split copies back out of it, and
+the caller's master tensor only supplies the initial values.
+``layout="split"`` steps the caller's master tensor and two moment buffers
+in place.  Both layouts give bit-identical results.
+
 ``state_dict`` / ``load_state_dict`` carry the step counter and the fp32
 master, exp_avg and exp_avg_sq between runs: a resumed run continues bit
 for bit (the bf16 parameter is the master's re-cast, rewritten every step).
@@ -24,17 +32,31 @@ import torch
 from . import _binding as zs
 
 
+_STATE_NAMES = ("master", "exp_avg", "exp_avg_sq")
+
+
 class ShardOptimizer:
     def __init__(self, master: torch.Tensor, *, lr: float, betas=(0.9, 0.999), eps: float = 1e-8,
                  weight_decay: float = 0.0, grad_scale: float = 1.0, max_norm: float = 0.0,
-                 param_bf16: Optional[torch.Tensor] = None, compute_norm: Optional[bool] = None):
+                 param_bf16: Optional[torch.Tensor] = None, compute_norm: Optional[bool] = None,
+                 layout: str = "tiled"):
         if master.dtype != torch.float32 or master.device.type != "cuda":
             raise TypeError("master must be an fp32 GPU tensor")
+        if layout not in ("tiled", "split"):
+            raise ValueError("layout must be 'tiled' or 'split'")
         n = master.numel()
         dev = master.device
-        self.master = master
-        self.exp_avg = torch.zeros(n, dtype=torch.float32, device=dev)
-        self.exp_avg_sq = torch.zeros(n, dtype=torch.float32, device=dev)
+        self.n = n
+        self.layout = layout
+        if layout == "tiled":
+            # the master's values go into the tiled buffer; the moments start at zero
+            self.state = torch.empty(zs.state_tiled_numel(n), dtype=torch.float32, device=dev)
+            zs.state_tile(master.reshape(-1), None, None, self.state, n=n)
+            self._split = None
+        else:
+            self.state = None
+            self._split = {"master": master, "exp_avg": torch.zeros(n, dtype=torch.float32, device=dev),
+                           "exp_avg_sq": torch.zeros(n, dtype=torch.float32, device=dev)}
         self.acc = torch.empty(n, dtype=torch.float32, device=dev)
         self.param_bf16 = param_bf16
         self.lr, self.betas, self.eps = lr, betas, eps
@@ -46,6 +68,50 @@ class ShardOptimizer:
         self._norm_ready = False
         self.t = 0
         self._pending = 0
+
+    def _state_tensor(self, name: str) -> torch.Tensor:
+        if self._split is not None:
+            return self._split[name]
+        out = torch.empty(self.n, dtype=torch.float32, device=self.acc.device)
+        dst = [out if k == name else None for k in _STATE_NAMES]
+        zs.state_untile(self.state, *dst, n=self.n)
+        return out
+
+    # split layout: the live buffers; tiled layout: fresh copies read out of the tiled state
+    master = property(lambda self: self._state_tensor("master"))
+    exp_avg = property(lambda self: self._state_tensor("exp_avg"))
+    exp_avg_sq = property(lambda self: self._state_tensor("exp_avg_sq"))
+
+    def _adamw(self, hp: zs.AdamWConfig, norm) -> None:
+        if self._split is not None:
+            zs.adamw_step(hp, self._split["master"], self._split["exp_avg"], self._split["exp_avg_sq"], self.acc,
+                          self.param_bf16, norm_sq=norm)
+        else:
+            zs.adamw_step_tiled(hp, self.state, self.acc, self.param_bf16, norm_sq=norm)
+
+    def _adamw_dev(self, scalars_dev: torch.Tensor, norm) -> None:
+        if self._split is not None:
+            zs.adamw_step_dev(scalars_dev, self._split["master"], self._split["exp_avg"], self._split["exp_avg_sq"],
+                              self.acc, self.param_bf16, norm_sq=norm)
+        else:
+            zs.adamw_step_tiled_dev(scalars_dev, self.state, self.acc, self.param_bf16, norm_sq=norm)
+
+    def _save(self) -> dict:
+        """Device copies of the optimizer state (and bf16 parameter)."""
+        saved = {"state": self.state.clone()} if self._split is None else \
+            {k: v.clone() for k, v in self._split.items()}
+        if self.param_bf16 is not None:
+            saved["param_bf16"] = self.param_bf16.clone()
+        return saved
+
+    def _restore(self, saved: dict) -> None:
+        if self._split is None:
+            self.state.copy_(saved["state"])
+        else:
+            for k in _STATE_NAMES:
+                self._split[k].copy_(saved[k])
+        if self.param_bf16 is not None:
+            self.param_bf16.copy_(saved["param_bf16"])
 
     def accumulate(self, grad: torch.Tensor, last: bool = False) -> None:
         """Add one micro-batch gradient (fp32 or bf16) into the fp32 buffer.
@@ -77,7 +143,7 @@ class ShardOptimizer:
             norm = self.norm_sq
         hp = self.hp(extra_norm_sq)
         hp.step = self.t + 1
-        zs.adamw_step(hp, self.master, self.exp_avg, self.exp_avg_sq, self.acc, self.param_bf16, norm_sq=norm)
+        self._adamw(hp, norm)
         self.t += 1
         self._pending = 0
         self._norm_ready = False
@@ -92,28 +158,35 @@ class ShardOptimizer:
         advances on the host and its scalars are copied in by the graph.
         Capturing runs the step once, as graph capture requires, on the
         optimizer's state and restores it after, so it briefly holds a copy
-        of the fp32 master and moments (12 B per element)."""
+        of the fp32 master and moments (12 B per element, plus the tiled
+        layout's padding)."""
         return CapturedStep(self, list(grads), extra_norm_sq)
 
     def state_dict(self) -> dict:
         """The optimizer state: the step counter and the fp32 master,
-        exp_avg and exp_avg_sq (the live device tensors, not copies)."""
-        return {"step": self.t, "master": self.master, "exp_avg": self.exp_avg, "exp_avg_sq": self.exp_avg_sq}
+        exp_avg and exp_avg_sq as split arrays (split layout: the live
+        device tensors; tiled layout: fresh copies read out of the tiled
+        buffer), so a checkpoint does not depend on the layout."""
+        return {"step": self.t, **{k: self._state_tensor(k) for k in _STATE_NAMES}}
 
     def load_state_dict(self, state: dict) -> None:
         """Copy a state_dict's tensors (any device) into this shard's buffers
         and take its step counter; sizes must match.  Drops any pending
         accumulation."""
-        names = ("master", "exp_avg", "exp_avg_sq")
-        for name in names:   # every check before the first copy: a refused state changes nothing
-            src, dst = state[name], getattr(self, name)
-            if src.numel() != dst.numel() or src.dtype != torch.float32:
-                raise ValueError(f"load_state_dict: {name} must be {dst.numel()} float32 elements")
+        for name in _STATE_NAMES:   # every check before the first copy: a refused state changes nothing
+            src = state[name]
+            if src.numel() != self.n or src.dtype != torch.float32:
+                raise ValueError(f"load_state_dict: {name} must be {self.n} float32 elements")
         t = int(state["step"])
         if t < 0:
             raise ValueError("load_state_dict: step must be >= 0")
-        for name in names:
-            getattr(self, name).copy_(state[name].reshape(-1))
+        dev = self.acc.device
+        if self._split is None:
+            srcs = [state[k].reshape(-1).to(dev).contiguous() for k in _STATE_NAMES]
+            zs.state_tile(*srcs, self.state, n=self.n)
+        else:
+            for name in _STATE_NAMES:
+                self._split[name].copy_(state[name].reshape(-1))
         self.t = t
         self._pending = 0
         self._norm_ready = False
@@ -130,7 +203,7 @@ class CapturedStep:
         self.opt = opt
         self.grads = grads
         self.extra_norm_sq = extra_norm_sq
-        dev = opt.master.device
+        dev = opt.acc.device
         nbytes = len(zs.scalars_bytes(zs.AdamWConfig(lr=opt.lr)))
         self._host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
         self._dev = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -140,16 +213,13 @@ class CapturedStep:
         side.wait_stream(torch.cuda.current_stream(dev))
         # one warm-up run on a side stream, as capture requires; the state it
         # steps is saved first and restored after, so capturing changes nothing
-        saved = {k: getattr(opt, k).clone() for k in ("master", "exp_avg", "exp_avg_sq")}
-        saved_bf16 = opt.param_bf16.clone() if opt.param_bf16 is not None else None
+        saved = opt._save()
         with torch.cuda.stream(side):
             self._body()
         torch.cuda.current_stream(dev).wait_stream(side)
         torch.cuda.synchronize(dev)
-        for k, v in saved.items():
-            getattr(opt, k).copy_(v)
-        if saved_bf16 is not None:
-            opt.param_bf16.copy_(saved_bf16)
+        opt._restore(saved)
+        del saved
         torch.cuda.synchronize(dev)
         self.graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(self.graph):
@@ -171,8 +241,7 @@ class CapturedStep:
             else:
                 zs.grad_accum(opt.acc, g, overwrite=(k == 0))
         self._dev.copy_(self._host, non_blocking=True)
-        zs.adamw_step_dev(self._dev, opt.master, opt.exp_avg, opt.exp_avg_sq, opt.acc, opt.param_bf16,
-                          norm_sq=opt.norm_sq if opt.compute_norm else None)
+        opt._adamw_dev(self._dev, opt.norm_sq if opt.compute_norm else None)
 
     def replay(self) -> None:
         """Run the next step.  Waits for the previous replay to have read the

@@ -327,6 +327,81 @@ ZS_API int32_t adamw_step_dev(const zs_adamw_scalars* scalars_dev, float* master
                               const double* norm_sq_dev, void* hip_stream);
 
 /*
+ * Tiled optimizer state — a storage layout of this library, not of the
+ * pages.  The pages keep an fp32 master, exp_avg and exp_avg_sq per
+ * parameter ([Memory page] §"一、显存账本": 4 + 4 + 4 of the 16 B per
+ * parameter) and update each element independently, so where the three
+ * values sit changes no result.  The tiled layout keeps them in one fp32
+ * buffer: the shard's elements are grouped in tiles of ZS_STATE_TILE; tile t
+ * holds the masters of its elements [t*ZS_STATE_TILE, (t+1)*ZS_STATE_TILE),
+ * then their exp_avgs, then their exp_avg_sqs, each a run of ZS_STATE_TILE
+ * floats:
+ *   state[(3*t + 0)*ZS_STATE_TILE + j]  master     of element t*ZS_STATE_TILE + j
+ *   state[(3*t + 1)*ZS_STATE_TILE + j]  exp_avg    of that element
+ *   state[(3*t + 2)*ZS_STATE_TILE + j]  exp_avg_sq of that element
+ * The last tile keeps full-length runs; positions past n are padding, never
+ * read by the step.  The AdamW step streams this layout faster than three
+ * separate buffers on gfx950 (its three state accesses per element fall in
+ * one region, so fewer DRAM rows are open at once); bytes and results are
+ * the same.  A tiled state buffer must be 16-byte aligned (every hipMalloc
+ * allocation is) and hold state_tiled_numel(n) floats.
+ */
+#define ZS_STATE_TILE 8192
+
+/* Floats in the tiled state of n elements: 3 * ZS_STATE_TILE * ceil(n /
+ * ZS_STATE_TILE).  -1 for n < 0 or n above the per-call limit.  Host only. */
+ZS_API int64_t state_tiled_numel(int64_t n);
+
+/*
+ * state_tile — split arrays into the tiled layout.  master, exp_avg,
+ * exp_avg_sq: device fp32[n], read; each may be NULL, which stands for zeros
+ * (a fresh optimizer's moments).  state: device fp32[state_tiled_numel(n)],
+ * written in full, the last tile's padding as zeros.  Bit-exact copies.
+ * state must not overlap a source; the sources may overlap one another.
+ * Errors: ZS_EINVAL (state NULL or not 16-byte aligned with n > 0, a source
+ * not 4-byte aligned, n out of range), ZS_EOVERLAP, ZS_EHIP.
+ */
+ZS_API int32_t state_tile(const float* master, const float* exp_avg, const float* exp_avg_sq, float* state,
+                          int64_t n, void* hip_stream);
+
+/*
+ * state_untile — the inverse: master, exp_avg, exp_avg_sq (device fp32[n],
+ * written; each may be NULL: that stream is skipped) from the tiled state
+ * (device fp32[state_tiled_numel(n)], read).  Bit-exact copies; checkpoints
+ * and state_dicts use the split arrays.  The destinations must not overlap
+ * the state or one another.  Errors: as state_tile.
+ */
+ZS_API int32_t state_untile(const float* state, float* master, float* exp_avg, float* exp_avg_sq, int64_t n,
+                            void* hip_stream);
+
+/*
+ * adamw_step_tiled — adamw_step on a tiled state: the same update, order of
+ * operations, clip and non-finite skip ([ZeRO page] §ZeRO-1/2/3 step;
+ * decoupled decay as in adamw_step), with master, exp_avg and exp_avg_sq
+ * read from and written back to their places in `state`.  Results are bit
+ * for bit those of adamw_step on the untiled arrays; 30 B per element (28
+ * without param_bf16), as adamw_step.
+ * state: device fp32[state_tiled_numel(n)], 16-byte aligned, read-write
+ * (padding untouched); grad: device fp32[n], read; param_bf16: device
+ * bf16[n] or NULL, written; norm_sq_dev as in adamw_step.  No two of them
+ * may overlap, nor overlap *norm_sq_dev.
+ * Errors: ZS_EINVAL (as adamw_step, or state not 16-byte aligned),
+ * ZS_EOVERLAP, ZS_EHIP.
+ */
+ZS_API int32_t adamw_step_tiled(const zs_adamw* hp, float* state, const float* grad, uint16_t* param_bf16,
+                                int64_t n, const double* norm_sq_dev, void* hip_stream);
+
+/*
+ * adamw_step_tiled_dev — adamw_step_tiled with its scalars read from device
+ * memory when the kernels run, as adamw_step_dev does for adamw_step (one
+ * captured HIP graph replays every step).  scalars_dev: device, 8-byte
+ * aligned, read; it must not overlap a written buffer.  Other arguments,
+ * results and errors as adamw_step_tiled.
+ */
+ZS_API int32_t adamw_step_tiled_dev(const zs_adamw_scalars* scalars_dev, float* state, const float* grad,
+                                    uint16_t* param_bf16, int64_t n, const double* norm_sq_dev, void* hip_stream);
+
+/*
  * adamw_step_no_master — the same update with no fp32 master: the bf16
  * parameter shard is read, updated and rounded back in place.
  * [ZeRO page] §"ZeRO-3: 切分参数", ZeRO3Optimizer.step (the update is added

@@ -37,7 +37,7 @@ def no_launch_reached():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 17 and set(names) == set(B.EXPORTS), names
+    assert len(names) == 22 and set(names) == set(B.EXPORTS), names
     L = zs.lib()
     for name in names:
         assert getattr(L, name) is not None
@@ -187,6 +187,70 @@ def test_adamw_scalars_and_step_dev_reject():
     assert call(norm=FAKE + 2**21 + 8) == B.ZS_EOVERLAP      # norm inside exp_avg_sq
     assert call(n=(1 << 39) + 1) == B.ZS_EINVAL
     assert call(n=0) == B.ZS_OK
+
+
+def test_state_tile_constant_matches_the_header():
+    """ZS_STATE_TILE in the header, the binding's constant and the tests'
+    layout definition (test_oracle_pins: 8192) agree."""
+    text = open(HEADER).read()
+    assert int(re.search(r"#define ZS_STATE_TILE (\d+)", text).group(1)) == B.STATE_TILE == 8192
+
+
+def test_state_tiled_numel():
+    L = zs.lib()
+    T = B.STATE_TILE
+    for n in (0, 1, T - 1, T, T + 1, 5 * T, 842301952, 1 << 39):
+        assert L.state_tiled_numel(n) == oracle.state_tiled_numel(n, T) == 3 * T * (-(-n // T)), n
+    assert L.state_tiled_numel(-1) == -1 and L.state_tiled_numel((1 << 39) + 1) == -1
+
+
+def test_state_tile_and_untile_reject():
+    L = zs.lib()
+    n = 1024
+    st = FAKE + 2**30
+    sb = 3 * B.STATE_TILE * 4                                   # tiled bytes of 1024 elements
+    tile = lambda p=FAKE, m=FAKE + 2**20, v=FAKE + 2**21, s=st, k=n: L.state_tile(p, m, v, s, k, None)
+    untile = lambda p=FAKE, m=FAKE + 2**20, v=FAKE + 2**21, s=st, k=n: L.state_untile(s, p, m, v, k, None)
+    for call in (tile, untile):
+        assert call(s=0) == B.ZS_EINVAL
+        assert call(s=st + 4) == B.ZS_EINVAL                      # the state must be 16-byte aligned
+        assert call(p=FAKE + 2) == B.ZS_EINVAL                    # fp32 must be 4-byte aligned
+        assert call(k=-1) == B.ZS_EINVAL
+        assert call(k=(1 << 39) + 1) == B.ZS_EINVAL
+        assert call(v=st + sb - 4) == B.ZS_EOVERLAP               # a split array over the state's end
+        assert call(k=0) == B.ZS_OK
+        assert call(s=0, k=0) == B.ZS_OK
+    assert untile(m=FAKE + 64) == B.ZS_EOVERLAP                   # two destinations overlap
+    assert tile(p=FAKE + 2, m=0, v=0) == B.ZS_EINVAL
+
+
+def test_adamw_step_tiled_rejects():
+    L = zs.lib()
+    n = 1024
+    st = FAKE
+    sb = 3 * B.STATE_TILE * 4
+    call = lambda hp=None, s=st, g=FAKE + 2**20, b=0, k=n, norm=0: L.adamw_step_tiled(
+        ctypes.byref(hp or _hp()), s, g, b, k, norm, None)
+    for bad in (dict(step=0), dict(beta1=1.0), dict(eps=0.0), dict(lr=-1.0), dict(grad_scale=0.0)):
+        assert call(hp=_hp(**bad)) == B.ZS_EINVAL, bad
+    assert L.adamw_step_tiled(None, st, FAKE + 2**20, 0, n, 0, None) == B.ZS_EINVAL
+    assert call(s=0) == B.ZS_EINVAL
+    assert call(g=0) == B.ZS_EINVAL
+    assert call(s=st + 4) == B.ZS_EINVAL                            # the state must be 16-byte aligned
+    assert call(g=FAKE + 2**20 + 2) == B.ZS_EINVAL
+    assert call(b=FAKE + 2**21 + 1) == B.ZS_EINVAL
+    assert call(norm=FAKE + 2**22 + 4) == B.ZS_EINVAL
+    assert call(g=st + sb - 8) == B.ZS_EOVERLAP                     # grad over the end of the state
+    assert call(b=FAKE + 2**20 + 64) == B.ZS_EOVERLAP               # bf16 output over the grad
+    assert call(norm=st + 1024) == B.ZS_EOVERLAP                    # norm inside the written state
+    assert call(k=(1 << 39) + 1) == B.ZS_EINVAL
+    assert call(k=0) == B.ZS_OK
+    sc = FAKE + 2**30
+    dev = lambda s=sc, k=n, norm=0: L.adamw_step_tiled_dev(s, st, FAKE + 2**20, 0, k, norm, None)
+    assert dev(s=0) == B.ZS_EINVAL
+    assert dev(s=sc + 4) == B.ZS_EINVAL
+    assert dev(s=st + 64) == B.ZS_EOVERLAP                          # scalars inside the written state
+    assert dev(k=0) == B.ZS_OK
 
 
 def test_adam_update_rejects():
@@ -349,9 +413,10 @@ def test_element_count_limit():
 
 
 def test_ceiling_library_rejects_before_launch():
-    """The benchmark's bandwidth-ceiling kernel (libzsceiling.so) exports one
-    symbol and rejects bad arguments, or returns for n == 0, without a
-    launch (a launch attempt here would return a HIP error, not -1 or 0)."""
+    """The benchmark's bandwidth-ceiling kernels (libzsceiling.so: the split
+    and the tiled state layout) reject bad arguments, or return for n == 0,
+    without a launch (a launch attempt here would return a HIP error, not -1
+    or 0)."""
     from fsdp_sharded_optimizer_amd import build as zbuild
     if not os.path.exists(zbuild.CEILING_LIB):
         pytest.skip("libzsceiling.so not built")
@@ -369,6 +434,17 @@ def test_ceiling_library_rejects_before_launch():
     assert f(a, a + 64, a + 128, a + 192, a + 258, 16, 0, None) == -1      # bf16 output off 16 bytes
     assert f(a, a + 64, a + 128, a + 192, None, 16, -1, None) == -1        # LDS reservation out of range
     assert f(a, a + 64, a + 128, a + 192, None, 16, 65537, None) == -1
+    t = L.zsc_adamw_traffic_tiled
+    t.restype = ctypes.c_int32
+    t.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]
+    assert t(a, a + 64, None, 0, 0, None) == 0
+    assert t(a, a + 64, None, -1, 0, None) == -1
+    assert t(a, a + 64, None, (1 << 31) + 1, 0, None) == -1               # one launch at most
+    assert t(None, a + 64, None, 16, 0, None) == -1
+    assert t(a + 4, a + 64, None, 16, 0, None) == -1                       # state off 16 bytes
+    assert t(a, a + 66, None, 16, 0, None) == -1                           # grad off 4 bytes
+    assert t(a, a + 64, a + 130, 16, 0, None) == -1                        # bf16 output off 16 bytes
+    assert t(a, a + 64, None, 16, 70000, None) == -1
 
 
 def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):

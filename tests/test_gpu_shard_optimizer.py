@@ -17,16 +17,17 @@ from tests.parity import NORM_TOL, StateCheck, bits_equal, from_np, to_np
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("layout", ["tiled", "split"])
 @pytest.mark.parametrize("fused", [True, False])
-def test_shard_optimizer_matches_the_oracle(fused):
-    print(f"ShardOptimizer fused={fused}", flush=True)
+def test_shard_optimizer_matches_the_oracle(fused, layout):
+    print(f"ShardOptimizer fused={fused} layout={layout}", flush=True)
     n, M, scale, lr, wd = 100_003, 4, 1 / 32, 3e-4, 0.1
     rng = np.random.default_rng(17)
     p0 = rng.uniform(-0.1, 0.1, n).astype(np.float32)
     master = from_np(p0.copy())
     param = torch.empty(n, dtype=torch.bfloat16, device="cuda")
     opt = zs.ShardOptimizer(master, lr=lr, betas=(0.9, 0.95), weight_decay=wd, grad_scale=scale, max_norm=1.0,
-                            param_bf16=param)
+                            param_bf16=param, layout=layout)
     p_ref, m_ref, v_ref = p0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
     b_ref = np.zeros(n, np.uint16)
     for t in range(1, 4):
@@ -49,7 +50,9 @@ def test_shard_optimizer_matches_the_oracle(fused):
         assert coef < 1.0                                 # every step clips
         g2 = (acc_ref * np.float32(scale)) * np.float32(coef)
         s = oracle.adamw_scalars(H)
-        gpu = {"p": to_np(master), "m": to_np(opt.exp_avg), "v": to_np(opt.exp_avg_sq), "b": to_np(param)}
+        gpu = {"p": to_np(opt.master), "m": to_np(opt.exp_avg), "v": to_np(opt.exp_avg_sq), "b": to_np(param)}
+        if layout == "split":
+            assert opt.master is master                   # the caller's tensor is stepped in place
         res = StateCheck(0.9, lr, wd, s.step_size).check(gpu, {"p": p_ref, "m": m_ref, "v": v_ref, "b": b_ref},
                                                           prev, g2, f"t={t}")
         print(f"  t={t} norm {math.sqrt(S + extra):.4f} coef {coef:.4f} {res}", flush=True)
@@ -61,13 +64,39 @@ def test_shard_optimizer_refuses_a_step_without_gradients():
         opt.step()
     with pytest.raises(TypeError):
         zs.ShardOptimizer(torch.zeros(16, device="cuda", dtype=torch.float64), lr=1e-3)
+    with pytest.raises(ValueError):
+        zs.ShardOptimizer(torch.zeros(16, device="cuda"), lr=1e-3, layout="interleaved")
 
 
-def test_shard_optimizer_resume_is_bit_identical():
+def test_layouts_give_identical_bits():
+    """The same five steps under the tiled and the split layout: master,
+    moments and bf16 parameter bit-identical after every step."""
+    n, M = 3 * zs.STATE_TILE + 1001, 2
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    p0 = torch.rand(n, generator=gen, device="cuda") * 0.2 - 0.1
+    kw = dict(lr=3e-4, betas=(0.9, 0.95), weight_decay=0.1, grad_scale=1 / 16, max_norm=1.0)
+    opts = [zs.ShardOptimizer(p0.clone(), param_bf16=torch.empty(n, dtype=torch.bfloat16, device="cuda"),
+                              layout=lay, **kw) for lay in ("tiled", "split")]
+    for t in range(1, 6):
+        mbs = [(torch.randn(n, generator=gen, device="cuda") * 0.05 * t).to(torch.bfloat16) for _ in range(M)]
+        for opt in opts:
+            for k, g in enumerate(mbs):
+                opt.accumulate(g, last=k == M - 1)
+            opt.step(extra_norm_sq=0.5)
+        torch.cuda.synchronize()
+        for name in ("master", "exp_avg", "exp_avg_sq", "param_bf16"):
+            assert bits_equal(to_np(getattr(opts[0], name)), to_np(getattr(opts[1], name))), (t, name)
+
+
+@pytest.mark.parametrize("layouts", [("tiled", "tiled"), ("split", "tiled"), ("tiled", "split")])
+def test_shard_optimizer_resume_is_bit_identical(layouts):
     """Five steps in one run against two steps, a state_dict copied to the
     host, a fresh optimizer loading it and three more steps: master, moments,
-    bf16 parameter and step counter bit-identical."""
-    print("ShardOptimizer resume", flush=True)
+    bf16 parameter and step counter bit-identical, also when the run is
+    resumed under the other state layout (checkpoints hold split arrays)."""
+    print(f"ShardOptimizer resume {layouts}", flush=True)
+    saved_layout, resumed_layout = layouts
     n, M, scale = 70_001, 2, 1 / 16
     rng = np.random.default_rng(23)
     p0 = rng.uniform(-0.1, 0.1, n).astype(np.float32)
@@ -84,11 +113,11 @@ def test_shard_optimizer_resume_is_bit_identical():
     whole = zs.ShardOptimizer(from_np(p0.copy()), param_bf16=torch.empty(n, dtype=torch.bfloat16, device="cuda"),
                               **kw)
     run(whole, grads)
-    first = zs.ShardOptimizer(from_np(p0.copy()), **kw)
+    first = zs.ShardOptimizer(from_np(p0.copy()), layout=saved_layout, **kw)
     run(first, grads[:2])
     saved = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in first.state_dict().items()}
     del first
-    resumed = zs.ShardOptimizer(torch.empty(n, device="cuda"),
+    resumed = zs.ShardOptimizer(torch.empty(n, device="cuda"), layout=resumed_layout,
                                 param_bf16=torch.empty(n, dtype=torch.bfloat16, device="cuda"), **kw)
     resumed.load_state_dict(saved)
     assert resumed.t == 2
@@ -103,17 +132,18 @@ def test_shard_optimizer_resume_is_bit_identical():
     assert resumed.t == 5 and bits_equal(to_np(resumed.master), before)   # a refused state changes nothing
 
 
+@pytest.mark.parametrize("layout", ["tiled", "split"])
 @pytest.mark.parametrize("max_norm", [0.5, 0.0])
-def test_captured_step_replays_like_eager_steps(max_norm):
+def test_captured_step_replays_like_eager_steps(max_norm, layout):
     """ShardOptimizer.capture: one graph, replayed for four steps with new
     gradients each time, bit-identical to the same steps taken eagerly by a
     twin optimizer (step counter, master, moments, bf16 parameter, norm)."""
-    print(f"ShardOptimizer capture max_norm={max_norm}", flush=True)
+    print(f"ShardOptimizer capture max_norm={max_norm} layout={layout}", flush=True)
     n, M, scale = 50_003, 3, 1 / 24
     gen = torch.Generator(device="cuda")
     gen.manual_seed(31)
     p0 = torch.rand(n, generator=gen, device="cuda") * 0.2 - 0.1
-    kw = dict(lr=3e-4, betas=(0.9, 0.95), weight_decay=0.1, grad_scale=scale, max_norm=max_norm)
+    kw = dict(lr=3e-4, betas=(0.9, 0.95), weight_decay=0.1, grad_scale=scale, max_norm=max_norm, layout=layout)
     a = zs.ShardOptimizer(p0.clone(), param_bf16=torch.empty(n, dtype=torch.bfloat16, device="cuda"), **kw)
     b = zs.ShardOptimizer(p0.clone(), param_bf16=torch.empty(n, dtype=torch.bfloat16, device="cuda"), **kw)
     grads = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for _ in range(M)]
