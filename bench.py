@@ -36,8 +36,9 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0   # MI355X published HBM3E bandwidth
 
-# HBM bytes per adamw_step launch, per shard size (the Llama-7B shard and the
-# 70B ZeRO-3 shard), from two rocprofv3 --pmc runs of this script for that
+# HBM bytes per AdamW launch (adamw_step_tiled, the step's kernel, and
+# adamw_step, the same step on split buffers), per shard size (the Llama-7B
+# shard and the 70B ZeRO-3 shard), from two rocprofv3 --pmc runs of this script for that
 # workload (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what
 # the same counter reads for the 4 GiB device copy this script also runs
 # (FETCH_SIZE reads about 2,097,194 KiB for it: x2.0; WRITE_SIZE reads
@@ -45,12 +46,17 @@ HBM_PEAK_GBPS = 8000.0   # MI355X published HBM3E bandwidth
 # hash covers the kernel file and its header.
 PMC_SOURCES = ("csrc/adamw.hip", "csrc/zs_common.h")
 PMC_TRAFFIC = {
-    "adamw_step_tiled": [],
+    "adamw_step_tiled": [
+        {"sha256_16": "e9e3e53f9b30e2a6", "shard_elems": 842301952,
+         "fetch_kib": 6580552.7, "fetch_scale": 2.0, "write_kib": 11515855.1, "write_scale": 1.0},
+        {"sha256_16": "e9e3e53f9b30e2a6", "shard_elems": 1093750000,
+         "fetch_kib": 8545001.9, "fetch_scale": 2.0, "write_kib": 14953621.8, "write_scale": 1.0},
+    ],
     "adamw_step": [
-        {"sha256_16": "1fec0d6ae7b7f2ea", "shard_elems": 842301952,
-         "fetch_kib": 6580558.7, "fetch_scale": 2.0, "write_kib": 11515848.1, "write_scale": 1.0},
-        {"sha256_16": "1fec0d6ae7b7f2ea", "shard_elems": 1093750000,
-         "fetch_kib": 8545004.1, "fetch_scale": 2.0, "write_kib": 14953617.1, "write_scale": 1.0},
+        {"sha256_16": "e9e3e53f9b30e2a6", "shard_elems": 842301952,
+         "fetch_kib": 6580510.0, "fetch_scale": 2.0, "write_kib": 11515848.8, "write_scale": 1.0},
+        {"sha256_16": "e9e3e53f9b30e2a6", "shard_elems": 1093750000,
+         "fetch_kib": 8544948.0, "fetch_scale": 2.0, "write_kib": 14953615.2, "write_scale": 1.0},
     ],
 }
 
@@ -656,6 +662,7 @@ def main():
             "ms": r["split_ms"], "bytes_per_elem": bpe["adamw_step"],
             "gbps": adamw_bytes / (r["split_ms"] * 1e-3) / 1e9,
             "frac": adamw_bytes / (r["split_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "traffic": pmc_traffic("adamw_step", n),
             "traffic_ceiling": ceiling_report(r["ceiling_split_ms"], adamw_bytes, r["split_ms"])},
         "cpu_baseline": cpu,
         "flat_unit": flat,
