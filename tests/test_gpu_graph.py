@@ -156,10 +156,11 @@ def test_one_graph_replays_every_step_with_device_scalars():
 
 def test_every_other_entry_point_replays_bit_exact():
     """flat_pack (bit copy with padding; widening), grad_reduce_chunks,
-    grad_norm_sq, adamw_step_no_master, adam_update, flat_unpack (re-cast)
-    and flat_apply_update (bf16 and fp32 tensors) captured in one graph and
-    replayed four times with fresh inputs, each replay bit-identical to the
-    same calls made eagerly on a twin state."""
+    grad_norm_sq, adamw_step_no_master, adam_update, flat_unpack (re-cast),
+    flat_apply_update (bf16 and fp32 tensors), adamw_step_tiled on a tiled
+    state, state_untile and state_tile captured in one graph and replayed
+    four times with fresh inputs, each replay bit-identical to the same
+    calls made eagerly on a twin state."""
     dev = torch.device("cuda")
     gen = torch.Generator(device=dev)
     gen.manual_seed(11)
@@ -186,7 +187,16 @@ def test_every_other_entry_point_replays_bit_exact():
                 "upd": torch.empty(T, device=dev),
                 "outs": [torch.empty(k, dtype=torch.bfloat16, device=dev) for k in sizes],
                 "tb": [(torch.rand(k, generator=gen, device=dev) - 0.5).to(torch.bfloat16) for k in sizes],
-                "tf": [torch.rand(k, generator=gen, device=dev) - 0.5 for k in sizes]}
+                "tf": [torch.rand(k, generator=gen, device=dev) - 0.5 for k in sizes],
+                "state": tiled(torch.rand(T, generator=gen, device=dev) * 0.2 - 0.1),
+                "bt": torch.empty(T, dtype=torch.bfloat16, device=dev),
+                "um": torch.empty(T, device=dev), "uv": torch.empty(T, device=dev),
+                "state2": torch.empty(zs.state_tiled_numel(T), device=dev)}
+
+    def tiled(master):
+        st = torch.empty(zs.state_tiled_numel(T), device=dev)
+        zs.state_tile(master, None, None, st)
+        return st
 
     a = side()
     b = {k: ([t.clone() for t in v] if isinstance(v, list) else v.clone()) for k, v in a.items()}
@@ -201,6 +211,9 @@ def test_every_other_entry_point_replays_bit_exact():
         zs.flat_unpack(s["flat32"], s["outs"])
         zs.flat_apply_update(s["upd"], s["tb"])
         zs.flat_apply_update(s["upd"], s["tf"])
+        zs.adamw_step_tiled(hp, s["state"], s["acc"], s["bt"], norm_sq=s["norm"])
+        zs.state_untile(s["state"], None, s["um"], s["uv"], n=T)
+        zs.state_tile(s["m1"], None, s["v1"], s["state2"])
 
     def fresh(r):
         for p in params:

@@ -152,6 +152,60 @@ def test_adamw_forms_across_pieces(offset):
     release()
 
 
+STATE_TILE = 8192   # ZS_STATE_TILE (test_abi checks the header against this value)
+
+
+@pytest.mark.parametrize("b_off", [0, 1])
+def test_tiled_state_across_pieces(b_off):
+    """state_tile, a clipped adamw_step_tiled and state_untile over N
+    elements (a launch piece starts the tiled state 3 * 2^31 floats in):
+    the state read at the layout's positions and the untiled arrays
+    bit-exact on the sample.  b_off = 1 puts the bf16 output off a 16-byte
+    boundary (the element-wise path, 2^31 work-items per piece)."""
+    need_gib(72)
+    log(f"tiled state across pieces n={N} bf16 offset={b_off}")
+    idx = sample_indices(N, seed=61 + b_off)
+    master = fill_uniform(buffer(N, 0), -0.1, 0.1, 601)
+    m = fill_normal(buffer(N, 0), 1e-4, 602)
+    v = fill_uniform(buffer(N, 0), 0.0, 1e-8, 603)
+    grad = fill_normal(buffer(N, 0), 1e-3, 604)
+    bf16 = buffer(N, b_off, torch.bfloat16)
+    state = torch.empty(zs.state_tiled_numel(N), dtype=torch.float32, device=DEV)
+    where = (idx // STATE_TILE) * (3 * STATE_TILE) + idx % STATE_TILE
+    p_ref, m_ref, v_ref, g_s = host(master[idx]), host(m[idx]), host(v[idx]), host(grad[idx])
+
+    log("  state_tile")
+    zs.state_tile(master, m, v, state)
+    for k, (name, ref) in enumerate((("master", p_ref), ("m", m_ref), ("v", v_ref))):
+        check(f"tile {name}", state, where + k * STATE_TILE, ref)
+    tail = torch.arange(N, zs.state_tiled_numel(N) // 3, device=DEV)      # the last tile's unused ends
+    tail_at = (tail // STATE_TILE) * (3 * STATE_TILE) + tail % STATE_TILE
+    for k in range(3):
+        assert not host(state[tail_at + k * STATE_TILE]).view(np.uint32).any()
+
+    log("  adamw_step_tiled")
+    scale, extra, max_norm = 1.0 / 64, 2.0, 1.0
+    S = oracle.grad_norm_sq(host(grad), scale)
+    assert oracle.clip_coef(S, extra, max_norm) < 1.0
+    norm = torch.tensor([S], dtype=torch.float64, device=DEV)
+    hp = zs.AdamWConfig(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, grad_scale=scale,
+                        max_norm=max_norm, extra_norm_sq=extra, step=3)
+    zs.adamw_step_tiled(hp, state, grad, bf16, norm_sq=norm)
+    H = oracle.make_hp(3e-4, 0.9, 0.95, 1e-8, 0.1, scale, max_norm, extra, 3)
+    b_ref = np.empty(idx.numel(), np.uint16)
+    assert oracle.adamw_step(H, p_ref, m_ref, v_ref, g_s, b_ref, norm_sq=S) == 0
+    for k, (name, ref) in enumerate((("master", p_ref), ("m", m_ref), ("v", v_ref))):
+        check(f"step {name}", state, where + k * STATE_TILE, ref)
+    check("bf16", bf16, idx, b_ref)
+
+    log("  state_untile")
+    zs.state_untile(state, master, m, v)
+    for name, gpu, ref in (("master", master, p_ref), ("m", m, m_ref), ("v", v, v_ref)):
+        check(f"untile {name}", gpu, idx, ref)
+    del master, m, v, grad, bf16, state
+    release()
+
+
 @pytest.mark.parametrize("offset", [0, 1])
 def test_accumulations_across_pieces(offset):
     """grad_accum (overwrite, add) and grad_accum_norm_sq (the accumulating

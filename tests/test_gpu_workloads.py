@@ -49,15 +49,26 @@ def host(t: torch.Tensor) -> np.ndarray:
     return to_np(t)
 
 
-def run_shard(w: workloads.Workload, n: int, sampled: bool, full_norm: bool, fused: bool = True):
+STATE_TILE = 8192   # ZS_STATE_TILE (test_abi checks the header against this value)
+
+
+def run_shard(w: workloads.Workload, n: int, sampled: bool, full_norm: bool, fused: bool = True,
+              layout: str = "split"):
     """Drive the library and the oracle through w.steps steps of one shard.
     fused: the last micro-batch forms the norm in the same pass
     (grad_accum_norm_sq, as bench.py runs it); otherwise grad_accum for
-    every micro-batch, then grad_norm_sq."""
+    every micro-batch, then grad_norm_sq.  layout "tiled": the optimizer
+    state in one tiled buffer and adamw_step_tiled (as bench.py times the
+    step); the compared elements are read at the positions the header's
+    layout gives them."""
     master = workloads.master_init(w, n, DEV)
     param = master.to(torch.bfloat16) if w.bf16_param else None
-    exp_avg = torch.zeros(n, dtype=torch.float32, device=DEV)
-    exp_avg_sq = torch.zeros(n, dtype=torch.float32, device=DEV)
+    if layout == "tiled":
+        state = torch.empty(zs.state_tiled_numel(n), dtype=torch.float32, device=DEV)
+        zs.state_tile(master, None, None, state)
+    else:
+        exp_avg = torch.zeros(n, dtype=torch.float32, device=DEV)
+        exp_avg_sq = torch.zeros(n, dtype=torch.float32, device=DEV)
     acc = torch.empty(n, dtype=torch.float32, device=DEV)
     norm = torch.zeros(1, dtype=torch.float64, device=DEV)
     ws = torch.empty(max(zs.grad_norm_sq_workspace_bytes(n), zs.grad_accum_norm_sq_workspace_bytes(n), 8),
@@ -66,6 +77,13 @@ def run_shard(w: workloads.Workload, n: int, sampled: bool, full_norm: bool, fus
     idx = sample_indices(n, seed=w.cfg) if sampled else None
     pick = (lambda t: t[idx]) if sampled else (lambda t: t)
     p_ref = host(pick(master))
+    if layout == "tiled":
+        e = idx if sampled else torch.arange(n, device=DEV)
+        where = (e // STATE_TILE) * (3 * STATE_TILE) + e % STATE_TILE   # each element's master in the state
+        state_at = lambda k: state[where + k * STATE_TILE]              # k = 0 master, 1 exp_avg, 2 exp_avg_sq
+        del master
+    else:
+        state_at = lambda k: pick((master, exp_avg, exp_avg_sq)[k])
     m_ref = np.zeros(p_ref.size, np.float32)
     v_ref = np.zeros(p_ref.size, np.float32)
     b_ref = host(pick(param)) if param is not None else None
@@ -98,7 +116,10 @@ def run_shard(w: workloads.Workload, n: int, sampled: bool, full_norm: bool, fus
         hp = zs.AdamWConfig(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
                             weight_decay=w.weight_decay, grad_scale=w.grad_scale, max_norm=w.max_norm,
                             extra_norm_sq=extra, step=t)
-        zs.adamw_step(hp, master, exp_avg, exp_avg_sq, acc, param, norm_sq=norm)
+        if layout == "tiled":
+            zs.adamw_step_tiled(hp, state, acc, param, norm_sq=norm)
+        else:
+            zs.adamw_step(hp, master, exp_avg, exp_avg_sq, acc, param, norm_sq=norm)
         ohp = oracle.make_hp(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, w.grad_scale, w.max_norm,
                              extra, t)
         prev = {"p": p_ref.copy(), "m": m_ref.copy()}
@@ -108,13 +129,13 @@ def run_shard(w: workloads.Workload, n: int, sampled: bool, full_norm: bool, fus
         assert oracle.adamw_step(ohp, p_ref, m_ref, v_ref, acc_ref, b_ref, norm_sq=clip_norm) == 0
         coef = oracle.clip_coef(clip_norm, extra, w.max_norm) if clip_norm is not None else 1.0
         g2 = (acc_ref * np.float32(w.grad_scale)) * np.float32(coef)
-        gpu = {"p": host(pick(master)), "m": host(pick(exp_avg)), "v": host(pick(exp_avg_sq)),
+        gpu = {"p": host(state_at(0)), "m": host(state_at(1)), "v": host(state_at(2)),
                "b": host(pick(param)) if param is not None else None}
         s = oracle.adamw_scalars(ohp)
         res = StateCheck(w.beta1, w.lr, w.weight_decay, s.step_size).check(
             gpu, {"p": p_ref, "m": m_ref, "v": v_ref, "b": b_ref}, prev, g2, f"{w.name} t={t}")
         res.update(step=t, coef=coef, norm=math.sqrt(s_gpu + extra), secs=round(time.perf_counter() - t0, 1))
-        log(f"  {w.name} n={n} {res}")
+        log(f"  {w.name} n={n} {layout} {res}")
         report.append(res)
     return report
 
@@ -123,11 +144,12 @@ def run_shard(w: workloads.Workload, n: int, sampled: bool, full_norm: bool, fus
 # small sizes: every element
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("layout", ["split", "tiled"])
 @pytest.mark.parametrize("name,n,fused", [("llama7b_shard", 1_000_037, True), ("llama7b_shard", 1_000_037, False),
                                           ("llama13b_shard_clip", 600_011, True),
                                           ("llama13b_shard_clip", 600_011, False),
                                           ("zero3_70b_shard", 2_000_003, True), ("zero3_70b_shard", 2_000_003, False)])
-def test_workload_small(name, n, fused):
+def test_workload_small(name, n, fused, layout):
     """Every element, at a reduced shard length.  The gradient std is scaled
     by sqrt(full/n) so the global norm, and with it the clipping pattern of
     the 13B workload, is the one of the full shard."""
@@ -135,8 +157,8 @@ def test_workload_small(name, n, fused):
     w = workloads.WORKLOADS[name]
     _, start, end, _ = zs.zero_shard_range(w.total, w.world, w.rank)
     w = replace(w, grad_std=w.grad_std * math.sqrt((end - start) / n))
-    log(f"workload {name} small n={n}")
-    rep = run_shard(w, n, sampled=False, full_norm=False, fused=fused)
+    log(f"workload {name} small n={n} {layout}")
+    rep = run_shard(w, n, sampled=False, full_norm=False, fused=fused, layout=layout)
     if name == "llama13b_shard_clip":
         clipped = [r["step"] for r in rep if r["coef"] < 1.0]
         assert clipped == [2, 5, 8], clipped
@@ -270,14 +292,19 @@ def test_full_fsdp_unit_70b_block():
     log(f"  unit {res} bf16 identical {frac:.6f}")
 
 
-@pytest.mark.parametrize("name,full_norm,fused", [("llama7b_shard", False, True), ("zero3_70b_shard", True, False),
-                                                  ("llama13b_shard_clip", True, True)])
-def test_full_shard(name, full_norm, fused):
+@pytest.mark.parametrize("name,full_norm,fused,layout", [
+    ("llama7b_shard", False, True, "tiled"), ("llama7b_shard", False, True, "split"),
+    ("zero3_70b_shard", True, False, "tiled"), ("zero3_70b_shard", True, True, "tiled"),
+    ("llama13b_shard_clip", True, True, "tiled")])
+def test_full_shard(name, full_norm, fused, layout):
+    """The real shard lengths in bench.py's launch configuration (the tiled
+    state; the 7B shard also on split buffers): the norm over the whole
+    shard, the optimizer state on sampled elements."""
     w = workloads.WORKLOADS[name]
     _, start, end, _ = zs.zero_shard_range(w.total, w.world, w.rank)
     n = end - start
-    log(f"full {name}: shard of {n} elements, {w.steps} steps x {w.micro_batches} micro-batches")
-    rep = run_shard(w, n, sampled=True, full_norm=full_norm, fused=fused)
+    log(f"full {name} ({layout}): shard of {n} elements, {w.steps} steps x {w.micro_batches} micro-batches")
+    rep = run_shard(w, n, sampled=True, full_norm=full_norm, fused=fused, layout=layout)
     if name == "llama13b_shard_clip":
         assert [r["step"] for r in rep if r["coef"] < 1.0] == [2, 5, 8]
     if name == "zero3_70b_shard":
