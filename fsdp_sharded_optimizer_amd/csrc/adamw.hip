@@ -18,11 +18,11 @@
 // exp_avg and exp_avg_sq in one buffer, three runs of kStateTile floats per
 // tile of elements.  Same bytes and arithmetic; a wave's three state
 // accesses then fall in one 96 KiB region instead of three separate
-// buffers, which keeps fewer DRAM rows open: on gfx950 the trivial-arithmetic
-// probe of this traffic gains 4 to 6 points of the peak and the AdamW step
-// about 3 (84-85 % against 81-82 %), with residency capped at 11 workgroups
-// per CU (14 KiB reserved each; the split layout's 10 per CU is 1 point lower
-// here).
+// buffers, which keeps fewer DRAM rows open: on gfx950 the AdamW step runs
+// at 85 % of the peak against 80-83 % on split buffers (7B, 70B and 13B
+// shard sizes, clipped or not), with residency capped at 11 workgroups per
+// CU (14 KiB reserved each; 10, 12 and 13 per CU measure 0.7-1.6 points
+// lower).
 //
 // Layout: every array is a flat 1-D fp32 (bf16) buffer; thread k of the grid
 // owns the 4 consecutive elements [4k, 4k+4): one 128-bit access per fp32
@@ -125,10 +125,19 @@ __global__ __launch_bounds__(BS) void adamw_kernel(const AdamwArgs a) {
         // The loads are issued before the clip coefficient is resolved, so
         // the latency of the norm's read overlaps with them.
         const f32x4 g4 = ld_stream_f32x4_a4(a.grad + first);   // read-only: dword alignment suffices
-        float* const ts = TILED ? a.state + tiled_offset(first) : nullptr;
-        float* const p_at = TILED ? ts : a.master + first;
-        float* const m_at = TILED ? ts + kStateTile : a.exp_avg + first;
-        float* const v_at = TILED ? ts + 2 * kStateTile : a.exp_avg_sq + first;
+        // this lane's master (master forms only), exp_avg and exp_avg_sq
+        float* p_at = nullptr;
+        float* m_at;
+        float* v_at;
+        if constexpr (TILED) {
+            p_at = a.state + tiled_offset(first);
+            m_at = p_at + kStateTile;
+            v_at = p_at + 2 * kStateTile;
+        } else {
+            if constexpr (FORM == kMaster || FORM == kMasterBf16) p_at = a.master + first;
+            m_at = a.exp_avg + first;
+            v_at = a.exp_avg_sq + first;
+        }
         f32x4 p4 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         if constexpr (FORM == kNoMaster) {
             const u32x2 w = ld_stream(reinterpret_cast<const u32x2*>(a.param_bf16 + first));
@@ -166,7 +175,7 @@ __global__ __launch_bounds__(BS) void adamw_kernel(const AdamwArgs a) {
     if (!clip_coef(sc, a.norm_sq, coef)) return;
     const int64_t last = first + VEC < n ? first + VEC : n;
     for (int64_t i = first; i < last; ++i) {
-        float* const ts = TILED ? a.state + tiled_offset(i) : nullptr;
+        float* const ts = TILED ? a.state + tiled_offset(i) : nullptr;   // the element's master in the state
         float* const m_at = TILED ? ts + kStateTile : a.exp_avg + i;
         float* const v_at = TILED ? ts + 2 * kStateTile : a.exp_avg_sq + i;
         float m = *m_at, v = *v_at;
