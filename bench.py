@@ -170,6 +170,24 @@ def step_bytes_per_elem(w) -> dict:
             "grad_accum_norm_sq_last": last, "adamw_step": adamw, "step": accum + adamw}
 
 
+def step_kernel_rates(bpe: dict, n: int, r: dict) -> dict:
+    """Algorithmic bandwidth of each part of the timed step (HIP events on
+    the launch stream): the accumulations of every micro-batch but the last
+    (one overwriting launch and the rest accumulating, by time the largest
+    share of the step), the last micro-batch with the norm, and AdamW."""
+    parts = {
+        "grad_accum_all_but_last": (bpe["step"] - bpe["grad_accum_norm_sq_last"] - bpe["adamw_step"], r["accum_ms"]),
+        "grad_accum_norm_sq_last": (bpe["grad_accum_norm_sq_last"], r["last_ms"]),
+        "adamw_step_tiled": (bpe["adamw_step"], r["adamw_ms"]),
+    }
+    out = {}
+    for name, (b, ms) in parts.items():
+        gbps = b * n / (ms * 1e-3) / 1e9 if (ms > 0 and b > 0) else None
+        out[name] = {"bytes_per_elem": b, "ms": ms, "gbps": gbps,
+                     "frac": gbps / HBM_PEAK_GBPS if gbps is not None else None}
+    return out
+
+
 def ceiling_report(ms_by_lds: dict, nbytes: int, adamw_ms: float) -> dict:
     """The AdamW-traffic kernel's time at each residency cap, its best, and
     the AdamW step's bandwidth as a fraction of that best."""
@@ -650,6 +668,7 @@ def main():
         "step_hbm_frac": step_gbps / HBM_PEAK_GBPS,
         "kernels_ms": {"grad_accum_all_but_last": r["accum_ms"], "grad_accum_norm_sq_last": r["last_ms"],
                        "adamw_step_tiled": r["adamw_ms"]},
+        "step_kernels": step_kernel_rates(bpe, n, r),
         "bytes_per_elem": bpe,
         "device_copy_gbps": r["copy_gbps"],
         "timing_events": timing_events(),
