@@ -1,6 +1,7 @@
 """Property tests of the C ABI's host-side validation (CPU only).
 
-Random argument sets for adamw_step, flat_pack and flat_unpack: sizes,
+Random argument sets for adamw_step, flat_pack and flat_unpack, and for
+the tiled-state calls (adamw_step_tiled, state_tile, state_untile): sizes,
 alignments, null pointers, overlapping buffers and hyperparameters.  A
 Python model of the rules include/zshard.h documents (and of the order in
 which they are checked) predicts each return code.  Only argument sets the
@@ -172,3 +173,126 @@ def test_flat_validation_matches_the_documented_rules(tensors, flat, dts, pad, u
     else:
         got = L.flat_pack(arr, count, t_dt, flat or None, flat_dt, padded, None)
     assert got == want, (tensors, count, hex(flat), flat_dt, t_dt, padded, unpack)
+
+
+# ---------------------------------------------------------------------------
+# tiled state: adamw_step_tiled, state_tile, state_untile
+# ---------------------------------------------------------------------------
+
+TILE = 8192   # ZS_STATE_TILE (test_abi checks the header against this value)
+
+
+def tiled_bytes(n):
+    return 4 * 3 * TILE * (-(-n // TILE))
+
+
+# slots 64 KiB apart: a tiled state of up to one tile (96 KiB) overlaps the next slot or two
+big_pointers = st.sampled_from([0] + [None] * 9).flatmap(
+    lambda z: st.just(0) if z == 0 else st.builds(lambda slot, off: BASE + slot * 65536 + off, st.integers(0, 7),
+                                                    st.sampled_from([0, 0, 0, 4, 8, 16, 64, 1, 2, 6])))
+tiled_sizes = st.sampled_from([-1, 0, 1, 3, 1000, 5000, 8192, 9000, MAX_ELEMS + 1])
+
+
+def hp_model(hp, n, norm):
+    """adamw_step's shared hyperparameter, size and norm-alignment checks."""
+    lr, b1, b2, eps, wd, scale, max_norm, extra, step = hp
+    if not (0 <= n <= MAX_ELEMS) or step < 1:
+        return EINVAL
+    if not (0.0 <= b1 < 1.0) or not (0.0 <= b2 < 1.0):
+        return EINVAL
+    if not (eps > 0.0 and math.isfinite(eps)) or not (lr >= 0.0 and math.isfinite(lr)):
+        return EINVAL
+    if not (wd >= 0.0 and math.isfinite(wd)) or not (scale > 0.0 and math.isfinite(scale)):
+        return EINVAL
+    if math.isnan(max_norm) or extra < 0.0:
+        return EINVAL
+    if norm and norm % 8:
+        return EINVAL
+    return None
+
+
+def tiled_step_model(hp, state, g, b, n, norm):
+    rc = hp_model(hp, n, norm)
+    if rc is not None:
+        return rc
+    if n == 0:
+        return OK
+    if not (state and g):
+        return EINVAL
+    if state % 16 or g % 4 or (b and b % 2):
+        return EINVAL
+    bufs = [(state, tiled_bytes(n), True), (g, 4 * n, False), (b, 2 * n if b else 0, True)]
+    for i in range(3):
+        for j in range(i + 1, 3):
+            if overlap(bufs[i][0], bufs[i][1], bufs[j][0], bufs[j][1]):
+                return EOVERLAP
+        if norm and bufs[i][2] and overlap(bufs[i][0], bufs[i][1], norm, 8):
+            return EOVERLAP
+    return None
+
+
+@SETTINGS
+@given(hp=hyperparameters(), ptrs=st.tuples(big_pointers, big_pointers, big_pointers), n=tiled_sizes,
+       norm=st.one_of(st.just(0), st.builds(lambda slot, off: BASE + slot * 65536 + off,
+                                            st.integers(0, 7), st.sampled_from([0, 8, 40000, 4]))))
+def test_adamw_step_tiled_validation_matches_the_documented_rules(hp, ptrs, n, norm):
+    state, g, b = ptrs
+    want = tiled_step_model(hp, state, g, b, n, norm)
+    if want is None:
+        return   # a valid call would launch a kernel: not made here
+    c = B.AdamW(*hp[:8], hp[8])
+    got = zs.lib().adamw_step_tiled(ctypes.byref(c), state or None, g or None, b or None, n, norm or None, None)
+    assert got == want, (hp, [hex(p) for p in ptrs], n, hex(norm))
+
+
+def tile_model(srcs, state, n):
+    if not (0 <= n <= MAX_ELEMS):
+        return EINVAL
+    if n == 0:
+        return OK
+    if not state or state % 16:
+        return EINVAL
+    for src in srcs:
+        if src and src % 4:
+            return EINVAL
+        if src and overlap(src, 4 * n, state, tiled_bytes(n)):
+            return EOVERLAP
+    return None
+
+
+def untile_model(state, dsts, n):
+    if not (0 <= n <= MAX_ELEMS):
+        return EINVAL
+    if n == 0:
+        return OK
+    if not state or state % 16:
+        return EINVAL
+    for k, d in enumerate(dsts):
+        if not d:
+            continue
+        if d % 4:
+            return EINVAL
+        if overlap(d, 4 * n, state, tiled_bytes(n)):
+            return EOVERLAP
+        for e in dsts[k + 1:]:
+            if e and overlap(d, 4 * n, e, 4 * n):
+                return EOVERLAP
+    return None
+
+
+@SETTINGS
+@given(ptrs=st.tuples(big_pointers, big_pointers, big_pointers, big_pointers), n=tiled_sizes, untile=st.booleans())
+def test_state_tile_validation_matches_the_documented_rules(ptrs, n, untile):
+    a, b, c, state = ptrs
+    L = zs.lib()
+    if untile:
+        want = untile_model(state, (a, b, c), n)
+        if want is None:
+            return
+        got = L.state_untile(state or None, a or None, b or None, c or None, n, None)
+    else:
+        want = tile_model((a, b, c), state, n)
+        if want is None:
+            return
+        got = L.state_tile(a or None, b or None, c or None, state or None, n, None)
+    assert got == want, (untile, [hex(p) for p in ptrs], n)
