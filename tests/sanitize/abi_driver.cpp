@@ -55,6 +55,23 @@ int main() {
                                nullptr) == ZS_EINVAL, 6);
     CHECK(adam_update(&hp, f, f + 1024, f + 2048, f + 4096, 8, nullptr, nullptr) == ZS_EINVAL, 6);   // decay
 
+    // tiled state: sizes near the per-call limit, overlaps with the state's padded end, misalignment
+    CHECK(state_tiled_numel(-1) == -1 && state_tiled_numel((int64_t(1) << 39) + 1) == -1, 14);
+    CHECK(state_tiled_numel(int64_t(1) << 39) == 3 * (int64_t(1) << 39), 14);
+    CHECK(state_tiled_numel(1) == 3 * ZS_STATE_TILE, 14);
+    float* st = static_cast<float*>(fake(1ull << 32));
+    CHECK(adamw_step_tiled(&bad, st, f, nullptr, 16, nullptr, nullptr) == ZS_EINVAL, 15);
+    CHECK(adamw_step_tiled(&hp, st + 1, f, nullptr, 16, nullptr, nullptr) == ZS_EINVAL, 15);   // state off 16 bytes
+    CHECK(adamw_step_tiled(&hp, st, st + 3 * ZS_STATE_TILE - 1, nullptr, 16, nullptr, nullptr) == ZS_EOVERLAP, 15);
+    CHECK(adamw_step_tiled(&hp, st, f, nullptr, int64_t(1) << 40, nullptr, nullptr) == ZS_EINVAL, 15);
+    CHECK(adamw_step_tiled(&hp, st, f, nullptr, 0, nullptr, nullptr) == ZS_OK, 15);
+    CHECK(adamw_step_tiled_dev(nullptr, st, f, nullptr, 16, nullptr, nullptr) == ZS_EINVAL, 15);
+    CHECK(state_tile(f, nullptr, st + 100, st, 16, nullptr) == ZS_EOVERLAP, 16);
+    CHECK(state_tile(f, nullptr, nullptr, st + 2, 16, nullptr) == ZS_EINVAL, 16);
+    CHECK(state_untile(st, f, f + 8, nullptr, 16, nullptr) == ZS_EOVERLAP, 16);
+    CHECK(state_untile(st, f, nullptr, nullptr, int64_t(1) << 40, nullptr) == ZS_EINVAL, 16);
+    CHECK(state_untile(st, nullptr, nullptr, nullptr, 0, nullptr) == ZS_OK, 16);
+
     CHECK(grad_accum(f, f + 1, 3, 8, 0, nullptr) == ZS_EINVAL, 7);
     CHECK(grad_accum(f, f + 1, ZS_F32, 8, 0, nullptr) == ZS_EOVERLAP, 7);
     CHECK(grad_accum(f, f + 1, ZS_F32, 0, 0, nullptr) == ZS_OK, 7);
