@@ -447,6 +447,25 @@ def test_ceiling_library_rejects_before_launch():
     assert t(a, a + 64, None, 16, 70000, None) == -1
 
 
+def test_plain_c_consumer(tmp_path):
+    """include/zshard.h compiles as strict C11 and libzshard.so links from C:
+    tests/c_consumer.c (host-only calls and rejecting paths) builds with gcc
+    -Wall -Wextra -Wpedantic -Werror and runs clean."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    exe = str(tmp_path / "c_consumer")
+    libdir = os.path.dirname(B.LIB_PATH)
+    subprocess.run([gcc, "-std=c11", "-Wall", "-Wextra", "-Wpedantic", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    "-o", exe, os.path.join(ROOT, "tests", "c_consumer.c"), B.LIB_PATH,
+                    f"-Wl,-rpath,{libdir}"], check=True)
+    out = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, (out.returncode, out.stderr)
+    assert out.stdout.strip() == "c consumer: ok"
+
+
 def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
     """No fallback path: with the library absent every call raises."""
     monkeypatch.setattr(B, "_lib", None)
