@@ -33,10 +33,11 @@
 // gfx950's 160 KiB per CU (12 KiB, 13 per CU, for the six-stream forms).  Eight concurrent streams per element (4 read,
 // 4 written) otherwise keep too many DRAM rows open at once; on gfx950 the
 // cap lifts the kernel from 74 % to 83 % of the 8 TB/s peak (fewer waves:
-// 64-71 %; more: 73-81 %).  A misaligned shard (a view whose element offset
-// is not a multiple of 4) takes the VEC = 1 instantiation of the same code,
-// in 256-thread workgroups without the cap; the read-only gradient alone may
-// sit at any 4-byte boundary on the vector path.
+// 64-71 %; more: 73-81 %).  A shard whose master or moments are views at an
+// element offset that is not a multiple of 4 takes the VEC = 1 instantiation
+// of the same code, in 256-thread workgroups without the cap; the read-only
+// gradient may sit at any 4-byte boundary and the write-only output (bf16
+// re-cast, ZeRO-1 update) at any element offset on the vector path.
 #include "zs_common.h"
 
 namespace zs {
@@ -108,9 +109,15 @@ enum Form : int { kMaster = 0, kMasterBf16 = 1, kNoMaster = 2, kUpdate = 3 };
 // the caller copied in beforehand.
 // TILED: master, exp_avg and exp_avg_sq come from the tiled state buffer
 // (master forms only); 4 consecutive elements never straddle a tile.
-template <int VEC, int FORM, int BS, bool DEV, bool TILED = false>
+// OUT_ALIGNED = false: the one output stream that is only written, the bf16
+// re-cast or the ZeRO-1 update, starts off a 16-byte boundary (a view at
+// any element offset of a larger buffer); the vector path then writes it
+// element by element (16- or 32-bit stores) and keeps 128-bit accesses for
+// everything else: 81 % of the peak against 65 % for the element-wise path.
+template <int VEC, int FORM, int BS, bool DEV, bool TILED = false, bool OUT_ALIGNED = true>
 __global__ __launch_bounds__(BS) void adamw_kernel(const AdamwArgs a) {
     static_assert(!TILED || FORM == kMaster || FORM == kMasterBf16, "tiled state holds a master");
+    static_assert(OUT_ALIGNED || FORM == kMasterBf16 || FORM == kUpdate, "a write-only output to split");
     constexpr bool kReadP = FORM != kUpdate;
     const AdamwScalars sc = DEV ? *a.sc_dev : a.sc;
     const int64_t n = a.n;
@@ -161,13 +168,25 @@ __global__ __launch_bounds__(BS) void adamw_kernel(const AdamwArgs a) {
         }
         if constexpr (FORM == kMaster || FORM == kMasterBf16)
             st_stream(reinterpret_cast<f32x4*>(p_at), f32x4{ps[0], ps[1], ps[2], ps[3]});
-        if constexpr (FORM == kUpdate)
-            st_stream(reinterpret_cast<f32x4*>(a.update + first), f32x4{ps[0], ps[1], ps[2], ps[3]});
+        if constexpr (FORM == kUpdate) {
+            if constexpr (OUT_ALIGNED) {
+                st_stream(reinterpret_cast<f32x4*>(a.update + first), f32x4{ps[0], ps[1], ps[2], ps[3]});
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) st_stream(a.update + first + j, ps[j]);
+            }
+        }
         st_stream(reinterpret_cast<f32x4*>(m_at), f32x4{ms[0], ms[1], ms[2], ms[3]});
         st_stream(reinterpret_cast<f32x4*>(v_at), f32x4{vs[0], vs[1], vs[2], vs[3]});
-        if constexpr (FORM == kMasterBf16 || FORM == kNoMaster)
-            st_stream(reinterpret_cast<u32x2*>(a.param_bf16 + first),
-                      u32x2{pack_bf16x2(ps[0], ps[1]), pack_bf16x2(ps[2], ps[3])});
+        if constexpr (FORM == kMasterBf16 || FORM == kNoMaster) {
+            if constexpr (OUT_ALIGNED) {
+                st_stream(reinterpret_cast<u32x2*>(a.param_bf16 + first),
+                          u32x2{pack_bf16x2(ps[0], ps[1]), pack_bf16x2(ps[2], ps[3])});
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) st_stream(a.param_bf16 + first + j, (uint16_t)f32_to_bf16_rne(ps[j]));
+            }
+        }
         return;
     }
     // scalar path: VEC == 1, or the ragged tail of the VEC == 4 grid
@@ -200,7 +219,7 @@ T* advance(T* p, int64_t off) { return p == nullptr ? nullptr : p + off; }
 
 // one launch per kLaunchElems elements, each on its own slice of the buffers
 // (a multiple of kStateTile: a piece of the tiled state starts at 3*off)
-template <int VEC, int FORM, int BS, bool DEV, bool TILED = false>
+template <int VEC, int FORM, int BS, bool DEV, bool TILED = false, bool OUT_ALIGNED = true>
 hipError_t launch(const AdamwArgs& a, unsigned lds, hipStream_t stream) {
     static_assert(kLaunchElems % kStateTile == 0, "launch pieces start on a tile");
     for (int64_t off = 0; off < a.n; off += kLaunchElems) {
@@ -214,46 +233,54 @@ hipError_t launch(const AdamwArgs& a, unsigned lds, hipStream_t stream) {
         p.param_bf16 = advance(a.param_bf16, off);
         p.update = advance(a.update, off);
         const int64_t blocks = ((p.n + VEC - 1) / VEC + BS - 1) / BS;
-        hipLaunchKernelGGL((adamw_kernel<VEC, FORM, BS, DEV, TILED>), dim3((unsigned)blocks), dim3(BS), lds, stream,
-                           p);
+        hipLaunchKernelGGL((adamw_kernel<VEC, FORM, BS, DEV, TILED, OUT_ALIGNED>), dim3((unsigned)blocks), dim3(BS),
+                           lds, stream, p);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
 }
 
+// vec_ok: the vector path's alignment holds for every stream but the
+// write-only output; out_aligned: that output (bf16 re-cast or update) is
+// 16-byte aligned too.  The tiled state is 16-byte aligned by contract, so
+// the tiled forms always take the vector path.
 template <int FORM, bool DEV = false, bool TILED = false>
-hipError_t launch_form(const AdamwArgs& a, bool vec_ok, hipStream_t stream) {
+hipError_t launch_form(const AdamwArgs& a, bool vec_ok, bool out_aligned, hipStream_t stream) {
     constexpr unsigned lds = TILED ? kVecLdsReserveTiled
                              : (FORM == kNoMaster || FORM == kUpdate) ? kVecLdsReserve6 : kVecLdsReserve;
+    if constexpr (FORM == kMasterBf16 || FORM == kUpdate) {
+        if (vec_ok && !out_aligned) return launch<4, FORM, kVecBlock, DEV, TILED, false>(a, lds, stream);
+    }
     if (vec_ok) return launch<4, FORM, kVecBlock, DEV, TILED>(a, lds, stream);
-    return launch<1, FORM, kBlock, DEV, TILED>(a, 0, stream);
+    if constexpr (TILED) return hipErrorInvalidValue;   // not reached: the entry point always passes vec_ok
+    else return launch<1, FORM, kBlock, DEV, TILED>(a, 0, stream);
 }
 
 }  // namespace
 
-hipError_t launch_adamw(const AdamwArgs& a, bool vec_ok, hipStream_t stream) {
+hipError_t launch_adamw(const AdamwArgs& a, bool vec_ok, bool out_aligned, hipStream_t stream) {
     if (a.sc_dev != nullptr)
-        return a.param_bf16 != nullptr ? launch_form<kMasterBf16, true>(a, vec_ok, stream)
-                                       : launch_form<kMaster, true>(a, vec_ok, stream);
-    return a.param_bf16 != nullptr ? launch_form<kMasterBf16>(a, vec_ok, stream)
-                                   : launch_form<kMaster>(a, vec_ok, stream);
+        return a.param_bf16 != nullptr ? launch_form<kMasterBf16, true>(a, vec_ok, out_aligned, stream)
+                                       : launch_form<kMaster, true>(a, vec_ok, true, stream);
+    return a.param_bf16 != nullptr ? launch_form<kMasterBf16>(a, vec_ok, out_aligned, stream)
+                                   : launch_form<kMaster>(a, vec_ok, true, stream);
 }
 
-hipError_t launch_adamw_tiled(const AdamwArgs& a, bool vec_ok, hipStream_t stream) {
+hipError_t launch_adamw_tiled(const AdamwArgs& a, bool out_aligned, hipStream_t stream) {
     if (a.sc_dev != nullptr)
-        return a.param_bf16 != nullptr ? launch_form<kMasterBf16, true, true>(a, vec_ok, stream)
-                                       : launch_form<kMaster, true, true>(a, vec_ok, stream);
-    return a.param_bf16 != nullptr ? launch_form<kMasterBf16, false, true>(a, vec_ok, stream)
-                                   : launch_form<kMaster, false, true>(a, vec_ok, stream);
+        return a.param_bf16 != nullptr ? launch_form<kMasterBf16, true, true>(a, true, out_aligned, stream)
+                                       : launch_form<kMaster, true, true>(a, true, true, stream);
+    return a.param_bf16 != nullptr ? launch_form<kMasterBf16, false, true>(a, true, out_aligned, stream)
+                                   : launch_form<kMaster, false, true>(a, true, true, stream);
 }
 
 hipError_t launch_adamw_no_master(const AdamwArgs& a, bool vec_ok, hipStream_t stream) {
-    return launch_form<kNoMaster>(a, vec_ok, stream);
+    return launch_form<kNoMaster>(a, vec_ok, true, stream);
 }
 
-hipError_t launch_adam_update(const AdamwArgs& a, bool vec_ok, hipStream_t stream) {
-    return launch_form<kUpdate>(a, vec_ok, stream);
+hipError_t launch_adam_update(const AdamwArgs& a, bool vec_ok, bool out_aligned, hipStream_t stream) {
+    return launch_form<kUpdate>(a, vec_ok, out_aligned, stream);
 }
 
 }  // namespace zs

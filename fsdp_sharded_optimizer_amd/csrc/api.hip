@@ -274,10 +274,11 @@ static int32_t adamw_master(const zs_adamw* hp, const zs_adamw_scalars* sc_dev, 
     a.grad = grad;
     a.param_bf16 = param_bf16;
     a.n = n;
-    // written streams 16-byte aligned; the read-only gradient is 4-byte aligned already
-    const bool vec = aligned(master, 16) && aligned(exp_avg, 16) && aligned(exp_avg_sq, 16) &&
-                     (param_bf16 == nullptr || aligned(param_bf16, 16));
-    return hip_status(zs::launch_adamw(a, vec, as_stream(hip_stream)));
+    // the read-write state 16-byte aligned (the read-only gradient is 4-byte
+    // aligned already); the write-only bf16 output may sit at any element offset
+    const bool vec = aligned(master, 16) && aligned(exp_avg, 16) && aligned(exp_avg_sq, 16);
+    const bool out_aligned = param_bf16 == nullptr || aligned(param_bf16, 16);
+    return hip_status(zs::launch_adamw(a, vec, out_aligned, as_stream(hip_stream)));
 }
 
 int32_t adamw_step(const zs_adamw* hp, float* master, float* exp_avg, float* exp_avg_sq,
@@ -384,9 +385,10 @@ static int32_t adamw_tiled(const zs_adamw* hp, const zs_adamw_scalars* sc_dev, f
     a.grad = grad;
     a.param_bf16 = param_bf16;
     a.n = n;
-    // the state is 16-byte aligned by contract; the bf16 output decides the path
-    const bool vec = param_bf16 == nullptr || aligned(param_bf16, 16);
-    return hip_status(zs::launch_adamw_tiled(a, vec, as_stream(hip_stream)));
+    // the state is 16-byte aligned by contract, so the vector path always
+    // applies; a bf16 output off a 16-byte boundary is written element by element
+    const bool out_aligned = param_bf16 == nullptr || aligned(param_bf16, 16);
+    return hip_status(zs::launch_adamw_tiled(a, out_aligned, as_stream(hip_stream)));
 }
 
 int32_t adamw_step_tiled(const zs_adamw* hp, float* state, const float* grad, uint16_t* param_bf16, int64_t n,
@@ -445,8 +447,11 @@ int32_t adam_update(const zs_adamw* hp, float* exp_avg, float* exp_avg_sq, const
     a.grad = grad;
     a.update = update;
     a.n = n;
-    const bool vec = aligned(update, 16) && aligned(exp_avg, 16) && aligned(exp_avg_sq, 16);
-    return hip_status(zs::launch_adam_update(a, vec, as_stream(hip_stream)));
+    // the moments 16-byte aligned; the write-only update may sit at any element
+    // offset (a rank's chunk of the gathered buffer)
+    const bool vec = aligned(exp_avg, 16) && aligned(exp_avg_sq, 16);
+    const bool out_aligned = aligned(update, 16);
+    return hip_status(zs::launch_adam_update(a, vec, out_aligned, as_stream(hip_stream)));
 }
 
 // ---------------------------------------------------------------------------

@@ -114,10 +114,13 @@ constexpr int64_t kLaunchElems = int64_t(1) << 31;
 inline int64_t launch_piece(int64_t n, int64_t off) { return n - off < kLaunchElems ? n - off : kLaunchElems; }
 
 // Launchers: enqueue on `stream`, return the hipError_t of the (first failed) launch.
-hipError_t launch_adamw(const AdamwArgs& a, bool vec_ok, hipStream_t stream);
+// vec_ok: every stream but the write-only output (bf16 re-cast, ZeRO-1
+// update) allows the 128-bit path; out_aligned: that output is 16-byte
+// aligned as well (else it is written element by element on the same path).
+hipError_t launch_adamw(const AdamwArgs& a, bool vec_ok, bool out_aligned, hipStream_t stream);
 hipError_t launch_adamw_no_master(const AdamwArgs& a, bool vec_ok, hipStream_t stream);
-hipError_t launch_adam_update(const AdamwArgs& a, bool vec_ok, hipStream_t stream);
-hipError_t launch_adamw_tiled(const AdamwArgs& a, bool vec_ok, hipStream_t stream);
+hipError_t launch_adam_update(const AdamwArgs& a, bool vec_ok, bool out_aligned, hipStream_t stream);
+hipError_t launch_adamw_tiled(const AdamwArgs& a, bool out_aligned, hipStream_t stream);
 // split fp32 arrays (each nullable: zeros) -> tiled state, padding zeroed; and back
 // (each destination nullable: skipped)
 hipError_t launch_state_tile(const float* const src[3], float* state, int64_t n, hipStream_t stream);

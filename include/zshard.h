@@ -42,7 +42,10 @@
  *     a faster code path: 128-bit accesses when every buffer a call writes
  *     is 16-byte aligned and every buffer it only reads is 4-byte aligned
  *     (a view at any element offset of an fp32 buffer, or at an even one of
- *     a bf16 buffer); element-wise accesses otherwise.
+ *     a bf16 buffer); element-wise accesses otherwise.  The AdamW steps and
+ *     adam_update relax this for their one write-only output (param_bf16,
+ *     update): at any element offset it is written element by element while
+ *     everything else keeps the 128-bit path.
  *   - bf16 values are passed as their 16-bit patterns (uint16_t).
  */
 #ifndef ZSHARD_H

@@ -246,6 +246,34 @@ def test_adamw_bit_exact_given_the_oracle_norm(n, offset, grad_off):
         assert canary_ok(gw, grad_off, n)
 
 
+@pytest.mark.parametrize("n", [7, 2049, 100_003])
+@pytest.mark.parametrize("b_off", [1, 2, 3])
+@pytest.mark.parametrize("grad_off", [0, 1])
+def test_adamw_bf16_output_at_any_offset(n, b_off, grad_off):
+    """Master and moments 16-byte aligned, the bf16 output a view at element
+    offset 1, 2 or 3 (the 128-bit path with element-wise bf16 stores): five
+    clipped steps bit-identical to the oracle given its norm, the bf16
+    buffer's canaries on both sides untouched."""
+    print(f"adamw bf16 output offset n={n} b_off={b_off} grad_off={grad_off}", flush=True)
+    rng = np.random.default_rng(n + 7 * b_off + grad_off)
+    p_ref = rng.uniform(-0.1, 0.1, n).astype(np.float32)
+    m_ref, v_ref, b_ref = np.zeros(n, np.float32), np.zeros(n, np.float32), np.zeros(n, np.uint16)
+    p, _ = dev_buf(p_ref, 0)
+    m, _ = dev_buf(m_ref, 0)
+    v, _ = dev_buf(v_ref, 0)
+    b, bw = dev_buf(b_ref, b_off, bf16=True)
+    for t in range(1, 6):
+        acc = (rng.standard_normal(n) * 1e-2).astype(np.float32)
+        S = oracle.grad_norm_sq(acc, 1 / 32)
+        hp_gpu, hp_orc = _hp(t, scale=1 / 32, max_norm=math.sqrt(S) * 0.8 if t % 2 else 0.0, extra=0.25 * S)
+        oracle.adamw_step(hp_orc, p_ref, m_ref, v_ref, acc, b_ref, norm_sq=S)
+        g, _ = dev_buf(acc, grad_off)
+        zs.adamw_step(hp_gpu, p, m, v, g, b, norm_sq=torch.tensor([S], dtype=torch.float64, device="cuda"))
+        for name, gpu, ref in (("p", p, p_ref), ("m", m, m_ref), ("v", v, v_ref), ("b", b, b_ref)):
+            assert bits_equal(to_np(gpu), ref), (t, name, identical_fraction(to_np(gpu), ref))
+        assert canary_ok(bw, b_off, n)
+
+
 def test_adamw_skips_on_nonfinite_norm():
     n = 4099
     rng = np.random.default_rng(5)
@@ -483,7 +511,7 @@ def test_no_master_stalls_on_the_gpu():
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("n", [1, 7, 4097, 100_003])
-@pytest.mark.parametrize("offset,upd_off", [(0, 0), (1, 1), (3, 3), (1, 0), (3, 0)])
+@pytest.mark.parametrize("offset,upd_off", [(0, 0), (1, 1), (3, 3), (1, 0), (3, 0), (0, 1), (0, 2), (0, 3)])
 @pytest.mark.parametrize("clip", [False, True])
 def test_adam_update_bit_exact(n, offset, upd_off, clip):
     """The gradient (and the update) as views at any element offset, as a
@@ -740,13 +768,17 @@ def test_adam_update_and_no_master_special_values():
 # every size from 0 to 257, aligned and as misaligned views
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("offset", [0, 1])
-def test_every_small_size(offset):
+@pytest.mark.parametrize("offset,out_off", [(0, 0), (1, 1), (0, 1), (0, 2), (0, 3)])
+def test_every_small_size(offset, out_off):
     """Each entry point at every n in [0, 257] (all tails of the 4- and
     8-element vectors and of the first workgroup tiles), against the oracle:
-    accumulations, reductions and the three step forms bit-exact, the norm
-    within the bar, flatten and unflatten of a random 3-way split bit-exact."""
-    rng = np.random.default_rng(1234 + offset)
+    accumulations, reductions and the step forms (split and tiled state)
+    bit-exact, the norm within the bar, flatten and unflatten of a random
+    3-way split bit-exact.  out_off places the write-only outputs (the bf16
+    re-cast, the ZeRO-1 update) at their own element offset: with every
+    other buffer aligned that is the 128-bit path with element-wise output
+    stores."""
+    rng = np.random.default_rng(1234 + offset + 10 * out_off)
     norm = torch.zeros(1, dtype=torch.float64, device="cuda")
     for n in range(0, 258):
         g32 = (rng.standard_normal(n) * 1e-2).astype(np.float32)
@@ -787,17 +819,26 @@ def test_every_small_size(offset):
         v0 = (rng.uniform(0, 1e-7, n)).astype(np.float32)
         pr, mr, vr, br = p0.copy(), m0.copy(), v0.copy(), np.zeros(n, np.uint16)
         oracle.adamw_step(hp_orc, pr, mr, vr, g32, br, norm_sq=S)
-        p, m, v, b = dev_buf(p0, offset)[0], dev_buf(m0, offset)[0], dev_buf(v0, offset)[0], \
-            dev_buf(np.zeros(n, np.uint16), offset, bf16=True)[0]
+        p, m, v = dev_buf(p0, offset)[0], dev_buf(m0, offset)[0], dev_buf(v0, offset)[0]
+        b, bw = dev_buf(np.zeros(n, np.uint16), out_off, bf16=True)
         zs.adamw_step(hp_gpu, p, m, v, dev_buf(g32, offset)[0], b, norm_sq=nrm)
         for name, x, r in (("p", p, pr), ("m", m, mr), ("v", v, vr), ("b", b, br)):
             assert bits_equal(to_np(x), r), ("adamw_step", n, name)
+        assert canary_ok(bw, out_off, n), ("adamw_step bf16 canary", n)
+        st, stw = dev_buf(oracle.state_tile(p0, m0, v0, n, 8192), 0)
+        bt, btw = dev_buf(np.zeros(n, np.uint16), out_off, bf16=True)
+        zs.adamw_step_tiled(hp_gpu, st, dev_buf(g32, offset)[0], bt, norm_sq=nrm)
+        assert bits_equal(to_np(st), oracle.state_tile(pr, mr, vr, n, 8192)), ("adamw_step_tiled", n)
+        assert bits_equal(to_np(bt), br) and canary_ok(btw, out_off, n) and canary_ok(stw, 0, st.numel()), \
+            ("adamw_step_tiled bf16", n)
         mu, vu, uu = m0.copy(), v0.copy(), np.empty(n, np.float32)
         oracle.adam_update(hp0_orc, mu, vu, g32, uu, norm_sq=S)
-        m, v, u = dev_buf(m0, offset)[0], dev_buf(v0, offset)[0], dev_buf(np.zeros(n, np.float32), offset)[0]
+        m, v = dev_buf(m0, offset)[0], dev_buf(v0, offset)[0]
+        u, uw = dev_buf(np.zeros(n, np.float32), out_off)
         zs.adam_update(hp0_gpu, m, v, dev_buf(g32, offset)[0], u, norm_sq=nrm)
         for name, x, r in (("update", u, uu), ("m", m, mu), ("v", v, vu)):
             assert bits_equal(to_np(x), r), ("adam_update", n, name)
+        assert canary_ok(uw, out_off, n), ("adam_update canary", n)
         b0 = oracle.bf16_rne(p0)
         bn, mn, vn = b0.copy(), m0.copy(), v0.copy()
         oracle.adamw_step_no_master(hp_orc, bn, mn, vn, g32, norm_sq=S)

@@ -161,7 +161,7 @@ def test_tiled_state_across_pieces(b_off):
     elements (a launch piece starts the tiled state 3 * 2^31 floats in):
     the state read at the layout's positions and the untiled arrays
     bit-exact on the sample.  b_off = 1 puts the bf16 output off a 16-byte
-    boundary (the element-wise path, 2^31 work-items per piece)."""
+    boundary (element-wise bf16 stores inside the 128-bit path)."""
     need_gib(72)
     log(f"tiled state across pieces n={N} bf16 offset={b_off}")
     idx = sample_indices(N, seed=61 + b_off)

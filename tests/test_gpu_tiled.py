@@ -5,8 +5,8 @@ buffer, three runs of ZS_STATE_TILE floats per tile of elements.  The
 conversions must match the oracle's layout bit for bit (padding included);
 the tiled AdamW step, read back through the oracle's untile, must meet the
 same bar as adamw_step and, handed the oracle's norm, be bit-identical to the
-oracle.  Sizes span several tiles, ragged ends and the scalar path (a bf16
-output off a 16-byte boundary).  Every buffer carries a canary tail.
+oracle.  Sizes span several tiles and ragged ends, with the bf16 output at
+every element offset modulo 4.  Every buffer carries a canary tail.
 """
 import math
 
@@ -82,13 +82,14 @@ def test_state_tile_all_sources_missing_and_empty():
 
 
 @pytest.mark.parametrize("n", SIZES)
-@pytest.mark.parametrize("b_off", [0, 1])
+@pytest.mark.parametrize("b_off", [0, 1, 2, 3])
 @pytest.mark.parametrize("mode", ["adam_f32", "adamw_bf16", "adamw_bf16_clip"])
 def test_adamw_step_tiled_parity(n, b_off, mode):
     """Three steps on a tiled state; after each, the state read back through
     the oracle's untile meets the bar against the oracle on split arrays,
-    and the padding of the last tile is untouched.  b_off = 1 puts the bf16
-    output off a 16-byte boundary (the element-wise path)."""
+    and the padding of the last tile is untouched.  b_off = 1..3 puts the
+    bf16 output off a 16-byte boundary (element-wise bf16 stores inside the
+    128-bit path)."""
     print(f"adamw tiled n={n} b_off={b_off} mode={mode}", flush=True)
     rng = np.random.default_rng(n * 5 + b_off + len(mode))
     p_ref = rng.uniform(-0.1, 0.1, n).astype(np.float32)
