@@ -168,6 +168,24 @@ int32_t grad_accum_norm_sq(float* acc, const void* grad, int32_t grad_dtype, int
                                                     as_stream(hip_stream)));
 }
 
+// Elements to run element by element before the vector path when every
+// buffer of `bufs` (fp32, read and written by the step) sits at the same
+// offset off a 128-byte boundary: advancing all of them by that many elements
+// (1-31, at most n) puts each wave's 1 KiB accesses on whole cache lines.
+// A read-modify-write stream that is 16-byte aligned but not line aligned
+// runs the vector path at 59-64 % of the HBM peak on gfx950 (waves share
+// partly written lines), below the element-wise path's 65 %; peeled, 78-80 %.
+// 0 when the buffers are line aligned already or their offsets differ.
+constexpr uintptr_t kLineBytes = 128;
+static int64_t shared_head(float* const* bufs, int count, int64_t n) {
+    const uintptr_t off = addr(bufs[0]) & (kLineBytes - 1);
+    if (off == 0) return 0;
+    for (int i = 1; i < count; ++i)
+        if ((addr(bufs[i]) & (kLineBytes - 1)) != off) return 0;
+    const int64_t head = (int64_t)((kLineBytes - off) / 4);   // off is a multiple of 4 (fp32 alignment)
+    return head < n ? head : n;
+}
+
 static int32_t adamw_check_hp(const zs_adamw* hp, int64_t n, const double* norm_sq_dev) {
     if (hp == nullptr || !size_ok(n)) return ZS_EINVAL;
     if (hp->step < 1) return ZS_EINVAL;
@@ -275,9 +293,26 @@ static int32_t adamw_master(const zs_adamw* hp, const zs_adamw_scalars* sc_dev, 
     a.param_bf16 = param_bf16;
     a.n = n;
     // the read-write state 16-byte aligned (the read-only gradient is 4-byte
-    // aligned already); the write-only bf16 output may sit at any element offset
-    const bool vec = aligned(master, 16) && aligned(exp_avg, 16) && aligned(exp_avg_sq, 16);
-    const bool out_aligned = param_bf16 == nullptr || aligned(param_bf16, 16);
+    // aligned already); the write-only bf16 output may sit at any element
+    // offset.  Views sharing one offset off a 128-byte boundary run their
+    // first 1-31 elements element by element and the rest on the vector path.
+    float* const state[3] = {master, exp_avg, exp_avg_sq};
+    const int64_t head = shared_head(state, 3, n);
+    if (head > 0) {
+        zs::AdamwArgs h = a;
+        h.n = head;
+        rc = hip_status(zs::launch_adamw(h, false, true, as_stream(hip_stream)));
+        if (rc != ZS_OK) return rc;
+        a.master += head;
+        a.exp_avg += head;
+        a.exp_avg_sq += head;
+        a.grad += head;
+        if (a.param_bf16 != nullptr) a.param_bf16 += head;
+        a.n -= head;
+    }
+    const bool vec = aligned(a.master, 16) && aligned(a.exp_avg, 16) && aligned(a.exp_avg_sq, 16);
+    const bool out_aligned = a.param_bf16 == nullptr || aligned(a.param_bf16, 16);
+    if (a.n == 0) return ZS_OK;
     return hip_status(zs::launch_adamw(a, vec, out_aligned, as_stream(hip_stream)));
 }
 
@@ -448,9 +483,25 @@ int32_t adam_update(const zs_adamw* hp, float* exp_avg, float* exp_avg_sq, const
     a.update = update;
     a.n = n;
     // the moments 16-byte aligned; the write-only update may sit at any element
-    // offset (a rank's chunk of the gathered buffer)
-    const bool vec = aligned(exp_avg, 16) && aligned(exp_avg_sq, 16);
-    const bool out_aligned = aligned(update, 16);
+    // offset (a rank's chunk of the gathered buffer).  Moments sharing one
+    // offset off a 128-byte boundary run their first 1-31 elements element by
+    // element and the rest on the vector path.
+    float* const moments[2] = {exp_avg, exp_avg_sq};
+    const int64_t head = shared_head(moments, 2, n);
+    if (head > 0) {
+        zs::AdamwArgs h = a;
+        h.n = head;
+        rc = hip_status(zs::launch_adam_update(h, false, true, as_stream(hip_stream)));
+        if (rc != ZS_OK) return rc;
+        a.exp_avg += head;
+        a.exp_avg_sq += head;
+        a.grad += head;
+        a.update += head;
+        a.n -= head;
+    }
+    const bool vec = aligned(a.exp_avg, 16) && aligned(a.exp_avg_sq, 16);
+    const bool out_aligned = aligned(a.update, 16);
+    if (a.n == 0) return ZS_OK;
     return hip_status(zs::launch_adam_update(a, vec, out_aligned, as_stream(hip_stream)));
 }
 

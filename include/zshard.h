@@ -45,7 +45,11 @@
  *     a bf16 buffer); element-wise accesses otherwise.  The AdamW steps and
  *     adam_update relax this for their one write-only output (param_bf16,
  *     update): at any element offset it is written element by element while
- *     everything else keeps the 128-bit path.
+ *     everything else keeps the 128-bit path.  Full speed wants buffers that
+ *     are read and written to start on a 128-byte boundary (whole cache lines
+ *     per wave); adamw_step, adamw_step_dev and adam_update run the first
+ *     1-31 elements of views that share one offset off that boundary element
+ *     by element and the rest on the 128-bit path.
  *   - bf16 values are passed as their 16-bit patterns (uint16_t).
  */
 #ifndef ZSHARD_H

@@ -274,6 +274,47 @@ def test_adamw_bf16_output_at_any_offset(n, b_off, grad_off):
         assert canary_ok(bw, b_off, n)
 
 
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 7, 31, 32, 33, 2049, 100_003])
+@pytest.mark.parametrize("off", [1, 2, 3, 4, 8, 31])
+def test_shared_offset_views_peel_their_head(n, off):
+    """Master and moments (adamw_step), or the moments (adam_update), as
+    views sharing one element offset off a 128-byte boundary, with the bf16
+    output, the update and the gradient at other offsets: the call runs its
+    first 1-31 elements element by element and the rest on the vector path.
+    Three clipped steps bit-identical to the oracle given its norm, every
+    canary untouched (also when n is shorter than the head)."""
+    print(f"shared offset n={n} off={off}", flush=True)
+    rng = np.random.default_rng(100 * n + off)
+    p_ref = rng.uniform(-0.1, 0.1, n).astype(np.float32)
+    m_ref, v_ref, b_ref = np.zeros(n, np.float32), np.zeros(n, np.float32), np.zeros(n, np.uint16)
+    m2_ref, v2_ref, u_ref = np.zeros(n, np.float32), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    p, pw = dev_buf(p_ref, off)
+    m, mw = dev_buf(m_ref, off)
+    v, vw = dev_buf(v_ref, off)
+    b, bw = dev_buf(b_ref, (off + 1) % 4, bf16=True)
+    m2, m2w = dev_buf(m2_ref, off)
+    v2, v2w = dev_buf(v2_ref, off)
+    u, uw = dev_buf(u_ref, (off + 3) % 4)
+    for t in range(1, 4):
+        acc = (rng.standard_normal(n) * 1e-2).astype(np.float32)
+        S = oracle.grad_norm_sq(acc, 1 / 16)
+        norm = torch.tensor([S], dtype=torch.float64, device="cuda")
+        g, gw = dev_buf(acc, (off + 2) % 4)
+        hp_gpu, hp_orc = _hp(t, scale=1 / 16, max_norm=0.6 * math.sqrt(S), extra=0.1 * S)
+        hu_gpu, hu_orc = _hp(t, wd=0.0, scale=1 / 16, max_norm=0.6 * math.sqrt(S), extra=0.1 * S)
+        oracle.adamw_step(hp_orc, p_ref, m_ref, v_ref, acc, b_ref, norm_sq=S)
+        oracle.adam_update(hu_orc, m2_ref, v2_ref, acc, u_ref, norm_sq=S)
+        zs.adamw_step(hp_gpu, p, m, v, g, b, norm_sq=norm)
+        zs.adam_update(hu_gpu, m2, v2, g, u, norm_sq=norm)
+        for name, gpu, ref in (("p", p, p_ref), ("m", m, m_ref), ("v", v, v_ref), ("b", b, b_ref),
+                               ("m2", m2, m2_ref), ("v2", v2, v2_ref), ("update", u, u_ref)):
+            assert bits_equal(to_np(gpu), ref), (t, name, identical_fraction(to_np(gpu), ref))
+        assert canary_ok(gw, (off + 2) % 4, n)
+    for whole, o in ((pw, off), (mw, off), (vw, off), (bw, (off + 1) % 4), (m2w, off), (v2w, off),
+                     (uw, (off + 3) % 4)):
+        assert canary_ok(whole, o, n)
+
+
 def test_adamw_skips_on_nonfinite_norm():
     n = 4099
     rng = np.random.default_rng(5)
