@@ -1,0 +1,136 @@
+/*
+ * One rank's optimizer step driven from C through libzshard.so on the GPU,
+ * checked against the oracle (liboracle.so, linked here as test
+ * infrastructure).  Built and run by tests/test_gpu_c_abi.py with gcc
+ * -std=c11: the C ABI used the way the header documents it, with device
+ * memory from hipMalloc and the default stream.
+ *
+ * A ragged shard of n elements: three bf16 micro-batches accumulated in fp32
+ * (grad_accum twice, grad_accum_norm_sq for the last), the master tiled into
+ * the tiled state (state_tile), one clipped AdamW step (adamw_step_tiled) with
+ * the bf16 re-cast, then state_untile.  Inputs come from a counter-based
+ * generator in this file and feed both sides.  The GPU norm must be within
+ * 1e-5 of the oracle's; the step, handed the oracle's norm, must be
+ * bit-identical to the oracle's (accumulator, master, moments, bf16 output).
+ * Prints "c gpu step: ok" and exits 0, else the number of the failed check.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "zshard.h"
+
+/* oracle (tests only) */
+typedef struct {
+    double lr, beta1, beta2, eps, weight_decay, grad_scale, max_norm, extra_norm_sq;
+    int64_t step;
+} orc_adamw_hp;
+int orc_grad_accum(float* acc, const void* grad, int32_t grad_dtype, int64_t n, int32_t overwrite);
+double orc_grad_norm_sq(const float* acc, int64_t n, double grad_scale);
+int orc_adamw_step(const orc_adamw_hp* hp, float* master, float* exp_avg, float* exp_avg_sq, const float* grad,
+                   uint16_t* param_bf16, int64_t n, const double* norm_sq);
+
+#define CHECK(cond, code) do { if (!(cond)) { fprintf(stderr, "check %d failed: %s\n", code, #cond); return code; } } while (0)
+#define HIPOK(x, code) CHECK((x) == hipSuccess, code)
+
+/* splitmix64 of a counter: a uniform value in [0, 1) */
+static double uniform(uint64_t k)
+{
+    uint64_t z = k * 0x9E3779B97F4A7C15ull + 0x5EED;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    return (double)(z >> 11) * (1.0 / 9007199254740992.0);
+}
+
+static uint16_t bf16_bits_trunc(float x)   /* an input value: the top half of x */
+{
+    uint32_t u;
+    memcpy(&u, &x, 4);
+    return (uint16_t)(u >> 16);
+}
+
+int main(void)
+{
+    const int64_t n = 100003;
+    const int M = 3;
+    const double scale = 1.0 / 24;
+    float* p_ref = malloc(sizeof(float) * n);
+    float* m_ref = calloc((size_t)n, sizeof(float));
+    float* v_ref = calloc((size_t)n, sizeof(float));
+    float* acc_ref = malloc(sizeof(float) * n);
+    uint16_t* b_ref = malloc(sizeof(uint16_t) * n);
+    uint16_t* g = malloc(sizeof(uint16_t) * n * M);
+    float* back = malloc(sizeof(float) * n);
+    uint16_t* back16 = malloc(sizeof(uint16_t) * n);
+    CHECK(p_ref && m_ref && v_ref && acc_ref && b_ref && g && back && back16, 1);
+    for (int64_t i = 0; i < n; ++i) p_ref[i] = (float)(0.2 * uniform((uint64_t)i) - 0.1);
+    for (int64_t i = 0; i < n * M; ++i)
+        g[i] = bf16_bits_trunc((float)(0.02 * (uniform((uint64_t)(n + i)) + uniform((uint64_t)(2 * n * M + i)) - 1.0)));
+
+    /* device buffers */
+    float *d_master, *d_state, *d_acc, *d_p, *d_m, *d_v;
+    uint16_t *d_g, *d_b;
+    double *d_norm, *d_norm_ref;
+    void* d_ws;
+    const int64_t ws_bytes = grad_accum_norm_sq_workspace_bytes(n);
+    const int64_t st = state_tiled_numel(n);
+    CHECK(ws_bytes > 0 && st == 3 * (int64_t)ZS_STATE_TILE * ((n + ZS_STATE_TILE - 1) / ZS_STATE_TILE), 2);
+    HIPOK(hipMalloc((void**)&d_master, sizeof(float) * n), 3);
+    HIPOK(hipMalloc((void**)&d_state, sizeof(float) * st), 3);
+    HIPOK(hipMalloc((void**)&d_acc, sizeof(float) * n), 3);
+    HIPOK(hipMalloc((void**)&d_p, sizeof(float) * n), 3);
+    HIPOK(hipMalloc((void**)&d_m, sizeof(float) * n), 3);
+    HIPOK(hipMalloc((void**)&d_v, sizeof(float) * n), 3);
+    HIPOK(hipMalloc((void**)&d_g, sizeof(uint16_t) * n * M), 3);
+    HIPOK(hipMalloc((void**)&d_b, sizeof(uint16_t) * n), 3);
+    HIPOK(hipMalloc((void**)&d_norm, sizeof(double)), 3);
+    HIPOK(hipMalloc((void**)&d_norm_ref, sizeof(double)), 3);
+    HIPOK(hipMalloc(&d_ws, (size_t)ws_bytes), 3);
+    HIPOK(hipMemcpy(d_master, p_ref, sizeof(float) * n, hipMemcpyHostToDevice), 4);
+    HIPOK(hipMemcpy(d_g, g, sizeof(uint16_t) * n * M, hipMemcpyHostToDevice), 4);
+
+    /* the library's step */
+    CHECK(state_tile(d_master, NULL, NULL, d_state, n, NULL) == ZS_OK, 5);
+    for (int k = 0; k < M - 1; ++k)
+        CHECK(grad_accum(d_acc, d_g + (size_t)k * n, ZS_BF16, n, k == 0, NULL) == ZS_OK, 6);
+    CHECK(grad_accum_norm_sq(d_acc, d_g + (size_t)(M - 1) * n, ZS_BF16, n, 0, scale, d_norm, d_ws, ws_bytes, NULL)
+          == ZS_OK, 7);
+
+    /* the oracle's */
+    for (int k = 0; k < M; ++k) CHECK(orc_grad_accum(acc_ref, g + (size_t)k * n, 1, n, k == 0) == 0, 8);
+    const double S = orc_grad_norm_sq(acc_ref, n, scale);
+    double S_gpu = 0.0;
+    HIPOK(hipMemcpy(&S_gpu, d_norm, sizeof(double), hipMemcpyDeviceToHost), 9);
+    CHECK(fabs(sqrt(S_gpu) - sqrt(S)) <= 1e-5 * sqrt(S), 9);
+    HIPOK(hipMemcpy(back, d_acc, sizeof(float) * n, hipMemcpyDeviceToHost), 10);
+    CHECK(memcmp(back, acc_ref, sizeof(float) * n) == 0, 10);
+
+    const double max_norm = 0.5 * sqrt(S), extra = 0.2 * S;   /* the clip applies */
+    zs_adamw hp = {3e-4, 0.9, 0.95, 1e-8, 0.1, scale, max_norm, extra, 1};
+    orc_adamw_hp ohp = {3e-4, 0.9, 0.95, 1e-8, 0.1, scale, max_norm, extra, 1};
+    HIPOK(hipMemcpy(d_norm_ref, &S, sizeof(double), hipMemcpyHostToDevice), 11);
+    CHECK(adamw_step_tiled(&hp, d_state, d_acc, d_b, n, d_norm_ref, NULL) == ZS_OK, 11);
+    CHECK(orc_adamw_step(&ohp, p_ref, m_ref, v_ref, acc_ref, b_ref, n, &S) == 0, 12);
+    CHECK(state_untile(d_state, d_p, d_m, d_v, n, NULL) == ZS_OK, 13);
+    HIPOK(hipDeviceSynchronize(), 14);
+    HIPOK(hipMemcpy(back, d_p, sizeof(float) * n, hipMemcpyDeviceToHost), 15);
+    CHECK(memcmp(back, p_ref, sizeof(float) * n) == 0, 15);
+    HIPOK(hipMemcpy(back, d_m, sizeof(float) * n, hipMemcpyDeviceToHost), 16);
+    CHECK(memcmp(back, m_ref, sizeof(float) * n) == 0, 16);
+    HIPOK(hipMemcpy(back, d_v, sizeof(float) * n, hipMemcpyDeviceToHost), 17);
+    CHECK(memcmp(back, v_ref, sizeof(float) * n) == 0, 17);
+    HIPOK(hipMemcpy(back16, d_b, sizeof(uint16_t) * n, hipMemcpyDeviceToHost), 18);
+    CHECK(memcmp(back16, b_ref, sizeof(uint16_t) * n) == 0, 18);
+    CHECK(zs_last_hip_error() == 0, 19);
+
+    hipFree(d_master); hipFree(d_state); hipFree(d_acc); hipFree(d_p); hipFree(d_m); hipFree(d_v);
+    hipFree(d_g); hipFree(d_b); hipFree(d_norm); hipFree(d_norm_ref); hipFree(d_ws);
+    free(p_ref); free(m_ref); free(v_ref); free(acc_ref); free(b_ref); free(g); free(back); free(back16);
+    printf("c gpu step: ok\n");
+    return 0;
+}
