@@ -86,6 +86,12 @@ def _configure(L):
     L.orc_adam_update.restype = ctypes.c_int
     L.orc_flat_apply_update.argtypes = [P, P, P, I32, I32]
     L.orc_flat_apply_update.restype = ctypes.c_int
+    L.orc_moments_tiled_numel.argtypes = [I64, I64]
+    L.orc_moments_tiled_numel.restype = I64
+    L.orc_moments_tile.argtypes = [P, P, P, I64, I64]
+    L.orc_moments_tile.restype = ctypes.c_int
+    L.orc_moments_untile.argtypes = [P, P, P, I64, I64]
+    L.orc_moments_untile.restype = ctypes.c_int
     L.orc_state_tiled_numel.argtypes = [I64, I64]
     L.orc_state_tiled_numel.restype = I64
     L.orc_state_tile.argtypes = [P, P, P, P, I64, I64]
@@ -328,4 +334,39 @@ def state_untile(state: np.ndarray, n: int, tile: int):
     rc = lib().orc_state_untile(_ptr(state), _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]), int(n), int(tile))
     if rc != 0:
         raise ValueError("state_untile: invalid arguments")
+    return tuple(outs)
+
+
+def moments_tiled_numel(n: int, tile: int) -> int:
+    """Floats of the tiled moments (exp_avg, exp_avg_sq) for n elements (-1 if invalid)."""
+    return int(lib().orc_moments_tiled_numel(int(n), int(tile)))
+
+
+def moments_tile(exp_avg, exp_avg_sq, n: int, tile: int) -> np.ndarray:
+    """The tiled moments buffer of two fp32 arrays of n elements (None = zeros)."""
+    srcs = []
+    for a, nm in ((exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq")):
+        if a is not None:
+            _need(a, np.float32, nm)
+            if a.size != n:
+                raise ValueError(f"moments_tile: {nm} size mismatch")
+        srcs.append(a)
+    total = moments_tiled_numel(n, tile)
+    if total < 0:
+        raise ValueError("moments_tile: invalid arguments")
+    buf = np.full(total, np.nan, dtype=np.float32)   # poison: every float must be written
+    if lib().orc_moments_tile(_ptr(srcs[0]), _ptr(srcs[1]), _ptr(buf), int(n), int(tile)) != 0:
+        raise ValueError("moments_tile: invalid arguments")
+    return buf
+
+
+def moments_untile(buf: np.ndarray, n: int, tile: int):
+    """(exp_avg, exp_avg_sq) fp32 arrays of n elements from tiled moments."""
+    _need(buf, np.float32, "moments")
+    total = moments_tiled_numel(n, tile)
+    if total < 0 or buf.size < total:
+        raise ValueError("moments_untile: buffer too small or invalid arguments")
+    outs = [np.empty(int(n), dtype=np.float32) for _ in range(2)]
+    if lib().orc_moments_untile(_ptr(buf), _ptr(outs[0]), _ptr(outs[1]), int(n), int(tile)) != 0:
+        raise ValueError("moments_untile: invalid arguments")
     return tuple(outs)

@@ -494,57 +494,88 @@ int orc_flat_apply_update(const float* update, void* const* dst, const int64_t* 
 /* keep an fp32 master, exp_avg and exp_avg_sq per parameter ([Memory   */
 /* page] "一、显存账本": 4 + 4 + 4 of the 16 B per parameter) and update */
 /* every element on its own ([Memory page] same section; [ZeRO page]    */
-/* §ZeRO-1/2/3 step), so where the three values are stored cannot       */
-/* change any result.  The layout groups the shard in tiles of `tile`   */
-/* elements; tile t holds, one after the other, the master, exp_avg and */
-/* exp_avg_sq of its elements [t*tile, (t+1)*tile).                     */
+/* §ZeRO-1/2/3 step), so where the values are stored cannot change any  */
+/* result.  The layout groups the shard in tiles of `tile` elements;    */
+/* tile t holds, one after the other, a run of each array (master,      */
+/* exp_avg, exp_avg_sq; or exp_avg, exp_avg_sq alone) for its elements  */
+/* [t*tile, (t+1)*tile).                                                */
 /* ------------------------------------------------------------------ */
-/* floats a tiled buffer of n elements occupies: three runs of `tile` per
- * started tile.  -1 for n < 0 or tile < 1. */
-int64_t orc_state_tiled_numel(int64_t n, int64_t tile)
+/* floats a tiled buffer of n elements occupies with `runs` arrays per tile:
+ * runs runs of `tile` per started tile.  -1 for n < 0, tile < 1 or runs < 1. */
+int64_t orc_tiled_runs_numel(int64_t n, int64_t tile, int runs)
 {
-    if (n < 0 || tile < 1) return -1;
+    if (n < 0 || tile < 1 || runs < 1) return -1;
     int64_t tiles = n / tile;
     if (n % tile != 0) tiles += 1;
-    return 3 * tile * tiles;
+    return (int64_t)runs * tile * tiles;
 }
 
-/* state[(3t + k)*tile + j] = src_k[t*tile + j] for t*tile + j < n, and 0 past
- * n (the unused end of the last tile).  A NULL src_k stands for zeros.
- * Returns 0, or -1 for n < 0 or tile < 1. */
-int orc_state_tile(const float* master, const float* exp_avg, const float* exp_avg_sq, float* state,
-                   int64_t n, int64_t tile)
+/* buf[(runs*t + k)*tile + j] = src[k][t*tile + j] for t*tile + j < n, and 0
+ * past n (the unused end of the last tile).  A NULL src[k] stands for zeros.
+ * Returns 0, or -1 for n < 0, tile < 1 or runs < 1. */
+int orc_tile_runs(const float* const* src, int runs, float* buf, int64_t n, int64_t tile)
 {
-    int64_t total = orc_state_tiled_numel(n, tile);
+    int64_t total = orc_tiled_runs_numel(n, tile, runs);
     if (total < 0) return -1;
-    const float* src[3] = {master, exp_avg, exp_avg_sq};
-    int64_t tiles = total / (3 * tile);
+    int64_t tiles = total / ((int64_t)runs * tile);
     for (int64_t t = 0; t < tiles; ++t)
-        for (int k = 0; k < 3; ++k)
+        for (int k = 0; k < runs; ++k)
             for (int64_t j = 0; j < tile; ++j) {
                 int64_t e = t * tile + j;
                 float x = 0.0f;
                 if (e < n && src[k] != NULL) x = src[k][e];
-                state[(3 * t + k) * tile + j] = x;
+                buf[((int64_t)runs * t + k) * tile + j] = x;
             }
     return 0;
 }
 
-/* The inverse: dst_k[e] = state[(3*(e / tile) + k)*tile + e % tile] for
- * e < n; a NULL dst_k is skipped.  Returns 0, or -1 for n < 0 or tile < 1. */
-int orc_state_untile(const float* state, float* master, float* exp_avg, float* exp_avg_sq,
-                     int64_t n, int64_t tile)
+/* The inverse: dst[k][e] = buf[(runs*(e / tile) + k)*tile + e % tile] for
+ * e < n; a NULL dst[k] is skipped.  Returns 0, or -1 for bad arguments. */
+int orc_untile_runs(const float* buf, int runs, float* const* dst, int64_t n, int64_t tile)
 {
-    if (orc_state_tiled_numel(n, tile) < 0) return -1;
-    float* dst[3] = {master, exp_avg, exp_avg_sq};
-    for (int k = 0; k < 3; ++k) {
+    if (orc_tiled_runs_numel(n, tile, runs) < 0) return -1;
+    for (int k = 0; k < runs; ++k) {
         if (dst[k] == NULL) continue;
         for (int64_t e = 0; e < n; ++e) {
             int64_t t = e / tile, j = e % tile;
-            dst[k][e] = state[(3 * t + k) * tile + j];
+            dst[k][e] = buf[((int64_t)runs * t + k) * tile + j];
         }
     }
     return 0;
+}
+
+/* The optimizer state of a master form: master, exp_avg, exp_avg_sq (three
+ * runs per tile). */
+int64_t orc_state_tiled_numel(int64_t n, int64_t tile) { return orc_tiled_runs_numel(n, tile, 3); }
+
+int orc_state_tile(const float* master, const float* exp_avg, const float* exp_avg_sq, float* state,
+                   int64_t n, int64_t tile)
+{
+    const float* src[3] = {master, exp_avg, exp_avg_sq};
+    return orc_tile_runs(src, 3, state, n, tile);
+}
+
+int orc_state_untile(const float* state, float* master, float* exp_avg, float* exp_avg_sq,
+                     int64_t n, int64_t tile)
+{
+    float* dst[3] = {master, exp_avg, exp_avg_sq};
+    return orc_untile_runs(state, 3, dst, n, tile);
+}
+
+/* The moments alone (the no-master and ZeRO-1 forms hold no fp32 master):
+ * exp_avg, exp_avg_sq (two runs per tile). */
+int64_t orc_moments_tiled_numel(int64_t n, int64_t tile) { return orc_tiled_runs_numel(n, tile, 2); }
+
+int orc_moments_tile(const float* exp_avg, const float* exp_avg_sq, float* moments, int64_t n, int64_t tile)
+{
+    const float* src[2] = {exp_avg, exp_avg_sq};
+    return orc_tile_runs(src, 2, moments, n, tile);
+}
+
+int orc_moments_untile(const float* moments, float* exp_avg, float* exp_avg_sq, int64_t n, int64_t tile)
+{
+    float* dst[2] = {exp_avg, exp_avg_sq};
+    return orc_untile_runs(moments, 2, dst, n, tile);
 }
 
 /* Thread count OpenMP will use for the loops above (reported by the

@@ -142,6 +142,13 @@ int main(void)
             CHECK(orc_state_tile(p, m, v, st, -1, tile) == -1, 14);
             CHECK(orc_state_untile(st, p, m, v, n, 0) == -1, 14);
             free(st);
+            const int64_t ms = orc_moments_tiled_numel(n, tile);
+            CHECK(ms >= 2 * n && ms < 2 * (n + tile), 14);
+            float* mo = xmalloc(sizeof(float) * ms);
+            CHECK(orc_moments_tile(m, NULL, mo, n, tile) == 0, 14);
+            CHECK(orc_moments_untile(mo, NULL, v, n, tile) == 0, 14);
+            CHECK(orc_moments_tile(m, v, mo, n, 0) == -1, 14);
+            free(mo);
         }
         free(acc); free(g32); free(g16); free(p); free(m); free(v); free(u); free(b);
     }

@@ -89,13 +89,16 @@ MUTANTS = [
      "p[j] = (uint16_t)(f32_bits(orc_bf16_widen(p[j]) + u) >> 16);"),
     ("apply: fp32 update subtracted", "p[j] = p[j] + u;", "p[j] = p[j] - u;"),
     ("tiled state: streams laid out tile-major instead of per tile",
-     "state[(3 * t + k) * tile + j] = x;", "state[(k * tiles + t) * tile + j] = x;"),
+     "buf[((int64_t)runs * t + k) * tile + j] = x;", "buf[((int64_t)k * tiles + t) * tile + j] = x;"),
     ("tiled state: one tile too many when n is a multiple of the tile", "if (n % tile != 0) tiles += 1;",
      "tiles += 1;"),
     ("tiled state: the end of the last tile left unwritten", "float x = 0.0f;\n                if (e < n",
-     "float x = state[(3 * t + k) * tile + j];\n                if (e < n"),
+     "float x = buf[((int64_t)runs * t + k) * tile + j];\n                if (e < n"),
     ("tiled state: untile reads the previous run",
-     "dst[k][e] = state[(3 * t + k) * tile + j];", "dst[k][e] = state[(3 * t + (k > 0 ? k - 1 : 0)) * tile + j];"),
+     "dst[k][e] = buf[((int64_t)runs * t + k) * tile + j];",
+     "dst[k][e] = buf[((int64_t)runs * t + (k > 0 ? k - 1 : 0)) * tile + j];"),
+    ("tiled moments: untile swaps the two runs", "float* dst[2] = {exp_avg, exp_avg_sq};",
+     "float* dst[2] = {exp_avg_sq, exp_avg};"),
 ]
 
 
@@ -138,7 +141,10 @@ def pin_suite():
         lambda: pins.test_state_tile_element_positions_brute_force(orc),
         lambda: pins.test_state_tile_bits_and_missing_sources(orc),
         lambda: pins.test_state_tile_then_step_equals_step(orc),
+        lambda: pins.test_moments_tile_then_update_equals_update(orc),
     ]
+    for n, tile in ((5, 4), (64, 16), (8193, 8192)):
+        suite.append(lambda n=n, tile=tile: pins.test_moments_tile_matches_numpy_reshape(orc, n, tile))
     for n, tile in ((5, 4), (17, 8), (64, 16), (8193, 8192)):
         suite.append(lambda n=n, tile=tile: pins.test_state_tile_matches_numpy_reshape(orc, n, tile))
     for seed in range(3):

@@ -836,3 +836,40 @@ def test_state_tile_then_step_equals_step(orc):
     oracle.adamw_step(H, p2, m2, v2, g)
     for a, b in ((p, p2), (m, m2), (v, v2)):
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("n,tile", [(0, 4), (1, 4), (5, 4), (8, 4), (17, 8), (64, 16), (8193, 8192)])
+def test_moments_tile_matches_numpy_reshape(orc, n, tile):
+    """The moments-only layout against its numpy definition: the buffer as
+    [tiles, 2, tile] holds exp_avg and exp_avg_sq of the tile's elements in
+    rows 0 and 1, the end of the last tile zero; untile inverts it."""
+    rng = np.random.default_rng(7 * n + tile)
+    m, v = (rng.standard_normal(n).astype(np.float32) for _ in range(2))
+    buf = oracle.moments_tile(m, v, n, tile)
+    tiles = -(-n // tile)
+    assert buf.size == oracle.moments_tiled_numel(n, tile) == 2 * tile * tiles
+    view = buf.reshape(tiles, 2, tile)
+    for k, src in enumerate((m, v)):
+        run = view[:, k, :].reshape(-1)
+        assert np.array_equal(run[:n].view(np.uint32), src.view(np.uint32))
+        assert np.all(run[n:].view(np.uint32) == 0)
+    for a, b in zip(oracle.moments_untile(buf, n, tile), (m, v)):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert oracle.moments_tiled_numel(-1, 4) == -1
+
+
+def test_moments_tile_then_update_equals_update(orc):
+    """Tiling the moments, running the ZeRO-1 update and the no-master step
+    on the arrays read back, equals running them on the split arrays."""
+    rng = np.random.default_rng(11)
+    n, tile = 777, 32
+    m = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+    v = rng.uniform(0, 1e-7, n).astype(np.float32)
+    g = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    H = hp(lr=3e-4, beta1=0.9, beta2=0.95, step=2)
+    m2, v2 = oracle.moments_untile(oracle.moments_tile(m, v, n, tile), n, tile)
+    u1, u2 = np.empty(n, np.float32), np.empty(n, np.float32)
+    oracle.adam_update(H, m, v, g, u1)
+    oracle.adam_update(H, m2, v2, g, u2)
+    for a, b in ((m, m2), (v, v2), (u1, u2)):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
