@@ -47,15 +47,15 @@ HBM_PEAK_GBPS = 8000.0   # MI355X published HBM3E bandwidth
 PMC_SOURCES = ("csrc/adamw.hip", "csrc/zs_common.h")
 PMC_TRAFFIC = {
     "adamw_step_tiled": [
-        {"sha256_16": "020349a2ce5052b9", "shard_elems": 842301952,
+        {"sha256_16": "ba1b28dbf08f72dd", "shard_elems": 842301952,
          "fetch_kib": 6580552.4, "fetch_scale": 2.0, "write_kib": 11515857.7, "write_scale": 1.0},
-        {"sha256_16": "020349a2ce5052b9", "shard_elems": 1093750000,
+        {"sha256_16": "ba1b28dbf08f72dd", "shard_elems": 1093750000,
          "fetch_kib": 8545002.6, "fetch_scale": 2.0, "write_kib": 14953618.9, "write_scale": 1.0},
     ],
     "adamw_step": [
-        {"sha256_16": "020349a2ce5052b9", "shard_elems": 842301952,
+        {"sha256_16": "ba1b28dbf08f72dd", "shard_elems": 842301952,
          "fetch_kib": 6580517.5, "fetch_scale": 2.0, "write_kib": 11515853.2, "write_scale": 1.0},
-        {"sha256_16": "020349a2ce5052b9", "shard_elems": 1093750000,
+        {"sha256_16": "ba1b28dbf08f72dd", "shard_elems": 1093750000,
          "fetch_kib": 8544955.5, "fetch_scale": 2.0, "write_kib": 14953618.7, "write_scale": 1.0},
     ],
 }
@@ -340,20 +340,27 @@ def run_gpu(w, steps: int, warmup: int):
     norm_ms = n0.elapsed_time(n1) / 5
 
     # outside the step: the variant with no fp32 master (24 B/element), on the
-    # same buffers (state after the timed steps)
-    no_master_ms = None
+    # same buffers (state after the timed steps), then on tiled moments
+    no_master_ms = no_master_tiled_ms = None
     if param is not None:
-        n0, n1 = ev(), ev()
-        hp = zs.AdamWConfig(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
-                            grad_scale=w.grad_scale, step=t + 1)
-        zs.adamw_step_no_master(hp, param, exp_avg, exp_avg_sq, acc)
-        n0.record()
-        for k in range(3):
-            hp.step = t + 2 + k
-            zs.adamw_step_no_master(hp, param, exp_avg, exp_avg_sq, acc)
-        n1.record()
-        torch.cuda.synchronize()
-        no_master_ms = n0.elapsed_time(n1) / 3
+        def time_no_master(fn):
+            hp = zs.AdamWConfig(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
+                                grad_scale=w.grad_scale, step=t + 1)
+            fn(hp)
+            n0, n1 = ev(), ev()
+            n0.record()
+            for k in range(3):
+                hp.step = t + 2 + k
+                fn(hp)
+            n1.record()
+            torch.cuda.synchronize()
+            return n0.elapsed_time(n1) / 3
+
+        no_master_ms = time_no_master(lambda hp: zs.adamw_step_no_master(hp, param, exp_avg, exp_avg_sq, acc))
+        moments = torch.empty(zs.moments_tiled_numel(n), dtype=torch.float32, device=dev)
+        zs.moments_tile(exp_avg, exp_avg_sq, moments)
+        no_master_tiled_ms = time_no_master(lambda hp: zs.adamw_step_no_master_tiled(hp, param, moments, acc))
+        del moments
 
     # achievable-bandwidth reference for the AdamW step's own traffic: the
     # same bytes per element and accesses, one addition per stream in place
@@ -381,6 +388,7 @@ def run_gpu(w, steps: int, warmup: int):
     del src, dst
     return {"n": n, "wall_s": wall, "accum_ms": acc_ms, "last_ms": last_ms, "adamw_ms": adamw_ms, "graph_ms": graph_ms,
             "split_ms": split_ms, "reduce_ms": reduce_ms, "chunks": len(grads), "no_master_ms": no_master_ms,
+            "no_master_tiled_ms": no_master_tiled_ms,
             "copy_gbps": copy_gbps, "ceiling_ms": ceiling, "ceiling_split_ms": ceiling_split, "norm_ms": norm_ms}
 
 
@@ -518,12 +526,24 @@ def run_zero1_flow(w, shapes, reps: int = 3):
         zs.adam_update(hp, m, v, flat_grad[start:end], mine)
 
     upd_ms = timed(update)
-    del m, v, flat_grad
+    # the same update with the rank's moments tiled (two runs per tile)
+    moments = torch.empty(zs.moments_tiled_numel(n), dtype=torch.float32, device=dev)
+    zs.moments_tile(m, v, moments)
+
+    def update_tiled(k):
+        hp = zs.AdamWConfig(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=0.0,
+                            grad_scale=1.0 / w.world, step=k + 1)
+        zs.adam_update_tiled(hp, moments, flat_grad[start:end], mine)
+
+    upd_tiled_ms = timed(update_tiled)
+    del m, v, flat_grad, moments
     out = {"workload": f"{w.name} as ZeRO-1: full flat fp32 grad and gathered update of {w.total} elements, "
                        f"rank {w.rank} of {w.world}",
            "tensors": len(shapes),
            "adam_update": {"ms": upd_ms, "elements": n, "bytes_per_elem": 24,
-                           "gbps": 24 * n / (upd_ms * 1e-3) / 1e9}}
+                           "gbps": 24 * n / (upd_ms * 1e-3) / 1e9},
+           "adam_update_tiled": {"ms": upd_tiled_ms, "elements": n, "bytes_per_elem": 24,
+                                 "gbps": 24 * n / (upd_tiled_ms * 1e-3) / 1e9}}
     from workloads import numel_of
     for dtype, bpe, key in ((torch.bfloat16, 8, "apply_bf16"), (torch.float32, 12, "apply_f32")):
         buf = torch.empty(w.total, dtype=dtype, device=dev).uniform_(-0.1, 0.1)
@@ -692,6 +712,9 @@ def main():
         "adamw_step_no_master": None if r["no_master_ms"] is None else {
             "ms": r["no_master_ms"], "bytes_per_elem": 24,
             "gbps": 24 * n / (r["no_master_ms"] * 1e-3) / 1e9},
+        "adamw_step_no_master_tiled": None if r["no_master_tiled_ms"] is None else {
+            "ms": r["no_master_tiled_ms"], "bytes_per_elem": 24,
+            "gbps": 24 * n / (r["no_master_tiled_ms"] * 1e-3) / 1e9},
         "reduce_chunks": None if r["reduce_ms"] is None else {
             "chunks": r["chunks"], "ms": r["reduce_ms"],
             "gbps": (r["chunks"] * (2 if w.grad_dtype == "bf16" else 4) + 4) * n / (r["reduce_ms"] * 1e-3) / 1e9},

@@ -20,6 +20,9 @@ The Python names mirror the C ABI in include/zshard.h:
     state_untile(state, master, exp_avg, exp_avg_sq, n=None)   tiled -> split (None: skipped)
     adamw_step_tiled(hp, state, grad, param_bf16=None, norm_sq=None)
     adamw_step_tiled_dev(scalars_dev, state, grad, param_bf16=None, norm_sq=None)
+    moments_tiled_numel(n) / moments_tile(exp_avg, exp_avg_sq, moments, n=None) / moments_untile(...)
+    adam_update_tiled(hp, moments, grad, update, norm_sq=None)
+    adamw_step_no_master_tiled(hp, param_bf16, moments, grad, norm_sq=None)
 
 All device work runs in the library's gfx950 HIP kernels on the current
 torch stream; torch supplies device memory and the stream only.
@@ -32,10 +35,12 @@ from ._binding import (  # noqa: F401
     ZShardError,
     AdamWScalars,
     adam_update,
+    adam_update_tiled,
     adamw_scalars,
     adamw_step,
     adamw_step_dev,
     adamw_step_no_master,
+    adamw_step_no_master_tiled,
     adamw_step_tiled,
     adamw_step_tiled_dev,
     flat_apply_update,
@@ -48,6 +53,9 @@ from ._binding import (  # noqa: F401
     grad_norm_sq,
     grad_norm_sq_workspace_bytes,
     lib,
+    moments_tile,
+    moments_tiled_numel,
+    moments_untile,
     scalars_bytes,
     state_tile,
     state_tiled_numel,

@@ -31,7 +31,8 @@ EXPORTS = (
     "grad_norm_sq_workspace_bytes", "grad_norm_sq", "grad_accum_norm_sq_workspace_bytes",
     "grad_accum_norm_sq", "adamw_step", "adamw_scalars", "adamw_step_dev", "adamw_step_no_master", "adam_update",
     "flat_apply_update", "state_tiled_numel", "state_tile", "state_untile", "adamw_step_tiled",
-    "adamw_step_tiled_dev",
+    "adamw_step_tiled_dev", "moments_tiled_numel", "moments_tile", "moments_untile", "adam_update_tiled",
+    "adamw_step_no_master_tiled",
     "zs_strerror", "zs_last_hip_error",
 )
 
@@ -144,6 +145,16 @@ def lib() -> ctypes.CDLL:
         L.adamw_step_tiled.restype = I32
         L.adamw_step_tiled_dev.argtypes = [P, P, P, P, I64, P, P]
         L.adamw_step_tiled_dev.restype = I32
+        L.moments_tiled_numel.argtypes = [I64]
+        L.moments_tiled_numel.restype = I64
+        L.moments_tile.argtypes = [P, P, P, I64, P]
+        L.moments_tile.restype = I32
+        L.moments_untile.argtypes = [P, P, P, I64, P]
+        L.moments_untile.restype = I32
+        L.adam_update_tiled.argtypes = [ctypes.POINTER(AdamW), P, P, P, I64, P, P]
+        L.adam_update_tiled.restype = I32
+        L.adamw_step_no_master_tiled.argtypes = [ctypes.POINTER(AdamW), P, P, P, I64, P, P]
+        L.adamw_step_no_master_tiled.restype = I32
         L.zs_strerror.argtypes = [I32]
         L.zs_strerror.restype = ctypes.c_char_p
         L.zs_last_hip_error.argtypes = []
@@ -492,3 +503,75 @@ def adamw_step_tiled_dev(scalars_dev: torch.Tensor, state: torch.Tensor, grad: t
         _dev(scalars_dev, "scalars_dev"), _state_buffer(state, n, "adamw_step_tiled_dev"),
         _dev(grad, "grad", torch.float32), _dev(param_bf16, "param_bf16", torch.bfloat16), n,
         _norm(norm_sq, "adamw_step_tiled_dev"), _stream(stream)))
+
+
+def moments_tiled_numel(n: int) -> int:
+    """Floats of the tiled moments (exp_avg, exp_avg_sq) of n elements (host only)."""
+    out = int(lib().moments_tiled_numel(int(n)))
+    if out < 0:
+        raise ValueError(f"moments_tiled_numel: invalid element count {n}")
+    return out
+
+
+def _moments_buffer(moments: torch.Tensor, n: int, fn: str) -> int:
+    if moments.numel() < moments_tiled_numel(n):
+        raise ValueError(f"{fn}: moments hold {moments.numel()} floats, the tiled layout of {n} elements needs "
+                         f"{moments_tiled_numel(n)}")
+    return _dev(moments, "moments", torch.float32)
+
+
+def moments_tile(exp_avg: Optional[torch.Tensor], exp_avg_sq: Optional[torch.Tensor], moments: torch.Tensor,
+                 n: Optional[int] = None, stream=None) -> None:
+    """Split fp32 moments (None = zeros) into the tiled moments buffer."""
+    srcs = (exp_avg, exp_avg_sq)
+    if n is None:
+        n = next((t.numel() for t in srcs if t is not None), None)
+        if n is None:
+            raise ValueError("moments_tile: give n when every source is None")
+    for t, nm in zip(srcs, ("exp_avg", "exp_avg_sq")):
+        if t is not None and t.numel() != n:
+            raise ValueError(f"moments_tile: {nm} size mismatch")
+    _check("moments_tile", lib().moments_tile(
+        _dev(exp_avg, "exp_avg", torch.float32), _dev(exp_avg_sq, "exp_avg_sq", torch.float32),
+        _moments_buffer(moments, n, "moments_tile"), int(n), _stream(stream)))
+
+
+def moments_untile(moments: torch.Tensor, exp_avg: Optional[torch.Tensor], exp_avg_sq: Optional[torch.Tensor],
+                   n: Optional[int] = None, stream=None) -> None:
+    """The tiled moments back into split fp32 arrays (None = that stream skipped)."""
+    dsts = (exp_avg, exp_avg_sq)
+    if n is None:
+        n = next((t.numel() for t in dsts if t is not None), None)
+        if n is None:
+            raise ValueError("moments_untile: give n when every destination is None")
+    for t, nm in zip(dsts, ("exp_avg", "exp_avg_sq")):
+        if t is not None and t.numel() != n:
+            raise ValueError(f"moments_untile: {nm} size mismatch")
+    _check("moments_untile", lib().moments_untile(
+        _moments_buffer(moments, n, "moments_untile"), _dev(exp_avg, "exp_avg", torch.float32),
+        _dev(exp_avg_sq, "exp_avg_sq", torch.float32), int(n), _stream(stream)))
+
+
+def adam_update_tiled(hp: AdamWConfig, moments: torch.Tensor, grad: torch.Tensor, update: torch.Tensor,
+                      norm_sq: Optional[torch.Tensor] = None, stream=None) -> None:
+    """adam_update on tiled moments: the update vector into ``update``."""
+    n = update.numel()
+    if grad.numel() != n:
+        raise ValueError("adam_update_tiled: grad size mismatch")
+    c = hp.c_struct()
+    _check("adam_update_tiled", lib().adam_update_tiled(
+        ctypes.byref(c), _moments_buffer(moments, n, "adam_update_tiled"), _dev(grad, "grad", torch.float32),
+        _dev(update, "update", torch.float32), n, _norm(norm_sq, "adam_update_tiled"), _stream(stream)))
+
+
+def adamw_step_no_master_tiled(hp: AdamWConfig, param_bf16: torch.Tensor, moments: torch.Tensor,
+                               grad: torch.Tensor, norm_sq: Optional[torch.Tensor] = None, stream=None) -> None:
+    """adamw_step_no_master on tiled moments (the bf16 parameter in place)."""
+    n = param_bf16.numel()
+    if grad.numel() != n:
+        raise ValueError("adamw_step_no_master_tiled: grad size mismatch")
+    c = hp.c_struct()
+    _check("adamw_step_no_master_tiled", lib().adamw_step_no_master_tiled(
+        ctypes.byref(c), _dev(param_bf16, "param_bf16", torch.bfloat16),
+        _moments_buffer(moments, n, "adamw_step_no_master_tiled"), _dev(grad, "grad", torch.float32), n,
+        _norm(norm_sq, "adamw_step_no_master_tiled"), _stream(stream)))

@@ -14,9 +14,9 @@
 // that writes the update vector -u instead of a parameter (Adam without
 // decay; R grad, m, v and W m, v, update: 24 B/element).
 //
-// The master forms also run on the tiled state layout (TILED): master,
-// exp_avg and exp_avg_sq in one buffer, three runs of kStateTile floats per
-// tile of elements.  Same bytes and arithmetic; a wave's three state
+// Every form also runs on a tiled state (TILED): master, exp_avg and
+// exp_avg_sq in one buffer, three runs of kStateTile floats per tile of
+// elements (the moments alone, two runs, for the no-master and update forms).  Same bytes and arithmetic; a wave's three state
 // accesses then fall in one 96 KiB region instead of three separate
 // buffers, which keeps fewer DRAM rows open: on gfx950 the AdamW step runs
 // at 85 % of the peak against 80-83 % on split buffers (7B, 70B and 13B
@@ -107,8 +107,10 @@ enum Form : int { kMaster = 0, kMasterBf16 = 1, kNoMaster = 2, kUpdate = 3 };
 // DEV: the scalars come from device memory (one uniform load per wave) instead
 // of the kernel arguments, so a captured graph replays any step whose scalars
 // the caller copied in beforehand.
-// TILED: master, exp_avg and exp_avg_sq come from the tiled state buffer
-// (master forms only); 4 consecutive elements never straddle a tile.
+// TILED: the state comes from a tiled buffer: master, exp_avg, exp_avg_sq
+// (3 runs per tile) for the master forms, exp_avg, exp_avg_sq (2 runs) for
+// the no-master and update forms; 4 consecutive elements never straddle a
+// tile.
 // OUT_ALIGNED = false: the one output stream that is only written, the bf16
 // re-cast or the ZeRO-1 update, starts off a 16-byte boundary (a view at
 // any element offset of a larger buffer); the vector path then writes it
@@ -116,8 +118,9 @@ enum Form : int { kMaster = 0, kMasterBf16 = 1, kNoMaster = 2, kUpdate = 3 };
 // everything else: 81 % of the peak against 65 % for the element-wise path.
 template <int VEC, int FORM, int BS, bool DEV, bool TILED = false, bool OUT_ALIGNED = true>
 __global__ __launch_bounds__(BS) void adamw_kernel(const AdamwArgs a) {
-    static_assert(!TILED || FORM == kMaster || FORM == kMasterBf16, "tiled state holds a master");
     static_assert(OUT_ALIGNED || FORM == kMasterBf16 || FORM == kUpdate, "a write-only output to split");
+    constexpr bool kMasterForm = FORM == kMaster || FORM == kMasterBf16;
+    constexpr int kRuns = kMasterForm ? 3 : 2;   // runs per tile of the tiled state
     constexpr bool kReadP = FORM != kUpdate;
     const AdamwScalars sc = DEV ? *a.sc_dev : a.sc;
     const int64_t n = a.n;
@@ -137,9 +140,10 @@ __global__ __launch_bounds__(BS) void adamw_kernel(const AdamwArgs a) {
         float* m_at;
         float* v_at;
         if constexpr (TILED) {
-            p_at = a.state + tiled_offset(first);
-            m_at = p_at + kStateTile;
-            v_at = p_at + 2 * kStateTile;
+            float* const t = a.state + tiled_offset<kRuns>(first);
+            if constexpr (kMasterForm) p_at = t;
+            m_at = kMasterForm ? t + kStateTile : t;
+            v_at = m_at + kStateTile;
         } else {
             if constexpr (FORM == kMaster || FORM == kMasterBf16) p_at = a.master + first;
             m_at = a.exp_avg + first;
@@ -194,9 +198,9 @@ __global__ __launch_bounds__(BS) void adamw_kernel(const AdamwArgs a) {
     if (!clip_coef(sc, a.norm_sq, coef)) return;
     const int64_t last = first + VEC < n ? first + VEC : n;
     for (int64_t i = first; i < last; ++i) {
-        float* const ts = TILED ? a.state + tiled_offset(i) : nullptr;   // the element's master in the state
-        float* const m_at = TILED ? ts + kStateTile : a.exp_avg + i;
-        float* const v_at = TILED ? ts + 2 * kStateTile : a.exp_avg_sq + i;
+        float* const ts = TILED ? a.state + tiled_offset<kRuns>(i) : nullptr;   // the element's first run
+        float* const m_at = TILED ? (kMasterForm ? ts + kStateTile : ts) : a.exp_avg + i;
+        float* const v_at = TILED ? m_at + kStateTile : a.exp_avg_sq + i;
         float m = *m_at, v = *v_at;
         const float u = adam_elem(sc, coef, a.grad[i], m, v);
         *m_at = m;
@@ -218,14 +222,15 @@ template <typename T>
 T* advance(T* p, int64_t off) { return p == nullptr ? nullptr : p + off; }
 
 // one launch per kLaunchElems elements, each on its own slice of the buffers
-// (a multiple of kStateTile: a piece of the tiled state starts at 3*off)
+// (a multiple of kStateTile: a piece of the tiled state starts at runs*off)
 template <int VEC, int FORM, int BS, bool DEV, bool TILED = false, bool OUT_ALIGNED = true>
 hipError_t launch(const AdamwArgs& a, unsigned lds, hipStream_t stream) {
     static_assert(kLaunchElems % kStateTile == 0, "launch pieces start on a tile");
+    constexpr int64_t runs = (FORM == kMaster || FORM == kMasterBf16) ? 3 : 2;
     for (int64_t off = 0; off < a.n; off += kLaunchElems) {
         AdamwArgs p = a;
         p.n = launch_piece(a.n, off);
-        p.state = advance(a.state, 3 * off);
+        p.state = advance(a.state, runs * off);
         p.master = advance(a.master, off);
         p.exp_avg = advance(a.exp_avg, off);
         p.exp_avg_sq = advance(a.exp_avg_sq, off);
@@ -243,17 +248,20 @@ hipError_t launch(const AdamwArgs& a, unsigned lds, hipStream_t stream) {
 
 // vec_ok: the vector path's alignment holds for every stream but the
 // write-only output; out_aligned: that output (bf16 re-cast or update) is
-// 16-byte aligned too.  The tiled state is 16-byte aligned by contract, so
-// the tiled forms always take the vector path.
+// 16-byte aligned too.  A tiled state is 16-byte aligned by contract, so the
+// tiled forms take the vector path, except the no-master form with its bf16
+// parameter (read and written) off a 16-byte boundary.  The six-stream forms
+// keep the 13-per-CU cap tiled too (tiled moments for the update form: 84.5 %
+// there, 83.9 % at 11 per CU).
 template <int FORM, bool DEV = false, bool TILED = false>
 hipError_t launch_form(const AdamwArgs& a, bool vec_ok, bool out_aligned, hipStream_t stream) {
-    constexpr unsigned lds = TILED ? kVecLdsReserveTiled
-                             : (FORM == kNoMaster || FORM == kUpdate) ? kVecLdsReserve6 : kVecLdsReserve;
+    constexpr bool six = FORM == kNoMaster || FORM == kUpdate;
+    constexpr unsigned lds = six ? kVecLdsReserve6 : TILED ? kVecLdsReserveTiled : kVecLdsReserve;
     if constexpr (FORM == kMasterBf16 || FORM == kUpdate) {
         if (vec_ok && !out_aligned) return launch<4, FORM, kVecBlock, DEV, TILED, false>(a, lds, stream);
     }
     if (vec_ok) return launch<4, FORM, kVecBlock, DEV, TILED>(a, lds, stream);
-    if constexpr (TILED) return hipErrorInvalidValue;   // not reached: the entry point always passes vec_ok
+    if constexpr (TILED && FORM != kNoMaster) return hipErrorInvalidValue;   // not reached: always vec_ok
     else return launch<1, FORM, kBlock, DEV, TILED>(a, 0, stream);
 }
 
@@ -281,6 +289,14 @@ hipError_t launch_adamw_no_master(const AdamwArgs& a, bool vec_ok, hipStream_t s
 
 hipError_t launch_adam_update(const AdamwArgs& a, bool vec_ok, bool out_aligned, hipStream_t stream) {
     return launch_form<kUpdate>(a, vec_ok, out_aligned, stream);
+}
+
+hipError_t launch_adam_update_tiled(const AdamwArgs& a, bool out_aligned, hipStream_t stream) {
+    return launch_form<kUpdate, false, true>(a, true, out_aligned, stream);
+}
+
+hipError_t launch_adamw_no_master_tiled(const AdamwArgs& a, bool vec_ok, hipStream_t stream) {
+    return launch_form<kNoMaster, false, true>(a, vec_ok, true, stream);
 }
 
 }  // namespace zs

@@ -346,42 +346,65 @@ int32_t adamw_step_dev(const zs_adamw_scalars* scalars_dev, float* master, float
 
 static_assert(ZS_STATE_TILE == zs::kStateTile, "tile length of the header and the kernels");
 
-int64_t state_tiled_numel(int64_t n) {
+static int64_t tiled_runs_numel(int64_t n, int runs) {
     if (!size_ok(n)) return -1;
-    return 3 * ((n + zs::kStateTile - 1) / zs::kStateTile) * zs::kStateTile;
+    return runs * ((n + zs::kStateTile - 1) / zs::kStateTile) * zs::kStateTile;
+}
+
+int64_t state_tiled_numel(int64_t n) { return tiled_runs_numel(n, 3); }
+int64_t moments_tiled_numel(int64_t n) { return tiled_runs_numel(n, 2); }
+
+// split arrays (each nullable: zeros) into a tiled buffer of `runs` runs per tile
+static int32_t tile_runs(const float* const* src, int runs, float* buf, int64_t n, void* hip_stream) {
+    if (!size_ok(n)) return ZS_EINVAL;
+    if (n == 0) return ZS_OK;
+    if (buf == nullptr || !aligned(buf, 16)) return ZS_EINVAL;
+    const int64_t buf_bytes = tiled_runs_numel(n, runs) * 4;
+    for (int k = 0; k < runs; ++k) {
+        if (src[k] != nullptr && !aligned(src[k], 4)) return ZS_EINVAL;
+        if (overlap(src[k], src[k] ? n * 4 : 0, buf, buf_bytes)) return ZS_EOVERLAP;
+    }
+    return hip_status(zs::launch_tile_runs(src, runs, buf, n, as_stream(hip_stream)));
+}
+
+// a tiled buffer of `runs` runs per tile into split arrays (each nullable: skipped)
+static int32_t untile_runs(const float* buf, int runs, float* const* dst, int64_t n, void* hip_stream) {
+    if (!size_ok(n)) return ZS_EINVAL;
+    if (n == 0) return ZS_OK;
+    if (buf == nullptr || !aligned(buf, 16)) return ZS_EINVAL;
+    const int64_t buf_bytes = tiled_runs_numel(n, runs) * 4;
+    bool vec = true;
+    for (int k = 0; k < runs; ++k) {
+        if (dst[k] == nullptr) continue;
+        if (!aligned(dst[k], 4)) return ZS_EINVAL;
+        if (overlap(dst[k], n * 4, buf, buf_bytes)) return ZS_EOVERLAP;
+        for (int j = k + 1; j < runs; ++j)
+            if (dst[j] != nullptr && overlap(dst[k], n * 4, dst[j], n * 4)) return ZS_EOVERLAP;
+        vec = vec && aligned(dst[k], 16);
+    }
+    return hip_status(zs::launch_untile_runs(buf, runs, dst, n, vec, as_stream(hip_stream)));
 }
 
 int32_t state_tile(const float* master, const float* exp_avg, const float* exp_avg_sq, float* state, int64_t n,
                    void* hip_stream) {
-    if (!size_ok(n)) return ZS_EINVAL;
-    if (n == 0) return ZS_OK;
-    if (state == nullptr || !aligned(state, 16)) return ZS_EINVAL;
     const float* src[3] = {master, exp_avg, exp_avg_sq};
-    const int64_t state_bytes = state_tiled_numel(n) * 4;
-    for (int k = 0; k < 3; ++k) {
-        if (src[k] != nullptr && !aligned(src[k], 4)) return ZS_EINVAL;
-        if (overlap(src[k], src[k] ? n * 4 : 0, state, state_bytes)) return ZS_EOVERLAP;
-    }
-    return hip_status(zs::launch_state_tile(src, state, n, as_stream(hip_stream)));
+    return tile_runs(src, 3, state, n, hip_stream);
 }
 
 int32_t state_untile(const float* state, float* master, float* exp_avg, float* exp_avg_sq, int64_t n,
                      void* hip_stream) {
-    if (!size_ok(n)) return ZS_EINVAL;
-    if (n == 0) return ZS_OK;
-    if (state == nullptr || !aligned(state, 16)) return ZS_EINVAL;
     float* dst[3] = {master, exp_avg, exp_avg_sq};
-    const int64_t state_bytes = state_tiled_numel(n) * 4;
-    bool vec = true;
-    for (int k = 0; k < 3; ++k) {
-        if (dst[k] == nullptr) continue;
-        if (!aligned(dst[k], 4)) return ZS_EINVAL;
-        if (overlap(dst[k], n * 4, state, state_bytes)) return ZS_EOVERLAP;
-        for (int j = k + 1; j < 3; ++j)
-            if (dst[j] != nullptr && overlap(dst[k], n * 4, dst[j], n * 4)) return ZS_EOVERLAP;
-        vec = vec && aligned(dst[k], 16);
-    }
-    return hip_status(zs::launch_state_untile(state, dst, n, vec, as_stream(hip_stream)));
+    return untile_runs(state, 3, dst, n, hip_stream);
+}
+
+int32_t moments_tile(const float* exp_avg, const float* exp_avg_sq, float* moments, int64_t n, void* hip_stream) {
+    const float* src[2] = {exp_avg, exp_avg_sq};
+    return tile_runs(src, 2, moments, n, hip_stream);
+}
+
+int32_t moments_untile(const float* moments, float* exp_avg, float* exp_avg_sq, int64_t n, void* hip_stream) {
+    float* dst[2] = {exp_avg, exp_avg_sq};
+    return untile_runs(moments, 2, dst, n, hip_stream);
 }
 
 // the tiled master-form step: host scalars (hp) or a device copy of them (sc_dev)
@@ -436,6 +459,49 @@ int32_t adamw_step_tiled_dev(const zs_adamw_scalars* scalars_dev, float* state, 
                              uint16_t* param_bf16, int64_t n, const double* norm_sq_dev, void* hip_stream) {
     if (scalars_dev == nullptr) return ZS_EINVAL;
     return adamw_tiled(nullptr, scalars_dev, state, grad, param_bf16, n, norm_sq_dev, hip_stream);
+}
+
+int32_t adam_update_tiled(const zs_adamw* hp, float* moments, const float* grad, float* update, int64_t n,
+                          const double* norm_sq_dev, void* hip_stream) {
+    int32_t rc = adamw_check_hp(hp, n, norm_sq_dev);
+    if (rc != ZS_OK) return rc;
+    if (hp->weight_decay != 0.0) return ZS_EINVAL;
+    if (n == 0) return ZS_OK;
+    if (moments == nullptr || grad == nullptr || update == nullptr) return ZS_EINVAL;
+    if (!aligned(moments, 16) || !aligned(grad, 4) || !aligned(update, 4)) return ZS_EINVAL;
+    const void* bufs[5] = {moments, grad, update, nullptr, nullptr};
+    const int64_t bytes[5] = {moments_tiled_numel(n) * 4, n * 4, n * 4, 0, 0};
+    const bool written[5] = {true, false, true, false, false};
+    rc = adamw_check_overlap(bufs, bytes, written, norm_sq_dev);
+    if (rc != ZS_OK) return rc;
+    zs::AdamwArgs a = make_args(hp, norm_sq_dev);
+    a.state = moments;
+    a.grad = grad;
+    a.update = update;
+    a.n = n;
+    // the moments are 16-byte aligned by contract; the update may sit at any element offset
+    return hip_status(zs::launch_adam_update_tiled(a, aligned(update, 16), as_stream(hip_stream)));
+}
+
+int32_t adamw_step_no_master_tiled(const zs_adamw* hp, uint16_t* param_bf16, float* moments, const float* grad,
+                                   int64_t n, const double* norm_sq_dev, void* hip_stream) {
+    int32_t rc = adamw_check_hp(hp, n, norm_sq_dev);
+    if (rc != ZS_OK) return rc;
+    if (n == 0) return ZS_OK;
+    if (param_bf16 == nullptr || moments == nullptr || grad == nullptr) return ZS_EINVAL;
+    if (!aligned(param_bf16, 2) || !aligned(moments, 16) || !aligned(grad, 4)) return ZS_EINVAL;
+    const void* bufs[5] = {param_bf16, moments, grad, nullptr, nullptr};
+    const int64_t bytes[5] = {n * 2, moments_tiled_numel(n) * 4, n * 4, 0, 0};
+    const bool written[5] = {true, true, false, false, false};
+    rc = adamw_check_overlap(bufs, bytes, written, norm_sq_dev);
+    if (rc != ZS_OK) return rc;
+    zs::AdamwArgs a = make_args(hp, norm_sq_dev);
+    a.state = moments;
+    a.grad = grad;
+    a.param_bf16 = param_bf16;
+    a.n = n;
+    // the bf16 parameter is read and written: the vector path needs it 16-byte aligned
+    return hip_status(zs::launch_adamw_no_master_tiled(a, aligned(param_bf16, 16), as_stream(hip_stream)));
 }
 
 int32_t adamw_step_no_master(const zs_adamw* hp, uint16_t* param_bf16, float* exp_avg, float* exp_avg_sq,

@@ -77,23 +77,26 @@ struct AdamwScalars {
 };
 
 // --- tiled optimizer state ------------------------------------------------
-// The fp32 master, exp_avg and exp_avg_sq of a shard in one buffer: for each
-// tile of kStateTile elements, the tile's masters, then its exp_avgs, then its
-// exp_avg_sqs, each a run of kStateTile floats (the last tile keeps full-length
-// runs; its unused ends are padding).  Element i's master sits at
-// tiled_offset(i), its exp_avg kStateTile floats later, its exp_avg_sq
-// 2*kStateTile later.  Equal to ZS_STATE_TILE in zshard.h (checked in api.hip).
+// R fp32 arrays of a shard in one buffer: for each tile of kStateTile
+// elements, a run of kStateTile floats of each array, one after the other
+// (the last tile keeps full-length runs; its unused ends are padding).  The
+// state of the master forms has R = 3 runs (master, exp_avg, exp_avg_sq), the
+// moments of the no-master and update forms R = 2 (exp_avg, exp_avg_sq).
+// Element i's first value sits at tiled_offset<R>(i), its k-th k*kStateTile
+// floats later.  kStateTile equals ZS_STATE_TILE in zshard.h (checked in
+// api.hip).
 constexpr int64_t kStateTile = 8192;
+template <int R = 3>
 __host__ __device__ __forceinline__ int64_t tiled_offset(int64_t i) {
     const uint64_t u = (uint64_t)i;
-    return (int64_t)((u / kStateTile) * (3 * kStateTile) + (u % kStateTile));
+    return (int64_t)((u / kStateTile) * (R * kStateTile) + (u % kStateTile));
 }
 
 struct AdamwArgs {
     AdamwScalars sc;            // in the kernel arguments, unless sc_dev is set
     const AdamwScalars* sc_dev; // device copy of the scalars (a step replayable from a graph), nullable
     const double* norm_sq;      // device, nullable
-    float* state;               // tiled form: master, exp_avg, exp_avg_sq in the tiled layout
+    float* state;               // tiled forms: master, exp_avg, exp_avg_sq (or the moments alone) tiled
     float* master;
     float* exp_avg;
     float* exp_avg_sq;
@@ -121,11 +124,13 @@ hipError_t launch_adamw(const AdamwArgs& a, bool vec_ok, bool out_aligned, hipSt
 hipError_t launch_adamw_no_master(const AdamwArgs& a, bool vec_ok, hipStream_t stream);
 hipError_t launch_adam_update(const AdamwArgs& a, bool vec_ok, bool out_aligned, hipStream_t stream);
 hipError_t launch_adamw_tiled(const AdamwArgs& a, bool out_aligned, hipStream_t stream);
-// split fp32 arrays (each nullable: zeros) -> tiled state, padding zeroed; and back
-// (each destination nullable: skipped)
-hipError_t launch_state_tile(const float* const src[3], float* state, int64_t n, hipStream_t stream);
-hipError_t launch_state_untile(const float* state, float* const dst[3], int64_t n, bool vec_ok,
-                               hipStream_t stream);
+hipError_t launch_adam_update_tiled(const AdamwArgs& a, bool out_aligned, hipStream_t stream);
+hipError_t launch_adamw_no_master_tiled(const AdamwArgs& a, bool vec_ok, hipStream_t stream);
+// runs (2 or 3) split fp32 arrays (each nullable: zeros) -> tiled buffer,
+// padding zeroed; and back (each destination nullable: skipped)
+hipError_t launch_tile_runs(const float* const* src, int runs, float* buf, int64_t n, hipStream_t stream);
+hipError_t launch_untile_runs(const float* buf, int runs, float* const* dst, int64_t n, bool vec_ok,
+                              hipStream_t stream);
 hipError_t launch_grad_accum(float* acc, const void* grad, int grad_bf16, int64_t n,
                              int overwrite, bool vec_ok, hipStream_t stream);
 int64_t norm_partials(int64_t n);   // grad_norm_sq's stage-1 partials for n elements

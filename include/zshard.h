@@ -409,6 +409,23 @@ ZS_API int32_t adamw_step_tiled_dev(const zs_adamw_scalars* scalars_dev, float* 
                                     uint16_t* param_bf16, int64_t n, const double* norm_sq_dev, void* hip_stream);
 
 /*
+ * Tiled moments — the same layout for the forms that keep no fp32 master
+ * (adamw_step_no_master, adam_update): per tile of ZS_STATE_TILE elements,
+ * the tile's exp_avgs, then its exp_avg_sqs, two runs of ZS_STATE_TILE floats:
+ *   moments[(2*t + 0)*ZS_STATE_TILE + j]  exp_avg    of element t*ZS_STATE_TILE + j
+ *   moments[(2*t + 1)*ZS_STATE_TILE + j]  exp_avg_sq of that element
+ * moments_tiled_numel(n) floats (2 * ZS_STATE_TILE * ceil(n / ZS_STATE_TILE),
+ * -1 for an invalid n; host only), 16-byte aligned.  moments_tile and
+ * moments_untile convert as state_tile and state_untile do (NULL source:
+ * zeros; NULL destination: skipped; same rules and errors).
+ */
+ZS_API int64_t moments_tiled_numel(int64_t n);
+ZS_API int32_t moments_tile(const float* exp_avg, const float* exp_avg_sq, float* moments, int64_t n,
+                            void* hip_stream);
+ZS_API int32_t moments_untile(const float* moments, float* exp_avg, float* exp_avg_sq, int64_t n,
+                              void* hip_stream);
+
+/*
  * adamw_step_no_master — the same update with no fp32 master: the bf16
  * parameter shard is read, updated and rounded back in place.
  * [ZeRO page] §"ZeRO-3: 切分参数", ZeRO3Optimizer.step (the update is added
@@ -443,6 +460,23 @@ ZS_API int32_t adamw_step_no_master(const zs_adamw* hp, uint16_t* param_bf16, fl
  */
 ZS_API int32_t adam_update(const zs_adamw* hp, float* exp_avg, float* exp_avg_sq, const float* grad, float* update,
                            int64_t n, const double* norm_sq_dev, void* hip_stream);
+
+/*
+ * adam_update_tiled, adamw_step_no_master_tiled — adam_update and
+ * adamw_step_no_master with exp_avg and exp_avg_sq read from and written
+ * back to tiled moments: the same arithmetic, results bit for bit, bytes per
+ * element and rules (adam_update_tiled requires weight_decay = 0).
+ * moments: device fp32[moments_tiled_numel(n)], 16-byte aligned, read-write
+ * (padding untouched); grad: device fp32[n], read; update: device fp32[n],
+ * written, at any element offset; param_bf16: device bf16[n], read-write.  No
+ * two may overlap, nor overlap *norm_sq_dev.  Errors: as the split forms, or
+ * ZS_EINVAL for moments not 16-byte aligned.
+ */
+ZS_API int32_t adam_update_tiled(const zs_adamw* hp, float* moments, const float* grad, float* update, int64_t n,
+                                 const double* norm_sq_dev, void* hip_stream);
+ZS_API int32_t adamw_step_no_master_tiled(const zs_adamw* hp, uint16_t* param_bf16, float* moments,
+                                          const float* grad, int64_t n, const double* norm_sq_dev,
+                                          void* hip_stream);
 
 /* Static description of a return code. */
 ZS_API const char* zs_strerror(int32_t code);

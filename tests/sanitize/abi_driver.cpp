@@ -71,6 +71,12 @@ int main() {
     CHECK(state_untile(st, f, f + 8, nullptr, 16, nullptr) == ZS_EOVERLAP, 16);
     CHECK(state_untile(st, f, nullptr, nullptr, int64_t(1) << 40, nullptr) == ZS_EINVAL, 16);
     CHECK(state_untile(st, nullptr, nullptr, nullptr, 0, nullptr) == ZS_OK, 16);
+    CHECK(moments_tiled_numel(1) == 2 * ZS_STATE_TILE && moments_tiled_numel(-1) == -1, 17);
+    CHECK(moments_tile(f, nullptr, st + 2, 16, nullptr) == ZS_EINVAL, 17);
+    CHECK(moments_untile(st, f, f + 4, 16, nullptr) == ZS_EOVERLAP, 17);
+    CHECK(adam_update_tiled(&hp, st, f, f + 4096, 16, nullptr, nullptr) == ZS_EINVAL, 17);   // decay refused
+    CHECK(adamw_step_no_master_tiled(&hp, static_cast<uint16_t*>(fake(1)), st, f, 16, nullptr, nullptr) ==
+              ZS_EINVAL, 17);
 
     CHECK(grad_accum(f, f + 1, 3, 8, 0, nullptr) == ZS_EINVAL, 7);
     CHECK(grad_accum(f, f + 1, ZS_F32, 8, 0, nullptr) == ZS_EOVERLAP, 7);

@@ -37,7 +37,7 @@ def no_launch_reached():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 22 and set(names) == set(B.EXPORTS), names
+    assert len(names) == 27 and set(names) == set(B.EXPORTS), names
     L = zs.lib()
     for name in names:
         assert getattr(L, name) is not None
@@ -251,6 +251,38 @@ def test_adamw_step_tiled_rejects():
     assert dev(s=sc + 4) == B.ZS_EINVAL
     assert dev(s=st + 64) == B.ZS_EOVERLAP                          # scalars inside the written state
     assert dev(k=0) == B.ZS_OK
+
+
+def test_moments_calls_reject():
+    L = zs.lib()
+    T = B.STATE_TILE
+    n = 1024
+    mo = FAKE + 2**30
+    mb = 2 * T * 4                                                # tiled bytes of 1024 elements
+    assert L.moments_tiled_numel(1) == 2 * T and L.moments_tiled_numel(-1) == -1
+    assert L.moments_tiled_numel(5 * T + 1) == oracle.moments_tiled_numel(5 * T + 1, T) == 12 * T
+    assert L.moments_tile(FAKE, FAKE + 2**20, mo + 4, n, None) == B.ZS_EINVAL             # off 16 bytes
+    assert L.moments_tile(FAKE, mo + mb - 4, mo, n, None) == B.ZS_EOVERLAP
+    assert L.moments_untile(mo, FAKE, FAKE + 8, n, None) == B.ZS_EOVERLAP                  # two destinations
+    assert L.moments_untile(mo, FAKE + 2, None, n, None) == B.ZS_EINVAL
+    assert L.moments_tile(None, None, None, 0, None) == B.ZS_OK
+    upd = lambda hp=None, m=mo, g=FAKE, u=FAKE + 2**20, k=n, norm=0: L.adam_update_tiled(
+        ctypes.byref(hp or _hp()), m, g, u, k, norm, None)
+    assert upd(hp=_hp(weight_decay=0.1)) == B.ZS_EINVAL                                      # no decay
+    assert upd(hp=_hp(step=0)) == B.ZS_EINVAL
+    assert upd(m=mo + 4) == B.ZS_EINVAL
+    assert upd(u=FAKE + 2**20 + 2) == B.ZS_EINVAL                                            # fp32: 4 bytes
+    assert upd(g=mo + 16) == B.ZS_EOVERLAP
+    assert upd(norm=mo + 64) == B.ZS_EOVERLAP                                                # norm in the moments
+    assert upd(k=0) == B.ZS_OK
+    nm = lambda hp=None, p=FAKE, m=mo, g=FAKE + 2**20, k=n, norm=0: L.adamw_step_no_master_tiled(
+        ctypes.byref(hp or _hp()), p, m, g, k, norm, None)
+    assert nm(hp=_hp(eps=0.0)) == B.ZS_EINVAL
+    assert nm(p=FAKE + 1) == B.ZS_EINVAL                                                     # bf16: 2 bytes
+    assert nm(m=mo + 8) == B.ZS_EINVAL
+    assert nm(p=mo + mb - 2) == B.ZS_EOVERLAP
+    assert nm(k=(1 << 39) + 1) == B.ZS_EINVAL
+    assert nm(k=0) == B.ZS_OK
 
 
 def test_adam_update_rejects():

@@ -296,3 +296,42 @@ def test_state_tile_validation_matches_the_documented_rules(ptrs, n, untile):
             return
         got = L.state_tile(a or None, b or None, c or None, state or None, n, None)
     assert got == want, (untile, [hex(p) for p in ptrs], n)
+
+
+def moments_update_model(hp, moments, g, u, n, norm):
+    rc = hp_model(hp, n, norm)
+    if rc is not None:
+        return rc
+    if hp[4] != 0.0:   # weight decay
+        return EINVAL
+    if n == 0:
+        return OK
+    if not (moments and g and u):
+        return EINVAL
+    if moments % 16 or g % 4 or u % 4:
+        return EINVAL
+    bufs = [(moments, 4 * 2 * TILE * (-(-n // TILE)), True), (g, 4 * n, False), (u, 4 * n, True)]
+    for i in range(3):
+        for j in range(i + 1, 3):
+            if overlap(bufs[i][0], bufs[i][1], bufs[j][0], bufs[j][1]):
+                return EOVERLAP
+        if norm and bufs[i][2] and overlap(bufs[i][0], bufs[i][1], norm, 8):
+            return EOVERLAP
+    return None
+
+
+@SETTINGS
+@given(hp=hyperparameters(), ptrs=st.tuples(big_pointers, big_pointers, big_pointers), n=tiled_sizes,
+       wd0=st.booleans(),
+       norm=st.one_of(st.just(0), st.builds(lambda slot, off: BASE + slot * 65536 + off,
+                                            st.integers(0, 7), st.sampled_from([0, 8, 40000, 4]))))
+def test_adam_update_tiled_validation_matches_the_documented_rules(hp, ptrs, n, wd0, norm):
+    if wd0:
+        hp = hp[:4] + (0.0,) + hp[5:]
+    mo, g, u = ptrs
+    want = moments_update_model(hp, mo, g, u, n, norm)
+    if want is None:
+        return
+    c = B.AdamW(*hp[:8], hp[8])
+    got = zs.lib().adam_update_tiled(ctypes.byref(c), mo or None, g or None, u or None, n, norm or None, None)
+    assert got == want, (hp, [hex(p) for p in ptrs], n, hex(norm))

@@ -158,7 +158,9 @@ def test_every_other_entry_point_replays_bit_exact():
     """flat_pack (bit copy with padding; widening), grad_reduce_chunks,
     grad_norm_sq, adamw_step_no_master, adam_update, flat_unpack (re-cast),
     flat_apply_update (bf16 and fp32 tensors), adamw_step_tiled on a tiled
-    state, state_untile and state_tile captured in one graph and replayed
+    state, state_untile, state_tile, adam_update_tiled and
+    adamw_step_no_master_tiled on tiled moments, moments_untile and
+    moments_tile captured in one graph and replayed
     four times with fresh inputs, each replay bit-identical to the same
     calls made eagerly on a twin state."""
     dev = torch.device("cuda")
@@ -191,7 +193,12 @@ def test_every_other_entry_point_replays_bit_exact():
                 "state": tiled(torch.rand(T, generator=gen, device=dev) * 0.2 - 0.1),
                 "bt": torch.empty(T, dtype=torch.bfloat16, device=dev),
                 "um": torch.empty(T, device=dev), "uv": torch.empty(T, device=dev),
-                "state2": torch.empty(zs.state_tiled_numel(T), device=dev)}
+                "state2": torch.empty(zs.state_tiled_numel(T), device=dev),
+                "mo": torch.zeros(zs.moments_tiled_numel(T), device=dev),
+                "mo2": torch.zeros(zs.moments_tiled_numel(T), device=dev),
+                "mo3": torch.empty(zs.moments_tiled_numel(T), device=dev),
+                "upd2": torch.empty(T, device=dev), "um2": torch.empty(T, device=dev),
+                "p16b": (torch.rand(T, generator=gen, device=dev) * 0.2 - 0.1).to(torch.bfloat16)}
 
     def tiled(master):
         st = torch.empty(zs.state_tiled_numel(T), device=dev)
@@ -214,6 +221,10 @@ def test_every_other_entry_point_replays_bit_exact():
         zs.adamw_step_tiled(hp, s["state"], s["acc"], s["bt"], norm_sq=s["norm"])
         zs.state_untile(s["state"], None, s["um"], s["uv"], n=T)
         zs.state_tile(s["m1"], None, s["v1"], s["state2"])
+        zs.adam_update_tiled(hu, s["mo"], s["acc"], s["upd2"], norm_sq=s["norm"])
+        zs.adamw_step_no_master_tiled(hp, s["p16b"], s["mo2"], s["acc"], norm_sq=s["norm"])
+        zs.moments_untile(s["mo"], s["um2"], None, n=T)
+        zs.moments_tile(s["m2"], s["v2"], s["mo3"])
 
     def fresh(r):
         for p in params:

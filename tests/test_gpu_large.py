@@ -206,6 +206,60 @@ def test_tiled_state_across_pieces(b_off):
     release()
 
 
+@pytest.mark.parametrize("out_off", [0, 1])
+def test_tiled_moments_across_pieces(out_off):
+    """moments_tile, a clipped adam_update_tiled (the update a view
+    out_off elements into its buffer), adamw_step_no_master_tiled and
+    moments_untile over N elements (a launch piece starts the tiled moments
+    2 * 2^31 floats in): bit-exact on the sample."""
+    need_gib(62)
+    log(f"tiled moments across pieces n={N} out_off={out_off}")
+    idx = sample_indices(N, seed=71 + out_off)
+    m = fill_normal(buffer(N, 0), 1e-4, 701)
+    v = fill_uniform(buffer(N, 0), 0.0, 1e-8, 702)
+    grad = fill_normal(buffer(N, 0), 1e-3, 703)
+    upd = buffer(N, out_off)
+    param = bf16_normal(N, out_off, 0.05, 704)
+    mo = torch.empty(zs.moments_tiled_numel(N), dtype=torch.float32, device=DEV)
+    where = (idx // STATE_TILE) * (2 * STATE_TILE) + idx % STATE_TILE
+    m_ref, v_ref, g_s, b_ref = host(m[idx]), host(v[idx]), host(grad[idx]), host(param[idx])
+
+    log("  moments_tile")
+    zs.moments_tile(m, v, mo)
+    check("tile m", mo, where, m_ref)
+    check("tile v", mo, where + STATE_TILE, v_ref)
+
+    scale, extra, max_norm = 1.0 / 64, 2.0, 1.0
+    S = oracle.grad_norm_sq(host(grad), scale)
+    assert oracle.clip_coef(S, extra, max_norm) < 1.0
+    norm = torch.tensor([S], dtype=torch.float64, device=DEV)
+    log("  adam_update_tiled")
+    hu = zs.AdamWConfig(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.0, grad_scale=scale,
+                        max_norm=max_norm, extra_norm_sq=extra, step=3)
+    zs.adam_update_tiled(hu, mo, grad, upd, norm_sq=norm)
+    u_ref = np.empty(idx.numel(), np.float32)
+    H = oracle.make_hp(3e-4, 0.9, 0.95, 1e-8, 0.0, scale, max_norm, extra, 3)
+    assert oracle.adam_update(H, m_ref, v_ref, g_s, u_ref, norm_sq=S) == 0
+    check("update", upd, idx, u_ref)
+    check("m", mo, where, m_ref)
+    check("v", mo, where + STATE_TILE, v_ref)
+
+    log("  adamw_step_no_master_tiled")
+    hp = zs.AdamWConfig(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, grad_scale=scale,
+                        max_norm=max_norm, extra_norm_sq=extra, step=4)
+    zs.adamw_step_no_master_tiled(hp, param, mo, grad, norm_sq=norm)
+    H = oracle.make_hp(3e-4, 0.9, 0.95, 1e-8, 0.1, scale, max_norm, extra, 4)
+    assert oracle.adamw_step_no_master(H, b_ref, m_ref, v_ref, g_s, norm_sq=S) == 0
+    check("bf16", param, idx, b_ref)
+
+    log("  moments_untile")
+    zs.moments_untile(mo, m, v)
+    check("untile m", m, idx, m_ref)
+    check("untile v", v, idx, v_ref)
+    del m, v, grad, upd, param, mo
+    release()
+
+
 @pytest.mark.parametrize("offset", [0, 1])
 def test_accumulations_across_pieces(offset):
     """grad_accum (overwrite, add) and grad_accum_norm_sq (the accumulating

@@ -217,3 +217,87 @@ def test_adamw_step_tiled_skips_on_nonfinite_norm():
     zs.adamw_step_tiled(zs.AdamWConfig(lr=1e-3, extra_norm_sq=float("inf"), step=1), st, g, b, norm_sq=norm)
     torch.cuda.synchronize()
     assert bits_equal(to_np(st), state0)
+
+
+# ---------------------------------------------------------------------------
+# tiled moments (exp_avg, exp_avg_sq): the no-master and ZeRO-1 update forms
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n", [1, 5, 8192, 8193, 3 * 8192 + 7, 100_003])
+@pytest.mark.parametrize("offset", [0, 1])
+def test_moments_tile_untile_bit_exact(n, offset):
+    """moments_tile from (possibly misaligned) views, one source missing,
+    equals the oracle's layout bit for bit, padding zeros included;
+    moments_untile inverts it into views."""
+    print(f"moments tile/untile n={n} offset={offset}", flush=True)
+    rng = np.random.default_rng(3 * n + offset)
+    _, m, v = random_state(rng, n)
+    want = oracle.moments_tile(None, v, n, T)
+    assert zs.moments_tiled_numel(n) == want.size
+    vd, vw = dev_buf(v, offset)
+    mo, mow = state_dev(np.full(want.size, np.nan, np.float32))
+    zs.moments_tile(None, vd, mo, n=n)
+    torch.cuda.synchronize()
+    assert bits_equal(to_np(mo), want) and canary_ok(mow, 0, want.size) and canary_ok(vw, offset, n)
+    full, _ = state_dev(oracle.moments_tile(m, v, n, T))
+    outs = [dev_buf(np.zeros(n, np.float32), offset) for _ in range(2)]
+    zs.moments_untile(full, outs[0][0], outs[1][0])
+    torch.cuda.synchronize()
+    assert bits_equal(to_np(outs[0][0]), m) and bits_equal(to_np(outs[1][0]), v)
+    for view, whole in outs:
+        assert canary_ok(whole, offset, n)
+
+
+@pytest.mark.parametrize("n", [1, 7, 8193, 100_003])
+@pytest.mark.parametrize("upd_off", [0, 1, 2, 3])
+@pytest.mark.parametrize("clip", [False, True])
+def test_adam_update_tiled_bit_exact(n, upd_off, clip):
+    """Four steps of the ZeRO-1 update on tiled moments, the update a view
+    at any element offset, handed the oracle's norm: moments and update
+    bit-identical to the oracle's split-array adam_update."""
+    print(f"adam_update tiled n={n} upd_off={upd_off} clip={clip}", flush=True)
+    rng = np.random.default_rng(11 * n + upd_off + 5 * clip)
+    m_ref, v_ref, u_ref = np.zeros(n, np.float32), np.zeros(n, np.float32), np.empty(n, np.float32)
+    mo, mow = state_dev(oracle.moments_tile(m_ref, v_ref, n, T))
+    u, uw = dev_buf(np.zeros(n, np.float32), upd_off)
+    for t in range(1, 5):
+        acc = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+        S = oracle.grad_norm_sq(acc, 1 / 8)
+        hp_gpu, hp_orc = _hp(t, lr=1e-4, b2=0.999, wd=0.0, scale=1 / 8,
+                             max_norm=0.7 * math.sqrt(S * 8) if clip else 0.0, extra=7 * S)
+        assert oracle.adam_update(hp_orc, m_ref, v_ref, acc, u_ref, norm_sq=S if clip else None) == 0
+        g, gw = dev_buf(acc, 1)
+        norm = torch.tensor([S], dtype=torch.float64, device="cuda") if clip else None
+        zs.adam_update_tiled(hp_gpu, mo, g, u, norm_sq=norm)
+        torch.cuda.synchronize()
+        assert bits_equal(to_np(mo), oracle.moments_tile(m_ref, v_ref, n, T)), t
+        assert bits_equal(to_np(u), u_ref), (t, identical_fraction(to_np(u), u_ref))
+        assert canary_ok(gw, 1, n)
+    assert canary_ok(mow, 0, mo.numel()) and canary_ok(uw, upd_off, n)
+
+
+@pytest.mark.parametrize("n", [1, 7, 8193, 100_003])
+@pytest.mark.parametrize("p_off", [0, 1, 3])
+@pytest.mark.parametrize("clip", [False, True])
+def test_adamw_no_master_tiled_bit_exact(n, p_off, clip):
+    """Four steps of the no-master update on tiled moments, the bf16
+    parameter aligned (vector path) or at an odd element offset (the
+    element-wise path), handed the oracle's norm: bit-identical."""
+    print(f"no-master tiled n={n} p_off={p_off} clip={clip}", flush=True)
+    rng = np.random.default_rng(13 * n + p_off + 7 * clip)
+    b_ref = oracle.bf16_rne(rng.uniform(-0.1, 0.1, n).astype(np.float32))
+    m_ref, v_ref = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    mo, mow = state_dev(oracle.moments_tile(m_ref, v_ref, n, T))
+    b, bw = dev_buf(b_ref, p_off, bf16=True)
+    for t in range(1, 5):
+        acc = (rng.standard_normal(n) * 1e-2).astype(np.float32)
+        S = oracle.grad_norm_sq(acc, 1 / 16)
+        hp_gpu, hp_orc = _hp(t, lr=2e-3, scale=1 / 16, max_norm=0.5 * math.sqrt(S) if clip else 0.0, extra=0.1 * S)
+        assert oracle.adamw_step_no_master(hp_orc, b_ref, m_ref, v_ref, acc, norm_sq=S if clip else None) == 0
+        g, _ = dev_buf(acc, 0)
+        norm = torch.tensor([S], dtype=torch.float64, device="cuda") if clip else None
+        zs.adamw_step_no_master_tiled(hp_gpu, b, mo, g, norm_sq=norm)
+        torch.cuda.synchronize()
+        assert bits_equal(to_np(mo), oracle.moments_tile(m_ref, v_ref, n, T)), t
+        assert bits_equal(to_np(b), b_ref), (t, identical_fraction(to_np(b), b_ref))
+    assert canary_ok(mow, 0, mo.numel()) and canary_ok(bw, p_off, n)
