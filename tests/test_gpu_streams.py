@@ -54,11 +54,12 @@ def test_calls_run_on_the_stream_they_are_given():
     acc = torch.zeros(n, device="cuda")
     flat = torch.zeros(1008, dtype=torch.bfloat16, device="cuda")
     master, m, v = (torch.zeros(n, device="cuda") for _ in range(3))
+    state = torch.zeros(zs.state_tiled_numel(n), device="cuda")   # the same step on the tiled layout
     hp = zs.AdamWConfig(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, grad_scale=1.0, step=1)
     spin = _spin_ms()
     observed = False
     for attempt in range(3):   # the check needs the host to read within the spin: retry if it did not
-        for t in (acc, flat, master, m, v):
+        for t in (acc, flat, master, m, v, state):
             t.zero_()
         torch.cuda.synchronize()
         s = _held_side_stream()
@@ -66,7 +67,8 @@ def test_calls_run_on_the_stream_they_are_given():
         zs.grad_accum(acc, g, overwrite=True, stream=s)
         zs.flat_pack(srcs, flat, 1008, stream=s)
         zs.adamw_step(hp, master, m, v, acc, stream=s)
-        early = [to_np(t) for t in (acc, flat, master)]   # the default stream does not wait for s
+        zs.adamw_step_tiled(hp, state, acc, stream=s)
+        early = [to_np(t) for t in (acc, flat, master, state)]   # the default stream does not wait for s
         host_ms = (time.perf_counter() - t0) * 1e3
         s.synchronize()
         if host_ms < 0.5 * spin:
@@ -82,15 +84,20 @@ def test_calls_run_on_the_stream_they_are_given():
     H = oracle.make_hp(1e-3, 0.9, 0.999, 1e-8, 0.0, 1.0, 0.0, 0.0, 1)
     assert oracle.adamw_step(H, p_ref, m_ref, v_ref, oracle.bf16_widen(g_np)) == 0
     assert bits_equal(to_np(master), p_ref) and bits_equal(to_np(m), m_ref) and bits_equal(to_np(v), v_ref)
+    split = [torch.empty(n, device="cuda") for _ in range(3)]
+    zs.state_untile(state, *split)
+    for got, want in zip(split, (p_ref, m_ref, v_ref)):
+        assert bits_equal(to_np(got), want)
 
 
-def test_two_host_threads_on_two_streams_match_serial_runs():
+@pytest.mark.parametrize("layout", ["split", "tiled"])
+def test_two_host_threads_on_two_streams_match_serial_runs(layout):
     """The library keeps no global state (only a thread-local error code):
     two host threads, each driving its own shard on its own stream through
     ten accumulate / fused-norm / clipped-AdamW steps, end bit-identical to
     the same sequences run one after the other on the default stream."""
     import threading
-    print("two threads, two streams", flush=True)
+    print(f"two threads, two streams, {layout} state", flush=True)
     n, M, steps, scale = 300_007, 3, 10, 1 / 24
     gen = torch.Generator(device="cuda")
     gen.manual_seed(99)
@@ -99,10 +106,14 @@ def test_two_host_threads_on_two_streams_match_serial_runs():
     init = [(torch.rand(n, generator=gen, device="cuda") * 0.2 - 0.1) for _ in range(2)]
 
     def make(i):
-        return {"master": init[i].clone(), "m": torch.zeros(n, device="cuda"), "v": torch.zeros(n, device="cuda"),
-                "b": torch.empty(n, dtype=torch.bfloat16, device="cuda"), "acc": torch.empty(n, device="cuda"),
-                "norm": torch.zeros(1, dtype=torch.float64, device="cuda"),
-                "ws": torch.empty(zs.grad_accum_norm_sq_workspace_bytes(n), dtype=torch.uint8, device="cuda")}
+        d = {"master": init[i].clone(), "m": torch.zeros(n, device="cuda"), "v": torch.zeros(n, device="cuda"),
+             "b": torch.empty(n, dtype=torch.bfloat16, device="cuda"), "acc": torch.empty(n, device="cuda"),
+             "norm": torch.zeros(1, dtype=torch.float64, device="cuda"),
+             "ws": torch.empty(zs.grad_accum_norm_sq_workspace_bytes(n), dtype=torch.uint8, device="cuda"),
+             "state": torch.empty(zs.state_tiled_numel(n), device="cuda")}
+        if layout == "tiled":
+            zs.state_tile(d["master"], None, None, d["state"])
+        return d
 
     def run(i, s, stream):
         for t in range(1, steps + 1):
@@ -111,7 +122,12 @@ def test_two_host_threads_on_two_streams_match_serial_runs():
             zs.grad_accum_norm_sq(s["acc"], grads[i][M - 1], False, scale, s["norm"], s["ws"], stream=stream)
             hp = zs.AdamWConfig(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, grad_scale=scale,
                                 max_norm=0.5, extra_norm_sq=0.01 * i, step=t)
-            zs.adamw_step(hp, s["master"], s["m"], s["v"], s["acc"], s["b"], norm_sq=s["norm"], stream=stream)
+            if layout == "split":
+                zs.adamw_step(hp, s["master"], s["m"], s["v"], s["acc"], s["b"], norm_sq=s["norm"], stream=stream)
+            else:
+                zs.adamw_step_tiled(hp, s["state"], s["acc"], s["b"], norm_sq=s["norm"], stream=stream)
+        if layout == "tiled":
+            zs.state_untile(s["state"], s["master"], s["m"], s["v"], stream=stream)
 
     serial = [make(0), make(1)]
     run(0, serial[0], None)
