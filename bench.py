@@ -327,6 +327,27 @@ def run_gpu(w, steps: int, warmup: int):
         torch.cuda.synchronize()
         reduce_ms = r0.elapsed_time(r1) / 3
 
+    # outside the step: the same step with the step's micro-batch gradients
+    # all kept in device memory (ShardOptimizer.accumulate_all): one pass sums
+    # them (bit-identical accumulator), then the standalone norm and the same
+    # AdamW on the tiled state
+    staged_ms = None
+    if len(grads) > 1:
+        def staged(tt: int):
+            zs.grad_reduce_chunks(acc, grads, True)
+            zs.grad_norm_sq(acc, w.grad_scale, norm, ws)
+            zs.adamw_step_tiled(step_hp(tt), state, acc, param, norm_sq=norm)
+
+        staged(t + 1)
+        s0, s1 = ev(), ev()
+        s0.record()
+        for k in range(steps):
+            staged(t + 2 + k)
+        s1.record()
+        torch.cuda.synchronize()
+        staged_ms = s0.elapsed_time(s1) / steps
+        t += 1 + steps
+
     # outside the step: the standalone squared norm over the accumulated
     # gradient (4 B/element), as when the gradient arrives from a
     # reduce-scatter instead of this rank's own accumulation
@@ -387,7 +408,8 @@ def run_gpu(w, steps: int, warmup: int):
     copy_gbps = 2 * src.numel() * 4 / (copy_ms * 1e-3) / 1e9
     del src, dst
     return {"n": n, "wall_s": wall, "accum_ms": acc_ms, "last_ms": last_ms, "adamw_ms": adamw_ms, "graph_ms": graph_ms,
-            "split_ms": split_ms, "reduce_ms": reduce_ms, "chunks": len(grads), "no_master_ms": no_master_ms,
+            "split_ms": split_ms, "reduce_ms": reduce_ms, "staged_ms": staged_ms, "chunks": len(grads),
+            "no_master_ms": no_master_ms,
             "no_master_tiled_ms": no_master_tiled_ms,
             "copy_gbps": copy_gbps, "ceiling_ms": ceiling, "ceiling_split_ms": ceiling_split, "norm_ms": norm_ms}
 
@@ -622,6 +644,17 @@ def run_cpu_baseline(w, target_s: float = 10.0, sample: int = 1 << 25):
             "phases": phases}
 
 
+def _staged(r, n: int, w) -> dict:
+    """The step with its micro-batch gradients staged in device memory: the
+    one-pass sum (gradient bytes per micro-batch + 4 written), the norm (4)
+    and AdamW (30), timed back to back over the bench's step count."""
+    bpe = r["chunks"] * (2 if w.grad_dtype == "bf16" else 4) + 4 + 4 + 30
+    gbps = bpe * n / (r["staged_ms"] * 1e-3) / 1e9
+    return {"ms": r["staged_ms"], "elements_per_s": n / (r["staged_ms"] * 1e-3), "bytes_per_elem": bpe,
+            "gbps": gbps, "frac": gbps / HBM_PEAK_GBPS,
+            "staged_grad_bytes_per_elem": r["chunks"] * (2 if w.grad_dtype == "bf16" else 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -718,6 +751,7 @@ def main():
         "reduce_chunks": None if r["reduce_ms"] is None else {
             "chunks": r["chunks"], "ms": r["reduce_ms"],
             "gbps": (r["chunks"] * (2 if w.grad_dtype == "bf16" else 4) + 4) * n / (r["reduce_ms"] * 1e-3) / 1e9},
+        "staged_step": None if r["staged_ms"] is None else _staged(r, n, w),
     }
     print(json.dumps(out), flush=True)
 

@@ -5,7 +5,9 @@ exp_avg_sq, the fp32 gradient accumulator, the bf16 parameter shard and the
 norm scratch.  A step is: ``accumulate`` once per micro-batch (the last one
 may form the squared norm in the same pass), then ``step``: the norm (if
 not formed yet and requested) and the fused AdamW update with the bf16
-re-cast.  Nothing here computes; it orders calls.
+re-cast.  Where a step's micro-batch gradients are all kept in device memory
+(2 B per element each in bf16), ``accumulate_all`` sums them in one pass
+instead.  Nothing here computes; it orders calls.
 
 ``layout="tiled"`` (the default) keeps master, exp_avg and exp_avg_sq in
 one buffer in the library's tiled state layout, which the AdamW step
@@ -125,6 +127,18 @@ class ShardOptimizer:
             zs.grad_accum(self.acc, grad, overwrite=first)
             self._norm_ready = False
         self._pending += 1
+
+    def accumulate_all(self, grads: list) -> None:
+        """Add several micro-batch gradients held in device memory at once
+        (one dtype, fp32 or bf16) into the fp32 buffer in one pass, in list
+        order: bit-identical to accumulate() on each in turn, for far fewer
+        bytes (the buffer is read and written once, not once per gradient).
+        The norm, if wanted, is formed by step()."""
+        if not grads:
+            raise ValueError("accumulate_all: at least one gradient")
+        zs.grad_reduce_chunks(self.acc, [g.reshape(-1) for g in grads], overwrite=self._pending == 0)
+        self._norm_ready = False
+        self._pending += len(grads)
 
     def hp(self, extra_norm_sq: float = 0.0) -> zs.AdamWConfig:
         return zs.AdamWConfig(lr=self.lr, beta1=self.betas[0], beta2=self.betas[1], eps=self.eps,

@@ -164,3 +164,40 @@ def test_captured_step_replays_like_eager_steps(max_norm, layout):
         if max_norm > 0:
             assert a.norm_sq.item() == b.norm_sq.item()
         _ = (a.acc * 2).sum().item()   # unrelated eager work between replays
+
+
+@pytest.mark.parametrize("layout", ["tiled", "split"])
+def test_accumulate_all_matches_one_call_per_micro_batch(layout):
+    """accumulate_all over a step's staged micro-batch gradients (19 of them:
+    more than one pass of 16, and after one accumulate()) against accumulate()
+    per micro-batch with the norm formed by step(): accumulator equal to the
+    oracle's left fold, and accumulator, norm, master, moments and bf16
+    parameter bit-identical between the two over three clipped steps."""
+    print(f"ShardOptimizer accumulate_all layout={layout}", flush=True)
+    n, M = 2 * zs.STATE_TILE + 777, 19
+    rng = np.random.default_rng(41)
+    p0 = from_np(rng.uniform(-0.1, 0.1, n).astype(np.float32))
+    kw = dict(lr=3e-4, betas=(0.9, 0.95), weight_decay=0.1, grad_scale=1 / M, max_norm=0.5, layout=layout)
+    a, b = (zs.ShardOptimizer(p0.clone(), param_bf16=torch.empty(n, dtype=torch.bfloat16, device="cuda"), **kw)
+            for _ in range(2))
+    for t in range(1, 4):
+        mbs = [oracle.bf16_rne((rng.standard_normal(n) * 0.05 * (k + t)).astype(np.float32)) for k in range(M)]
+        gpu = [from_np(g, bf16=True) for g in mbs]
+        a.accumulate(gpu[0])
+        a.accumulate_all(gpu[1:])
+        for g in gpu:
+            b.accumulate(g)
+        acc_ref = np.empty(n, np.float32)
+        for k, g in enumerate(mbs):
+            oracle.grad_accum(acc_ref, g, oracle.BF16, overwrite=(k == 0))
+        torch.cuda.synchronize()
+        assert bits_equal(to_np(a.acc), acc_ref), t
+        a.step(extra_norm_sq=0.1)
+        b.step(extra_norm_sq=0.1)
+        torch.cuda.synchronize()
+        assert a.norm_sq.item() == b.norm_sq.item()
+        assert oracle.clip_coef(a.norm_sq.item(), 0.1, 0.5) < 1.0   # every step clips
+        for name in ("acc", "master", "exp_avg", "exp_avg_sq", "param_bf16"):
+            assert bits_equal(to_np(getattr(a, name)), to_np(getattr(b, name))), (t, name)
+    with pytest.raises(ValueError):
+        a.accumulate_all([])
