@@ -229,8 +229,8 @@ def run_gpu(w, steps: int, warmup: int):
     acc = torch.empty(n, dtype=torch.float32, device=dev)
     grads = [workloads.grad_draw(w, n, 1, mb, dev) for mb in range(w.micro_batches)]
     norm = torch.zeros(1, dtype=torch.float64, device=dev)
-    ws = torch.empty(max(zs.grad_accum_norm_sq_workspace_bytes(n), zs.grad_norm_sq_workspace_bytes(n), 8),
-                     dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(zs.grad_accum_norm_sq_workspace_bytes(n), zs.grad_norm_sq_workspace_bytes(n),
+                         zs.grad_reduce_chunks_norm_sq_workspace_bytes(n), 8), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     log(f"[bench] inputs resident: {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
 
@@ -329,13 +329,12 @@ def run_gpu(w, steps: int, warmup: int):
 
     # outside the step: the same step with the step's micro-batch gradients
     # all kept in device memory (ShardOptimizer.accumulate_all): one pass sums
-    # them (bit-identical accumulator), then the standalone norm and the same
+    # them (bit-identical accumulator) and forms the norm, then the same
     # AdamW on the tiled state
     staged_ms = None
     if len(grads) > 1:
         def staged(tt: int):
-            zs.grad_reduce_chunks(acc, grads, True)
-            zs.grad_norm_sq(acc, w.grad_scale, norm, ws)
+            zs.grad_reduce_chunks_norm_sq(acc, grads, True, w.grad_scale, norm, ws)
             zs.adamw_step_tiled(step_hp(tt), state, acc, param, norm_sq=norm)
 
         staged(t + 1)
@@ -646,9 +645,9 @@ def run_cpu_baseline(w, target_s: float = 10.0, sample: int = 1 << 25):
 
 def _staged(r, n: int, w) -> dict:
     """The step with its micro-batch gradients staged in device memory: the
-    one-pass sum (gradient bytes per micro-batch + 4 written), the norm (4)
+    one-pass sum with the norm (gradient bytes per micro-batch + 4 written)
     and AdamW (30), timed back to back over the bench's step count."""
-    bpe = r["chunks"] * (2 if w.grad_dtype == "bf16" else 4) + 4 + 4 + 30
+    bpe = r["chunks"] * (2 if w.grad_dtype == "bf16" else 4) + 4 + 30
     gbps = bpe * n / (r["staged_ms"] * 1e-3) / 1e9
     return {"ms": r["staged_ms"], "elements_per_s": n / (r["staged_ms"] * 1e-3), "bytes_per_elem": bpe,
             "gbps": gbps, "frac": gbps / HBM_PEAK_GBPS,

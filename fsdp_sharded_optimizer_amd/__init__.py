@@ -7,6 +7,7 @@ The Python names mirror the C ABI in include/zshard.h:
     flat_unpack(flat, dst_tensors)
     grad_accum(acc, grad, overwrite)
     grad_reduce_chunks(acc, chunks, overwrite)
+    grad_reduce_chunks_norm_sq(acc, chunks, overwrite, grad_scale, out, workspace=None)
     grad_accum_norm_sq(acc, grad, overwrite, grad_scale, out, workspace=None)
     grad_norm_sq(grad, grad_scale, out, workspace=None)
     adamw_step(hp, master, exp_avg, exp_avg_sq, grad, param_bf16=None, norm_sq=None)
@@ -50,6 +51,8 @@ from ._binding import (  # noqa: F401
     grad_accum_norm_sq,
     grad_accum_norm_sq_workspace_bytes,
     grad_reduce_chunks,
+    grad_reduce_chunks_norm_sq,
+    grad_reduce_chunks_norm_sq_workspace_bytes,
     grad_norm_sq,
     grad_norm_sq_workspace_bytes,
     lib,

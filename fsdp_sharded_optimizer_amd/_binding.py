@@ -32,7 +32,7 @@ EXPORTS = (
     "grad_accum_norm_sq", "adamw_step", "adamw_scalars", "adamw_step_dev", "adamw_step_no_master", "adam_update",
     "flat_apply_update", "state_tiled_numel", "state_tile", "state_untile", "adamw_step_tiled",
     "adamw_step_tiled_dev", "moments_tiled_numel", "moments_tile", "moments_untile", "adam_update_tiled",
-    "adamw_step_no_master_tiled",
+    "adamw_step_no_master_tiled", "grad_reduce_chunks_norm_sq_workspace_bytes", "grad_reduce_chunks_norm_sq",
     "zs_strerror", "zs_last_hip_error",
 )
 
@@ -115,6 +115,10 @@ def lib() -> ctypes.CDLL:
         L.grad_accum.restype = I32
         L.grad_reduce_chunks.argtypes = [P, P, I32, I32, I64, I32, P]
         L.grad_reduce_chunks.restype = I32
+        L.grad_reduce_chunks_norm_sq_workspace_bytes.argtypes = [I64]
+        L.grad_reduce_chunks_norm_sq_workspace_bytes.restype = I64
+        L.grad_reduce_chunks_norm_sq.argtypes = [P, P, I32, I32, I64, I32, D, P, P, I64, P]
+        L.grad_reduce_chunks_norm_sq.restype = I32
         L.grad_norm_sq_workspace_bytes.argtypes = [I64]
         L.grad_norm_sq_workspace_bytes.restype = I64
         L.grad_norm_sq.argtypes = [P, I64, D, P, P, I64, P]
@@ -300,6 +304,42 @@ def grad_reduce_chunks(acc: torch.Tensor, chunks: Sequence[torch.Tensor], overwr
     _check("grad_reduce_chunks", lib().grad_reduce_chunks(
         _dev(acc, "acc", torch.float32), ctypes.cast(ptrs, ctypes.c_void_p), len(chunks),
         ZS_BF16 if dt is None else dt, n, 1 if overwrite else 0, _stream(stream)))
+
+
+def _chunk_ptrs(chunks: Sequence[torch.Tensor], n: int, fn: str):
+    ptrs = (ctypes.c_void_p * max(len(chunks), 1))()
+    dt = None
+    for k, c in enumerate(chunks):
+        if c.numel() != n:
+            raise ValueError(f"{fn}: size mismatch")
+        code = _dtype_code(c)
+        if dt is not None and code != dt:
+            raise TypeError(f"{fn}: all chunks must share one dtype")
+        dt = code
+        ptrs[k] = _dev(c, f"chunks[{k}]")
+    return ptrs, ZS_BF16 if dt is None else dt
+
+
+def grad_reduce_chunks_norm_sq_workspace_bytes(n: int) -> int:
+    return int(lib().grad_reduce_chunks_norm_sq_workspace_bytes(int(n)))
+
+
+def grad_reduce_chunks_norm_sq(acc: torch.Tensor, chunks: Sequence[torch.Tensor], overwrite: bool,
+                               grad_scale: float, out: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                               stream=None) -> torch.Tensor:
+    """grad_reduce_chunks, then out[0] (fp64, device) = squared norm of fl32(acc * scale), in one pass."""
+    n = acc.numel()
+    ptrs, dt = _chunk_ptrs(chunks, n, "grad_reduce_chunks_norm_sq")
+    need = grad_reduce_chunks_norm_sq_workspace_bytes(n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=acc.device)
+    if out.dtype != torch.float64 or out.numel() < 1:
+        raise TypeError("grad_reduce_chunks_norm_sq: out must hold one float64")
+    _check("grad_reduce_chunks_norm_sq", lib().grad_reduce_chunks_norm_sq(
+        _dev(acc, "acc", torch.float32), ctypes.cast(ptrs, ctypes.c_void_p), len(chunks), dt, n,
+        1 if overwrite else 0, float(grad_scale), _dev(out, "out"), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
 
 
 def grad_norm_sq_workspace_bytes(n: int) -> int:

@@ -233,13 +233,19 @@ template <> struct Raw4<false> {
     static __device__ __forceinline__ f32x4 widen(T w) { return w; }
 };
 
-template <bool VEC, bool BF16, bool OVERWRITE>
+// NORM: the pass that folds the last chunks also adds the squares of the
+// scaled sums, one binary64 partial per wave (512 elements), as the fused
+// accumulation does for one micro-batch.
+template <bool VEC, bool BF16, bool OVERWRITE, bool NORM>
 __global__ __launch_bounds__(kReduceBlock) void reduce_chunks_kernel(float* __restrict__ acc, const ChunkBatch b,
-                                                                     int64_t n) {
+                                                                     int64_t n, float scale,
+                                                                     double* __restrict__ partials) {
+    static_assert(kReduceBlock == 64, "the norm's partial is one wave's butterfly");
     constexpr int64_t kGroup = kReduceBlock * 4;
     const int64_t tile = (int64_t)blockIdx.x * kGroup * kReduceGroups;
     const int64_t lane0 = tile + threadIdx.x * 4;
     const int count = b.count;
+    double s0 = 0.0, s1 = 0.0;
     if (VEC && tile + kGroup * kReduceGroups <= n) {   // whole tile in range
         using R = Raw4<BF16>;
         f32x4 r[kReduceGroups];
@@ -264,29 +270,49 @@ __global__ __launch_bounds__(kReduceBlock) void reduce_chunks_kernel(float* __re
                 }
             }
             st_stream(reinterpret_cast<f32x4*>(acc + lane0 + q * kGroup), r[q]);
-        }
-        return;
-    }
-    // ragged tile (or a misaligned buffer): element by element
-#pragma unroll
-    for (int q = 0; q < kReduceGroups; ++q) {
-        const int64_t first = lane0 + q * kGroup;
-        const int64_t last = first + 4 < n ? first + 4 : n;
-        for (int64_t i = first; i < last; ++i) {
-            float r = OVERWRITE ? 0.0f : acc[i];
-            for (int k = 0; k < count; ++k) {
-                const float g = load1<BF16>(b.chunk[k], i);
-                r = (OVERWRITE && k == 0) ? g : r + g;
+            if (NORM) {
+                const float rv[4] = {r[q].x, r[q].y, r[q].z, r[q].w};
+                add_squares4(rv, scale, s0, s1);
             }
-            acc[i] = r;
         }
+    } else {
+        // ragged tile (or a misaligned buffer): element by element, the same
+        // association for the norm (out-of-range elements add +0)
+#pragma unroll
+        for (int q = 0; q < kReduceGroups; ++q) {
+            const int64_t first = lane0 + q * kGroup;
+            float rv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t i = first + j;
+                if (i < n) {
+                    float r = OVERWRITE ? 0.0f : acc[i];
+                    for (int k = 0; k < count; ++k) {
+                        const float g = load1<BF16>(b.chunk[k], i);
+                        r = (OVERWRITE && k == 0) ? g : r + g;
+                    }
+                    acc[i] = r;
+                    rv[j] = r;
+                }
+            }
+            if (NORM) add_squares4(rv, scale, s0, s1);
+        }
+    }
+    if (NORM) {
+        const double total = wave_sum(s0 + s1);
+        if (threadIdx.x == 0) partials[blockIdx.x] = total;
     }
 }
 
-// one launch per kLaunchElems elements, the chunk pointers advanced with acc
-template <bool VEC, bool BF16, bool OVERWRITE>
-hipError_t launch_reduce(float* acc, const ChunkBatch& b, int64_t n, hipStream_t stream) {
-    const int64_t per = (int64_t)kReduceBlock * 4 * kReduceGroups;
+constexpr int64_t kReducePerBlock = (int64_t)kReduceBlock * 4 * kReduceGroups;
+static_assert(kLaunchElems % kReducePerBlock == 0, "pieces keep the partials' positions");
+
+// one launch per kLaunchElems elements, the chunk pointers advanced with acc;
+// piece k's partials follow piece k-1's
+template <bool VEC, bool BF16, bool OVERWRITE, bool NORM>
+hipError_t launch_reduce(float* acc, const ChunkBatch& b, int64_t n, float scale, double* partials,
+                         hipStream_t stream) {
+    const int64_t per = kReducePerBlock;
     const int64_t gsz = BF16 ? 2 : 4;
     const unsigned lds = VEC ? reduce_lds_reserve(BF16, b.count) : 0u;
     for (int64_t off = 0; off < n; off += kLaunchElems) {
@@ -294,28 +320,49 @@ hipError_t launch_reduce(float* acc, const ChunkBatch& b, int64_t n, hipStream_t
         ChunkBatch p = b;
         for (int k = 0; k < b.count; ++k) p.chunk[k] = static_cast<const char*>(b.chunk[k]) + off * gsz;
         const int64_t blocks = (m + per - 1) / per;
-        hipLaunchKernelGGL((reduce_chunks_kernel<VEC, BF16, OVERWRITE>), dim3((unsigned)blocks), dim3(kReduceBlock),
-                           lds, stream, acc + off, p, m);
+        hipLaunchKernelGGL((reduce_chunks_kernel<VEC, BF16, OVERWRITE, NORM>), dim3((unsigned)blocks),
+                           dim3(kReduceBlock), lds, stream, acc + off, p, m, scale,
+                           NORM ? partials + off / per : nullptr);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
 }
 
+template <bool NORM>
+hipError_t dispatch_reduce(float* acc, const ChunkBatch& b, bool bf16, int64_t n, bool overwrite, bool vec,
+                           float scale, double* partials, hipStream_t stream) {
+    if (vec) {
+        if (bf16) return overwrite ? launch_reduce<true, true, true, NORM>(acc, b, n, scale, partials, stream)
+                                   : launch_reduce<true, true, false, NORM>(acc, b, n, scale, partials, stream);
+        return overwrite ? launch_reduce<true, false, true, NORM>(acc, b, n, scale, partials, stream)
+                         : launch_reduce<true, false, false, NORM>(acc, b, n, scale, partials, stream);
+    }
+    if (bf16) return overwrite ? launch_reduce<false, true, true, NORM>(acc, b, n, scale, partials, stream)
+                               : launch_reduce<false, true, false, NORM>(acc, b, n, scale, partials, stream);
+    return overwrite ? launch_reduce<false, false, true, NORM>(acc, b, n, scale, partials, stream)
+                     : launch_reduce<false, false, false, NORM>(acc, b, n, scale, partials, stream);
+}
+
 }  // namespace
 
 hipError_t launch_reduce_chunks(float* acc, const ChunkBatch& b, int grad_bf16, int64_t n, int overwrite,
                                 bool vec_ok, hipStream_t stream) {
-    if (vec_ok) {
-        if (grad_bf16) return overwrite ? launch_reduce<true, true, true>(acc, b, n, stream)
-                                        : launch_reduce<true, true, false>(acc, b, n, stream);
-        return overwrite ? launch_reduce<true, false, true>(acc, b, n, stream)
-                         : launch_reduce<true, false, false>(acc, b, n, stream);
+    return dispatch_reduce<false>(acc, b, grad_bf16 != 0, n, overwrite != 0, vec_ok, 0.0f, nullptr, stream);
+}
+
+int64_t reduce_norm_partials(int64_t n) { return n <= 0 ? 0 : (n + kReducePerBlock - 1) / kReducePerBlock; }
+
+hipError_t launch_reduce_chunks_norm_sq(float* acc, const ChunkBatch& b, int grad_bf16, int64_t n, int overwrite,
+                                        bool vec_ok, float scale, double* out, double* workspace,
+                                        hipStream_t stream) {
+    const int64_t parts = reduce_norm_partials(n);
+    if (n > 0) {
+        const hipError_t e = dispatch_reduce<true>(acc, b, grad_bf16 != 0, n, overwrite != 0, vec_ok, scale,
+                                                   workspace, stream);
+        if (e != hipSuccess) return e;
     }
-    if (grad_bf16) return overwrite ? launch_reduce<false, true, true>(acc, b, n, stream)
-                                    : launch_reduce<false, true, false>(acc, b, n, stream);
-    return overwrite ? launch_reduce<false, false, true>(acc, b, n, stream)
-                     : launch_reduce<false, false, false>(acc, b, n, stream);
+    return launch_sum_partials(workspace, parts, workspace + parts, out, stream);
 }
 
 }  // namespace zs

@@ -116,6 +116,57 @@ int32_t grad_reduce_chunks(float* acc, const void* const* chunks, int32_t count,
     return ZS_OK;
 }
 
+int64_t grad_reduce_chunks_norm_sq_workspace_bytes(int64_t n) {
+    if (!size_ok(n)) return -1;
+    const int64_t parts = zs::reduce_norm_partials(n);
+    return parts == 0 ? 0 : (parts + zs::kReduceChunks) * (int64_t)sizeof(double);
+}
+
+int32_t grad_reduce_chunks_norm_sq(float* acc, const void* const* chunks, int32_t count, int32_t grad_dtype,
+                                   int64_t n, int32_t overwrite, double grad_scale, double* out_sq_dev,
+                                   void* workspace, int64_t workspace_bytes, void* hip_stream) {
+    if (!dtype_ok(grad_dtype) || !size_ok(n) || count < 1) return ZS_EINVAL;
+    if (out_sq_dev == nullptr || !aligned(out_sq_dev, 8)) return ZS_EINVAL;
+    if (!(grad_scale > 0.0) || !std::isfinite(grad_scale)) return ZS_EINVAL;
+    if (chunks == nullptr) return ZS_EINVAL;
+    const int64_t gsz = elem_size(grad_dtype);
+    if (n > 0 && (acc == nullptr || !aligned(acc, 4))) return ZS_EINVAL;
+    const int64_t need = grad_reduce_chunks_norm_sq_workspace_bytes(n);
+    if (need > 0 && (workspace == nullptr || !aligned(workspace, 8))) return ZS_EINVAL;
+    if (workspace_bytes < need) return ZS_EWORKSPACE;
+    if (overlap(acc, n * 4, out_sq_dev, 8) || overlap(workspace, need, out_sq_dev, 8) ||
+        overlap(workspace, need, acc, n * 4))
+        return ZS_EOVERLAP;
+    bool vec = aligned(acc, 16);
+    for (int32_t k = 0; k < count && n > 0; ++k) {
+        if (chunks[k] == nullptr || !aligned(chunks[k], (uintptr_t)gsz)) return ZS_EINVAL;
+        if (overlap(acc, n * 4, chunks[k], n * gsz) || overlap(chunks[k], n * gsz, out_sq_dev, 8) ||
+            overlap(workspace, need, chunks[k], n * gsz))
+            return ZS_EOVERLAP;
+        vec = vec && aligned(chunks[k], 4);   // read-only: dword alignment suffices
+    }
+    hipStream_t stream = as_stream(hip_stream);
+    // every pass but the last folds up to 16 chunks; the last also forms the norm
+    int32_t k0 = 0;
+    for (;;) {
+        zs::ChunkBatch b;
+        std::memset(&b, 0, sizeof(b));
+        b.count = count - k0 < zs::kReduceMaxChunks ? count - k0 : zs::kReduceMaxChunks;
+        for (int32_t k = 0; k < b.count; ++k) b.chunk[k] = chunks[k0 + k];
+        const int ow = (k0 == 0 && overwrite) ? 1 : 0;
+        if (k0 + b.count == count)
+            return hip_status(zs::launch_reduce_chunks_norm_sq(acc, b, grad_dtype == ZS_BF16, n, ow, vec,
+                                                               (float)grad_scale, out_sq_dev,
+                                                               static_cast<double*>(workspace), stream));
+        if (n > 0) {
+            const int32_t rc =
+                hip_status(zs::launch_reduce_chunks(acc, b, grad_dtype == ZS_BF16, n, ow, vec, stream));
+            if (rc != ZS_OK) return rc;
+        }
+        k0 += b.count;
+    }
+}
+
 int64_t grad_norm_sq_workspace_bytes(int64_t n) {
     if (!size_ok(n)) return -1;
     // one partial per 4096-element tile, then (beyond one workgroup's share)

@@ -150,6 +150,11 @@ struct ChunkBatch {
 };
 hipError_t launch_reduce_chunks(float* acc, const ChunkBatch& b, int grad_bf16, int64_t n, int overwrite,
                                 bool vec_ok, hipStream_t stream);
+// the same pass also forming the squared norm (partials, then their sum)
+int64_t reduce_norm_partials(int64_t n);
+hipError_t launch_reduce_chunks_norm_sq(float* acc, const ChunkBatch& b, int grad_bf16, int64_t n, int overwrite,
+                                        bool vec_ok, float scale, double* out, double* workspace,
+                                        hipStream_t stream);
 
 // One launch of the flatten/unflatten copy covers up to kFlatMaxTensors
 // tensors (the table travels in the kernel arguments; no device allocation).

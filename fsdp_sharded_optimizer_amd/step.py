@@ -65,7 +65,8 @@ class ShardOptimizer:
         self.weight_decay, self.grad_scale, self.max_norm = weight_decay, grad_scale, max_norm
         self.compute_norm = (max_norm > 0) if compute_norm is None else compute_norm
         self.norm_sq = torch.zeros(1, dtype=torch.float64, device=dev)
-        ws = max(zs.grad_norm_sq_workspace_bytes(n), zs.grad_accum_norm_sq_workspace_bytes(n), 8)
+        ws = max(zs.grad_norm_sq_workspace_bytes(n), zs.grad_accum_norm_sq_workspace_bytes(n),
+                 zs.grad_reduce_chunks_norm_sq_workspace_bytes(n), 8)
         self.workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
         self._norm_ready = False
         self.t = 0
@@ -128,16 +129,23 @@ class ShardOptimizer:
             self._norm_ready = False
         self._pending += 1
 
-    def accumulate_all(self, grads: list) -> None:
+    def accumulate_all(self, grads: list, last: bool = False) -> None:
         """Add several micro-batch gradients held in device memory at once
         (one dtype, fp32 or bf16) into the fp32 buffer in one pass, in list
         order: bit-identical to accumulate() on each in turn, for far fewer
         bytes (the buffer is read and written once, not once per gradient).
-        The norm, if wanted, is formed by step()."""
+        With last=True (and a norm wanted) the same pass also forms the
+        squared norm, as accumulate(last=True) does."""
         if not grads:
             raise ValueError("accumulate_all: at least one gradient")
-        zs.grad_reduce_chunks(self.acc, [g.reshape(-1) for g in grads], overwrite=self._pending == 0)
-        self._norm_ready = False
+        flat = [g.reshape(-1) for g in grads]
+        first = self._pending == 0
+        if last and self.compute_norm:
+            zs.grad_reduce_chunks_norm_sq(self.acc, flat, first, self.grad_scale, self.norm_sq, self.workspace)
+            self._norm_ready = True
+        else:
+            zs.grad_reduce_chunks(self.acc, flat, overwrite=first)
+            self._norm_ready = False
         self._pending += len(grads)
 
     def hp(self, extra_norm_sq: float = 0.0) -> zs.AdamWConfig:

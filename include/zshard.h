@@ -208,6 +208,37 @@ ZS_API int32_t grad_reduce_chunks(float* acc, const void* const* chunks, int32_t
                                   int32_t overwrite, void* hip_stream);
 
 /*
+ * grad_reduce_chunks_norm_sq_workspace_bytes — bytes of device workspace
+ * grad_reduce_chunks_norm_sq needs for n elements (0 for n == 0; -1 for
+ * n < 0 or n > 2^39).  Host only.
+ */
+ZS_API int64_t grad_reduce_chunks_norm_sq_workspace_bytes(int64_t n);
+
+/*
+ * grad_reduce_chunks_norm_sq — grad_reduce_chunks followed by grad_norm_sq
+ * of the result, in one pass over the buffer: for a step whose micro-batch
+ * gradients are all held in device memory, [ZeRO page] §"组合策略" recipe
+ * (gradient accumulation over micro-batches, then the global-norm clip) with
+ * the accumulation taken in one fold.
+ * acc: as grad_reduce_chunks, bit for bit the same left fold, in rank (or
+ * micro-batch) order.  *out_sq_dev (device binary64) = sum over i of
+ * (grad_scale * acc[i])^2 after the fold, summed as grad_accum_norm_sq sums
+ * (binary64 partials per 512 elements in a fixed tree: bit-reproducible,
+ * within 1e-5 relative of the exact sum).  count >= 1; chunks as in
+ * grad_reduce_chunks; workspace: device, 8-byte aligned, at least
+ * grad_reduce_chunks_norm_sq_workspace_bytes(n) bytes, scratch owned by the
+ * caller for the duration of the call.  n == 0 writes 0.
+ * Errors: ZS_EINVAL (count < 1, bad dtype or size, null or misaligned
+ * pointers, grad_scale not finite and > 0), ZS_EWORKSPACE (workspace too
+ * small), ZS_EOVERLAP (acc, a chunk, the workspace or *out_sq_dev overlap;
+ * chunks may alias each other), ZS_EHIP.  On an error nothing is launched,
+ * except ZS_EHIP from a launch after the first pass of more than 16 chunks.
+ */
+ZS_API int32_t grad_reduce_chunks_norm_sq(float* acc, const void* const* chunks, int32_t count, int32_t grad_dtype,
+                                          int64_t n, int32_t overwrite, double grad_scale, double* out_sq_dev,
+                                          void* workspace, int64_t workspace_bytes, void* hip_stream);
+
+/*
  * grad_norm_sq_workspace_bytes — bytes of device workspace grad_norm_sq
  * needs for n elements (0 for n == 0; -1 for n < 0 or n > 2^39).  Host only.
  */

@@ -37,7 +37,7 @@ def no_launch_reached():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 27 and set(names) == set(B.EXPORTS), names
+    assert len(names) == 29 and set(names) == set(B.EXPORTS), names
     L = zs.lib()
     for name in names:
         assert getattr(L, name) is not None
@@ -383,6 +383,33 @@ def test_grad_accum_norm_sq_rejects():
     assert call(g=FAKE + 64) == B.ZS_EOVERLAP                      # grad inside acc
     assert call(out=FAKE + 16) == B.ZS_EOVERLAP                    # norm inside acc
     assert call(ws=g + 1024) == B.ZS_EOVERLAP                      # workspace inside grad
+    assert call(n=-1) == B.ZS_EINVAL
+
+
+def test_grad_reduce_chunks_norm_sq_rejects():
+    L = zs.lib()
+    n = 1 << 20
+    need = zs.grad_reduce_chunks_norm_sq_workspace_bytes(n)
+    assert need == (n // 512 + 2048) * 8         # one partial per 512 elements + the chunk stage
+    assert zs.grad_reduce_chunks_norm_sq_workspace_bytes(0) == 0
+    assert zs.grad_reduce_chunks_norm_sq_workspace_bytes(2**39 + 1) == -1
+    acc, ws, out = FAKE, FAKE + 2**31, FAKE + 2**32
+    chunks = (ctypes.c_void_p * 2)(FAKE + 2**30, FAKE + 2**30 + 2**22)
+    call = lambda **k: L.grad_reduce_chunks_norm_sq(
+        k.get("acc", acc), k.get("chunks", chunks), k.get("count", 2), k.get("dt", B.ZS_BF16), k.get("n", n), 1,
+        k.get("s", 1.0), k.get("out", out), k.get("ws", ws), k.get("wsb", need), None)
+    assert call(count=0) == B.ZS_EINVAL and call(count=-1) == B.ZS_EINVAL
+    assert call(wsb=need - 8) == B.ZS_EWORKSPACE
+    assert call(dt=5) == B.ZS_EINVAL
+    assert call(chunks=None) == B.ZS_EINVAL
+    assert call(out=0) == B.ZS_EINVAL and call(out=out + 4) == B.ZS_EINVAL
+    assert call(s=float("inf")) == B.ZS_EINVAL and call(s=0.0) == B.ZS_EINVAL
+    assert call(acc=0) == B.ZS_EINVAL and call(acc=acc + 2) == B.ZS_EINVAL
+    assert call(ws=0) == B.ZS_EINVAL
+    assert call(chunks=(ctypes.c_void_p * 2)(FAKE + 2**30, FAKE + 64)) == B.ZS_EOVERLAP   # a chunk inside acc
+    assert call(chunks=(ctypes.c_void_p * 2)(FAKE + 2**30, FAKE + 2**30 + 1)) == B.ZS_EINVAL  # odd bf16 address
+    assert call(out=FAKE + 16) == B.ZS_EOVERLAP                    # norm inside acc
+    assert call(ws=FAKE + 2**30 + 1024) == B.ZS_EOVERLAP           # workspace inside a chunk
     assert call(n=-1) == B.ZS_EINVAL
 
 

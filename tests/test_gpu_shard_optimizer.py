@@ -166,14 +166,19 @@ def test_captured_step_replays_like_eager_steps(max_norm, layout):
         _ = (a.acc * 2).sum().item()   # unrelated eager work between replays
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("layout", ["tiled", "split"])
-def test_accumulate_all_matches_one_call_per_micro_batch(layout):
+def test_accumulate_all_matches_one_call_per_micro_batch(layout, fused):
     """accumulate_all over a step's staged micro-batch gradients (19 of them:
     more than one pass of 16, and after one accumulate()) against accumulate()
     per micro-batch with the norm formed by step(): accumulator equal to the
     oracle's left fold, and accumulator, norm, master, moments and bf16
-    parameter bit-identical between the two over three clipped steps."""
-    print(f"ShardOptimizer accumulate_all layout={layout}", flush=True)
+    parameter bit-identical between the two over three clipped steps.  With
+    fused=True the one pass also forms the norm: the accumulator is still
+    bit-identical and the norm within the fused norms' tolerance of the
+    oracle's norm of the same accumulator (its last bits, and so the clipped
+    step's, may differ from the separate norm pass's)."""
+    print(f"ShardOptimizer accumulate_all layout={layout} fused={fused}", flush=True)
     n, M = 2 * zs.STATE_TILE + 777, 19
     rng = np.random.default_rng(41)
     p0 = from_np(rng.uniform(-0.1, 0.1, n).astype(np.float32))
@@ -184,7 +189,7 @@ def test_accumulate_all_matches_one_call_per_micro_batch(layout):
         mbs = [oracle.bf16_rne((rng.standard_normal(n) * 0.05 * (k + t)).astype(np.float32)) for k in range(M)]
         gpu = [from_np(g, bf16=True) for g in mbs]
         a.accumulate(gpu[0])
-        a.accumulate_all(gpu[1:])
+        a.accumulate_all(gpu[1:], last=fused)
         for g in gpu:
             b.accumulate(g)
         acc_ref = np.empty(n, np.float32)
@@ -195,9 +200,14 @@ def test_accumulate_all_matches_one_call_per_micro_batch(layout):
         a.step(extra_norm_sq=0.1)
         b.step(extra_norm_sq=0.1)
         torch.cuda.synchronize()
-        assert a.norm_sq.item() == b.norm_sq.item()
         assert oracle.clip_coef(a.norm_sq.item(), 0.1, 0.5) < 1.0   # every step clips
-        for name in ("acc", "master", "exp_avg", "exp_avg_sq", "param_bf16"):
+        assert bits_equal(to_np(a.acc), to_np(b.acc))
+        if fused:
+            S = oracle.grad_norm_sq(acc_ref, 1 / M)
+            assert abs(a.norm_sq.item() - S) <= NORM_TOL * S
+            continue
+        assert a.norm_sq.item() == b.norm_sq.item()
+        for name in ("master", "exp_avg", "exp_avg_sq", "param_bf16"):
             assert bits_equal(to_np(getattr(a, name)), to_np(getattr(b, name))), (t, name)
     with pytest.raises(ValueError):
         a.accumulate_all([])
