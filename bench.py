@@ -47,15 +47,15 @@ HBM_PEAK_GBPS = 8000.0   # MI355X published HBM3E bandwidth
 PMC_SOURCES = ("csrc/adamw.hip", "csrc/zs_common.h")
 PMC_TRAFFIC = {
     "adamw_step_tiled": [
-        {"sha256_16": "ba1b28dbf08f72dd", "shard_elems": 842301952,
+        {"sha256_16": "7122c719bce82d1d", "shard_elems": 842301952,
          "fetch_kib": 6580552.4, "fetch_scale": 2.0, "write_kib": 11515857.7, "write_scale": 1.0},
-        {"sha256_16": "ba1b28dbf08f72dd", "shard_elems": 1093750000,
+        {"sha256_16": "7122c719bce82d1d", "shard_elems": 1093750000,
          "fetch_kib": 8545002.6, "fetch_scale": 2.0, "write_kib": 14953618.9, "write_scale": 1.0},
     ],
     "adamw_step": [
-        {"sha256_16": "ba1b28dbf08f72dd", "shard_elems": 842301952,
+        {"sha256_16": "7122c719bce82d1d", "shard_elems": 842301952,
          "fetch_kib": 6580517.5, "fetch_scale": 2.0, "write_kib": 11515853.2, "write_scale": 1.0},
-        {"sha256_16": "ba1b28dbf08f72dd", "shard_elems": 1093750000,
+        {"sha256_16": "7122c719bce82d1d", "shard_elems": 1093750000,
          "fetch_kib": 8544955.5, "fetch_scale": 2.0, "write_kib": 14953618.7, "write_scale": 1.0},
     ],
 }
