@@ -321,10 +321,11 @@ float orc_clip_coef(double norm_sq_local, double extra_norm_sq, double max_norm)
  * ([ZeRO page] "组合策略" recipe: a non-finite grad norm skips the update).
  *
  * Per element, in this order, one rounding per operation, no fusion
- * ([ZeRO page] §ZeRO-1 step: exp_avg.mul_(beta1).add_(g, alpha=1-beta1);
- * exp_avg_sq.mul_(beta2).addcmul_(g, g, value=1-beta2);
- * denom = sqrt(exp_avg_sq)/sqrt(bias_correction2) + eps;
- * update = exp_avg/denom * (-step_size); p += update):
+ * ([ZeRO page] §"ZeRO-1: 切分优化器状态", the optimizer step: first and
+ * second moments as exponential moving averages of g and g^2, the second
+ * moment's square root divided by the square root of its bias correction
+ * before eps is added, the first moment over that denominator scaled by the
+ * learning rate over the first bias correction, subtracted from p):
  *   g  = fl(fl(acc*scale) * coef)
  *   m  = fl(fl(beta1*m) + fl((1-beta1)*g))
  *   v  = fl(fl(beta2*v) + fl((1-beta2)*fl(g*g)))
@@ -425,7 +426,13 @@ int orc_adamw_step_no_master(const orc_adamw_hp* hp, uint16_t* param_bf16, float
  * weight decay, and a decoupled decay has no update-vector form that adds
  * to the same bits, so weight_decay must be 0 (else -1).  Adding the update
  * to p gives fl(p - u): the master path of orc_adamw_step with decay 1.
- * Returns 0 (written), 1 (skipped: non-finite norm) or -1.
+ * A non-finite S skips the step ([ZeRO page] "组合策略" recipe: a
+ * non-finite grad norm skips the update): the moments are left untouched and
+ * every update[i] is written as -0.0, the identity of IEEE addition
+ * (x + -0.0 == x for every x, -0.0 and NaN included), so the apply that
+ * follows the all-gather leaves every parameter as it was instead of adding
+ * whatever the update buffer held before.
+ * Returns 0 (written), 1 (skipped: non-finite norm, update = -0.0) or -1.
  */
 int orc_adam_update(const orc_adamw_hp* hp, float* exp_avg, float* exp_avg_sq, const float* grad,
                     float* update, int64_t n, const double* norm_sq)
@@ -435,7 +442,10 @@ int orc_adam_update(const orc_adamw_hp* hp, float* exp_avg, float* exp_avg_sq, c
     float coef = 1.0f;
     if (norm_sq) {
         double S = *norm_sq + hp->extra_norm_sq;
-        if (!isfinite(S)) return 1;
+        if (!isfinite(S)) {
+            for (int64_t i = 0; i < n; ++i) update[i] = -0.0f;
+            return 1;
+        }
         coef = orc_clip_coef(*norm_sq, hp->extra_norm_sq, hp->max_norm);
     }
     const float neg_step_size = -s.step_size;

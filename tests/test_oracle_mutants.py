@@ -84,6 +84,10 @@ MUTANTS = [
      "        exp_avg_sq[i] = v;\n        update[i]"),
     ("zero-1 update: bias correction of v dropped", "float denom = sqrtf(v) / s.bias_correction2_sqrt + s.eps;",
      "float denom = sqrtf(v) + s.eps;"),
+    ("zero-1 update: a skipped step leaves the stale update",
+     "for (int64_t i = 0; i < n; ++i) update[i] = -0.0f;", ""),
+    ("zero-1 update: a skipped step writes +0.0 (turns -0.0 parameters into +0.0)",
+     "update[i] = -0.0f;", "update[i] = 0.0f;"),
     ("apply: offset ignored", "float u = update[offset + j];", "float u = update[j];"),
     ("apply: bf16 truncated instead of rounded", "p[j] = orc_bf16_rne(orc_bf16_widen(p[j]) + u);",
      "p[j] = (uint16_t)(f32_bits(orc_bf16_widen(p[j]) + u) >> 16);"),
@@ -133,9 +137,10 @@ def pin_suite():
         lambda: pins.test_no_master_one_step_equals_master_recast(orc),
         lambda: pins.test_no_master_stalls_below_half_an_ulp(orc),
         lambda: pins.test_adam_update_added_to_param_equals_master_step(orc),
-        lambda: pins.test_adam_update_vs_pages_zero1_float64(orc),
+        lambda: pins.test_adam_update_vs_adam_equations_float64(orc),
         lambda: pins.test_adam_update_step1_closed_form(orc),
         lambda: pins.test_adam_update_rejects_decay_and_skips_nonfinite(orc),
+        lambda: pins.test_skipped_adam_update_applies_as_identity(orc),
         lambda: pins.test_flat_apply_update_zero_update_is_identity(orc),
         lambda: pins.test_zero1_flow_equals_one_buffer_step(orc),
         lambda: pins.test_state_tile_element_positions_brute_force(orc),

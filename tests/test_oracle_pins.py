@@ -636,27 +636,38 @@ def test_adam_update_added_to_param_equals_master_step(orc):
         assert np.array_equal(m1, m2) and np.array_equal(v1, v2)
 
 
-def test_adam_update_vs_pages_zero1_float64(orc):
-    """The ZeRO page's ZeRO-1 step (mul_/add_/addcmul_, sqrt / sqrt(bc2) + eps,
-    exp_avg / denom * -step_size) run with torch float64 ops on the CPU; the
-    fp32 update and moments agree to a few fp32 ulps per step."""
+def _adam_update_float64(g, m, v, t, lr, b1, b2, eps):
+    """Adam written from its equations in float64 (ZeRO page, §"ZeRO-1:
+    切分优化器状态": exponential moving averages of g and g^2, both bias
+    corrected, eps added to the corrected second moment's square root, the
+    update is minus the learning rate times the corrected first moment over
+    that denominator).  Returns the update and the new moments."""
+    m = b1 * m + (1.0 - b1) * g
+    v = b2 * v + (1.0 - b2) * g * g
+    m_hat = m / (1.0 - b1 ** t)
+    v_hat = v / (1.0 - b2 ** t)
+    return -lr * m_hat / (np.sqrt(v_hat) + eps), m, v
+
+
+def test_adam_update_vs_adam_equations_float64(orc):
+    """The oracle's fp32 update and moments against Adam's equations
+    evaluated in numpy float64 (the bias-corrected form m_hat / (sqrt(v_hat)
+    + eps), not the oracle's op order): they agree to a few fp32 ulps per
+    step."""
     rng = np.random.default_rng(43)
     n = 4096
     lr, b1, b2, eps = 1e-4, 0.9, 0.999, 1e-8
     m, v, upd = np.zeros(n, np.float32), np.zeros(n, np.float32), np.empty(n, np.float32)
-    em, ev = torch.zeros(n, dtype=torch.float64), torch.zeros(n, dtype=torch.float64)
+    em, ev = np.zeros(n), np.zeros(n)
     for t in range(1, 9):
         acc = (rng.standard_normal(n) * 1e-3).astype(np.float32)
         assert oracle.adam_update(hp(lr=lr, beta1=b1, beta2=b2, eps=eps, scale=1 / 8, step=t), m, v, acc, upd) == 0
-        g = torch.from_numpy(acc).double() / 8
-        kappa_m = (b1 * em.abs() + (1 - b1) * g.abs()).numpy()   # guards a cancellation in m
-        em.mul_(b1).add_(g, alpha=1 - b1)
-        ev.mul_(b2).addcmul_(g, g, value=1 - b2)
-        denom = (ev.sqrt() / math.sqrt(1 - b2 ** t)).add_(eps)
-        ref = (em / denom * (-lr / (1 - b1 ** t))).numpy()
+        g = acc.astype(np.float64) / 8
+        kappa_m = b1 * np.abs(em) + (1 - b1) * np.abs(g)   # guards a cancellation in m
+        ref, em, ev = _adam_update_float64(g, em, ev, t, lr, b1, b2, eps)
         assert np.max(np.abs(upd - ref)) <= 4e-7 * t * lr, t
-        assert np.max(np.abs(m - em.numpy()) / kappa_m) <= 1e-6 * t
-        assert np.max(np.abs(v - ev.numpy()) / ev.numpy()) <= 1e-6 * t
+        assert np.max(np.abs(m - em) / kappa_m) <= 1e-6 * t
+        assert np.max(np.abs(v - ev) / ev) <= 1e-6 * t
 
 
 def test_adam_update_step1_closed_form(orc):
@@ -680,7 +691,38 @@ def test_adam_update_rejects_decay_and_skips_nonfinite(orc):
         oracle.adam_update(hp(wd=0.1), m, v, g, u)
     u[:] = 7.0
     assert oracle.adam_update(hp(max_norm=1.0), m, v, g + 1, u, norm_sq=float("nan")) == 1
-    assert np.all(u == 7.0) and np.all(m == 0)
+    # skipped: the moments stay, the update is -0.0 everywhere (what the
+    # apply after the all-gather must add to change nothing)
+    assert np.all(m == 0) and np.all(v == 0)
+    assert np.all(u.view(np.uint32) == 0x80000000)
+    assert oracle.adam_update(hp(), m, v, g + 1, u, norm_sq=float("inf")) == 1
+
+
+def test_skipped_adam_update_applies_as_identity(orc):
+    """A skipped ZeRO-1 step (non-finite norm) followed by the apply leaves
+    every parameter bit for bit as it was: -0.0 is the identity of IEEE
+    addition (numpy float32 addition agrees), so +-0.0, subnormals, +-inf,
+    NaN and ordinary fp32 values all survive; bf16 parameters (finite, +-0,
+    +-inf) too."""
+    specials = np.array([0.0, -0.0, 1e-45, -1e-45, 1.17549435e-38, np.inf, -np.inf, np.nan, 1.0, -3.5e-7,
+                         3.4028235e38], np.float32)
+    rng = np.random.default_rng(7)
+    p32 = np.concatenate([specials, rng.uniform(-1, 1, 1000).astype(np.float32)])
+    n = p32.size
+    m, v = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    upd = np.full(n, 5.0, np.float32)   # a stale update from an earlier step
+    g = rng.standard_normal(n).astype(np.float32)
+    assert oracle.adam_update(hp(max_norm=1.0), m, v, g, upd, norm_sq=float("nan")) == 1
+    numpy_sum = p32 + upd
+    assert np.array_equal(numpy_sum.view(np.uint32), p32.view(np.uint32))
+    before = p32.copy()
+    oracle.flat_apply_update(upd, [p32], F32)
+    assert np.array_equal(p32.view(np.uint32), before.view(np.uint32))
+    b16 = np.concatenate([np.array([0x0000, 0x8000, 0x7F80, 0xFF80, 0x0001, 0x3F80], np.uint16),
+                          oracle.bf16_rne(rng.uniform(-1, 1, n - 6).astype(np.float32))])
+    b_before = b16.copy()
+    oracle.flat_apply_update(upd, [b16], BF16)
+    assert np.array_equal(b16, b_before)
 
 
 @pytest.mark.parametrize("seed", range(3))
