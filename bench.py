@@ -36,46 +36,16 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0   # MI355X published HBM3E bandwidth
 
-# HBM bytes per AdamW launch (adamw_step_tiled, the step's kernel, and
-# adamw_step, the same step on split buffers), per shard size (the Llama-7B
-# shard and the 70B ZeRO-3 shard), from two rocprofv3 --pmc runs of this script for that
-# workload (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what
-# the same counter reads for the 4 GiB device copy this script also runs
-# (FETCH_SIZE reads about 2,097,194 KiB for it: x2.0; WRITE_SIZE reads
-# 4,194,304 KiB: x1.0).  Valid only for the kernel source it was taken on: the
-# hash covers the kernel file and its header.
-PMC_SOURCES = ("csrc/adamw.hip", "csrc/zs_common.h")
-PMC_TRAFFIC = {
-    "adamw_step_tiled": [
-        {"sha256_16": "7122c719bce82d1d", "shard_elems": 842301952,
-         "fetch_kib": 6580552.4, "fetch_scale": 2.0, "write_kib": 11515857.7, "write_scale": 1.0},
-        {"sha256_16": "7122c719bce82d1d", "shard_elems": 1093750000,
-         "fetch_kib": 8545002.6, "fetch_scale": 2.0, "write_kib": 14953618.9, "write_scale": 1.0},
-    ],
-    "adamw_step": [
-        {"sha256_16": "7122c719bce82d1d", "shard_elems": 842301952,
-         "fetch_kib": 6580517.5, "fetch_scale": 2.0, "write_kib": 11515853.2, "write_scale": 1.0},
-        {"sha256_16": "7122c719bce82d1d", "shard_elems": 1093750000,
-         "fetch_kib": 8544955.5, "fetch_scale": 2.0, "write_kib": 14953618.7, "write_scale": 1.0},
-    ],
-}
-
-
-def pmc_traffic(kernel: str, n: int):
-    """Measured HBM bytes per launch, or None if there is no record for this
-    shard size or the kernel changed since it was taken."""
-    import hashlib
-    recs = [r for r in PMC_TRAFFIC.get(kernel, []) if r["shard_elems"] == n]
-    if not recs:
-        return None
-    rec = recs[0]
-    h = hashlib.sha256()
-    for rel in PMC_SOURCES:
-        with open(os.path.join(ROOT, "fsdp_sharded_optimizer_amd", rel), "rb") as f:
-            h.update(f.read())
-    if h.hexdigest()[:16] != rec["sha256_16"]:
-        return None
-    return rec["fetch_kib"] * 1024 * rec["fetch_scale"] + rec["write_kib"] * 1024 * rec["write_scale"]
+# The kernels whose HBM traffic the JSON line reports, as rocprofv3 names
+# them (bench_pmc.py keys each record to the gfx950 code object that
+# defines the kernel; a rebuilt kernel reports null until the counters are
+# taken again).
+K_ADAMW_TILED = "zs::(anonymous namespace)::adamw_kernel<4, 1, 64, false, true, true>"
+K_ADAMW_SPLIT = "zs::(anonymous namespace)::adamw_kernel<4, 1, 64, false, false, true>"
+K_ACCUM_FIRST = "zs::(anonymous namespace)::accum_kernel<1, 64, true, true, true, false>"
+K_ACCUM_ADD = "zs::(anonymous namespace)::accum_kernel<1, 64, true, true, false, false>"
+K_ACCUM_NORM_ADD = "zs::(anonymous namespace)::accum_kernel<1, 64, true, true, false, true>"
+K_ACCUM_NORM_FIRST = "zs::(anonymous namespace)::accum_kernel<4, 64, true, true, true, true>"
 
 
 def log(*a):
@@ -158,7 +128,9 @@ def timing_events() -> str:
 
 
 def step_bytes_per_elem(w) -> dict:
-    """Algorithmic HBM bytes per shard element of each kernel of one step."""
+    """Algorithmic HBM bytes per shard element of each kernel of one step
+    (the fused norm's binary64 partials, 8 B per 256 elements, come on top
+    of the last micro-batch's bytes: 0.03 B per element)."""
     g = 2 if w.grad_dtype == "bf16" else 4
     accum_first = g + 4
     accum_next = g + 8
@@ -168,6 +140,14 @@ def step_bytes_per_elem(w) -> dict:
     last = accum_first if w.micro_batches == 1 else accum_next
     return {"grad_accum_first": accum_first, "grad_accum_next": accum_next,
             "grad_accum_norm_sq_last": last, "adamw_step": adamw, "step": accum + adamw}
+
+
+def fused_norm_partials(w, n: int) -> int:
+    """Binary64 partials grad_accum_norm_sq writes for the last micro-batch:
+    one per 256 elements, or per 1024 when it overwrites from a bf16
+    gradient (a single micro-batch)."""
+    per = 1024 if (w.micro_batches == 1 and w.grad_dtype == "bf16") else 256
+    return (n + per - 1) // per
 
 
 def step_kernel_rates(bpe: dict, n: int, r: dict) -> dict:
@@ -182,7 +162,9 @@ def step_kernel_rates(bpe: dict, n: int, r: dict) -> dict:
     }
     out = {}
     for name, (b, ms) in parts.items():
-        gbps = b * n / (ms * 1e-3) / 1e9 if (ms > 0 and b > 0) else None
+        if b == 0:
+            continue
+        gbps = b * n / (ms * 1e-3) / 1e9 if ms > 0 else None
         out[name] = {"bytes_per_elem": b, "ms": ms, "gbps": gbps,
                      "frac": gbps / HBM_PEAK_GBPS if gbps is not None else None}
     return out
@@ -205,212 +187,261 @@ def shard_len(w) -> int:
     return end - start
 
 
+def traffic_of(label: str, n: int, digests: dict):
+    """Calibrated PMC bytes per launch from bench_pmc.json, or None when no
+    record was taken on the code object that is running."""
+    import bench_pmc
+    return bench_pmc.traffic(label, n, digests)
+
+
+def rate(nbytes: float, ms: float) -> dict:
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": ms, "gbps": gbps, "frac": gbps / HBM_PEAK_GBPS}
+
+
 # ---------------------------------------------------------------------------
-# GPU leg
+# GPU legs
 # ---------------------------------------------------------------------------
+
+class StepRig:
+    """One rank's resident buffers for a workload: the tiled optimizer
+    state (master values in, moments zero), the fp32 accumulator, the bf16
+    parameter, the step's micro-batch gradients (seeded draws), the norm
+    and its workspace."""
+
+    def __init__(self, w, dev):
+        import torch
+        import workloads
+        import fsdp_sharded_optimizer_amd as zs
+        self.w, self.dev = w, dev
+        self.n = n = shard_len(w)
+        log(f"[bench] workload={w.name} shard_elems={n} micro_batches={w.micro_batches}")
+        master = workloads.master_init(w, n, dev)
+        self.param = master.to(torch.bfloat16) if w.bf16_param else None
+        self.state = torch.empty(zs.state_tiled_numel(n), dtype=torch.float32, device=dev)
+        zs.state_tile(master, None, None, self.state)
+        del master
+        self.acc = torch.empty(n, dtype=torch.float32, device=dev)
+        self.grads = [workloads.grad_draw(w, n, 1, mb, dev) for mb in range(w.micro_batches)]
+        self.norm = torch.zeros(1, dtype=torch.float64, device=dev)
+        self.ws = torch.empty(max(zs.grad_accum_norm_sq_workspace_bytes(n), zs.grad_norm_sq_workspace_bytes(n),
+                                  zs.grad_reduce_chunks_norm_sq_workspace_bytes(n), 8), dtype=torch.uint8, device=dev)
+        self.t = 0
+
+    def hp(self, t: int):
+        import workloads
+        import fsdp_sharded_optimizer_amd as zs
+        w = self.w
+        return zs.AdamWConfig(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
+                              grad_scale=w.grad_scale, max_norm=w.max_norm,
+                              extra_norm_sq=workloads.other_ranks_norm_sq(w, 1, self.n), step=t)
+
+    def step(self, t: int, ev=None):
+        """The pages' schedule: one accumulation per micro-batch as its
+        gradient arrives, the last forming the norm, then AdamW (tiled
+        state, bf16 re-cast, clip when the workload clips).  ev: four events
+        recorded around the parts."""
+        import fsdp_sharded_optimizer_amd as zs
+        last = len(self.grads) - 1
+        if ev:
+            ev[0].record()
+        for mb, g in enumerate(self.grads[:last]):
+            zs.grad_accum(self.acc, g, overwrite=(mb == 0))
+        if ev:
+            ev[1].record()
+        zs.grad_accum_norm_sq(self.acc, self.grads[last], last == 0, self.w.grad_scale, self.norm, self.ws)
+        if ev:
+            ev[2].record()
+        zs.adamw_step_tiled(self.hp(t), self.state, self.acc, self.param, norm_sq=self.norm)
+        if ev:
+            ev[3].record()
+
+    def staged_step(self, t: int, k: int):
+        """The same step with the micro-batch gradients staged k at a time in
+        device memory: each group of k is summed in one pass
+        (grad_reduce_chunks, the same left fold bit for bit), the last group
+        forming the norm (grad_reduce_chunks_norm_sq); k = 1 is step()."""
+        import fsdp_sharded_optimizer_amd as zs
+        if k == 1:
+            return self.step(t)
+        groups = [self.grads[i:i + k] for i in range(0, len(self.grads), k)]
+        for j, grp in enumerate(groups[:-1]):
+            zs.grad_reduce_chunks(self.acc, grp, j == 0)
+        zs.grad_reduce_chunks_norm_sq(self.acc, groups[-1], len(groups) == 1, self.w.grad_scale, self.norm,
+                                      self.ws)
+        zs.adamw_step_tiled(self.hp(t), self.state, self.acc, self.param, norm_sq=self.norm)
+
+    def time_steps(self, steps: int, warmup: int) -> dict:
+        """W untimed steps, then K steps bracketed by synchronisations (wall
+        clock), each with HIP events around its parts on the launch stream."""
+        import math
+        import torch
+        ev = DeviceEvent
+        for _ in range(warmup):
+            self.t += 1
+            self.step(self.t)
+        torch.cuda.synchronize()
+        timing = []
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.t += 1
+            e = [ev() for _ in range(4)]
+            self.step(self.t, e)
+            timing.append(e)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        assert math.isfinite(self.norm.item()), "non-finite gradient norm in the bench"
+        return {"wall_s": wall, "ms_per_step": wall * 1e3 / steps,
+                "accum_ms": sum(e[0].elapsed_time(e[1]) for e in timing) / steps,
+                "last_ms": sum(e[1].elapsed_time(e[2]) for e in timing) / steps,
+                "adamw_ms": sum(e[2].elapsed_time(e[3]) for e in timing) / steps}
+
+
+def timed(fn, reps: int) -> float:
+    """Average ms of fn() over reps calls after one untimed call, HIP events
+    on the current stream."""
+    import torch
+    fn()
+    e0, e1 = DeviceEvent(), DeviceEvent()
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
 
 def run_gpu(w, steps: int, warmup: int):
     import torch
-    import workloads
     import fsdp_sharded_optimizer_amd as zs
+    from fsdp_sharded_optimizer_amd import ledger
 
-    n = shard_len(w)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    log(f"[bench] workload={w.name} shard_elems={n} micro_batches={w.micro_batches}")
-    master = workloads.master_init(w, n, dev)
-    param = master.to(torch.bfloat16) if w.bf16_param else None
-    # the step's optimizer state, tiled: master values in, moments zero
-    state = torch.empty(zs.state_tiled_numel(n), dtype=torch.float32, device=dev)
-    zs.state_tile(master, None, None, state)
-    # split buffers: the adamw_step comparison and the no-master variant
-    exp_avg = torch.zeros(n, dtype=torch.float32, device=dev)
-    exp_avg_sq = torch.zeros(n, dtype=torch.float32, device=dev)
-    acc = torch.empty(n, dtype=torch.float32, device=dev)
-    grads = [workloads.grad_draw(w, n, 1, mb, dev) for mb in range(w.micro_batches)]
-    norm = torch.zeros(1, dtype=torch.float64, device=dev)
-    ws = torch.empty(max(zs.grad_accum_norm_sq_workspace_bytes(n), zs.grad_norm_sq_workspace_bytes(n),
-                         zs.grad_reduce_chunks_norm_sq_workspace_bytes(n), 8), dtype=torch.uint8, device=dev)
+    rig = StepRig(w, dev)
+    n = rig.n
     torch.cuda.synchronize()
     log(f"[bench] inputs resident: {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
-
+    r = rig.time_steps(steps, warmup)
+    r["n"] = n
+    r["chunks"] = len(rig.grads)
     ev = DeviceEvent
-    timing = []   # per step: (start, last micro-batch start, adamw start, adamw end)
-    last = len(grads) - 1
-
-    def step_hp(t: int):
-        return zs.AdamWConfig(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
-                              weight_decay=w.weight_decay, grad_scale=w.grad_scale,
-                              max_norm=w.max_norm, extra_norm_sq=workloads.other_ranks_norm_sq(w, 1, n),
-                              step=t)
-
-    def one_step(t: int, record: bool):
-        e = [ev() for _ in range(4)] if record else None
-        if record:
-            e[0].record()
-        for mb, g in enumerate(grads[:last]):
-            zs.grad_accum(acc, g, overwrite=(mb == 0))
-        if record:
-            e[1].record()
-        zs.grad_accum_norm_sq(acc, grads[last], last == 0, w.grad_scale, norm, ws)
-        if record:
-            e[2].record()
-        zs.adamw_step_tiled(step_hp(t), state, acc, param, norm_sq=norm)
-        if record:
-            e[3].record()
-            timing.append(e)
-
-    t = 0
-    for _ in range(warmup):
-        t += 1
-        one_step(t, record=False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        t += 1
-        one_step(t, record=True)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    acc_ms = sum(e[0].elapsed_time(e[1]) for e in timing) / steps
-    last_ms = sum(e[1].elapsed_time(e[2]) for e in timing) / steps
-    adamw_ms = sum(e[2].elapsed_time(e[3]) for e in timing) / steps
-    assert math.isfinite(norm.item()), "non-finite gradient norm in the bench"
 
     # outside the step: the same step captured once in a HIP graph and
     # replayed (the library allocates, clears and synchronises nothing, so
     # the step captures as is; launch overhead matters for small shards)
-    graph_ms = None
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        one_step(t + 1, record=False)
+        rig.step(rig.t + 1)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        one_step(t + 1, record=False)
-    graph.replay()
-    g0, g1 = ev(), ev()
-    g0.record()
-    for _ in range(steps):
-        graph.replay()
-    g1.record()
-    torch.cuda.synchronize()
-    graph_ms = g0.elapsed_time(g1) / steps
+        rig.step(rig.t + 1)
+    r["graph_ms"] = timed(graph.replay, steps)
     del graph
 
     # outside the step: the same AdamW step on three separate state buffers
     # (adamw_step), loaded with the tiled state as the timed steps left it so
     # both layouts stream the same values
-    zs.state_untile(state, master, exp_avg, exp_avg_sq)
+    master = torch.empty(n, dtype=torch.float32, device=dev)
+    exp_avg = torch.empty(n, dtype=torch.float32, device=dev)
+    exp_avg_sq = torch.empty(n, dtype=torch.float32, device=dev)
+    zs.state_untile(rig.state, master, exp_avg, exp_avg_sq)
     split_ms = []
     for k in range(steps):
         e0, e1 = ev(), ev()
         e0.record()
-        zs.adamw_step(step_hp(t + 1 + k), master, exp_avg, exp_avg_sq, acc, param, norm_sq=norm)
+        zs.adamw_step(rig.hp(rig.t + 1 + k), master, exp_avg, exp_avg_sq, rig.acc, rig.param, norm_sq=rig.norm)
         e1.record()
         split_ms.append((e0, e1))
     torch.cuda.synchronize()
-    split_ms = sum(a.elapsed_time(b) for a, b in split_ms) / steps
+    r["split_ms"] = sum(a.elapsed_time(b) for a, b in split_ms) / steps
 
-    # outside the step: the reduce-scatter's arithmetic on this rank's shard,
-    # the same buffers read as N rank chunks, in one pass
-    reduce_ms = None
-    if len(grads) > 1:
-        r0, r1 = ev(), ev()
-        zs.grad_reduce_chunks(acc, grads, True)
-        r0.record()
-        for _ in range(3):
-            zs.grad_reduce_chunks(acc, grads, True)
-        r1.record()
-        torch.cuda.synchronize()
-        reduce_ms = r0.elapsed_time(r1) / 3
+    # outside the step: the one-pass sums of the step's micro-batch
+    # gradients alone, without and with the norm (the reduce-scatter's
+    # arithmetic on this rank's shard, the same buffers read as N chunks)
+    r["reduce_ms"] = r["reduce_norm_ms"] = None
+    if len(rig.grads) > 1:
+        r["reduce_ms"] = timed(lambda: zs.grad_reduce_chunks(rig.acc, rig.grads, True), 5)
+        r["reduce_norm_ms"] = timed(lambda: zs.grad_reduce_chunks_norm_sq(rig.acc, rig.grads, True, w.grad_scale,
+                                                                          rig.norm, rig.ws), 5)
 
-    # outside the step: the same step with the step's micro-batch gradients
-    # all kept in device memory (ShardOptimizer.accumulate_all): one pass sums
-    # them (bit-identical accumulator) and forms the norm, then the same
-    # AdamW on the tiled state
-    staged_ms = None
-    if len(grads) > 1:
-        def staged(tt: int):
-            zs.grad_reduce_chunks_norm_sq(acc, grads, True, w.grad_scale, norm, ws)
-            zs.adamw_step_tiled(step_hp(tt), state, acc, param, norm_sq=norm)
-
-        staged(t + 1)
-        s0, s1 = ev(), ev()
-        s0.record()
-        for k in range(steps):
-            staged(t + 2 + k)
-        s1.record()
-        torch.cuda.synchronize()
-        staged_ms = s0.elapsed_time(s1) / steps
-        t += 1 + steps
+    # outside the step: the step with its micro-batch gradients staged k at a
+    # time in device memory (ShardOptimizer.accumulate_all over groups of k):
+    # fewer passes over the fp32 accumulator for (k - 1) more bf16 gradient
+    # buffers resident
+    curve = []
+    if len(rig.grads) > 1:
+        g = 2 if w.grad_dtype == "bf16" else 4
+        M = len(rig.grads)
+        for k in (1, 2, 4, 8):
+            if k > M or M % k:
+                continue
+            G = M // k
+            bpe = (g * k + 4) + (G - 1) * (g * k + 8) + step_bytes_per_elem(w)["adamw_step"]
+            t0 = rig.t
+            ms = timed(lambda: rig.staged_step(t0 + 1, k), steps)
+            extra = ledger.library_shard_bytes(n, grad_buffers=k) - ledger.library_shard_bytes(n, grad_buffers=1)
+            curve.append({"k": k, "passes_over_acc": G, "bytes_per_elem": bpe, "elements_per_s": n / (ms * 1e-3),
+                          "extra_hbm_bytes": extra, **rate(bpe * n, ms)})
+            rig.t += steps + 1
+    r["staging_curve"] = curve
 
     # outside the step: the standalone squared norm over the accumulated
     # gradient (4 B/element), as when the gradient arrives from a
     # reduce-scatter instead of this rank's own accumulation
-    n0, n1 = ev(), ev()
-    zs.grad_norm_sq(acc, w.grad_scale, norm, ws)
-    n0.record()
-    for _ in range(5):
-        zs.grad_norm_sq(acc, w.grad_scale, norm, ws)
-    n1.record()
-    torch.cuda.synchronize()
-    norm_ms = n0.elapsed_time(n1) / 5
+    r["norm_ms"] = timed(lambda: zs.grad_norm_sq(rig.acc, w.grad_scale, rig.norm, rig.ws), 5)
 
     # outside the step: the variant with no fp32 master (24 B/element), on the
-    # same buffers (state after the timed steps), then on tiled moments
-    no_master_ms = no_master_tiled_ms = None
-    if param is not None:
-        def time_no_master(fn):
-            hp = zs.AdamWConfig(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
-                                grad_scale=w.grad_scale, step=t + 1)
-            fn(hp)
-            n0, n1 = ev(), ev()
-            n0.record()
-            for k in range(3):
-                hp.step = t + 2 + k
-                fn(hp)
-            n1.record()
-            torch.cuda.synchronize()
-            return n0.elapsed_time(n1) / 3
-
-        no_master_ms = time_no_master(lambda hp: zs.adamw_step_no_master(hp, param, exp_avg, exp_avg_sq, acc))
+    # split buffers, then on tiled moments
+    r["no_master_ms"] = r["no_master_tiled_ms"] = None
+    if rig.param is not None:
+        def no_master_hp():
+            rig.t += 1
+            return zs.AdamWConfig(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
+                                  grad_scale=w.grad_scale, step=rig.t)
+        r["no_master_ms"] = timed(lambda: zs.adamw_step_no_master(no_master_hp(), rig.param, exp_avg, exp_avg_sq,
+                                                                  rig.acc), 3)
         moments = torch.empty(zs.moments_tiled_numel(n), dtype=torch.float32, device=dev)
         zs.moments_tile(exp_avg, exp_avg_sq, moments)
-        no_master_tiled_ms = time_no_master(lambda hp: zs.adamw_step_no_master_tiled(hp, param, moments, acc))
+        r["no_master_tiled_ms"] = timed(lambda: zs.adamw_step_no_master_tiled(no_master_hp(), rig.param, moments,
+                                                                              rig.acc), 3)
         del moments
 
     # achievable-bandwidth reference for the AdamW step's own traffic: the
     # same bytes per element and accesses, one addition per stream in place
     # of the update, at several residency caps (run last on these buffers:
     # it changes them)
-    ceiling = {lds: _time_adamw_traffic(state, None, None, acc, param, n, lds, tiled=True)
-               for lds in CEILING_LDS}
-    ceiling_split = {lds: _time_adamw_traffic(master, exp_avg, exp_avg_sq, acc, param, n, lds)
-                     for lds in CEILING_LDS}
+    r["ceiling_ms"] = {lds: _time_adamw_traffic(rig.state, None, None, rig.acc, rig.param, n, lds, tiled=True)
+                       for lds in CEILING_LDS}
+    r["ceiling_split_ms"] = {lds: _time_adamw_traffic(master, exp_avg, exp_avg_sq, rig.acc, rig.param, n, lds)
+                             for lds in CEILING_LDS}
+    del rig, master, exp_avg, exp_avg_sq
+    torch.cuda.empty_cache()
 
     # achievable-bandwidth reference: a plain device copy of 4 GiB (also the
-    # calibration kernel for the HBM byte counters)
+    # calibration kernel for the HBM byte counters, which find it as the
+    # runtime copy kernel's largest dispatch)
     src = torch.empty(1 << 30, dtype=torch.float32, device=dev)
     src.fill_(1.0)
     dst = torch.empty_like(src)
-    dst.copy_(src)
-    c0, c1 = ev(), ev()
-    c0.record()
-    for _ in range(5):
-        dst.copy_(src)
-    c1.record()
-    torch.cuda.synchronize()
-    copy_ms = c0.elapsed_time(c1) / 5
-    copy_gbps = 2 * src.numel() * 4 / (copy_ms * 1e-3) / 1e9
+    copy_ms = timed(lambda: dst.copy_(src), 5)
+    r["copy_gbps"] = 2 * src.numel() * 4 / (copy_ms * 1e-3) / 1e9
     del src, dst
-    return {"n": n, "wall_s": wall, "accum_ms": acc_ms, "last_ms": last_ms, "adamw_ms": adamw_ms, "graph_ms": graph_ms,
-            "split_ms": split_ms, "reduce_ms": reduce_ms, "staged_ms": staged_ms, "chunks": len(grads),
-            "no_master_ms": no_master_ms,
-            "no_master_tiled_ms": no_master_tiled_ms,
-            "copy_gbps": copy_gbps, "ceiling_ms": ceiling, "ceiling_split_ms": ceiling_split, "norm_ms": norm_ms}
+    torch.cuda.empty_cache()
+    return r
+
+
+def run_step_leg(rig: StepRig, steps: int, warmup: int) -> dict:
+    """The timed step alone on another shard (the 70B ZeRO-3 shard): the
+    same kernels, the same launch configuration, in the same process."""
+    import torch
+    torch.cuda.synchronize()
+    r = rig.time_steps(steps, warmup)
+    r["n"] = rig.n
+    return r
 
 
 CEILING_LDS = (0, 8192, 12288, 14336, 16384, 20480)   # LDS reserved per one-wave workgroup
@@ -587,23 +618,69 @@ def run_zero1_flow(w, shapes, reps: int = 3):
 # CPU baseline leg: the oracle as it stands on a bounded sample
 # ---------------------------------------------------------------------------
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _mem_available() -> int:
+    try:
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemAvailable:"):
+                    return int(line.split()[1]) * 1024
+    except OSError:
+        pass
+    return 0
+
+
+def _oracle_threads() -> tuple:
+    """Threads for the oracle: every core of the process affinity mask,
+    capped by OMP_NUM_THREADS when the environment sets it (the host's CPU
+    share); returns (threads, affinity cores)."""
+    affinity = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    threads = min(affinity, int(cap)) if cap.isdigit() and int(cap) > 0 else affinity
+    return threads, affinity
+
+
 def run_cpu_baseline(w, target_s: float = 10.0, sample: int = 1 << 25):
+    """The oracle as it stands, timed on the host cores on the same
+    workload: whole steps (every micro-batch accumulation, the norm, AdamW
+    with the bf16 re-cast) over the full shard when the host has the memory
+    for it (inputs drawn by the same seeded recipe on the GPU and copied to
+    the host), else over the first `sample` elements; as many steps as fit
+    in about target_s.  Then the tiny ZeRO-1 workload single-threaded."""
     import numpy as np
     import torch
     import oracle
     import workloads
 
-    n = sample
-    master = workloads.master_init(w, n, "cpu").numpy().copy()
+    threads, affinity = _oracle_threads()
+    oracle.set_num_threads(threads)
+    n_full = shard_len(w)
+    g_bytes = 2 if w.grad_dtype == "bf16" else 4
+    need = n_full * (16 + (2 if w.bf16_param else 0) + w.micro_batches * g_bytes)
+    full = torch.cuda.is_available() and _mem_available() > 2 * need
+    n = n_full if full else sample
+    where = "cuda" if full else "cpu"
+    master = workloads.master_init(w, n, where).cpu().numpy()
     m = np.zeros(n, np.float32)
     v = np.zeros(n, np.float32)
     bf = np.zeros(n, np.uint16) if w.bf16_param else None
     code = oracle.BF16 if w.grad_dtype == "bf16" else oracle.F32
     grads = []
     for mb in range(w.micro_batches):
-        g = workloads.grad_draw(w, n, 1, mb, "cpu")
-        grads.append(g.view(torch.int16).numpy().view(np.uint16).copy() if code == oracle.BF16
-                     else g.numpy().copy())
+        g = workloads.grad_draw(w, n, 1, mb, where).cpu()
+        grads.append(g.view(torch.int16).numpy().view(np.uint16) if code == oracle.BF16 else g.numpy())
+        del g
     acc = np.empty(n, np.float32)
     done = 0
     phase = {"accumulate": 0.0, "norm": 0.0, "adamw": 0.0}
@@ -626,6 +703,7 @@ def run_cpu_baseline(w, target_s: float = 10.0, sample: int = 1 << 25):
         el = time.perf_counter() - t0
         if el >= target_s or done >= 1000:
             break
+    del master, m, v, bf, grads, acc
     bpe = step_bytes_per_elem(w)
     accum_bytes = bpe["step"] - bpe["adamw_step"]   # every micro-batch's accumulation
     phases = {
@@ -635,23 +713,57 @@ def run_cpu_baseline(w, target_s: float = 10.0, sample: int = 1 << 25):
         "adamw": {"ms_per_step": phase["adamw"] * 1e3 / done,
                   "gbps": bpe["adamw_step"] * n * done / phase["adamw"] / 1e9},
     }
-    return {"value": n * done / el, "unit": "elements/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"{n} elements of the same workload (first {n} of a shard drawn by the same "
-                      f"recipe on the CPU), {done} whole steps ({w.micro_batches} micro-batch "
-                      f"accumulations + norm + AdamW/bf16) in {el:.1f} s",
-            "phases": phases}
+    mode = "full shard" if full else "sample"
+    out = {"value": n * done / el, "unit": "elements/s", "cores": threads, "kind": "oracle",
+           "sample": (f"{mode}: {n} elements ({'the whole' if full else 'the first of the'} {n_full}-element "
+                      f"{w.name} shard, inputs by the same seeded recipe), {done} whole steps "
+                      f"({w.micro_batches} micro-batch accumulations + norm + AdamW/bf16) in {el:.1f} s"),
+           "mode": mode, "elements": n, "steps": done, "seconds": el,
+           "threads": threads, "affinity_cores": affinity, "cpu_model": _cpu_model(),
+           "phases": phases}
+    out["single_thread_c1"] = _cpu_tiny_zero1_single_thread(target_s=2.0)
+    return out
 
 
-def _staged(r, n: int, w) -> dict:
-    """The step with its micro-batch gradients staged in device memory: the
-    one-pass sum with the norm (gradient bytes per micro-batch + 4 written)
-    and AdamW (30), timed back to back over the bench's step count."""
-    bpe = r["chunks"] * (2 if w.grad_dtype == "bf16" else 4) + 4 + 30
-    gbps = bpe * n / (r["staged_ms"] * 1e-3) / 1e9
-    return {"ms": r["staged_ms"], "elements_per_s": n / (r["staged_ms"] * 1e-3), "bytes_per_elem": bpe,
-            "gbps": gbps, "frac": gbps / HBM_PEAK_GBPS,
-            "staged_grad_bytes_per_elem": r["chunks"] * (2 if w.grad_dtype == "bf16" else 4)}
+def _cpu_tiny_zero1_single_thread(target_s: float) -> dict:
+    """_cpu_tiny_zero1 in a child process with OMP_NUM_THREADS=1 (a fresh
+    OpenMP runtime: one thread for certain).  The child runs on the CPU
+    only."""
+    import subprocess
+    env = dict(os.environ, OMP_NUM_THREADS="1", HIP_VISIBLE_DEVICES="", CUDA_VISIBLE_DEVICES="")
+    code = (f"import json, sys; sys.path.insert(0, {ROOT!r}); import bench; "
+            f"print(json.dumps(bench._cpu_tiny_zero1({target_s!r})))")
+    proc = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=300)
+    if proc.returncode != 0:
+        raise RuntimeError(f"single-thread oracle leg failed: {proc.stderr[-2000:]}")
+    return json.loads(proc.stdout.strip().splitlines()[-1])
+
+
+def _cpu_tiny_zero1(target_s: float) -> dict:
+    """The tiny ZeRO-1 workload (rank 3's 125,001-element slice, 5 Adam
+    steps of fresh fp32 gradients) through the oracle on one thread,
+    repeated for about target_s: shard elements stepped per second."""
+    import numpy as np
+    import oracle
+    import workloads
+    w = workloads.WORKLOADS["tiny_zero1"]
+    _, start, end, _ = oracle.shard_range(w.total, w.world, w.rank)
+    n = end - start
+    p0 = workloads.master_init(w, w.total).numpy()[start:end].copy()
+    grads = [workloads.grad_draw(w, w.total, t, 0).numpy()[start:end].copy() for t in range(1, w.steps + 1)]
+    runs = 0
+    t0 = time.perf_counter()
+    while True:
+        p, m, v = p0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+        for t, g in enumerate(grads, 1):
+            hp = oracle.make_hp(w.lr, w.beta1, w.beta2, w.eps, 0.0, w.grad_scale, 0.0, 0.0, t)
+            oracle.adamw_step(hp, p, m, v, g)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= target_s:
+            break
+    return {"value": n * w.steps * runs / el, "unit": "elements/s", "threads": oracle.num_threads(),
+            "workload": w.name, "shard_elems": n, "steps_per_run": w.steps, "runs": runs, "seconds": el}
 
 
 def main():
@@ -660,6 +772,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama7b_shard")
+    ap.add_argument("--second-workload", default="zero3_70b_shard",
+                    help="a second shard timed in the same process after the first ('' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--no-zero1", action="store_true", help="skip the ZeRO-1 flow timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -671,27 +785,40 @@ def main():
         sys.exit(2)
 
     import workloads
-    if args.workload not in workloads.WORKLOADS:
-        sys.exit(f"unknown workload {args.workload}; one of {sorted(workloads.WORKLOADS)}")
+    for name in (args.workload, args.second_workload):
+        if name and name not in workloads.WORKLOADS:
+            sys.exit(f"unknown workload {name}; one of {sorted(workloads.WORKLOADS)}")
     w = workloads.WORKLOADS[args.workload]
 
     import fsdp_sharded_optimizer_amd as zs
+    import bench_pmc
     zs.lib()
+    digests = bench_pmc.kernel_digests()
 
+    # both shards' buffers are allocated up front, each on fresh device
+    # memory as a rank allocates its buffers once (re-allocating after a
+    # large free measured up to 3 points lower on gfx950, differing from run
+    # to run with the physical placement)
+    import torch
+    torch.cuda.set_device(0)
+    second_rig = None
+    if args.second_workload and args.second_workload != w.name:
+        second_rig = StepRig(workloads.WORKLOADS[args.second_workload], torch.device("cuda", 0))
     r = run_gpu(w, args.steps, args.warmup)
     n = r["n"]
+    second = None
+    if second_rig is not None:
+        second = (second_rig.w, run_step_leg(second_rig, args.steps, args.warmup))
+        del second_rig
+        torch.cuda.empty_cache()
     flat = None
     if w.unit_shapes:
-        import torch
-        torch.cuda.empty_cache()
         flat = run_flat(w)
     zero1 = None
     if w.name == "llama7b_shard" and not args.no_zero1:
-        import torch
-        torch.cuda.empty_cache()
         zero1 = run_zero1_flow(w, workloads.LLAMA7B)
     bpe = step_bytes_per_elem(w)
-    ms_per_step = r["wall_s"] * 1e3 / args.steps
+    ms_per_step = r["ms_per_step"]
     adamw_bytes = bpe["adamw_step"] * n
     achieved = adamw_bytes / (r["adamw_ms"] * 1e-3) / 1e9
     cpu = None
@@ -699,6 +826,28 @@ def main():
         log("[bench] timing the oracle on the host cores ...")
         cpu = run_cpu_baseline(w, args.cpu_seconds)
     step_gbps = bpe["step"] * n / (ms_per_step * 1e-3) / 1e9
+
+    # kernels whose HBM traffic has records (bench_pmc.py): label, kernel,
+    # shard length, algorithmic bytes per launch
+    def entry(label, kernel, nn, nbytes, per_wg=256):
+        # one-wave workgroups of per_wg elements: the launch's grid in work-items
+        return {"label": label, "kernel": kernel, "shard_elems": nn, "algorithmic_bytes": nbytes,
+                "grid": -(-nn // per_wg) * 64}
+
+    pmc = [entry("adamw_step_tiled", K_ADAMW_TILED, n, adamw_bytes),
+           entry("adamw_step", K_ADAMW_SPLIT, n, adamw_bytes)]
+    if w.micro_batches > 2 and w.grad_dtype == "bf16":
+        pmc += [entry("grad_accum_first", K_ACCUM_FIRST, n, 6 * n),
+                entry("grad_accum_add", K_ACCUM_ADD, n, 10 * n),
+                entry("grad_accum_norm_sq_last", K_ACCUM_NORM_ADD, n, 10 * n + 8 * fused_norm_partials(w, n))]
+
+    def roofline(wl, rr, nn):
+        b = step_bytes_per_elem(wl)["adamw_step"] * nn
+        ach = b / (rr["adamw_ms"] * 1e-3) / 1e9
+        return {"kernel": "adamw_step_tiled", "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS, "traffic": traffic_of("adamw_step_tiled", nn, digests),
+                "traffic_unit": "bytes/launch", "algorithmic_bytes": b, "launch_ms": rr["adamw_ms"]}
+
     out = {
         "metric": "AdamW shard step: elements/s and achieved HBM GB/s (% of peak) per GPU",
         "value": n / (ms_per_step * 1e-3),
@@ -725,33 +874,59 @@ def main():
         "device_copy_gbps": r["copy_gbps"],
         "timing_events": timing_events(),
         "adamw_traffic_ceiling": ceiling_report(r["ceiling_ms"], adamw_bytes, r["adamw_ms"]),
-        "roofline": {"kernel": "adamw_step_tiled", "bound": "hbm", "achieved": achieved,
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": pmc_traffic("adamw_step_tiled", n), "traffic_unit": "bytes/launch",
-                     "algorithmic_bytes": adamw_bytes, "launch_ms": r["adamw_ms"]},
+        "roofline": roofline(w, r, n),
         "adamw_step_split": {
             "ms": r["split_ms"], "bytes_per_elem": bpe["adamw_step"],
             "gbps": adamw_bytes / (r["split_ms"] * 1e-3) / 1e9,
             "frac": adamw_bytes / (r["split_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-            "traffic": pmc_traffic("adamw_step", n),
+            "traffic": traffic_of("adamw_step", n, digests),
             "traffic_ceiling": ceiling_report(r["ceiling_split_ms"], adamw_bytes, r["split_ms"])},
         "cpu_baseline": cpu,
         "flat_unit": flat,
         "zero1_flow": zero1,
-        "grad_norm_sq": {"ms": r["norm_ms"], "bytes_per_elem": 4,
-                         "gbps": 4 * n / (r["norm_ms"] * 1e-3) / 1e9,
-                         "frac": 4 * n / (r["norm_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+        "grad_norm_sq": {"bytes_per_elem": 4, **rate(4 * n, r["norm_ms"])},
         "adamw_step_no_master": None if r["no_master_ms"] is None else {
-            "ms": r["no_master_ms"], "bytes_per_elem": 24,
-            "gbps": 24 * n / (r["no_master_ms"] * 1e-3) / 1e9},
+            "bytes_per_elem": 24, **rate(24 * n, r["no_master_ms"])},
         "adamw_step_no_master_tiled": None if r["no_master_tiled_ms"] is None else {
-            "ms": r["no_master_tiled_ms"], "bytes_per_elem": 24,
-            "gbps": 24 * n / (r["no_master_tiled_ms"] * 1e-3) / 1e9},
+            "bytes_per_elem": 24, **rate(24 * n, r["no_master_tiled_ms"])},
         "reduce_chunks": None if r["reduce_ms"] is None else {
-            "chunks": r["chunks"], "ms": r["reduce_ms"],
-            "gbps": (r["chunks"] * (2 if w.grad_dtype == "bf16" else 4) + 4) * n / (r["reduce_ms"] * 1e-3) / 1e9},
-        "staged_step": None if r["staged_ms"] is None else _staged(r, n, w),
+            "chunks": r["chunks"], "bytes_per_elem": r["chunks"] * (2 if w.grad_dtype == "bf16" else 4) + 4,
+            **rate((r["chunks"] * (2 if w.grad_dtype == "bf16" else 4) + 4) * n, r["reduce_ms"])},
+        "reduce_chunks_norm_sq": None if r["reduce_norm_ms"] is None else {
+            "chunks": r["chunks"], "bytes_per_elem": r["chunks"] * (2 if w.grad_dtype == "bf16" else 4) + 4,
+            "of_plain_fold": r["reduce_norm_ms"] / r["reduce_ms"],
+            **rate((r["chunks"] * (2 if w.grad_dtype == "bf16" else 4) + 4) * n, r["reduce_norm_ms"])},
+        "staging_curve": r["staging_curve"],
     }
+    if w.micro_batches > 2 and w.grad_dtype == "bf16":
+        # measured bytes of the step's accumulation parts, from the per-kernel records
+        t_first, t_add, t_last = (traffic_of(k, n, digests) for k in
+                                  ("grad_accum_first", "grad_accum_add", "grad_accum_norm_sq_last"))
+        sk = out["step_kernels"]
+        sk["grad_accum_all_but_last"]["algorithmic_bytes"] = (6 + 10 * (w.micro_batches - 2)) * n
+        sk["grad_accum_all_but_last"]["traffic"] = (None if t_first is None or t_add is None
+                                                    else t_first + (w.micro_batches - 2) * t_add)
+        sk["grad_accum_norm_sq_last"]["algorithmic_bytes"] = pmc[-1]["algorithmic_bytes"]
+        sk["grad_accum_norm_sq_last"]["traffic"] = t_last
+    if second is not None:
+        w2, r2 = second
+        n2 = r2["n"]
+        bpe2 = step_bytes_per_elem(w2)
+        last_bytes = bpe2["grad_accum_norm_sq_last"] * n2 + 8 * fused_norm_partials(w2, n2)
+        first_q4 = w2.micro_batches == 1 and w2.grad_dtype == "bf16"   # four groups per lane
+        pmc += [entry("adamw_step_tiled", K_ADAMW_TILED, n2, bpe2["adamw_step"] * n2),
+                entry("grad_accum_norm_sq_last", K_ACCUM_NORM_FIRST if first_q4 else K_ACCUM_NORM_ADD, n2,
+                      last_bytes, 1024 if first_q4 else 256)]
+        out["roofline_second"] = {"workload": w2.name, **roofline(w2, r2, n2)}
+        sk2 = step_kernel_rates(bpe2, n2, r2)
+        sk2["grad_accum_norm_sq_last"]["algorithmic_bytes"] = last_bytes
+        sk2["grad_accum_norm_sq_last"]["traffic"] = traffic_of("grad_accum_norm_sq_last", n2, digests)
+        out["second_workload"] = {
+            "workload": w2.name, "shard_elems": n2, "micro_batches": w2.micro_batches, "clip": w2.max_norm > 0,
+            "ms_per_step": r2["ms_per_step"], "elements_per_s": n2 / (r2["ms_per_step"] * 1e-3),
+            "bytes_per_elem": bpe2, "step_kernels": sk2}
+    out["pmc_kernels"] = pmc
+    out["code_objects_sha256"] = sorted(set(digests.values()))
     print(json.dumps(out), flush=True)
 
 

@@ -20,9 +20,12 @@
 // Fused norm association (fixed by n, the overwrite flag and the gradient
 // dtype): each lane adds the squares of its Q groups of 4 elements, 0 and 2
 // into one running sum, 1 and 3 into the other; the 64 lanes combine in a
-// fixed butterfly into one binary64 partial per 256*Q elements; the partials
-// are reduced in fixed contiguous chunks (at most kReduceChunks), then by one
-// workgroup.
+// fixed butterfly into one binary64 partial per 256*Q elements, stored at
+// the workgroup's XCD-contiguous slot (xcd_slot: each partial written once,
+// as a whole line with its neighbours); the partials are reduced in fixed
+// contiguous chunks of slots (at most kReduceChunks), then by one workgroup.
+// Two groups per lane (one partial per 512 elements) measured 79 % against
+// 85 % for one; four with residency capped, 82 %.
 #include "reduce.h"
 
 namespace zs {
@@ -92,7 +95,7 @@ __global__ __launch_bounds__(BS) void accum_kernel(float* __restrict__ acc, cons
     }
     if (NORM) {
         const double total = wave_sum(s0 + s1);
-        if (threadIdx.x == 0) partials[blockIdx.x] = total;
+        if (threadIdx.x == 0) partials[xcd_slot(blockIdx.x, gridDim.x)] = total;
     }
 }
 
@@ -300,7 +303,7 @@ __global__ __launch_bounds__(kReduceBlock) void reduce_chunks_kernel(float* __re
     }
     if (NORM) {
         const double total = wave_sum(s0 + s1);
-        if (threadIdx.x == 0) partials[blockIdx.x] = total;
+        if (threadIdx.x == 0) partials[xcd_slot(blockIdx.x, gridDim.x)] = total;
     }
 }
 

@@ -73,7 +73,7 @@ __device__ __forceinline__ float apply_step(const AdamwScalars& a, float p, floa
 
 // Clip coefficient from the squared norm, in binary64 (uniform per wave).
 // Returns false when the global squared norm is not finite: the step is
-// skipped and nothing is written.
+// skipped, no state is written (the update form writes -0.0, see below).
 __device__ __forceinline__ bool clip_coef(const AdamwScalars& a, const double* norm_sq, float& coef) {
     coef = 1.0f;
     if (norm_sq == nullptr) return true;
@@ -86,6 +86,20 @@ __device__ __forceinline__ bool clip_coef(const AdamwScalars& a, const double* n
         coef = (float)c;
     }
     return true;
+}
+
+// A skipped ZeRO-1 step (non-finite global norm) still writes its update
+// vector: -0.0, the identity of IEEE addition, so the apply that follows the
+// all-gather leaves every parameter bit for bit as it was (the moments are
+// not written).  Four consecutive elements from `at`.
+template <bool OUT_ALIGNED>
+__device__ __forceinline__ void skip_update(float* at) {
+    if constexpr (OUT_ALIGNED) {
+        st_stream(reinterpret_cast<f32x4*>(at), f32x4{-0.0f, -0.0f, -0.0f, -0.0f});
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) st_stream(at + j, -0.0f);
+    }
 }
 
 // vector path: one wave per workgroup, with LDS reserved per workgroup to
@@ -160,7 +174,10 @@ __global__ __launch_bounds__(BS) void adamw_kernel(const AdamwArgs a) {
         const f32x4 m4 = ld_stream(reinterpret_cast<const f32x4*>(m_at));
         const f32x4 v4 = ld_stream(reinterpret_cast<const f32x4*>(v_at));
         float coef;
-        if (!clip_coef(sc, a.norm_sq, coef)) return;
+        if (!clip_coef(sc, a.norm_sq, coef)) {
+            if constexpr (FORM == kUpdate) skip_update<OUT_ALIGNED>(a.update + first);
+            return;
+        }
         float gs[4] = {g4.x, g4.y, g4.z, g4.w};
         float ps[4] = {p4.x, p4.y, p4.z, p4.w};
         float ms[4] = {m4.x, m4.y, m4.z, m4.w};
@@ -194,9 +211,13 @@ __global__ __launch_bounds__(BS) void adamw_kernel(const AdamwArgs a) {
         return;
     }
     // scalar path: VEC == 1, or the ragged tail of the VEC == 4 grid
-    float coef;
-    if (!clip_coef(sc, a.norm_sq, coef)) return;
     const int64_t last = first + VEC < n ? first + VEC : n;
+    float coef;
+    if (!clip_coef(sc, a.norm_sq, coef)) {
+        if constexpr (FORM == kUpdate)
+            for (int64_t i = first; i < last; ++i) a.update[i] = -0.0f;
+        return;
+    }
     for (int64_t i = first; i < last; ++i) {
         float* const ts = TILED ? a.state + tiled_offset<kRuns>(i) : nullptr;   // the element's first run
         float* const m_at = TILED ? (kMasterForm ? ts + kStateTile : ts) : a.exp_avg + i;

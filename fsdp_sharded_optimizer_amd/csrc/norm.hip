@@ -8,12 +8,13 @@
 // binary64 running sums (its groups in order, elements 0 and 2 of each into
 // one sum, 1 and 3 into the other); the 64 lanes of a wave are combined by a
 // fixed butterfly of cross-lane shuffles, the 4 waves through LDS, and each
-// workgroup writes one binary64 partial to the workspace.  Residency is
-// capped at 6 workgroups per CU by 24 KiB of reserved LDS.  Measured on
-// gfx950 (842M elements, random data): 87.3-87.7 % of the HBM peak, against
-// 83.7-84.0 % for a grid-striding grid of 2048 workgroups (the earlier
-// shape), 85-87 % with two loads per lane, 72-75 % with one; a plain fp32
-// read-sum of the same shape reaches 88.8 %.
+// workgroup writes one binary64 partial to the workspace, at its
+// XCD-contiguous slot (xcd_slot).  Residency is capped at 6 workgroups per
+// CU by 24 KiB of reserved LDS.  Measured on gfx950 (842M elements, random
+// data): 91.4 % of the HBM peak with the slots, 86.7 % with the partials in
+// workgroup order (each then written back as its own partly filled sector);
+// earlier shapes: 83.7-84.0 % for a grid-striding grid of 2048 workgroups,
+// 85-87 % with two loads per lane, 72-75 % with one.
 // Stage 2: the partials are added in a fixed tree (contiguous chunks, then
 // one workgroup).  The association is fixed by n alone, so the result is
 // bit-identical run to run.  The gradient is only read, so any
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(kBlock) void norm_partial_kernel(const float* __res
         }
     }
     const double total = block_sum(s0 + s1);
-    if (threadIdx.x == 0) partials[blockIdx.x] = total;
+    if (threadIdx.x == 0) partials[xcd_slot(blockIdx.x, gridDim.x)] = total;
 }
 
 __global__ __launch_bounds__(kBlock) void norm_final_kernel(const double* __restrict__ partials,

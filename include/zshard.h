@@ -485,7 +485,11 @@ ZS_API int32_t adamw_step_no_master(const zs_adamw* hp, uint16_t* param_bf16, fl
  * Adding the update to an fp32 parameter gives the bits adamw_step gives.
  * exp_avg, exp_avg_sq: device fp32[n], read-write; grad: device fp32[n],
  * read; update: device fp32[n], written.  No two may overlap, nor overlap
- * *norm_sq_dev.  A non-finite S writes nothing.
+ * *norm_sq_dev.  A non-finite S skips the step ([ZeRO page] §"组合策略"
+ * recipe): exp_avg and exp_avg_sq are left unchanged and every update[i] is
+ * written as -0.0, the identity of IEEE addition, so flat_apply_update of the
+ * gathered update leaves every parameter as it was (fp32 bit for bit; bf16
+ * too, except that a NaN parameter is rewritten as the quiet NaN 0x7FC0).
  * Errors: ZS_EINVAL (as adamw_step, or weight_decay != 0), ZS_EOVERLAP,
  * ZS_EHIP.
  */

@@ -100,6 +100,8 @@ def _configure(L):
     L.orc_state_untile.restype = ctypes.c_int
     L.orc_num_threads.argtypes = []
     L.orc_num_threads.restype = ctypes.c_int
+    L.orc_set_num_threads.argtypes = [ctypes.c_int]
+    L.orc_set_num_threads.restype = None
     return L
 
 
@@ -146,6 +148,11 @@ def _np_dtype(code: int):
 
 def num_threads() -> int:
     return int(lib().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads the OpenMP loops use from now on (results do not depend on it)."""
+    lib().orc_set_num_threads(int(n))
 
 
 def bf16_rne(x, out: np.ndarray = None) -> np.ndarray:

@@ -593,6 +593,8 @@ int orc_moments_untile(const float* moments, float* exp_avg, float* exp_avg_sq, 
 #ifdef _OPENMP
 #include <omp.h>
 int orc_num_threads(void) { return omp_get_max_threads(); }
+void orc_set_num_threads(int n) { if (n > 0) omp_set_num_threads(n); }
 #else
 int orc_num_threads(void) { return 1; }
+void orc_set_num_threads(int n) { (void)n; }
 #endif

@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "../../include/zshard.h"
+#include "../../fsdp_sharded_optimizer_amd/csrc/zs_common.h"
 
 #define CHECK(cond, code)                                          \
     do {                                                           \
@@ -23,7 +24,25 @@
 static const uintptr_t FAKE = 0x7F0000000000ull;
 static void* fake(uint64_t off) { return reinterpret_cast<void*>(FAKE + off); }
 
+// The norm kernels' partial slots (zs::xcd_slot) are a bijection of [0, nb)
+// for every grid size: each partial lands in the workspace, no two share one.
+static int check_xcd_slots() {
+    std::vector<int64_t> sizes;
+    for (int64_t nb = 1; nb <= 2100; ++nb) sizes.push_back(nb);
+    for (int64_t nb : {3290242LL, 1645121LL, 205640LL, 397213LL, 8388608LL, 8388607LL}) sizes.push_back(nb);
+    for (int64_t nb : sizes) {
+        std::vector<unsigned char> seen((size_t)nb, 0);
+        for (int64_t b = 0; b < nb; ++b) {
+            const int64_t s = zs::xcd_slot(b, nb);
+            if (s < 0 || s >= nb || seen[(size_t)s]) return 1;
+            seen[(size_t)s] = 1;
+        }
+    }
+    return 0;
+}
+
 int main() {
+    CHECK(check_xcd_slots() == 0, 30);
     for (int64_t T = 0; T <= 64; ++T)
         for (int32_t N = 1; N <= 9; ++N)
             for (int32_t r = 0; r < N; ++r) {

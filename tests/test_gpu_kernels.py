@@ -590,9 +590,54 @@ def test_adam_update_skips_on_nonfinite_norm():
     norm = torch.tensor([float("nan")], dtype=torch.float64, device="cuda")
     zs.adam_update(_hp(1, wd=0.0, max_norm=1.0)[0], m, v, g, u, norm_sq=norm)
     torch.cuda.synchronize()
-    assert torch.all(u == 7.0) and torch.all(m == 1) and torch.all(v == 1)
+    assert torch.all(m == 1) and torch.all(v == 1)
+    assert np.all(to_np(u).view(np.uint32) == 0x80000000)   # -0.0: the apply adds nothing
     with pytest.raises(zs.ZShardError):
         zs.adam_update(_hp(1, wd=0.1)[0], m, v, g, u)
+
+
+@pytest.mark.parametrize("tiled", [False, True])
+@pytest.mark.parametrize("n,upd_off", [(1, 0), (4099, 0), (4099, 1), (70_001, 3)])
+@pytest.mark.parametrize("bad", [float("nan"), float("inf")])
+def test_skipped_zero1_step_leaves_parameters_unchanged(tiled, n, upd_off, bad):
+    """A non-finite global norm in the ZeRO-1 flow: adam_update
+    (adam_update_tiled) over a buffer holding a stale update, then
+    flat_apply_update of that buffer into fp32 and bf16 parameters (with
+    +-0.0, subnormals and +-inf among them).  Every parameter and moment is
+    bit-identical afterwards and the update is -0.0, as in the oracle."""
+    print(f"skipped zero-1 step tiled={tiled} n={n} update offset={upd_off} norm={bad}", flush=True)
+    rng = np.random.default_rng(n + upd_off)
+    g = from_np(rng.standard_normal(n).astype(np.float32))
+    m0 = rng.standard_normal(n).astype(np.float32)
+    v0 = np.abs(rng.standard_normal(n)).astype(np.float32)
+    uw = torch.full((n + upd_off,), 5.0, device="cuda")   # stale values from an earlier step
+    u = uw[upd_off:]
+    norm = torch.tensor([bad], dtype=torch.float64, device="cuda")
+    hp_gpu = _hp(3, wd=0.0, max_norm=1.0)[0]
+    if tiled:
+        mo = torch.empty(zs.moments_tiled_numel(n), device="cuda")
+        zs.moments_tile(from_np(m0), from_np(v0), mo)
+        zs.adam_update_tiled(hp_gpu, mo, g, u, norm_sq=norm)
+        m, v = torch.empty(n, device="cuda"), torch.empty(n, device="cuda")
+        zs.moments_untile(mo, m, v)
+    else:
+        m, v = from_np(m0), from_np(v0)
+        zs.adam_update(hp_gpu, m, v, g, u, norm_sq=norm)
+    u_ref = np.full(n, 5.0, np.float32)
+    hp_orc = oracle.make_hp(hp_gpu.lr, hp_gpu.beta1, hp_gpu.beta2, hp_gpu.eps, 0.0, hp_gpu.grad_scale, 1.0,
+                            0.0, 3)
+    assert oracle.adam_update(hp_orc, m0.copy(), v0.copy(), to_np(g), u_ref, norm_sq=bad) == 1
+    assert bits_equal(to_np(u), u_ref)
+    assert bits_equal(to_np(m), m0) and bits_equal(to_np(v), v0)
+    specials = np.array([0.0, -0.0, 1e-45, -1e-45, np.inf, -np.inf, 1.0, -2.5], np.float32)
+    p32 = np.resize(specials, n) * np.float32(1.0)
+    p32[len(specials):] = rng.uniform(-1, 1, max(n - len(specials), 0)).astype(np.float32)
+    pb = oracle.bf16_rne(p32)
+    dev32, devb = from_np(p32), from_np(pb, bf16=True)
+    zs.flat_apply_update(u, [dev32])
+    zs.flat_apply_update(u, [devb])
+    assert bits_equal(to_np(dev32), p32)
+    assert bits_equal(to_np(devb), pb)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

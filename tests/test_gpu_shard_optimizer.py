@@ -177,14 +177,20 @@ def test_accumulate_all_matches_one_call_per_micro_batch(layout, fused):
     fused=True the one pass also forms the norm: the accumulator is still
     bit-identical and the norm within the fused norms' tolerance of the
     oracle's norm of the same accumulator (its last bits, and so the clipped
-    step's, may differ from the separate norm pass's)."""
+    step's, may differ from the separate norm pass's).  In both cases the
+    master, moments and bf16 parameter of the accumulate_all optimizer are
+    bit-identical to the oracle's AdamW stepped from the oracle's
+    accumulator with the GPU's own norm."""
     print(f"ShardOptimizer accumulate_all layout={layout} fused={fused}", flush=True)
     n, M = 2 * zs.STATE_TILE + 777, 19
     rng = np.random.default_rng(41)
-    p0 = from_np(rng.uniform(-0.1, 0.1, n).astype(np.float32))
+    p0_host = rng.uniform(-0.1, 0.1, n).astype(np.float32)
+    p0 = from_np(p0_host)
     kw = dict(lr=3e-4, betas=(0.9, 0.95), weight_decay=0.1, grad_scale=1 / M, max_norm=0.5, layout=layout)
     a, b = (zs.ShardOptimizer(p0.clone(), param_bf16=torch.empty(n, dtype=torch.bfloat16, device="cuda"), **kw)
             for _ in range(2))
+    ref = {"master": p0_host.copy(), "exp_avg": np.zeros(n, np.float32), "exp_avg_sq": np.zeros(n, np.float32),
+           "param_bf16": np.zeros(n, np.uint16)}
     for t in range(1, 4):
         mbs = [oracle.bf16_rne((rng.standard_normal(n) * 0.05 * (k + t)).astype(np.float32)) for k in range(M)]
         gpu = [from_np(g, bf16=True) for g in mbs]
@@ -202,6 +208,11 @@ def test_accumulate_all_matches_one_call_per_micro_batch(layout, fused):
         torch.cuda.synchronize()
         assert oracle.clip_coef(a.norm_sq.item(), 0.1, 0.5) < 1.0   # every step clips
         assert bits_equal(to_np(a.acc), to_np(b.acc))
+        hp_orc = oracle.make_hp(3e-4, 0.9, 0.95, 1e-8, 0.1, 1 / M, 0.5, 0.1, t)
+        assert oracle.adamw_step(hp_orc, ref["master"], ref["exp_avg"], ref["exp_avg_sq"], acc_ref,
+                                 ref["param_bf16"], norm_sq=a.norm_sq.item()) == 0
+        for name in ("master", "exp_avg", "exp_avg_sq", "param_bf16"):
+            assert bits_equal(to_np(getattr(a, name)), ref[name]), (t, name, "vs the oracle")
         if fused:
             S = oracle.grad_norm_sq(acc_ref, 1 / M)
             assert abs(a.norm_sq.item() - S) <= NORM_TOL * S
@@ -211,3 +222,35 @@ def test_accumulate_all_matches_one_call_per_micro_batch(layout, fused):
             assert bits_equal(to_np(getattr(a, name)), to_np(getattr(b, name))), (t, name)
     with pytest.raises(ValueError):
         a.accumulate_all([])
+
+
+@pytest.mark.parametrize("layout", ["split", "tiled"])
+@pytest.mark.parametrize("k", [1, 4])
+def test_ledger_bytes_match_the_device_allocator(layout, k):
+    """ledger.library_shard_bytes against what torch's device allocator
+    hands out for one rank's buffers: a ShardOptimizer (fp32 master,
+    exp_avg, exp_avg_sq and accumulator, split or tiled) with its bf16
+    parameter and k bf16 micro-batch gradients in flight.  The allocated
+    bytes grow by the ledger's figure plus the norm's fp64 and workspace (and
+    the tiled state's last-tile padding), up to the allocator's rounding of
+    each buffer to 512 bytes."""
+    from fsdp_sharded_optimizer_amd import ledger
+    n = (1 << 22) + 12345
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    before = torch.cuda.memory_allocated()
+    master = torch.zeros(n, device="cuda")
+    opt = zs.ShardOptimizer(master, lr=1e-3, param_bf16=torch.empty(n, dtype=torch.bfloat16, device="cuda"),
+                            layout=layout)
+    if layout == "tiled":
+        del master            # the tiled state holds the values; the caller's tensor may go
+    grads = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for _ in range(k)]
+    torch.cuda.synchronize()
+    got = torch.cuda.memory_allocated() - before
+    want = ledger.library_shard_bytes(n, grad_buffers=k) + 8 + opt.workspace.numel()
+    if layout == "tiled":
+        want += (zs.state_tiled_numel(n) - 3 * n) * 4
+    buffers = 4 + k + (3 if layout == "split" else 2)   # + norm, workspace, param; master / state, acc
+    print(f"ledger {layout} k={k}: allocated {got}, ledger + norm scratch {want}", flush=True)
+    assert want <= got <= want + 512 * buffers, (got, want)
+    del opt, grads

@@ -7,11 +7,13 @@ drawn on the GPU with seeded generators and copied to the host for the
 oracle, so both sides consume the same bits; no oracle input comes from
 the library's outputs.
 
-Small cases compare every element.  Full-size cases (the real shard
-lengths) compare the squared norm over the whole shard (the oracle
-accumulates the full micro-batches itself) and the optimizer state on a
-sample of elements (the update is element-wise, so the oracle steps the
-sampled elements alone), plus every element of the FSDP unit.
+Small cases compare every element.  At the real shard lengths, the bench's
+launch configuration is compared element by element over the whole shard
+(or fixed 1 GiB slices when the host lacks the memory; the test names the
+mode), and longer or other configurations compare the squared norm over
+the whole shard and the optimizer state on a sample of elements (the update
+is element-wise, so the oracle steps the sampled elements alone), plus
+every element of the FSDP unit.
 """
 import math
 import time
@@ -293,13 +295,14 @@ def test_full_fsdp_unit_70b_block():
 
 
 @pytest.mark.parametrize("name,full_norm,fused,layout", [
-    ("llama7b_shard", False, True, "tiled"), ("llama7b_shard", False, True, "split"),
-    ("zero3_70b_shard", True, False, "tiled"), ("zero3_70b_shard", True, True, "tiled"),
+    ("llama7b_shard", True, True, "split"), ("zero3_70b_shard", True, False, "tiled"),
     ("llama13b_shard_clip", True, True, "tiled")])
 def test_full_shard(name, full_norm, fused, layout):
-    """The real shard lengths in bench.py's launch configuration (the tiled
-    state; the 7B shard also on split buffers): the norm over the whole
-    shard, the optimizer state on sampled elements."""
+    """The real shard lengths in the configurations the every-element test
+    below does not run: the 7B shard on split buffers, the 70B shard with
+    the norm as its own pass, and all ten steps of the 13B workload (its
+    clip pattern, steps 2, 5 and 8); the norm over the whole shard, the
+    optimizer state on sampled elements."""
     w = workloads.WORKLOADS[name]
     _, start, end, _ = zs.zero_shard_range(w.total, w.world, w.rank)
     n = end - start
@@ -309,6 +312,129 @@ def test_full_shard(name, full_norm, fused, layout):
         assert [r["step"] for r in rep if r["coef"] < 1.0] == [2, 5, 8]
     if name == "zero3_70b_shard":
         assert all(0.70 < r["coef"] < 0.76 for r in rep), rep
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# full sizes, every element (or fixed 1 GiB slices when the host is short of
+# memory): the bench's launch configuration against the oracle holding the
+# same state
+# ---------------------------------------------------------------------------
+
+CMP_CHUNK = 1 << 26         # elements per comparison chunk: 256 MiB of fp32
+SLICE = 1 << 28             # a 1 GiB slice of fp32 state
+
+
+def _host_mem_available() -> int:
+    with open("/proc/meminfo") as f:
+        for line in f:
+            if line.startswith("MemAvailable:"):
+                return int(line.split()[1]) * 1024
+    return 0
+
+
+def _tiled_chunk(state: torch.Tensor, c0: int, c1: int, k: int) -> np.ndarray:
+    """Elements [c0, c1) (c0 a multiple of the tile) of run k (0 master, 1
+    exp_avg, 2 exp_avg_sq) of a tiled state, copied to the host."""
+    t0, t1 = c0 // STATE_TILE, (c1 + STATE_TILE - 1) // STATE_TILE
+    blk = state[3 * STATE_TILE * t0:3 * STATE_TILE * t1].view(t1 - t0, 3, STATE_TILE)
+    return host(blk[:, k, :].reshape(-1)[:c1 - c0])
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,steps", [("llama7b_shard", 3), ("zero3_70b_shard", 2), ("llama13b_shard_clip", 2)])
+def test_full_shard_every_element(name, steps):
+    """The real shard lengths through the bench's launch configuration
+    (grad_accum per micro-batch, grad_accum_norm_sq for the last,
+    adamw_step_tiled with the bf16 re-cast, clipped where the workload
+    clips) next to the oracle stepping the same state from the same inputs.
+    Every step compares, element by element: the accumulator (bit-exact,
+    whole shard), the squared norm over the whole shard (1e-5), and the
+    master, exp_avg, exp_avg_sq and bf16 parameter of the compared ranges,
+    read back in 256 MiB chunks.  Mode "full": the compared range is the
+    whole shard; mode "slices" (when the host lacks the memory for the
+    oracle's full state): the first, middle and last 1 GiB of state, exact
+    by the update's element-wise independence (Memory page, 一、显存账本).
+    Where the GPU's fp32 clip coefficient equals the oracle's (always, unless
+    the two norms straddle a rounding boundary of it), every compared element
+    must be bit-identical; otherwise the 2e-6 / 1-ulp bar applies."""
+    w = workloads.WORKLOADS[name]
+    _, start, end, _ = zs.zero_shard_range(w.total, w.world, w.rank)
+    n = end - start
+    # the oracle's accumulator, master, exp_avg, exp_avg_sq and bf16 parameter,
+    # one gradient draw, and room for the chunks in flight
+    need = n * (4 * 4 + 2 + (2 if w.grad_dtype == "bf16" else 4)) + (4 << 30)
+    mode = "full" if _host_mem_available() > 1.5 * need else "slices"
+    if mode == "full":
+        ranges = [(0, n)]
+    else:
+        mid = (n // 2 // STATE_TILE) * STATE_TILE
+        ranges = [(0, SLICE), (mid, mid + SLICE), (n - n % STATE_TILE - SLICE, n)]
+    log(f"full {name} every element: n={n}, {steps} steps x {w.micro_batches} micro-batches, mode={mode}, "
+        f"compared elements per step {sum(b - a for a, b in ranges)}")
+
+    master = workloads.master_init(w, n, DEV)
+    param = master.to(torch.bfloat16)
+    state = torch.empty(zs.state_tiled_numel(n), dtype=torch.float32, device=DEV)
+    zs.state_tile(master, None, None, state)
+    ref = []
+    for a, b in ranges:
+        ref.append({"p": host(master[a:b]), "m": np.zeros(b - a, np.float32), "v": np.zeros(b - a, np.float32),
+                    "b": host(param[a:b])})
+    del master
+    acc = torch.empty(n, dtype=torch.float32, device=DEV)
+    norm = torch.zeros(1, dtype=torch.float64, device=DEV)
+    ws = torch.empty(max(zs.grad_accum_norm_sq_workspace_bytes(n), 8), dtype=torch.uint8, device=DEV)
+    acc_ref = np.empty(n, np.float32)
+    code = oracle.BF16 if w.grad_dtype == "bf16" else oracle.F32
+    last = w.micro_batches - 1
+    for t in range(1, steps + 1):
+        t0 = time.perf_counter()
+        for mb in range(w.micro_batches):
+            g = workloads.grad_draw(w, n, t, mb, DEV)
+            if mb == last:
+                zs.grad_accum_norm_sq(acc, g, mb == 0, w.grad_scale, norm, ws)
+            else:
+                zs.grad_accum(acc, g, overwrite=(mb == 0))
+            oracle.grad_accum(acc_ref, host(g), code, overwrite=(mb == 0))
+            del g
+        s_gpu = float(norm.item())
+        s_ref = oracle.grad_norm_sq(acc_ref, w.grad_scale)
+        assert abs(math.sqrt(s_gpu) - math.sqrt(s_ref)) <= NORM_TOL * math.sqrt(s_ref), (t, s_gpu, s_ref)
+        for c0 in range(0, n, CMP_CHUNK):
+            c1 = min(c0 + CMP_CHUNK, n)
+            assert bits_equal(host(acc[c0:c1]), acc_ref[c0:c1]), (t, "acc", c0)
+        extra = workloads.other_ranks_norm_sq(w, t, n)
+        hp = zs.AdamWConfig(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
+                            grad_scale=w.grad_scale, max_norm=w.max_norm, extra_norm_sq=extra, step=t)
+        zs.adamw_step_tiled(hp, state, acc, param, norm_sq=norm)
+        ohp = oracle.make_hp(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, w.grad_scale, w.max_norm, extra, t)
+        coef_gpu = oracle.clip_coef(s_gpu, extra, w.max_norm)
+        coef = oracle.clip_coef(s_ref, extra, w.max_norm)
+        same_coef = np.float32(coef_gpu) == np.float32(coef)
+        checker = StateCheck(w.beta1, w.lr, w.weight_decay, 0.0)
+        compared = identical = 0
+        for (a, b), r in zip(ranges, ref):
+            # the state before the step: only the tolerance path needs it
+            prev = None if same_coef else {"p": r["p"].copy(), "m": r["m"].copy()}
+            assert oracle.adamw_step(ohp, r["p"], r["m"], r["v"], np.ascontiguousarray(acc_ref[a:b]), r["b"],
+                                     norm_sq=s_ref) == 0
+            for c0 in range(a, b, CMP_CHUNK):
+                c1 = min(c0 + CMP_CHUNK, b)
+                lo, hi = c0 - a, c1 - a
+                gpu = {"p": _tiled_chunk(state, c0, c1, 0), "m": _tiled_chunk(state, c0, c1, 1),
+                       "v": _tiled_chunk(state, c0, c1, 2), "b": host(param[c0:c1])}
+                orc = {k: r[k][lo:hi] for k in ("p", "m", "v", "b")}
+                same = all(bits_equal(gpu[k], orc[k]) for k in ("p", "m", "v", "b"))
+                if not same:
+                    assert not same_coef, (t, c0, "not bit-identical although the clip coefficients agree")
+                    g2 = (acc_ref[c0:c1] * np.float32(w.grad_scale)) * np.float32(coef)
+                    checker.check(gpu, orc, {"p": prev["p"][lo:hi], "m": prev["m"][lo:hi]}, g2, f"{name} t={t}")
+                compared += c1 - c0
+                identical += (c1 - c0) if same else 0
+        log(f"  {name} t={t} mode={mode} compared={compared} bit-identical={identical} coef={coef:.6f} "
+            f"norm={math.sqrt(s_gpu + extra):.6f} secs={time.perf_counter() - t0:.1f}")
+    del state, acc, param, acc_ref, ref
     torch.cuda.empty_cache()
 
 
