@@ -9,6 +9,7 @@ The Python names mirror the C ABI in include/zshard.h:
     grad_reduce_chunks(acc, chunks, overwrite)
     grad_reduce_chunks_norm_sq(acc, chunks, overwrite, grad_scale, out, workspace=None)
     grad_accum_norm_sq(acc, grad, overwrite, grad_scale, out, workspace=None)
+    grad_accum_norm_sq_noalloc(acc, grad, overwrite, grad_scale, out)   partials in a static device scratch
     grad_norm_sq(grad, grad_scale, out, workspace=None)
     adamw_step(hp, master, exp_avg, exp_avg_sq, grad, param_bf16=None, norm_sq=None)
     adamw_scalars(hp) / scalars_bytes(hp)       the step's binary32 scalars, on the host
@@ -31,6 +32,7 @@ torch stream; torch supplies device memory and the stream only.
 from ._binding import (  # noqa: F401
     EXPORTS,
     LIB_PATH,
+    NOALLOC_MAX_ELEMS,
     STATE_TILE,
     AdamWConfig,
     ZShardError,
@@ -49,6 +51,7 @@ from ._binding import (  # noqa: F401
     flat_unpack,
     grad_accum,
     grad_accum_norm_sq,
+    grad_accum_norm_sq_noalloc,
     grad_accum_norm_sq_workspace_bytes,
     grad_reduce_chunks,
     grad_reduce_chunks_norm_sq,

@@ -33,8 +33,9 @@ EXPORTS = (
     "flat_apply_update", "state_tiled_numel", "state_tile", "state_untile", "adamw_step_tiled",
     "adamw_step_tiled_dev", "moments_tiled_numel", "moments_tile", "moments_untile", "adam_update_tiled",
     "adamw_step_no_master_tiled", "grad_reduce_chunks_norm_sq_workspace_bytes", "grad_reduce_chunks_norm_sq",
-    "zs_strerror", "zs_last_hip_error",
+    "grad_accum_norm_sq_noalloc", "zs_strerror", "zs_last_hip_error",
 )
+NOALLOC_MAX_ELEMS = 2_146_959_360   # ZS_NOALLOC_MAX_ELEMS
 
 STATE_TILE = 8192   # ZS_STATE_TILE: elements per tile of the tiled optimizer state
 
@@ -127,6 +128,8 @@ def lib() -> ctypes.CDLL:
         L.grad_accum_norm_sq_workspace_bytes.restype = I64
         L.grad_accum_norm_sq.argtypes = [P, P, I32, I64, I32, D, P, P, I64, P]
         L.grad_accum_norm_sq.restype = I32
+        L.grad_accum_norm_sq_noalloc.argtypes = [P, P, I32, I64, I32, D, P, P]
+        L.grad_accum_norm_sq_noalloc.restype = I32
         L.adamw_step.argtypes = [ctypes.POINTER(AdamW), P, P, P, P, P, I64, P, P]
         L.adamw_step.restype = I32
         L.adamw_scalars.argtypes = [ctypes.POINTER(AdamW), ctypes.POINTER(AdamWScalars)]
@@ -381,6 +384,21 @@ def grad_accum_norm_sq(acc: torch.Tensor, grad: torch.Tensor, overwrite: bool, g
         _dev(acc, "acc", torch.float32), _dev(grad, "grad"), _dtype_code(grad), n, 1 if overwrite else 0,
         float(grad_scale), _dev(out, "out"), _dev(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def grad_accum_norm_sq_noalloc(acc: torch.Tensor, grad: torch.Tensor, overwrite: bool, grad_scale: float,
+                               out: torch.Tensor, stream=None) -> torch.Tensor:
+    """grad_accum_norm_sq with the partials in the library's static device
+    scratch: no workspace, nothing allocated (n <= NOALLOC_MAX_ELEMS)."""
+    n = acc.numel()
+    if grad.numel() != n:
+        raise ValueError("grad_accum_norm_sq_noalloc: size mismatch")
+    if out.dtype != torch.float64 or out.numel() < 1:
+        raise TypeError("grad_accum_norm_sq_noalloc: out must hold one float64")
+    _check("grad_accum_norm_sq_noalloc", lib().grad_accum_norm_sq_noalloc(
+        _dev(acc, "acc", torch.float32), _dev(grad, "grad"), _dtype_code(grad), n, 1 if overwrite else 0,
+        float(grad_scale), _dev(out, "out"), _stream(stream)))
     return out
 
 

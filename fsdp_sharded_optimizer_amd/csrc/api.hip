@@ -5,6 +5,7 @@
 // launching anything when they are wrong.  Valid calls only enqueue kernels
 // on the caller's stream.  Host scalars are formed in binary64 and rounded
 // to binary32 once.
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstddef>
@@ -46,6 +47,44 @@ inline bool size_ok(int64_t n) { return n >= 0 && n <= kMaxElems; }
 
 }  // namespace
 
+// The scratch of grad_accum_norm_sq_noalloc: one array per GPU (each device
+// holds its own copy of a __device__ variable), sized for the partials and
+// chunk stage of ZS_NOALLOC_MAX_ELEMS elements.  In host code `scratch`
+// names a host-side stand-in, not device memory: kernels get the address
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device and kept in g_scratch_ptr.
+constexpr int64_t kScratchBytes = ZS_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) double scratch[kScratchBytes / 8];
+constexpr int kScratchDevices = 64;
+static std::atomic<void*> g_scratch_ptr[kScratchDevices];
+
+static_assert(ZS_NOALLOC_MAX_ELEMS % 256 == 0 &&
+                  (ZS_NOALLOC_MAX_ELEMS / 256 + zs::kReduceChunks) * 8 == kScratchBytes,
+              "the largest call's partials and chunk stage fill the scratch exactly");
+
+// Device address of the current device's scratch (ZS_OK), looked up on the
+// first call on that device.  Two threads racing on the first call look it
+// up twice and store the same address.
+static int32_t current_scratch(void** out) {
+    int dev = -1;
+    int32_t rc = hip_status(hipGetDevice(&dev));
+    if (rc != ZS_OK) return rc;
+    if (dev >= 0 && dev < kScratchDevices) {
+        void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+        if (p != nullptr) {
+            *out = p;
+            return ZS_OK;
+        }
+    }
+    void* p = nullptr;
+    rc = hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (rc != ZS_OK) return rc;
+    if (p == nullptr) return hip_status(hipErrorInvalidSymbol);
+    if (dev >= 0 && dev < kScratchDevices) g_scratch_ptr[dev].store(p, std::memory_order_release);
+    *out = p;
+    return ZS_OK;
+}
+
 extern "C" {
 
 const char* zs_strerror(int32_t code) {
@@ -54,7 +93,7 @@ const char* zs_strerror(int32_t code) {
         case ZS_EINVAL: return "invalid argument";
         case ZS_EOVERLAP: return "buffers overlap";
         case ZS_EWORKSPACE: return "workspace too small";
-        case ZS_EHIP: return "HIP launch failed";
+        case ZS_EHIP: return "HIP call failed";
         default: return "unknown error code";
     }
 }
@@ -217,6 +256,30 @@ int32_t grad_accum_norm_sq(float* acc, const void* grad, int32_t grad_dtype, int
                                                     (float)grad_scale, out_sq_dev,
                                                     static_cast<double*>(workspace), vec,
                                                     as_stream(hip_stream)));
+}
+
+// ---------------------------------------------------------------------------
+// grad_accum_norm_sq with its partials in a static device array
+// ---------------------------------------------------------------------------
+
+int32_t grad_accum_norm_sq_noalloc(float* acc, const void* grad, int32_t grad_dtype, int64_t n, int32_t overwrite,
+                                   double grad_scale, double* out_sq_dev, void* hip_stream) {
+    // the size limit and the argument checks come before any device call
+    if (n < 0 || n > ZS_NOALLOC_MAX_ELEMS) return ZS_EINVAL;
+    const int64_t need = grad_accum_norm_sq_workspace_bytes(n);
+    if (need < 0 || need > kScratchBytes) return ZS_EINVAL;
+    if (!dtype_ok(grad_dtype) || out_sq_dev == nullptr || !aligned(out_sq_dev, 8)) return ZS_EINVAL;
+    if (!(grad_scale > 0.0) || !std::isfinite(grad_scale)) return ZS_EINVAL;
+    if (n > 0 && (acc == nullptr || grad == nullptr || !aligned(acc, 4) ||
+                  !aligned(grad, (uintptr_t)elem_size(grad_dtype))))
+        return ZS_EINVAL;
+    void* ws = nullptr;
+    const int32_t rc = current_scratch(&ws);
+    if (rc != ZS_OK) return rc;
+    // the workspace entry point's checks (overlap with the scratch included)
+    // and launches, on the scratch
+    return grad_accum_norm_sq(acc, grad, grad_dtype, n, overwrite, grad_scale, out_sq_dev, ws, kScratchBytes,
+                              hip_stream);
 }
 
 // Elements to run element by element before the vector path when every

@@ -79,7 +79,7 @@ enum {
                            dtype, misalignment, size mismatch */
     ZS_EOVERLAP = -2,   /* two buffers that must be disjoint overlap */
     ZS_EWORKSPACE = -3, /* workspace smaller than grad_norm_sq_workspace_bytes */
-    ZS_EHIP = -4        /* a HIP launch failed; see zs_last_hip_error() */
+    ZS_EHIP = -4        /* a HIP launch (or another HIP call) failed; see zs_last_hip_error() */
 };
 
 /* One rank's range of the flat buffer. */
@@ -290,6 +290,33 @@ ZS_API int64_t grad_accum_norm_sq_workspace_bytes(int64_t n);
 ZS_API int32_t grad_accum_norm_sq(float* acc, const void* grad, int32_t grad_dtype, int64_t n, int32_t overwrite,
                                   double grad_scale, double* out_sq_dev, void* workspace, int64_t workspace_bytes,
                                   void* hip_stream);
+
+/*
+ * grad_accum_norm_sq_noalloc — grad_accum_norm_sq for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  It takes no workspace and
+ * allocates nothing; the norm's partials go to a scratch array the library
+ * holds in device memory, ZS_NOALLOC_SCRATCH_BYTES (64 MiB) on each GPU it
+ * runs on, kept until the process ends.  n is at most ZS_NOALLOC_MAX_ELEMS
+ * (2,146,959,360 elements).  Results are bit for bit those of
+ * grad_accum_norm_sq (the same kernels and partial layout).
+ * The first call on a device, with that device current, looks up the
+ * array's device address (hipGetSymbolAddress); make that call outside a
+ * graph capture.  Every call on one GPU uses that GPU's one array: calls
+ * that overlap in time (two streams, two threads, two captured graphs
+ * replaying at once) race on it and give wrong norms, so order them (one
+ * stream, or events).  The array keeps the last call's partials; nothing
+ * in it needs to start at zero (every partial a call reads, it wrote).
+ * Arguments as grad_accum_norm_sq, without the workspace.
+ * Errors: ZS_EINVAL (as grad_accum_norm_sq, or n > ZS_NOALLOC_MAX_ELEMS,
+ * both found before any device call), ZS_EOVERLAP, ZS_EHIP (a launch, or
+ * the array's address could not be obtained).
+ */
+#define ZS_NOALLOC_SCRATCH_BYTES (64ll << 20)
+#define ZS_NOALLOC_MAX_ELEMS 2146959360ll
+ZS_API int32_t grad_accum_norm_sq_noalloc(float* acc, const void* grad, int32_t grad_dtype, int64_t n,
+                                          int32_t overwrite, double grad_scale, double* out_sq_dev,
+                                          void* hip_stream);
 
 /*
  * adamw_step — the fused AdamW update of one rank's shard.

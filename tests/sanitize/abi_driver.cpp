@@ -43,6 +43,13 @@ static int check_xcd_slots() {
 
 int main() {
     CHECK(check_xcd_slots() == 0, 30);
+    // the no-alloc norm: sizes beyond its scratch and bad arguments, before any device call
+    CHECK(grad_accum_norm_sq_noalloc((float*)fake(0), fake(1 << 30), ZS_BF16, ZS_NOALLOC_MAX_ELEMS + 1, 0, 1.0,
+                                     (double*)fake(3ull << 30), nullptr) == ZS_EINVAL, 31);
+    CHECK(grad_accum_norm_sq_noalloc((float*)fake(0), fake(1 << 30), ZS_BF16, 64, 0, -1.0,
+                                     (double*)fake(3ull << 30), nullptr) == ZS_EINVAL, 31);
+    CHECK(grad_accum_norm_sq_noalloc(nullptr, fake(1 << 30), ZS_BF16, 64, 0, 1.0, (double*)fake(3ull << 30),
+                                     nullptr) == ZS_EINVAL, 31);
     for (int64_t T = 0; T <= 64; ++T)
         for (int32_t N = 1; N <= 9; ++N)
             for (int32_t r = 0; r < N; ++r) {

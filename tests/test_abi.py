@@ -37,7 +37,7 @@ def no_launch_reached():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 29 and set(names) == set(B.EXPORTS), names
+    assert len(names) == 30 and set(names) == set(B.EXPORTS), names
     L = zs.lib()
     for name in names:
         assert getattr(L, name) is not None
@@ -545,3 +545,25 @@ def test_product_code_does_not_use_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", text, flags=re.M), f
                 assert "orc_" not in text and "liboracle" not in text and "oracle/" not in text, f
+
+
+def test_noalloc_rejects_before_any_device_call():
+    """grad_accum_norm_sq_noalloc validates on the host first: a size beyond
+    its scratch, a bad dtype or scale, null or misaligned pointers come back
+    ZS_EINVAL without a HIP call (no GPU here; the fixture checks that no
+    launch was attempted)."""
+    L = zs.lib()
+    f = L.grad_accum_norm_sq_noalloc
+    acc, g, out = FAKE, FAKE + 2**32, FAKE + 2**33
+    assert B.NOALLOC_MAX_ELEMS == 2_146_959_360
+    assert zs.grad_accum_norm_sq_workspace_bytes(B.NOALLOC_MAX_ELEMS) == 64 << 20
+    for n in (B.NOALLOC_MAX_ELEMS + 1, 1 << 39, -1):
+        assert f(acc, g, B.ZS_BF16, n, 0, 1.0, out, None) == B.ZS_EINVAL, n
+    assert f(acc, g, 7, 16, 0, 1.0, out, None) == B.ZS_EINVAL
+    assert f(acc, g, B.ZS_BF16, 16, 0, 0.0, out, None) == B.ZS_EINVAL
+    assert f(acc, g, B.ZS_BF16, 16, 0, float("nan"), out, None) == B.ZS_EINVAL
+    assert f(acc, g, B.ZS_BF16, 16, 0, 1.0, None, None) == B.ZS_EINVAL
+    assert f(acc, g, B.ZS_BF16, 16, 0, 1.0, out + 4, None) == B.ZS_EINVAL
+    assert f(None, g, B.ZS_BF16, 16, 0, 1.0, out, None) == B.ZS_EINVAL
+    assert f(acc + 2, g, B.ZS_BF16, 16, 0, 1.0, out, None) == B.ZS_EINVAL
+    assert f(acc, g + 1, B.ZS_BF16, 16, 0, 1.0, out, None) == B.ZS_EINVAL
