@@ -721,22 +721,10 @@ def run_cpu_baseline(w, target_s: float = 10.0, sample: int = 1 << 25):
            "mode": mode, "elements": n, "steps": done, "seconds": el,
            "threads": threads, "affinity_cores": affinity, "cpu_model": _cpu_model(),
            "phases": phases}
-    out["single_thread_c1"] = _cpu_tiny_zero1_single_thread(target_s=2.0)
+    oracle.set_num_threads(1)
+    out["single_thread_c1"] = _cpu_tiny_zero1(target_s=2.0)
+    oracle.set_num_threads(threads)
     return out
-
-
-def _cpu_tiny_zero1_single_thread(target_s: float) -> dict:
-    """_cpu_tiny_zero1 in a child process with OMP_NUM_THREADS=1 (a fresh
-    OpenMP runtime: one thread for certain).  The child runs on the CPU
-    only."""
-    import subprocess
-    env = dict(os.environ, OMP_NUM_THREADS="1", HIP_VISIBLE_DEVICES="", CUDA_VISIBLE_DEVICES="")
-    code = (f"import json, sys; sys.path.insert(0, {ROOT!r}); import bench; "
-            f"print(json.dumps(bench._cpu_tiny_zero1({target_s!r})))")
-    proc = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=300)
-    if proc.returncode != 0:
-        raise RuntimeError(f"single-thread oracle leg failed: {proc.stderr[-2000:]}")
-    return json.loads(proc.stdout.strip().splitlines()[-1])
 
 
 def _cpu_tiny_zero1(target_s: float) -> dict:

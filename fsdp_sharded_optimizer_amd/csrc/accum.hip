@@ -206,11 +206,18 @@ constexpr int kReduceGroups = 2;
 
 // LDS reserved (never touched) per workgroup to cap residency, by chunk
 // dtype and count, as measured on gfx950: a few bf16 chunks want a mild cap
-// (2 chunks: 81 -> 85 %, 4: 82 -> 85 %), 5-8 bf16 chunks over an 842M shard
-// 20 KiB (8 workgroups per CU: 76 -> 79 %); more chunks, or fp32 chunks
-// beyond two, run best uncapped.
-unsigned reduce_lds_reserve(bool bf16, int count) {
-    if (bf16) return count <= 2 ? 8192u : count <= 4 ? 12288u : count <= 8 ? 20480u : 0u;
+// (2 chunks: 81 -> 84 %, 4: 77 -> 83 %), 5-8 bf16 chunks over an 842M shard
+// 20 KiB (8 workgroups per CU: 72 -> 82 %); more chunks, or fp32 chunks
+// beyond two, run best uncapped.  The pass that also forms the norm keeps
+// each wave longer (the binary64 squares and the butterfly at its end) and
+// wants one step more residency: bf16, 2 chunks uncapped (83 %), 4 at 8 KiB
+// (81.5 %), 8 at 14.5 KiB (11 workgroups per CU: 81.1 % against 74.8 % at
+// the plain fold's 20 KiB, within 1 % of the plain fold's best).
+unsigned reduce_lds_reserve(bool bf16, int count, bool norm) {
+    if (bf16) {
+        if (norm) return count <= 2 ? 0u : count <= 4 ? 8192u : count <= 8 ? 14848u : 0u;
+        return count <= 2 ? 8192u : count <= 4 ? 12288u : count <= 8 ? 20480u : 0u;
+    }
     return count <= 2 ? 12288u : 0u;
 }
 
@@ -317,7 +324,7 @@ hipError_t launch_reduce(float* acc, const ChunkBatch& b, int64_t n, float scale
                          hipStream_t stream) {
     const int64_t per = kReducePerBlock;
     const int64_t gsz = BF16 ? 2 : 4;
-    const unsigned lds = VEC ? reduce_lds_reserve(BF16, b.count) : 0u;
+    const unsigned lds = VEC ? reduce_lds_reserve(BF16, b.count, NORM) : 0u;
     for (int64_t off = 0; off < n; off += kLaunchElems) {
         const int64_t m = launch_piece(n, off);
         ChunkBatch p = b;

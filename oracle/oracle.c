@@ -32,6 +32,21 @@
 #define ORC_F32 0
 #define ORC_BF16 1
 
+/* Threads of every OpenMP loop below: the count orc_set_num_threads set,
+ * else OpenMP's default (no result depends on it). */
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+static int g_team = 0;
+static int orc_team(void)
+{
+#ifdef _OPENMP
+    return g_team > 0 ? g_team : omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
 /* ------------------------------------------------------------------ */
 /* bit helpers                                                          */
 /* ------------------------------------------------------------------ */
@@ -62,7 +77,7 @@ float orc_bf16_widen(uint16_t b) { return bits_f32((uint32_t)b << 16); }
 
 void orc_bf16_rne_array(const float* x, uint16_t* out, int64_t n)
 {
-    #pragma omp parallel for schedule(static)
+    #pragma omp parallel for schedule(static) num_threads(orc_team())
     for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_rne(x[i]);
 }
 
@@ -191,7 +206,7 @@ int orc_flat_unpack(const void* flat, int32_t flat_dtype, void* const* dst, cons
 int orc_grad_accum(float* acc, const void* grad, int32_t grad_dtype, int64_t n, int32_t overwrite)
 {
     if (n < 0 || !dtype_ok(grad_dtype)) return -1;
-    #pragma omp parallel for schedule(static)
+    #pragma omp parallel for schedule(static) num_threads(orc_team())
     for (int64_t i = 0; i < n; ++i) {
         float g = load_as_f32(grad, grad_dtype, i);
         if (overwrite) acc[i] = g;
@@ -224,7 +239,7 @@ double orc_grad_norm_sq(const float* acc, int64_t n, double grad_scale)
     int64_t nblocks = (n + ORC_NORM_BLOCK - 1) / ORC_NORM_BLOCK;
     double* part = (double*)malloc((size_t)nblocks * sizeof(double));
     if (!part) return NAN;
-    #pragma omp parallel for schedule(static)
+    #pragma omp parallel for schedule(static) num_threads(orc_team())
     for (int64_t b = 0; b < nblocks; ++b) {
         int64_t lo = b * ORC_NORM_BLOCK;
         int64_t hi = lo + ORC_NORM_BLOCK < n ? lo + ORC_NORM_BLOCK : n;
@@ -345,7 +360,7 @@ int orc_adamw_step(const orc_adamw_hp* hp, float* master, float* exp_avg, float*
         if (!isfinite(S)) return 1;
         coef = orc_clip_coef(*norm_sq, hp->extra_norm_sq, hp->max_norm);
     }
-    #pragma omp parallel for schedule(static)
+    #pragma omp parallel for schedule(static) num_threads(orc_team())
     for (int64_t i = 0; i < n; ++i) {
         float g = grad[i] * s.grad_scale;
         g = g * coef;
@@ -394,7 +409,7 @@ int orc_adamw_step_no_master(const orc_adamw_hp* hp, uint16_t* param_bf16, float
         if (!isfinite(S)) return 1;
         coef = orc_clip_coef(*norm_sq, hp->extra_norm_sq, hp->max_norm);
     }
-    #pragma omp parallel for schedule(static)
+    #pragma omp parallel for schedule(static) num_threads(orc_team())
     for (int64_t i = 0; i < n; ++i) {
         float g = grad[i] * s.grad_scale;
         g = g * coef;
@@ -449,7 +464,7 @@ int orc_adam_update(const orc_adamw_hp* hp, float* exp_avg, float* exp_avg_sq, c
         coef = orc_clip_coef(*norm_sq, hp->extra_norm_sq, hp->max_norm);
     }
     const float neg_step_size = -s.step_size;
-    #pragma omp parallel for schedule(static)
+    #pragma omp parallel for schedule(static) num_threads(orc_team())
     for (int64_t i = 0; i < n; ++i) {
         float g = grad[i] * s.grad_scale;
         g = g * coef;
@@ -590,11 +605,5 @@ int orc_moments_untile(const float* moments, float* exp_avg, float* exp_avg_sq, 
 
 /* Thread count OpenMP will use for the loops above (reported by the
  * CPU-baseline timing). */
-#ifdef _OPENMP
-#include <omp.h>
-int orc_num_threads(void) { return omp_get_max_threads(); }
-void orc_set_num_threads(int n) { if (n > 0) omp_set_num_threads(n); }
-#else
-int orc_num_threads(void) { return 1; }
-void orc_set_num_threads(int n) { (void)n; }
-#endif
+int orc_num_threads(void) { return orc_team(); }
+void orc_set_num_threads(int n) { if (n > 0) g_team = n; }

@@ -136,6 +136,14 @@ def run_shard(w: workloads.Workload, n: int, sampled: bool, full_norm: bool, fus
         s = oracle.adamw_scalars(ohp)
         res = StateCheck(w.beta1, w.lr, w.weight_decay, s.step_size).check(
             gpu, {"p": p_ref, "m": m_ref, "v": v_ref, "b": b_ref}, prev, g2, f"{w.name} t={t}")
+        # the two sides run the same IEEE operations: with the same fp32 clip
+        # coefficient (the norms differ only in their last bits), every
+        # compared element is bit-identical, beyond the tolerance above
+        coef_gpu = oracle.clip_coef(s_gpu, extra, w.max_norm) if clip_norm is not None else 1.0
+        if np.float32(coef_gpu) == np.float32(coef):
+            for k, ref_arr in (("p", p_ref), ("m", m_ref), ("v", v_ref), ("b", b_ref)):
+                if ref_arr is not None:
+                    assert bits_equal(gpu[k], ref_arr), (w.name, t, k, identical_fraction(gpu[k], ref_arr))
         res.update(step=t, coef=coef, norm=math.sqrt(s_gpu + extra), secs=round(time.perf_counter() - t0, 1))
         log(f"  {w.name} n={n} {layout} {res}")
         report.append(res)
@@ -199,6 +207,7 @@ def test_tiny_zero1_rank3_view():
             {"p": p_all[start:end], "m": host(m), "v": host(v)}, {"p": p_ref, "m": m_ref, "v": v_ref},
             prev, g_ref * np.float32(w.grad_scale), f"tiny t={t}")
         log(f"  tiny_zero1 {res}")
+        assert bits_equal(p_all[start:end], p_ref) and bits_equal(host(m), m_ref) and bits_equal(host(v), v_ref)
         assert bits_equal(p_all[:start], p_all0[:start]) and bits_equal(p_all[end:], p_all0[end:])
     assert not host(flat_p)[w.total:].any()
 
@@ -242,6 +251,8 @@ def _unit(w, shapes):
         {"p": host(master), "m": host(m), "v": host(v), "b": host(flat[start:end])},
         {"p": master_ref, "m": m_ref, "v": v_ref, "b": b_ref}, prev, acc_ref * np.float32(w.grad_scale),
         "unit")
+    for got, want in ((master, master_ref), (m, m_ref), (v, v_ref), (flat[start:end], b_ref)):
+        assert bits_equal(host(got), want), "unit step not bit-identical"
     outs = [torch.empty_like(p) for p in params]
     zs.flat_unpack(flat, outs)
     outs_ref = oracle.flat_unpack(flat_ref, oracle.BF16, [p.size for p in params_ref], oracle.BF16)
