@@ -101,19 +101,19 @@ def kernel_digests(lib_path: str = LIB) -> dict:
     return out
 
 
-def load_records() -> list:
-    if not os.path.exists(RECORDS):
+def load_records(path: str = RECORDS) -> list:
+    if not os.path.exists(path):
         return []
-    with open(RECORDS) as f:
+    with open(path) as f:
         return json.load(f)["records"]
 
 
-def traffic(label: str, n: int, digests: dict = None):
+def traffic(label: str, n: int, digests: dict = None, path: str = RECORDS):
     """Calibrated HBM bytes per launch of the kernel bench.py labels
     `label` at shard length n, or None: no record for it, or the code object
     that defines its kernel is not the one the record was taken on."""
     digests = kernel_digests() if digests is None else digests
-    for r in load_records():
+    for r in load_records(path):
         if r["label"] == label and r["shard_elems"] == n:
             if digests.get(r["symbol"]) != r["code_object_sha256"]:
                 return None
@@ -167,7 +167,7 @@ def _mean_for_grid(rows, grid):
     return sum(vals) / len(vals), len(vals)
 
 
-def record(fetch_dir: str, write_dir: str, bench_log: str) -> list:
+def record(fetch_dir: str, write_dir: str, bench_log: str, path: str = RECORDS, lib_path: str = LIB) -> list:
     """Records for the kernels bench.py lists in its `pmc_kernels` (label,
     kernel name as rocprofv3 prints it, shard length, grid size of the
     launch, algorithmic bytes), from the JSON line the counter passes'
@@ -179,7 +179,7 @@ def record(fetch_dir: str, write_dir: str, bench_log: str) -> list:
     write = _counter_rows(write_dir, "WRITE_SIZE")
     fscale = COPY_BYTES / 1024 / _copy_reading(fetch[COPY_KERNEL])
     wscale = COPY_BYTES / 1024 / _copy_reading(write[COPY_KERNEL])
-    digests = kernel_digests()
+    digests = kernel_digests(lib_path)
     if sorted(set(digests.values())) != bench["code_objects_sha256"]:
         raise RuntimeError("the library here is not the build the counter passes ran")
     symbols = list(digests)
@@ -191,7 +191,7 @@ def record(fetch_dir: str, write_dir: str, bench_log: str) -> list:
             raise RuntimeError(f"{name}: {len(hits)} matches among the profiled kernels")
         return hits[0]
 
-    recs = load_records()
+    recs = load_records(path)
     new = []
     for info in bench["pmc_kernels"]:
         label, name, n, grid = info["label"], info["kernel"], info["shard_elems"], info["grid"]
@@ -209,7 +209,7 @@ def record(fetch_dir: str, write_dir: str, bench_log: str) -> list:
         recs = [r for r in recs if not (r["label"] == label and r["shard_elems"] == n)]
         recs.append(rec)
         new.append(rec)
-    with open(RECORDS, "w") as f:
+    with open(path, "w") as f:
         json.dump({"about": "rocprofv3 FETCH_SIZE / WRITE_SIZE per dispatch (KiB) of bench.py's kernels, "
                             "written by bench_pmc.py record; scales from the 4 GiB device copy",
                    "records": recs}, f, indent=1)
