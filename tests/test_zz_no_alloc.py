@@ -93,3 +93,67 @@ def test_noalloc_binding_and_limits():
     # the output overlapping the accumulator: rejected by the shared checks
     assert L.grad_accum_norm_sq_noalloc(acc.data_ptr(), g.data_ptr(), B.ZS_BF16, n, 0, 1.0,
                                         acc.data_ptr() + 16, None) == B.ZS_EOVERLAP
+
+
+def test_noalloc_step_captured_in_a_graph():
+    """The use it is for: a rank's step with no workspace anywhere (two
+    accumulations, the fused last one through grad_accum_norm_sq_noalloc,
+    the clipped tiled AdamW) captured once in a HIP graph after a first
+    eager call on the device, replayed with fresh gradients; every replay
+    bit-identical to the same step run eagerly on a twin state with the
+    workspace entry point, with eager work between replays."""
+    n, M, scale = 300_007, 3, 1 / 24
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(19)
+    master = torch.rand(n, generator=gen, device=dev) * 0.2 - 0.1
+    states = []
+    for _ in range(2):
+        st = torch.empty(zs.state_tiled_numel(n), device=dev)
+        zs.state_tile(master, None, None, st)
+        states.append({"state": st, "b": torch.empty(n, dtype=torch.bfloat16, device=dev),
+                       "acc": torch.empty(n, device=dev), "norm": torch.zeros(1, dtype=torch.float64, device=dev)})
+    graph_side, eager_side = states
+    ws = torch.empty(zs.grad_accum_norm_sq_workspace_bytes(n), dtype=torch.uint8, device=dev)
+    grads = [torch.empty(n, dtype=torch.bfloat16, device=dev) for _ in range(M)]
+    hp = zs.AdamWConfig(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, grad_scale=scale,
+                        max_norm=0.5, extra_norm_sq=0.01, step=3)
+
+    def step(s, noalloc):
+        for k in range(M - 1):
+            zs.grad_accum(s["acc"], grads[k], overwrite=(k == 0))
+        if noalloc:
+            zs.grad_accum_norm_sq_noalloc(s["acc"], grads[M - 1], False, scale, s["norm"])
+        else:
+            zs.grad_accum_norm_sq(s["acc"], grads[M - 1], False, scale, s["norm"], ws)
+        zs.adamw_step_tiled(hp, s["state"], s["acc"], s["b"], norm_sq=s["norm"])
+
+    def fresh(r):
+        for k, g in enumerate(grads):
+            g.copy_((torch.randn(n, generator=gen, device=dev) * (1e-2 * (r + 1) * (k + 1))).to(torch.bfloat16))
+
+    fresh(0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):       # the first call on the device, and torch's warm-up, outside the capture
+        step(graph_side, True)
+        step(eager_side, False)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(graph_side, True)
+    torch.cuda.synchronize()
+    for r in range(1, 4):
+        print(f"noalloc graph replay {r}", flush=True)
+        fresh(r)
+        torch.cuda.synchronize()
+        graph.replay()
+        step(eager_side, False)
+        torch.cuda.synchronize()
+        assert graph_side["norm"].item() == eager_side["norm"].item(), r
+        for k in ("state", "b", "acc"):
+            a, b = graph_side[k], eager_side[k]
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)), (r, k)
+        _ = (eager_side["acc"] * 2).sum().item()   # unrelated eager work between replays
