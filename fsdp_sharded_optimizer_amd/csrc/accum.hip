@@ -205,18 +205,27 @@ constexpr int kReduceBlock = 64;
 constexpr int kReduceGroups = 2;
 
 // LDS reserved (never touched) per workgroup to cap residency, by chunk
-// dtype and count, as measured on gfx950: a few bf16 chunks want a mild cap
-// (2 chunks: 81 -> 84 %, 4: 77 -> 83 %), 5-8 bf16 chunks over an 842M shard
-// 20 KiB (8 workgroups per CU: 72 -> 82 %); more chunks, or fp32 chunks
-// beyond two, run best uncapped.  The pass that also forms the norm keeps
-// each wave longer (the binary64 squares and the butterfly at its end) and
-// wants one step more residency: bf16, 2 chunks uncapped (83 %), 4 at 8 KiB
-// (81.5 %), 8 at 14.5 KiB (11 workgroups per CU: 81.1 % against 74.8 % at
-// the plain fold's 20 KiB, within 1 % of the plain fold's best).
-unsigned reduce_lds_reserve(bool bf16, int count, bool norm) {
+// dtype and count, whether the pass overwrites the accumulator or adds into
+// it (one more stream: the accumulator read), and whether it forms the norm,
+// as measured on gfx950 over the 842M-element shard (% of the HBM peak at the
+// cap taken / uncapped):
+//   bf16 chunks   overwrite          add                overwrite + norm   add + norm
+//   2             8 KiB  84 / 81     12 KiB 83.5 / 77   none 83            8 KiB  81.5 / 78
+//   3-4           12 KiB 83 / 77     16 KiB 83 / 73     8 KiB  81.5 / 78   12 KiB 83 / 73
+//   5-8           20 KiB 82 / 72     20 KiB 80 / -      14.5 KiB 81 / 72   18 KiB 81 / -
+// (14.5 KiB is 11 workgroups per CU, 18 KiB 9).  The pass that forms the
+// norm keeps each wave longer (the binary64 squares and the butterfly at
+// its end) and mostly wants one step more residency.  More chunks, or fp32
+// chunks beyond two, run best uncapped.
+unsigned reduce_lds_reserve(bool bf16, int count, bool overwrite, bool norm) {
     if (bf16) {
-        if (norm) return count <= 2 ? 0u : count <= 4 ? 8192u : count <= 8 ? 14848u : 0u;
-        return count <= 2 ? 8192u : count <= 4 ? 12288u : count <= 8 ? 20480u : 0u;
+        if (count > 8) return 0u;
+        const int c = count <= 2 ? 0 : count <= 4 ? 1 : 2;
+        static constexpr unsigned kCap[2][2][3] = {
+            {{12288u, 16384u, 20480u}, {8192u, 12288u, 18176u}},   // add: plain, norm
+            {{8192u, 12288u, 20480u}, {0u, 8192u, 14848u}},        // overwrite: plain, norm
+        };
+        return kCap[overwrite ? 1 : 0][norm ? 1 : 0][c];
     }
     return count <= 2 ? 12288u : 0u;
 }
@@ -324,7 +333,7 @@ hipError_t launch_reduce(float* acc, const ChunkBatch& b, int64_t n, float scale
                          hipStream_t stream) {
     const int64_t per = kReducePerBlock;
     const int64_t gsz = BF16 ? 2 : 4;
-    const unsigned lds = VEC ? reduce_lds_reserve(BF16, b.count, NORM) : 0u;
+    const unsigned lds = VEC ? reduce_lds_reserve(BF16, b.count, OVERWRITE, NORM) : 0u;
     for (int64_t off = 0; off < n; off += kLaunchElems) {
         const int64_t m = launch_piece(n, off);
         ChunkBatch p = b;

@@ -12,6 +12,8 @@
  * generator in this file and feed both sides.  The GPU norm must be within
  * 1e-5 of the oracle's; the step, handed the oracle's norm, must be
  * bit-identical to the oracle's (accumulator, master, moments, bf16 output).
+ * The same three accumulations once more with grad_accum_norm_sq_noalloc for
+ * the last (no workspace) must give the same accumulator and norm bit for bit.
  * Prints "c gpu step: ok" and exits 0, else the number of the failed check.
  */
 #include <math.h>
@@ -75,7 +77,8 @@ int main(void)
     /* device buffers */
     float *d_master, *d_state, *d_acc, *d_p, *d_m, *d_v;
     uint16_t *d_g, *d_b;
-    double *d_norm, *d_norm_ref;
+    double *d_norm, *d_norm_ref, *d_norm2;
+    float* d_acc2;
     void* d_ws;
     const int64_t ws_bytes = grad_accum_norm_sq_workspace_bytes(n);
     const int64_t st = state_tiled_numel(n);
@@ -90,6 +93,8 @@ int main(void)
     HIPOK(hipMalloc((void**)&d_b, sizeof(uint16_t) * n), 3);
     HIPOK(hipMalloc((void**)&d_norm, sizeof(double)), 3);
     HIPOK(hipMalloc((void**)&d_norm_ref, sizeof(double)), 3);
+    HIPOK(hipMalloc((void**)&d_norm2, sizeof(double)), 3);
+    HIPOK(hipMalloc((void**)&d_acc2, sizeof(float) * n), 3);
     HIPOK(hipMalloc(&d_ws, (size_t)ws_bytes), 3);
     HIPOK(hipMemcpy(d_master, p_ref, sizeof(float) * n, hipMemcpyHostToDevice), 4);
     HIPOK(hipMemcpy(d_g, g, sizeof(uint16_t) * n * M, hipMemcpyHostToDevice), 4);
@@ -110,6 +115,19 @@ int main(void)
     HIPOK(hipMemcpy(back, d_acc, sizeof(float) * n, hipMemcpyDeviceToHost), 10);
     CHECK(memcmp(back, acc_ref, sizeof(float) * n) == 0, 10);
 
+    /* the same accumulations with the no-alloc form for the last micro-batch */
+    for (int k = 0; k < M - 1; ++k)
+        CHECK(grad_accum(d_acc2, d_g + (size_t)k * n, ZS_BF16, n, k == 0, NULL) == ZS_OK, 20);
+    CHECK(grad_accum_norm_sq_noalloc(d_acc2, d_g + (size_t)(M - 1) * n, ZS_BF16, n, 0, scale, d_norm2, NULL)
+          == ZS_OK, 20);
+    CHECK(grad_accum_norm_sq_noalloc(d_acc2, d_g, ZS_BF16, ZS_NOALLOC_MAX_ELEMS + 1, 0, scale, d_norm2, NULL)
+          == ZS_EINVAL, 20);
+    double S_noalloc = 0.0;
+    HIPOK(hipMemcpy(&S_noalloc, d_norm2, sizeof(double), hipMemcpyDeviceToHost), 21);
+    CHECK(memcmp(&S_noalloc, &S_gpu, sizeof(double)) == 0, 21);
+    HIPOK(hipMemcpy(back, d_acc2, sizeof(float) * n, hipMemcpyDeviceToHost), 22);
+    CHECK(memcmp(back, acc_ref, sizeof(float) * n) == 0, 22);
+
     const double max_norm = 0.5 * sqrt(S), extra = 0.2 * S;   /* the clip applies */
     zs_adamw hp = {3e-4, 0.9, 0.95, 1e-8, 0.1, scale, max_norm, extra, 1};
     orc_adamw_hp ohp = {3e-4, 0.9, 0.95, 1e-8, 0.1, scale, max_norm, extra, 1};
@@ -129,7 +147,7 @@ int main(void)
     CHECK(zs_last_hip_error() == 0, 19);
 
     hipFree(d_master); hipFree(d_state); hipFree(d_acc); hipFree(d_p); hipFree(d_m); hipFree(d_v);
-    hipFree(d_g); hipFree(d_b); hipFree(d_norm); hipFree(d_norm_ref); hipFree(d_ws);
+    hipFree(d_g); hipFree(d_b); hipFree(d_norm); hipFree(d_norm_ref); hipFree(d_ws); hipFree(d_norm2); hipFree(d_acc2);
     free(p_ref); free(m_ref); free(v_ref); free(acc_ref); free(b_ref); free(g); free(back); free(back16);
     printf("c gpu step: ok\n");
     return 0;
