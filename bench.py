@@ -5,20 +5,23 @@
 
 One step is one pass of the whole hot path over one batch of synthetic
 input, on one rank's real-size shard (inputs resident in HBM):
-  grad_accum over every micro-batch but the last (bf16 -> fp32),
-  grad_accum_norm_sq for the last one (the accumulation and this shard's
-  squared norm in one pass; the norm is formed every step: it feeds the clip
-  when the workload clips and the non-finite skip always), and the fused
-  AdamW step with the bf16 re-cast, on the optimizer state held in the
-  library's tiled layout (adamw_step_tiled, as ShardOptimizer holds it by
-  default).  The same AdamW step on three separate state buffers
-  (adamw_step) is timed after the step on the same evolved state.
+  grad_accum over every micro-batch but the last (bf16 -> fp32);
+  grad_sum_norm_sq: this shard's squared norm of the last micro-batch's sum
+  (accumulator + last gradient, read, not stored; the norm is formed every
+  step: it feeds the clip when the workload clips and the non-finite skip
+  always); and adamw_step_tiled_sum: the fused AdamW step with the bf16
+  re-cast on the optimizer state held in the library's tiled layout,
+  forming the same sum again as it reads it (ShardOptimizer's schedule for
+  its default layout).  The same step as two calls that store the sum first
+  (grad_accum_norm_sq, then adamw_step_tiled) is timed after it, and the
+  AdamW step on three separate state buffers (adamw_step) after that.
 The shard range is host arithmetic done once at set-up.  Default workload:
 the Llama-7B-shaped buffer over 8 ranks, one 842,301,952-element shard,
-8 micro-batches.
+8 micro-batches; a second shard (the 70B ZeRO-3 one) is timed in the same
+process.
 
 Prints ONE JSON line: whole-step throughput (shard elements per second),
-the roofline of the dominant kernel (adamw_step_tiled, timed live with HIP
+the roofline of the dominant kernel (the step's AdamW, timed live with HIP
 events on the launch stream) and the CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
@@ -40,8 +43,13 @@ HBM_PEAK_GBPS = 8000.0   # MI355X published HBM3E bandwidth
 # them (bench_pmc.py keys each record to the gfx950 code object that
 # defines the kernel; a rebuilt kernel reports null until the counters are
 # taken again).
-K_ADAMW_TILED = "zs::(anonymous namespace)::adamw_kernel<4, 1, 64, false, true, true>"
-K_ADAMW_SPLIT = "zs::(anonymous namespace)::adamw_kernel<4, 1, 64, false, false, true>"
+K_ADAMW_TILED = "zs::(anonymous namespace)::adamw_kernel<4, 1, 64, false, true, true, 0>"
+K_ADAMW_SPLIT = "zs::(anonymous namespace)::adamw_kernel<4, 1, 64, false, false, true, 0>"
+# the step's AdamW on the last micro-batch's sum: bf16 gradient alone (1) or onto the accumulator (2)
+K_ADAMW_SUM_BF16 = "zs::(anonymous namespace)::adamw_kernel<4, 1, 64, false, true, true, 1>"
+K_ADAMW_SUM_ACC_BF16 = "zs::(anonymous namespace)::adamw_kernel<4, 1, 64, false, true, true, 2>"
+K_SUM_NORM_ADD = "zs::(anonymous namespace)::sum_norm_kernel<1, 1, 1, true, true, false>"
+K_SUM_NORM_FIRST = "zs::(anonymous namespace)::sum_norm_kernel<4, 1, 1, true, true, true>"
 K_ACCUM_FIRST = "zs::(anonymous namespace)::accum_kernel<1, 64, true, true, true, false>"
 K_ACCUM_ADD = "zs::(anonymous namespace)::accum_kernel<1, 64, true, true, false, false>"
 K_ACCUM_NORM_ADD = "zs::(anonymous namespace)::accum_kernel<1, 64, true, true, false, true>"
@@ -129,37 +137,52 @@ def timing_events() -> str:
 
 def step_bytes_per_elem(w) -> dict:
     """Algorithmic HBM bytes per shard element of each kernel of one step
-    (the fused norm's binary64 partials, 8 B per 256 elements, come on top
-    of the last micro-batch's bytes: 0.03 B per element)."""
+    (the norm's binary64 partials, 8 B per 256 elements, come on top of the
+    last micro-batch's bytes: 0.03 B per element).  The step folds the last
+    micro-batch into AdamW: its norm pass reads the accumulator and the last
+    gradient (the gradient alone for a single micro-batch) and AdamW reads
+    them again instead of one stored sum.  The *_two_call entries are the
+    same step with the sum stored first (grad_accum_norm_sq, then
+    adamw_step_tiled on it)."""
     g = 2 if w.grad_dtype == "bf16" else 4
     accum_first = g + 4
     accum_next = g + 8
+    M = w.micro_batches
     adamw = 28 + (2 if w.bf16_param else 0)
-    # the last micro-batch also forms the norm, without another read
-    accum = accum_first + (w.micro_batches - 1) * accum_next
-    last = accum_first if w.micro_batches == 1 else accum_next
+    acc_read = 4 if M > 1 else 0
+    before_last = 0 if M == 1 else accum_first + (M - 2) * accum_next
+    norm_last = g + acc_read
+    adamw_sum = adamw - 4 + g + acc_read
+    last_two_call = accum_first if M == 1 else accum_next
     return {"grad_accum_first": accum_first, "grad_accum_next": accum_next,
-            "grad_accum_norm_sq_last": last, "adamw_step": adamw, "step": accum + adamw}
+            "grad_accum_all_but_last": before_last, "grad_sum_norm_sq_last": norm_last,
+            "adamw_step_sum": adamw_sum, "step": before_last + norm_last + adamw_sum,
+            "grad_accum_norm_sq_last": last_two_call, "adamw_step": adamw,
+            "step_two_call": before_last + last_two_call + adamw}
 
 
 def fused_norm_partials(w, n: int) -> int:
-    """Binary64 partials grad_accum_norm_sq writes for the last micro-batch:
-    one per 256 elements, or per 1024 when it overwrites from a bf16
-    gradient (a single micro-batch)."""
+    """Binary64 partials the last micro-batch's norm pass writes (either
+    schedule): one per 256 elements, or per 1024 when the step has a single
+    bf16 micro-batch."""
     per = 1024 if (w.micro_batches == 1 and w.grad_dtype == "bf16") else 256
     return (n + per - 1) // per
 
 
-def step_kernel_rates(bpe: dict, n: int, r: dict) -> dict:
+def step_kernel_rates(bpe: dict, n: int, r: dict, two_call: bool = False) -> dict:
     """Algorithmic bandwidth of each part of the timed step (HIP events on
     the launch stream): the accumulations of every micro-batch but the last
     (one overwriting launch and the rest accumulating, by time the largest
-    share of the step), the last micro-batch with the norm, and AdamW."""
-    parts = {
-        "grad_accum_all_but_last": (bpe["step"] - bpe["grad_accum_norm_sq_last"] - bpe["adamw_step"], r["accum_ms"]),
-        "grad_accum_norm_sq_last": (bpe["grad_accum_norm_sq_last"], r["last_ms"]),
-        "adamw_step_tiled": (bpe["adamw_step"], r["adamw_ms"]),
-    }
+    share of the step), the last micro-batch's norm (with its accumulation,
+    two_call) and AdamW."""
+    if two_call:
+        parts = {"grad_accum_all_but_last": (bpe["grad_accum_all_but_last"], r["accum_ms"]),
+                 "grad_accum_norm_sq_last": (bpe["grad_accum_norm_sq_last"], r["last_ms"]),
+                 "adamw_step_tiled": (bpe["adamw_step"], r["adamw_ms"])}
+    else:
+        parts = {"grad_accum_all_but_last": (bpe["grad_accum_all_but_last"], r["accum_ms"]),
+                 "grad_sum_norm_sq_last": (bpe["grad_sum_norm_sq_last"], r["last_ms"]),
+                 "adamw_step_tiled_sum": (bpe["adamw_step_sum"], r["adamw_ms"])}
     out = {}
     for name, (b, ms) in parts.items():
         if b == 0:
@@ -237,10 +260,31 @@ class StepRig:
                               extra_norm_sq=workloads.other_ranks_norm_sq(w, 1, self.n), step=t)
 
     def step(self, t: int, ev=None):
-        """The pages' schedule: one accumulation per micro-batch as its
-        gradient arrives, the last forming the norm, then AdamW (tiled
-        state, bf16 re-cast, clip when the workload clips).  ev: four events
+        """The step as ShardOptimizer runs it on its tiled state: one
+        accumulation per micro-batch as its gradient arrives, but the last;
+        the last one's norm of the sum (not stored), then AdamW on that sum
+        (bf16 re-cast, clip when the workload clips).  ev: four events
         recorded around the parts."""
+        import fsdp_sharded_optimizer_amd as zs
+        last = len(self.grads) - 1
+        if ev:
+            ev[0].record()
+        for mb, g in enumerate(self.grads[:last]):
+            zs.grad_accum(self.acc, g, overwrite=(mb == 0))
+        if ev:
+            ev[1].record()
+        acc = self.acc if last > 0 else None
+        zs.grad_sum_norm_sq(acc, self.grads[last], last == 0, self.w.grad_scale, self.norm, self.ws)
+        if ev:
+            ev[2].record()
+        zs.adamw_step_tiled_sum(self.hp(t), self.state, acc, self.grads[last], self.param, norm_sq=self.norm)
+        if ev:
+            ev[3].record()
+
+    def two_call_step(self, t: int, ev=None):
+        """The same step with the last micro-batch's sum stored first: the
+        accumulation forming the norm in the same pass, then AdamW reading
+        the stored sum (the same results, bit for bit)."""
         import fsdp_sharded_optimizer_amd as zs
         last = len(self.grads) - 1
         if ev:
@@ -260,10 +304,11 @@ class StepRig:
         """The same step with the micro-batch gradients staged k at a time in
         device memory: each group of k is summed in one pass
         (grad_reduce_chunks, the same left fold bit for bit), the last group
-        forming the norm (grad_reduce_chunks_norm_sq); k = 1 is step()."""
+        forming the norm (grad_reduce_chunks_norm_sq), then AdamW on the
+        stored sum; k = 1 is two_call_step()."""
         import fsdp_sharded_optimizer_amd as zs
         if k == 1:
-            return self.step(t)
+            return self.two_call_step(t)
         groups = [self.grads[i:i + k] for i in range(0, len(self.grads), k)]
         for j, grp in enumerate(groups[:-1]):
             zs.grad_reduce_chunks(self.acc, grp, j == 0)
@@ -271,22 +316,23 @@ class StepRig:
                                       self.ws)
         zs.adamw_step_tiled(self.hp(t), self.state, self.acc, self.param, norm_sq=self.norm)
 
-    def time_steps(self, steps: int, warmup: int) -> dict:
+    def time_steps(self, steps: int, warmup: int, two_call: bool = False) -> dict:
         """W untimed steps, then K steps bracketed by synchronisations (wall
         clock), each with HIP events around its parts on the launch stream."""
         import math
         import torch
         ev = DeviceEvent
+        run = self.two_call_step if two_call else self.step
         for _ in range(warmup):
             self.t += 1
-            self.step(self.t)
+            run(self.t)
         torch.cuda.synchronize()
         timing = []
         t0 = time.perf_counter()
         for _ in range(steps):
             self.t += 1
             e = [ev() for _ in range(4)]
-            self.step(self.t, e)
+            run(self.t, e)
             timing.append(e)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
@@ -341,6 +387,10 @@ def run_gpu(w, steps: int, warmup: int):
         rig.step(rig.t + 1)
     r["graph_ms"] = timed(graph.replay, steps)
     del graph
+
+    # outside the step: the same step with the last micro-batch's sum stored
+    # first (grad_accum_norm_sq, then adamw_step_tiled on the stored sum)
+    r["two_call"] = rig.time_steps(steps, 1, two_call=True)
 
     # outside the step: the same AdamW step on three separate state buffers
     # (adamw_step), loaded with the tiled state as the timed steps left it so
@@ -441,6 +491,7 @@ def run_step_leg(rig: StepRig, steps: int, warmup: int) -> dict:
     torch.cuda.synchronize()
     r = rig.time_steps(steps, warmup)
     r["n"] = rig.n
+    r["two_call"] = rig.time_steps(steps, 1, two_call=True)
     return r
 
 
@@ -705,7 +756,7 @@ def run_cpu_baseline(w, target_s: float = 10.0, sample: int = 1 << 25):
             break
     del master, m, v, bf, grads, acc
     bpe = step_bytes_per_elem(w)
-    accum_bytes = bpe["step"] - bpe["adamw_step"]   # every micro-batch's accumulation
+    accum_bytes = bpe["step_two_call"] - bpe["adamw_step"]   # every micro-batch's accumulation, stored
     phases = {
         "accumulate": {"ms_per_step": phase["accumulate"] * 1e3 / done,
                        "gbps": accum_bytes * n * done / phase["accumulate"] / 1e9},
@@ -807,8 +858,8 @@ def main():
         zero1 = run_zero1_flow(w, workloads.LLAMA7B)
     bpe = step_bytes_per_elem(w)
     ms_per_step = r["ms_per_step"]
-    adamw_bytes = bpe["adamw_step"] * n
-    achieved = adamw_bytes / (r["adamw_ms"] * 1e-3) / 1e9
+    tc = r["two_call"]
+    adamw_bytes = bpe["adamw_step"] * n            # the AdamW step on a stored gradient, either layout
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host cores ...")
@@ -822,19 +873,59 @@ def main():
         return {"label": label, "kernel": kernel, "shard_elems": nn, "algorithmic_bytes": nbytes,
                 "grid": -(-nn // per_wg) * 64}
 
-    pmc = [entry("adamw_step_tiled", K_ADAMW_TILED, n, adamw_bytes),
-           entry("adamw_step", K_ADAMW_SPLIT, n, adamw_bytes)]
-    if w.micro_batches > 2 and w.grad_dtype == "bf16":
+    def sum_entries(wl, nn):
+        """The step's last micro-batch and AdamW (bf16 gradients)."""
+        b = step_bytes_per_elem(wl)
+        single = wl.micro_batches == 1
+        return [entry("adamw_step_tiled_sum", K_ADAMW_SUM_BF16 if single else K_ADAMW_SUM_ACC_BF16, nn,
+                      b["adamw_step_sum"] * nn),
+                entry("grad_sum_norm_sq_last", K_SUM_NORM_FIRST if single else K_SUM_NORM_ADD, nn,
+                      b["grad_sum_norm_sq_last"] * nn + 8 * fused_norm_partials(wl, nn), 1024 if single else 256)]
+
+    def two_call_entries(wl, nn):
+        b = step_bytes_per_elem(wl)
+        single = wl.micro_batches == 1
+        return [entry("adamw_step_tiled", K_ADAMW_TILED, nn, b["adamw_step"] * nn),
+                entry("grad_accum_norm_sq_last", K_ACCUM_NORM_FIRST if single else K_ACCUM_NORM_ADD, nn,
+                      b["grad_accum_norm_sq_last"] * nn + 8 * fused_norm_partials(wl, nn), 1024 if single else 256)]
+
+    bf16_grads = w.grad_dtype == "bf16"
+    pmc = [entry("adamw_step", K_ADAMW_SPLIT, n, adamw_bytes)]
+    if bf16_grads:
+        pmc += sum_entries(w, n) + two_call_entries(w, n)
+    if w.micro_batches > 2 and bf16_grads:
         pmc += [entry("grad_accum_first", K_ACCUM_FIRST, n, 6 * n),
-                entry("grad_accum_add", K_ACCUM_ADD, n, 10 * n),
-                entry("grad_accum_norm_sq_last", K_ACCUM_NORM_ADD, n, 10 * n + 8 * fused_norm_partials(w, n))]
+                entry("grad_accum_add", K_ACCUM_ADD, n, 10 * n)]
 
     def roofline(wl, rr, nn):
-        b = step_bytes_per_elem(wl)["adamw_step"] * nn
+        """The step's AdamW, on the last micro-batch's sum."""
+        b = step_bytes_per_elem(wl)["adamw_step_sum"] * nn
         ach = b / (rr["adamw_ms"] * 1e-3) / 1e9
-        return {"kernel": "adamw_step_tiled", "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS, "traffic": traffic_of("adamw_step_tiled", nn, digests),
-                "traffic_unit": "bytes/launch", "algorithmic_bytes": b, "launch_ms": rr["adamw_ms"]}
+        return {"kernel": "adamw_step_tiled_sum", "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
+                "traffic": traffic_of("adamw_step_tiled_sum", nn, digests), "traffic_unit": "bytes/launch",
+                "algorithmic_bytes": b, "launch_ms": rr["adamw_ms"]}
+
+    def with_traffic(kernels: dict, nn: int, wl) -> dict:
+        """Measured bytes per launch next to the algorithmic ones, for the
+        parts that have records."""
+        b = step_bytes_per_elem(wl)
+        parts = {"grad_sum_norm_sq_last": b["grad_sum_norm_sq_last"] * nn + 8 * fused_norm_partials(wl, nn),
+                 "grad_accum_norm_sq_last": b["grad_accum_norm_sq_last"] * nn + 8 * fused_norm_partials(wl, nn),
+                 "adamw_step_tiled_sum": b["adamw_step_sum"] * nn, "adamw_step_tiled": b["adamw_step"] * nn}
+        for name, nbytes in parts.items():
+            if name in kernels:
+                kernels[name]["algorithmic_bytes"] = nbytes
+                kernels[name]["traffic"] = traffic_of(name, nn, digests) if wl.grad_dtype == "bf16" else None
+        return kernels
+
+    def two_call_report(wl, rr, nn):
+        b = step_bytes_per_elem(wl)
+        t = rr["two_call"]
+        return {"ms_per_step": t["ms_per_step"], "elements_per_s": nn / (t["ms_per_step"] * 1e-3),
+                "bytes_per_elem": b["step_two_call"], "step_kernels": with_traffic(
+                    step_kernel_rates(b, nn, t, two_call=True), nn, wl),
+                "one_pass_speedup": t["ms_per_step"] / rr["ms_per_step"]}
 
     out = {
         "metric": "AdamW shard step: elements/s and achieved HBM GB/s (% of peak) per GPU",
@@ -855,13 +946,14 @@ def main():
         "graph_ms_per_step": r["graph_ms"],
         "step_hbm_gbps": step_gbps,
         "step_hbm_frac": step_gbps / HBM_PEAK_GBPS,
-        "kernels_ms": {"grad_accum_all_but_last": r["accum_ms"], "grad_accum_norm_sq_last": r["last_ms"],
-                       "adamw_step_tiled": r["adamw_ms"]},
-        "step_kernels": step_kernel_rates(bpe, n, r),
+        "kernels_ms": {"grad_accum_all_but_last": r["accum_ms"], "grad_sum_norm_sq_last": r["last_ms"],
+                       "adamw_step_tiled_sum": r["adamw_ms"]},
+        "step_kernels": with_traffic(step_kernel_rates(bpe, n, r), n, w),
         "bytes_per_elem": bpe,
+        "step_two_call": two_call_report(w, r, n),
         "device_copy_gbps": r["copy_gbps"],
         "timing_events": timing_events(),
-        "adamw_traffic_ceiling": ceiling_report(r["ceiling_ms"], adamw_bytes, r["adamw_ms"]),
+        "adamw_traffic_ceiling": ceiling_report(r["ceiling_ms"], adamw_bytes, tc["adamw_ms"]),
         "roofline": roofline(w, r, n),
         "adamw_step_split": {
             "ms": r["split_ms"], "bytes_per_elem": bpe["adamw_step"],
@@ -886,33 +978,25 @@ def main():
             **rate((r["chunks"] * (2 if w.grad_dtype == "bf16" else 4) + 4) * n, r["reduce_norm_ms"])},
         "staging_curve": r["staging_curve"],
     }
-    if w.micro_batches > 2 and w.grad_dtype == "bf16":
-        # measured bytes of the step's accumulation parts, from the per-kernel records
-        t_first, t_add, t_last = (traffic_of(k, n, digests) for k in
-                                  ("grad_accum_first", "grad_accum_add", "grad_accum_norm_sq_last"))
+    if w.micro_batches > 2 and bf16_grads:
+        # measured bytes of the accumulations before the last, from the per-kernel records
+        t_first, t_add = (traffic_of(k, n, digests) for k in ("grad_accum_first", "grad_accum_add"))
         sk = out["step_kernels"]
-        sk["grad_accum_all_but_last"]["algorithmic_bytes"] = (6 + 10 * (w.micro_batches - 2)) * n
+        sk["grad_accum_all_but_last"]["algorithmic_bytes"] = bpe["grad_accum_all_but_last"] * n
         sk["grad_accum_all_but_last"]["traffic"] = (None if t_first is None or t_add is None
                                                     else t_first + (w.micro_batches - 2) * t_add)
-        sk["grad_accum_norm_sq_last"]["algorithmic_bytes"] = pmc[-1]["algorithmic_bytes"]
-        sk["grad_accum_norm_sq_last"]["traffic"] = t_last
     if second is not None:
         w2, r2 = second
         n2 = r2["n"]
         bpe2 = step_bytes_per_elem(w2)
-        last_bytes = bpe2["grad_accum_norm_sq_last"] * n2 + 8 * fused_norm_partials(w2, n2)
-        first_q4 = w2.micro_batches == 1 and w2.grad_dtype == "bf16"   # four groups per lane
-        pmc += [entry("adamw_step_tiled", K_ADAMW_TILED, n2, bpe2["adamw_step"] * n2),
-                entry("grad_accum_norm_sq_last", K_ACCUM_NORM_FIRST if first_q4 else K_ACCUM_NORM_ADD, n2,
-                      last_bytes, 1024 if first_q4 else 256)]
+        if w2.grad_dtype == "bf16":
+            pmc += sum_entries(w2, n2) + two_call_entries(w2, n2)
         out["roofline_second"] = {"workload": w2.name, **roofline(w2, r2, n2)}
-        sk2 = step_kernel_rates(bpe2, n2, r2)
-        sk2["grad_accum_norm_sq_last"]["algorithmic_bytes"] = last_bytes
-        sk2["grad_accum_norm_sq_last"]["traffic"] = traffic_of("grad_accum_norm_sq_last", n2, digests)
         out["second_workload"] = {
             "workload": w2.name, "shard_elems": n2, "micro_batches": w2.micro_batches, "clip": w2.max_norm > 0,
             "ms_per_step": r2["ms_per_step"], "elements_per_s": n2 / (r2["ms_per_step"] * 1e-3),
-            "bytes_per_elem": bpe2, "step_kernels": sk2}
+            "bytes_per_elem": bpe2, "step_kernels": with_traffic(step_kernel_rates(bpe2, n2, r2), n2, w2),
+            "step_two_call": two_call_report(w2, r2, n2)}
     out["pmc_kernels"] = pmc
     out["code_objects_sha256"] = sorted(set(digests.values()))
     print(json.dumps(out), flush=True)

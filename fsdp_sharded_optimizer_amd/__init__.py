@@ -11,6 +11,7 @@ The Python names mirror the C ABI in include/zshard.h:
     grad_accum_norm_sq(acc, grad, overwrite, grad_scale, out, workspace=None)
     grad_accum_norm_sq_noalloc(acc, grad, overwrite, grad_scale, out)   partials in a static device scratch
     grad_norm_sq(grad, grad_scale, out, workspace=None)
+    grad_sum_norm_sq(acc, grad, overwrite, grad_scale, out, workspace=None)   grad_accum_norm_sq's norm, no store
     adamw_step(hp, master, exp_avg, exp_avg_sq, grad, param_bf16=None, norm_sq=None)
     adamw_scalars(hp) / scalars_bytes(hp)       the step's binary32 scalars, on the host
     adamw_step_dev(scalars_dev, master, exp_avg, exp_avg_sq, grad, param_bf16=None, norm_sq=None)
@@ -22,6 +23,8 @@ The Python names mirror the C ABI in include/zshard.h:
     state_untile(state, master, exp_avg, exp_avg_sq, n=None)   tiled -> split (None: skipped)
     adamw_step_tiled(hp, state, grad, param_bf16=None, norm_sq=None)
     adamw_step_tiled_dev(scalars_dev, state, grad, param_bf16=None, norm_sq=None)
+    adamw_step_tiled_sum(hp, state, acc, grad, param_bf16=None, norm_sq=None)   gradient fl(acc + widen(grad))
+    adamw_step_tiled_sum_dev(scalars_dev, state, acc, grad, param_bf16=None, norm_sq=None)
     moments_tiled_numel(n) / moments_tile(exp_avg, exp_avg_sq, moments, n=None) / moments_untile(...)
     adam_update_tiled(hp, moments, grad, update, norm_sq=None)
     adamw_step_no_master_tiled(hp, param_bf16, moments, grad, norm_sq=None)
@@ -46,6 +49,8 @@ from ._binding import (  # noqa: F401
     adamw_step_no_master_tiled,
     adamw_step_tiled,
     adamw_step_tiled_dev,
+    adamw_step_tiled_sum,
+    adamw_step_tiled_sum_dev,
     flat_apply_update,
     flat_pack,
     flat_unpack,
@@ -58,6 +63,7 @@ from ._binding import (  # noqa: F401
     grad_reduce_chunks_norm_sq_workspace_bytes,
     grad_norm_sq,
     grad_norm_sq_workspace_bytes,
+    grad_sum_norm_sq,
     lib,
     moments_tile,
     moments_tiled_numel,

@@ -33,7 +33,8 @@ EXPORTS = (
     "flat_apply_update", "state_tiled_numel", "state_tile", "state_untile", "adamw_step_tiled",
     "adamw_step_tiled_dev", "moments_tiled_numel", "moments_tile", "moments_untile", "adam_update_tiled",
     "adamw_step_no_master_tiled", "grad_reduce_chunks_norm_sq_workspace_bytes", "grad_reduce_chunks_norm_sq",
-    "grad_accum_norm_sq_noalloc", "zs_strerror", "zs_last_hip_error",
+    "grad_accum_norm_sq_noalloc", "grad_sum_norm_sq", "adamw_step_tiled_sum", "adamw_step_tiled_sum_dev",
+    "zs_strerror", "zs_last_hip_error",
 )
 NOALLOC_MAX_ELEMS = 2_146_959_360   # ZS_NOALLOC_MAX_ELEMS
 
@@ -130,6 +131,12 @@ def lib() -> ctypes.CDLL:
         L.grad_accum_norm_sq.restype = I32
         L.grad_accum_norm_sq_noalloc.argtypes = [P, P, I32, I64, I32, D, P, P]
         L.grad_accum_norm_sq_noalloc.restype = I32
+        L.grad_sum_norm_sq.argtypes = [P, P, I32, I64, I32, D, P, P, I64, P]
+        L.grad_sum_norm_sq.restype = I32
+        L.adamw_step_tiled_sum.argtypes = [ctypes.POINTER(AdamW), P, P, P, I32, P, I64, P, P]
+        L.adamw_step_tiled_sum.restype = I32
+        L.adamw_step_tiled_sum_dev.argtypes = [P, P, P, P, I32, P, I64, P, P]
+        L.adamw_step_tiled_sum_dev.restype = I32
         L.adamw_step.argtypes = [ctypes.POINTER(AdamW), P, P, P, P, P, I64, P, P]
         L.adamw_step.restype = I32
         L.adamw_scalars.argtypes = [ctypes.POINTER(AdamW), ctypes.POINTER(AdamWScalars)]
@@ -402,6 +409,27 @@ def grad_accum_norm_sq_noalloc(acc: torch.Tensor, grad: torch.Tensor, overwrite:
     return out
 
 
+def grad_sum_norm_sq(acc: Optional[torch.Tensor], grad: torch.Tensor, overwrite: bool, grad_scale: float,
+                     out: torch.Tensor, workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """out[0] = the squared norm grad_accum_norm_sq(acc, grad, overwrite, ...)
+    would form, bit for bit, without writing acc (not read when overwrite)."""
+    n = grad.numel()
+    if overwrite:
+        acc = None
+    elif acc is None or acc.numel() != n:
+        raise ValueError("grad_sum_norm_sq: acc must hold the gradient's numel unless overwrite")
+    need = grad_accum_norm_sq_workspace_bytes(n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=grad.device)
+    if out.dtype != torch.float64 or out.numel() < 1:
+        raise TypeError("grad_sum_norm_sq: out must hold one float64")
+    _check("grad_sum_norm_sq", lib().grad_sum_norm_sq(
+        _dev(acc, "acc", torch.float32), _dev(grad, "grad"), _dtype_code(grad), n, 1 if overwrite else 0,
+        float(grad_scale), _dev(out, "out"), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
 def adamw_step(hp: AdamWConfig, master: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor,
                grad: torch.Tensor, param_bf16: Optional[torch.Tensor] = None,
                norm_sq: Optional[torch.Tensor] = None, stream=None) -> None:
@@ -561,6 +589,45 @@ def adamw_step_tiled_dev(scalars_dev: torch.Tensor, state: torch.Tensor, grad: t
         _dev(scalars_dev, "scalars_dev"), _state_buffer(state, n, "adamw_step_tiled_dev"),
         _dev(grad, "grad", torch.float32), _dev(param_bf16, "param_bf16", torch.bfloat16), n,
         _norm(norm_sq, "adamw_step_tiled_dev"), _stream(stream)))
+
+
+def _sum_args(acc: Optional[torch.Tensor], grad: torch.Tensor, param_bf16: Optional[torch.Tensor], fn: str):
+    n = grad.numel()
+    if acc is not None and acc.numel() != n:
+        raise ValueError(f"{fn}: acc size mismatch")
+    if param_bf16 is not None and param_bf16.numel() != n:
+        raise ValueError(f"{fn}: param_bf16 size mismatch")
+    return n
+
+
+def adamw_step_tiled_sum(hp: AdamWConfig, state: torch.Tensor, acc: Optional[torch.Tensor], grad: torch.Tensor,
+                         param_bf16: Optional[torch.Tensor] = None, norm_sq: Optional[torch.Tensor] = None,
+                         stream=None) -> None:
+    """adamw_step_tiled on the last micro-batch's sum fl(acc + widen(grad))
+    (widen(grad) alone when acc is None), formed as it is read: acc is not
+    written.  Bit for bit grad_accum then adamw_step_tiled."""
+    n = _sum_args(acc, grad, param_bf16, "adamw_step_tiled_sum")
+    c = hp.c_struct()
+    _check("adamw_step_tiled_sum", lib().adamw_step_tiled_sum(
+        ctypes.byref(c), _state_buffer(state, n, "adamw_step_tiled_sum"), _dev(acc, "acc", torch.float32),
+        _dev(grad, "grad"), _dtype_code(grad), _dev(param_bf16, "param_bf16", torch.bfloat16), n,
+        _norm(norm_sq, "adamw_step_tiled_sum"), _stream(stream)))
+
+
+def adamw_step_tiled_sum_dev(scalars_dev: torch.Tensor, state: torch.Tensor, acc: Optional[torch.Tensor],
+                             grad: torch.Tensor, param_bf16: Optional[torch.Tensor] = None,
+                             norm_sq: Optional[torch.Tensor] = None, stream=None) -> None:
+    """adamw_step_tiled_sum with its scalars read from device memory when
+    the kernels run (scalars_dev: uint8 GPU tensor holding scalars_bytes(hp))."""
+    if scalars_dev.dtype != torch.uint8 or scalars_dev.numel() < ctypes.sizeof(AdamWScalars):
+        raise TypeError("adamw_step_tiled_sum_dev: scalars_dev must be a uint8 tensor of at least "
+                        f"{ctypes.sizeof(AdamWScalars)} bytes")
+    n = _sum_args(acc, grad, param_bf16, "adamw_step_tiled_sum_dev")
+    _check("adamw_step_tiled_sum_dev", lib().adamw_step_tiled_sum_dev(
+        _dev(scalars_dev, "scalars_dev"), _state_buffer(state, n, "adamw_step_tiled_sum_dev"),
+        _dev(acc, "acc", torch.float32), _dev(grad, "grad"), _dtype_code(grad),
+        _dev(param_bf16, "param_bf16", torch.bfloat16), n, _norm(norm_sq, "adamw_step_tiled_sum_dev"),
+        _stream(stream)))
 
 
 def moments_tiled_numel(n: int) -> int:

@@ -146,7 +146,129 @@ hipError_t dispatch(float* acc, const void* grad, int grad_bf16, int64_t n, bool
                      : launch<Q, false, false, OVERWRITE, NORM>(acc, grad, n, scale, partials, 0, stream);
 }
 
+// The squared norm of the fused pass without its store, for a step that
+// forms the last micro-batch's sum again as it reads it (the AdamW step's
+// summed-gradient forms).  Each wave runs, for K consecutive one-wave
+// workgroups of accum_kernel<Q, 64, ...> (virtual blocks vb0 .. vb0+K-1 of
+// nvb), exactly what each computes for its partial: the same Q groups per
+// lane, sums, butterfly and slot, so the partials, and the norm formed from
+// them, are bit for bit the fused pass's.  Read-only: acc (unless OVERWRITE)
+// and grad, dword alignment suffices for both; on the vector path every load
+// of the wave's K blocks is issued before the first square.
+template <int Q, int W, int K, bool VEC, bool BF16, bool OVERWRITE>
+__global__ __launch_bounds__(W * 64) void sum_norm_kernel(const float* __restrict__ acc,
+                                                          const void* __restrict__ grad, int64_t n, int64_t nvb,
+                                                          float scale, double* __restrict__ partials) {
+    constexpr int64_t kGroup = 256;   // one wave's 64 lanes x 4 elements
+    constexpr int64_t kSpan = kGroup * Q;   // elements per virtual block
+    const int64_t vb0 = ((int64_t)blockIdx.x * W + (threadIdx.x >> 6)) * K;
+    if (vb0 >= nvb) return;   // the last workgroup's spare waves (whole waves)
+    const int lane = threadIdx.x & 63;
+    if (VEC && (vb0 + K) * kSpan <= n) {   // all K blocks whole
+        f32x4 g[K * Q], a[K * Q];
+#pragma unroll
+        for (int k = 0; k < K * Q; ++k) {
+            const int64_t at = vb0 * kSpan + k * kGroup + lane * 4;
+            g[k] = load4<BF16>(grad, at);
+            if (!OVERWRITE) a[k] = ld_stream_f32x4_a4(acc + at);
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            double s0 = 0.0, s1 = 0.0;
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                const int j = k * Q + q;
+                const f32x4 r = OVERWRITE ? g[j]
+                                          : f32x4{a[j].x + g[j].x, a[j].y + g[j].y, a[j].z + g[j].z,
+                                                  a[j].w + g[j].w};
+                const float rv[4] = {r.x, r.y, r.z, r.w};
+                add_squares4(rv, scale, s0, s1);
+            }
+            const double total = wave_sum(s0 + s1);
+            if (lane == 0) partials[xcd_slot(vb0 + k, nvb)] = total;
+        }
+        return;
+    }
+    // the ragged end: block by block, element by element (out-of-range
+    // elements add +0), as the fused kernel's ragged tile
+    for (int k = 0; k < K && vb0 + k < nvb; ++k) {
+        double s0 = 0.0, s1 = 0.0;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int64_t first = (vb0 + k) * kSpan + q * kGroup + lane * 4;
+            float rv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t i = first + j;
+                if (i < n) {
+                    const float g = load1<BF16>(grad, i);
+                    rv[j] = OVERWRITE ? g : acc[i] + g;
+                }
+            }
+            add_squares4(rv, scale, s0, s1);
+        }
+        const double total = wave_sum(s0 + s1);
+        if (lane == 0) partials[xcd_slot(vb0 + k, nvb)] = total;
+    }
+}
+
+constexpr int kSumNormWaves = 1;   // waves per workgroup of sum_norm_kernel
+constexpr int kSumNormBlocks = 1;  // virtual blocks per wave
+
+// launch pieces and partial positions as launch() gives the fused kernel
+template <int Q, bool VEC, bool BF16, bool OVERWRITE>
+hipError_t launch_sum_norm(const float* acc, const void* grad, int64_t n, float scale, double* partials,
+                           hipStream_t stream) {
+    const int64_t gsz = BF16 ? 2 : 4;
+    for (int64_t off = 0; off < n; off += kLaunchElems) {
+        const int64_t m = launch_piece(n, off);
+        const int64_t nvb = (m + per_block<Q>() - 1) / per_block<Q>();
+        const int64_t per_wg = (int64_t)kSumNormWaves * kSumNormBlocks;
+        const int64_t blocks = (nvb + per_wg - 1) / per_wg;
+        hipLaunchKernelGGL((sum_norm_kernel<Q, kSumNormWaves, kSumNormBlocks, VEC, BF16, OVERWRITE>),
+                           dim3((unsigned)blocks),
+                           dim3(kSumNormWaves * 64), 0, stream, OVERWRITE ? nullptr : acc + off,
+                           static_cast<const char*>(grad) + off * gsz, m, nvb, scale, partials + off / per_block<Q>());
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+template <int Q, bool OVERWRITE>
+hipError_t dispatch_sum_norm(const float* acc, const void* grad, int grad_bf16, int64_t n, bool vec, float scale,
+                             double* partials, hipStream_t stream) {
+    if (vec)
+        return grad_bf16 ? launch_sum_norm<Q, true, true, OVERWRITE>(acc, grad, n, scale, partials, stream)
+                         : launch_sum_norm<Q, true, false, OVERWRITE>(acc, grad, n, scale, partials, stream);
+    return grad_bf16 ? launch_sum_norm<Q, false, true, OVERWRITE>(acc, grad, n, scale, partials, stream)
+                     : launch_sum_norm<Q, false, false, OVERWRITE>(acc, grad, n, scale, partials, stream);
+}
+
 }  // namespace
+
+hipError_t launch_grad_sum_norm_sq(const float* acc, const void* grad, int grad_bf16, int64_t n, int overwrite,
+                                   float scale, double* out, double* workspace, bool vec_ok,
+                                   hipStream_t stream) {
+    int64_t parts = 0;
+    if (n > 0) {
+        hipError_t e;
+        // the fused pass's shapes: Q = 4 for an overwriting bf16 gradient, else 1
+        if (overwrite && grad_bf16) {
+            parts = (n + per_block<kFusedQOverwrite>() - 1) / per_block<kFusedQOverwrite>();
+            e = dispatch_sum_norm<kFusedQOverwrite, true>(acc, grad, grad_bf16, n, vec_ok, scale, workspace,
+                                                          stream);
+        } else {
+            parts = (n + per_block<kFusedQAdd>() - 1) / per_block<kFusedQAdd>();
+            e = overwrite ? dispatch_sum_norm<kFusedQAdd, true>(acc, grad, grad_bf16, n, vec_ok, scale, workspace,
+                                                                stream)
+                          : dispatch_sum_norm<kFusedQAdd, false>(acc, grad, grad_bf16, n, vec_ok, scale,
+                                                                 workspace, stream);
+        }
+        if (e != hipSuccess) return e;
+    }
+    return launch_sum_partials(workspace, parts, workspace + accum_norm_partials(n), out, stream);
+}
 
 hipError_t launch_grad_accum(float* acc, const void* grad, int grad_bf16, int64_t n, int overwrite,
                              bool vec_ok, hipStream_t stream) {

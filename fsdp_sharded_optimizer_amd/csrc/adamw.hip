@@ -9,6 +9,15 @@
 // gfx950 vector rate at 8 TB/s, so the kernel is HBM-bound: the design goal
 // is deep memory-level parallelism and fully coalesced 128-bit accesses.
 //
+// The master forms on the tiled state also take the gradient as the last
+// micro-batch's sum, formed as it is read (GS): fl(acc + widen(g)) from the
+// fp32 accumulator and the micro-batch's bf16 or fp32 gradient, or widen(g)
+// alone for a step of one micro-batch.  It is the value the accumulation
+// would have stored, so the step is bit for bit the one that follows an
+// accumulation, and the accumulator is never written: the last micro-batch
+// and the step move 32 B/element (bf16 micro-batch; 28 alone) instead of the
+// accumulation's 10 (6) plus the step's 30.
+//
 // Two more forms share the code: the bf16 parameter updated in place with no
 // master (the ZeRO page's ZeRO-3 step; 24 B/element), and the ZeRO-1 form
 // that writes the update vector -u instead of a parameter (Adam without
@@ -71,6 +80,38 @@ __device__ __forceinline__ float apply_step(const AdamwScalars& a, float p, floa
     return pd - u;
 }
 
+// Four consecutive gradient elements from `first` (vector path; every source
+// is read-only, so dword alignment suffices) and one element (scalar path),
+// for the gradient source GS; the sums round as the accumulation does.
+template <int GS>
+__device__ __forceinline__ f32x4 grad4(const AdamwArgs& a, int64_t first) {
+    if constexpr (GS == kGradF32) {
+        return ld_stream_f32x4_a4(a.grad + first);
+    } else if constexpr (GS == kGradSumF32) {
+        const f32x4 s = ld_stream_f32x4_a4(a.grad + first);
+        const f32x4 g = ld_stream_f32x4_a4(static_cast<const float*>(a.grad_mb) + first);
+        return f32x4{s.x + g.x, s.y + g.y, s.z + g.z, s.w + g.w};
+    } else {
+        const u32x2 w = ld_stream_u32x2_a4(static_cast<const uint16_t*>(a.grad_mb) + first);
+        const f32x4 g = {bf16_to_f32(w.x & 0xFFFFu), bf16_to_f32(w.x >> 16), bf16_to_f32(w.y & 0xFFFFu),
+                         bf16_to_f32(w.y >> 16)};
+        if constexpr (GS == kGradBf16) return g;
+        const f32x4 s = ld_stream_f32x4_a4(a.grad + first);
+        return f32x4{s.x + g.x, s.y + g.y, s.z + g.z, s.w + g.w};
+    }
+}
+
+template <int GS>
+__device__ __forceinline__ float grad1(const AdamwArgs& a, int64_t i) {
+    if constexpr (GS == kGradF32) return a.grad[i];
+    else if constexpr (GS == kGradSumF32) return a.grad[i] + static_cast<const float*>(a.grad_mb)[i];
+    else {
+        const float g = bf16_to_f32(static_cast<const uint16_t*>(a.grad_mb)[i]);
+        if constexpr (GS == kGradBf16) return g;
+        else return a.grad[i] + g;
+    }
+}
+
 // Clip coefficient from the squared norm, in binary64 (uniform per wave).
 // Returns false when the global squared norm is not finite: the step is
 // skipped, no state is written (the update form writes -0.0, see below).
@@ -130,9 +171,11 @@ enum Form : int { kMaster = 0, kMasterBf16 = 1, kNoMaster = 2, kUpdate = 3 };
 // any element offset of a larger buffer); the vector path then writes it
 // element by element (16- or 32-bit stores) and keeps 128-bit accesses for
 // everything else: 81 % of the peak against 65 % for the element-wise path.
-template <int VEC, int FORM, int BS, bool DEV, bool TILED = false, bool OUT_ALIGNED = true>
+// GS: where the gradient comes from (GradSource; the master forms only).
+template <int VEC, int FORM, int BS, bool DEV, bool TILED = false, bool OUT_ALIGNED = true, int GS = kGradF32>
 __global__ __launch_bounds__(BS) void adamw_kernel(const AdamwArgs a) {
     static_assert(OUT_ALIGNED || FORM == kMasterBf16 || FORM == kUpdate, "a write-only output to split");
+    static_assert(GS == kGradF32 || FORM == kMaster || FORM == kMasterBf16, "summed gradients: master forms");
     constexpr bool kMasterForm = FORM == kMaster || FORM == kMasterBf16;
     constexpr int kRuns = kMasterForm ? 3 : 2;   // runs per tile of the tiled state
     constexpr bool kReadP = FORM != kUpdate;
@@ -148,7 +191,7 @@ __global__ __launch_bounds__(BS) void adamw_kernel(const AdamwArgs a) {
         // One 128-bit access per fp32 stream, lane-contiguous across the wave.
         // The loads are issued before the clip coefficient is resolved, so
         // the latency of the norm's read overlaps with them.
-        const f32x4 g4 = ld_stream_f32x4_a4(a.grad + first);   // read-only: dword alignment suffices
+        const f32x4 g4 = grad4<GS>(a, first);
         // this lane's master (master forms only), exp_avg and exp_avg_sq
         float* p_at = nullptr;
         float* m_at;
@@ -223,7 +266,7 @@ __global__ __launch_bounds__(BS) void adamw_kernel(const AdamwArgs a) {
         float* const m_at = TILED ? (kMasterForm ? ts + kStateTile : ts) : a.exp_avg + i;
         float* const v_at = TILED ? m_at + kStateTile : a.exp_avg_sq + i;
         float m = *m_at, v = *v_at;
-        const float u = adam_elem(sc, coef, a.grad[i], m, v);
+        const float u = adam_elem(sc, coef, grad1<GS>(a, i), m, v);
         *m_at = m;
         *v_at = v;
         if constexpr (FORM == kUpdate) {
@@ -244,10 +287,11 @@ T* advance(T* p, int64_t off) { return p == nullptr ? nullptr : p + off; }
 
 // one launch per kLaunchElems elements, each on its own slice of the buffers
 // (a multiple of kStateTile: a piece of the tiled state starts at runs*off)
-template <int VEC, int FORM, int BS, bool DEV, bool TILED = false, bool OUT_ALIGNED = true>
+template <int VEC, int FORM, int BS, bool DEV, bool TILED = false, bool OUT_ALIGNED = true, int GS = kGradF32>
 hipError_t launch(const AdamwArgs& a, unsigned lds, hipStream_t stream) {
     static_assert(kLaunchElems % kStateTile == 0, "launch pieces start on a tile");
     constexpr int64_t runs = (FORM == kMaster || FORM == kMasterBf16) ? 3 : 2;
+    constexpr int64_t mb_size = GS == kGradSumF32 ? 4 : 2;   // bytes per micro-batch gradient element
     for (int64_t off = 0; off < a.n; off += kLaunchElems) {
         AdamwArgs p = a;
         p.n = launch_piece(a.n, off);
@@ -256,11 +300,12 @@ hipError_t launch(const AdamwArgs& a, unsigned lds, hipStream_t stream) {
         p.exp_avg = advance(a.exp_avg, off);
         p.exp_avg_sq = advance(a.exp_avg_sq, off);
         p.grad = advance(a.grad, off);
+        p.grad_mb = a.grad_mb == nullptr ? nullptr : static_cast<const char*>(a.grad_mb) + off * mb_size;
         p.param_bf16 = advance(a.param_bf16, off);
         p.update = advance(a.update, off);
         const int64_t blocks = ((p.n + VEC - 1) / VEC + BS - 1) / BS;
-        hipLaunchKernelGGL((adamw_kernel<VEC, FORM, BS, DEV, TILED, OUT_ALIGNED>), dim3((unsigned)blocks), dim3(BS),
-                           lds, stream, p);
+        hipLaunchKernelGGL((adamw_kernel<VEC, FORM, BS, DEV, TILED, OUT_ALIGNED, GS>), dim3((unsigned)blocks),
+                           dim3(BS), lds, stream, p);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -274,16 +319,28 @@ hipError_t launch(const AdamwArgs& a, unsigned lds, hipStream_t stream) {
 // parameter (read and written) off a 16-byte boundary.  The six-stream forms
 // keep the 13-per-CU cap tiled too (tiled moments for the update form: 84.5 %
 // there, 83.9 % at 11 per CU).
-template <int FORM, bool DEV = false, bool TILED = false>
+// The summed-gradient forms take the element-wise path on a tiled state too,
+// for a bf16 micro-batch gradient off a 4-byte boundary.
+template <int FORM, bool DEV = false, bool TILED = false, int GS = kGradF32>
 hipError_t launch_form(const AdamwArgs& a, bool vec_ok, bool out_aligned, hipStream_t stream) {
     constexpr bool six = FORM == kNoMaster || FORM == kUpdate;
     constexpr unsigned lds = six ? kVecLdsReserve6 : TILED ? kVecLdsReserveTiled : kVecLdsReserve;
     if constexpr (FORM == kMasterBf16 || FORM == kUpdate) {
-        if (vec_ok && !out_aligned) return launch<4, FORM, kVecBlock, DEV, TILED, false>(a, lds, stream);
+        if (vec_ok && !out_aligned) return launch<4, FORM, kVecBlock, DEV, TILED, false, GS>(a, lds, stream);
     }
-    if (vec_ok) return launch<4, FORM, kVecBlock, DEV, TILED>(a, lds, stream);
-    if constexpr (TILED && FORM != kNoMaster) return hipErrorInvalidValue;   // not reached: always vec_ok
-    else return launch<1, FORM, kBlock, DEV, TILED>(a, 0, stream);
+    if (vec_ok) return launch<4, FORM, kVecBlock, DEV, TILED, true, GS>(a, lds, stream);
+    if constexpr (TILED && FORM != kNoMaster && GS == kGradF32) return hipErrorInvalidValue;   // always vec_ok
+    else return launch<1, FORM, kBlock, DEV, TILED, true, GS>(a, 0, stream);
+}
+
+template <int GS>
+hipError_t launch_tiled_sum(const AdamwArgs& a, bool vec_ok, bool out_aligned, hipStream_t stream) {
+    if (a.sc_dev != nullptr)
+        return a.param_bf16 != nullptr
+                   ? launch_form<kMasterBf16, true, true, GS>(a, vec_ok, out_aligned, stream)
+                   : launch_form<kMaster, true, true, GS>(a, vec_ok, true, stream);
+    return a.param_bf16 != nullptr ? launch_form<kMasterBf16, false, true, GS>(a, vec_ok, out_aligned, stream)
+                                   : launch_form<kMaster, false, true, GS>(a, vec_ok, true, stream);
 }
 
 }  // namespace
@@ -310,6 +367,16 @@ hipError_t launch_adamw_no_master(const AdamwArgs& a, bool vec_ok, hipStream_t s
 
 hipError_t launch_adam_update(const AdamwArgs& a, bool vec_ok, bool out_aligned, hipStream_t stream) {
     return launch_form<kUpdate>(a, vec_ok, out_aligned, stream);
+}
+
+hipError_t launch_adamw_tiled_sum(const AdamwArgs& a, int grad_source, bool vec_ok, bool out_aligned,
+                                  hipStream_t stream) {
+    switch (grad_source) {
+    case kGradBf16: return launch_tiled_sum<kGradBf16>(a, vec_ok, out_aligned, stream);
+    case kGradSumBf16: return launch_tiled_sum<kGradSumBf16>(a, vec_ok, out_aligned, stream);
+    case kGradSumF32: return launch_tiled_sum<kGradSumF32>(a, vec_ok, out_aligned, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_adam_update_tiled(const AdamwArgs& a, bool out_aligned, hipStream_t stream) {

@@ -258,6 +258,30 @@ int32_t grad_accum_norm_sq(float* acc, const void* grad, int32_t grad_dtype, int
                                                     as_stream(hip_stream)));
 }
 
+int32_t grad_sum_norm_sq(const float* acc, const void* grad, int32_t grad_dtype, int64_t n, int32_t overwrite,
+                         double grad_scale, double* out_sq_dev, void* workspace, int64_t workspace_bytes,
+                         void* hip_stream) {
+    if (!dtype_ok(grad_dtype) || !size_ok(n)) return ZS_EINVAL;
+    if (out_sq_dev == nullptr || !aligned(out_sq_dev, 8)) return ZS_EINVAL;
+    if (!(grad_scale > 0.0) || !std::isfinite(grad_scale)) return ZS_EINVAL;
+    const int64_t gsz = elem_size(grad_dtype);
+    if (overwrite) acc = nullptr;   // not read
+    if (n > 0 && (grad == nullptr || !aligned(grad, (uintptr_t)gsz))) return ZS_EINVAL;
+    if (n > 0 && !overwrite && (acc == nullptr || !aligned(acc, 4))) return ZS_EINVAL;
+    const int64_t need = grad_accum_norm_sq_workspace_bytes(n);
+    if (need > 0 && (workspace == nullptr || !aligned(workspace, 8))) return ZS_EINVAL;
+    if (workspace_bytes < need) return ZS_EWORKSPACE;
+    const int64_t acc_bytes = acc == nullptr ? 0 : n * 4;
+    // only the workspace and *out_sq_dev are written
+    if (overlap(acc, acc_bytes, out_sq_dev, 8) || overlap(grad, n * gsz, out_sq_dev, 8) ||
+        overlap(workspace, need, out_sq_dev, 8) || overlap(workspace, need, acc, acc_bytes) ||
+        overlap(workspace, need, grad, n * gsz))
+        return ZS_EOVERLAP;
+    return hip_status(zs::launch_grad_sum_norm_sq(acc, grad, grad_dtype == ZS_BF16, n, overwrite != 0,
+                                                  (float)grad_scale, out_sq_dev, static_cast<double*>(workspace),
+                                                  aligned(grad, 4), as_stream(hip_stream)));
+}
+
 // ---------------------------------------------------------------------------
 // grad_accum_norm_sq with its partials in a static device array
 // ---------------------------------------------------------------------------
@@ -573,6 +597,73 @@ int32_t adamw_step_tiled_dev(const zs_adamw_scalars* scalars_dev, float* state, 
                              uint16_t* param_bf16, int64_t n, const double* norm_sq_dev, void* hip_stream) {
     if (scalars_dev == nullptr) return ZS_EINVAL;
     return adamw_tiled(nullptr, scalars_dev, state, grad, param_bf16, n, norm_sq_dev, hip_stream);
+}
+
+// the tiled step on the last micro-batch's sum: host scalars (hp) or a device copy (sc_dev)
+static int32_t adamw_tiled_sum(const zs_adamw* hp, const zs_adamw_scalars* sc_dev, float* state, const float* acc,
+                               const void* grad, int32_t grad_dtype, uint16_t* param_bf16, int64_t n,
+                               const double* norm_sq_dev, void* hip_stream) {
+    int32_t rc;
+    if (sc_dev == nullptr) {
+        rc = adamw_check_hp(hp, n, norm_sq_dev);
+        if (rc != ZS_OK) return rc;
+    } else {
+        if (!size_ok(n) || !aligned(sc_dev, 8)) return ZS_EINVAL;
+        if (norm_sq_dev != nullptr && !aligned(norm_sq_dev, 8)) return ZS_EINVAL;
+    }
+    if (!dtype_ok(grad_dtype)) return ZS_EINVAL;
+    if (n == 0) return ZS_OK;
+    const int64_t gsz = elem_size(grad_dtype);
+    if (state == nullptr || grad == nullptr) return ZS_EINVAL;
+    if (!aligned(state, 16) || !aligned(grad, (uintptr_t)gsz) || (acc != nullptr && !aligned(acc, 4)) ||
+        (param_bf16 != nullptr && !aligned(param_bf16, 2)))
+        return ZS_EINVAL;
+    const void* bufs[5] = {state, acc, grad, param_bf16, nullptr};
+    const int64_t bytes[5] = {state_tiled_numel(n) * 4, acc ? n * 4 : 0, n * gsz, param_bf16 ? n * 2 : 0, 0};
+    const bool written[5] = {true, false, false, true, false};
+    rc = adamw_check_overlap(bufs, bytes, written, norm_sq_dev);
+    if (rc != ZS_OK) return rc;
+    if (sc_dev != nullptr)   // the scalars are read while the buffers are written
+        for (int i = 0; i < 5; ++i)
+            if (written[i] && overlap(bufs[i], bytes[i], sc_dev, (int64_t)sizeof(zs_adamw_scalars)))
+                return ZS_EOVERLAP;
+    zs::AdamwArgs a;
+    if (sc_dev == nullptr) {
+        a = make_args(hp, norm_sq_dev);
+    } else {
+        std::memset(&a, 0, sizeof(a));
+        a.sc_dev = reinterpret_cast<const zs::AdamwScalars*>(sc_dev);
+        a.norm_sq = norm_sq_dev;
+    }
+    a.state = state;
+    a.grad = acc;
+    a.grad_mb = grad;
+    a.param_bf16 = param_bf16;
+    a.n = n;
+    const int source = grad_dtype == ZS_F32 ? (acc != nullptr ? zs::kGradSumF32 : zs::kGradF32)
+                                            : (acc != nullptr ? zs::kGradSumBf16 : zs::kGradBf16);
+    const bool out_aligned = param_bf16 == nullptr || aligned(param_bf16, 16);
+    if (source == zs::kGradF32) {   // one fp32 micro-batch: the plain tiled step on it
+        a.grad = static_cast<const float*>(grad);
+        a.grad_mb = nullptr;
+        return hip_status(zs::launch_adamw_tiled(a, out_aligned, as_stream(hip_stream)));
+    }
+    return hip_status(zs::launch_adamw_tiled_sum(a, source, aligned(grad, 4), out_aligned, as_stream(hip_stream)));
+}
+
+int32_t adamw_step_tiled_sum(const zs_adamw* hp, float* state, const float* acc, const void* grad,
+                             int32_t grad_dtype, uint16_t* param_bf16, int64_t n, const double* norm_sq_dev,
+                             void* hip_stream) {
+    if (hp == nullptr) return ZS_EINVAL;
+    return adamw_tiled_sum(hp, nullptr, state, acc, grad, grad_dtype, param_bf16, n, norm_sq_dev, hip_stream);
+}
+
+int32_t adamw_step_tiled_sum_dev(const zs_adamw_scalars* scalars_dev, float* state, const float* acc,
+                                 const void* grad, int32_t grad_dtype, uint16_t* param_bf16, int64_t n,
+                                 const double* norm_sq_dev, void* hip_stream) {
+    if (scalars_dev == nullptr) return ZS_EINVAL;
+    return adamw_tiled_sum(nullptr, scalars_dev, state, acc, grad, grad_dtype, param_bf16, n, norm_sq_dev,
+                           hip_stream);
 }
 
 int32_t adam_update_tiled(const zs_adamw* hp, float* moments, const float* grad, float* update, int64_t n,

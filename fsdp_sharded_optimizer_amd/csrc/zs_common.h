@@ -100,7 +100,8 @@ struct AdamwArgs {
     float* master;
     float* exp_avg;
     float* exp_avg_sq;
-    const float* grad;
+    const float* grad;          // the fp32 gradient; the fp32 accumulator for the summed-gradient forms
+    const void* grad_mb;        // summed-gradient forms: the last micro-batch's gradient (bf16 or fp32)
     uint16_t* param_bf16;       // nullable
     float* update;              // the ZeRO-1 form's output
     int64_t n;
@@ -143,6 +144,13 @@ hipError_t launch_adam_update(const AdamwArgs& a, bool vec_ok, bool out_aligned,
 hipError_t launch_adamw_tiled(const AdamwArgs& a, bool out_aligned, hipStream_t stream);
 hipError_t launch_adam_update_tiled(const AdamwArgs& a, bool out_aligned, hipStream_t stream);
 hipError_t launch_adamw_no_master_tiled(const AdamwArgs& a, bool vec_ok, hipStream_t stream);
+// The tiled master-form step whose gradient is the last micro-batch's sum,
+// formed as it is read: grad_source 1 = widen(bf16 grad_mb) (no accumulator),
+// 2 = fl(grad + widen(bf16 grad_mb)), 3 = fl(grad + fp32 grad_mb).  vec_ok:
+// grad_mb is 4-byte aligned (else the element-wise path).
+enum GradSource : int { kGradF32 = 0, kGradBf16 = 1, kGradSumBf16 = 2, kGradSumF32 = 3 };
+hipError_t launch_adamw_tiled_sum(const AdamwArgs& a, int grad_source, bool vec_ok, bool out_aligned,
+                                  hipStream_t stream);
 // runs (2 or 3) split fp32 arrays (each nullable: zeros) -> tiled buffer,
 // padding zeroed; and back (each destination nullable: skipped)
 hipError_t launch_tile_runs(const float* const* src, int runs, float* buf, int64_t n, hipStream_t stream);
@@ -157,6 +165,11 @@ hipError_t launch_grad_accum_norm_sq(float* acc, const void* grad, int grad_bf16
                                      hipStream_t stream);
 hipError_t launch_grad_norm_sq(const float* grad, int64_t n, float scale, double* out,
                                double* workspace, hipStream_t stream);
+// launch_grad_accum_norm_sq's norm, bit for bit, without its store (acc is
+// read, not written; not read when overwrite is set)
+hipError_t launch_grad_sum_norm_sq(const float* acc, const void* grad, int grad_bf16, int64_t n, int overwrite,
+                                   float scale, double* out, double* workspace, bool vec_ok,
+                                   hipStream_t stream);
 
 // Up to kReduceMaxChunks rank chunks summed per launch (pointers travel in
 // the kernel arguments).

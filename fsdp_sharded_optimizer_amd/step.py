@@ -5,9 +5,13 @@ exp_avg_sq, the fp32 gradient accumulator, the bf16 parameter shard and the
 norm scratch.  A step is: ``accumulate`` once per micro-batch (the last one
 may form the squared norm in the same pass), then ``step``: the norm (if
 not formed yet and requested) and the fused AdamW update with the bf16
-re-cast.  Where a step's micro-batch gradients are all kept in device memory
-(2 B per element each in bf16), ``accumulate_all`` sums them in one pass
-instead.  Nothing here computes; it orders calls.
+re-cast.  ``step(last_grad=g)`` takes the last micro-batch's gradient
+itself instead: on the tiled state its sum with the accumulator is never
+stored (the norm pass reads both, and so does AdamW), which saves the
+accumulator's write and re-read, 8 B per element; the results are the same
+bit for bit.  Where a step's micro-batch gradients are all kept in device
+memory (2 B per element each in bf16), ``accumulate_all`` sums them in one
+pass instead.  Nothing here computes; it orders calls.
 
 ``layout="tiled"`` (the default) keeps master, exp_avg and exp_avg_sq in
 one buffer in the library's tiled state layout, which the AdamW step
@@ -153,9 +157,25 @@ class ShardOptimizer:
                               weight_decay=self.weight_decay, grad_scale=self.grad_scale,
                               max_norm=self.max_norm, extra_norm_sq=extra_norm_sq, step=self.t)
 
-    def step(self, extra_norm_sq: float = 0.0) -> None:
+    def step(self, extra_norm_sq: float = 0.0, last_grad: Optional[torch.Tensor] = None) -> None:
         """Norm (if clipping or asked for), then the fused AdamW update.  The
-        step counter advances only once the update is enqueued."""
+        step counter advances only once the update is enqueued.
+
+        last_grad: the last micro-batch's gradient, not yet accumulated (the
+        step is then accumulate(last_grad, last=True) followed by step(),
+        with the same results bit for bit).  On the tiled state the sum is
+        formed where it is read and never stored: the norm pass reads the
+        accumulator and last_grad (grad_sum_norm_sq), AdamW reads them again
+        (adamw_step_tiled_sum), and the accumulator keeps the earlier
+        micro-batches' sum."""
+        if last_grad is not None:
+            if self._norm_ready:
+                raise RuntimeError("step(last_grad=...) after accumulate(..., last=True)")
+            if self._split is not None:
+                self.accumulate(last_grad, last=True)
+            else:
+                self._step_on_sum(last_grad, extra_norm_sq)
+                return
         if self._pending == 0:
             raise RuntimeError("step() without an accumulated gradient")
         norm = None
@@ -166,6 +186,20 @@ class ShardOptimizer:
         hp = self.hp(extra_norm_sq)
         hp.step = self.t + 1
         self._adamw(hp, norm)
+        self.t += 1
+        self._pending = 0
+        self._norm_ready = False
+
+    def _step_on_sum(self, last_grad: torch.Tensor, extra_norm_sq: float) -> None:
+        acc = self.acc if self._pending > 0 else None   # a single micro-batch: its gradient alone
+        g = last_grad.reshape(-1)
+        norm = None
+        if self.compute_norm:
+            zs.grad_sum_norm_sq(acc, g, acc is None, self.grad_scale, self.norm_sq, self.workspace)
+            norm = self.norm_sq
+        hp = self.hp(extra_norm_sq)
+        hp.step = self.t + 1
+        zs.adamw_step_tiled_sum(hp, self.state, acc, g, self.param_bf16, norm_sq=norm)
         self.t += 1
         self._pending = 0
         self._norm_ready = False
@@ -255,15 +289,29 @@ class CapturedStep:
         self._host.numpy()[:] = np.frombuffer(zs.scalars_bytes(hp), dtype=np.uint8)
 
     def _body(self) -> None:
+        """The step as ShardOptimizer runs it: on the tiled state the last
+        gradient is folded into the norm pass and AdamW (step(last_grad=)),
+        on the split state it is accumulated with the norm first."""
         opt = self.opt
         last = len(self.grads) - 1
-        for k, g in enumerate(self.grads):
-            if k == last and opt.compute_norm:
-                zs.grad_accum_norm_sq(opt.acc, g, k == 0, opt.grad_scale, opt.norm_sq, opt.workspace)
-            else:
-                zs.grad_accum(opt.acc, g, overwrite=(k == 0))
+        tiled = opt._split is None
+        for k, g in enumerate(self.grads[:last]):
+            zs.grad_accum(opt.acc, g, overwrite=(k == 0))
+        g = self.grads[last]
+        norm = opt.norm_sq if opt.compute_norm else None
+        if tiled:
+            acc = opt.acc if last > 0 else None
+            if opt.compute_norm:
+                zs.grad_sum_norm_sq(acc, g, acc is None, opt.grad_scale, opt.norm_sq, opt.workspace)
+            self._dev.copy_(self._host, non_blocking=True)
+            zs.adamw_step_tiled_sum_dev(self._dev, opt.state, acc, g, opt.param_bf16, norm_sq=norm)
+            return
+        if opt.compute_norm:
+            zs.grad_accum_norm_sq(opt.acc, g, last == 0, opt.grad_scale, opt.norm_sq, opt.workspace)
+        else:
+            zs.grad_accum(opt.acc, g, overwrite=(last == 0))
         self._dev.copy_(self._host, non_blocking=True)
-        opt._adamw_dev(self._dev, opt.norm_sq if opt.compute_norm else None)
+        opt._adamw_dev(self._dev, norm)
 
     def replay(self) -> None:
         """Run the next step.  Waits for the previous replay to have read the

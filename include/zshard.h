@@ -292,6 +292,28 @@ ZS_API int32_t grad_accum_norm_sq(float* acc, const void* grad, int32_t grad_dty
                                   void* hip_stream);
 
 /*
+ * grad_sum_norm_sq — the squared norm grad_accum_norm_sq forms, without its
+ * store: for a step that folds the last micro-batch into the AdamW update
+ * (adamw_step_tiled_sum) instead of accumulating it first.  Same sources as
+ * grad_accum_norm_sq ([ZeRO page] "梯度累积" and §"组合策略"; [Accum page]
+ * §"梯度累积：用时间换显存": the clip follows the last micro-batch).
+ * *out_sq_dev receives, bit for bit, the value grad_accum_norm_sq(acc, grad,
+ * grad_dtype, n, overwrite, grad_scale, ...) would write (the same
+ * association, fixed by n, overwrite and grad_dtype), and acc is left as it
+ * is: read when overwrite == 0; not read, and may be NULL, when overwrite !=
+ * 0.  Read-only passes: 6 B/element (bf16 gradient onto an accumulator), 2
+ * (bf16, overwrite), 8 and 4 for fp32.
+ * acc: device fp32[n], 4-byte aligned; grad: device [n] of grad_dtype;
+ * out_sq_dev: device double, written (0 when n == 0); workspace: device,
+ * >= grad_accum_norm_sq_workspace_bytes(n) bytes, 8-byte aligned.
+ * Errors: ZS_EINVAL, ZS_EWORKSPACE, ZS_EOVERLAP (the workspace or
+ * *out_sq_dev with any other buffer), ZS_EHIP.
+ */
+ZS_API int32_t grad_sum_norm_sq(const float* acc, const void* grad, int32_t grad_dtype, int64_t n, int32_t overwrite,
+                                double grad_scale, double* out_sq_dev, void* workspace, int64_t workspace_bytes,
+                                void* hip_stream);
+
+/*
  * grad_accum_norm_sq_noalloc — grad_accum_norm_sq for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc.  It takes no workspace and
@@ -465,6 +487,43 @@ ZS_API int32_t adamw_step_tiled(const zs_adamw* hp, float* state, const float* g
  */
 ZS_API int32_t adamw_step_tiled_dev(const zs_adamw_scalars* scalars_dev, float* state, const float* grad,
                                     uint16_t* param_bf16, int64_t n, const double* norm_sq_dev, void* hip_stream);
+
+/*
+ * adamw_step_tiled_sum — adamw_step_tiled whose gradient is the last
+ * micro-batch's accumulation, formed as it is read instead of stored first:
+ * element i's gradient is the value grad_accum would leave in acc[i] for
+ * this micro-batch, fl(acc[i] + widen(grad[i])), or widen(grad[i]) when acc
+ * is NULL (a step of one micro-batch: grad_accum with overwrite).  The
+ * accumulation and the step are the pages' ([ZeRO page] "梯度累积" and
+ * §ZeRO-1/2/3 step; [Accum page] §"梯度累积：用时间换显存"); doing them in one
+ * pass is this library's schedule.  Results are bit for bit those of
+ * grad_accum(acc, grad, grad_dtype, n, acc == NULL) followed by
+ * adamw_step_tiled(hp, state, acc, ...), but acc is only read, never
+ * written: it does not hold the final gradient afterwards.  With the norm
+ * from grad_sum_norm_sq, the last micro-batch and the step move 32 B per
+ * element (bf16 gradient onto an accumulator; 28 with acc NULL) plus the
+ * norm's read-only pass (6; 2), against grad_accum_norm_sq's 10 (6) and
+ * adamw_step_tiled's 30.
+ * state: as adamw_step_tiled; acc: device fp32[n], 4-byte aligned, read, or
+ * NULL; grad: device [n] of grad_dtype (ZS_BF16 or ZS_F32), read;
+ * param_bf16, norm_sq_dev as adamw_step_tiled.  No two of state, acc, grad,
+ * param_bf16 may overlap, nor a written one overlap *norm_sq_dev.
+ * Errors: ZS_EINVAL (as adamw_step_tiled, or a bad grad_dtype), ZS_EOVERLAP,
+ * ZS_EHIP.
+ */
+ZS_API int32_t adamw_step_tiled_sum(const zs_adamw* hp, float* state, const float* acc, const void* grad,
+                                    int32_t grad_dtype, uint16_t* param_bf16, int64_t n, const double* norm_sq_dev,
+                                    void* hip_stream);
+
+/*
+ * adamw_step_tiled_sum_dev — adamw_step_tiled_sum with its scalars read from
+ * device memory when the kernels run (as adamw_step_tiled_dev).
+ * scalars_dev: device, 8-byte aligned, read; it must not overlap a written
+ * buffer.  Other arguments, results and errors as adamw_step_tiled_sum.
+ */
+ZS_API int32_t adamw_step_tiled_sum_dev(const zs_adamw_scalars* scalars_dev, float* state, const float* acc,
+                                        const void* grad, int32_t grad_dtype, uint16_t* param_bf16, int64_t n,
+                                        const double* norm_sq_dev, void* hip_stream);
 
 /*
  * Tiled moments — the same layout for the forms that keep no fp32 master

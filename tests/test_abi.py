@@ -37,7 +37,7 @@ def no_launch_reached():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 30 and set(names) == set(B.EXPORTS), names
+    assert len(names) == 33 and set(names) == set(B.EXPORTS), names
     L = zs.lib()
     for name in names:
         assert getattr(L, name) is not None
@@ -384,6 +384,69 @@ def test_grad_accum_norm_sq_rejects():
     assert call(out=FAKE + 16) == B.ZS_EOVERLAP                    # norm inside acc
     assert call(ws=g + 1024) == B.ZS_EOVERLAP                      # workspace inside grad
     assert call(n=-1) == B.ZS_EINVAL
+
+
+def test_grad_sum_norm_sq_rejects():
+    L = zs.lib()
+    n = 1 << 20
+    need = zs.grad_accum_norm_sq_workspace_bytes(n)
+    acc, g, ws, out = FAKE, FAKE + 2**30, FAKE + 2**31, FAKE + 2**32
+    call = lambda **k: L.grad_sum_norm_sq(k.get("acc", acc), k.get("g", g), k.get("dt", B.ZS_BF16), k.get("n", n),
+                                          k.get("ovr", 0), k.get("s", 1.0), k.get("out", out), k.get("ws", ws),
+                                          k.get("wsb", need), None)
+    assert call(wsb=need - 8) == B.ZS_EWORKSPACE
+    assert call(dt=5) == B.ZS_EINVAL
+    assert call(out=0) == B.ZS_EINVAL
+    assert call(out=out + 4) == B.ZS_EINVAL
+    assert call(s=float("inf")) == B.ZS_EINVAL
+    assert call(acc=0) == B.ZS_EINVAL                              # an accumulator is read unless overwrite
+    assert call(acc=acc + 2) == B.ZS_EINVAL
+    assert call(g=g + 1) == B.ZS_EINVAL                            # bf16 at an odd address
+    assert call(ws=0) == B.ZS_EINVAL
+    assert call(out=FAKE + 16) == B.ZS_EOVERLAP                    # norm inside acc
+    assert call(ws=g + 1024) == B.ZS_EOVERLAP                      # workspace inside grad
+    assert call(ws=FAKE + 64) == B.ZS_EOVERLAP                     # workspace inside acc
+    assert call(n=-1) == B.ZS_EINVAL
+    # overwrite: the accumulator is not read, so none is needed and none can overlap
+    assert call(ovr=1, acc=0, wsb=need - 8) == B.ZS_EWORKSPACE
+    assert call(ovr=1, acc=ws + 64, g=0) == B.ZS_EINVAL           # a gradient is still needed
+
+
+def test_adamw_step_tiled_sum_rejects():
+    L = zs.lib()
+    n = 1024
+    st = FAKE
+    sb = 3 * B.STATE_TILE * 4
+    acc0, g0 = FAKE + 2**20, FAKE + 2**21
+    call = lambda hp=None, s=st, a=acc0, g=g0, dt=B.ZS_BF16, b=0, k=n, norm=0: L.adamw_step_tiled_sum(
+        ctypes.byref(hp or _hp()), s, a, g, dt, b, k, norm, None)
+    for bad in (dict(step=0), dict(beta2=-0.1), dict(eps=float("nan")), dict(grad_scale=0.0)):
+        assert call(hp=_hp(**bad)) == B.ZS_EINVAL, bad
+    assert L.adamw_step_tiled_sum(None, st, acc0, g0, B.ZS_BF16, 0, n, 0, None) == B.ZS_EINVAL
+    assert call(dt=7) == B.ZS_EINVAL
+    assert call(s=0) == B.ZS_EINVAL
+    assert call(g=0) == B.ZS_EINVAL
+    assert call(s=st + 4) == B.ZS_EINVAL                            # the state must be 16-byte aligned
+    assert call(a=acc0 + 2) == B.ZS_EINVAL                          # fp32 accumulator off 4 bytes
+    assert call(g=g0 + 1) == B.ZS_EINVAL                            # bf16 gradient at an odd address
+    assert call(g=g0 + 2, dt=B.ZS_F32) == B.ZS_EINVAL               # fp32 gradient off 4 bytes
+    assert call(b=FAKE + 2**22 + 1) == B.ZS_EINVAL
+    assert call(norm=FAKE + 2**23 + 4) == B.ZS_EINVAL
+    assert call(a=st + sb - 8) == B.ZS_EOVERLAP                     # accumulator over the end of the state
+    assert call(g=st + 64) == B.ZS_EOVERLAP                         # gradient inside the state
+    assert call(g=acc0 + 64) == B.ZS_EOVERLAP                       # gradient inside the accumulator
+    assert call(b=g0 + 64) == B.ZS_EOVERLAP                         # bf16 output over the gradient
+    assert call(norm=st + 1024) == B.ZS_EOVERLAP                    # norm inside the written state
+    assert call(k=(1 << 39) + 1) == B.ZS_EINVAL
+    assert call(k=0) == B.ZS_OK
+    assert call(k=0, s=0, a=0, g=0) == B.ZS_OK                      # nothing to step: no buffer needed
+    sc = FAKE + 2**30
+    dev = lambda s=sc, k=n, norm=0, dt=B.ZS_BF16: L.adamw_step_tiled_sum_dev(s, st, acc0, g0, dt, 0, k, norm, None)
+    assert L.adamw_step_tiled_sum_dev(0, st, acc0, g0, B.ZS_BF16, 0, n, 0, None) == B.ZS_EINVAL
+    assert dev(s=sc + 4) == B.ZS_EINVAL
+    assert dev(dt=3) == B.ZS_EINVAL
+    assert dev(s=st + 64) == B.ZS_EOVERLAP                          # scalars inside the written state
+    assert dev(k=0) == B.ZS_OK
 
 
 def test_grad_reduce_chunks_norm_sq_rejects():

@@ -10,7 +10,7 @@ import pytest
 import bench_pmc
 from fsdp_sharded_optimizer_amd import build as zbuild
 
-ADAMW = "zs::(anonymous namespace)::adamw_kernel<4, 1, 64, false, true, true>"
+ADAMW = "zs::(anonymous namespace)::adamw_kernel<4, 1, 64, false, true, true, 0>"
 
 
 @pytest.fixture(scope="module")

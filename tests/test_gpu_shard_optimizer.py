@@ -1,8 +1,10 @@
 """ShardOptimizer (the call-ordering layer) on the GPU against the oracle.
 
 Four bf16 micro-batches per step, a global-norm clip with the other ranks'
-share as a stand-in, three steps, on a ragged shard; once with the norm
-formed in the last accumulation pass and once with a separate norm pass.
+share as a stand-in, three steps, on a ragged shard; with the norm formed in
+the last accumulation pass, with a separate norm pass, and with the last
+micro-batch handed to step() (on the tiled state, its sum with the
+accumulator formed where it is read, never stored).
 """
 import math
 
@@ -18,9 +20,10 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("layout", ["tiled", "split"])
-@pytest.mark.parametrize("fused", [True, False])
-def test_shard_optimizer_matches_the_oracle(fused, layout):
-    print(f"ShardOptimizer fused={fused} layout={layout}", flush=True)
+@pytest.mark.parametrize("mode", ["fused", "separate", "last_grad"])
+def test_shard_optimizer_matches_the_oracle(mode, layout):
+    print(f"ShardOptimizer mode={mode} layout={layout}", flush=True)
+    fused = mode == "fused"
     n, M, scale, lr, wd = 100_003, 4, 1 / 32, 3e-4, 0.1
     rng = np.random.default_rng(17)
     p0 = rng.uniform(-0.1, 0.1, n).astype(np.float32)
@@ -34,17 +37,22 @@ def test_shard_optimizer_matches_the_oracle(fused, layout):
         mbs = [oracle.bf16_rne((rng.standard_normal(n) * 0.05 * t).astype(np.float32)) for _ in range(M)]
         acc_ref = np.empty(n, np.float32)
         for k, g in enumerate(mbs):
+            if k == M - 1:
+                before_last = acc_ref.copy()
             oracle.grad_accum(acc_ref, g, oracle.BF16, overwrite=(k == 0))
-            opt.accumulate(from_np(g, bf16=True), last=fused and k == M - 1)
+            if mode != "last_grad" or k < M - 1:
+                opt.accumulate(from_np(g, bf16=True), last=fused and k == M - 1)
         S = oracle.grad_norm_sq(acc_ref, scale)
         extra = 3.0 * S                                   # the other ranks' share
         prev = {"p": p_ref.copy(), "m": m_ref.copy()}
         H = oracle.make_hp(lr, 0.9, 0.95, 1e-8, wd, scale, 1.0, extra, t)
         assert oracle.adamw_step(H, p_ref, m_ref, v_ref, acc_ref, b_ref, norm_sq=S) == 0
-        opt.step(extra_norm_sq=extra)
+        opt.step(extra_norm_sq=extra, last_grad=from_np(mbs[-1], bf16=True) if mode == "last_grad" else None)
         torch.cuda.synchronize()
         assert opt.t == t
-        assert bits_equal(to_np(opt.acc), acc_ref)
+        # the tiled state's one-pass step never stores the last micro-batch's sum
+        stored = before_last if (mode == "last_grad" and layout == "tiled") else acc_ref
+        assert bits_equal(to_np(opt.acc), stored)
         assert abs(opt.norm_sq.item() - S) <= NORM_TOL * S
         coef = oracle.clip_coef(S, extra, 1.0)
         assert coef < 1.0                                 # every step clips
@@ -148,15 +156,18 @@ def test_captured_step_replays_like_eager_steps(max_norm, layout):
     b = zs.ShardOptimizer(p0.clone(), param_bf16=torch.empty(n, dtype=torch.bfloat16, device="cuda"), **kw)
     grads = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for _ in range(M)]
     cap = a.capture(grads, extra_norm_sq=0.02)
+    # the twin runs the schedule the capture records: on the tiled state the
+    # last gradient goes to step() (its sum with the accumulator never stored)
+    tiled = layout == "tiled"
     torch.cuda.synchronize()
     assert a.t == 0 and bits_equal(to_np(a.master), to_np(p0))   # capturing changed nothing
     for t in range(1, 5):
         for k, g in enumerate(grads):
             g.copy_((torch.randn(n, generator=gen, device="cuda") * 1e-2 * (k + t)).to(torch.bfloat16))
         cap.replay()
-        for k, g in enumerate(grads):
+        for k, g in enumerate(grads[:M - 1] if tiled else grads):
             b.accumulate(g, last=k == M - 1)
-        b.step(extra_norm_sq=0.02)
+        b.step(extra_norm_sq=0.02, last_grad=grads[-1] if tiled else None)
         torch.cuda.synchronize()
         assert a.t == b.t == t
         for name in ("master", "exp_avg", "exp_avg_sq", "param_bf16", "acc"):
@@ -164,6 +175,49 @@ def test_captured_step_replays_like_eager_steps(max_norm, layout):
         if max_norm > 0:
             assert a.norm_sq.item() == b.norm_sq.item()
         _ = (a.acc * 2).sum().item()   # unrelated eager work between replays
+
+
+@pytest.mark.parametrize("layout", ["tiled", "split"])
+@pytest.mark.parametrize("M", [1, 3])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("max_norm", [0.4, 0.0])
+def test_step_with_last_grad_equals_accumulate_then_step(layout, M, dtype, max_norm):
+    """step(last_grad=g) against accumulate(g, last=True) then step(), over
+    four steps of M micro-batches: master, moments, bf16 parameter and norm
+    bit-identical; on the tiled state the accumulator keeps the earlier
+    micro-batches' sum (bit for bit the oracle's fold of them)."""
+    print(f"ShardOptimizer last_grad layout={layout} M={M} dtype={dtype} max_norm={max_norm}", flush=True)
+    n = 2 * zs.STATE_TILE + 4099
+    rng = np.random.default_rng(M * 7 + (dtype == torch.float32) + int(max_norm * 10))
+    p0 = from_np(rng.uniform(-0.1, 0.1, n).astype(np.float32))
+    kw = dict(lr=3e-4, betas=(0.9, 0.95), weight_decay=0.1, grad_scale=1 / (4 * M), max_norm=max_norm,
+              layout=layout, compute_norm=True)
+    a, b = (zs.ShardOptimizer(p0.clone(), param_bf16=torch.empty(n, dtype=torch.bfloat16, device="cuda"), **kw)
+            for _ in range(2))
+    bf16 = dtype == torch.bfloat16
+    for t in range(1, 5):
+        mbs = [(rng.standard_normal(n) * 0.05 * (k + t)).astype(np.float32) for k in range(M)]
+        mbs = [oracle.bf16_rne(g) for g in mbs] if bf16 else mbs
+        gpu = [from_np(g, bf16=bf16) for g in mbs]
+        for g in gpu[:-1]:
+            a.accumulate(g)
+            b.accumulate(g)
+        a.step(extra_norm_sq=0.05, last_grad=gpu[-1])
+        b.accumulate(gpu[-1], last=True)
+        b.step(extra_norm_sq=0.05)
+        torch.cuda.synchronize()
+        assert a.t == b.t == t
+        assert a.norm_sq.item() == b.norm_sq.item(), t
+        for name in ("master", "exp_avg", "exp_avg_sq", "param_bf16"):
+            assert bits_equal(to_np(getattr(a, name)), to_np(getattr(b, name))), (t, name)
+        if layout == "tiled" and M > 1:
+            acc_ref = np.empty(n, np.float32)
+            for k, g in enumerate(mbs[:-1]):
+                oracle.grad_accum(acc_ref, g, oracle.BF16 if bf16 else oracle.F32, overwrite=(k == 0))
+            assert bits_equal(to_np(a.acc), acc_ref), t
+    with pytest.raises(RuntimeError):   # the last micro-batch handed over twice
+        a.accumulate(gpu[0], last=True)
+        a.step(last_grad=gpu[0])
 
 
 @pytest.mark.parametrize("fused", [False, True])

@@ -1,0 +1,222 @@
+"""GPU parity of the step that folds the last micro-batch into AdamW.
+
+grad_sum_norm_sq forms the squared norm of the last micro-batch's sum
+without storing it, and adamw_step_tiled_sum steps the tiled state on that
+sum, formed again as it is read.  Against the oracle: the norm within the bar
+of the oracle's norm of its accumulated gradient; handed the oracle's norm,
+the state and bf16 output bit-identical to the oracle's accumulate-then-step.
+Against the library's own two-call path: the norm bit for bit that of
+grad_accum_norm_sq (same association), the state and output bit for bit
+those of grad_accum then adamw_step_tiled, and the accumulator untouched.
+Sizes span several tiles and the norm's partial blocks with ragged ends;
+offsets put the gradient off 4-byte (bf16, the element-wise path) and
+16-byte boundaries and the bf16 output off 16 bytes.  Every buffer carries a
+canary tail.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import fsdp_sharded_optimizer_amd as zs
+from tests.parity import bits_equal, identical_fraction, to_np
+from tests.test_gpu_kernels import NORM_TOL, _hp, canary_ok, dev_buf
+
+pytestmark = pytest.mark.gpu
+
+T = 8192   # ZS_STATE_TILE
+SIZES = [1, 3, 255, 256, 257, 1023, 1024, 1025, 8193, 100_003, 1_000_037]
+
+
+def _grad(rng, n, dtype):
+    g32 = (rng.standard_normal(n) * 1e-2).astype(np.float32)
+    return oracle.bf16_rne(g32) if dtype == "bf16" else g32
+
+
+def _code(dtype):
+    return oracle.BF16 if dtype == "bf16" else oracle.F32
+
+
+@pytest.mark.parametrize("n", SIZES)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("overwrite", [False, True])
+@pytest.mark.parametrize("acc_off,grad_off", [(0, 0), (1, 1), (3, 2)])
+def test_grad_sum_norm_sq(n, dtype, overwrite, acc_off, grad_off):
+    """The norm of the last micro-batch's sum: within the bar of the
+    oracle's, bit for bit grad_accum_norm_sq's, and the accumulator (and the
+    gradient) left as they were."""
+    print(f"grad_sum_norm_sq n={n} dtype={dtype} overwrite={overwrite} offsets={acc_off},{grad_off}", flush=True)
+    rng = np.random.default_rng(n * 11 + acc_off * 3 + grad_off + 7 * overwrite)
+    acc0 = (rng.standard_normal(n) * 1e-2).astype(np.float32)
+    g = _grad(rng, n, dtype)
+    scale = 1.0 / 16
+    ref = acc0.copy()
+    oracle.grad_accum(ref, g, _code(dtype), overwrite=overwrite)
+    want = oracle.grad_norm_sq(ref, scale)
+    acc, acc_whole = dev_buf(acc0, acc_off)
+    gd, g_whole = dev_buf(g, grad_off, bf16=(dtype == "bf16"))
+    out = torch.full((1,), float("nan"), dtype=torch.float64, device="cuda")
+    zs.grad_sum_norm_sq(acc, gd, overwrite, scale, out)
+    got = out.item()
+    assert abs(math.sqrt(got) - math.sqrt(want)) <= NORM_TOL * math.sqrt(want)
+    assert bits_equal(to_np(acc), acc0), "the accumulator was written"
+    assert canary_ok(acc_whole, acc_off, n) and canary_ok(g_whole, grad_off, n)
+    # the fused pass that stores the sum forms the same bits
+    acc2, _ = dev_buf(acc0, 0)
+    out2 = torch.full((1,), float("nan"), dtype=torch.float64, device="cuda")
+    zs.grad_accum_norm_sq(acc2, gd, overwrite, scale, out2)
+    assert out2.item() == got
+    assert bits_equal(to_np(acc2), ref)
+
+
+def test_grad_sum_norm_sq_overwrite_reads_no_accumulator_and_empty():
+    n = 70_001
+    rng = np.random.default_rng(5)
+    g = _grad(rng, n, "bf16")
+    gd, _ = dev_buf(g, 0, bf16=True)
+    out = torch.full((1,), float("nan"), dtype=torch.float64, device="cuda")
+    zs.grad_sum_norm_sq(None, gd, True, 1.0 / 8, out)
+    ref = np.empty(n, np.float32)
+    oracle.grad_accum(ref, g, oracle.BF16, overwrite=True)
+    want = oracle.grad_norm_sq(ref, 1.0 / 8)
+    assert abs(math.sqrt(out.item()) - math.sqrt(want)) <= NORM_TOL * math.sqrt(want)
+    e = torch.empty(0, dtype=torch.bfloat16, device="cuda")
+    zs.grad_sum_norm_sq(None, e, True, 1.0, out)
+    assert out.item() == 0.0
+    # closed form: 2^23 + 3 elements of 2^-7 onto an accumulator of 2^-7, at
+    # scale 1/8: every sum is 2^-6, the norm exactly (2^23 + 3) * 2^-18
+    n = (1 << 23) + 3
+    acc = torch.full((n,), 2.0**-7, dtype=torch.float32, device="cuda")
+    gb = torch.full((n,), 2.0**-7, dtype=torch.bfloat16, device="cuda")
+    zs.grad_sum_norm_sq(acc, gb, False, 1.0 / 8, out)
+    assert out.item() == n * 2.0**-18
+    assert torch.all(acc == 2.0**-7)
+
+
+@pytest.mark.parametrize("n", SIZES)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("with_acc", [True, False])
+@pytest.mark.parametrize("grad_off,b_off", [(0, 0), (1, 1), (2, 3)])
+def test_adamw_step_tiled_sum_bit_exact(n, dtype, with_acc, grad_off, b_off):
+    """Three steps, each on the sum of an accumulator and a last
+    micro-batch (or the micro-batch alone).  Handed the oracle's norm, the
+    tiled state and the bf16 output equal the oracle's accumulate-then-step
+    bit for bit.  With the GPU's own norms, the one-pass path
+    (grad_sum_norm_sq, adamw_step_tiled_sum) equals the two-call path
+    (grad_accum_norm_sq, adamw_step_tiled) bit for bit, norm included, and
+    never writes the accumulator."""
+    print(f"adamw_step_tiled_sum n={n} dtype={dtype} acc={with_acc} offsets={grad_off},{b_off}", flush=True)
+    rng = np.random.default_rng(n * 3 + grad_off * 5 + b_off + 11 * with_acc + len(dtype))
+    p_ref = rng.uniform(-0.1, 0.1, n).astype(np.float32)
+    m_ref, v_ref, b_ref = np.zeros(n, np.float32), np.zeros(n, np.float32), np.zeros(n, np.uint16)
+    start = oracle.state_tile(p_ref, m_ref, v_ref, n, T)
+    st, stw = dev_buf(start, 0)             # one-pass path, oracle's norm
+    st_one, st_one_w = dev_buf(start, 0)    # one-pass path, its own norm
+    st_two, _ = dev_buf(start, 0)           # two-call path, its own norm
+    b, bw = dev_buf(b_ref, b_off, bf16=True)
+    b_one, b_one_w = dev_buf(b_ref, b_off, bf16=True)
+    b_two, _ = dev_buf(b_ref, b_off, bf16=True)
+    norm = torch.zeros(1, dtype=torch.float64, device="cuda")
+    norm_one = torch.zeros(1, dtype=torch.float64, device="cuda")
+    norm_two = torch.zeros(1, dtype=torch.float64, device="cuda")
+    scale = 1.0 / 32
+    for t in range(1, 4):
+        acc0 = (rng.standard_normal(n) * 1e-2).astype(np.float32)
+        g = _grad(rng, n, dtype)
+        ref = acc0.copy()
+        oracle.grad_accum(ref, g, _code(dtype), overwrite=not with_acc)
+        S = oracle.grad_norm_sq(ref, scale)
+        hp_gpu, hp_orc = _hp(t, scale=scale, max_norm=math.sqrt(S) * 0.8 if t != 2 else 0.0, extra=0.25 * S)
+        oracle.adamw_step(hp_orc, p_ref, m_ref, v_ref, ref, b_ref, norm_sq=S)
+        acc, acc_whole = dev_buf(acc0, 0)
+        acc_arg = acc if with_acc else None
+        gd, g_whole = dev_buf(g, grad_off, bf16=(dtype == "bf16"))
+        norm.fill_(S)
+        zs.adamw_step_tiled_sum(hp_gpu, st, acc_arg, gd, b, norm_sq=norm)
+        zs.grad_sum_norm_sq(acc_arg, gd, not with_acc, scale, norm_one)
+        zs.adamw_step_tiled_sum(hp_gpu, st_one, acc_arg, gd, b_one, norm_sq=norm_one)
+        acc2, _ = dev_buf(acc0, 0)
+        zs.grad_accum_norm_sq(acc2, gd, not with_acc, scale, norm_two)
+        zs.adamw_step_tiled(hp_gpu, st_two, acc2, b_two, norm_sq=norm_two)
+        torch.cuda.synchronize()
+        want = oracle.state_tile(p_ref, m_ref, v_ref, n, T)
+        got = to_np(st)
+        assert bits_equal(got, want), (t, identical_fraction(got, want))
+        assert bits_equal(to_np(b), b_ref), t
+        assert norm_one.item() == norm_two.item(), t
+        assert abs(math.sqrt(norm_one.item()) - math.sqrt(S)) <= NORM_TOL * math.sqrt(S)
+        assert bits_equal(to_np(st_one), to_np(st_two)), t
+        assert bits_equal(to_np(b_one), to_np(b_two)), t
+        assert bits_equal(to_np(acc), acc0), "the accumulator was written"
+        assert canary_ok(acc_whole, 0, n) and canary_ok(g_whole, grad_off, n)
+    assert canary_ok(stw, 0, st.numel()) and canary_ok(bw, b_off, n)
+    assert canary_ok(st_one_w, 0, st.numel()) and canary_ok(b_one_w, b_off, n)
+
+
+@pytest.mark.parametrize("with_acc", [True, False])
+def test_adamw_step_tiled_sum_dev_scalars_and_no_output(with_acc):
+    """Scalars from device memory give the host-scalar step's bits; without
+    a bf16 output the state is the same as with one."""
+    n = 3 * T + 77
+    rng = np.random.default_rng(41 + with_acc)
+    p0 = rng.uniform(-0.1, 0.1, n).astype(np.float32)
+    start = oracle.state_tile(p0, None, None, n, T)
+    st_h, _ = dev_buf(start, 0)
+    st_d, _ = dev_buf(start, 0)
+    st_n, _ = dev_buf(start, 0)
+    b_h = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+    b_d = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+    norm = torch.zeros(1, dtype=torch.float64, device="cuda")
+    sc = torch.empty(64, dtype=torch.uint8, device="cuda")
+    for t in range(1, 5):
+        acc, _ = dev_buf((rng.standard_normal(n) * 1e-2).astype(np.float32), 0)
+        gd, _ = dev_buf(_grad(rng, n, "bf16"), 0, bf16=True)
+        acc_arg = acc if with_acc else None
+        zs.grad_sum_norm_sq(acc_arg, gd, not with_acc, 1 / 32, norm)
+        hp = zs.AdamWConfig(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, grad_scale=1 / 32,
+                            max_norm=0.3, extra_norm_sq=0.01, step=t)
+        zs.adamw_step_tiled_sum(hp, st_h, acc_arg, gd, b_h, norm_sq=norm)
+        zs.adamw_step_tiled_sum(hp, st_n, acc_arg, gd, None, norm_sq=norm)
+        sc[:56].copy_(torch.frombuffer(bytearray(zs.scalars_bytes(hp)), dtype=torch.uint8))
+        zs.adamw_step_tiled_sum_dev(sc, st_d, acc_arg, gd, b_d, norm_sq=norm)
+        torch.cuda.synchronize()
+        assert bits_equal(to_np(st_d), to_np(st_h)), t
+        assert bits_equal(to_np(st_n), to_np(st_h)), t
+        assert bits_equal(to_np(b_d), to_np(b_h)), t
+
+
+@pytest.mark.parametrize("bad", [float("nan"), float("inf")])
+def test_adamw_step_tiled_sum_skips_on_nonfinite_norm(bad):
+    """A non-finite global norm leaves the state and the output as they were."""
+    n = 2 * T + 5
+    rng = np.random.default_rng(3)
+    start = oracle.state_tile(rng.uniform(-0.1, 0.1, n).astype(np.float32), None, None, n, T)
+    st, _ = dev_buf(start, 0)
+    b = torch.full((n,), 1.5, dtype=torch.bfloat16, device="cuda")
+    acc, _ = dev_buf((rng.standard_normal(n) * 1e-2).astype(np.float32), 0)
+    gd, _ = dev_buf(_grad(rng, n, "bf16"), 0, bf16=True)
+    norm = torch.tensor([bad], dtype=torch.float64, device="cuda")
+    hp, _ = _hp(1, max_norm=1.0)
+    zs.adamw_step_tiled_sum(hp, st, acc, gd, b, norm_sq=norm)
+    torch.cuda.synchronize()
+    assert bits_equal(to_np(st), start)
+    assert torch.all(b == 1.5)
+
+
+def test_adamw_step_tiled_sum_rejects():
+    n = 1000
+    st = torch.zeros(zs.state_tiled_numel(n), dtype=torch.float32, device="cuda")
+    acc = torch.zeros(n, dtype=torch.float32, device="cuda")
+    g = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+    hp, _ = _hp(1)
+    with pytest.raises(ValueError):   # size mismatch, caught in the binding
+        zs.adamw_step_tiled_sum(hp, st, acc[:10], g)
+    with pytest.raises(zs.ZShardError):   # the gradient overlapping the state
+        zs.adamw_step_tiled_sum(hp, st, acc, st[:n].view(torch.bfloat16)[:n])
+    with pytest.raises(zs.ZShardError):   # the accumulator overlapping the state
+        zs.adamw_step_tiled_sum(hp, st, st[8:8 + n], g)
+    with pytest.raises(zs.ZShardError):   # workspace too small
+        out = torch.zeros(1, dtype=torch.float64, device="cuda")
+        zs.grad_sum_norm_sq(acc, g, False, 1.0, out, torch.empty(8, dtype=torch.uint8, device="cuda"))

@@ -54,15 +54,19 @@ def host(t: torch.Tensor) -> np.ndarray:
 STATE_TILE = 8192   # ZS_STATE_TILE (test_abi checks the header against this value)
 
 
-def run_shard(w: workloads.Workload, n: int, sampled: bool, full_norm: bool, fused: bool = True,
+def run_shard(w: workloads.Workload, n: int, sampled: bool, full_norm: bool, fused=True,
               layout: str = "split"):
     """Drive the library and the oracle through w.steps steps of one shard.
-    fused: the last micro-batch forms the norm in the same pass
-    (grad_accum_norm_sq, as bench.py runs it); otherwise grad_accum for
-    every micro-batch, then grad_norm_sq.  layout "tiled": the optimizer
-    state in one tiled buffer and adamw_step_tiled (as bench.py times the
-    step); the compared elements are read at the positions the header's
-    layout gives them."""
+    fused True: the last micro-batch forms the norm in the same pass
+    (grad_accum_norm_sq); False: grad_accum for every micro-batch, then
+    grad_norm_sq; "sum" (tiled layout): the last micro-batch is not stored,
+    its norm pass and AdamW read the accumulator and its gradient
+    (grad_sum_norm_sq, adamw_step_tiled_sum: bench.py's step).  layout
+    "tiled": the optimizer state in one tiled buffer and adamw_step_tiled;
+    the compared elements are read at the positions the header's layout
+    gives them."""
+    one_pass = fused == "sum"
+    assert not one_pass or layout == "tiled"
     master = workloads.master_init(w, n, DEV)
     param = master.to(torch.bfloat16) if w.bf16_param else None
     if layout == "tiled":
@@ -93,11 +97,17 @@ def run_shard(w: workloads.Workload, n: int, sampled: bool, full_norm: bool, fus
     acc_full = np.empty(n, np.float32) if full_norm else None
     code = oracle.BF16 if w.grad_dtype == "bf16" else oracle.F32
     report = []
+    last = w.micro_batches - 1
     for t in range(1, w.steps + 1):
         t0 = time.perf_counter()
         for mb in range(w.micro_batches):
             g = workloads.grad_draw(w, n, t, mb, DEV)
-            if fused and mb == w.micro_batches - 1:
+            if one_pass and mb == last:
+                zs.grad_sum_norm_sq(acc if mb > 0 else None, g, mb == 0, w.grad_scale, norm, ws)
+                g_last = g
+                if mb > 0:   # the accumulator holds the earlier micro-batches' sum, bit for bit
+                    assert bits_equal(host(pick(acc)), acc_ref), (t, "acc before the last")
+            elif fused and mb == last:
                 zs.grad_accum_norm_sq(acc, g, mb == 0, w.grad_scale, norm, ws)
             else:
                 zs.grad_accum(acc, g, overwrite=(mb == 0))
@@ -112,13 +122,17 @@ def run_shard(w: workloads.Workload, n: int, sampled: bool, full_norm: bool, fus
             if (full_norm or not sampled) else None
         if s_ref is not None:
             assert abs(math.sqrt(s_gpu) - math.sqrt(s_ref)) <= NORM_TOL * math.sqrt(s_ref), (t, s_gpu, s_ref)
-        # the accumulated gradient itself is bit-exact
-        assert bits_equal(host(pick(acc)), acc_ref), (t, "acc")
+        # the accumulated gradient itself is bit-exact (the one-pass step never stores it)
+        if not one_pass:
+            assert bits_equal(host(pick(acc)), acc_ref), (t, "acc")
         extra = workloads.other_ranks_norm_sq(w, t, n)
         hp = zs.AdamWConfig(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
                             weight_decay=w.weight_decay, grad_scale=w.grad_scale, max_norm=w.max_norm,
                             extra_norm_sq=extra, step=t)
-        if layout == "tiled":
+        if one_pass:
+            zs.adamw_step_tiled_sum(hp, state, acc if last > 0 else None, g_last, param, norm_sq=norm)
+            del g_last
+        elif layout == "tiled":
             zs.adamw_step_tiled(hp, state, acc, param, norm_sq=norm)
         else:
             zs.adamw_step(hp, master, exp_avg, exp_avg_sq, acc, param, norm_sq=norm)
@@ -156,14 +170,19 @@ def run_shard(w: workloads.Workload, n: int, sampled: bool, full_norm: bool, fus
 
 @pytest.mark.parametrize("layout", ["split", "tiled"])
 @pytest.mark.parametrize("name,n,fused", [("llama7b_shard", 1_000_037, True), ("llama7b_shard", 1_000_037, False),
+                                          ("llama7b_shard", 1_000_037, "sum"),
                                           ("llama13b_shard_clip", 600_011, True),
                                           ("llama13b_shard_clip", 600_011, False),
-                                          ("zero3_70b_shard", 2_000_003, True), ("zero3_70b_shard", 2_000_003, False)])
+                                          ("llama13b_shard_clip", 600_011, "sum"),
+                                          ("zero3_70b_shard", 2_000_003, True), ("zero3_70b_shard", 2_000_003, False),
+                                          ("zero3_70b_shard", 2_000_003, "sum")])
 def test_workload_small(name, n, fused, layout):
     """Every element, at a reduced shard length.  The gradient std is scaled
     by sqrt(full/n) so the global norm, and with it the clipping pattern of
     the 13B workload, is the one of the full shard."""
     from dataclasses import replace
+    if fused == "sum" and layout != "tiled":
+        pytest.skip("the one-pass step runs on the tiled state")
     w = workloads.WORKLOADS[name]
     _, start, end, _ = zs.zero_shard_range(w.total, w.world, w.rank)
     w = replace(w, grad_std=w.grad_std * math.sqrt((end - start) / n))
@@ -356,11 +375,13 @@ def _tiled_chunk(state: torch.Tensor, c0: int, c1: int, k: int) -> np.ndarray:
 @pytest.mark.parametrize("name,steps", [("llama7b_shard", 3), ("zero3_70b_shard", 2), ("llama13b_shard_clip", 2)])
 def test_full_shard_every_element(name, steps):
     """The real shard lengths through the bench's launch configuration
-    (grad_accum per micro-batch, grad_accum_norm_sq for the last,
-    adamw_step_tiled with the bf16 re-cast, clipped where the workload
-    clips) next to the oracle stepping the same state from the same inputs.
-    Every step compares, element by element: the accumulator (bit-exact,
-    whole shard), the squared norm over the whole shard (1e-5), and the
+    (grad_accum per micro-batch but the last; for the last, grad_sum_norm_sq
+    and adamw_step_tiled_sum with the bf16 re-cast, clipped where the
+    workload clips, the sum never stored) next to the oracle stepping the
+    same state from the same inputs (accumulating every micro-batch, then
+    its norm and AdamW).  Every step compares, element by element: the
+    accumulator before the last micro-batch (bit-exact, whole shard), the
+    squared norm over the whole shard (1e-5), and the
     master, exp_avg, exp_avg_sq and bf16 parameter of the compared ranges,
     read back in 256 MiB chunks.  Mode "full": the compared range is the
     whole shard; mode "slices" (when the host lacks the memory for the
@@ -404,7 +425,12 @@ def test_full_shard_every_element(name, steps):
         for mb in range(w.micro_batches):
             g = workloads.grad_draw(w, n, t, mb, DEV)
             if mb == last:
-                zs.grad_accum_norm_sq(acc, g, mb == 0, w.grad_scale, norm, ws)
+                if mb > 0:   # the accumulator before the last micro-batch, bit-exact
+                    for c0 in range(0, n, CMP_CHUNK):
+                        c1 = min(c0 + CMP_CHUNK, n)
+                        assert bits_equal(host(acc[c0:c1]), acc_ref[c0:c1]), (t, "acc", c0)
+                zs.grad_sum_norm_sq(acc if mb > 0 else None, g, mb == 0, w.grad_scale, norm, ws)
+                g_last = g
             else:
                 zs.grad_accum(acc, g, overwrite=(mb == 0))
             oracle.grad_accum(acc_ref, host(g), code, overwrite=(mb == 0))
@@ -412,13 +438,11 @@ def test_full_shard_every_element(name, steps):
         s_gpu = float(norm.item())
         s_ref = oracle.grad_norm_sq(acc_ref, w.grad_scale)
         assert abs(math.sqrt(s_gpu) - math.sqrt(s_ref)) <= NORM_TOL * math.sqrt(s_ref), (t, s_gpu, s_ref)
-        for c0 in range(0, n, CMP_CHUNK):
-            c1 = min(c0 + CMP_CHUNK, n)
-            assert bits_equal(host(acc[c0:c1]), acc_ref[c0:c1]), (t, "acc", c0)
         extra = workloads.other_ranks_norm_sq(w, t, n)
         hp = zs.AdamWConfig(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
                             grad_scale=w.grad_scale, max_norm=w.max_norm, extra_norm_sq=extra, step=t)
-        zs.adamw_step_tiled(hp, state, acc, param, norm_sq=norm)
+        zs.adamw_step_tiled_sum(hp, state, acc if last > 0 else None, g_last, param, norm_sq=norm)
+        del g_last
         ohp = oracle.make_hp(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, w.grad_scale, w.max_norm, extra, t)
         coef_gpu = oracle.clip_coef(s_gpu, extra, w.max_norm)
         coef = oracle.clip_coef(s_ref, extra, w.max_norm)
