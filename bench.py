@@ -48,7 +48,7 @@ K_ADAMW_SPLIT = "zs::(anonymous namespace)::adamw_kernel<4, 1, 64, false, false,
 # the step's AdamW on the last micro-batch's sum: bf16 gradient alone (1) or onto the accumulator (2)
 K_ADAMW_SUM_BF16 = "zs::(anonymous namespace)::adamw_kernel<4, 1, 64, false, true, true, 1>"
 K_ADAMW_SUM_ACC_BF16 = "zs::(anonymous namespace)::adamw_kernel<4, 1, 64, false, true, true, 2>"
-K_SUM_NORM_ADD = "zs::(anonymous namespace)::sum_norm_kernel<1, 1, 1, true, true, false>"
+K_SUM_NORM_ADD = "zs::(anonymous namespace)::sum_norm_kernel<1, 1, 2, true, true, false>"
 K_SUM_NORM_FIRST = "zs::(anonymous namespace)::sum_norm_kernel<4, 1, 1, true, true, true>"
 K_ACCUM_FIRST = "zs::(anonymous namespace)::accum_kernel<1, 64, true, true, true, false>"
 K_ACCUM_ADD = "zs::(anonymous namespace)::accum_kernel<1, 64, true, true, false, false>"
@@ -879,8 +879,9 @@ def main():
         single = wl.micro_batches == 1
         return [entry("adamw_step_tiled_sum", K_ADAMW_SUM_BF16 if single else K_ADAMW_SUM_ACC_BF16, nn,
                       b["adamw_step_sum"] * nn),
+                # one wave per 1024 elements (single bf16 micro-batch), else two blocks of 256 per wave
                 entry("grad_sum_norm_sq_last", K_SUM_NORM_FIRST if single else K_SUM_NORM_ADD, nn,
-                      b["grad_sum_norm_sq_last"] * nn + 8 * fused_norm_partials(wl, nn), 1024 if single else 256)]
+                      b["grad_sum_norm_sq_last"] * nn + 8 * fused_norm_partials(wl, nn), 1024 if single else 512)]
 
     def two_call_entries(wl, nn):
         b = step_bytes_per_elem(wl)
