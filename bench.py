@@ -868,10 +868,19 @@ def main():
 
     # kernels whose HBM traffic has records (bench_pmc.py): label, kernel,
     # shard length, algorithmic bytes per launch
-    def entry(label, kernel, nn, nbytes, per_wg=256):
+    def entry(label, kernel, nn, nbytes, per_wg=256, workgroups=None):
         # one-wave workgroups of per_wg elements: the launch's grid in work-items
+        wgs = -(-nn // per_wg) if workgroups is None else workgroups
         return {"label": label, "kernel": kernel, "shard_elems": nn, "algorithmic_bytes": nbytes,
-                "grid": -(-nn // per_wg) * 64}
+                "grid": wgs * 64}
+
+    def sum_norm_workgroups(nn, single):
+        """grad_sum_norm_sq's one-wave workgroups: 8 x ceil(blocks per XCD
+        / blocks per wave), blocks of 1024 elements (single bf16 micro-batch,
+        one per wave) or 256 (two per wave)."""
+        span, per_wave = (1024, 1) if single else (256, 2)
+        blocks = -(-nn // span)
+        return 8 * -(-(-(-blocks // 8)) // per_wave)
 
     def sum_entries(wl, nn):
         """The step's last micro-batch and AdamW (bf16 gradients)."""
@@ -879,9 +888,9 @@ def main():
         single = wl.micro_batches == 1
         return [entry("adamw_step_tiled_sum", K_ADAMW_SUM_BF16 if single else K_ADAMW_SUM_ACC_BF16, nn,
                       b["adamw_step_sum"] * nn),
-                # one wave per 1024 elements (single bf16 micro-batch), else two blocks of 256 per wave
                 entry("grad_sum_norm_sq_last", K_SUM_NORM_FIRST if single else K_SUM_NORM_ADD, nn,
-                      b["grad_sum_norm_sq_last"] * nn + 8 * fused_norm_partials(wl, nn), 1024 if single else 512)]
+                      b["grad_sum_norm_sq_last"] * nn + 8 * fused_norm_partials(wl, nn),
+                      workgroups=sum_norm_workgroups(nn, single))]
 
     def two_call_entries(wl, nn):
         b = step_bytes_per_elem(wl)

@@ -148,54 +148,62 @@ hipError_t dispatch(float* acc, const void* grad, int grad_bf16, int64_t n, bool
 
 // The squared norm of the fused pass without its store, for a step that
 // forms the last micro-batch's sum again as it reads it (the AdamW step's
-// summed-gradient forms).  Each wave runs, for K consecutive one-wave
-// workgroups of accum_kernel<Q, 64, ...> (virtual blocks vb0 .. vb0+K-1 of
-// nvb), exactly what each computes for its partial: the same Q groups per
-// lane, sums, butterfly and slot, so the partials, and the norm formed from
-// them, are bit for bit the fused pass's.  Read-only: acc (unless OVERWRITE)
-// and grad, dword alignment suffices for both; on the vector path every load
-// of the wave's K blocks is issued before the first square.
+// summed-gradient forms).  Each wave runs, for K of the one-wave workgroups
+// of accum_kernel<Q, 64, ...> (virtual blocks of nvb), exactly what each
+// computes for its partial: the same Q groups per lane, sums, butterfly
+// and slot, so the partials, and the norm formed from them, are bit for bit
+// the fused pass's.  The K blocks of a wave are those its XCD would have run
+// (workgroup B runs on XCD B mod 8; its blocks are 8j + B mod 8 for K
+// consecutive j), so its partials fall in its XCD's run of slots and every
+// line of partials is still written by one XCD.  Read-only: acc (unless
+// OVERWRITE) and grad, dword alignment suffices for both; on the vector path
+// every load of the wave's K blocks is issued before the first square.
 template <int Q, int W, int K, bool VEC, bool BF16, bool OVERWRITE>
 __global__ __launch_bounds__(W * 64) void sum_norm_kernel(const float* __restrict__ acc,
                                                           const void* __restrict__ grad, int64_t n, int64_t nvb,
                                                           float scale, double* __restrict__ partials) {
     constexpr int64_t kGroup = 256;   // one wave's 64 lanes x 4 elements
     constexpr int64_t kSpan = kGroup * Q;   // elements per virtual block
-    const int64_t vb0 = ((int64_t)blockIdx.x * W + (threadIdx.x >> 6)) * K;
-    if (vb0 >= nvb) return;   // the last workgroup's spare waves (whole waves)
+    const int64_t wave = threadIdx.x >> 6;
+    if (xcd_block(blockIdx.x, wave, 0, W, K) >= nvb) return;   // no block for this wave (whole waves)
     const int lane = threadIdx.x & 63;
-    if (VEC && (vb0 + K) * kSpan <= n) {   // all K blocks whole
+    const int64_t vb_last = xcd_block(blockIdx.x, wave, K - 1, W, K);
+    if (VEC && (vb_last + 1) * kSpan <= n) {   // all K blocks exist and are whole
         f32x4 g[K * Q], a[K * Q];
 #pragma unroll
-        for (int k = 0; k < K * Q; ++k) {
-            const int64_t at = vb0 * kSpan + k * kGroup + lane * 4;
-            g[k] = load4<BF16>(grad, at);
-            if (!OVERWRITE) a[k] = ld_stream_f32x4_a4(acc + at);
+        for (int k = 0; k < K; ++k) {
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                const int64_t at = xcd_block(blockIdx.x, wave, k, W, K) * kSpan + q * kGroup + lane * 4;
+                g[k * Q + q] = load4<BF16>(grad, at);
+                if (!OVERWRITE) a[k * Q + q] = ld_stream_f32x4_a4(acc + at);
+            }
         }
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             double s0 = 0.0, s1 = 0.0;
 #pragma unroll
             for (int q = 0; q < Q; ++q) {
-                const int j = k * Q + q;
-                const f32x4 r = OVERWRITE ? g[j]
-                                          : f32x4{a[j].x + g[j].x, a[j].y + g[j].y, a[j].z + g[j].z,
-                                                  a[j].w + g[j].w};
+                const int i = k * Q + q;
+                const f32x4 r = OVERWRITE ? g[i]
+                                          : f32x4{a[i].x + g[i].x, a[i].y + g[i].y, a[i].z + g[i].z,
+                                                  a[i].w + g[i].w};
                 const float rv[4] = {r.x, r.y, r.z, r.w};
                 add_squares4(rv, scale, s0, s1);
             }
             const double total = wave_sum(s0 + s1);
-            if (lane == 0) partials[xcd_slot(vb0 + k, nvb)] = total;
+            if (lane == 0) partials[xcd_slot(xcd_block(blockIdx.x, wave, k, W, K), nvb)] = total;
         }
         return;
     }
     // the ragged end: block by block, element by element (out-of-range
     // elements add +0), as the fused kernel's ragged tile
-    for (int k = 0; k < K && vb0 + k < nvb; ++k) {
+    for (int k = 0; k < K && xcd_block(blockIdx.x, wave, k, W, K) < nvb; ++k) {
+        const int64_t vb = xcd_block(blockIdx.x, wave, k, W, K);
         double s0 = 0.0, s1 = 0.0;
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
-            const int64_t first = (vb0 + k) * kSpan + q * kGroup + lane * 4;
+            const int64_t first = vb * kSpan + q * kGroup + lane * 4;
             float rv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -208,15 +216,16 @@ __global__ __launch_bounds__(W * 64) void sum_norm_kernel(const float* __restric
             add_squares4(rv, scale, s0, s1);
         }
         const double total = wave_sum(s0 + s1);
-        if (lane == 0) partials[xcd_slot(vb0 + k, nvb)] = total;
+        if (lane == 0) partials[xcd_slot(vb, nvb)] = total;
     }
 }
 
 // One-wave workgroups, uncapped, as the fused kernel; each wave takes two
-// virtual blocks of the accumulating shape (Q = 1: 82.6 % of the HBM peak on
-// gfx950 for a bf16 gradient onto the accumulator, against 81.4 % for one,
-// 79.7 % for four; two or four waves per workgroup 76-79 %) and one of the
-// overwriting bf16 shape (Q = 4: 90 %, against 88 % for two).
+// blocks of the accumulating shape (Q = 1: 89.3 % of the HBM peak on gfx950
+// for a bf16 gradient onto the accumulator, against 81.4 % for one and 85.5 %
+// for four; two blocks that are neighbours in memory instead of in their
+// XCD's run measured 82.6 %, their partials written 2x) and one of the
+// overwriting bf16 shape (Q = 4: 92.5 %, against 91.8 % for two).
 constexpr int kSumNormWaves = 1;   // waves per workgroup of sum_norm_kernel
 template <int Q>
 constexpr int sum_norm_blocks() { return Q == 1 ? 2 : 1; }   // virtual blocks per wave
@@ -230,8 +239,7 @@ hipError_t launch_sum_norm(const float* acc, const void* grad, int64_t n, float 
         const int64_t m = launch_piece(n, off);
         const int64_t nvb = (m + per_block<Q>() - 1) / per_block<Q>();
         constexpr int K = sum_norm_blocks<Q>();
-        const int64_t per_wg = (int64_t)kSumNormWaves * K;
-        const int64_t blocks = (nvb + per_wg - 1) / per_wg;
+        const int64_t blocks = sum_norm_grid(nvb, kSumNormWaves, K);
         hipLaunchKernelGGL((sum_norm_kernel<Q, kSumNormWaves, K, VEC, BF16, OVERWRITE>),
                            dim3((unsigned)blocks),
                            dim3(kSumNormWaves * 64), 0, stream, OVERWRITE ? nullptr : acc + off,

@@ -134,6 +134,20 @@ __host__ __device__ constexpr int64_t xcd_slot(int64_t b, int64_t nb) {
     return x * q + (x < r ? x : r) + j;
 }
 
+// The block a wave runs when one launch's waves each take K of the blocks a
+// grid of one-wave workgroups would have run, and the workgroups W waves
+// each: the k-th block of wave w of workgroup B is one its XCD (B mod 8)
+// would have run, 8j + B mod 8 for K consecutive j, so what the wave writes
+// per block at xcd_slot stays in that XCD's run of slots.  A grid of
+// 8 * ceil(ceil(nb / 8) / (W * K)) workgroups covers every block of [0, nb)
+// once (the blocks at or past nb are skipped).
+__host__ __device__ constexpr int64_t xcd_block(int64_t B, int64_t w, int64_t k, int64_t W, int64_t K) {
+    return 8 * (((B >> 3) * W + w) * K + k) + (B & 7);
+}
+__host__ __device__ constexpr int64_t sum_norm_grid(int64_t nb, int64_t W, int64_t K) {
+    return 8 * (((nb + 7) / 8 + W * K - 1) / (W * K));
+}
+
 // Launchers: enqueue on `stream`, return the hipError_t of the (first failed) launch.
 // vec_ok: every stream but the write-only output (bf16 re-cast, ZeRO-1
 // update) allows the 128-bit path; out_aligned: that output is 16-byte

@@ -41,8 +41,34 @@ static int check_xcd_slots() {
     return 0;
 }
 
+// The waves of a launch that each take K blocks (zs::xcd_block, grid
+// zs::sum_norm_grid) run every block of [0, nb) once, and each block on the
+// XCD that would have run it as a one-wave workgroup of its own.
+static int check_xcd_blocks() {
+    for (int64_t W : {1, 2, 4})
+        for (int64_t K : {1, 2, 3, 4, 8})
+            for (int64_t nb = 1; nb <= 700; ++nb) {
+                std::vector<unsigned char> seen((size_t)nb, 0);
+                const int64_t grid = zs::sum_norm_grid(nb, W, K);
+                if (grid % 8) return 1;
+                for (int64_t B = 0; B < grid; ++B)
+                    for (int64_t w = 0; w < W; ++w)
+                        for (int64_t k = 0; k < K; ++k) {
+                            const int64_t vb = zs::xcd_block(B, w, k, W, K);
+                            if (vb < 0) return 2;
+                            if (vb >= nb) continue;
+                            if (seen[(size_t)vb] || (vb & 7) != (B & 7)) return 3;
+                            seen[(size_t)vb] = 1;
+                        }
+                for (unsigned char c : seen)
+                    if (!c) return 4;
+            }
+    return 0;
+}
+
 int main() {
     CHECK(check_xcd_slots() == 0, 30);
+    CHECK(check_xcd_blocks() == 0, 32);
     // the no-alloc norm: sizes beyond its scratch and bad arguments, before any device call
     CHECK(grad_accum_norm_sq_noalloc((float*)fake(0), fake(1 << 30), ZS_BF16, ZS_NOALLOC_MAX_ELEMS + 1, 0, 1.0,
                                      (double*)fake(3ull << 30), nullptr) == ZS_EINVAL, 31);
