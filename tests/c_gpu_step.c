@@ -14,6 +14,10 @@
  * bit-identical to the oracle's (accumulator, master, moments, bf16 output).
  * The same three accumulations once more with grad_accum_norm_sq_noalloc for
  * the last (no workspace) must give the same accumulator and norm bit for bit.
+ * And the one-pass form of the same step: two accumulations, then
+ * grad_sum_norm_sq and adamw_step_tiled_sum on accumulator + third gradient:
+ * the same norm bit for bit, the same state and bf16 output as the oracle's,
+ * the accumulator left holding the first two micro-batches' sum.
  * Prints "c gpu step: ok" and exits 0, else the number of the failed check.
  */
 #include <math.h>
@@ -78,7 +82,9 @@ int main(void)
     float *d_master, *d_state, *d_acc, *d_p, *d_m, *d_v;
     uint16_t *d_g, *d_b;
     double *d_norm, *d_norm_ref, *d_norm2;
-    float* d_acc2;
+    float *d_acc2, *d_acc3, *d_state2;
+    uint16_t* d_b2;
+    double* d_norm3;
     void* d_ws;
     const int64_t ws_bytes = grad_accum_norm_sq_workspace_bytes(n);
     const int64_t st = state_tiled_numel(n);
@@ -95,6 +101,10 @@ int main(void)
     HIPOK(hipMalloc((void**)&d_norm_ref, sizeof(double)), 3);
     HIPOK(hipMalloc((void**)&d_norm2, sizeof(double)), 3);
     HIPOK(hipMalloc((void**)&d_acc2, sizeof(float) * n), 3);
+    HIPOK(hipMalloc((void**)&d_acc3, sizeof(float) * n), 3);
+    HIPOK(hipMalloc((void**)&d_state2, sizeof(float) * st), 3);
+    HIPOK(hipMalloc((void**)&d_b2, sizeof(uint16_t) * n), 3);
+    HIPOK(hipMalloc((void**)&d_norm3, sizeof(double)), 3);
     HIPOK(hipMalloc(&d_ws, (size_t)ws_bytes), 3);
     HIPOK(hipMemcpy(d_master, p_ref, sizeof(float) * n, hipMemcpyHostToDevice), 4);
     HIPOK(hipMemcpy(d_g, g, sizeof(uint16_t) * n * M, hipMemcpyHostToDevice), 4);
@@ -128,6 +138,16 @@ int main(void)
     HIPOK(hipMemcpy(back, d_acc2, sizeof(float) * n, hipMemcpyDeviceToHost), 22);
     CHECK(memcmp(back, acc_ref, sizeof(float) * n) == 0, 22);
 
+    /* the one-pass form: the third micro-batch folded into the norm and the step */
+    CHECK(state_tile(d_master, NULL, NULL, d_state2, n, NULL) == ZS_OK, 23);
+    for (int k = 0; k < M - 1; ++k)
+        CHECK(grad_accum(d_acc3, d_g + (size_t)k * n, ZS_BF16, n, k == 0, NULL) == ZS_OK, 23);
+    CHECK(grad_sum_norm_sq(d_acc3, d_g + (size_t)(M - 1) * n, ZS_BF16, n, 0, scale, d_norm3, d_ws, ws_bytes, NULL)
+          == ZS_OK, 23);
+    double S_one = 0.0;
+    HIPOK(hipMemcpy(&S_one, d_norm3, sizeof(double), hipMemcpyDeviceToHost), 24);
+    CHECK(memcmp(&S_one, &S_gpu, sizeof(double)) == 0, 24);
+
     const double max_norm = 0.5 * sqrt(S), extra = 0.2 * S;   /* the clip applies */
     zs_adamw hp = {3e-4, 0.9, 0.95, 1e-8, 0.1, scale, max_norm, extra, 1};
     orc_adamw_hp ohp = {3e-4, 0.9, 0.95, 1e-8, 0.1, scale, max_norm, extra, 1};
@@ -144,10 +164,27 @@ int main(void)
     CHECK(memcmp(back, v_ref, sizeof(float) * n) == 0, 17);
     HIPOK(hipMemcpy(back16, d_b, sizeof(uint16_t) * n, hipMemcpyDeviceToHost), 18);
     CHECK(memcmp(back16, b_ref, sizeof(uint16_t) * n) == 0, 18);
+    CHECK(adamw_step_tiled_sum(&hp, d_state2, d_acc3, d_g + (size_t)(M - 1) * n, ZS_BF16, d_b2, n, d_norm_ref, NULL)
+          == ZS_OK, 25);
+    CHECK(state_untile(d_state2, d_p, d_m, d_v, n, NULL) == ZS_OK, 25);
+    HIPOK(hipDeviceSynchronize(), 25);
+    HIPOK(hipMemcpy(back, d_p, sizeof(float) * n, hipMemcpyDeviceToHost), 26);
+    CHECK(memcmp(back, p_ref, sizeof(float) * n) == 0, 26);
+    HIPOK(hipMemcpy(back, d_m, sizeof(float) * n, hipMemcpyDeviceToHost), 26);
+    CHECK(memcmp(back, m_ref, sizeof(float) * n) == 0, 26);
+    HIPOK(hipMemcpy(back, d_v, sizeof(float) * n, hipMemcpyDeviceToHost), 26);
+    CHECK(memcmp(back, v_ref, sizeof(float) * n) == 0, 26);
+    HIPOK(hipMemcpy(back16, d_b2, sizeof(uint16_t) * n, hipMemcpyDeviceToHost), 27);
+    CHECK(memcmp(back16, b_ref, sizeof(uint16_t) * n) == 0, 27);
+    /* the accumulator holds the first M - 1 micro-batches' sum */
+    for (int k = 0; k < M - 1; ++k) CHECK(orc_grad_accum(acc_ref, g + (size_t)k * n, 1, n, k == 0) == 0, 28);
+    HIPOK(hipMemcpy(back, d_acc3, sizeof(float) * n, hipMemcpyDeviceToHost), 28);
+    CHECK(memcmp(back, acc_ref, sizeof(float) * n) == 0, 28);
     CHECK(zs_last_hip_error() == 0, 19);
 
     hipFree(d_master); hipFree(d_state); hipFree(d_acc); hipFree(d_p); hipFree(d_m); hipFree(d_v);
     hipFree(d_g); hipFree(d_b); hipFree(d_norm); hipFree(d_norm_ref); hipFree(d_ws); hipFree(d_norm2); hipFree(d_acc2);
+    hipFree(d_acc3); hipFree(d_state2); hipFree(d_b2); hipFree(d_norm3);
     free(p_ref); free(m_ref); free(v_ref); free(acc_ref); free(b_ref); free(g); free(back); free(back16);
     printf("c gpu step: ok\n");
     return 0;

@@ -306,6 +306,64 @@ def test_accumulations_across_pieces(offset):
 
 
 @pytest.mark.parametrize("offset", [0, 1])
+def test_one_pass_last_micro_batch_across_pieces(offset):
+    """grad_sum_norm_sq and a clipped adamw_step_tiled_sum over N elements,
+    on accumulator + bf16 gradient and on the gradient alone (offset 1: the
+    gradient 2 bytes off a 4-byte boundary, the element-wise paths): the
+    norm bit for bit grad_accum_norm_sq's and within the bar of the
+    oracle's over the whole buffer, the state and bf16 output bit-exact on
+    the sample, the accumulator unchanged."""
+    need_gib(80)
+    log(f"one-pass last micro-batch across pieces n={N} offset={offset}")
+    idx = sample_indices(N, seed=81 + offset)
+    where = (idx // STATE_TILE) * (3 * STATE_TILE) + idx % STATE_TILE
+    master = fill_uniform(buffer(N, 0), -0.1, 0.1, 801)
+    state = torch.empty(zs.state_tiled_numel(N), dtype=torch.float32, device=DEV)
+    zs.state_tile(master, None, None, state)
+    p_ref = host(master[idx])
+    del master
+    m_ref, v_ref = np.zeros(idx.numel(), np.float32), np.zeros(idx.numel(), np.float32)
+    b_ref = np.empty(idx.numel(), np.uint16)
+    bf16 = buffer(N, offset, torch.bfloat16)
+    acc = fill_normal(buffer(N, 0), 1e-3, 802)
+    g = bf16_normal(N, offset, 1e-3, 803)
+    scale, extra, max_norm = 1.0 / 64, 2.0, 1.0
+    ws = torch.empty(zs.grad_accum_norm_sq_workspace_bytes(N), dtype=torch.uint8, device=DEV)
+    acc_s, g_s = host(acc[idx]), host(g[idx])
+    for step, with_acc in ((3, True), (4, False)):
+        log(f"  step {step}: {'accumulator + gradient' if with_acc else 'the gradient alone'}")
+        a = acc if with_acc else None
+        norm = torch.zeros(1, dtype=torch.float64, device=DEV)
+        zs.grad_sum_norm_sq(a, g, not with_acc, scale, norm, ws)
+        full = host(acc) if with_acc else np.empty(N, np.float32)
+        oracle.grad_accum(full, host(g), oracle.BF16, overwrite=not with_acc)
+        S = oracle.grad_norm_sq(full, scale)
+        del full
+        assert abs(math.sqrt(norm.item()) - math.sqrt(S)) <= NORM_TOL * math.sqrt(S)
+        stored = buffer(N, 0)
+        stored.copy_(acc)
+        norm2 = torch.zeros(1, dtype=torch.float64, device=DEV)
+        zs.grad_accum_norm_sq(stored, g, not with_acc, scale, norm2, ws)
+        assert norm.item() == norm2.item()
+        del stored
+        assert oracle.clip_coef(S, extra, max_norm) < 1.0
+        norm.fill_(S)
+        hp = zs.AdamWConfig(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, grad_scale=scale,
+                            max_norm=max_norm, extra_norm_sq=extra, step=step)
+        zs.adamw_step_tiled_sum(hp, state, a, g, bf16, norm_sq=norm)
+        gsum = acc_s.copy() if with_acc else np.empty(idx.numel(), np.float32)
+        oracle.grad_accum(gsum, g_s, oracle.BF16, overwrite=not with_acc)
+        H = oracle.make_hp(3e-4, 0.9, 0.95, 1e-8, 0.1, scale, max_norm, extra, step)
+        assert oracle.adamw_step(H, p_ref, m_ref, v_ref, gsum, b_ref, norm_sq=S) == 0
+        for k, (name, ref) in enumerate((("master", p_ref), ("m", m_ref), ("v", v_ref))):
+            check(f"step {name}", state, where + k * STATE_TILE, ref)
+        check("bf16", bf16, idx, b_ref)
+        check("acc unchanged", acc, idx, acc_s)
+    del state, bf16, acc, g, ws
+    release()
+
+
+@pytest.mark.parametrize("offset", [0, 1])
 def test_reduce_chunks_across_pieces(offset):
     """Three bf16 rank chunks (the third the first again) summed into acc
     over N elements, overwriting: bit-exact on the sample."""
