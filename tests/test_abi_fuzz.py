@@ -1,7 +1,8 @@
 """Property tests of the C ABI's host-side validation (CPU only).
 
-Random argument sets for adamw_step, flat_pack and flat_unpack, and for
-the tiled-state calls (adamw_step_tiled, state_tile, state_untile): sizes,
+Random argument sets for adamw_step, flat_pack and flat_unpack, for the
+tiled-state calls (adamw_step_tiled, state_tile, state_untile, and the
+one-pass last micro-batch: adamw_step_tiled_sum, grad_sum_norm_sq): sizes,
 alignments, null pointers, overlapping buffers and hyperparameters.  A
 Python model of the rules include/zshard.h documents (and of the order in
 which they are checked) predicts each return code.  Only argument sets the
@@ -335,3 +336,98 @@ def test_adam_update_tiled_validation_matches_the_documented_rules(hp, ptrs, n, 
     c = B.AdamW(*hp[:8], hp[8])
     got = zs.lib().adam_update_tiled(ctypes.byref(c), mo or None, g or None, u or None, n, norm or None, None)
     assert got == want, (hp, [hex(p) for p in ptrs], n, hex(norm))
+
+
+# ---------------------------------------------------------------------------
+# the one-pass last micro-batch: adamw_step_tiled_sum, grad_sum_norm_sq
+# ---------------------------------------------------------------------------
+
+F32, BF16 = B.ZS_F32, B.ZS_BF16
+dtypes = st.sampled_from([F32, BF16, BF16, 7])
+
+
+def tiled_sum_model(hp, state, acc, g, dt, b, n, norm):
+    rc = hp_model(hp, n, norm)
+    if rc is not None:
+        return rc
+    if dt not in (F32, BF16):
+        return EINVAL
+    if n == 0:
+        return OK
+    gsz = 4 if dt == F32 else 2
+    if not (state and g):
+        return EINVAL
+    if state % 16 or g % gsz or (acc and acc % 4) or (b and b % 2):
+        return EINVAL
+    bufs = [(state, tiled_bytes(n), True), (acc, 4 * n if acc else 0, False), (g, gsz * n, False),
+            (b, 2 * n if b else 0, True)]
+    for i in range(4):
+        for j in range(i + 1, 4):
+            if overlap(bufs[i][0], bufs[i][1], bufs[j][0], bufs[j][1]):
+                return EOVERLAP
+        if norm and bufs[i][2] and overlap(bufs[i][0], bufs[i][1], norm, 8):
+            return EOVERLAP
+    return None
+
+
+@SETTINGS
+@given(hp=hyperparameters(), ptrs=st.tuples(big_pointers, big_pointers, big_pointers, big_pointers),
+       dt=dtypes, n=tiled_sizes,
+       norm=st.one_of(st.just(0), st.builds(lambda slot, off: BASE + slot * 65536 + off,
+                                            st.integers(0, 7), st.sampled_from([0, 8, 40000, 4]))))
+def test_adamw_step_tiled_sum_validation_matches_the_documented_rules(hp, ptrs, dt, n, norm):
+    state, acc, g, b = ptrs
+    want = tiled_sum_model(hp, state, acc, g, dt, b, n, norm)
+    if want is None:
+        return   # a valid call would launch a kernel: not made here
+    c = B.AdamW(*hp[:8], hp[8])
+    got = zs.lib().adamw_step_tiled_sum(ctypes.byref(c), state or None, acc or None, g or None, dt, b or None, n,
+                                        norm or None, None)
+    assert got == want, (hp, [hex(p) for p in ptrs], dt, n, hex(norm))
+
+
+def sum_norm_workspace(n):
+    return 0 if n <= 0 else ((n + 255) // 256 + 2048) * 8
+
+
+def sum_norm_model(acc, g, dt, n, overwrite, scale, out, ws, wsb):
+    if dt not in (F32, BF16) or not (0 <= n <= MAX_ELEMS):
+        return EINVAL
+    if not out or out % 8:
+        return EINVAL
+    if not (scale > 0.0 and math.isfinite(scale)):
+        return EINVAL
+    gsz = 4 if dt == F32 else 2
+    if overwrite:
+        acc = 0   # not read
+    if n > 0 and (not g or g % gsz):
+        return EINVAL
+    if n > 0 and not overwrite and (not acc or acc % 4):
+        return EINVAL
+    need = sum_norm_workspace(n)
+    if need > 0 and (not ws or ws % 8):
+        return EINVAL
+    if wsb < need:
+        return B.ZS_EWORKSPACE
+    acc_bytes = 4 * n if acc else 0
+    if (overlap(acc, acc_bytes, out, 8) or overlap(g, gsz * n, out, 8) or overlap(ws, need, out, 8)
+            or overlap(ws, need, acc, acc_bytes) or overlap(ws, need, g, gsz * n)):
+        return EOVERLAP
+    return None
+
+
+@SETTINGS
+@given(ptrs=st.tuples(pointers, pointers, pointers, pointers), dt=dtypes,
+       n=st.sampled_from([-1, 0, 1, 3, 255, 1000, 5000, MAX_ELEMS + 1]), overwrite=st.booleans(),
+       scale=st.sampled_from([1.0 / 64, 1.0 / 64, 0.0, -1.0, math.inf, math.nan]),
+       ws_short=st.sampled_from([0, 0, 0, 8]))
+def test_grad_sum_norm_sq_validation_matches_the_documented_rules(ptrs, dt, n, overwrite, scale, ws_short):
+    acc, g, out, ws = ptrs
+    need = sum_norm_workspace(n)
+    wsb = max(need - ws_short, 0)
+    want = sum_norm_model(acc, g, dt, n, overwrite, scale, out, ws, wsb)
+    if want is None:
+        return   # a valid call would launch a kernel (n == 0 too: it writes the norm 0)
+    got = zs.lib().grad_sum_norm_sq(acc or None, g or None, dt, n, 1 if overwrite else 0, scale, out or None,
+                                    ws or None, wsb, None)
+    assert got == want, ([hex(p) for p in ptrs], dt, n, overwrite, scale, wsb)
