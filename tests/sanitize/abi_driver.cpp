@@ -137,6 +137,29 @@ int main() {
     CHECK(grad_norm_sq(f, 1 << 20, 1.0, d, d + 1, 8, nullptr) == ZS_EWORKSPACE, 8);   // needs 8 KiB
     CHECK(grad_accum_norm_sq(f, f + 4096, ZS_BF16, 1 << 16, 1, 1.0, d, d + 8, 16, nullptr) == ZS_EWORKSPACE, 8);
 
+    // the one-pass last micro-batch: a missing accumulator only where one is read, overlaps, limits
+    uint16_t* gb = static_cast<uint16_t*>(fake(1ull << 28));
+    CHECK(grad_sum_norm_sq(nullptr, gb, ZS_BF16, 1 << 16, 0, 1.0, d, d + 8, 1 << 30, nullptr) == ZS_EINVAL, 33);
+    CHECK(grad_sum_norm_sq(nullptr, gb, ZS_BF16, 1 << 16, 1, 1.0, d, d + 8, 16, nullptr) == ZS_EWORKSPACE, 33);
+    CHECK(grad_sum_norm_sq(f, gb + 1, ZS_F32, 1 << 16, 0, 1.0, d, d + 8, 1 << 30, nullptr) == ZS_EINVAL, 33);
+    CHECK(grad_sum_norm_sq(f, gb, ZS_BF16, 1 << 16, 0, 1.0, reinterpret_cast<double*>(f + 64), d + 8, 1 << 30,
+                           nullptr) == ZS_EOVERLAP, 33);
+    CHECK(grad_sum_norm_sq(f, gb, ZS_BF16, (int64_t(1) << 39) + 1, 0, 1.0, d, d + 8, 1 << 30, nullptr) == ZS_EINVAL,
+          33);
+    CHECK(adamw_step_tiled_sum(&bad, st, f, gb, ZS_BF16, nullptr, 16, nullptr, nullptr) == ZS_EINVAL, 34);
+    CHECK(adamw_step_tiled_sum(&hp, st, f, gb, 9, nullptr, 16, nullptr, nullptr) == ZS_EINVAL, 34);
+    char* fb = reinterpret_cast<char*>(f);
+    CHECK(adamw_step_tiled_sum(&hp, st, reinterpret_cast<float*>(fb + 2), gb, ZS_BF16, nullptr, 16, nullptr,
+                               nullptr) == ZS_EINVAL, 34);   // fp32 accumulator off 4 bytes
+    CHECK(adamw_step_tiled_sum(&hp, st, f, reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(gb) + 1), ZS_BF16,
+                               nullptr, 16, nullptr, nullptr) == ZS_EINVAL, 34);   // bf16 at an odd address
+    CHECK(adamw_step_tiled_sum(&hp, st, st + 8, gb, ZS_BF16, nullptr, 16, nullptr, nullptr) == ZS_EOVERLAP, 34);
+    CHECK(adamw_step_tiled_sum(&hp, st, nullptr, st + 3 * ZS_STATE_TILE - 4, ZS_BF16, nullptr, 16, nullptr,
+                               nullptr) == ZS_EOVERLAP, 34);
+    CHECK(adamw_step_tiled_sum(&hp, st, f, gb, ZS_BF16, nullptr, int64_t(1) << 40, nullptr, nullptr) == ZS_EINVAL, 34);
+    CHECK(adamw_step_tiled_sum(&hp, nullptr, nullptr, nullptr, ZS_BF16, nullptr, 0, nullptr, nullptr) == ZS_OK, 34);
+    CHECK(adamw_step_tiled_sum_dev(nullptr, st, f, gb, ZS_BF16, nullptr, 16, nullptr, nullptr) == ZS_EINVAL, 34);
+
     // chunk tables and tensor lists of every length up to 40, exactly sized;
     // the last entry is the one that fails, so every entry is read
     for (int count = 1; count <= 40; ++count) {
