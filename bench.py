@@ -193,12 +193,12 @@ def step_kernel_rates(bpe: dict, n: int, r: dict, two_call: bool = False) -> dic
     return out
 
 
-def ceiling_report(ms_by_lds: dict, nbytes: int, adamw_ms: float) -> dict:
+def ceiling_report(ms_by_lds: dict, nbytes: int, adamw_ms: float, kernel: str = "zsc_adamw_traffic") -> dict:
     """The AdamW-traffic kernel's time at each residency cap, its best, and
     the AdamW step's bandwidth as a fraction of that best."""
     best = min(ms_by_lds, key=ms_by_lds.get)
     gbps = nbytes / (ms_by_lds[best] * 1e-3) / 1e9
-    return {"kernel": "zsc_adamw_traffic", "algorithmic_bytes": nbytes,
+    return {"kernel": kernel, "algorithmic_bytes": nbytes,
             "ms_by_lds_bytes": {str(k): v for k, v in ms_by_lds.items()},
             "best_lds_bytes": best, "gbps": gbps, "frac": gbps / HBM_PEAK_GBPS,
             "adamw_step_of_ceiling": ms_by_lds[best] / adamw_ms}
@@ -315,6 +315,15 @@ class StepRig:
         zs.grad_reduce_chunks_norm_sq(self.acc, groups[-1], len(groups) == 1, self.w.grad_scale, self.norm,
                                       self.ws)
         zs.adamw_step_tiled(self.hp(t), self.state, self.acc, self.param, norm_sq=self.norm)
+
+    def sum_ceiling(self) -> dict:
+        """The step's AdamW traffic (accumulator + last bf16 gradient, or the
+        gradient alone) with trivial arithmetic, at each residency cap (it
+        changes the state: run after the timed steps)."""
+        last = len(self.grads) - 1
+        acc = self.acc if last > 0 else None
+        return {lds: _time_adamw_traffic(self.state, None, None, acc, self.param, self.n, lds, tiled=True,
+                                         grad_bf16=self.grads[last]) for lds in CEILING_LDS}
 
     def time_steps(self, steps: int, warmup: int, two_call: bool = False) -> dict:
         """W untimed steps, then K steps bracketed by synchronisations (wall
@@ -466,6 +475,7 @@ def run_gpu(w, steps: int, warmup: int):
     # it changes them)
     r["ceiling_ms"] = {lds: _time_adamw_traffic(rig.state, None, None, rig.acc, rig.param, n, lds, tiled=True)
                        for lds in CEILING_LDS}
+    r["ceiling_sum_ms"] = rig.sum_ceiling()
     r["ceiling_split_ms"] = {lds: _time_adamw_traffic(master, exp_avg, exp_avg_sq, rig.acc, rig.param, n, lds)
                              for lds in CEILING_LDS}
     del rig, master, exp_avg, exp_avg_sq
@@ -492,6 +502,7 @@ def run_step_leg(rig: StepRig, steps: int, warmup: int) -> dict:
     r = rig.time_steps(steps, warmup)
     r["n"] = rig.n
     r["two_call"] = rig.time_steps(steps, 1, two_call=True)
+    r["ceiling_sum_ms"] = rig.sum_ceiling()
     return r
 
 
@@ -499,11 +510,13 @@ CEILING_LDS = (0, 8192, 12288, 14336, 16384, 20480)   # LDS reserved per one-wav
 
 
 def _time_adamw_traffic(master, exp_avg, exp_avg_sq, grad, bf16, n: int, lds: int, reps: int = 5,
-                        tiled: bool = False) -> float:
+                        tiled: bool = False, grad_bf16=None) -> float:
     """Average launch time of the AdamW-traffic ceiling kernel
     (libzsceiling.so, built next to libzshard.so), each launch bracketed by
     HIP events on the stream it runs on.  tiled: `master` is the tiled state
-    buffer and the kernel walks that layout."""
+    buffer and the kernel walks that layout.  grad_bf16: the gradient is
+    `grad` (an fp32 accumulator, or None) plus this bf16 micro-batch
+    gradient, as adamw_step_tiled_sum reads it."""
     import ctypes
     import torch
     from fsdp_sharded_optimizer_amd import build as zbuild
@@ -513,7 +526,13 @@ def _time_adamw_traffic(master, exp_avg, exp_avg_sq, grad, bf16, n: int, lds: in
     lib = ctypes.CDLL(zbuild.CEILING_LIB)
     stream = torch.cuda.current_stream()
     bptr = bf16.data_ptr() if bf16 is not None else None
-    if tiled:
+    if grad_bf16 is not None:
+        f = lib.zsc_adamw_traffic_tiled_sum
+        f.restype = ctypes.c_int32
+        f.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]
+        args = [master.data_ptr(), grad.data_ptr() if grad is not None else None, grad_bf16.data_ptr(), bptr, n, lds,
+                stream.cuda_stream]
+    elif tiled:
         f = lib.zsc_adamw_traffic_tiled
         f.restype = ctypes.c_int32
         f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]
@@ -908,13 +927,16 @@ def main():
                 entry("grad_accum_add", K_ACCUM_ADD, n, 10 * n)]
 
     def roofline(wl, rr, nn):
-        """The step's AdamW, on the last micro-batch's sum."""
+        """The step's AdamW, on the last micro-batch's sum; its traffic with
+        trivial arithmetic at the best residency beside it."""
         b = step_bytes_per_elem(wl)["adamw_step_sum"] * nn
         ach = b / (rr["adamw_ms"] * 1e-3) / 1e9
         return {"kernel": "adamw_step_tiled_sum", "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
                 "traffic": traffic_of("adamw_step_tiled_sum", nn, digests), "traffic_unit": "bytes/launch",
-                "algorithmic_bytes": b, "launch_ms": rr["adamw_ms"]}
+                "algorithmic_bytes": b, "launch_ms": rr["adamw_ms"],
+                "traffic_ceiling": ceiling_report(rr["ceiling_sum_ms"], b, rr["adamw_ms"],
+                                                  "zsc_adamw_traffic_tiled_sum")}
 
     def with_traffic(kernels: dict, nn: int, wl) -> dict:
         """Measured bytes per launch next to the algorithmic ones, for the
@@ -963,7 +985,7 @@ def main():
         "step_two_call": two_call_report(w, r, n),
         "device_copy_gbps": r["copy_gbps"],
         "timing_events": timing_events(),
-        "adamw_traffic_ceiling": ceiling_report(r["ceiling_ms"], adamw_bytes, tc["adamw_ms"]),
+        "adamw_traffic_ceiling": ceiling_report(r["ceiling_ms"], adamw_bytes, tc["adamw_ms"], "zsc_adamw_traffic_tiled"),
         "roofline": roofline(w, r, n),
         "adamw_step_split": {
             "ms": r["split_ms"], "bytes_per_elem": bpe["adamw_step"],

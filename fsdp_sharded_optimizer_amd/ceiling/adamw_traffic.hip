@@ -30,6 +30,14 @@
 // elements: the masters, then the exp_avgs, then the exp_avg_sqs, 8192 floats
 // each), the reference for adamw_step_tiled.  state: 16-byte aligned, at
 // least 3 * 8192 * ceil(n / 8192) floats.
+//
+//   int32_t zsc_adamw_traffic_tiled_sum(float* state, const float* acc_or_null,
+//                                       const uint16_t* grad_bf16, uint16_t* bf16_or_null,
+//                                       int64_t n, int32_t lds_bytes, void* hip_stream)
+// The traffic of adamw_step_tiled_sum: the gradient read as an fp32
+// accumulator plus a bf16 micro-batch gradient (32 B/element with the bf16
+// output), or the bf16 gradient alone (acc NULL: 28 B/element), summed as the
+// step sums them.  acc 4-byte aligned, grad_bf16 4-byte aligned.
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
@@ -42,12 +50,34 @@ typedef float f32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 constexpr int kBlock = 64;
 constexpr int64_t kTile = 8192;   // libzshard's ZS_STATE_TILE
 
+typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
+
+__device__ inline float widen(uint32_t h) { return __uint_as_float(h << 16); }
+
+// SRC: the gradient is g (0), widen(gb) (1) or g + widen(gb) (2).
+template <int SRC>
+__device__ inline f32x4 grad4(const float* g, const uint16_t* gb, int64_t first) {
+    f32x4 r = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (SRC != 1) r = __builtin_nontemporal_load(reinterpret_cast<const f32x4_a4*>(g + first));
+    if (SRC != 0) {
+        const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2_a4*>(gb + first));
+        r += f32x4{widen(w.x & 0xFFFFu), widen(w.x >> 16), widen(w.y & 0xFFFFu), widen(w.y >> 16)};
+    }
+    return r;
+}
+
+template <int SRC>
+__device__ inline float grad1(const float* g, const uint16_t* gb, int64_t i) {
+    return (SRC != 1 ? g[i] : 0.0f) + (SRC != 0 ? widen(gb[i]) : 0.0f);
+}
+
 // TILED: p is the tiled state (m and v unused); element i's three values sit
 // at tile_base + (i mod kTile) + {0, 1, 2} * kTile.
-template <bool BF16, bool TILED>
+template <bool BF16, bool TILED, int SRC = 0>
 __global__ __launch_bounds__(kBlock) void adamw_traffic_kernel(float* __restrict__ p, float* __restrict__ m,
                                                                float* __restrict__ v, const float* __restrict__ g,
-                                                               uint16_t* __restrict__ b, int64_t n) {
+                                                               uint16_t* __restrict__ b, int64_t n,
+                                                               const uint16_t* __restrict__ gb = nullptr) {
     const int64_t first = ((int64_t)blockIdx.x * kBlock + threadIdx.x) * 4;
     if (first + 4 <= n) {
         float* pp = p + first;
@@ -58,7 +88,7 @@ __global__ __launch_bounds__(kBlock) void adamw_traffic_kernel(float* __restrict
             mp = pp + kTile;
             vp = pp + 2 * kTile;
         }
-        const f32x4 g4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4_a4*>(g + first));
+        const f32x4 g4 = grad4<SRC>(g, gb, first);
         f32x4 p4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(pp));
         f32x4 m4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(mp));
         f32x4 v4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(vp));
@@ -84,9 +114,10 @@ __global__ __launch_bounds__(kBlock) void adamw_traffic_kernel(float* __restrict
             mi = pi + kTile;
             vi = pi + 2 * kTile;
         }
-        *pi += g[i];
-        *mi += g[i];
-        *vi += g[i];
+        const float gi = grad1<SRC>(g, gb, i);
+        *pi += gi;
+        *mi += gi;
+        *vi += gi;
         if (BF16) b[i] = (uint16_t)(__float_as_uint(*pi) >> 16);
     }
 }
@@ -130,5 +161,31 @@ extern "C" __attribute__((visibility("default"))) int32_t zsc_adamw_traffic_tile
     else
         hipLaunchKernelGGL((adamw_traffic_kernel<false, true>), dim3((unsigned)blocks), dim3(kBlock), (unsigned)lds_bytes,
                            s, state, nullptr, nullptr, grad, bf16, n);
+    return (int32_t)hipGetLastError();
+}
+
+extern "C" __attribute__((visibility("default"))) int32_t zsc_adamw_traffic_tiled_sum(
+        float* state, const float* acc, const uint16_t* grad, uint16_t* bf16, int64_t n, int32_t lds_bytes,
+        void* hip_stream) {
+    if (n < 0 || (int64_t)1 << 31 < n || lds_bytes < 0 || lds_bytes > 65536) return -1;
+    if (n == 0) return 0;
+    if (!state || !grad) return -1;
+    if (!aligned(state, 16) || !aligned(grad, 4) || (acc && !aligned(acc, 4)) || (bf16 && !aligned(bf16, 16)))
+        return -1;
+    const int64_t blocks = (n + 4 * kBlock - 1) / (4 * kBlock);
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    const unsigned lds = (unsigned)lds_bytes;
+    if (acc && bf16)
+        hipLaunchKernelGGL((adamw_traffic_kernel<true, true, 2>), dim3((unsigned)blocks), dim3(kBlock), lds, s, state,
+                           nullptr, nullptr, acc, bf16, n, grad);
+    else if (acc)
+        hipLaunchKernelGGL((adamw_traffic_kernel<false, true, 2>), dim3((unsigned)blocks), dim3(kBlock), lds, s,
+                           state, nullptr, nullptr, acc, bf16, n, grad);
+    else if (bf16)
+        hipLaunchKernelGGL((adamw_traffic_kernel<true, true, 1>), dim3((unsigned)blocks), dim3(kBlock), lds, s, state,
+                           nullptr, nullptr, nullptr, bf16, n, grad);
+    else
+        hipLaunchKernelGGL((adamw_traffic_kernel<false, true, 1>), dim3((unsigned)blocks), dim3(kBlock), lds, s,
+                           state, nullptr, nullptr, nullptr, bf16, n, grad);
     return (int32_t)hipGetLastError();
 }

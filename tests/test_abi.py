@@ -567,6 +567,17 @@ def test_ceiling_library_rejects_before_launch():
     assert t(a, a + 66, None, 16, 0, None) == -1                           # grad off 4 bytes
     assert t(a, a + 64, a + 130, 16, 0, None) == -1                        # bf16 output off 16 bytes
     assert t(a, a + 64, None, 16, 70000, None) == -1
+    u = L.zsc_adamw_traffic_tiled_sum
+    u.restype = ctypes.c_int32
+    u.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]
+    assert u(a, a + 64, a + 128, None, 0, 0, None) == 0
+    assert u(a, a + 64, a + 128, None, (1 << 31) + 1, 0, None) == -1
+    assert u(a, a + 64, None, None, 16, 0, None) == -1                     # no gradient
+    assert u(a + 8, None, a + 128, None, 16, 0, None) == -1                # state off 16 bytes
+    assert u(a, a + 66, a + 128, None, 16, 0, None) == -1                  # accumulator off 4 bytes
+    assert u(a, a + 64, a + 130, None, 16, 0, None) == -1                  # bf16 gradient off 4 bytes
+    assert u(a, None, a + 128, a + 136, 16, 0, None) == -1                 # bf16 output off 16 bytes
+    assert u(a, None, a + 128, None, 16, -5, None) == -1
 
 
 def test_plain_c_consumer(tmp_path):
