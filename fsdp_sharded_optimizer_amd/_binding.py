@@ -34,6 +34,7 @@ EXPORTS = (
     "adamw_step_tiled_dev", "moments_tiled_numel", "moments_tile", "moments_untile", "adam_update_tiled",
     "adamw_step_no_master_tiled", "grad_reduce_chunks_norm_sq_workspace_bytes", "grad_reduce_chunks_norm_sq",
     "grad_accum_norm_sq_noalloc", "grad_sum_norm_sq", "adamw_step_tiled_sum", "adamw_step_tiled_sum_dev",
+    "adamw_step_sum", "adamw_step_sum_dev",
     "zs_strerror", "zs_last_hip_error",
 )
 NOALLOC_MAX_ELEMS = 2_146_959_360   # ZS_NOALLOC_MAX_ELEMS
@@ -137,6 +138,10 @@ def lib() -> ctypes.CDLL:
         L.adamw_step_tiled_sum.restype = I32
         L.adamw_step_tiled_sum_dev.argtypes = [P, P, P, P, I32, P, I64, P, P]
         L.adamw_step_tiled_sum_dev.restype = I32
+        L.adamw_step_sum.argtypes = [ctypes.POINTER(AdamW), P, P, P, P, P, I32, P, I64, P, P]
+        L.adamw_step_sum.restype = I32
+        L.adamw_step_sum_dev.argtypes = [P, P, P, P, P, P, I32, P, I64, P, P]
+        L.adamw_step_sum_dev.restype = I32
         L.adamw_step.argtypes = [ctypes.POINTER(AdamW), P, P, P, P, P, I64, P, P]
         L.adamw_step.restype = I32
         L.adamw_scalars.argtypes = [ctypes.POINTER(AdamW), ctypes.POINTER(AdamWScalars)]
@@ -598,6 +603,45 @@ def _sum_args(acc: Optional[torch.Tensor], grad: torch.Tensor, param_bf16: Optio
     if param_bf16 is not None and param_bf16.numel() != n:
         raise ValueError(f"{fn}: param_bf16 size mismatch")
     return n
+
+
+def _split_sum_args(master, exp_avg, exp_avg_sq, acc, grad, param_bf16, fn: str):
+    n = _sum_args(acc, grad, param_bf16, fn)
+    if master.numel() != n or exp_avg.numel() != n or exp_avg_sq.numel() != n:
+        raise ValueError(f"{fn}: size mismatch")
+    return n
+
+
+def adamw_step_sum(hp: AdamWConfig, master: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor,
+                   acc: Optional[torch.Tensor], grad: torch.Tensor, param_bf16: Optional[torch.Tensor] = None,
+                   norm_sq: Optional[torch.Tensor] = None, stream=None) -> None:
+    """adamw_step on the last micro-batch's sum fl(acc + widen(grad))
+    (widen(grad) alone when acc is None), formed as it is read: acc is not
+    written.  Bit for bit grad_accum then adamw_step."""
+    n = _split_sum_args(master, exp_avg, exp_avg_sq, acc, grad, param_bf16, "adamw_step_sum")
+    c = hp.c_struct()
+    _check("adamw_step_sum", lib().adamw_step_sum(
+        ctypes.byref(c), _dev(master, "master", torch.float32), _dev(exp_avg, "exp_avg", torch.float32),
+        _dev(exp_avg_sq, "exp_avg_sq", torch.float32), _dev(acc, "acc", torch.float32), _dev(grad, "grad"),
+        _dtype_code(grad), _dev(param_bf16, "param_bf16", torch.bfloat16), n, _norm(norm_sq, "adamw_step_sum"),
+        _stream(stream)))
+
+
+def adamw_step_sum_dev(scalars_dev: torch.Tensor, master: torch.Tensor, exp_avg: torch.Tensor,
+                       exp_avg_sq: torch.Tensor, acc: Optional[torch.Tensor], grad: torch.Tensor,
+                       param_bf16: Optional[torch.Tensor] = None, norm_sq: Optional[torch.Tensor] = None,
+                       stream=None) -> None:
+    """adamw_step_sum with its scalars read from device memory when the
+    kernels run (scalars_dev: uint8 GPU tensor holding scalars_bytes(hp))."""
+    if scalars_dev.dtype != torch.uint8 or scalars_dev.numel() < ctypes.sizeof(AdamWScalars):
+        raise TypeError("adamw_step_sum_dev: scalars_dev must be a uint8 tensor of at least "
+                        f"{ctypes.sizeof(AdamWScalars)} bytes")
+    n = _split_sum_args(master, exp_avg, exp_avg_sq, acc, grad, param_bf16, "adamw_step_sum_dev")
+    _check("adamw_step_sum_dev", lib().adamw_step_sum_dev(
+        _dev(scalars_dev, "scalars_dev"), _dev(master, "master", torch.float32),
+        _dev(exp_avg, "exp_avg", torch.float32), _dev(exp_avg_sq, "exp_avg_sq", torch.float32),
+        _dev(acc, "acc", torch.float32), _dev(grad, "grad"), _dtype_code(grad),
+        _dev(param_bf16, "param_bf16", torch.bfloat16), n, _norm(norm_sq, "adamw_step_sum_dev"), _stream(stream)))
 
 
 def adamw_step_tiled_sum(hp: AdamWConfig, state: torch.Tensor, acc: Optional[torch.Tensor], grad: torch.Tensor,

@@ -9,7 +9,7 @@
 // gfx950 vector rate at 8 TB/s, so the kernel is HBM-bound: the design goal
 // is deep memory-level parallelism and fully coalesced 128-bit accesses.
 //
-// The master forms on the tiled state also take the gradient as the last
+// The master forms (tiled or split state) also take the gradient as the last
 // micro-batch's sum, formed as it is read (GS): fl(acc + widen(g)) from the
 // fp32 accumulator and the micro-batch's bf16 or fp32 gradient, or widen(g)
 // alone for a step of one micro-batch.  It is the value the accumulation
@@ -320,7 +320,8 @@ hipError_t launch(const AdamwArgs& a, unsigned lds, hipStream_t stream) {
 // keep the 13-per-CU cap tiled too (tiled moments for the update form: 84.5 %
 // there, 83.9 % at 11 per CU).
 // The summed-gradient forms take the element-wise path on a tiled state too,
-// for a bf16 micro-batch gradient off a 4-byte boundary.
+// for a bf16 micro-batch gradient off a 4-byte boundary (split buffers: also
+// for state off a 16-byte boundary, as the stored-gradient form).
 template <int FORM, bool DEV = false, bool TILED = false, int GS = kGradF32>
 hipError_t launch_form(const AdamwArgs& a, bool vec_ok, bool out_aligned, hipStream_t stream) {
     constexpr bool six = FORM == kNoMaster || FORM == kUpdate;
@@ -333,14 +334,25 @@ hipError_t launch_form(const AdamwArgs& a, bool vec_ok, bool out_aligned, hipStr
     else return launch<1, FORM, kBlock, DEV, TILED, true, GS>(a, 0, stream);
 }
 
-template <int GS>
-hipError_t launch_tiled_sum(const AdamwArgs& a, bool vec_ok, bool out_aligned, hipStream_t stream) {
+template <int GS, bool TILED>
+hipError_t launch_sum(const AdamwArgs& a, bool vec_ok, bool out_aligned, hipStream_t stream) {
     if (a.sc_dev != nullptr)
         return a.param_bf16 != nullptr
-                   ? launch_form<kMasterBf16, true, true, GS>(a, vec_ok, out_aligned, stream)
-                   : launch_form<kMaster, true, true, GS>(a, vec_ok, true, stream);
-    return a.param_bf16 != nullptr ? launch_form<kMasterBf16, false, true, GS>(a, vec_ok, out_aligned, stream)
-                                   : launch_form<kMaster, false, true, GS>(a, vec_ok, true, stream);
+                   ? launch_form<kMasterBf16, true, TILED, GS>(a, vec_ok, out_aligned, stream)
+                   : launch_form<kMaster, true, TILED, GS>(a, vec_ok, true, stream);
+    return a.param_bf16 != nullptr ? launch_form<kMasterBf16, false, TILED, GS>(a, vec_ok, out_aligned, stream)
+                                   : launch_form<kMaster, false, TILED, GS>(a, vec_ok, true, stream);
+}
+
+template <bool TILED>
+hipError_t launch_sum_source(const AdamwArgs& a, int grad_source, bool vec_ok, bool out_aligned,
+                             hipStream_t stream) {
+    switch (grad_source) {
+    case kGradBf16: return launch_sum<kGradBf16, TILED>(a, vec_ok, out_aligned, stream);
+    case kGradSumBf16: return launch_sum<kGradSumBf16, TILED>(a, vec_ok, out_aligned, stream);
+    case kGradSumF32: return launch_sum<kGradSumF32, TILED>(a, vec_ok, out_aligned, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
@@ -371,12 +383,12 @@ hipError_t launch_adam_update(const AdamwArgs& a, bool vec_ok, bool out_aligned,
 
 hipError_t launch_adamw_tiled_sum(const AdamwArgs& a, int grad_source, bool vec_ok, bool out_aligned,
                                   hipStream_t stream) {
-    switch (grad_source) {
-    case kGradBf16: return launch_tiled_sum<kGradBf16>(a, vec_ok, out_aligned, stream);
-    case kGradSumBf16: return launch_tiled_sum<kGradSumBf16>(a, vec_ok, out_aligned, stream);
-    case kGradSumF32: return launch_tiled_sum<kGradSumF32>(a, vec_ok, out_aligned, stream);
-    default: return hipErrorInvalidValue;
-    }
+    return launch_sum_source<true>(a, grad_source, vec_ok, out_aligned, stream);
+}
+
+hipError_t launch_adamw_sum(const AdamwArgs& a, int grad_source, bool vec_ok, bool out_aligned,
+                            hipStream_t stream) {
+    return launch_sum_source<false>(a, grad_source, vec_ok, out_aligned, stream);
 }
 
 hipError_t launch_adam_update_tiled(const AdamwArgs& a, bool out_aligned, hipStream_t stream) {

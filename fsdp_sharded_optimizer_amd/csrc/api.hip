@@ -454,6 +454,103 @@ static int32_t adamw_master(const zs_adamw* hp, const zs_adamw_scalars* sc_dev, 
     return hip_status(zs::launch_adamw(a, vec, out_aligned, as_stream(hip_stream)));
 }
 
+// the split master-form step on the last micro-batch's sum (acc, nullable, +
+// grad of grad_dtype): host scalars (hp) or a device copy of them (sc_dev)
+static int32_t adamw_master_sum(const zs_adamw* hp, const zs_adamw_scalars* sc_dev, float* master, float* exp_avg,
+                                float* exp_avg_sq, const float* acc, const void* grad, int32_t grad_dtype,
+                                uint16_t* param_bf16, int64_t n, const double* norm_sq_dev, void* hip_stream) {
+    int32_t rc;
+    if (sc_dev == nullptr) {
+        rc = adamw_check_hp(hp, n, norm_sq_dev);
+        if (rc != ZS_OK) return rc;
+    } else {
+        if (!size_ok(n) || !aligned(sc_dev, 8)) return ZS_EINVAL;
+        if (norm_sq_dev != nullptr && !aligned(norm_sq_dev, 8)) return ZS_EINVAL;
+    }
+    if (!dtype_ok(grad_dtype)) return ZS_EINVAL;
+    if (n == 0) return ZS_OK;
+    const int64_t gsz = elem_size(grad_dtype);
+    if (master == nullptr || exp_avg == nullptr || exp_avg_sq == nullptr || grad == nullptr) return ZS_EINVAL;
+    if (!aligned(master, 4) || !aligned(exp_avg, 4) || !aligned(exp_avg_sq, 4) || !aligned(grad, (uintptr_t)gsz) ||
+        (acc != nullptr && !aligned(acc, 4)) || (param_bf16 != nullptr && !aligned(param_bf16, 2)))
+        return ZS_EINVAL;
+    const void* bufs[6] = {master, exp_avg, exp_avg_sq, acc, grad, param_bf16};
+    const int64_t bytes[6] = {n * 4, n * 4, n * 4, acc ? n * 4 : 0, n * gsz, param_bf16 ? n * 2 : 0};
+    const bool written[6] = {true, true, true, false, false, true};
+    for (int i = 0; i < 6; ++i) {
+        for (int j = i + 1; j < 6; ++j)
+            if (overlap(bufs[i], bytes[i], bufs[j], bytes[j])) return ZS_EOVERLAP;
+        if (norm_sq_dev != nullptr && written[i] && overlap(bufs[i], bytes[i], norm_sq_dev, 8)) return ZS_EOVERLAP;
+        if (sc_dev != nullptr && written[i] && overlap(bufs[i], bytes[i], sc_dev, (int64_t)sizeof(zs_adamw_scalars)))
+            return ZS_EOVERLAP;
+    }
+    zs::AdamwArgs a;
+    if (sc_dev == nullptr) {
+        a = make_args(hp, norm_sq_dev);
+    } else {
+        std::memset(&a, 0, sizeof(a));
+        a.sc_dev = reinterpret_cast<const zs::AdamwScalars*>(sc_dev);
+        a.norm_sq = norm_sq_dev;
+    }
+    a.master = master;
+    a.exp_avg = exp_avg;
+    a.exp_avg_sq = exp_avg_sq;
+    a.grad = acc;
+    a.grad_mb = grad;
+    a.param_bf16 = param_bf16;
+    a.n = n;
+    const int source = grad_dtype == ZS_F32 ? (acc != nullptr ? zs::kGradSumF32 : zs::kGradF32)
+                                            : (acc != nullptr ? zs::kGradSumBf16 : zs::kGradBf16);
+    if (source == zs::kGradF32) {   // one fp32 micro-batch: the stored-gradient step on it
+        a.grad = static_cast<const float*>(grad);
+        a.grad_mb = nullptr;
+    }
+    auto launch = [&](const zs::AdamwArgs& x, bool vec, bool out_aligned) {
+        return source == zs::kGradF32 ? zs::launch_adamw(x, vec, out_aligned, as_stream(hip_stream))
+                                      : zs::launch_adamw_sum(x, source, vec, out_aligned, as_stream(hip_stream));
+    };
+    // as adamw_step: views sharing one offset off a 128-byte boundary run
+    // their first 1-31 elements element by element, the rest on the vector
+    // path when the state is 16-byte aligned and the gradient's micro-batch
+    // part 4-byte aligned
+    float* const state[3] = {master, exp_avg, exp_avg_sq};
+    const int64_t head = shared_head(state, 3, n);
+    if (head > 0) {
+        zs::AdamwArgs h = a;
+        h.n = head;
+        rc = hip_status(launch(h, false, true));
+        if (rc != ZS_OK) return rc;
+        a.master += head;
+        a.exp_avg += head;
+        a.exp_avg_sq += head;
+        if (a.grad != nullptr) a.grad += head;
+        if (a.grad_mb != nullptr) a.grad_mb = static_cast<const char*>(a.grad_mb) + head * gsz;
+        if (a.param_bf16 != nullptr) a.param_bf16 += head;
+        a.n -= head;
+    }
+    const bool vec = aligned(a.master, 16) && aligned(a.exp_avg, 16) && aligned(a.exp_avg_sq, 16) &&
+                     (a.grad_mb == nullptr || aligned(a.grad_mb, 4));
+    const bool out_aligned = a.param_bf16 == nullptr || aligned(a.param_bf16, 16);
+    if (a.n == 0) return ZS_OK;
+    return hip_status(launch(a, vec, out_aligned));
+}
+
+int32_t adamw_step_sum(const zs_adamw* hp, float* master, float* exp_avg, float* exp_avg_sq, const float* acc,
+                       const void* grad, int32_t grad_dtype, uint16_t* param_bf16, int64_t n,
+                       const double* norm_sq_dev, void* hip_stream) {
+    if (hp == nullptr) return ZS_EINVAL;
+    return adamw_master_sum(hp, nullptr, master, exp_avg, exp_avg_sq, acc, grad, grad_dtype, param_bf16, n,
+                            norm_sq_dev, hip_stream);
+}
+
+int32_t adamw_step_sum_dev(const zs_adamw_scalars* scalars_dev, float* master, float* exp_avg, float* exp_avg_sq,
+                           const float* acc, const void* grad, int32_t grad_dtype, uint16_t* param_bf16,
+                           int64_t n, const double* norm_sq_dev, void* hip_stream) {
+    if (scalars_dev == nullptr) return ZS_EINVAL;
+    return adamw_master_sum(nullptr, scalars_dev, master, exp_avg, exp_avg_sq, acc, grad, grad_dtype, param_bf16, n,
+                            norm_sq_dev, hip_stream);
+}
+
 int32_t adamw_step(const zs_adamw* hp, float* master, float* exp_avg, float* exp_avg_sq,
                    const float* grad, uint16_t* param_bf16, int64_t n, const double* norm_sq_dev,
                    void* hip_stream) {

@@ -158,13 +158,17 @@ hipError_t launch_adam_update(const AdamwArgs& a, bool vec_ok, bool out_aligned,
 hipError_t launch_adamw_tiled(const AdamwArgs& a, bool out_aligned, hipStream_t stream);
 hipError_t launch_adam_update_tiled(const AdamwArgs& a, bool out_aligned, hipStream_t stream);
 hipError_t launch_adamw_no_master_tiled(const AdamwArgs& a, bool vec_ok, hipStream_t stream);
-// The tiled master-form step whose gradient is the last micro-batch's sum,
+// The master-form step whose gradient is the last micro-batch's sum,
 // formed as it is read: grad_source 1 = widen(bf16 grad_mb) (no accumulator),
 // 2 = fl(grad + widen(bf16 grad_mb)), 3 = fl(grad + fp32 grad_mb).  vec_ok:
 // grad_mb is 4-byte aligned (else the element-wise path).
 enum GradSource : int { kGradF32 = 0, kGradBf16 = 1, kGradSumBf16 = 2, kGradSumF32 = 3 };
 hipError_t launch_adamw_tiled_sum(const AdamwArgs& a, int grad_source, bool vec_ok, bool out_aligned,
                                   hipStream_t stream);
+// the same on split master, exp_avg and exp_avg_sq (vec_ok: the state 16-byte
+// aligned and grad_mb 4-byte aligned)
+hipError_t launch_adamw_sum(const AdamwArgs& a, int grad_source, bool vec_ok, bool out_aligned,
+                            hipStream_t stream);
 // runs (2 or 3) split fp32 arrays (each nullable: zeros) -> tiled buffer,
 // padding zeroed; and back (each destination nullable: skipped)
 hipError_t launch_tile_runs(const float* const* src, int runs, float* buf, int64_t n, hipStream_t stream);

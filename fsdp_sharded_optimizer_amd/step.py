@@ -6,10 +6,9 @@ norm scratch.  A step is: ``accumulate`` once per micro-batch (the last one
 may form the squared norm in the same pass), then ``step``: the norm (if
 not formed yet and requested) and the fused AdamW update with the bf16
 re-cast.  ``step(last_grad=g)`` takes the last micro-batch's gradient
-itself instead: on the tiled state its sum with the accumulator is never
-stored (the norm pass reads both, and so does AdamW), which saves the
-accumulator's write and re-read, 8 B per element; the results are the same
-bit for bit.  Where a step's micro-batch gradients are all kept in device
+itself instead: its sum with the accumulator is never stored (the norm pass
+reads both, and so does AdamW), which saves the accumulator's write and
+re-read, 8 B per element; the results are the same bit for bit.  Where a step's micro-batch gradients are all kept in device
 memory (2 B per element each in bf16), ``accumulate_all`` sums them in one
 pass instead.  Nothing here computes; it orders calls.
 
@@ -96,13 +95,6 @@ class ShardOptimizer:
         else:
             zs.adamw_step_tiled(hp, self.state, self.acc, self.param_bf16, norm_sq=norm)
 
-    def _adamw_dev(self, scalars_dev: torch.Tensor, norm) -> None:
-        if self._split is not None:
-            zs.adamw_step_dev(scalars_dev, self._split["master"], self._split["exp_avg"], self._split["exp_avg_sq"],
-                              self.acc, self.param_bf16, norm_sq=norm)
-        else:
-            zs.adamw_step_tiled_dev(scalars_dev, self.state, self.acc, self.param_bf16, norm_sq=norm)
-
     def _save(self) -> dict:
         """Device copies of the optimizer state (and bf16 parameter)."""
         saved = {"state": self.state.clone()} if self._split is None else \
@@ -162,20 +154,17 @@ class ShardOptimizer:
         step counter advances only once the update is enqueued.
 
         last_grad: the last micro-batch's gradient, not yet accumulated (the
-        step is then accumulate(last_grad, last=True) followed by step(),
-        with the same results bit for bit).  On the tiled state the sum is
+        step is then the same, bit for bit, as accumulate(last_grad,
+        last=True) followed by step()).  Its sum with the accumulator is
         formed where it is read and never stored: the norm pass reads the
         accumulator and last_grad (grad_sum_norm_sq), AdamW reads them again
-        (adamw_step_tiled_sum), and the accumulator keeps the earlier
-        micro-batches' sum."""
+        (adamw_step_tiled_sum, or adamw_step_sum on the split state), and
+        the accumulator keeps the earlier micro-batches' sum."""
         if last_grad is not None:
             if self._norm_ready:
                 raise RuntimeError("step(last_grad=...) after accumulate(..., last=True)")
-            if self._split is not None:
-                self.accumulate(last_grad, last=True)
-            else:
-                self._step_on_sum(last_grad, extra_norm_sq)
-                return
+            self._step_on_sum(last_grad, extra_norm_sq)
+            return
         if self._pending == 0:
             raise RuntimeError("step() without an accumulated gradient")
         norm = None
@@ -199,15 +188,20 @@ class ShardOptimizer:
             norm = self.norm_sq
         hp = self.hp(extra_norm_sq)
         hp.step = self.t + 1
-        zs.adamw_step_tiled_sum(hp, self.state, acc, g, self.param_bf16, norm_sq=norm)
+        if self._split is not None:
+            zs.adamw_step_sum(hp, self._split["master"], self._split["exp_avg"], self._split["exp_avg_sq"], acc, g,
+                              self.param_bf16, norm_sq=norm)
+        else:
+            zs.adamw_step_tiled_sum(hp, self.state, acc, g, self.param_bf16, norm_sq=norm)
         self.t += 1
         self._pending = 0
         self._norm_ready = False
 
     def capture(self, grads: list, extra_norm_sq: float = 0.0) -> "CapturedStep":
-        """Record one whole step (accumulate every tensor of ``grads`` in
-        order, the norm if wanted, AdamW with the bf16 re-cast) into a HIP
-        graph whose AdamW scalars are read from device memory, so the same
+        """Record one whole step (accumulate every tensor of ``grads`` but
+        the last in order, then the last one's norm if wanted and AdamW with
+        the bf16 re-cast on the sum, as step(last_grad=) runs them) into a
+        HIP graph whose AdamW scalars are read from device memory, so the same
         graph replays every later step.  ``grads`` are fixed device tensors
         the caller refills with each step's micro-batch gradients before
         ``replay()``.  Nothing is allocated at replay; the step counter
@@ -289,29 +283,24 @@ class CapturedStep:
         self._host.numpy()[:] = np.frombuffer(zs.scalars_bytes(hp), dtype=np.uint8)
 
     def _body(self) -> None:
-        """The step as ShardOptimizer runs it: on the tiled state the last
-        gradient is folded into the norm pass and AdamW (step(last_grad=)),
-        on the split state it is accumulated with the norm first."""
+        """The step as ShardOptimizer runs it with step(last_grad=): the last
+        gradient folded into the norm pass and AdamW, its sum never stored."""
         opt = self.opt
         last = len(self.grads) - 1
-        tiled = opt._split is None
         for k, g in enumerate(self.grads[:last]):
             zs.grad_accum(opt.acc, g, overwrite=(k == 0))
         g = self.grads[last]
         norm = opt.norm_sq if opt.compute_norm else None
-        if tiled:
-            acc = opt.acc if last > 0 else None
-            if opt.compute_norm:
-                zs.grad_sum_norm_sq(acc, g, acc is None, opt.grad_scale, opt.norm_sq, opt.workspace)
-            self._dev.copy_(self._host, non_blocking=True)
-            zs.adamw_step_tiled_sum_dev(self._dev, opt.state, acc, g, opt.param_bf16, norm_sq=norm)
-            return
+        acc = opt.acc if last > 0 else None
         if opt.compute_norm:
-            zs.grad_accum_norm_sq(opt.acc, g, last == 0, opt.grad_scale, opt.norm_sq, opt.workspace)
-        else:
-            zs.grad_accum(opt.acc, g, overwrite=(last == 0))
+            zs.grad_sum_norm_sq(acc, g, acc is None, opt.grad_scale, opt.norm_sq, opt.workspace)
         self._dev.copy_(self._host, non_blocking=True)
-        opt._adamw_dev(self._dev, norm)
+        if opt._split is not None:
+            s = opt._split
+            zs.adamw_step_sum_dev(self._dev, s["master"], s["exp_avg"], s["exp_avg_sq"], acc, g, opt.param_bf16,
+                                  norm_sq=norm)
+        else:
+            zs.adamw_step_tiled_sum_dev(self._dev, opt.state, acc, g, opt.param_bf16, norm_sq=norm)
 
     def replay(self) -> None:
         """Run the next step.  Waits for the previous replay to have read the

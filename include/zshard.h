@@ -373,6 +373,25 @@ ZS_API int32_t adamw_step(const zs_adamw* hp, float* master, float* exp_avg, flo
                           const double* norm_sq_dev, void* hip_stream);
 
 /*
+ * adamw_step_sum — adamw_step whose gradient is the last micro-batch's
+ * accumulation, formed as it is read (the split-buffer form of
+ * adamw_step_tiled_sum, below): element i's gradient is fl(acc[i] +
+ * widen(grad[i])), or widen(grad[i]) when acc is NULL.  Results are bit for
+ * bit those of grad_accum(acc, grad, grad_dtype, n, acc == NULL) followed by
+ * adamw_step(hp, master, exp_avg, exp_avg_sq, acc, ...); acc is only read.
+ * Same sources as adamw_step_tiled_sum.
+ * master, exp_avg, exp_avg_sq, param_bf16, norm_sq_dev: as adamw_step;
+ * acc: device fp32[n], 4-byte aligned, read, or NULL; grad: device [n] of
+ * grad_dtype (ZS_BF16 or ZS_F32), read.  No two of the six buffers may
+ * overlap, nor a written one overlap *norm_sq_dev.
+ * Errors: ZS_EINVAL (as adamw_step, or a bad grad_dtype), ZS_EOVERLAP,
+ * ZS_EHIP.
+ */
+ZS_API int32_t adamw_step_sum(const zs_adamw* hp, float* master, float* exp_avg, float* exp_avg_sq, const float* acc,
+                              const void* grad, int32_t grad_dtype, uint16_t* param_bf16, int64_t n,
+                              const double* norm_sq_dev, void* hip_stream);
+
+/*
  * The per-step scalars of adamw_step, formed on the host from zs_adamw in
  * binary64 and each rounded to binary32 once (beta1, beta2, 1 - beta1,
  * 1 - beta2, lr / (1 - beta1^t), sqrt(1 - beta2^t), eps, 1 - lr*wd,
@@ -412,6 +431,16 @@ ZS_API int32_t adamw_scalars(const zs_adamw* hp, zs_adamw_scalars* out);
 ZS_API int32_t adamw_step_dev(const zs_adamw_scalars* scalars_dev, float* master, float* exp_avg,
                               float* exp_avg_sq, const float* grad, uint16_t* param_bf16, int64_t n,
                               const double* norm_sq_dev, void* hip_stream);
+
+/*
+ * adamw_step_sum_dev — adamw_step_sum with its scalars read from device
+ * memory when the kernels run (as adamw_step_dev).  scalars_dev: device,
+ * 8-byte aligned, read; it must not overlap a written buffer.  Other
+ * arguments, results and errors as adamw_step_sum.
+ */
+ZS_API int32_t adamw_step_sum_dev(const zs_adamw_scalars* scalars_dev, float* master, float* exp_avg,
+                                  float* exp_avg_sq, const float* acc, const void* grad, int32_t grad_dtype,
+                                  uint16_t* param_bf16, int64_t n, const double* norm_sq_dev, void* hip_stream);
 
 /*
  * Tiled optimizer state — a storage layout of this library, not of the

@@ -37,7 +37,7 @@ def no_launch_reached():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 33 and set(names) == set(B.EXPORTS), names
+    assert len(names) == 35 and set(names) == set(B.EXPORTS), names
     L = zs.lib()
     for name in names:
         assert getattr(L, name) is not None
@@ -446,6 +446,37 @@ def test_adamw_step_tiled_sum_rejects():
     assert dev(s=sc + 4) == B.ZS_EINVAL
     assert dev(dt=3) == B.ZS_EINVAL
     assert dev(s=st + 64) == B.ZS_EOVERLAP                          # scalars inside the written state
+    assert dev(k=0) == B.ZS_OK
+
+
+def test_adamw_step_sum_rejects():
+    L = zs.lib()
+    n = 1024
+    p, m, v = FAKE, FAKE + 2**16, FAKE + 2**17
+    acc0, g0 = FAKE + 2**20, FAKE + 2**21
+    call = lambda hp=None, a=acc0, g=g0, dt=B.ZS_BF16, b=0, k=n, norm=0, pp=p: L.adamw_step_sum(
+        ctypes.byref(hp or _hp()), pp, m, v, a, g, dt, b, k, norm, None)
+    for bad in (dict(step=0), dict(beta1=1.5), dict(eps=0.0), dict(max_norm=float("nan"))):
+        assert call(hp=_hp(**bad)) == B.ZS_EINVAL, bad
+    assert L.adamw_step_sum(None, p, m, v, acc0, g0, B.ZS_BF16, 0, n, 0, None) == B.ZS_EINVAL
+    assert call(dt=2) == B.ZS_EINVAL
+    assert call(pp=0) == B.ZS_EINVAL
+    assert call(g=0) == B.ZS_EINVAL
+    assert call(pp=p + 2) == B.ZS_EINVAL                            # master off 4 bytes
+    assert call(a=acc0 + 2) == B.ZS_EINVAL                          # accumulator off 4 bytes
+    assert call(g=g0 + 1) == B.ZS_EINVAL                            # bf16 gradient at an odd address
+    assert call(b=FAKE + 2**22 + 1) == B.ZS_EINVAL
+    assert call(a=m + 64) == B.ZS_EOVERLAP                          # accumulator inside exp_avg
+    assert call(g=acc0 + 64) == B.ZS_EOVERLAP                       # gradient inside the accumulator
+    assert call(b=p + 64) == B.ZS_EOVERLAP                          # bf16 output inside the master
+    assert call(norm=v + 64) == B.ZS_EOVERLAP                       # norm inside a written buffer
+    assert call(k=(1 << 39) + 1) == B.ZS_EINVAL
+    assert call(k=0) == B.ZS_OK
+    sc = FAKE + 2**30
+    dev = lambda s=sc, k=n: L.adamw_step_sum_dev(s, p, m, v, acc0, g0, B.ZS_BF16, 0, k, 0, None)
+    assert dev(s=0) == B.ZS_EINVAL
+    assert dev(s=sc + 4) == B.ZS_EINVAL
+    assert dev(s=m + 8) == B.ZS_EOVERLAP                            # scalars inside exp_avg
     assert dev(k=0) == B.ZS_OK
 
 

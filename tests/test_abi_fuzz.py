@@ -1,9 +1,10 @@
 """Property tests of the C ABI's host-side validation (CPU only).
 
 Random argument sets for adamw_step, flat_pack and flat_unpack, for the
-tiled-state calls (adamw_step_tiled, state_tile, state_untile, and the
-one-pass last micro-batch: adamw_step_tiled_sum, grad_sum_norm_sq): sizes,
-alignments, null pointers, overlapping buffers and hyperparameters.  A
+tiled-state calls (adamw_step_tiled, state_tile, state_untile), and for
+the one-pass last micro-batch (adamw_step_tiled_sum, adamw_step_sum,
+grad_sum_norm_sq): sizes, alignments, null pointers, overlapping buffers
+and hyperparameters.  A
 Python model of the rules include/zshard.h documents (and of the order in
 which they are checked) predicts each return code.  Only argument sets the
 model says must fail, or are no-ops, are passed to the library, so no call
@@ -431,3 +432,43 @@ def test_grad_sum_norm_sq_validation_matches_the_documented_rules(ptrs, dt, n, o
     got = zs.lib().grad_sum_norm_sq(acc or None, g or None, dt, n, 1 if overwrite else 0, scale, out or None,
                                     ws or None, wsb, None)
     assert got == want, ([hex(p) for p in ptrs], dt, n, overwrite, scale, wsb)
+
+
+def split_sum_model(hp, p, m, v, acc, g, dt, b, n, norm):
+    rc = hp_model(hp, n, norm)
+    if rc is not None:
+        return rc
+    if dt not in (F32, BF16):
+        return EINVAL
+    if n == 0:
+        return OK
+    gsz = 4 if dt == F32 else 2
+    if not (p and m and v and g):
+        return EINVAL
+    if p % 4 or m % 4 or v % 4 or g % gsz or (acc and acc % 4) or (b and b % 2):
+        return EINVAL
+    bufs = [(p, 4 * n, True), (m, 4 * n, True), (v, 4 * n, True), (acc, 4 * n if acc else 0, False),
+            (g, gsz * n, False), (b, 2 * n if b else 0, True)]
+    for i in range(6):
+        for j in range(i + 1, 6):
+            if overlap(bufs[i][0], bufs[i][1], bufs[j][0], bufs[j][1]):
+                return EOVERLAP
+        if norm and bufs[i][2] and overlap(bufs[i][0], bufs[i][1], norm, 8):
+            return EOVERLAP
+    return None
+
+
+@SETTINGS
+@given(hp=hyperparameters(), ptrs=st.tuples(pointers, pointers, pointers, pointers, pointers, pointers),
+       dt=dtypes, n=st.sampled_from([-1, 0, 1, 3, 255, 1000, MAX_ELEMS + 1]),
+       norm=st.one_of(st.just(0), st.builds(lambda slot, off: BASE + slot * 4096 + off,
+                                            st.integers(0, 7), st.sampled_from([0, 8, 2000, 4]))))
+def test_adamw_step_sum_validation_matches_the_documented_rules(hp, ptrs, dt, n, norm):
+    p, m, v, acc, g, b = ptrs
+    want = split_sum_model(hp, p, m, v, acc, g, dt, b, n, norm)
+    if want is None:
+        return   # a valid call would launch a kernel: not made here
+    c = B.AdamW(*hp[:8], hp[8])
+    got = zs.lib().adamw_step_sum(ctypes.byref(c), p or None, m or None, v or None, acc or None, g or None, dt,
+                                  b or None, n, norm or None, None)
+    assert got == want, (hp, [hex(x) for x in ptrs], dt, n, hex(norm))

@@ -50,8 +50,8 @@ def test_shard_optimizer_matches_the_oracle(mode, layout):
         opt.step(extra_norm_sq=extra, last_grad=from_np(mbs[-1], bf16=True) if mode == "last_grad" else None)
         torch.cuda.synchronize()
         assert opt.t == t
-        # the tiled state's one-pass step never stores the last micro-batch's sum
-        stored = before_last if (mode == "last_grad" and layout == "tiled") else acc_ref
+        # the one-pass step never stores the last micro-batch's sum
+        stored = before_last if mode == "last_grad" else acc_ref
         assert bits_equal(to_np(opt.acc), stored)
         assert abs(opt.norm_sq.item() - S) <= NORM_TOL * S
         coef = oracle.clip_coef(S, extra, 1.0)
@@ -156,18 +156,17 @@ def test_captured_step_replays_like_eager_steps(max_norm, layout):
     b = zs.ShardOptimizer(p0.clone(), param_bf16=torch.empty(n, dtype=torch.bfloat16, device="cuda"), **kw)
     grads = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for _ in range(M)]
     cap = a.capture(grads, extra_norm_sq=0.02)
-    # the twin runs the schedule the capture records: on the tiled state the
-    # last gradient goes to step() (its sum with the accumulator never stored)
-    tiled = layout == "tiled"
+    # the twin runs the schedule the capture records: the last gradient goes
+    # to step() (its sum with the accumulator never stored)
     torch.cuda.synchronize()
     assert a.t == 0 and bits_equal(to_np(a.master), to_np(p0))   # capturing changed nothing
     for t in range(1, 5):
         for k, g in enumerate(grads):
             g.copy_((torch.randn(n, generator=gen, device="cuda") * 1e-2 * (k + t)).to(torch.bfloat16))
         cap.replay()
-        for k, g in enumerate(grads[:M - 1] if tiled else grads):
-            b.accumulate(g, last=k == M - 1)
-        b.step(extra_norm_sq=0.02, last_grad=grads[-1] if tiled else None)
+        for g in grads[:M - 1]:
+            b.accumulate(g)
+        b.step(extra_norm_sq=0.02, last_grad=grads[-1])
         torch.cuda.synchronize()
         assert a.t == b.t == t
         for name in ("master", "exp_avg", "exp_avg_sq", "param_bf16", "acc"):
@@ -184,8 +183,8 @@ def test_captured_step_replays_like_eager_steps(max_norm, layout):
 def test_step_with_last_grad_equals_accumulate_then_step(layout, M, dtype, max_norm):
     """step(last_grad=g) against accumulate(g, last=True) then step(), over
     four steps of M micro-batches: master, moments, bf16 parameter and norm
-    bit-identical; on the tiled state the accumulator keeps the earlier
-    micro-batches' sum (bit for bit the oracle's fold of them)."""
+    bit-identical; the accumulator keeps the earlier micro-batches' sum (bit
+    for bit the oracle's fold of them)."""
     print(f"ShardOptimizer last_grad layout={layout} M={M} dtype={dtype} max_norm={max_norm}", flush=True)
     n = 2 * zs.STATE_TILE + 4099
     rng = np.random.default_rng(M * 7 + (dtype == torch.float32) + int(max_norm * 10))
@@ -210,7 +209,7 @@ def test_step_with_last_grad_equals_accumulate_then_step(layout, M, dtype, max_n
         assert a.norm_sq.item() == b.norm_sq.item(), t
         for name in ("master", "exp_avg", "exp_avg_sq", "param_bf16"):
             assert bits_equal(to_np(getattr(a, name)), to_np(getattr(b, name))), (t, name)
-        if layout == "tiled" and M > 1:
+        if M > 1:
             acc_ref = np.empty(n, np.float32)
             for k, g in enumerate(mbs[:-1]):
                 oracle.grad_accum(acc_ref, g, oracle.BF16 if bf16 else oracle.F32, overwrite=(k == 0))

@@ -220,3 +220,88 @@ def test_adamw_step_tiled_sum_rejects():
     with pytest.raises(zs.ZShardError):   # workspace too small
         out = torch.zeros(1, dtype=torch.float64, device="cuda")
         zs.grad_sum_norm_sq(acc, g, False, 1.0, out, torch.empty(8, dtype=torch.uint8, device="cuda"))
+
+
+# split state: (master, exp_avg, exp_avg_sq) offsets, the gradient's offset
+SPLIT_OFFSETS = [((0, 0, 0), 0), ((3, 3, 3), 1), ((1, 2, 0), 0), ((8, 8, 8), 2)]
+
+
+@pytest.mark.parametrize("n", [1, 255, 257, 8193, 100_003])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("with_acc", [True, False])
+@pytest.mark.parametrize("offs,grad_off", SPLIT_OFFSETS)
+def test_adamw_step_sum_split_bit_exact(n, dtype, with_acc, offs, grad_off):
+    """The split-buffer form, two steps: handed the oracle's norm, master,
+    moments and bf16 output equal the oracle's accumulate-then-step bit for
+    bit; with the GPU's own norm, equal grad_accum_norm_sq then adamw_step.
+    Offsets: all aligned; the state sharing one offset off a 128-byte
+    boundary (peeled) with the gradient 2 bytes off 4 (bf16: element-wise);
+    the state at different offsets (element-wise); a shared 32-byte offset."""
+    print(f"adamw_step_sum n={n} dtype={dtype} acc={with_acc} offs={offs} grad_off={grad_off}", flush=True)
+    rng = np.random.default_rng(n + 17 * grad_off + 5 * sum(offs) + with_acc + len(dtype))
+    p_ref = rng.uniform(-0.1, 0.1, n).astype(np.float32)
+    m_ref, v_ref, b_ref = np.zeros(n, np.float32), np.zeros(n, np.float32), np.zeros(n, np.uint16)
+    bufs = [dev_buf(x, o) for x, o in zip((p_ref, m_ref, v_ref), offs)]
+    two = [dev_buf(x, o) for x, o in zip((p_ref, m_ref, v_ref), offs)]
+    b, bw = dev_buf(b_ref, 1, bf16=True)
+    b_two, _ = dev_buf(b_ref, 1, bf16=True)
+    scale = 1.0 / 16
+    for t in range(1, 3):
+        acc0 = (rng.standard_normal(n) * 1e-2).astype(np.float32)
+        g = _grad(rng, n, dtype)
+        ref = acc0.copy()
+        oracle.grad_accum(ref, g, _code(dtype), overwrite=not with_acc)
+        S = oracle.grad_norm_sq(ref, scale)
+        hp_gpu, hp_orc = _hp(t, scale=scale, max_norm=math.sqrt(S) * 0.7, extra=0.1 * S)
+        oracle.adamw_step(hp_orc, p_ref, m_ref, v_ref, ref, b_ref, norm_sq=S)
+        acc, acc_whole = dev_buf(acc0, 0)
+        gd, g_whole = dev_buf(g, grad_off, bf16=(dtype == "bf16"))
+        norm = torch.tensor([S], dtype=torch.float64, device="cuda")
+        zs.adamw_step_sum(hp_gpu, *(x for x, _ in bufs), acc if with_acc else None, gd, b, norm_sq=norm)
+        # the two-call path with its own norm, and the one-pass norm next to it
+        own = torch.zeros(1, dtype=torch.float64, device="cuda")
+        zs.grad_sum_norm_sq(acc if with_acc else None, gd, not with_acc, scale, own)
+        acc2, _ = dev_buf(acc0, 0)
+        own2 = torch.zeros(1, dtype=torch.float64, device="cuda")
+        zs.grad_accum_norm_sq(acc2, gd, not with_acc, scale, own2)
+        torch.cuda.synchronize()
+        assert own.item() == own2.item()
+        for (x, _), want in zip(bufs, (p_ref, m_ref, v_ref)):
+            assert bits_equal(to_np(x), want), (t, identical_fraction(to_np(x), want))
+        assert bits_equal(to_np(b), b_ref), t
+        assert bits_equal(to_np(acc), acc0), "the accumulator was written"
+        # the two-call path from the same start, with the oracle's norm: the same bits
+        zs.adamw_step(hp_gpu, *(x for x, _ in two), acc2, b_two, norm_sq=norm)
+        torch.cuda.synchronize()
+        for (x, _), (y, _) in zip(two, bufs):
+            assert bits_equal(to_np(x), to_np(y)), t
+        assert canary_ok(acc_whole, 0, n) and canary_ok(g_whole, grad_off, n)
+    for (x, whole), o in zip(bufs, offs):
+        assert canary_ok(whole, o, n)
+    assert canary_ok(bw, 1, n)
+
+
+def test_adamw_step_sum_dev_scalars():
+    """Split state, scalars from device memory: the host-scalar step's bits."""
+    n = 50_003
+    rng = np.random.default_rng(12)
+    p0 = rng.uniform(-0.1, 0.1, n).astype(np.float32)
+    h = [dev_buf(x, 0)[0] for x in (p0, np.zeros(n, np.float32), np.zeros(n, np.float32))]
+    d = [dev_buf(x, 0)[0] for x in (p0, np.zeros(n, np.float32), np.zeros(n, np.float32))]
+    b_h = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+    b_d = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+    norm = torch.zeros(1, dtype=torch.float64, device="cuda")
+    sc = torch.empty(64, dtype=torch.uint8, device="cuda")
+    for t in range(1, 4):
+        acc, _ = dev_buf((rng.standard_normal(n) * 1e-2).astype(np.float32), 0)
+        gd, _ = dev_buf(_grad(rng, n, "bf16"), 0, bf16=True)
+        zs.grad_sum_norm_sq(acc, gd, False, 1 / 32, norm)
+        hp = zs.AdamWConfig(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, grad_scale=1 / 32,
+                            max_norm=0.3, extra_norm_sq=0.01, step=t)
+        zs.adamw_step_sum(hp, *h, acc, gd, b_h, norm_sq=norm)
+        sc[:56].copy_(torch.frombuffer(bytearray(zs.scalars_bytes(hp)), dtype=torch.uint8))
+        zs.adamw_step_sum_dev(sc, *d, acc, gd, b_d, norm_sq=norm)
+        torch.cuda.synchronize()
+        for x, y in zip(h, d):
+            assert bits_equal(to_np(x), to_np(y)), t
+        assert bits_equal(to_np(b_h), to_np(b_d)), t
