@@ -417,6 +417,11 @@ def run_gpu(w, steps: int, warmup: int):
         split_ms.append((e0, e1))
     torch.cuda.synchronize()
     r["split_ms"] = sum(a.elapsed_time(b) for a, b in split_ms) / steps
+    # and the step's own AdamW (accumulator + last gradient) on those split buffers
+    last = len(rig.grads) - 1
+    acc_arg = rig.acc if last > 0 else None
+    r["split_sum_ms"] = timed(lambda: zs.adamw_step_sum(rig.hp(rig.t + 1), master, exp_avg, exp_avg_sq, acc_arg,
+                                                        rig.grads[last], rig.param, norm_sq=rig.norm), steps)
 
     # outside the step: the one-pass sums of the step's micro-batch
     # gradients alone, without and with the norm (the reduce-scatter's
@@ -993,6 +998,8 @@ def main():
             "frac": adamw_bytes / (r["split_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
             "traffic": traffic_of("adamw_step", n, digests),
             "traffic_ceiling": ceiling_report(r["ceiling_split_ms"], adamw_bytes, r["split_ms"])},
+        "adamw_step_sum_split": {"ms": r["split_sum_ms"], "bytes_per_elem": bpe["adamw_step_sum"],
+                                 **rate(bpe["adamw_step_sum"] * n, r["split_sum_ms"])},
         "cpu_baseline": cpu,
         "flat_unit": flat,
         "zero1_flow": zero1,

@@ -59,14 +59,13 @@ def run_shard(w: workloads.Workload, n: int, sampled: bool, full_norm: bool, fus
     """Drive the library and the oracle through w.steps steps of one shard.
     fused True: the last micro-batch forms the norm in the same pass
     (grad_accum_norm_sq); False: grad_accum for every micro-batch, then
-    grad_norm_sq; "sum" (tiled layout): the last micro-batch is not stored,
-    its norm pass and AdamW read the accumulator and its gradient
-    (grad_sum_norm_sq, adamw_step_tiled_sum: bench.py's step).  layout
-    "tiled": the optimizer state in one tiled buffer and adamw_step_tiled;
-    the compared elements are read at the positions the header's layout
-    gives them."""
+    grad_norm_sq; "sum": the last micro-batch is not stored, its norm pass
+    and AdamW read the accumulator and its gradient (grad_sum_norm_sq, then
+    adamw_step_tiled_sum, bench.py's step, or adamw_step_sum on split
+    state).  layout "tiled": the optimizer state in one tiled buffer and
+    adamw_step_tiled; the compared elements are read at the positions the
+    header's layout gives them."""
     one_pass = fused == "sum"
-    assert not one_pass or layout == "tiled"
     master = workloads.master_init(w, n, DEV)
     param = master.to(torch.bfloat16) if w.bf16_param else None
     if layout == "tiled":
@@ -129,8 +128,11 @@ def run_shard(w: workloads.Workload, n: int, sampled: bool, full_norm: bool, fus
         hp = zs.AdamWConfig(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
                             weight_decay=w.weight_decay, grad_scale=w.grad_scale, max_norm=w.max_norm,
                             extra_norm_sq=extra, step=t)
-        if one_pass:
+        if one_pass and layout == "tiled":
             zs.adamw_step_tiled_sum(hp, state, acc if last > 0 else None, g_last, param, norm_sq=norm)
+            del g_last
+        elif one_pass:
+            zs.adamw_step_sum(hp, master, exp_avg, exp_avg_sq, acc if last > 0 else None, g_last, param, norm_sq=norm)
             del g_last
         elif layout == "tiled":
             zs.adamw_step_tiled(hp, state, acc, param, norm_sq=norm)
@@ -172,8 +174,7 @@ SMALL = [("llama7b_shard", 1_000_037), ("llama13b_shard_clip", 600_011), ("zero3
 
 
 @pytest.mark.parametrize("name,n,fused,layout",
-                         [(w, n, f, lay) for w, n in SMALL for f in (True, False) for lay in ("split", "tiled")] +
-                         [(w, n, "sum", "tiled") for w, n in SMALL])
+                         [(w, n, f, lay) for w, n in SMALL for f in (True, False, "sum") for lay in ("split", "tiled")])
 def test_workload_small(name, n, fused, layout):
     """Every element, at a reduced shard length.  The gradient std is scaled
     by sqrt(full/n) so the global norm, and with it the clipping pattern of
