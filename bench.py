@@ -990,7 +990,8 @@ def main():
         "step_two_call": two_call_report(w, r, n),
         "device_copy_gbps": r["copy_gbps"],
         "timing_events": timing_events(),
-        "adamw_traffic_ceiling": ceiling_report(r["ceiling_ms"], adamw_bytes, tc["adamw_ms"], "zsc_adamw_traffic_tiled"),
+        "adamw_traffic_ceiling": ceiling_report(r["ceiling_ms"], adamw_bytes, tc["adamw_ms"],
+                                                "zsc_adamw_traffic_tiled"),
         "roofline": roofline(w, r, n),
         "adamw_step_split": {
             "ms": r["split_ms"], "bytes_per_elem": bpe["adamw_step"],

@@ -15,7 +15,8 @@ The Python names mirror the C ABI in include/zshard.h:
     adamw_step(hp, master, exp_avg, exp_avg_sq, grad, param_bf16=None, norm_sq=None)
     adamw_scalars(hp) / scalars_bytes(hp)       the step's binary32 scalars, on the host
     adamw_step_dev(scalars_dev, master, exp_avg, exp_avg_sq, grad, param_bf16=None, norm_sq=None)
-    adamw_step_sum(hp, master, exp_avg, exp_avg_sq, acc, grad, param_bf16=None, norm_sq=None)   gradient fl(acc + widen(grad))
+    adamw_step_sum(hp, master, exp_avg, exp_avg_sq, acc, grad, param_bf16=None, norm_sq=None)
+                                                the step on fl(acc + widen(grad)), the sum not stored
     adamw_step_sum_dev(scalars_dev, master, exp_avg, exp_avg_sq, acc, grad, param_bf16=None, norm_sq=None)
     adamw_step_no_master(hp, param_bf16, exp_avg, exp_avg_sq, grad, norm_sq=None)
     adam_update(hp, exp_avg, exp_avg_sq, grad, update, norm_sq=None)

@@ -8,9 +8,10 @@ not formed yet and requested) and the fused AdamW update with the bf16
 re-cast.  ``step(last_grad=g)`` takes the last micro-batch's gradient
 itself instead: its sum with the accumulator is never stored (the norm pass
 reads both, and so does AdamW), which saves the accumulator's write and
-re-read, 8 B per element; the results are the same bit for bit.  Where a step's micro-batch gradients are all kept in device
-memory (2 B per element each in bf16), ``accumulate_all`` sums them in one
-pass instead.  Nothing here computes; it orders calls.
+re-read, 8 B per element; the results are the same bit for bit.  Where a
+step's micro-batch gradients are all kept in device memory (2 B per element
+each in bf16), ``accumulate_all`` sums them in one pass instead.  Nothing
+here computes; it orders calls.
 
 ``layout="tiled"`` (the default) keeps master, exp_avg and exp_avg_sq in
 one buffer in the library's tiled state layout, which the AdamW step
