@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Shard length against allocation history, in one process on one GPU.
 
-    python bench_alloc.py [--reps 10] [--rounds 2]
+    python bench_alloc.py [--reps 10] [--rounds 2] [--pad-gib G ...]
 
 Part 1 (shard length): the accumulation (grad_accum, add), the fused last
 micro-batch (grad_accum_norm_sq, add) and the clipped tiled AdamW step
@@ -11,6 +11,9 @@ interleaved rounds: the same physical memory for every length.
 Part 2 (allocation history): the AdamW step on the 70B ZeRO-3 and the
 Llama-7B shards (bench.py's step rig) allocated fresh, with the other shard
 resident, and re-allocated after the other shard's buffers were freed.
+Part 3 (--pad-gib): the one-pass step of the Llama-7B rig (bench.py's timed
+step) allocated behind G GiB of padding held in device memory, for each G:
+the same buffers at other physical pages.
 
 One line per measurement: what, shard length, ms per launch (HIP events on
 the launch stream) and % of the 8 TB/s HBM peak for the kernel's
@@ -35,6 +38,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--reps", type=int, default=10)
     ap.add_argument("--rounds", type=int, default=2)
+    ap.add_argument("--pad-gib", type=int, nargs="*", default=[])
     args = ap.parse_args()
 
     import torch
@@ -79,7 +83,7 @@ def main():
     W7, W70 = workloads.WORKLOADS["llama7b_shard"], workloads.WORKLOADS["zero3_70b_shard"]
 
     def adamw(rig, what):
-        rig.step(rig.t + 1)   # accumulator and norm of a real step in place
+        rig.two_call_step(rig.t + 1)   # the stored sum and norm of a real step in place
         rig.t += 1
         line(what, rig.n, 30, timed(lambda: zs.adamw_step_tiled(rig.hp(rig.t), rig.state, rig.acc, rig.param,
                                                                 norm_sq=rig.norm), args.reps))
@@ -103,6 +107,17 @@ def main():
         a = StepRig(W70, dev)
         adamw(a, f"r{r} 70B shard, re-allocated after the 7B freed")
         del a
+        free()
+
+    # part 3: the one-pass step behind padding
+    for gib in args.pad_gib:
+        pad = torch.empty(gib << 28, dtype=torch.float32, device=dev) if gib > 0 else None
+        rig = StepRig(W7, dev)
+        res = rig.time_steps(args.reps, 2)
+        n = rig.n
+        line(f"pad {gib} GiB: one-pass step's AdamW", n, 32, res["adamw_ms"])
+        line(f"pad {gib} GiB: accumulation of 7 micro-batches", n, 66, res["accum_ms"])
+        del rig, pad
         free()
     print("done", flush=True)
 
