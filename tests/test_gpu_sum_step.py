@@ -305,3 +305,65 @@ def test_adamw_step_sum_dev_scalars():
         for x, y in zip(h, d):
             assert bits_equal(to_np(x), to_np(y)), t
         assert bits_equal(to_np(b_h), to_np(b_d)), t
+
+
+def test_one_pass_random_configurations():
+    """160 seeded random cases (length up to 70,000 across tile and block
+    edges; bf16 or fp32 gradient, with or without an accumulator; tiled or
+    split state at random element offsets; bf16 output present or not, at
+    random offsets; clip on or off): the one-pass norm is grad_accum_norm_sq's
+    bits, and the one-pass step, handed the oracle's norm, the oracle's
+    accumulate-then-step bits."""
+    rng = np.random.default_rng(2027)
+    for case in range(160):
+        n = int(rng.choice([int(rng.integers(1, 600)), int(rng.integers(1, 70_000)),
+                            int(rng.choice([255, 256, 257, 1023, 1024, 1025, 8191, 8192, 8193, 16384]))]))
+        dtype = str(rng.choice(["bf16", "f32"]))
+        with_acc = bool(rng.integers(0, 2))
+        tiled = bool(rng.integers(0, 2))
+        offs = [int(x) for x in rng.integers(0, 4, size=3)] if not tiled else [0, 0, 0]
+        if rng.integers(0, 2):
+            offs = [offs[0]] * 3   # a shared offset: the peeled form
+        g_off, b_off = int(rng.integers(0, 3)), int(rng.integers(0, 4))
+        with_b = bool(rng.integers(0, 4))
+        clip = bool(rng.integers(0, 2))
+        scale = float(rng.choice([1 / 8, 1 / 64]))
+        tag = (case, n, dtype, with_acc, tiled, offs, g_off, b_off, with_b, clip)
+        p = rng.uniform(-0.1, 0.1, n).astype(np.float32)
+        m = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+        v = rng.uniform(0, 1e-6, n).astype(np.float32)
+        acc0 = (rng.standard_normal(n) * 1e-2).astype(np.float32)
+        g = _grad(rng, n, dtype)
+        ref = acc0.copy()
+        oracle.grad_accum(ref, g, _code(dtype), overwrite=not with_acc)
+        S = oracle.grad_norm_sq(ref, scale)
+        hp_gpu, hp_orc = _hp(int(rng.integers(1, 9)), scale=scale, max_norm=math.sqrt(S) * 0.6 if clip else 0.0,
+                             extra=0.3 * S)
+        b_ref = np.zeros(n, np.uint16)
+        p_ref, m_ref, v_ref = p.copy(), m.copy(), v.copy()
+        oracle.adamw_step(hp_orc, p_ref, m_ref, v_ref, ref, b_ref if with_b else None, norm_sq=S)
+        acc, _ = dev_buf(acc0, 0)
+        acc_arg = acc if with_acc else None
+        gd, _ = dev_buf(g, g_off, bf16=(dtype == "bf16"))
+        b = dev_buf(np.zeros(n, np.uint16), b_off, bf16=True)[0] if with_b else None
+        # the norm: bit for bit the fused pass's
+        one = torch.zeros(1, dtype=torch.float64, device="cuda")
+        zs.grad_sum_norm_sq(acc_arg, gd, not with_acc, scale, one)
+        acc2, _ = dev_buf(acc0, 0)
+        two = torch.zeros(1, dtype=torch.float64, device="cuda")
+        zs.grad_accum_norm_sq(acc2, gd, not with_acc, scale, two)
+        norm = torch.tensor([S], dtype=torch.float64, device="cuda")
+        if tiled:
+            st, _ = dev_buf(oracle.state_tile(p, m, v, n, T), 0)
+            zs.adamw_step_tiled_sum(hp_gpu, st, acc_arg, gd, b, norm_sq=norm)
+            got = oracle.state_untile(to_np(st), n, T)
+        else:
+            bufs = [dev_buf(x, o)[0] for x, o in zip((p, m, v), offs)]
+            zs.adamw_step_sum(hp_gpu, *bufs, acc_arg, gd, b, norm_sq=norm)
+            got = [to_np(x) for x in bufs]
+        torch.cuda.synchronize()
+        assert one.item() == two.item(), tag
+        for x, want in zip(got, (p_ref, m_ref, v_ref)):
+            assert bits_equal(x, want), (tag, identical_fraction(x, want))
+        if with_b:
+            assert bits_equal(to_np(b), b_ref), tag
