@@ -376,6 +376,26 @@ static_assert(offsetof(zs_adamw_scalars, max_norm) == offsetof(zs::AdamwScalars,
 static_assert(offsetof(zs_adamw_scalars, extra_norm_sq) == offsetof(zs::AdamwScalars, extra_norm_sq),
               "scalar layout");
 
+// The scalars of a master-form step: host hyperparameters (hp, validated
+// here) or a device copy of adamw_scalars' output (sc_dev: only its
+// alignment can be checked); and the kernels' arguments for either.
+static int32_t check_scalars(const zs_adamw* hp, const zs_adamw_scalars* sc_dev, int64_t n,
+                             const double* norm_sq_dev) {
+    if (sc_dev == nullptr) return adamw_check_hp(hp, n, norm_sq_dev);
+    if (!size_ok(n) || !aligned(sc_dev, 8)) return ZS_EINVAL;
+    if (norm_sq_dev != nullptr && !aligned(norm_sq_dev, 8)) return ZS_EINVAL;
+    return ZS_OK;
+}
+
+static zs::AdamwArgs step_args(const zs_adamw* hp, const zs_adamw_scalars* sc_dev, const double* norm_sq_dev) {
+    if (sc_dev == nullptr) return make_args(hp, norm_sq_dev);
+    zs::AdamwArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.sc_dev = reinterpret_cast<const zs::AdamwScalars*>(sc_dev);
+    a.norm_sq = norm_sq_dev;
+    return a;
+}
+
 // the five buffers (any may be absent: bytes 0) pairwise disjoint, and none
 // that is written overlapping the norm
 static int32_t adamw_check_overlap(const void* const* bufs, const int64_t* bytes, const bool* written,
@@ -393,14 +413,8 @@ static int32_t adamw_check_overlap(const void* const* bufs, const int64_t* bytes
 static int32_t adamw_master(const zs_adamw* hp, const zs_adamw_scalars* sc_dev, float* master, float* exp_avg,
                             float* exp_avg_sq, const float* grad, uint16_t* param_bf16, int64_t n,
                             const double* norm_sq_dev, void* hip_stream) {
-    int32_t rc;
-    if (sc_dev == nullptr) {
-        rc = adamw_check_hp(hp, n, norm_sq_dev);
-        if (rc != ZS_OK) return rc;
-    } else {
-        if (!size_ok(n) || !aligned(sc_dev, 8)) return ZS_EINVAL;
-        if (norm_sq_dev != nullptr && !aligned(norm_sq_dev, 8)) return ZS_EINVAL;
-    }
+    int32_t rc = check_scalars(hp, sc_dev, n, norm_sq_dev);
+    if (rc != ZS_OK) return rc;
     if (n == 0) return ZS_OK;
     if (master == nullptr || exp_avg == nullptr || exp_avg_sq == nullptr || grad == nullptr)
         return ZS_EINVAL;
@@ -416,14 +430,7 @@ static int32_t adamw_master(const zs_adamw* hp, const zs_adamw_scalars* sc_dev, 
         for (int i = 0; i < 5; ++i)
             if (written[i] && overlap(bufs[i], bytes[i], sc_dev, (int64_t)sizeof(zs_adamw_scalars)))
                 return ZS_EOVERLAP;
-    zs::AdamwArgs a;
-    if (sc_dev == nullptr) {
-        a = make_args(hp, norm_sq_dev);
-    } else {
-        std::memset(&a, 0, sizeof(a));
-        a.sc_dev = reinterpret_cast<const zs::AdamwScalars*>(sc_dev);
-        a.norm_sq = norm_sq_dev;
-    }
+    zs::AdamwArgs a = step_args(hp, sc_dev, norm_sq_dev);
     a.master = master;
     a.exp_avg = exp_avg;
     a.exp_avg_sq = exp_avg_sq;
@@ -459,14 +466,8 @@ static int32_t adamw_master(const zs_adamw* hp, const zs_adamw_scalars* sc_dev, 
 static int32_t adamw_master_sum(const zs_adamw* hp, const zs_adamw_scalars* sc_dev, float* master, float* exp_avg,
                                 float* exp_avg_sq, const float* acc, const void* grad, int32_t grad_dtype,
                                 uint16_t* param_bf16, int64_t n, const double* norm_sq_dev, void* hip_stream) {
-    int32_t rc;
-    if (sc_dev == nullptr) {
-        rc = adamw_check_hp(hp, n, norm_sq_dev);
-        if (rc != ZS_OK) return rc;
-    } else {
-        if (!size_ok(n) || !aligned(sc_dev, 8)) return ZS_EINVAL;
-        if (norm_sq_dev != nullptr && !aligned(norm_sq_dev, 8)) return ZS_EINVAL;
-    }
+    int32_t rc = check_scalars(hp, sc_dev, n, norm_sq_dev);
+    if (rc != ZS_OK) return rc;
     if (!dtype_ok(grad_dtype)) return ZS_EINVAL;
     if (n == 0) return ZS_OK;
     const int64_t gsz = elem_size(grad_dtype);
@@ -484,14 +485,7 @@ static int32_t adamw_master_sum(const zs_adamw* hp, const zs_adamw_scalars* sc_d
         if (sc_dev != nullptr && written[i] && overlap(bufs[i], bytes[i], sc_dev, (int64_t)sizeof(zs_adamw_scalars)))
             return ZS_EOVERLAP;
     }
-    zs::AdamwArgs a;
-    if (sc_dev == nullptr) {
-        a = make_args(hp, norm_sq_dev);
-    } else {
-        std::memset(&a, 0, sizeof(a));
-        a.sc_dev = reinterpret_cast<const zs::AdamwScalars*>(sc_dev);
-        a.norm_sq = norm_sq_dev;
-    }
+    zs::AdamwArgs a = step_args(hp, sc_dev, norm_sq_dev);
     a.master = master;
     a.exp_avg = exp_avg;
     a.exp_avg_sq = exp_avg_sq;
@@ -645,14 +639,8 @@ int32_t moments_untile(const float* moments, float* exp_avg, float* exp_avg_sq, 
 // the tiled master-form step: host scalars (hp) or a device copy of them (sc_dev)
 static int32_t adamw_tiled(const zs_adamw* hp, const zs_adamw_scalars* sc_dev, float* state, const float* grad,
                            uint16_t* param_bf16, int64_t n, const double* norm_sq_dev, void* hip_stream) {
-    int32_t rc;
-    if (sc_dev == nullptr) {
-        rc = adamw_check_hp(hp, n, norm_sq_dev);
-        if (rc != ZS_OK) return rc;
-    } else {
-        if (!size_ok(n) || !aligned(sc_dev, 8)) return ZS_EINVAL;
-        if (norm_sq_dev != nullptr && !aligned(norm_sq_dev, 8)) return ZS_EINVAL;
-    }
+    int32_t rc = check_scalars(hp, sc_dev, n, norm_sq_dev);
+    if (rc != ZS_OK) return rc;
     if (n == 0) return ZS_OK;
     if (state == nullptr || grad == nullptr) return ZS_EINVAL;
     if (!aligned(state, 16) || !aligned(grad, 4) || (param_bf16 != nullptr && !aligned(param_bf16, 2)))
@@ -666,14 +654,7 @@ static int32_t adamw_tiled(const zs_adamw* hp, const zs_adamw_scalars* sc_dev, f
         for (int i = 0; i < 5; ++i)
             if (written[i] && overlap(bufs[i], bytes[i], sc_dev, (int64_t)sizeof(zs_adamw_scalars)))
                 return ZS_EOVERLAP;
-    zs::AdamwArgs a;
-    if (sc_dev == nullptr) {
-        a = make_args(hp, norm_sq_dev);
-    } else {
-        std::memset(&a, 0, sizeof(a));
-        a.sc_dev = reinterpret_cast<const zs::AdamwScalars*>(sc_dev);
-        a.norm_sq = norm_sq_dev;
-    }
+    zs::AdamwArgs a = step_args(hp, sc_dev, norm_sq_dev);
     a.state = state;
     a.grad = grad;
     a.param_bf16 = param_bf16;
@@ -700,14 +681,8 @@ int32_t adamw_step_tiled_dev(const zs_adamw_scalars* scalars_dev, float* state, 
 static int32_t adamw_tiled_sum(const zs_adamw* hp, const zs_adamw_scalars* sc_dev, float* state, const float* acc,
                                const void* grad, int32_t grad_dtype, uint16_t* param_bf16, int64_t n,
                                const double* norm_sq_dev, void* hip_stream) {
-    int32_t rc;
-    if (sc_dev == nullptr) {
-        rc = adamw_check_hp(hp, n, norm_sq_dev);
-        if (rc != ZS_OK) return rc;
-    } else {
-        if (!size_ok(n) || !aligned(sc_dev, 8)) return ZS_EINVAL;
-        if (norm_sq_dev != nullptr && !aligned(norm_sq_dev, 8)) return ZS_EINVAL;
-    }
+    int32_t rc = check_scalars(hp, sc_dev, n, norm_sq_dev);
+    if (rc != ZS_OK) return rc;
     if (!dtype_ok(grad_dtype)) return ZS_EINVAL;
     if (n == 0) return ZS_OK;
     const int64_t gsz = elem_size(grad_dtype);
@@ -724,14 +699,7 @@ static int32_t adamw_tiled_sum(const zs_adamw* hp, const zs_adamw_scalars* sc_de
         for (int i = 0; i < 5; ++i)
             if (written[i] && overlap(bufs[i], bytes[i], sc_dev, (int64_t)sizeof(zs_adamw_scalars)))
                 return ZS_EOVERLAP;
-    zs::AdamwArgs a;
-    if (sc_dev == nullptr) {
-        a = make_args(hp, norm_sq_dev);
-    } else {
-        std::memset(&a, 0, sizeof(a));
-        a.sc_dev = reinterpret_cast<const zs::AdamwScalars*>(sc_dev);
-        a.norm_sq = norm_sq_dev;
-    }
+    zs::AdamwArgs a = step_args(hp, sc_dev, norm_sq_dev);
     a.state = state;
     a.grad = acc;
     a.grad_mb = grad;
