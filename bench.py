@@ -228,27 +228,48 @@ def rate(nbytes: float, ms: float) -> dict:
 
 class StepRig:
     """One rank's resident buffers for a workload: the tiled optimizer
-    state (master values in, moments zero), the fp32 accumulator, the bf16
-    parameter, the step's micro-batch gradients (seeded draws), the norm
-    and its workspace."""
+    state (master values in, moments zero), the fp32 accumulator, the step's
+    micro-batch gradients (seeded draws) and the bf16 parameter, views of
+    one physically contiguous DeviceArena (in that order) unless ``arena``
+    is false; the norm and its workspace."""
 
-    def __init__(self, w, dev):
+    def __init__(self, w, dev, arena: bool = True):
         import torch
         import workloads
         import fsdp_sharded_optimizer_amd as zs
         self.w, self.dev = w, dev
         self.n = n = shard_len(w)
         log(f"[bench] workload={w.name} shard_elems={n} micro_batches={w.micro_batches}")
+        f32, gdt = torch.float32, (torch.bfloat16 if w.grad_dtype == "bf16" else torch.float32)
+        ws = max(zs.grad_accum_norm_sq_workspace_bytes(n), zs.grad_norm_sq_workspace_bytes(n),
+                 zs.grad_reduce_chunks_norm_sq_workspace_bytes(n), 8)
+        parts = ([(zs.state_tiled_numel(n), f32), (n, f32)] + [(n, gdt)] * w.micro_batches
+                 + [(n, torch.bfloat16)] * int(w.bf16_param))
+        self.arena = zs.DeviceArena(zs.DeviceArena.size(parts), dev) if arena else None
+
+        def take(numel, dtype):
+            return self.arena.take(numel, dtype) if arena else torch.empty(numel, dtype=dtype, device=dev)
+
+        self.state = take(*parts[0])
+        self.acc = take(*parts[1])
         master = workloads.master_init(w, n, dev)
-        self.param = master.to(torch.bfloat16) if w.bf16_param else None
-        self.state = torch.empty(zs.state_tiled_numel(n), dtype=torch.float32, device=dev)
         zs.state_tile(master, None, None, self.state)
+        self.grads = []
+        for mb in range(w.micro_batches):
+            self.grads.append(take(n, gdt))
+            self.grads[-1].copy_(workloads.grad_draw(w, n, 1, mb, dev))
+        self.param = take(n, torch.bfloat16).copy_(master) if w.bf16_param else None
         del master
-        self.acc = torch.empty(n, dtype=torch.float32, device=dev)
-        self.grads = [workloads.grad_draw(w, n, 1, mb, dev) for mb in range(w.micro_batches)]
+        # the norm and its partials stay ordinary allocations: the norm pass
+        # writes one 8-byte partial per 256 elements, scattered, and ran 5
+        # points slower with them in the contiguous block
         self.norm = torch.zeros(1, dtype=torch.float64, device=dev)
-        self.ws = torch.empty(max(zs.grad_accum_norm_sq_workspace_bytes(n), zs.grad_norm_sq_workspace_bytes(n),
-                                  zs.grad_reduce_chunks_norm_sq_workspace_bytes(n), 8), dtype=torch.uint8, device=dev)
+        self.ws = torch.empty(ws, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()   # the draws' temporaries
+        if self.arena is not None:
+            log(f"[bench] {w.name}: one {'contiguous' if self.arena.contiguous else 'ordinary'} "
+                f"block of {self.arena.nbytes / 2**30:.2f} GiB")
         self.t = 0
 
     def hp(self, t: int):
@@ -366,17 +387,16 @@ def timed(fn, reps: int) -> float:
     return e0.elapsed_time(e1) / reps
 
 
-def run_gpu(w, steps: int, warmup: int):
+def run_gpu(rig: StepRig, steps: int, warmup: int):
     import torch
     import fsdp_sharded_optimizer_amd as zs
     from fsdp_sharded_optimizer_amd import ledger
 
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-    rig = StepRig(w, dev)
+    w, dev = rig.w, rig.dev
     n = rig.n
     torch.cuda.synchronize()
-    log(f"[bench] inputs resident: {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
+    resident = rig.arena.nbytes if rig.arena is not None else torch.cuda.memory_allocated()
+    log(f"[bench] inputs resident: {resident / 2**30:.1f} GiB")
     r = rig.time_steps(steps, warmup)
     r["n"] = n
     r["chunks"] = len(rig.grads)
@@ -858,16 +878,21 @@ def main():
     zs.lib()
     digests = bench_pmc.kernel_digests()
 
-    # both shards' buffers are allocated up front, each on fresh device
-    # memory as a rank allocates its buffers once (re-allocating after a
-    # large free measured up to 3 points lower on gfx950, differing from run
-    # to run with the physical placement)
+    # both shards' buffers are allocated up front, as a rank allocates its
+    # buffers once, each shard's in one physically contiguous block (the
+    # timed workload's first): separate allocations made after other
+    # processes had allocated and freed device memory streamed up to 6
+    # points slower on gfx950, and a block placed behind tens of GiB of
+    # other allocations a few points slower
     import torch
     torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    rig = StepRig(w, dev)
     second_rig = None
     if args.second_workload and args.second_workload != w.name:
-        second_rig = StepRig(workloads.WORKLOADS[args.second_workload], torch.device("cuda", 0))
-    r = run_gpu(w, args.steps, args.warmup)
+        second_rig = StepRig(workloads.WORKLOADS[args.second_workload], dev)
+    r = run_gpu(rig, args.steps, args.warmup)
+    del rig
     n = r["n"]
     second = None
     if second_rig is not None:

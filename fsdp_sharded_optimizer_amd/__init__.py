@@ -32,6 +32,9 @@ The Python names mirror the C ABI in include/zshard.h:
     adam_update_tiled(hp, moments, grad, update, norm_sq=None)
     adamw_step_no_master_tiled(hp, param_bf16, moments, grad, norm_sq=None)
 
+DeviceArena(nbytes, device) holds one physically contiguous block of device
+memory and hands out 2 MiB-aligned views of it (ShardOptimizer(arena=...)).
+
 All device work runs in the library's gfx950 HIP kernels on the current
 torch stream; torch supplies device memory and the stream only.
 """
@@ -79,4 +82,5 @@ from ._binding import (  # noqa: F401
     state_untile,
     zero_shard_range,
 )
+from .arena import DeviceArena  # noqa: F401
 from .step import ShardOptimizer  # noqa: F401

@@ -21,6 +21,12 @@ the caller's master tensor only supplies the initial values.
 ``layout="split"`` steps the caller's master tensor and two moment buffers
 in place.  Both layouts give bit-identical results.
 
+``arena=DeviceArena(...)`` takes the optimizer's streamed buffers (the
+state and the accumulator, ``arena_parts``) from one physically contiguous
+block of device memory, which keeps the step's bandwidth independent of
+what the process and others allocated and freed before; the caller takes
+its gradient and parameter buffers from the same block.
+
 ``state_dict`` / ``load_state_dict`` carry the step counter and the fp32
 master, exp_avg and exp_avg_sq between runs: a resumed run continues bit
 for bit (the bf16 parameter is the master's re-cast, rewritten every step).
@@ -36,6 +42,7 @@ import numpy as np
 import torch
 
 from . import _binding as zs
+from .arena import DeviceArena
 
 
 _STATE_NAMES = ("master", "exp_avg", "exp_avg_sq")
@@ -45,29 +52,42 @@ class ShardOptimizer:
     def __init__(self, master: torch.Tensor, *, lr: float, betas=(0.9, 0.999), eps: float = 1e-8,
                  weight_decay: float = 0.0, grad_scale: float = 1.0, max_norm: float = 0.0,
                  param_bf16: Optional[torch.Tensor] = None, compute_norm: Optional[bool] = None,
-                 layout: str = "tiled"):
+                 layout: str = "tiled", arena: Optional[DeviceArena] = None):
         if master.dtype != torch.float32 or master.device.type != "cuda":
             raise TypeError("master must be an fp32 GPU tensor")
         if layout not in ("tiled", "split"):
             raise ValueError("layout must be 'tiled' or 'split'")
         n = master.numel()
         dev = master.device
+        if arena is not None and arena.device != dev:
+            raise ValueError(f"arena is on {arena.device}, master on {dev}")
         self.n = n
         self.layout = layout
+        self.arena = arena
+
+        def take(numel, dtype):
+            if arena is not None:
+                return arena.take(numel, dtype)
+            return torch.empty(numel, dtype=dtype, device=dev)
+
+        parts = iter(self.arena_parts(n, layout))
         if layout == "tiled":
             # the master's values go into the tiled buffer; the moments start at zero
-            self.state = torch.empty(zs.state_tiled_numel(n), dtype=torch.float32, device=dev)
+            self.state = take(*next(parts))
             zs.state_tile(master.reshape(-1), None, None, self.state, n=n)
             self._split = None
         else:
             self.state = None
-            self._split = {"master": master, "exp_avg": torch.zeros(n, dtype=torch.float32, device=dev),
-                           "exp_avg_sq": torch.zeros(n, dtype=torch.float32, device=dev)}
-        self.acc = torch.empty(n, dtype=torch.float32, device=dev)
+            self._split = {"master": master, "exp_avg": take(*next(parts)).zero_(),
+                           "exp_avg_sq": take(*next(parts)).zero_()}
+        self.acc = take(*next(parts))
         self.param_bf16 = param_bf16
         self.lr, self.betas, self.eps = lr, betas, eps
         self.weight_decay, self.grad_scale, self.max_norm = weight_decay, grad_scale, max_norm
         self.compute_norm = (max_norm > 0) if compute_norm is None else compute_norm
+        # the norm and its partials stay ordinary allocations: the norm pass
+        # writes one 8-byte partial per 256 elements, scattered, which ran
+        # 5 points slower in a contiguous block
         self.norm_sq = torch.zeros(1, dtype=torch.float64, device=dev)
         ws = max(zs.grad_norm_sq_workspace_bytes(n), zs.grad_accum_norm_sq_workspace_bytes(n),
                  zs.grad_reduce_chunks_norm_sq_workspace_bytes(n), 8)
@@ -75,6 +95,17 @@ class ShardOptimizer:
         self._norm_ready = False
         self.t = 0
         self._pending = 0
+
+    @staticmethod
+    def arena_parts(n: int, layout: str = "tiled") -> list:
+        """(numel, dtype) of each streamed buffer the optimizer takes from an
+        arena, in order: the state (tiled, or the two moments) and the
+        accumulator.  ``DeviceArena.size`` of these, plus the caller's own
+        parts (gradients, bf16 parameter), sizes an arena that holds a
+        rank's whole streamed working set."""
+        state = ([(zs.state_tiled_numel(n), torch.float32)] if layout == "tiled"
+                 else [(n, torch.float32), (n, torch.float32)])
+        return state + [(n, torch.float32)]
 
     def _state_tensor(self, name: str) -> torch.Tensor:
         if self._split is not None:
