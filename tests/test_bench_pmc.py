@@ -64,15 +64,18 @@ def _counter_csv(path, counter, rows):
 
 def test_record_calibrates_on_the_device_copy_and_selects_the_grid(tmp_path, digests):
     """Counters of two passes: the runtime copy kernel's largest dispatches
-    (the 4 GiB copy) set the scales, small copies are ignored, and the
-    kernel's dispatches at the listed grid are averaged (another grid of the
-    same kernel, another shard, is not)."""
+    (the 4 GiB copy) set the scales, smaller copies are ignored (also those
+    on the same grid, the step rigs' set-up copies), and the kernel's
+    dispatches at the listed grid are averaged (another grid of the same
+    kernel, another shard, is not)."""
     copy = bench_pmc.COPY_KERNEL
     k = "void " + ADAMW + "(zs::AdamwArgs)"
     _counter_csv(str(tmp_path / "f" / "x_counter_collection.csv"), "FETCH_SIZE",
-                 [(copy, 131072, 2097152.0), (copy, 512, 3.0), (k, 640, 100.0), (k, 640, 110.0), (k, 960, 999.0)])
+                 [(copy, 131072, 900000.0), (copy, 131072, 2097150.0), (copy, 131072, 2097154.0), (copy, 512, 3.0),
+                  (k, 640, 100.0), (k, 640, 110.0), (k, 960, 999.0)])
     _counter_csv(str(tmp_path / "w" / "x_counter_collection.csv"), "WRITE_SIZE",
-                 [(copy, 131072, 4194304.0), (copy, 512, 1.0), (k, 640, 300.0), (k, 640, 300.0), (k, 960, 7.0)])
+                 [(copy, 131072, 1800000.0), (copy, 131072, 4194304.0), (copy, 512, 1.0), (k, 640, 300.0),
+                  (k, 640, 300.0), (k, 960, 7.0)])
     log = tmp_path / "bench.log"
     bench = {"code_objects_sha256": sorted(set(digests.values())),
              "pmc_kernels": [{"label": "adamw_step_tiled", "kernel": ADAMW, "shard_elems": 2560, "grid": 640,
