@@ -12,10 +12,11 @@ Part 2 (allocation history): the AdamW step on the 70B ZeRO-3 and the
 Llama-7B shards (bench.py's step rig) allocated fresh, with the other shard
 resident, and re-allocated after the other shard's buffers were freed;
 each rig's buffers allocated one by one ("separate") and as views of one
-physically contiguous block ("arena", bench.py's policy).
+physically contiguous block ("arena", bench.py's policy; such a block is
+never freed, so a rig made again takes its pooled block back).
 Part 3 (--pad-gib): the one-pass step of the Llama-7B rig (bench.py's timed
-step) allocated behind G GiB of padding held in device memory, for each G:
-the same buffers at other physical pages (--pad-arena 0: separately).
+step, its buffers allocated one by one) allocated behind G GiB of padding
+held in device memory, for each G: the same buffers at other physical pages.
 
 One line per measurement: what, shard length, ms per launch (HIP events on
 the launch stream) and % of the 8 TB/s HBM peak for the kernel's
@@ -41,7 +42,6 @@ def main():
     ap.add_argument("--reps", type=int, default=10)
     ap.add_argument("--rounds", type=int, default=2)
     ap.add_argument("--pad-gib", type=int, nargs="*", default=[])
-    ap.add_argument("--pad-arena", type=int, default=1, help="part 3 rig in one contiguous block (1) or not (0)")
     args = ap.parse_args()
 
     import torch
@@ -117,7 +117,7 @@ def main():
     # part 3: the one-pass step behind padding
     for gib in args.pad_gib:
         pad = torch.empty(gib << 28, dtype=torch.float32, device=dev) if gib > 0 else None
-        rig = StepRig(W7, dev, args.pad_arena)
+        rig = StepRig(W7, dev, False)
         res = rig.time_steps(args.reps, 2)
         n = rig.n
         line(f"pad {gib} GiB: one-pass step's AdamW", n, 32, res["adamw_ms"])

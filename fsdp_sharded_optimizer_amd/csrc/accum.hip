@@ -11,11 +11,13 @@
 // fp32 load and a 128-bit fp32 access per lane).  A workgroup of BS threads
 // covers Q groups per lane, the q-th at offset q*BS*4 in its tile, every
 // load of the tile issued before the first store.  The plain forms and the
-// accumulating fused form run Q = 1 in one-wave workgroups, uncapped: the
-// fastest shape on gfx950 (84 % of peak for the accumulating form, 85 % for
-// the overwriting one, 84.5 % with the norm partials, against 82 %, 83 % and
-// 79.8 % in 256-thread workgroups with the best Q and residency cap); the
-// overwriting fused form runs Q = 4 (see launch_grad_accum_norm_sq).
+// accumulating fused form run Q = 1 in one-wave workgroups: the fastest
+// shape on gfx950 (84 % of peak for the accumulating form, 85 % for the
+// overwriting one, 84.5 % with the norm partials, against 82 %, 83 % and
+// 79.8 % in 256-thread workgroups with the best Q and residency cap), the
+// plain accumulating form with residency capped by reserved LDS (kAddLds*,
+// 86 % on contiguous buffers), the others uncapped; the overwriting fused
+// form runs Q = 4 (see launch_grad_accum_norm_sq).
 //
 // Fused norm association (fixed by n, the overwrite flag and the gradient
 // dtype): each lane adds the squares of its Q groups of 4 elements, 0 and 2
@@ -112,6 +114,15 @@ constexpr int64_t per_block() { return (int64_t)kAccumBlock * 4 * Q; }
 // measured 82.7 % on gfx950 against 76-78 % for Q = 1 (for an fp32 gradient
 // that shape gives 80 %).
 constexpr int kFusedQAdd = 1;
+// The plain accumulating form caps residency with reserved LDS: 6 KiB per
+// one-wave workgroup (26 per CU) for a bf16 gradient, 7 KiB (22) for an fp32
+// one.  On buffers carved from one physically contiguous block they measured
+// 86.2-86.3 % and 85.7-85.9 % of the peak against 84.2-84.3 % and 84.6-84.8 %
+// uncapped (bf16 at 7 / 8 KiB: 86.6 / 85.1-85.5 %); on an ordinary
+// allocation 84.1-84.2 % and 84.0-84.2 % against 83.9-84.0 % and 84.1 %.
+// The overwriting and fused forms run uncapped (a cap measured no better).
+constexpr unsigned kAddLdsBf16 = 6144;
+constexpr unsigned kAddLdsF32 = 7168;
 constexpr int kFusedQOverwrite = 4;
 constexpr unsigned kFusedOverwriteLds = 12288;
 
@@ -287,8 +298,9 @@ hipError_t launch_grad_sum_norm_sq(const float* acc, const void* grad, int grad_
 
 hipError_t launch_grad_accum(float* acc, const void* grad, int grad_bf16, int64_t n, int overwrite,
                              bool vec_ok, hipStream_t stream) {
-    return overwrite ? dispatch<1, false, true>(acc, grad, grad_bf16, n, vec_ok, 0.0f, nullptr, 0, stream)
-                     : dispatch<1, false, false>(acc, grad, grad_bf16, n, vec_ok, 0.0f, nullptr, 0, stream);
+    if (overwrite) return dispatch<1, false, true>(acc, grad, grad_bf16, n, vec_ok, 0.0f, nullptr, 0, stream);
+    return dispatch<1, false, false>(acc, grad, grad_bf16, n, vec_ok, 0.0f, nullptr,
+                                     grad_bf16 ? kAddLdsBf16 : kAddLdsF32, stream);
 }
 
 // workspace partials: the larger count of the two fused shapes

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import fsdp_sharded_optimizer_amd as zs
-from fsdp_sharded_optimizer_amd.arena import ALIGN
+from fsdp_sharded_optimizer_amd.arena import ALIGN, pooled_blocks
 from tests.parity import bits_equal, from_np, to_np
 
 pytestmark = pytest.mark.gpu
@@ -44,10 +44,12 @@ def test_views_aligned_disjoint_and_typed():
             assert torch.equal(v.cpu(), want)
 
 
-def test_views_keep_the_block_alive():
-    print("arena lifetime", flush=True)
+def test_views_keep_the_block_alive_and_the_pool_reuses_it():
+    print("arena lifetime and pool", flush=True)
     arena = zs.DeviceArena(2 * ALIGN, "cuda")
+    assert arena.contiguous
     alive = weakref.ref(arena)
+    block = (arena.capacity, arena.ptr)
     a = arena.take(100, torch.float32)
     b = arena.take(100, torch.bfloat16)
     del arena
@@ -59,10 +61,22 @@ def test_views_keep_the_block_alive():
     assert a.sum().item() == 150.0 and b.float().sum().item() == 250.0
     del a
     gc.collect()
-    assert alive() is not None
+    assert alive() is not None and block not in pooled_blocks()
     del b
     gc.collect()
-    assert alive() is None                        # freed with its last view
+    assert alive() is None                        # gone with its last view
+    assert block in pooled_blocks()               # its block kept for reuse, not freed
+    expect = min(b for b in pooled_blocks() if b[0] >= ALIGN)
+    again = zs.DeviceArena(ALIGN, "cuda")          # takes the smallest pooled block that holds it
+    held = (again.capacity, again.ptr)
+    assert again.contiguous and held == expect and held not in pooled_blocks()
+    v = again.take(ALIGN // 4, torch.float32)
+    v.fill_(3.0)
+    torch.cuda.synchronize()
+    assert v.sum().item() == 3.0 * (ALIGN // 4)
+    del again, v
+    gc.collect()
+    assert held in pooled_blocks()
 
 
 def test_take_rejects():
