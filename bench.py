@@ -400,6 +400,8 @@ def run_gpu(rig: StepRig, steps: int, warmup: int):
     r = rig.time_steps(steps, warmup)
     r["n"] = n
     r["chunks"] = len(rig.grads)
+    r["buffers"] = ("one physically contiguous block (DeviceArena)" if rig.arena is not None and rig.arena.contiguous
+                    else "separate allocations" if rig.arena is None else "one ordinary block")
     ev = DeviceEvent
 
     # outside the step: the same step captured once in a HIP graph and
@@ -1004,7 +1006,8 @@ def main():
         "data": "synthetic (seeded U(-0.1,0.1) master, N(0,std) bf16 micro-batch grads)",
         "config": {"workload": w.name, "shard_elems": n, "total_params": w.total, "world": w.world,
                    "rank": w.rank, "micro_batches": w.micro_batches, "grad_dtype": w.grad_dtype,
-                   "state": "fp32 master/exp_avg/exp_avg_sq (tiled layout) + bf16 param", "clip": w.max_norm > 0},
+                   "state": "fp32 master/exp_avg/exp_avg_sq (tiled layout) + bf16 param", "clip": w.max_norm > 0,
+                   "buffers": r["buffers"]},
         "graph_ms_per_step": r["graph_ms"],
         "step_hbm_gbps": step_gbps,
         "step_hbm_frac": step_gbps / HBM_PEAK_GBPS,

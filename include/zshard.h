@@ -51,6 +51,16 @@
  *     1-31 elements of views that share one offset off that boundary element
  *     by element and the rest on the 128-bit path.
  *   - bf16 values are passed as their 16-bit patterns (uint16_t).
+ *   - Placement (speed only): on gfx950 the streaming calls ran 1-6 points
+ *     of the HBM peak faster with a rank's streamed buffers (tiled state,
+ *     accumulator, micro-batch gradients, bf16 parameter) carved from one
+ *     hipExtMallocWithFlags(..., hipDeviceMallocContiguous) block allocated
+ *     at start-up than as separate allocations made after other processes
+ *     had allocated and freed device memory.  Such a block bypasses the L2
+ *     for writes, so keep the norm workspaces (sparse 8-byte partials) and
+ *     *out_sq_dev out of it, and do not free it before the process ends:
+ *     freeing memory of that kind has left later allocations holding stale
+ *     values on this hardware.
  */
 #ifndef ZSHARD_H
 #define ZSHARD_H
