@@ -142,3 +142,38 @@ def test_shard_optimizer_in_an_arena_is_bit_identical(layout, last_grad):
         assert bits_equal(to_np(a.acc), to_np(b.acc))
         assert a.norm_sq.item() == b.norm_sq.item()
         assert torch.equal(params[0].view(torch.int16), params[1].view(torch.int16))
+
+
+@pytest.mark.parametrize("layout", ["tiled", "split"])
+def test_captured_step_in_an_arena_replays_like_eager_steps(layout):
+    """ShardOptimizer.capture on an optimizer whose state, accumulator,
+    gradients and bf16 parameter are views of one contiguous block: four
+    replays with new gradients, bit-identical to the same steps taken
+    eagerly on separately allocated buffers."""
+    print(f"capture in an arena layout={layout}", flush=True)
+    n, M = 70_001, 3
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(47)
+    p0 = torch.rand(n, generator=gen, device="cuda") * 0.2 - 0.1
+    kw = dict(lr=3e-4, betas=(0.9, 0.95), weight_decay=0.1, grad_scale=1 / 24, max_norm=0.5, layout=layout)
+    parts = zs.ShardOptimizer.arena_parts(n, layout) + [(n, torch.bfloat16)] * (M + 1)
+    arena = zs.DeviceArena(zs.DeviceArena.size(parts), "cuda")
+    a = zs.ShardOptimizer(p0.clone(), param_bf16=arena.take(n, torch.bfloat16), arena=arena, **kw)
+    grads = [arena.take(n, torch.bfloat16) for _ in range(M)]
+    b = zs.ShardOptimizer(p0.clone(), param_bf16=torch.empty(n, dtype=torch.bfloat16, device="cuda"), **kw)
+    cap = a.capture(grads, extra_norm_sq=0.02)
+    torch.cuda.synchronize()
+    assert a.t == 0 and bits_equal(to_np(a.master), to_np(p0))
+    for t in range(1, 5):
+        for k, g in enumerate(grads):
+            g.copy_((torch.randn(n, generator=gen, device="cuda") * 1e-2 * (k + t)).to(torch.bfloat16))
+        cap.replay()
+        for g in grads[:M - 1]:
+            b.accumulate(g)
+        b.step(extra_norm_sq=0.02, last_grad=grads[-1])
+        torch.cuda.synchronize()
+        assert a.t == b.t == t
+        for name in ("master", "exp_avg", "exp_avg_sq", "param_bf16", "acc"):
+            assert bits_equal(to_np(getattr(a, name)), to_np(getattr(b, name))), (t, name)
+        assert a.norm_sq.item() == b.norm_sq.item()
+        _ = (b.acc * 2).sum().item()   # unrelated eager work between replays
