@@ -17,8 +17,9 @@ memory of that kind has left later allocations holding stale values on this
 hardware (a fresh tensor read back its pre-kernel contents after arenas had
 been freed), so a contiguous block is never returned to the driver: when the
 arena and every view of it are gone (each view keeps the arena alive), the
-block goes to a per-process pool, after a device synchronisation, and a
-later arena on the same device that fits in it reuses it.  Each device holds
+block goes to a per-process pool, and a later arena on the same device that
+fits in it reuses it after a device synchronisation (so work still queued
+on the old views ends first).  Each device holds
 its pooled blocks until the process ends.  When the runtime cannot give a
 contiguous block (device memory too fragmented), the arena falls back to an
 ordinary allocation of the same size, says so in ``contiguous``, and frees
@@ -104,6 +105,10 @@ class DeviceArena:
             fits = [b for b in pool if b[0] >= self.nbytes]
             if fits:   # the smallest pooled block that holds the request
                 block = min(fits)
+                with torch.cuda.device(self.device):
+                    rc = L.hipDeviceSynchronize()   # work queued on the block's last views has ended
+                if rc != 0:
+                    raise RuntimeError(f"DeviceArena: hipDeviceSynchronize returned {rc}")
                 pool.remove(block)
                 self.capacity, self.ptr = block
                 self.contiguous = True
@@ -152,9 +157,11 @@ class DeviceArena:
         ptr, self.ptr = getattr(self, "ptr", None), None
         if ptr is None or sys.is_finalizing():
             return   # nothing held, or the interpreter is shutting down: the process's end frees the block
+        if self.contiguous:
+            # back to the pool as it is (no synchronisation here, so dropping
+            # an arena never blocks); the arena that takes it back synchronises
+            _pool.setdefault(self.device.index, []).append((self.capacity, ptr))
+            return
         with torch.cuda.device(self.device):
-            _hip.hipDeviceSynchronize()   # work queued on the views ends before the block is reused or freed
-            if self.contiguous:
-                _pool.setdefault(self.device.index, []).append((self.capacity, ptr))
-            else:
-                _hip.hipFree(ctypes.c_void_p(ptr))
+            _hip.hipDeviceSynchronize()   # work queued on the views ends before the block is freed
+            _hip.hipFree(ctypes.c_void_p(ptr))
