@@ -18,6 +18,12 @@
  * grad_sum_norm_sq and adamw_step_tiled_sum on accumulator + third gradient:
  * the same norm bit for bit, the same state and bf16 output as the oracle's,
  * the accumulator left holding the first two micro-batches' sum.
+ * Run with the argument "contiguous", the streamed buffers (state, master,
+ * moments, accumulators, gradients, bf16 outputs) are carved from one
+ * hipExtMallocWithFlags(..., hipDeviceMallocContiguous) block, 256-byte
+ * aligned, as the header's placement note advises (the norms and the
+ * workspace stay hipMalloc'd, and the block is never freed: the process's
+ * end releases it); every check is the same.
  * Prints "c gpu step: ok" and exits 0, else the number of the failed check.
  */
 #include <math.h>
@@ -60,8 +66,21 @@ static uint16_t bf16_bits_trunc(float x)   /* an input value: the top half of x 
     return (uint16_t)(u >> 16);
 }
 
-int main(void)
+/* device memory for a streamed buffer: from the block when one is given (the
+ * next 256-byte-aligned bytes), else its own hipMalloc */
+static int dev_alloc(void** p, size_t bytes, char* block, size_t* used, size_t cap)
 {
+    if (block == NULL) return hipMalloc(p, bytes) == hipSuccess ? 0 : -1;
+    const size_t at = (*used + 255) / 256 * 256;
+    if (at + bytes > cap) return -1;
+    *p = block + at;
+    *used = at + bytes;
+    return 0;
+}
+
+int main(int argc, char** argv)
+{
+    const int contiguous = argc > 1 && strcmp(argv[1], "contiguous") == 0;
     const int64_t n = 100003;
     const int M = 3;
     const double scale = 1.0 / 24;
@@ -89,21 +108,27 @@ int main(void)
     const int64_t ws_bytes = grad_accum_norm_sq_workspace_bytes(n);
     const int64_t st = state_tiled_numel(n);
     CHECK(ws_bytes > 0 && st == 3 * (int64_t)ZS_STATE_TILE * ((n + ZS_STATE_TILE - 1) / ZS_STATE_TILE), 2);
-    HIPOK(hipMalloc((void**)&d_master, sizeof(float) * n), 3);
-    HIPOK(hipMalloc((void**)&d_state, sizeof(float) * st), 3);
-    HIPOK(hipMalloc((void**)&d_acc, sizeof(float) * n), 3);
-    HIPOK(hipMalloc((void**)&d_p, sizeof(float) * n), 3);
-    HIPOK(hipMalloc((void**)&d_m, sizeof(float) * n), 3);
-    HIPOK(hipMalloc((void**)&d_v, sizeof(float) * n), 3);
-    HIPOK(hipMalloc((void**)&d_g, sizeof(uint16_t) * n * M), 3);
-    HIPOK(hipMalloc((void**)&d_b, sizeof(uint16_t) * n), 3);
+    /* the streamed buffers: 7 fp32 arrays of n, 2 tiled states, M + 2 bf16 arrays, each padded to 256 bytes */
+    const size_t cap = 7 * (sizeof(float) * n + 256) + 2 * (sizeof(float) * st + 256) +
+                       (size_t)(M + 2) * (sizeof(uint16_t) * n + 256);
+    char* block = NULL;
+    size_t used = 0;
+    if (contiguous) HIPOK(hipExtMallocWithFlags((void**)&block, cap, hipDeviceMallocContiguous), 3);
+    CHECK(dev_alloc((void**)&d_master, sizeof(float) * n, block, &used, cap) == 0, 3);
+    CHECK(dev_alloc((void**)&d_state, sizeof(float) * st, block, &used, cap) == 0, 3);
+    CHECK(dev_alloc((void**)&d_acc, sizeof(float) * n, block, &used, cap) == 0, 3);
+    CHECK(dev_alloc((void**)&d_p, sizeof(float) * n, block, &used, cap) == 0, 3);
+    CHECK(dev_alloc((void**)&d_m, sizeof(float) * n, block, &used, cap) == 0, 3);
+    CHECK(dev_alloc((void**)&d_v, sizeof(float) * n, block, &used, cap) == 0, 3);
+    CHECK(dev_alloc((void**)&d_g, sizeof(uint16_t) * n * M, block, &used, cap) == 0, 3);
+    CHECK(dev_alloc((void**)&d_b, sizeof(uint16_t) * n, block, &used, cap) == 0, 3);
     HIPOK(hipMalloc((void**)&d_norm, sizeof(double)), 3);
     HIPOK(hipMalloc((void**)&d_norm_ref, sizeof(double)), 3);
     HIPOK(hipMalloc((void**)&d_norm2, sizeof(double)), 3);
-    HIPOK(hipMalloc((void**)&d_acc2, sizeof(float) * n), 3);
-    HIPOK(hipMalloc((void**)&d_acc3, sizeof(float) * n), 3);
-    HIPOK(hipMalloc((void**)&d_state2, sizeof(float) * st), 3);
-    HIPOK(hipMalloc((void**)&d_b2, sizeof(uint16_t) * n), 3);
+    CHECK(dev_alloc((void**)&d_acc2, sizeof(float) * n, block, &used, cap) == 0, 3);
+    CHECK(dev_alloc((void**)&d_acc3, sizeof(float) * n, block, &used, cap) == 0, 3);
+    CHECK(dev_alloc((void**)&d_state2, sizeof(float) * st, block, &used, cap) == 0, 3);
+    CHECK(dev_alloc((void**)&d_b2, sizeof(uint16_t) * n, block, &used, cap) == 0, 3);
     HIPOK(hipMalloc((void**)&d_norm3, sizeof(double)), 3);
     HIPOK(hipMalloc(&d_ws, (size_t)ws_bytes), 3);
     HIPOK(hipMemcpy(d_master, p_ref, sizeof(float) * n, hipMemcpyHostToDevice), 4);
@@ -182,9 +207,11 @@ int main(void)
     CHECK(memcmp(back, acc_ref, sizeof(float) * n) == 0, 28);
     CHECK(zs_last_hip_error() == 0, 19);
 
-    hipFree(d_master); hipFree(d_state); hipFree(d_acc); hipFree(d_p); hipFree(d_m); hipFree(d_v);
-    hipFree(d_g); hipFree(d_b); hipFree(d_norm); hipFree(d_norm_ref); hipFree(d_ws); hipFree(d_norm2); hipFree(d_acc2);
-    hipFree(d_acc3); hipFree(d_state2); hipFree(d_b2); hipFree(d_norm3);
+    if (!contiguous) {   /* a contiguous block is never freed: the process's end releases it */
+        hipFree(d_master); hipFree(d_state); hipFree(d_acc); hipFree(d_p); hipFree(d_m); hipFree(d_v);
+        hipFree(d_g); hipFree(d_b); hipFree(d_acc2); hipFree(d_acc3); hipFree(d_state2); hipFree(d_b2);
+    }
+    hipFree(d_norm); hipFree(d_norm_ref); hipFree(d_ws); hipFree(d_norm2); hipFree(d_norm3);
     free(p_ref); free(m_ref); free(v_ref); free(acc_ref); free(b_ref); free(g); free(back); free(back16);
     printf("c gpu step: ok\n");
     return 0;

@@ -1,6 +1,7 @@
 """The C ABI driven from a C program on the GPU (tests/c_gpu_step.c): device
-memory from hipMalloc, the library's calls in the order a rank's step makes
-them, the oracle linked beside it.  Built here with gcc -std=c11 against
+memory from hipMalloc, or the streamed buffers carved from one contiguous
+block as the header's placement note advises, the library's calls in the
+order a rank's step makes them, the oracle linked beside it.  Built here with gcc -std=c11 against
 include/zshard.h, libzshard.so, liboracle.so and the HIP runtime."""
 import os
 import shutil
@@ -16,7 +17,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 
-def test_c_program_runs_a_tiled_step_like_the_oracle(tmp_path):
+@pytest.mark.parametrize("placement", ["hipMalloc", "contiguous"])
+def test_c_program_runs_a_tiled_step_like_the_oracle(tmp_path, placement):
     gcc = shutil.which("gcc")
     if gcc is None:
         pytest.skip("gcc not available")
@@ -32,7 +34,8 @@ def test_c_program_runs_a_tiled_step_like_the_oracle(tmp_path):
                     "-L", os.path.join(ROCM, "lib"), "-lamdhip64", "-lm",
                     f"-Wl,-rpath,{os.path.dirname(B.LIB_PATH)}:{os.path.dirname(orc_so)}:{os.path.join(ROCM, 'lib')}"],
                    check=True)
-    print("c gpu step: run", flush=True)
-    out = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    print(f"c gpu step: run ({placement})", flush=True)
+    out = subprocess.run([exe] + (["contiguous"] if placement == "contiguous" else []), capture_output=True, text=True,
+                         timeout=120)
     assert out.returncode == 0, (out.returncode, out.stderr)
     assert out.stdout.strip() == "c gpu step: ok"
